@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""Benchmark: effective weight GB/s of batch-1 dequant GEMV on one MI355X.
+
+Metric (DBHOO-CIM page, section 4.4: effective bandwidth = weight bytes / latency): the
+algorithmic bytes of the packed weights (codes + every scale byte) divided by the GPU time,
+reported as GB/s and as a fraction of the 8 TB/s HBM peak.
+
+Workload (default): the 3-bit super-block matrix 4096 x 4096 (Laplace(0, 0.02) weights, fp16
+N(0, 1) activations, batch 1). One step is one launch of G independent batch-1 GEMVs of that
+shape (default G = 32, 230 MB of packed weights), each with its own matrix copy and its own
+activation vector. Steps rotate over enough copies (>= 1.2 GB) that every step reads its
+weights from HBM, not from the 256 MB last-level cache. A single 7.2 MB matrix per launch is
+also timed ("single_launch"): at ~1 us of streaming it is bound by launch cadence, not HBM.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "effective weight GB/s (and % of HBM peak) for batch-1 dequant GEMV"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="q3sb_gemv_4096")
+    ap.add_argument("--group", type=int, default=32, help="independent batch-1 GEMVs per launch")
+    ap.add_argument("--footprint-gb", type=float, default=1.2)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-single", action="store_true", help="skip the one-matrix-per-launch timing")
+    return ap.parse_args()
+
+
+def cpu_baseline(fmt, canonical, n, k, x, seconds):
+    """The oracle as it stands (NumPy decode + fp64 matvec), single-threaded, on a bounded
+    sample of rows of the same matrix; returns GB/s of packed weights processed."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    from oracle import gemv as ogemv
+    from oracle import int4
+    from oracle import superblock as sb
+
+    chunk = 64
+    done = 0
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        while time.perf_counter() - t0 < seconds:
+            r0 = done % n
+            r1 = min(n, r0 + chunk)
+            if fmt == "q4g32":
+                codes = canonical[: n * k // 2].reshape(n, k // 2)[r0:r1]
+                scales = canonical[n * k // 2:].view(np.float32).reshape(n, k // 32)[r0:r1]
+                w_hat = int4.decode(codes, scales, k)
+            else:
+                rec = canonical.reshape(n, k // 256, -1)[r0:r1]
+                w_hat = sb.decode(fmt, rec)
+            ogemv.gemv(w_hat, x)
+            done += r1 - r0
+        dt = time.perf_counter() - t0
+    row_bytes = canonical.size // n
+    return {"value": round(done * row_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": f"{done} rows ({done / n:.2f} passes) of the {n}x{k} {fmt} matrix: NumPy decode of the "
+                      f"canonical encoding + fp64 matvec, one thread, {dt:.1f} s"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on exactly one GPU; the dequant GEMV path is "
+                                   "single-GPU (row sharding across GPUs is a design note only)",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import dequant_gemv_q4g32_amd as qg
+    from workloads import WORKLOADS
+
+    wl = WORKLOADS[args.workload]
+    fmt = wl.fmt
+    n, k = wl.shapes[0]
+    dev = torch.device("cuda:0")
+    log(f"[bench] {args.workload}: {fmt} {n}x{k}, {args.group} GEMVs per launch")
+
+    w = wl.weights(0)
+    canonical = qg.quantize(fmt, w)
+    lay = qg.device_layout(fmt, n, k)
+    alg = lay.algorithmic_bytes
+    stride = (lay.total_bytes + 255) // 256 * 256
+    one = torch.from_numpy(qg.to_device_layout(fmt, canonical, n, k)).to(dev)
+
+    G = args.group
+    sets = max(3, int(np.ceil(args.footprint_gb * 1e9 / (G * stride))))
+    copies = sets * G
+    buf = torch.empty(copies * stride, dtype=torch.uint8, device=dev)
+    for c in range(copies):
+        buf[c * stride:c * stride + lay.total_bytes].copy_(one)
+    xs = torch.from_numpy(wl.x(0, m=copies)).to(dev)
+    ys = torch.empty((copies, n), dtype=torch.float16, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] {copies} copies x {stride / 1e6:.2f} MB = {copies * stride / 1e9:.2f} GB resident")
+
+    def step(i):
+        s = i % sets
+        qg.gemv_batched(fmt, buf[s * G * stride:], stride, xs[s * G:], ys[s * G:], G, n, k)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for i in range(args.steps):
+        step(args.warmup + i)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms = ev0.elapsed_time(ev1) / args.steps
+    gbps = G * alg / (ms * 1e-3) / 1e9
+    log(f"[bench] grouped: {ms * 1e3:.2f} us per launch, {gbps:.0f} GB/s")
+
+    # check the timed outputs of one set against a single-matrix launch (same kernels)
+    ref = qg.gemv(fmt, one, xs[0], n, k)
+    torch.cuda.synchronize()
+    assert torch.equal(ref, ys[0]), "grouped output differs from single launch"
+
+    # read ceiling over the same resident buffer
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    span = sets * G * stride // 3 // 16 * 16
+    for i in range(3):
+        qg.read_probe(buf[(i % 3) * span:], span, sink)
+    torch.cuda.synchronize()
+    ev0.record()
+    reps = 12
+    for i in range(reps):
+        qg.read_probe(buf[(i % 3) * span:], span, sink)
+    ev1.record()
+    torch.cuda.synchronize()
+    ceiling = span / (ev0.elapsed_time(ev1) / reps * 1e-3) / 1e9
+    log(f"[bench] read ceiling ({span / 1e6:.0f} MB per launch): {ceiling:.0f} GB/s")
+
+    single = None
+    if not args.no_single:
+        iters = 400
+        for i in range(20):
+            qg.gemv(fmt, buf[(i % copies) * stride:], xs[i % copies], n, k, out=ys[i % copies])
+        torch.cuda.synchronize()
+        ev0.record()
+        for i in range(iters):
+            qg.gemv(fmt, buf[(i % copies) * stride:], xs[i % copies], n, k, out=ys[i % copies])
+        ev1.record()
+        torch.cuda.synchronize()
+        us_stream = ev0.elapsed_time(ev1) / iters * 1e3
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(iters):
+                qg.gemv(fmt, buf[(i % copies) * stride:], xs[i % copies], n, k, out=ys[i % copies])
+        g.replay()
+        torch.cuda.synchronize()
+        ev0.record()
+        g.replay()
+        ev1.record()
+        torch.cuda.synchronize()
+        us_graph = ev0.elapsed_time(ev1) / iters * 1e3
+        single = {"us_per_gemv_stream": round(us_stream, 3), "GBps_stream": round(alg / us_stream / 1e3, 1),
+                  "us_per_gemv_graph": round(us_graph, 3), "GBps_graph": round(alg / us_graph / 1e3, 1)}
+        log(f"[bench] single launch: stream {us_stream:.2f} us, graph {us_graph:.2f} us per GEMV")
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("[bench] timing the oracle on the host ...")
+        cpu = cpu_baseline(fmt, canonical, n, k, wl.x(0)[0], args.cpu_seconds)
+        log(f"[bench] oracle: {cpu['value']} GB/s ({cpu['sample']})")
+
+    out = {
+        "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "fp16xfp16->fp32", "data": "synthetic",
+        "config": {"workload": f"{args.workload}: {fmt} {n}x{k}, batch 1, {G} independent matrices per launch",
+                   "fmt": fmt, "n": n, "k": k, "batch": 1, "matrices_per_launch": G,
+                   "algorithmic_bytes_per_matrix": alg, "resident_GB": round(copies * stride / 1e9, 3)},
+        "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+        "read_ceiling_GBps": round(ceiling, 1),
+        "frac_of_read_ceiling": round(gbps / ceiling, 4),
+        "single_launch": single,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

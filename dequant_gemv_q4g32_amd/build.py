@@ -1,0 +1,71 @@
+"""Build libqgemv.so in-tree with hipcc for gfx950.
+
+Host code (quantizers, layouts) is compiled as plain C++ with -ffp-contract=off so that no
+multiply-add is fused in the quantizers' integer decisions. Device code is compiled for
+gfx950 only, with packed fp32 instructions disabled.
+
+Usage: python dequant_gemv_q4g32_amd/build.py  (a plain script: it must not import the package,
+whose import loads the library it builds).
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(PKG)
+CSRC = os.path.join(PKG, "csrc")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(PKG, "libqgemv.so")
+
+HOST_SOURCES = ["host.cpp"]
+DEVICE_SOURCES = ["gemv.hip"]
+ARCH = "gfx950"
+
+
+def _hipcc() -> str:
+    for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if cand and os.path.exists(cand):
+            return cand
+    raise RuntimeError("hipcc not found; the ROCm toolchain is required to build libqgemv")
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"build step failed: {' '.join(cmd)}")
+    return res
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = _hipcc()
+    os.makedirs(BUILD, exist_ok=True)
+    objs = []
+    common = ["-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function", f"-I{ROOT}/include"]
+    for src in HOST_SOURCES:
+        obj = os.path.join(BUILD, src + ".o")
+        _run([hipcc, "-x", "c++", "-O2", "-ffp-contract=off", *common, "-c", os.path.join(CSRC, src), "-o", obj],
+             verbose)
+        objs.append(obj)
+    for src in DEVICE_SOURCES:
+        path = os.path.join(CSRC, src)
+        if not os.path.exists(path):
+            continue
+        obj = os.path.join(BUILD, src + ".o")
+        _run([hipcc, f"--offload-arch={ARCH}", "-O3", *common,
+              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+              "-c", path, "-o", obj], verbose)
+        objs.append(obj)
+    tmp = LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, "-lpthread"], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

@@ -1,0 +1,81 @@
+// Device layout of the packed formats: planes, per-lane units and bit placement.
+//
+// The unit of work of one lane is 64 consecutive weights of one row ("lane unit"). Every
+// plane is [n][row_bytes] row-major with row_bytes = (k / 64) * unit_bytes, so that lane u
+// of a wave reads its unit with one or two 128-bit (or 64/32-bit) loads and consecutive
+// lanes read consecutive bytes.
+//
+// Inside a unit the codes are placed so that one v_and_or_b32 (mask, | 0x6400 in both
+// halves) yields a pair of fp16 values (1024 + p*c_a, 1024 + p*c_b) for a power of two p,
+// which v_dot2_f32_f16 multiplies with the activation pair (x[2t], x[2t+1]). The 1024 and
+// the code offsets are folded into per-lane constants computed once from x.
+//
+// Placement per format (positions are unit-relative weight indices 0..63; "pair t" means
+// weights 2t (low fp16 half, bits 0..15) and 2t+1 (high half, bits 16..31)):
+//
+//  q4g32  plane 0 codes: 8 dwords/unit, dword i holds weights 8i..8i+7, weight 8i+e in
+//         nibble slot (e>>1) + 4*(e&1); plane 1 fp32 scales (one per group of 32).
+//  q2sb   plane 0 codes: 4 dwords/unit (a quarter super-block, 4 sub-blocks j of 16).
+//         Pair t of sub-block j = t>>3, r = t&7 sits in dword r>>1 at bit 2j + 8*(r&1)
+//         (+16 for the high half). Extraction mask 0x00030003 << 2j, class p = 4^j.
+//         plane 1 sub-block bytes (sc | m<<4, 4 per unit), plane 2 (fp16 d, fp16 dmin).
+//  q3sb   plane 0 (16 B/unit) + plane 1 (8 B/unit): two chunks of three dwords E0..E2, each
+//         chunk holding 32 codes = sub-blocks a (first 16) and b. Each 16-bit half holds five
+//         3-bit fields f0..f4 at bits 0,3,6,9,12; bit 15 is a spare. Sub-block a pairs
+//         r=0..7 -> (E0,f0) (E0,f3) (E1,f0) (E1,f3) (E2,f0) (E2,f3) (E0,f1) (E0,f4);
+//         sub-block b pairs -> (E1,f1) (E1,f4) (E2,f1) (E2,f4) (E0,f2) (E1,f2) (E2,f2) spare,
+//         where the spare pair's code bits 0,1,2 are bit 15 of E0,E1,E2 (low half) and
+//         bit 31 (high half). Plane 0 = chunk0 E0 E1 E2, chunk1 E0; plane 1 = chunk1 E1 E2.
+//         plane 2: 12 B/super-block of 6-bit sub-scales (canonical order), plane 3 fp16 d.
+//  q5sb   plane 0 low nibbles: 8 dwords/unit in the q4g32 nibble placement. plane 1 high
+//         bits: 2 dwords/unit; dword h serves nibble dwords 4h..4h+3 (sub-block h). For
+//         nibble dword i (i' = i & 3) and its pairs k = 0..3 (weights (2k, 2k+1) of the
+//         dword) the high bits sit at bits {4,20}+i', {8,24}+i', {12,28}+i', {16,0}+i'.
+//         plane 2: 3 B/unit of 6-bit fields [sc_2q, sc_2q+1, m_2q, m_2q+1]; plane 3 (d, dmin).
+//  q6sb   plane 0 low nibbles as q5sb. plane 1 high 2-bit fields: 4 dwords/unit; dword h
+//         serves nibble dwords 2h, 2h+1 (sub-block h); for i' = i & 1 the 2-bit fields sit at
+//         bits {4,20}+2i', {8,24}+2i', {12,28}+2i', {16,0}+2i'. plane 2 int8 sub-scales,
+//         plane 3 fp16 d.
+#pragma once
+#include <stdint.h>
+
+namespace qg {
+
+constexpr int kUnit = 64;          // weights per lane unit
+constexpr int kQK = 256;           // weights per super-block
+constexpr int64_t kPlaneAlign = 256;
+
+// Bytes per lane unit of each plane, and the number of planes.
+struct FmtPlanes {
+  int nplanes;
+  int unit_bytes[4];   // bytes per 64-weight unit; 0 for planes sized per super-block
+  int sb_bytes[4];     // bytes per 256-weight super-block (when unit_bytes == 0)
+};
+
+inline bool fmt_valid(int fmt) { return fmt == 2 || fmt == 3 || fmt == 4 || fmt == 5 || fmt == 6; }
+
+inline FmtPlanes fmt_planes(int fmt) {
+  switch (fmt) {
+    case 4: return {2, {32, 8, 0, 0}, {0, 0, 0, 0}};          // codes, fp32 scales
+    case 2: return {3, {16, 4, 0, 0}, {0, 0, 4, 0}};          // codes, sc|m, (d, dmin)
+    case 3: return {4, {16, 8, 0, 0}, {0, 0, 12, 2}};         // codes A, codes B, sc, d
+    case 5: return {4, {32, 8, 0, 0}, {0, 0, 12, 4}};         // lo, hi, sc/m, (d, dmin)
+    case 6: return {4, {32, 16, 4, 0}, {0, 0, 0, 2}};         // lo, hi, sc, d
+    default: return {0, {0, 0, 0, 0}, {0, 0, 0, 0}};
+  }
+}
+
+// Row bytes of plane p for a row of k weights (k a multiple of 256, or of 32 for q4g32).
+inline int64_t plane_row_bytes(int fmt, int p, int64_t k) {
+  FmtPlanes f = fmt_planes(fmt);
+  if (fmt == 4) return p == 0 ? k / 2 : (k / 32) * 4;
+  if (f.unit_bytes[p]) return (k / kUnit) * f.unit_bytes[p];
+  return (k / kQK) * f.sb_bytes[p];
+}
+
+inline int64_t align_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// q4g32 nibble slot of weight e (0..7) inside a code dword.
+inline int q4_slot(int e) { return (e >> 1) + 4 * (e & 1); }
+
+}  // namespace qg

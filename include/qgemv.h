@@ -1,0 +1,181 @@
+/*
+ * qgemv.h - C ABI of libqgemv: weight-only low-bit dequantize-and-multiply on MI355X (gfx950).
+ *
+ * Formats (one byte table per 256 weights, "二三五六位量化" page section 2.3; INT4 from the
+ * DBHOO-CIM page sections 2.1, 3.1, 3.2 and 4.1):
+ *
+ *   QG_Q4G32  INT4 symmetric, groups of 32 consecutive weights of a row, fp32 scale per group:
+ *             scale = max(max|w| / 8, 1e-12), q = clamp(rint(w / scale), -8, 7) in fp32,
+ *             w_hat = q * scale; 16 B of codes + 4 B of scale per group (5.0 bpw).
+ *   QG_Q2SB   256-weight super-block, 16 sub-blocks of 16, 2-bit codes c, 4-bit sub-scale sc
+ *             and 4-bit sub-min m, fp16 d and dmin: w_hat = d*sc*c - dmin*m  (84 B, 2.625 bpw).
+ *   QG_Q3SB   16 sub-blocks of 16, 3-bit codes, 6-bit sc, fp16 d: w_hat = d*sc*(c - 4)
+ *             (110 B, 3.4375 bpw).
+ *   QG_Q5SB   8 sub-blocks of 32, 5-bit codes (low-4-bit plane + high-bit plane), 6-bit sc and
+ *             m, fp16 d and dmin: w_hat = d*sc*c - dmin*m  (176 B, 5.5 bpw).
+ *   QG_Q6SB   16 sub-blocks of 16, 6-bit codes (low-4-bit plane + high-2-bit plane), int8 sc,
+ *             fp16 d: w_hat = d*sc*(c - 32)  (210 B, 6.5625 bpw).
+ *
+ * Super-block scales are chosen by "range-covering round to nearest" (the pages give the
+ * layouts, not the rule): with fp16_ceil(v) = smallest fp16 >= v, symmetric formats take
+ * t_j = max|w_j| / (o - 0.5), d = fp16_ceil(max_j t_j / Smax), sc_j = min(Smax, ceil(t_j / d));
+ * asymmetric formats take dmin = fp16_ceil(max_j(-min(0, min w_j)) / Smax),
+ * m_j = min(Smax, ceil(-min(0, min w_j) / dmin)), t_j = (max(0, max w_j) + dmin*m_j) / (2^b - 1)
+ * and d, sc_j as above; codes are rint (half to even) of w / (d*sc_j) (+ o), or of
+ * (w + dmin*m_j) / (d*sc_j), clamped. All in fp64. Every weight is then within d*sc_j / 2.
+ * Smax = 15 (q2sb), 63 (q3sb, q5sb), 127 (q6sb).
+ *
+ * Two encodings of a quantized matrix W [n][k] (W is out_features x in_features):
+ *   canonical  the pages' interchange layout. q4g32: codes [n][k/2] (byte = u[2j] | u[2j+1] << 4
+ *              with u = q + 8) followed by fp32 scales [n][k/32]. Super-block formats: records
+ *              [n][k/256] of 84/110/176/210 bytes; fields in the byte table's column order
+ *              (codes [, high-bit plane], sub-scales, d [, dmin]); every bit field is a
+ *              little-endian bitstream (code i at bits [b*i, b*i + b), section 2.2's unpack3
+ *              and unpack5); q2sb sub-block byte = sc | m << 4; q5sb's 12 bytes hold sixteen
+ *              6-bit fields sc0..sc7, m0..m7; fp16 values little-endian.
+ *   device     a planar, bit-permuted rearrangement of exactly the same bits, built for
+ *              128-bit coalesced lane loads and single-instruction field extraction on CDNA4.
+ *              Each plane is [n][row_bytes] row-major and starts 256-byte aligned. The planes
+ *              hold the same number of bytes as the canonical encoding (plus < 1 KiB of
+ *              inter-plane padding, never read). It is opaque: build it with
+ *              qg_to_device_layout and read it back with qg_from_device_layout.
+ *
+ * Conventions: all sizes are int64_t. fp16 values are passed as uint16_t bit patterns.
+ * `stream` is a hipStream_t (NULL = the default stream). Every function returns a qg_status.
+ *
+ * Ownership: the caller allocates and owns every buffer, host and device. The library never
+ * allocates, frees or synchronizes, and keeps no pointer past the call. Host functions are
+ * pure and thread-safe. Device functions validate their arguments on the host, return an
+ * error without launching anything if they are invalid, and otherwise enqueue kernels on
+ * `stream` and return; execution faults surface at the caller's next synchronization.
+ */
+#ifndef QGEMV_H
+#define QGEMV_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QG_ABI_VERSION 1
+
+typedef enum qg_format {
+  QG_Q2SB = 2,
+  QG_Q3SB = 3,
+  QG_Q4G32 = 4,
+  QG_Q5SB = 5,
+  QG_Q6SB = 6
+} qg_format;
+
+typedef enum qg_status {
+  QG_OK = 0,
+  QG_ERR_NULL = -1,      /* a required pointer is NULL                                      */
+  QG_ERR_SHAPE = -2,     /* n, k or m out of range (k % 256 for super-blocks, k % 32 q4g32)  */
+  QG_ERR_ALIGN = -3,     /* a device pointer or leading dimension is misaligned              */
+  QG_ERR_NONFINITE = -4, /* a weight is NaN or infinite                                     */
+  QG_ERR_RANGE = -5,     /* d or dmin does not fit fp16 (section 2.3's overflow warning)     */
+  QG_ERR_FORMAT = -6,    /* unknown format or bit width                                     */
+  QG_ERR_LAUNCH = -7,    /* the HIP runtime refused a launch                                 */
+  QG_ERR_DEVICE = -8     /* no usable gfx950 device / HIP runtime error                       */
+} qg_status;
+
+#define QG_MAX_PLANES 4
+
+/* Device layout of one n x k matrix. */
+typedef struct qg_layout {
+  int64_t total_bytes;                        /* bytes to allocate (planes + padding)        */
+  int64_t algorithmic_bytes;                  /* bytes one dequant-GEMV must read            */
+  int32_t nplanes;
+  int32_t reserved;
+  int64_t plane_offset[QG_MAX_PLANES];        /* from the buffer start, 256-byte aligned     */
+  int64_t plane_row_bytes[QG_MAX_PLANES];     /* bytes per row of each plane                 */
+} qg_layout;
+
+int qg_abi_version(void);
+const char *qg_strerror(int status);
+/* HIP's description of the last launch the library saw fail on this thread (QG_ERR_LAUNCH). */
+const char *qg_last_hip_error(void);
+
+/* ---- sizes and layouts (host) ------------------------------------------------------- */
+
+/* Bytes of the canonical encoding of an n x k matrix. */
+int qg_canonical_bytes(int fmt, int64_t n, int64_t k, int64_t *bytes);
+/* Device layout of an n x k matrix. */
+int qg_device_layout(int fmt, int64_t n, int64_t k, qg_layout *out);
+
+/* ---- bitstreams (host; "二三五六位量化" page section 2.2) ---------------------------- */
+
+/* Pack count codes of `bits` bits (1..8) into a little-endian bitstream of
+ * ceil(count*bits/8) bytes; code i occupies stream bits [bits*i, bits*i + bits).
+ * Codes must be < 2^bits (QG_ERR_RANGE otherwise). */
+int qg_pack_bits(int bits, const uint8_t *codes, int64_t count, uint8_t *out);
+/* Inverse of qg_pack_bits. */
+int qg_unpack_bits(int bits, const uint8_t *in, int64_t count, uint8_t *codes);
+
+/* ---- quantizers (host, synchronous) -------------------------------------------------- */
+
+/* Quantize fp32 W [n][ldw] (first k columns used, ldw >= k) into the canonical encoding
+ * `canonical` (qg_canonical_bytes(fmt, n, k) bytes). Multi-threaded over rows; the output is
+ * independent of the thread count. Errors: QG_ERR_SHAPE, QG_ERR_NONFINITE, QG_ERR_RANGE. */
+int qg_quantize(int fmt, const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
+int quantize_q4g32(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
+int quantize_q2sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
+int quantize_q3sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
+int quantize_q5sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
+int quantize_q6sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
+
+/* Canonical encoding (host) -> device layout (host buffer of qg_device_layout().total_bytes;
+ * padding is zeroed). A pure bit permutation. */
+int qg_to_device_layout(int fmt, const uint8_t *canonical, int64_t n, int64_t k, uint8_t *device_layout);
+/* Device layout (host copy) -> canonical encoding. Inverse of qg_to_device_layout. */
+int qg_from_device_layout(int fmt, const uint8_t *device_layout, int64_t n, int64_t k, uint8_t *canonical);
+
+/* ---- dequant GEMV, batch 1 (device) ------------------------------------------------------
+ * y[r] = sum_c W_hat[r][c] * x[c] for r < n, with W in device layout (`w`, 256-byte aligned),
+ * x fp16 [k] (16-byte aligned), y fp16 [n]; fp32 accumulation, one fp16 rounding at the end.
+ * The packed weights are streamed once with 128-bit loads and decoded in registers; no
+ * dequantized weight is ever written to memory (DBHOO-CIM page section 3.3; "二三五六位量化"
+ * page section 3.3's gemv_q3 and its Sigma-x rewrite). n == 0 is a no-op; k == 0 writes
+ * zeros. Errors: QG_ERR_NULL, QG_ERR_SHAPE, QG_ERR_ALIGN, QG_ERR_FORMAT, QG_ERR_LAUNCH. */
+int dequant_gemv_q4g32(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
+int dequant_gemv_q2sb(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
+int dequant_gemv_q3sb(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
+int dequant_gemv_q5sb(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
+int dequant_gemv_q6sb(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
+
+/* Generic form: y_f32 != 0 writes fp32 y (4-byte aligned) instead of fp16. */
+int qg_gemv(int fmt, const void *w, const uint16_t *x, void *y, int y_f32, int64_t n, int64_t k, void *stream);
+
+/* Strided batch of independent GEMVs of one shape in one launch: for b < count,
+ * y_b = W_b x_b with W_b at w + b*w_stride (bytes, multiple of 256), x_b at x + b*x_stride
+ * and y_b at y + b*y_stride (elements; x_stride a multiple of 8). Same numerics as qg_gemv.
+ * This is how a decode step issues several same-shape projections (or experts) without a
+ * launch per matrix. */
+int qg_gemv_batched(int fmt, const void *w, int64_t w_stride, const uint16_t *x, int64_t x_stride,
+                    void *y, int64_t y_stride, int y_f32, int64_t count, int64_t n, int64_t k, void *stream);
+
+/* ---- decode to memory (device; for verification, not for inference) ----------------------
+ * Writes W_hat as fp32 [n][k] to w_out (if non-NULL) and the integer codes as uint8 [n][k]
+ * to codes_out (if non-NULL; q4g32 writes the unsigned nibble u = q + 8). fp32 values are
+ * single-rounding products (q*scale, d*sc*(c - o), fma(d*sc, c, -dmin*m)), hence exactly
+ * fp32(W_hat). */
+int dequantize_q4g32(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
+int dequantize_q2sb(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
+int dequantize_q3sb(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
+int dequantize_q5sb(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
+int dequantize_q6sb(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
+int qg_dequantize(int fmt, const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
+
+/* ---- measurement (device) -----------------------------------------------------------------
+ * Streams `bytes` bytes (a multiple of 16; buf 16-byte aligned) through 128-bit loads and
+ * writes nothing except, with negligible probability, one word of `sink`: the achievable HBM
+ * read rate against which the GEMV kernels are judged (the DBHOO-CIM page, section 5.3,
+ * measures the machine's ceiling with STREAM first). */
+int qg_read_probe(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QGEMV_H */

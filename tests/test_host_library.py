@@ -1,0 +1,152 @@
+"""CPU tests of libqgemv's host side: symbol exports, bitstreams, the five quantizers against
+the oracle (byte-exact canonical encodings), the device-layout permutation and error codes.
+
+No GPU work is launched here. The oracle and the library share no code: agreement of their
+canonical bytes is agreement of two independent implementations of the same spec.
+"""
+import ctypes
+
+import numpy as np
+import pytest
+
+import dequant_gemv_q4g32_amd as qg
+from oracle import bitstream, int4
+from oracle import superblock as sb
+from workloads import laplace_weights, uniform_codes
+
+FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb"]
+
+
+def oracle_canonical(fmt, w):
+    if fmt == "q4g32":
+        codes, scales = int4.encode(w)
+        return np.concatenate([codes.reshape(-1), scales.reshape(-1).view(np.uint8)])
+    return sb.encode(fmt, w).reshape(-1)
+
+
+def test_exports_every_declared_symbol():
+    names = qg.declared_functions()
+    assert len(names) >= 27
+    for name in names:
+        assert hasattr(qg.lib, name), name
+    assert qg.lib.qg_abi_version() == 1
+
+
+def test_strerror():
+    assert qg.lib.qg_strerror(0) == b"ok"
+    for st in range(-8, 0):
+        assert qg.lib.qg_strerror(st) != b"unknown status"
+
+
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 5, 6, 7, 8])
+def test_bitstreams_match_oracle(bits):
+    codes = uniform_codes(4099, bits, seed=300 + bits)
+    got = qg.pack_bits(bits, codes)
+    want = bitstream.pack_bits(codes, bits)
+    assert np.array_equal(got, want)
+    assert np.array_equal(qg.unpack_bits(bits, got, codes.size), codes)
+    if bits < 8:
+        bad = codes.copy()
+        bad[17] = 1 << bits
+        with pytest.raises(qg.QGError):
+            qg.pack_bits(bits, bad)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("shape,seed,outl", [((7, 512), 1, 0.0), ((33, 1024), 2, 0.01), ((5, 4352), 3, 0.001)])
+def test_quantizer_matches_oracle(fmt, shape, seed, outl):
+    w = laplace_weights(*shape, 0.02, seed, outlier_frac=outl)
+    got = qg.quantize(fmt, w)
+    want = oracle_canonical(fmt, w)
+    assert got.shape == want.shape
+    diff = np.nonzero(got != want)[0]
+    assert diff.size == 0, f"{diff.size} bytes differ, first at {diff[:5]}"
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_quantizer_edge_blocks_match_oracle(fmt):
+    k = 768
+    w = laplace_weights(6, k, 0.02, 17, outlier_frac=0.01)
+    w[0, :] = 0.0                                  # all-zero row
+    w[1, 256:512] = np.float32(0.0125)             # constant super-block
+    w[2, 0:32] = np.abs(w[2, 0:32])                # positive-only groups
+    w[3, 32:64] = -np.abs(w[3, 32:64])             # negative-only groups
+    w[4, 5] = np.float32(6e4)                      # large but representable
+    w[5, ::7] = np.float32(1e-30)                  # tiny values
+    assert np.array_equal(qg.quantize(fmt, w), oracle_canonical(fmt, w))
+
+
+def test_q4g32_ragged_k():
+    w = laplace_weights(3, 96, 0.02, 5)           # k % 64 == 32
+    assert np.array_equal(qg.quantize("q4g32", w), oracle_canonical("q4g32", w))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n,k", [(1, 256), (9, 1280), (4, 4352), (2, 11008)])
+def test_device_layout_round_trip_and_sizes(fmt, n, k):
+    w = laplace_weights(n, k, 0.02, n + k)
+    can = qg.quantize(fmt, w)
+    lay = qg.device_layout(fmt, n, k)
+    assert lay.algorithmic_bytes == can.size == qg.canonical_bytes(fmt, n, k)
+    assert lay.total_bytes - lay.algorithmic_bytes < 1024
+    for p in range(lay.nplanes):
+        assert lay.plane_offset[p] % 256 == 0
+    dev = qg.to_device_layout(fmt, can, n, k)
+    assert dev.size == lay.total_bytes
+    assert np.array_equal(qg.from_device_layout(fmt, dev, n, k), can)
+    # a pure bit permutation: the number of set bits is preserved
+    assert np.unpackbits(dev).sum() == np.unpackbits(can).sum()
+
+
+def test_device_layout_q4g32_ragged():
+    w = laplace_weights(5, 160, 0.02, 8)
+    can = qg.quantize("q4g32", w)
+    dev = qg.to_device_layout("q4g32", can, 5, 160)
+    assert np.array_equal(qg.from_device_layout("q4g32", dev, 5, 160), can)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_algorithmic_bytes_match_oracle(fmt):
+    n, k = 64, 4096
+    want = int4.algorithmic_bytes(n, k) if fmt == "q4g32" else sb.algorithmic_bytes(fmt, n, k)
+    assert qg.device_layout(fmt, n, k).algorithmic_bytes == want
+
+
+def test_error_codes():
+    w = np.zeros((2, 256), np.float32)
+    with pytest.raises(qg.QGError) as e:
+        qg.quantize("q3sb", np.zeros((2, 200), np.float32))
+    assert e.value.status == -2
+    bad = w.copy()
+    bad[1, 3] = np.nan
+    for fmt in FMTS:
+        with pytest.raises(qg.QGError) as e:
+            qg.quantize(fmt, bad)
+        assert e.value.status == -4
+    big = w.copy()
+    big[0, 0] = np.float32(1e10)
+    for fmt in ("q2sb", "q3sb", "q5sb", "q6sb"):
+        with pytest.raises(qg.QGError) as e:
+            qg.quantize(fmt, big)
+        assert e.value.status == -5
+    assert qg.lib.qg_quantize(9, None, 1, 256, 256, None) == -6
+    out = ctypes.c_int64()
+    assert qg.lib.qg_canonical_bytes(3, 1, 100, ctypes.byref(out)) == -2
+    assert qg.lib.qg_canonical_bytes(4, 1, 96, ctypes.byref(out)) == 0 and out.value == 48 + 12
+
+
+def test_device_entry_points_validate_without_launching():
+    """Argument errors are returned before any HIP call, so they are checkable without a GPU."""
+    L = qg.lib
+    assert L.qg_gemv(3, None, None, None, 0, 4, 100, None) == -2          # k % 256
+    assert L.qg_gemv(4, None, None, None, 0, 4, 48, None) == -2           # k % 32
+    assert L.qg_gemv(7, None, None, None, 0, 4, 256, None) == -6          # format
+    assert L.qg_gemv(3, None, None, None, 0, 0, 256, None) == 0           # n == 0: no-op
+    assert L.qg_gemv(3, None, None, None, 0, 4, 256, None) == -1          # null
+    assert L.qg_gemv(3, 256, 16, 3, 0, 4, 256, None) == -3                # y misaligned
+    assert L.qg_gemv(3, 257, 16, 2, 0, 4, 256, None) == -3                # w misaligned
+    assert L.qg_gemv(3, 256, 18, 2, 0, 4, 256, None) == -3                # x misaligned
+    assert L.qg_gemv(3, 256, 16, 2, 0, 4, 256 * 1025, None) == -2         # k too long
+    assert L.qg_dequantize(3, None, None, None, 4, 256, None) == -1
+    assert L.qg_dequantize(5, 256, None, 16, 4, 100, None) == -2
+    assert L.qg_gemv_batched(2, 256, 100, 16, 0, 2, 4, 0, 3, 4, 256, None) == -3   # w stride
