@@ -69,6 +69,36 @@ __device__ __forceinline__ float wave_sum_to_63(float v) {
   return v;
 }
 
+// Raw buffer loads: the plane base lives in a buffer resource (scalar registers), the row
+// offset in a scalar soffset and only the lane offset in a vector register, so stepping
+// from row to row costs scalar instructions only. Loads past num_records return zero.
+// Planes whose bytes are each read by exactly one load instruction (codes, and per-unit scale
+// words) use the non-temporal hint (nt): they stream through the caches without displacing
+// anything. Metadata that several lanes, instructions or consecutive rows share (fp16
+// super-scales, 6-bit field windows) uses the default policy so the shared lines stay cached.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr int kRsrcFlags = 0x00020000;     // dword 3 of a raw buffer descriptor on GFX9 parts
+constexpr int kNT = 2;                     // cache-policy operand: nt
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes, kRsrcFlags);
+}
+__device__ __forceinline__ u32x4 bld4(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNT));
+}
+__device__ __forceinline__ u32x2 bld2(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kNT));
+}
+__device__ __forceinline__ uint32_t bld1_nt(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kNT);
+}
+__device__ __forceinline__ uint32_t bld1(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+}
+__device__ __forceinline__ uint16_t bldh(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+}
+
 __device__ __forceinline__ u32x4 ld4(const uint8_t *p) { return *reinterpret_cast<const u32x4 *>(p); }
 __device__ __forceinline__ u32x2 ld2(const uint8_t *p) { return *reinterpret_cast<const u32x2 *>(p); }
 __device__ __forceinline__ uint32_t ld1(const uint8_t *p) { return *reinterpret_cast<const uint32_t *>(p); }

@@ -34,23 +34,39 @@ struct GemvArgs {
   int y_f32;
   int wk;                   // waves per workgroup along K
   int wr;                   // row groups per workgroup
+  int nb;                   // row batches per row group (each R rows)
 };
 
-// Per-lane view of the planes: plane starts and row strides are wave-uniform (scalar
-// registers), the lane's byte offset inside a row is a 32-bit vector register, so every
-// load is a global_load with a scalar base and a vector offset.
+// Per-lane view of the planes: one buffer resource per plane (wave-uniform), the plane's row
+// stride (uniform) and the lane's byte offset inside a row (per lane).
 struct Lane {
-  const uint8_t *base[4];
-  int64_t prb[4];
+  rsrc_t rs[4];
+  uint32_t prb[4];
   uint32_t off[4];
-  int q;                    // quarter of the super-block this unit covers
-  __device__ const uint8_t *at(int p, int64_t r) const { return base[p] + r * prb[p] + off[p]; }
+  uint32_t sh;              // bit offset of this unit's 6-bit fields in its 8-byte window
+  __device__ uint32_t row(int p, int64_t r) const { return (uint32_t)r * prb[p]; }
 };
+
+// 6-bit sub-scale fields (12 bytes per super-block; a unit owns 3 of them, bytes 3q..3q+2 for
+// quarter q) are read as an 8-byte window starting at byte 4*max(0, q-1) and shifted right by
+// (24q) mod 32 bits: 0, 24, 16, 8 for q = 0..3. The window of q = 3 reaches 4 bytes past the
+// super-block, which is in bounds (the next super-block, or the plane that follows, or
+// buffer range checking returns zero).
+__device__ __forceinline__ uint32_t fields_off(int64_t u) {
+  const uint32_t q = (uint32_t)(u & 3);
+  return (uint32_t)((u >> 2) * 12) + (q ? 4 * (q - 1) : 0);
+}
+__device__ __forceinline__ uint32_t fields_sh(int64_t u) { return (uint32_t)((24 * (u & 3)) & 31); }
+__device__ __forceinline__ uint32_t fields24(const Lane &L, int p, int64_t r) {
+  const uint32_t lo = bld1(L.rs[p], L.off[p], L.row(p, r));
+  const uint32_t hi = bld1(L.rs[p], L.off[p] + 4, L.row(p, r));
+  return __builtin_amdgcn_alignbit(hi, lo, L.sh);   // low 24 bits are the unit's fields
+}
 
 // ------------------------------------------------------------------ per-format units -----
 // Each format provides:
 //   struct Raw              packed data of one unit of one row (registers)
-//   offsets(a, u, off)      the lane's byte offset in a row of each plane
+//   offsets(u, off)         the lane's byte offset in a row of each plane
 //   load(Raw&, lane, r)     issue the loads for row r
 //   prep(xp, kc)            per-lane constants from the unit's 32 x pairs
 //   dot(Raw, xp, kc)        the unit's contribution to y[r]
@@ -63,13 +79,15 @@ template <> struct Unit<4> {
   struct Raw { u32x4 c0, c1; float s0, s1; };
   __device__ static void offsets(int64_t u, uint32_t *off) { off[0] = (uint32_t)(u * 32); off[1] = (uint32_t)(u * 8); }
   __device__ static void load(Raw &q, const Lane &L, int64_t r, bool half) {
-    const uint8_t *pc = L.at(0, r);
-    const uint8_t *ps = L.at(1, r);
-    q.c0 = ld4(pc);
-    q.s0 = __builtin_bit_cast(float, ld1(ps));
-    q.c1 = ld4(pc + (half ? 0 : 16));          // a half unit has one group: its second group's
-    q.s1 = __builtin_bit_cast(float, ld1(ps + (half ? 0 : 4)));   // activations are zero
-
+    const uint32_t r0 = L.row(0, r), r1 = L.row(1, r);
+    q.c0 = bld4(L.rs[0], L.off[0], r0);
+    // a half unit (k % 64 == 32) has one group; its second group's activations are zero
+    q.c1 = bld4(L.rs[0], L.off[0] + (half ? 0u : 16u), r0);
+    // Two 32-bit loads, not one 64-bit load: this toolchain narrows a multi-dword buffer load
+    // whose elements are bit-cast to float to its first dword and reuses that dword for the
+    // second element (vectors used in integer arithmetic, like the code words, are unaffected).
+    q.s0 = __builtin_bit_cast(float, bld1(L.rs[1], L.off[1], r1));
+    q.s1 = __builtin_bit_cast(float, bld1(L.rs[1], L.off[1] + (half ? 0u : 4u), r1));
   }
   __device__ static void prep(const uint32_t *xp, float *kc) {
     for (int g = 0; g < 2; ++g) {
@@ -80,11 +98,11 @@ template <> struct Unit<4> {
         x16 = dot2(xp[16 * g + 4 * i + 1], kOnes, x16);
         x16 = dot2(xp[16 * g + 4 * i + 3], kOnes, x16);
       }
-      kc[g] = 1032.0f * x1 + 72.0f * x16;    // sum (u - 8) x = A1 + A16/16 - kc
+      kc[g] = -(1032.0f * x1 + 72.0f * x16);   // sum (u - 8) x = A1 + A16/16 with A1 starting here
     }
   }
   __device__ static float group(u32x4 c, const uint32_t *xp, float k0) {
-    float a1 = -k0, a16 = 0.f;
+    float a1 = k0, a16 = 0.f;
     uint32_t d[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -111,9 +129,9 @@ template <> struct Unit<2> {
     off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 4); off[2] = (uint32_t)((u >> 2) * 4);
   }
   __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
-    q.c = ld4(L.at(0, r));
-    q.sc = ld1(L.at(1, r));
-    q.dd = ld1(L.at(2, r));
+    q.c = bld4(L.rs[0], L.off[0], L.row(0, r));
+    q.sc = bld1_nt(L.rs[1], L.off[1], L.row(1, r));
+    q.dd = bld1(L.rs[2], L.off[2], L.row(2, r));
   }
   __device__ static void prep(const uint32_t *xp, float *kc) {
     for (int j = 0; j < 4; ++j) {
@@ -149,28 +167,18 @@ template <> struct Unit<2> {
   }
 };
 
-// 24 bits of 6-bit fields for quarter q of a super-block (12 B per super-block): bytes
-// 3q..3q+2, read as two dwords from byte 4*(q >> 1) of the super-block.
-__device__ __forceinline__ uint32_t fields24_offset(int64_t u) { return (uint32_t)((u >> 2) * 12 + (((u & 3) >> 1) << 2)); }
-__device__ __forceinline__ uint32_t fields24(const uint8_t *p, int q) {
-  uint64_t v = (uint64_t)ld1(p) | ((uint64_t)ld1(p + 4) << 32);
-  const int sh = (q == 0) ? 0 : (q == 1) ? 24 : (q == 2) ? 16 : 40;
-  return (uint32_t)(v >> sh) & 0xFFFFFFu;
-}
-__device__ __forceinline__ uint32_t load_fields24(const uint8_t *sb12, int q) { return fields24(sb12 + ((q >> 1) << 2), q); }
-
 // ---- 3-bit super-block (quarter super-block = two chunks of 32 codes)
 template <> struct Unit<3> {
   static constexpr int NK = 4;
   struct Raw { u32x4 a; u32x2 b; uint32_t f; uint16_t d; };
   __device__ static void offsets(int64_t u, uint32_t *off) {
-    off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 8); off[2] = fields24_offset(u); off[3] = (uint32_t)((u >> 2) * 2);
+    off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 8); off[2] = fields_off(u); off[3] = (uint32_t)((u >> 2) * 2);
   }
   __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
-    q.a = ld4(L.at(0, r));
-    q.b = ld2(L.at(1, r));
-    q.f = fields24(L.at(2, r), L.q);
-    q.d = ldh(L.at(3, r));
+    q.a = bld4(L.rs[0], L.off[0], L.row(0, r));
+    q.b = bld2(L.rs[1], L.off[1], L.row(1, r));
+    q.f = fields24(L, 2, r);
+    q.d = bldh(L.rs[3], L.off[3], L.row(3, r));
   }
   __device__ static void prep(const uint32_t *xp, float *kc) {
     for (int c = 0; c < 2; ++c) {
@@ -203,8 +211,8 @@ template <> struct Unit<3> {
     b64 = dot2(pick(e0, QG_SMASK(0x01C001C0u)), x[12], b64);
     b64 = dot2(pick(e1, QG_SMASK(0x01C001C0u)), x[13], b64);
     b64 = dot2(pick(e2, QG_SMASK(0x01C001C0u)), x[14], b64);
-    uint32_t t = pick(e09, QG_SMASK(0x00400040u));          // bit 15 of e0 -> 6, bit 31 -> 22
-    t = pick_or(e1 >> 8, QG_SMASK(0x00800080u), t);          // bit 15 of e1 -> 7
+    uint32_t t = keep(pick(e09, QG_SMASK(0x00400040u)));    // bit 15 of e0 -> 6, bit 31 -> 22
+    t = keep(pick_or(e1 >> 8, QG_SMASK(0x00800080u), t));    // bit 15 of e1 -> 7
     t = pick_or(e2 >> 7, QG_SMASK(0x01000100u), t);          // bit 15 of e2 -> 8
     b64 = dot2(t, x[15], b64);
     sa = __builtin_fmaf(a8, 0.125f, a1);
@@ -244,15 +252,15 @@ template <> struct Unit<5> {
   static constexpr int NK = 4;
   struct Raw { u32x4 l0, l1; u32x2 h; uint32_t f, dd; };
   __device__ static void offsets(int64_t u, uint32_t *off) {
-    off[0] = (uint32_t)(u * 32); off[1] = (uint32_t)(u * 8); off[2] = fields24_offset(u); off[3] = (uint32_t)((u >> 2) * 4);
+    off[0] = (uint32_t)(u * 32); off[1] = (uint32_t)(u * 8); off[2] = fields_off(u); off[3] = (uint32_t)((u >> 2) * 4);
   }
   __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
-    const uint8_t *pl = L.at(0, r);
-    q.l0 = ld4(pl);
-    q.l1 = ld4(pl + 16);
-    q.h = ld2(L.at(1, r));
-    q.f = fields24(L.at(2, r), L.q);
-    q.dd = ld1(L.at(3, r));
+    const uint32_t r0 = L.row(0, r);
+    q.l0 = bld4(L.rs[0], L.off[0], r0);
+    q.l1 = bld4(L.rs[0], L.off[0] + 16, r0);
+    q.h = bld2(L.rs[1], L.off[1], L.row(1, r));
+    q.f = fields24(L, 2, r);
+    q.dd = bld1(L.rs[3], L.off[3], L.row(3, r));
   }
   __device__ static void prep(const uint32_t *xp, float *kc) {
     for (int h = 0; h < 2; ++h) {
@@ -294,12 +302,12 @@ template <> struct Unit<6> {
     off[0] = (uint32_t)(u * 32); off[1] = (uint32_t)(u * 16); off[2] = (uint32_t)(u * 4); off[3] = (uint32_t)((u >> 2) * 2);
   }
   __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
-    const uint8_t *pl = L.at(0, r);
-    q.l0 = ld4(pl);
-    q.l1 = ld4(pl + 16);
-    q.h = ld4(L.at(1, r));
-    q.sc = ld1(L.at(2, r));
-    q.d = ldh(L.at(3, r));
+    const uint32_t r0 = L.row(0, r);
+    q.l0 = bld4(L.rs[0], L.off[0], r0);
+    q.l1 = bld4(L.rs[0], L.off[0] + 16, r0);
+    q.h = bld4(L.rs[1], L.off[1], L.row(1, r));
+    q.sc = bld1_nt(L.rs[2], L.off[2], L.row(2, r));
+    q.d = bldh(L.rs[3], L.off[3], L.row(3, r));
   }
   __device__ static void prep(const uint32_t *xp, float *kc) {
     for (int j = 0; j < 4; ++j) {
@@ -334,7 +342,8 @@ template <> struct Unit<6> {
 template <int F, int R>
 __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a) {
   using U = Unit<F>;
-  extern __shared__ float red[];               // [wr][R][wk] partial sums when wk > 1
+  using Raw = typename U::Raw;
+  extern __shared__ float red[];               // [wr][R * nb][wk] partial sums when wk > 1
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int wk = wave % a.wk;
@@ -347,6 +356,27 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a) {
   const int64_t b = blockIdx.y;
   const uint8_t *w = a.w + b * a.w_bstride;
   const uint16_t *x = a.x + b * a.x_bstride;
+
+  Lane L;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    L.rs[p] = make_rsrc(w + a.poff[p], (uint32_t)(a.prb[p] * a.n));
+    L.prb[p] = (uint32_t)a.prb[p];
+    L.off[p] = 0;
+  }
+  U::offsets(u, L.off);
+  L.sh = fields_sh(u);
+
+  // this row group's rows: nb consecutive batches of R rows; rows past n re-read row n-1
+  const int rows_here = R * a.nb;
+  const int64_t row_begin = ((int64_t)blockIdx.x * a.wr + wr) * rows_here;
+  auto load_batch = [&](Raw *q, int64_t r0) {
+#pragma unroll
+    for (int i = 0; i < R; ++i) U::load(q[i], L, r0 + i < a.n ? r0 + i : a.n - 1, half);
+  };
+  static_assert(R == 1 || R == 2, "rows per batch");
+  Raw qa[R], qb[R];
+  load_batch(qa, row_begin);                   // weights first: their latency covers the x work
 
   uint32_t xp[32];
   {
@@ -365,54 +395,57 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a) {
   float kc[U::NK];
   U::prep(xp, kc);
 
-  Lane L;
+  auto store_y = [&](int64_t r, float v) {
+    if (a.y_f32) reinterpret_cast<float *>(a.y)[b * a.y_bstride + r] = v;
+    else reinterpret_cast<_Float16 *>(a.y)[b * a.y_bstride + r] = (_Float16)v;
+  };
+  auto finish_batch = [&](const Raw *q, int j) {
+    const int64_t r0 = row_begin + (int64_t)j * R;
+    float part[R];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    L.base[p] = w + a.poff[p];
-    L.prb[p] = a.prb[p];
-    L.off[p] = 0;
-  }
-  U::offsets(u, L.off);
-  L.q = (int)(u & 3);
-
-  const int64_t row0 = ((int64_t)blockIdx.x * a.wr + wr) * R;
-  typename U::Raw q[R];
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const int64_t r = row0 + i < a.n ? row0 + i : a.n - 1;   // rows past n re-read row n-1
-    U::load(q[i], L, r, half);
-  }
-  float part[R];
-#pragma unroll
-  for (int i = 0; i < R; ++i) {
-    const float v = U::dot(q[i], xp, kc);
-    part[i] = wave_sum_to_63(act ? v : 0.f);
-  }
-  if (a.wk == 1) {
+    for (int i = 0; i < R; ++i) {
+      const float v = U::dot(q[i], xp, kc);
+      part[i] = wave_sum_to_63(act ? v : 0.f);
+    }
     if (lane == 63) {
 #pragma unroll
       for (int i = 0; i < R; ++i) {
-        const int64_t r = row0 + i;
-        if (r < a.n) {
-          if (a.y_f32) reinterpret_cast<float *>(a.y)[b * a.y_bstride + r] = part[i];
-          else reinterpret_cast<_Float16 *>(a.y)[b * a.y_bstride + r] = (_Float16)part[i];
+        if (a.wk == 1) {
+          if (r0 + i < a.n) store_y(r0 + i, part[i]);
+        } else {
+          red[(wr * rows_here + j * R + i) * a.wk + wk] = part[i];
         }
       }
     }
-    return;
+  };
+
+  // Software pipeline: the next batch's loads are in flight while this one is computed.
+  // Loads inside the steady-state loop are unconditional, so the wait before each compute
+  // covers only the older batch (a conditional prefetch would force a wait for everything).
+  int j = 0;
+  for (; j + 2 < a.nb; j += 2) {
+    load_batch(qb, row_begin + (int64_t)(j + 1) * R);
+    finish_batch(qa, j);
+    load_batch(qa, row_begin + (int64_t)(j + 2) * R);
+    finish_batch(qb, j + 1);
   }
-  if (lane == 63) {
-#pragma unroll
-    for (int i = 0; i < R; ++i) red[(wr * R + i) * a.wk + wk] = part[i];
+  if (j + 1 < a.nb) {
+    load_batch(qb, row_begin + (int64_t)(j + 1) * R);
+    finish_batch(qa, j);
+    finish_batch(qb, j + 1);
+  } else {
+    finish_batch(qa, j);
   }
+  if (a.wk == 1) return;
+  // K split over wk waves: one barrier, then the first wave of the row group adds the
+  // partial sums of all its rows and writes them (one row per lane)
   __syncthreads();
-  if (wk == 0 && lane < R) {
-    const int64_t r = row0 + lane;
-    float s = 0.f;
-    for (int j = 0; j < a.wk; ++j) s += red[(wr * R + lane) * a.wk + j];
-    if (r < a.n) {
-      if (a.y_f32) reinterpret_cast<float *>(a.y)[b * a.y_bstride + r] = s;
-      else reinterpret_cast<_Float16 *>(a.y)[b * a.y_bstride + r] = (_Float16)s;
+  if (wk == 0) {
+    for (int i = lane; i < rows_here; i += 64) {
+      const int64_t r = row_begin + i;
+      float sum = 0.f;
+      for (int j = 0; j < a.wk; ++j) sum += red[(wr * rows_here + i) * a.wk + j];
+      if (r < a.n) store_y(r, sum);
     }
   }
 }
@@ -437,6 +470,14 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4 *p, int64_t
 }
 
 // ------------------------------------------------------------------ device decode --------
+
+// 24 bits of 6-bit fields for quarter q of a super-block whose 12 field bytes start at sb12.
+__device__ __forceinline__ uint32_t load_fields24(const uint8_t *sb12, int q) {
+  const uint8_t *p = sb12 + ((q >> 1) << 2);
+  uint64_t v = (uint64_t)ld1(p) | ((uint64_t)ld1(p + 4) << 32);
+  const int sh = (q == 0) ? 0 : (q == 1) ? 24 : (q == 2) ? 16 : 40;
+  return (uint32_t)(v >> sh) & 0xFFFFFFu;
+}
 // One thread per (row, unit): decodes 64 codes from the device layout by the same bit
 // placement the GEMV kernels use and writes logical-order codes and fp32 W_hat.
 
@@ -604,20 +645,36 @@ int fill_args(int fmt, const void *w, int64_t n, int64_t k, GemvArgs &a) {
   return QG_OK;
 }
 
-constexpr int kRows = 4;
 constexpr int kMaxWk = 16;
+constexpr int64_t kSimds = 1024;           // 256 CUs x 4 SIMDs
+constexpr int64_t kWavesPerSimd = 4;       // resident waves the kernels' register use allows
+constexpr int kMaxBatches = 32;
 
+template <int F, int R>
+int launch_gemv_r(GemvArgs a, int64_t count, hipStream_t s) {
+  const int64_t groups_per_matrix = (a.n + R - 1) / R;          // batches of R rows
+  const int64_t target = kSimds * kWavesPerSimd / a.wk;         // row groups resident at once
+  int64_t nb = (groups_per_matrix * count) / target;
+  nb = nb < 1 ? 1 : (nb > kMaxBatches ? kMaxBatches : nb);
+  a.nb = (int)nb;
+  const int64_t rows_per_block = (int64_t)a.wr * R * nb;
+  dim3 grid((unsigned)((a.n + rows_per_block - 1) / rows_per_block), (unsigned)count);
+  dim3 block((unsigned)(64 * a.wk * a.wr));
+  size_t shm = a.wk > 1 ? (size_t)a.wr * R * nb * a.wk * sizeof(float) : 0;
+  return launch(gemv_kernel<F, R>, grid, block, shm, s, a);
+}
+
+// Rows per batch: 2 (double-buffered, so four rows of loads per wave in flight at 4 waves per
+// SIMD without spilling) when there are enough rows to keep every SIMD busy, else 1: small
+// problems are bound by latency, so they get as many waves as possible.
 template <int F>
 int launch_gemv_t(GemvArgs a, int64_t count, hipStream_t s) {
   const int wk = (int)((a.units + 63) / 64);
-  const int wr = wk >= 4 ? 1 : 4 / wk;
   a.wk = wk;
-  a.wr = wr;
-  const int64_t rows_per_block = (int64_t)wr * kRows;
-  dim3 grid((unsigned)((a.n + rows_per_block - 1) / rows_per_block), (unsigned)count);
-  dim3 block((unsigned)(64 * wk * wr));
-  size_t shm = wk > 1 ? (size_t)wr * kRows * wk * sizeof(float) : 0;
-  return launch(gemv_kernel<F, kRows>, grid, block, shm, s, a);
+  a.wr = wk >= 4 ? 1 : 4 / wk;
+  const int64_t rows = a.n * count, target = kSimds * kWavesPerSimd / wk;
+  if (rows >= 2 * target) return launch_gemv_r<F, 2>(a, count, s);
+  return launch_gemv_r<F, 1>(a, count, s);
 }
 
 int launch_gemv(int fmt, GemvArgs a, int64_t count, hipStream_t s) {
