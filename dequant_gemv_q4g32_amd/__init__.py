@@ -65,12 +65,14 @@ def _load() -> ctypes.CDLL:
         "qg_from_device_layout": ([i32, vp, i64, i64, vp], i32),
         "qg_gemv": ([i32, vp, vp, vp, i32, i64, i64, vp], i32),
         "qg_gemv_batched": ([i32, vp, i64, vp, i64, vp, i64, i32, i64, i64, i64, vp], i32),
+        "qg_gemm": ([i32, vp, vp, i64, vp, i64, i32, i64, i64, i64, vp], i32),
         "qg_dequantize": ([i32, vp, vp, vp, i64, i64, vp], i32),
         "qg_read_probe": ([vp, i64, vp, vp], i32),
     }
     for f in FORMATS:
         sig[f"quantize_{f}"] = ([vp, i64, i64, i64, vp], i32)
         sig[f"dequant_gemv_{f}"] = ([vp, vp, vp, i64, i64, vp], i32)
+        sig[f"dequant_gemm_{f}"] = ([vp, vp, i64, vp, i64, i64, i64, i64, vp], i32)
         sig[f"dequantize_{f}"] = ([vp, vp, vp, i64, i64, vp], i32)
     for name, (args, res) in sig.items():
         fn = getattr(lib, name)
@@ -210,6 +212,18 @@ def gemv_batched(fmt, w, w_stride: int, x, y, count: int, n: int, k: int, stream
                                 y.stride(0), int(y.dtype == torch.float32), count, n, k, _stream(stream)),
            "qg_gemv_batched")
     return y
+
+
+def gemm(fmt, w, X, n: int, k: int, out=None, out_f32: bool = False, stream=None):
+    """Y = X W_hat^T. w: uint8 device buffer (device layout), X: fp16 [m, k] (row stride
+    X.stride(0)) -> Y fp16/fp32 [m, n]."""
+    torch = _torch()
+    m = X.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32 if out_f32 else torch.float16, device=X.device)
+    _check(_lib.qg_gemm(_fmt(fmt), w.data_ptr(), X.data_ptr(), X.stride(0), out.data_ptr(), out.stride(0),
+                        int(out.dtype == torch.float32), m, n, k, _stream(stream)), "qg_gemm")
+    return out
 
 
 def dequantize(fmt, w, n: int, k: int, values: bool = True, codes: bool = True, stream=None):

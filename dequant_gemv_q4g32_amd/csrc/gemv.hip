@@ -18,6 +18,7 @@
 #include "../../include/qgemv.h"
 #include "device_common.h"
 #include "layout.h"
+#include "units.h"
 
 namespace qg {
 
@@ -31,327 +32,35 @@ struct GemvArgs {
   int64_t n, k, units;
   int64_t poff[4];
   int64_t prb[4];
+  int64_t m;                // activation rows (1 for the GEMV)
+  int64_t ldx, ldy;         // elements between activation rows / output rows
   int y_f32;
   int wk;                   // waves per workgroup along K
   int wr;                   // row groups per workgroup
+  int kpasses;              // passes over K (wk > 1 whenever kpasses > 1)
   int nb;                   // row batches per row group (each R rows)
 };
 
-// Per-lane view of the planes: one buffer resource per plane (wave-uniform), the plane's row
-// stride (uniform) and the lane's byte offset inside a row (per lane).
-struct Lane {
-  rsrc_t rs[4];
-  uint32_t prb[4];
-  uint32_t off[4];
-  uint32_t sh;              // bit offset of this unit's 6-bit fields in its 8-byte window
-  __device__ uint32_t row(int p, int64_t r) const { return (uint32_t)r * prb[p]; }
-};
+// ------------------------------------------------------------------ GEMV / small-M kernel -
+//
+// Template parameters: F format, M activation rows that share every decoded code (1 for the
+// GEMV), S lanes per 64-weight unit (1, or 2 to halve the activation registers when M is
+// large), R rows per pipelined batch, MP more than one pass over K.
 
-// 6-bit sub-scale fields (12 bytes per super-block; a unit owns 3 of them, bytes 3q..3q+2 for
-// quarter q) are read as an 8-byte window starting at byte 4*max(0, q-1) and shifted right by
-// (24q) mod 32 bits: 0, 24, 16, 8 for q = 0..3. The window of q = 3 reaches 4 bytes past the
-// super-block, which is in bounds (the next super-block, or the plane that follows, or
-// buffer range checking returns zero).
-__device__ __forceinline__ uint32_t fields_off(int64_t u) {
-  const uint32_t q = (uint32_t)(u & 3);
-  return (uint32_t)((u >> 2) * 12) + (q ? 4 * (q - 1) : 0);
-}
-__device__ __forceinline__ uint32_t fields_sh(int64_t u) { return (uint32_t)((24 * (u & 3)) & 31); }
-__device__ __forceinline__ uint32_t fields24(const Lane &L, int p, int64_t r) {
-  const uint32_t lo = bld1(L.rs[p], L.off[p], L.row(p, r));
-  const uint32_t hi = bld1(L.rs[p], L.off[p] + 4, L.row(p, r));
-  return __builtin_amdgcn_alignbit(hi, lo, L.sh);   // low 24 bits are the unit's fields
-}
-
-// ------------------------------------------------------------------ per-format units -----
-// Each format provides:
-//   struct Raw              packed data of one unit of one row (registers)
-//   offsets(u, off)         the lane's byte offset in a row of each plane
-//   load(Raw&, lane, r)     issue the loads for row r
-//   prep(xp, kc)            per-lane constants from the unit's 32 x pairs
-//   dot(Raw, xp, kc)        the unit's contribution to y[r]
-
-template <int F> struct Unit;
-
-// ---- INT4 group-32 (two groups per unit)
-template <> struct Unit<4> {
-  static constexpr int NK = 2;
-  struct Raw { u32x4 c0, c1; float s0, s1; };
-  __device__ static void offsets(int64_t u, uint32_t *off) { off[0] = (uint32_t)(u * 32); off[1] = (uint32_t)(u * 8); }
-  __device__ static void load(Raw &q, const Lane &L, int64_t r, bool half) {
-    const uint32_t r0 = L.row(0, r), r1 = L.row(1, r);
-    q.c0 = bld4(L.rs[0], L.off[0], r0);
-    // a half unit (k % 64 == 32) has one group; its second group's activations are zero
-    q.c1 = bld4(L.rs[0], L.off[0] + (half ? 0u : 16u), r0);
-    // Two 32-bit loads, not one 64-bit load: this toolchain narrows a multi-dword buffer load
-    // whose elements are bit-cast to float to its first dword and reuses that dword for the
-    // second element (vectors used in integer arithmetic, like the code words, are unaffected).
-    q.s0 = __builtin_bit_cast(float, bld1(L.rs[1], L.off[1], r1));
-    q.s1 = __builtin_bit_cast(float, bld1(L.rs[1], L.off[1] + (half ? 0u : 4u), r1));
-  }
-  __device__ static void prep(const uint32_t *xp, float *kc) {
-    for (int g = 0; g < 2; ++g) {
-      float x1 = 0.f, x16 = 0.f;
-      for (int i = 0; i < 4; ++i) {
-        x1 = dot2(xp[16 * g + 4 * i + 0], kOnes, x1);
-        x1 = dot2(xp[16 * g + 4 * i + 2], kOnes, x1);
-        x16 = dot2(xp[16 * g + 4 * i + 1], kOnes, x16);
-        x16 = dot2(xp[16 * g + 4 * i + 3], kOnes, x16);
-      }
-      kc[g] = -(1032.0f * x1 + 72.0f * x16);   // sum (u - 8) x = A1 + A16/16 with A1 starting here
-    }
-  }
-  __device__ static float group(u32x4 c, const uint32_t *xp, float k0) {
-    float a1 = k0, a16 = 0.f;
-    uint32_t d[4] = {c.x, c.y, c.z, c.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t v = d[i], v8 = v >> 8;
-      a1 = dot2(pick(v, QG_SMASK(0x000F000Fu)), xp[4 * i + 0], a1);
-      a16 = dot2(pick(v, QG_SMASK(0x00F000F0u)), xp[4 * i + 1], a16);
-      a1 = dot2(pick(v8, QG_SMASK(0x000F000Fu)), xp[4 * i + 2], a1);
-      a16 = dot2(pick(v8, QG_SMASK(0x00F000F0u)), xp[4 * i + 3], a16);
-    }
-    return __builtin_fmaf(a16, 0.0625f, a1);
-  }
-  __device__ static float dot(const Raw &q, const uint32_t *xp, const float *kc) {
-    float s0 = group(q.c0, xp, kc[0]);
-    float s1 = group(q.c1, xp + 16, kc[1]);
-    return __builtin_fmaf(q.s1, s1, q.s0 * s0);
-  }
-};
-
-// ---- 2-bit super-block (a unit is a quarter super-block: 4 sub-blocks of 16)
-template <> struct Unit<2> {
-  static constexpr int NK = 8;
-  struct Raw { u32x4 c; uint32_t sc, dd; };
-  __device__ static void offsets(int64_t u, uint32_t *off) {
-    off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 4); off[2] = (uint32_t)((u >> 2) * 4);
-  }
-  __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
-    q.c = bld4(L.rs[0], L.off[0], L.row(0, r));
-    q.sc = bld1_nt(L.rs[1], L.off[1], L.row(1, r));
-    q.dd = bld1(L.rs[2], L.off[2], L.row(2, r));
-  }
-  __device__ static void prep(const uint32_t *xp, float *kc) {
-    for (int j = 0; j < 4; ++j) {
-      float s = 0.f;
-      for (int r = 0; r < 8; ++r) s = dot2(xp[8 * j + r], kOnes, s);
-      kc[j] = s;                       // X_j
-      kc[4 + j] = -1024.0f * s;        // accumulator start
-    }
-  }
-  __device__ static float dot(const Raw &q, const uint32_t *xp, const float *kc) {
-    float A[4] = {kc[4], kc[5], kc[6], kc[7]};
-    uint32_t d[4] = {q.c.x, q.c.y, q.c.z, q.c.w};
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t v = d[i], v8 = v >> 8;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        A[j] = dot2(pick(v, QG_SMASK(0x00030003u << (2 * j))), xp[8 * j + 2 * i], A[j]);
-        A[j] = dot2(pick(v8, QG_SMASK(0x00030003u << (2 * j))), xp[8 * j + 2 * i + 1], A[j]);
-      }
-    }
-    const uint32_t s = q.sc;
-    float sa = 0.f, sm = 0.f;
-    const float inv4[4] = {1.0f, 0.25f, 0.0625f, 0.015625f};
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float scj = (float)((s >> (8 * j)) & 15u);
-      float mj = (float)((s >> (8 * j + 4)) & 15u);
-      sa = __builtin_fmaf(scj * inv4[j], A[j], sa);
-      sm = __builtin_fmaf(mj, kc[j], sm);
-    }
-    return __builtin_fmaf(half_lo(q.dd), sa, -half_hi(q.dd) * sm);
-  }
-};
-
-// ---- 3-bit super-block (quarter super-block = two chunks of 32 codes)
-template <> struct Unit<3> {
-  static constexpr int NK = 4;
-  struct Raw { u32x4 a; u32x2 b; uint32_t f; uint16_t d; };
-  __device__ static void offsets(int64_t u, uint32_t *off) {
-    off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 8); off[2] = fields_off(u); off[3] = (uint32_t)((u >> 2) * 2);
-  }
-  __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
-    q.a = bld4(L.rs[0], L.off[0], L.row(0, r));
-    q.b = bld2(L.rs[1], L.off[1], L.row(1, r));
-    q.f = fields24(L, 2, r);
-    q.d = bldh(L.rs[3], L.off[3], L.row(3, r));
-  }
-  __device__ static void prep(const uint32_t *xp, float *kc) {
-    for (int c = 0; c < 2; ++c) {
-      const uint32_t *x = xp + 16 * c;
-      float a1 = 0.f, a8 = 0.f, b8 = 0.f, b64 = 0.f;
-      for (int r = 0; r < 6; ++r) a1 = dot2(x[r], kOnes, a1);
-      for (int r = 6; r < 8; ++r) a8 = dot2(x[r], kOnes, a8);
-      for (int r = 8; r < 12; ++r) b8 = dot2(x[r], kOnes, b8);
-      for (int r = 12; r < 16; ++r) b64 = dot2(x[r], kOnes, b64);
-      kc[2 * c] = -(1028.0f * a1 + 132.0f * a8);            // start of a's class-1 sum
-      kc[2 * c + 1] = -8.0f * (132.0f * b8 + 20.0f * b64);  // start of b's class-8 sum
-    }
-  }
-  __device__ static void chunk(uint32_t e0, uint32_t e1, uint32_t e2, const uint32_t *x, float ka, float kb,
-                               float &sa, float &sb) {
-    const uint32_t e09 = e0 >> 9, e19 = e1 >> 9, e29 = e2 >> 9;
-    float a1 = ka, a8 = 0.f, b8 = kb, b64 = 0.f;
-    a1 = dot2(pick(e0, QG_SMASK(0x00070007u)), x[0], a1);
-    a1 = dot2(pick(e09, QG_SMASK(0x00070007u)), x[1], a1);
-    a1 = dot2(pick(e1, QG_SMASK(0x00070007u)), x[2], a1);
-    a1 = dot2(pick(e19, QG_SMASK(0x00070007u)), x[3], a1);
-    a1 = dot2(pick(e2, QG_SMASK(0x00070007u)), x[4], a1);
-    a1 = dot2(pick(e29, QG_SMASK(0x00070007u)), x[5], a1);
-    a8 = dot2(pick(e0, QG_SMASK(0x00380038u)), x[6], a8);
-    a8 = dot2(pick(e09, QG_SMASK(0x00380038u)), x[7], a8);
-    b8 = dot2(pick(e1, QG_SMASK(0x00380038u)), x[8], b8);
-    b8 = dot2(pick(e19, QG_SMASK(0x00380038u)), x[9], b8);
-    b8 = dot2(pick(e2, QG_SMASK(0x00380038u)), x[10], b8);
-    b8 = dot2(pick(e29, QG_SMASK(0x00380038u)), x[11], b8);
-    b64 = dot2(pick(e0, QG_SMASK(0x01C001C0u)), x[12], b64);
-    b64 = dot2(pick(e1, QG_SMASK(0x01C001C0u)), x[13], b64);
-    b64 = dot2(pick(e2, QG_SMASK(0x01C001C0u)), x[14], b64);
-    uint32_t t = keep(pick(e09, QG_SMASK(0x00400040u)));    // bit 15 of e0 -> 6, bit 31 -> 22
-    t = keep(pick_or(e1 >> 8, QG_SMASK(0x00800080u), t));    // bit 15 of e1 -> 7
-    t = pick_or(e2 >> 7, QG_SMASK(0x01000100u), t);          // bit 15 of e2 -> 8
-    b64 = dot2(t, x[15], b64);
-    sa = __builtin_fmaf(a8, 0.125f, a1);
-    sb = __builtin_fmaf(b64, 0.125f, b8);
-  }
-  __device__ static float dot(const Raw &q, const uint32_t *xp, const float *kc) {
-    float sa0, sb0, sa1, sb1;
-    chunk(q.a.x, q.a.y, q.a.z, xp, kc[0], kc[1], sa0, sb0);
-    chunk(q.a.w, q.b.x, q.b.y, xp + 16, kc[2], kc[3], sa1, sb1);
-    const uint32_t f = q.f;
-    float s0 = (float)(f & 63u), s1 = (float)((f >> 6) & 63u) * 0.125f;
-    float s2 = (float)((f >> 12) & 63u), s3 = (float)((f >> 18) & 63u) * 0.125f;
-    float acc = s0 * sa0;
-    acc = __builtin_fmaf(s1, sb0, acc);
-    acc = __builtin_fmaf(s2, sa1, acc);
-    acc = __builtin_fmaf(s3, sb1, acc);
-    return half_bits(q.d) * acc;
-  }
-};
-
-// ---- nibble plane + high-bit plane (q5sb: 1 high bit, 32-weight sub-blocks;
-//      q6sb: 2 high bits, 16-weight sub-blocks)
-template <int HB>
-__device__ __forceinline__ void nib_dword(uint32_t L, uint32_t H, int ip, const uint32_t *x, float &a1, float &a16) {
-  constexpr uint32_t m1 = HB == 1 ? 0x00100010u : 0x00300030u;
-  constexpr uint32_t m16 = HB == 1 ? 0x01000100u : 0x03000300u;
-  const int ra = HB * ip, rb = 8 + HB * ip;
-  const uint32_t ha = ra ? rotr(H, ra) : H, hb = rotr(H, rb);
-  const uint32_t L8 = L >> 8;
-  a1 = dot2(pick_or(L, QG_SMASK(0x000F000Fu), keep(pick(ha, QG_SMASK(m1)))), x[0], a1);
-  a16 = dot2(pick_or(L, QG_SMASK(0x00F000F0u), keep(pick(ha, QG_SMASK(m16)))), x[1], a16);
-  a1 = dot2(pick_or(L8, QG_SMASK(0x000F000Fu), keep(pick(hb, QG_SMASK(m1)))), x[2], a1);
-  a16 = dot2(pick_or(L8, QG_SMASK(0x00F000F0u), keep(pick(hb, QG_SMASK(m16)))), x[3], a16);
-}
-
-template <> struct Unit<5> {
-  static constexpr int NK = 4;
-  struct Raw { u32x4 l0, l1; u32x2 h; uint32_t f, dd; };
-  __device__ static void offsets(int64_t u, uint32_t *off) {
-    off[0] = (uint32_t)(u * 32); off[1] = (uint32_t)(u * 8); off[2] = fields_off(u); off[3] = (uint32_t)((u >> 2) * 4);
-  }
-  __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
-    const uint32_t r0 = L.row(0, r);
-    q.l0 = bld4(L.rs[0], L.off[0], r0);
-    q.l1 = bld4(L.rs[0], L.off[0] + 16, r0);
-    q.h = bld2(L.rs[1], L.off[1], L.row(1, r));
-    q.f = fields24(L, 2, r);
-    q.dd = bld1(L.rs[3], L.off[3], L.row(3, r));
-  }
-  __device__ static void prep(const uint32_t *xp, float *kc) {
-    for (int h = 0; h < 2; ++h) {
-      float x1 = 0.f, x16 = 0.f;
-      for (int i = 0; i < 4; ++i) {
-        x1 = dot2(xp[16 * h + 4 * i + 0], kOnes, x1);
-        x1 = dot2(xp[16 * h + 4 * i + 2], kOnes, x1);
-        x16 = dot2(xp[16 * h + 4 * i + 1], kOnes, x16);
-        x16 = dot2(xp[16 * h + 4 * i + 3], kOnes, x16);
-      }
-      kc[h] = -(1024.0f * x1 + 64.0f * x16);
-      kc[2 + h] = x1 + x16;
-    }
-  }
-  __device__ static float dot(const Raw &q, const uint32_t *xp, const float *kc) {
-    const uint32_t L[8] = {q.l0.x, q.l0.y, q.l0.z, q.l0.w, q.l1.x, q.l1.y, q.l1.z, q.l1.w};
-    const uint32_t H[2] = {q.h.x, q.h.y};
-    float S[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float a1 = kc[h], a16 = 0.f;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) nib_dword<1>(L[4 * h + i], H[h], i, xp + 16 * h + 4 * i, a1, a16);
-      S[h] = __builtin_fmaf(a16, 0.0625f, a1);
-    }
-    const uint32_t f = q.f;
-    float sc0 = (float)(f & 63u), sc1 = (float)((f >> 6) & 63u);
-    float m0 = (float)((f >> 12) & 63u), m1 = (float)((f >> 18) & 63u);
-    float sa = __builtin_fmaf(sc1, S[1], sc0 * S[0]);
-    float sm = __builtin_fmaf(m1, kc[3], m0 * kc[2]);
-    return __builtin_fmaf(half_lo(q.dd), sa, -half_hi(q.dd) * sm);
-  }
-};
-
-template <> struct Unit<6> {
-  static constexpr int NK = 4;
-  struct Raw { u32x4 l0, l1, h; uint32_t sc; uint16_t d; };
-  __device__ static void offsets(int64_t u, uint32_t *off) {
-    off[0] = (uint32_t)(u * 32); off[1] = (uint32_t)(u * 16); off[2] = (uint32_t)(u * 4); off[3] = (uint32_t)((u >> 2) * 2);
-  }
-  __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
-    const uint32_t r0 = L.row(0, r);
-    q.l0 = bld4(L.rs[0], L.off[0], r0);
-    q.l1 = bld4(L.rs[0], L.off[0] + 16, r0);
-    q.h = bld4(L.rs[1], L.off[1], L.row(1, r));
-    q.sc = bld1_nt(L.rs[2], L.off[2], L.row(2, r));
-    q.d = bldh(L.rs[3], L.off[3], L.row(3, r));
-  }
-  __device__ static void prep(const uint32_t *xp, float *kc) {
-    for (int j = 0; j < 4; ++j) {
-      float x1 = 0.f, x16 = 0.f;
-      for (int i = 0; i < 2; ++i) {
-        x1 = dot2(xp[8 * j + 4 * i + 0], kOnes, x1);
-        x1 = dot2(xp[8 * j + 4 * i + 2], kOnes, x1);
-        x16 = dot2(xp[8 * j + 4 * i + 1], kOnes, x16);
-        x16 = dot2(xp[8 * j + 4 * i + 3], kOnes, x16);
-      }
-      kc[j] = -(1056.0f * x1 + 96.0f * x16);   // 1024 + 32 offset, 64 + 32 offset
-    }
-  }
-  __device__ static float dot(const Raw &q, const uint32_t *xp, const float *kc) {
-    const uint32_t L[8] = {q.l0.x, q.l0.y, q.l0.z, q.l0.w, q.l1.x, q.l1.y, q.l1.z, q.l1.w};
-    const uint32_t H[4] = {q.h.x, q.h.y, q.h.z, q.h.w};
-    float acc = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      float a1 = kc[j], a16 = 0.f;
-      nib_dword<2>(L[2 * j], H[j], 0, xp + 8 * j, a1, a16);
-      nib_dword<2>(L[2 * j + 1], H[j], 1, xp + 8 * j + 4, a1, a16);
-      float sj = (float)(int8_t)((q.sc >> (8 * j)) & 0xFFu);
-      acc = __builtin_fmaf(sj, __builtin_fmaf(a16, 0.0625f, a1), acc);
-    }
-    return half_bits(q.d) * acc;
-  }
-};
-
-// ------------------------------------------------------------------ GEMV kernel ----------
-
-template <int F, int R>
-__global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a) {
+template <int F, int M, int S, int R, bool MP>
+__global__ __launch_bounds__(M > 4 ? 512 : 1024) void mv_kernel(GemvArgs a) {
   using U = Unit<F>;
   using Raw = typename U::Raw;
-  extern __shared__ float red[];               // [wr][R * nb][wk] partial sums when wk > 1
+  static_assert(R == 1 || R == 2, "rows per batch");
+  constexpr int UPW = 64 / S;                  // units per wave
+  constexpr int NP = 32 / S;                   // activation pairs per lane and row
+  constexpr int NK = U::NKS(S);
+  extern __shared__ float red[];               // [wr][R * nb][M][wk] partial sums when wk > 1
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);   // wave-uniform
   const int wk = wave % a.wk;
   const int wr = wave / a.wk;
-  const int64_t u_raw = (int64_t)wk * 64 + lane;
-  const bool act = u_raw < a.units;
-  const int64_t u = act ? u_raw : 0;           // inactive lanes read unit 0 and contribute 0
-  const bool half = (F == 4) && act && (u == a.units - 1) && (a.k % 64 != 0);
+  const int h = S == 1 ? 0 : (lane & 1);
 
   const int64_t b = blockIdx.y;
   const uint8_t *w = a.w + b * a.w_bstride;
@@ -362,90 +71,119 @@ __global__ __launch_bounds__(1024) void gemv_kernel(GemvArgs a) {
   for (int p = 0; p < 4; ++p) {
     L.rs[p] = make_rsrc(w + a.poff[p], (uint32_t)(a.prb[p] * a.n));
     L.prb[p] = (uint32_t)a.prb[p];
-    L.off[p] = 0;
   }
-  U::offsets(u, L.off);
-  L.sh = fields_sh(u);
 
   // this row group's rows: nb consecutive batches of R rows; rows past n re-read row n-1
   const int rows_here = R * a.nb;
   const int64_t row_begin = ((int64_t)blockIdx.x * a.wr + wr) * rows_here;
-  auto load_batch = [&](Raw *q, int64_t r0) {
-#pragma unroll
-    for (int i = 0; i < R; ++i) U::load(q[i], L, r0 + i < a.n ? r0 + i : a.n - 1, half);
+  auto store_y = [&](int mm, int64_t r, float v) {
+    const int64_t i = b * a.y_bstride + (int64_t)mm * a.ldy + r;
+    if (a.y_f32) reinterpret_cast<float *>(a.y)[i] = v;
+    else reinterpret_cast<_Float16 *>(a.y)[i] = (_Float16)v;
   };
-  static_assert(R == 1 || R == 2, "rows per batch");
-  Raw qa[R], qb[R];
-  load_batch(qa, row_begin);                   // weights first: their latency covers the x work
 
-  uint32_t xp[32];
-  {
-    const uint8_t *px = reinterpret_cast<const uint8_t *>(x) + (uint32_t)(u * 128);
+  // K passes: the wk waves of a row group cover wk * UPW units per pass. With more than one
+  // pass (long K with many activation rows) each wave accumulates its partial sums in LDS.
+  const int passes = MP ? a.kpasses : 1;
+  for (int kp = 0; kp < passes; ++kp) {
+    const int64_t u_raw = ((int64_t)kp * a.wk + wk) * UPW + (S == 1 ? lane : lane >> 1);
+    const bool act = u_raw < a.units;
+    const int64_t u = act ? u_raw : 0;         // inactive lanes read unit 0 and contribute 0
+    const bool half = (F == 4) && act && (u == a.units - 1) && (a.k % 64 != 0);
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      // a half unit (k % 64 == 32) has only 32 activations: re-read the first half, zero it
-      u32x4 v = ld4(px + 16 * ((F == 4 && half) ? (i & 3) : i));
-      const bool keepx = !(F == 4 && half && i >= 4);
-      xp[4 * i + 0] = keepx ? v.x : 0u;
-      xp[4 * i + 1] = keepx ? v.y : 0u;
-      xp[4 * i + 2] = keepx ? v.z : 0u;
-      xp[4 * i + 3] = keepx ? v.w : 0u;
-    }
-  }
-  float kc[U::NK];
-  U::prep(xp, kc);
+    for (int p = 0; p < 4; ++p) L.off[p] = 0;
+    U::offsets(u, L.off);
+    L.sh = fields_sh(u);
 
-  auto store_y = [&](int64_t r, float v) {
-    if (a.y_f32) reinterpret_cast<float *>(a.y)[b * a.y_bstride + r] = v;
-    else reinterpret_cast<_Float16 *>(a.y)[b * a.y_bstride + r] = (_Float16)v;
-  };
-  auto finish_batch = [&](const Raw *q, int j) {
-    const int64_t r0 = row_begin + (int64_t)j * R;
-    float part[R];
+    auto load_batch = [&](Raw *q, int64_t r0) {
 #pragma unroll
-    for (int i = 0; i < R; ++i) {
-      const float v = U::dot(q[i], xp, kc);
-      part[i] = wave_sum_to_63(act ? v : 0.f);
-    }
-    if (lane == 63) {
+      for (int i = 0; i < R; ++i) U::load(q[i], L, r0 + i < a.n ? r0 + i : a.n - 1, half);
+    };
+    Raw qa[R], qb[R];
+    load_batch(qa, row_begin);                 // weights first: their latency covers the x work
+
+    // The lane's activation pairs, 16 bytes (4 pairs) at a time: local pairs 4i..4i+3 are the
+    // unit's pairs pidx(h, 4i).. (consecutive), i.e. bytes 4 * pidx(h, 4i) of its 128.
+    uint32_t xp[M][NP];
 #pragma unroll
-      for (int i = 0; i < R; ++i) {
-        if (a.wk == 1) {
-          if (r0 + i < a.n) store_y(r0 + i, part[i]);
-        } else {
-          red[(wr * rows_here + j * R + i) * a.wk + wk] = part[i];
-        }
+    for (int mm = 0; mm < M; ++mm) {
+      const bool live = mm < a.m;
+      const uint8_t *px =
+          reinterpret_cast<const uint8_t *>(x + (int64_t)(live ? mm : 0) * a.ldx) + (uint32_t)(u * 128);
+#pragma unroll
+      for (int i = 0; i < NP / 4; ++i) {
+        uint32_t off = 4u * (uint32_t)U::pidx(h, 4 * i, S);
+        bool keepx = live;
+        // a half unit (k % 64 == 32) has only 32 activations: re-read the first half, zero it
+        if (F == 4 && half && off >= 64) { off -= 64; keepx = false; }
+        const u32x4 v = ld4(px + off);
+        xp[mm][4 * i + 0] = keepx ? v.x : 0u;
+        xp[mm][4 * i + 1] = keepx ? v.y : 0u;
+        xp[mm][4 * i + 2] = keepx ? v.z : 0u;
+        xp[mm][4 * i + 3] = keepx ? v.w : 0u;
       }
     }
-  };
+    float kc[M][NK];
+#pragma unroll
+    for (int mm = 0; mm < M; ++mm) U::template prep<S>(xp[mm], kc[mm]);
 
-  // Software pipeline: the next batch's loads are in flight while this one is computed.
-  // Loads inside the steady-state loop are unconditional, so the wait before each compute
-  // covers only the older batch (a conditional prefetch would force a wait for everything).
-  int j = 0;
-  for (; j + 2 < a.nb; j += 2) {
-    load_batch(qb, row_begin + (int64_t)(j + 1) * R);
-    finish_batch(qa, j);
-    load_batch(qa, row_begin + (int64_t)(j + 2) * R);
-    finish_batch(qb, j + 1);
-  }
-  if (j + 1 < a.nb) {
-    load_batch(qb, row_begin + (int64_t)(j + 1) * R);
-    finish_batch(qa, j);
-    finish_batch(qb, j + 1);
-  } else {
-    finish_batch(qa, j);
+    auto finish_batch = [&](const Raw *q, int j) {
+      const int64_t r0 = row_begin + (int64_t)j * R;
+      float part[R][M];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        float o[M];
+#pragma unroll
+        for (int mm = 0; mm < M; ++mm) o[mm] = 0.f;
+        U::template dot<M, S>(q[i], h, xp, kc, o);
+#pragma unroll
+        for (int mm = 0; mm < M; ++mm) part[i][mm] = wave_sum_to_63(act ? o[mm] : 0.f);
+      }
+      if (lane == 63) {
+#pragma unroll
+        for (int i = 0; i < R; ++i)
+#pragma unroll
+          for (int mm = 0; mm < M; ++mm) {
+            if (mm >= a.m) continue;
+            if (a.wk == 1) {
+              if (r0 + i < a.n) store_y(mm, r0 + i, part[i][mm]);
+            } else {
+              float &slot = red[((wr * rows_here + j * R + i) * M + mm) * a.wk + wk];
+              slot = (MP && kp) ? slot + part[i][mm] : part[i][mm];
+            }
+          }
+      }
+    };
+
+    // Software pipeline: the next batch's loads are in flight while this one is computed.
+    // Loads inside the steady-state loop are unconditional, so the wait before each compute
+    // covers only the older batch (a conditional prefetch would force a wait for everything).
+    int j = 0;
+    for (; j + 2 < a.nb; j += 2) {
+      load_batch(qb, row_begin + (int64_t)(j + 1) * R);
+      finish_batch(qa, j);
+      load_batch(qa, row_begin + (int64_t)(j + 2) * R);
+      finish_batch(qb, j + 1);
+    }
+    if (j + 1 < a.nb) {
+      load_batch(qb, row_begin + (int64_t)(j + 1) * R);
+      finish_batch(qa, j);
+      finish_batch(qb, j + 1);
+    } else {
+      finish_batch(qa, j);
+    }
   }
   if (a.wk == 1) return;
   // K split over wk waves: one barrier, then the first wave of the row group adds the
-  // partial sums of all its rows and writes them (one row per lane)
+  // partial sums of all its (row, m) outputs and writes them (one output per lane)
   __syncthreads();
   if (wk == 0) {
-    for (int i = lane; i < rows_here; i += 64) {
-      const int64_t r = row_begin + i;
+    for (int i = lane; i < rows_here * M; i += 64) {
+      const int64_t r = row_begin + i / M;
+      const int mm = i % M;
       float sum = 0.f;
-      for (int j = 0; j < a.wk; ++j) sum += red[(wr * rows_here + i) * a.wk + j];
-      if (r < a.n) store_y(r, sum);
+      for (int jj = 0; jj < a.wk; ++jj) sum += red[(wr * rows_here * M + i) * a.wk + jj];
+      if (r < a.n && mm < a.m) store_y(mm, r, sum);
     }
   }
 }
@@ -630,6 +368,9 @@ int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shm, hipStrea
 
 namespace {
 
+constexpr int64_t kMaxK = int64_t(1) << 20;   // at most 64 K passes in every configuration
+constexpr int64_t kMaxPlaneBytes = (int64_t(1) << 32) - 1;   // buffer resources are 32-bit ranges
+
 int fill_args(int fmt, const void *w, int64_t n, int64_t k, GemvArgs &a) {
   qg_layout L;
   int st = qg_device_layout(fmt, n, k, &L);
@@ -641,52 +382,87 @@ int fill_args(int fmt, const void *w, int64_t n, int64_t k, GemvArgs &a) {
   for (int p = 0; p < 4; ++p) {
     a.poff[p] = L.plane_offset[p];
     a.prb[p] = L.plane_row_bytes[p];
+    if (a.prb[p] * n > kMaxPlaneBytes) return QG_ERR_SHAPE;
   }
   return QG_OK;
 }
 
-constexpr int kMaxWk = 16;
+constexpr int kMaxWk = 16;                 // waves along K in one workgroup (1024 threads)
 constexpr int64_t kSimds = 1024;           // 256 CUs x 4 SIMDs
-constexpr int64_t kWavesPerSimd = 4;       // resident waves the kernels' register use allows
 constexpr int kMaxBatches = 32;
+constexpr int kMaxM = 8;                   // activation rows one streaming launch serves
 
-template <int F, int R>
-int launch_gemv_r(GemvArgs a, int64_t count, hipStream_t s) {
+// Resident waves per SIMD that a kernel's register and LDS use allow (asked once per kernel).
+int waves_per_simd(const void *kernel) {
+  int blocks = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&blocks, kernel, 64, 0) != hipSuccess || blocks < 4) return 1;
+  return blocks / 4 > 8 ? 8 : blocks / 4;
+}
+
+template <int F, int M, int S, int R, bool MP>
+int launch_mv(GemvArgs a, int64_t count, hipStream_t s) {
+  void (*kern)(GemvArgs) = mv_kernel<F, M, S, R, MP>;
+  static const int wps = waves_per_simd(reinterpret_cast<const void *>(kern));
   const int64_t groups_per_matrix = (a.n + R - 1) / R;          // batches of R rows
-  const int64_t target = kSimds * kWavesPerSimd / a.wk;         // row groups resident at once
+  const int64_t target = kSimds * wps / a.wk;                   // row groups resident at once
   int64_t nb = (groups_per_matrix * count) / target;
   nb = nb < 1 ? 1 : (nb > kMaxBatches ? kMaxBatches : nb);
   a.nb = (int)nb;
   const int64_t rows_per_block = (int64_t)a.wr * R * nb;
   dim3 grid((unsigned)((a.n + rows_per_block - 1) / rows_per_block), (unsigned)count);
   dim3 block((unsigned)(64 * a.wk * a.wr));
-  size_t shm = a.wk > 1 ? (size_t)a.wr * R * nb * a.wk * sizeof(float) : 0;
-  return launch(gemv_kernel<F, R>, grid, block, shm, s, a);
+  size_t shm = a.wk > 1 ? (size_t)a.wr * R * nb * M * a.wk * sizeof(float) : 0;
+  return launch(kern, grid, block, shm, s, a);
 }
 
-// Rows per batch: 2 (double-buffered, so four rows of loads per wave in flight at 4 waves per
-// SIMD without spilling) when there are enough rows to keep every SIMD busy, else 1: small
-// problems are bound by latency, so they get as many waves as possible.
-template <int F>
-int launch_gemv_t(GemvArgs a, int64_t count, hipStream_t s) {
-  const int wk = (int)((a.units + 63) / 64);
+// Waves along K: one per 64 / S units. Rows per batch: 2 (double-buffered, so four rows of
+// loads per wave in flight without spilling) when there are enough rows to keep every SIMD
+// busy, else 1: small problems are bound by latency and get as many waves as possible. With
+// M > 2 the activation registers leave room for one row per batch only.
+template <int F, int M, int S>
+int launch_mv_s(GemvArgs a, int64_t count, hipStream_t s) {
+  constexpr int UPW = 64 / S;
+  constexpr int max_wk = M > 4 ? kMaxWk / 2 : kMaxWk;        // the kernel's block-size bound
+  const int64_t waves_k = (a.units + UPW - 1) / UPW;
+  const int64_t passes = (waves_k + max_wk - 1) / max_wk;
+  if (passes > 64) return QG_ERR_SHAPE;
+  const int wk = (int)((waves_k + passes - 1) / passes);
+  a.kpasses = (int)passes;
   a.wk = wk;
   a.wr = wk >= 4 ? 1 : 4 / wk;
-  const int64_t rows = a.n * count, target = kSimds * kWavesPerSimd / wk;
-  if (rows >= 2 * target) return launch_gemv_r<F, 2>(a, count, s);
-  return launch_gemv_r<F, 1>(a, count, s);
+  if (passes > 1) return launch_mv<F, M, S, 1, true>(a, count, s);
+  if constexpr (M <= 2) {
+    const int64_t rows = a.n * count, target = kSimds * 4 / wk;
+    if (rows >= 2 * target) return launch_mv<F, M, S, 2, false>(a, count, s);
+  }
+  return launch_mv<F, M, S, 1, false>(a, count, s);
 }
 
-int launch_gemv(int fmt, GemvArgs a, int64_t count, hipStream_t s) {
+// M = 1: a lane owns a whole unit (32 activation VGPRs). M = 2..8: two lanes share a unit, so
+// eight rows of activations take 128 VGPRs; rows beyond m are zero and not stored.
+template <int F>
+int launch_mv_f(GemvArgs a, int64_t count, hipStream_t s) {
+  switch (a.m) {
+    case 1: return launch_mv_s<F, 1, 1>(a, count, s);
+    case 2: return launch_mv_s<F, 2, 2>(a, count, s);
+    case 3:
+    case 4: return launch_mv_s<F, 4, 2>(a, count, s);
+    default: return launch_mv_s<F, 8, 2>(a, count, s);
+  }
+}
+
+int launch_mv_fmt(int fmt, GemvArgs a, int64_t count, hipStream_t s) {
+  if (a.m < 1 || a.m > kMaxM) return QG_ERR_SHAPE;
   switch (fmt) {
-    case 2: return launch_gemv_t<2>(a, count, s);
-    case 3: return launch_gemv_t<3>(a, count, s);
-    case 4: return launch_gemv_t<4>(a, count, s);
-    case 5: return launch_gemv_t<5>(a, count, s);
-    case 6: return launch_gemv_t<6>(a, count, s);
+    case 2: return launch_mv_f<2>(a, count, s);
+    case 3: return launch_mv_f<3>(a, count, s);
+    case 4: return launch_mv_f<4>(a, count, s);
+    case 5: return launch_mv_f<5>(a, count, s);
+    case 6: return launch_mv_f<6>(a, count, s);
   }
   return QG_ERR_FORMAT;
 }
+
 
 }  // namespace
 
@@ -701,7 +477,7 @@ int qg_gemv_batched(int fmt, const void *w, int64_t w_stride, const uint16_t *x,
   if (!fmt_valid(fmt)) return QG_ERR_FORMAT;
   if (n < 0 || k < 0 || count < 0) return QG_ERR_SHAPE;
   if ((fmt == 4 && k % 32) || (fmt != 4 && k % kQK)) return QG_ERR_SHAPE;
-  if ((k + kUnit - 1) / kUnit > 64 * kMaxWk) return QG_ERR_SHAPE;
+  if (k > kMaxK) return QG_ERR_SHAPE;
   if (count > 65535) return QG_ERR_SHAPE;
   if (n == 0 || count == 0) return QG_OK;
   if (!y || (k > 0 && (!w || !x))) return QG_ERR_NULL;
@@ -724,11 +500,50 @@ int qg_gemv_batched(int fmt, const void *w, int64_t w_stride, const uint16_t *x,
   a.y = y;
   a.y_bstride = y_stride;
   a.y_f32 = y_f32;
-  return launch_gemv(fmt, a, count, s);
+  a.m = 1;
+  return launch_mv_fmt(fmt, a, count, s);
 }
 
 int qg_gemv(int fmt, const void *w, const uint16_t *x, void *y, int y_f32, int64_t n, int64_t k, void *stream) {
-  return qg_gemv_batched(fmt, w, 0, x, 0, y, n, y_f32, 1, n, k, stream);
+  return qg_gemv_batched(fmt, w, 0, x, 0, y, 0, y_f32, 1, n, k, stream);
+}
+
+int qg_gemm(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int64_t ldy, int y_f32, int64_t m,
+            int64_t n, int64_t k, void *stream) {
+  if (!fmt_valid(fmt)) return QG_ERR_FORMAT;
+  if (n < 0 || k < 0 || m < 0) return QG_ERR_SHAPE;
+  if ((fmt == 4 && k % 32) || (fmt != 4 && k % kQK)) return QG_ERR_SHAPE;
+  if (m > 1 && (ldx < k || ldy < n)) return QG_ERR_SHAPE;
+  if (k > kMaxK) return QG_ERR_SHAPE;
+  if (n == 0 || m == 0) return QG_OK;
+  if (!Y || (k > 0 && (!w || !X))) return QG_ERR_NULL;
+  if (!aligned(Y, y_f32 ? 4 : 2)) return QG_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t esz = y_f32 ? 4 : 2;
+  if (k == 0) {
+    for (int64_t i = 0; i < m; ++i) {
+      int st = launch(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s,
+                      static_cast<void *>(static_cast<char *>(Y) + i * ldy * esz), n, y_f32, (int64_t)0, n);
+      if (st != QG_OK) return st;
+    }
+    return QG_OK;
+  }
+  if (!aligned(w, 256) || !aligned(X, 16) || (m > 1 && ldx % 8)) return QG_ERR_ALIGN;
+  GemvArgs a{};
+  int st = fill_args(fmt, w, n, k, a);
+  if (st != QG_OK) return st;
+  a.ldx = ldx;
+  a.ldy = ldy;
+  a.y_f32 = y_f32;
+  // each launch serves up to kMaxM activation rows and streams the weights once
+  for (int64_t i0 = 0; i0 < m; i0 += kMaxM) {
+    a.x = X + i0 * ldx;
+    a.y = static_cast<char *>(Y) + i0 * ldy * esz;
+    a.m = m - i0 < kMaxM ? m - i0 : kMaxM;
+    st = launch_mv_fmt(fmt, a, 1, s);
+    if (st != QG_OK) return st;
+  }
+  return QG_OK;
 }
 
 int dequant_gemv_q4g32(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(4, w, x, y, 0, n, k, s); }
@@ -736,6 +551,26 @@ int dequant_gemv_q2sb(const void *w, const uint16_t *x, uint16_t *y, int64_t n, 
 int dequant_gemv_q3sb(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(3, w, x, y, 0, n, k, s); }
 int dequant_gemv_q5sb(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(5, w, x, y, 0, n, k, s); }
 int dequant_gemv_q6sb(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(6, w, x, y, 0, n, k, s); }
+int dequant_gemm_q4g32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m, int64_t n,
+                       int64_t k, void *s) {
+  return qg_gemm(4, w, X, ldx, Y, ldy, 0, m, n, k, s);
+}
+int dequant_gemm_q2sb(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m, int64_t n,
+                      int64_t k, void *s) {
+  return qg_gemm(2, w, X, ldx, Y, ldy, 0, m, n, k, s);
+}
+int dequant_gemm_q3sb(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m, int64_t n,
+                      int64_t k, void *s) {
+  return qg_gemm(3, w, X, ldx, Y, ldy, 0, m, n, k, s);
+}
+int dequant_gemm_q5sb(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m, int64_t n,
+                      int64_t k, void *s) {
+  return qg_gemm(5, w, X, ldx, Y, ldy, 0, m, n, k, s);
+}
+int dequant_gemm_q6sb(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m, int64_t n,
+                      int64_t k, void *s) {
+  return qg_gemm(6, w, X, ldx, Y, ldy, 0, m, n, k, s);
+}
 
 int qg_dequantize(int fmt, const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream) {
   if (!fmt_valid(fmt)) return QG_ERR_FORMAT;

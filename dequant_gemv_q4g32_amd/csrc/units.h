@@ -1,0 +1,438 @@
+// Per-format decode-and-dot of one 64-weight lane unit (see layout.h for the bit placement).
+//
+// Terms: a "pair" is two consecutive weights (2t, 2t+1) of the unit, multiplied by one
+// activation dword (x[2t], x[2t+1]) with v_dot2_f32_f16. A unit has 32 pairs. With S = 1 a
+// lane owns the whole unit; with S = 2 two lanes share it and lane half h owns pairs
+// pidx(h, p), p < 16 (the first or second 32 weights for every format but q2sb, whose
+// halves interleave; see pidx). M activation rows share every decoded code.
+//
+// Each code pair is turned into fp16 (1024 + p*c_a, 1024 + p*c_b) by one v_and_or_b32, for
+// a power of two p (the "class" of the bit position it sits at). Per class and sub-block
+// the products are accumulated in fp32, and the 1024s and the code offsets cancel against
+// per-lane constants built from sums of x ("kc"), which the accumulators start from. This
+// is the sum-of-x rewrite of "二三五六位量化" section 3.3: s * sum(q x) + m * sum(x).
+#pragma once
+#include "device_common.h"
+
+namespace qg {
+
+struct Lane {
+  rsrc_t rs[4];
+  uint32_t prb[4];
+  uint32_t off[4];
+  uint32_t sh;              // bit offset of this unit's 6-bit fields in its 8-byte window
+  __device__ uint32_t row(int p, int64_t r) const { return (uint32_t)r * prb[p]; }
+};
+
+// 6-bit sub-scale fields (12 bytes per super-block; a unit owns 3 of them, bytes 3q..3q+2 for
+// quarter q) are read as an 8-byte window starting at byte 4*max(0, q-1) and shifted right by
+// (24q) mod 32 bits: 0, 24, 16, 8 for q = 0..3. The window of q = 3 reaches 4 bytes past the
+// super-block, which is in bounds (the next super-block, or the plane that follows, or
+// buffer range checking returns zero).
+__device__ __forceinline__ uint32_t fields_off(int64_t u) {
+  const uint32_t q = (uint32_t)(u & 3);
+  return (uint32_t)((u >> 2) * 12) + (q ? 4 * (q - 1) : 0);
+}
+__device__ __forceinline__ uint32_t fields_sh(int64_t u) { return (uint32_t)((24 * (u & 3)) & 31); }
+__device__ __forceinline__ uint32_t fields24(const Lane &L, int p, int64_t r) {
+  const uint32_t lo = bld1(L.rs[p], L.off[p], L.row(p, r));
+  const uint32_t hi = bld1(L.rs[p], L.off[p] + 4, L.row(p, r));
+  return __builtin_amdgcn_alignbit(hi, lo, L.sh);   // low 24 bits are the unit's fields
+}
+
+__device__ __forceinline__ uint32_t sel(bool c, uint32_t a, uint32_t b) { return c ? a : b; }
+
+template <int F> struct Unit;
+
+// ---- INT4 group-32: a unit is two groups; with S = 2 a lane owns one group
+// NKS(S): per-lane constants per activation row, for S lanes per unit.
+template <> struct Unit<4> {
+  static constexpr int NK = 2;                    // constants per activation row (S = 1)
+  __host__ __device__ static constexpr int NKS(int S) { return NK / S; }
+  struct Raw { u32x4 c0, c1; float s0, s1; };
+  __device__ static int pidx(int h, int p, int S) { return S == 1 ? p : 16 * h + p; }
+  __device__ static void offsets(int64_t u, uint32_t *off) { off[0] = (uint32_t)(u * 32); off[1] = (uint32_t)(u * 8); }
+  __device__ static void load(Raw &q, const Lane &L, int64_t r, bool half) {
+    const uint32_t r0 = L.row(0, r), r1 = L.row(1, r);
+    q.c0 = bld4(L.rs[0], L.off[0], r0);
+    // a half unit (k % 64 == 32) has one group; its second group's activations are zero
+    q.c1 = bld4(L.rs[0], L.off[0] + (half ? 0u : 16u), r0);
+    // Two 32-bit loads, not one 64-bit load: this toolchain narrows a multi-dword buffer load
+    // whose elements are bit-cast to float to its first dword and reuses that dword for the
+    // second element (vectors used in integer arithmetic, like the code words, are unaffected).
+    q.s0 = __builtin_bit_cast(float, bld1(L.rs[1], L.off[1], r1));
+    q.s1 = __builtin_bit_cast(float, bld1(L.rs[1], L.off[1] + (half ? 0u : 4u), r1));
+  }
+  // xp: the lane's pairs (32 / S); kc: NK / S constants
+  template <int S> __device__ static void prep(const uint32_t *xp, float *kc) {
+#pragma unroll
+    for (int g = 0; g < 2 / S; ++g) {
+      float x1 = 0.f, x16 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x1 = dot2(xp[16 * g + 4 * i + 0], kOnes, x1);
+        x1 = dot2(xp[16 * g + 4 * i + 2], kOnes, x1);
+        x16 = dot2(xp[16 * g + 4 * i + 1], kOnes, x16);
+        x16 = dot2(xp[16 * g + 4 * i + 3], kOnes, x16);
+      }
+      kc[g] = -(1032.0f * x1 + 72.0f * x16);   // sum (u - 8) x = A1 + A16/16, A1 starting here
+    }
+  }
+  template <int M, int S>
+  __device__ static void dot(const Raw &q, int h, const uint32_t (*xp)[32 / S], const float (*kc)[NKS(S)], float *out) {
+#pragma unroll
+    for (int g = 0; g < 2 / S; ++g) {
+      const u32x4 c = S == 1 ? (g ? q.c1 : q.c0) : (h ? q.c1 : q.c0);
+      const float scale = S == 1 ? (g ? q.s1 : q.s0) : (h ? q.s1 : q.s0);
+      float a1[M], a16[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) { a1[m] = kc[m][g]; a16[m] = 0.f; }
+      const uint32_t d[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t v = d[i], v8 = v >> 8;
+        const uint32_t p0 = pick(v, QG_SMASK(0x000F000Fu)), p1 = pick(v, QG_SMASK(0x00F000F0u));
+        const uint32_t p2 = pick(v8, QG_SMASK(0x000F000Fu)), p3 = pick(v8, QG_SMASK(0x00F000F0u));
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          a1[m] = dot2(p0, xp[m][16 * g + 4 * i + 0], a1[m]);
+          a16[m] = dot2(p1, xp[m][16 * g + 4 * i + 1], a16[m]);
+          a1[m] = dot2(p2, xp[m][16 * g + 4 * i + 2], a1[m]);
+          a16[m] = dot2(p3, xp[m][16 * g + 4 * i + 3], a16[m]);
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < M; ++m) out[m] = __builtin_fmaf(scale, __builtin_fmaf(a16[m], 0.0625f, a1[m]), out[m]);
+    }
+  }
+};
+
+// ---- 2-bit super-block: a unit is a quarter super-block (4 sub-blocks of 16). Sub-block j
+// sits at class 4^j in every dword; with S = 2 lane half h owns dwords 2h, 2h+1, i.e. pairs
+// r = 4h..4h+3 of every sub-block.
+template <> struct Unit<2> {
+  static constexpr int NK = 4;
+  __host__ __device__ static constexpr int NKS(int) { return 4; }  // every half meets all 4 sub-blocks
+  struct Raw { u32x4 c; uint32_t sc, dd; };
+  __device__ static int pidx(int h, int p, int S) { return S == 1 ? p : 8 * (p >> 2) + 4 * h + (p & 3); }
+  __device__ static void offsets(int64_t u, uint32_t *off) {
+    off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 4); off[2] = (uint32_t)((u >> 2) * 4);
+  }
+  __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
+    q.c = bld4(L.rs[0], L.off[0], L.row(0, r));
+    q.sc = bld1_nt(L.rs[1], L.off[1], L.row(1, r));
+    q.dd = bld1(L.rs[2], L.off[2], L.row(2, r));
+  }
+  // kc[j]: sum of x over the lane's part of sub-block j (local pairs (8/S) j .. (8/S) j + 8/S - 1)
+  template <int S> __device__ static void prep(const uint32_t *xp, float *kc) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      float s = 0.f;
+#pragma unroll
+      for (int r = 0; r < 8 / S; ++r) s = dot2(xp[(8 / S) * j + r], kOnes, s);
+      kc[j] = s;
+    }
+  }
+  // Sub-block j sits at class 4^j: A_j = 1024 sum x + 4^j sum c x, so with sc'_j = sc_j / 4^j
+  //   y += d sum_j sc'_j A_j - sum_j (1024 d sc'_j + dmin m_j) sum x_j.
+  template <int M, int S>
+  __device__ static void dot(const Raw &q, int h, const uint32_t (*xp)[32 / S], const float (*kc)[NKS(S)], float *out) {
+    float A[M][4];
+#pragma unroll
+    for (int m = 0; m < M; ++m)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) A[m][j] = 0.f;
+    const uint32_t d[4] = {q.c.x, q.c.y, q.c.z, q.c.w};
+#pragma unroll
+    for (int ii = 0; ii < 4 / S; ++ii) {
+      const uint32_t v = S == 1 ? d[ii] : sel(h, d[2 + ii], d[ii]);
+      const uint32_t v8 = v >> 8;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const uint32_t pa = pick(v, QG_SMASK(0x00030003u << (2 * j))), pb = pick(v8, QG_SMASK(0x00030003u << (2 * j)));
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          A[m][j] = dot2(pa, xp[m][(8 / S) * j + 2 * ii], A[m][j]);
+          A[m][j] = dot2(pb, xp[m][(8 / S) * j + 2 * ii + 1], A[m][j]);
+        }
+      }
+    }
+    const uint32_t s = q.sc;
+    const float inv4[4] = {1.0f, 0.25f, 0.0625f, 0.015625f};
+    const float dv = half_lo(q.dd), dm = half_hi(q.dd);
+    float scj[4], cj[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      scj[j] = dv * ((float)((s >> (8 * j)) & 15u) * inv4[j]);
+      cj[j] = __builtin_fmaf(1024.0f, scj[j], dm * (float)((s >> (8 * j + 4)) & 15u));
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float acc = out[m];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        acc = __builtin_fmaf(scj[j], A[m][j], acc);
+        acc = __builtin_fmaf(-cj[j], kc[m][j], acc);
+      }
+      out[m] = acc;
+    }
+  }
+};
+
+// ---- 3-bit super-block: a unit is two chunks of 32 codes (sub-blocks a, b each); with S = 2
+// lane half h owns chunk h.
+template <> struct Unit<3> {
+  static constexpr int NK = 4;
+  __host__ __device__ static constexpr int NKS(int S) { return NK / S; }
+  struct Raw { u32x4 a; u32x2 b; uint32_t f; uint16_t d; };
+  __device__ static int pidx(int h, int p, int S) { return S == 1 ? p : 16 * h + p; }
+  __device__ static void offsets(int64_t u, uint32_t *off) {
+    off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 8); off[2] = fields_off(u); off[3] = (uint32_t)((u >> 2) * 2);
+  }
+  __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
+    q.a = bld4(L.rs[0], L.off[0], L.row(0, r));
+    q.b = bld2(L.rs[1], L.off[1], L.row(1, r));
+    q.f = fields24(L, 2, r);
+    q.d = bldh(L.rs[3], L.off[3], L.row(3, r));
+  }
+  template <int S> __device__ static void prep(const uint32_t *xp, float *kc) {
+#pragma unroll
+    for (int c = 0; c < 2 / S; ++c) {
+      const uint32_t *x = xp + 16 * c;
+      float a1 = 0.f, a8 = 0.f, b8 = 0.f, b64 = 0.f;
+#pragma unroll
+      for (int r = 0; r < 6; ++r) a1 = dot2(x[r], kOnes, a1);
+#pragma unroll
+      for (int r = 6; r < 8; ++r) a8 = dot2(x[r], kOnes, a8);
+#pragma unroll
+      for (int r = 8; r < 12; ++r) b8 = dot2(x[r], kOnes, b8);
+#pragma unroll
+      for (int r = 12; r < 16; ++r) b64 = dot2(x[r], kOnes, b64);
+      kc[2 * c] = -(1028.0f * a1 + 132.0f * a8);            // start of a's class-1 sum
+      kc[2 * c + 1] = -8.0f * (132.0f * b8 + 20.0f * b64);  // start of b's class-8 sum
+    }
+  }
+  // One chunk: three dwords e0..e2 holding 32 codes -> the 16 fp16 pairs of its two
+  // sub-blocks (a: P[0..7], classes 1 x6 and 8 x2; b: P[8..15], classes 8 x4 and 64 x4).
+  __device__ static void chunk_pairs(uint32_t e0, uint32_t e1, uint32_t e2, uint32_t *P) {
+    const uint32_t e09 = e0 >> 9, e19 = e1 >> 9, e29 = e2 >> 9;
+    P[0] = pick(e0, QG_SMASK(0x00070007u));
+    P[1] = pick(e09, QG_SMASK(0x00070007u));
+    P[2] = pick(e1, QG_SMASK(0x00070007u));
+    P[3] = pick(e19, QG_SMASK(0x00070007u));
+    P[4] = pick(e2, QG_SMASK(0x00070007u));
+    P[5] = pick(e29, QG_SMASK(0x00070007u));
+    P[6] = pick(e0, QG_SMASK(0x00380038u));
+    P[7] = pick(e09, QG_SMASK(0x00380038u));
+    P[8] = pick(e1, QG_SMASK(0x00380038u));
+    P[9] = pick(e19, QG_SMASK(0x00380038u));
+    P[10] = pick(e2, QG_SMASK(0x00380038u));
+    P[11] = pick(e29, QG_SMASK(0x00380038u));
+    P[12] = pick(e0, QG_SMASK(0x01C001C0u));
+    P[13] = pick(e1, QG_SMASK(0x01C001C0u));
+    P[14] = pick(e2, QG_SMASK(0x01C001C0u));
+    uint32_t t = keep(pick(e09, QG_SMASK(0x00400040u)));    // bit 15 of e0 -> 6, bit 31 -> 22
+    t = keep(pick_or(e1 >> 8, QG_SMASK(0x00800080u), t));    // bit 15 of e1 -> 7
+    P[15] = pick_or(e2 >> 7, QG_SMASK(0x01000100u), t);      // bit 15 of e2 -> 8
+  }
+  // sum (c - 4) x over sub-block a (sa) and 8 x that over b (sb) for one activation row
+  __device__ static void chunk_dot(const uint32_t *P, const uint32_t *x, float ka, float kb, float &sa, float &sb) {
+    float a1 = ka, a8 = 0.f, b8 = kb, b64 = 0.f;
+#pragma unroll
+    for (int r = 0; r < 6; ++r) a1 = dot2(P[r], x[r], a1);
+    a8 = dot2(P[6], x[6], a8);
+    a8 = dot2(P[7], x[7], a8);
+#pragma unroll
+    for (int r = 8; r < 12; ++r) b8 = dot2(P[r], x[r], b8);
+#pragma unroll
+    for (int r = 12; r < 16; ++r) b64 = dot2(P[r], x[r], b64);
+    sa = __builtin_fmaf(a8, 0.125f, a1);
+    sb = __builtin_fmaf(b64, 0.125f, b8);
+  }
+  template <int M, int S>
+  __device__ static void dot(const Raw &q, int h, const uint32_t (*xp)[32 / S], const float (*kc)[NKS(S)], float *out) {
+    const uint32_t f = q.f;
+    const float dv = half_bits(q.d);
+    if constexpr (S == 1) {
+      uint32_t P0[16], P1[16];
+      chunk_pairs(q.a.x, q.a.y, q.a.z, P0);
+      chunk_pairs(q.a.w, q.b.x, q.b.y, P1);
+      const float s0 = (float)(f & 63u), s1 = (float)((f >> 6) & 63u) * 0.125f;
+      const float s2 = (float)((f >> 12) & 63u), s3 = (float)((f >> 18) & 63u) * 0.125f;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float sa0, sb0, sa1, sb1;
+        chunk_dot(P0, xp[m], kc[m][0], kc[m][1], sa0, sb0);
+        chunk_dot(P1, xp[m] + 16, kc[m][2], kc[m][3], sa1, sb1);
+        float acc = s0 * sa0;
+        acc = __builtin_fmaf(s1, sb0, acc);
+        acc = __builtin_fmaf(s2, sa1, acc);
+        acc = __builtin_fmaf(s3, sb1, acc);
+        out[m] = __builtin_fmaf(dv, acc, out[m]);
+      }
+    } else {
+      // chunk h: (a.x, a.y, a.z) or (a.w, b.x, b.y); its sub-blocks are 2h, 2h+1
+      uint32_t P[16];
+      chunk_pairs(sel(h, q.a.w, q.a.x), sel(h, q.b.x, q.a.y), sel(h, q.b.y, q.a.z), P);
+      const uint32_t fh = f >> (12 * h);
+      const float s0 = (float)(fh & 63u), s1 = (float)((fh >> 6) & 63u) * 0.125f;
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float sa, sb;
+        chunk_dot(P, xp[m], kc[m][0], kc[m][1], sa, sb);
+        out[m] = __builtin_fmaf(dv, __builtin_fmaf(s1, sb, s0 * sa), out[m]);
+      }
+    }
+  }
+};
+
+// ---- nibble plane + high-bit plane (q5sb: 1 high bit, 32-weight sub-blocks;
+//      q6sb: 2 high bits, 16-weight sub-blocks). Produces the four pairs of one nibble dword.
+template <int HB>
+__device__ __forceinline__ void nib_pairs(uint32_t L, uint32_t H, int ip, uint32_t *P) {
+  constexpr uint32_t m1 = HB == 1 ? 0x00100010u : 0x00300030u;
+  constexpr uint32_t m16 = HB == 1 ? 0x01000100u : 0x03000300u;
+  const int ra = HB * ip, rb = 8 + HB * ip;
+  const uint32_t ha = ra ? rotr(H, ra) : H, hb = rotr(H, rb);
+  const uint32_t L8 = L >> 8;
+  P[0] = pick_or(L, QG_SMASK(0x000F000Fu), keep(pick(ha, QG_SMASK(m1))));    // class 1
+  P[1] = pick_or(L, QG_SMASK(0x00F000F0u), keep(pick(ha, QG_SMASK(m16))));   // class 16
+  P[2] = pick_or(L8, QG_SMASK(0x000F000Fu), keep(pick(hb, QG_SMASK(m1))));   // class 1
+  P[3] = pick_or(L8, QG_SMASK(0x00F000F0u), keep(pick(hb, QG_SMASK(m16))));  // class 16
+}
+
+// ---- 5-bit super-block: a unit is two sub-blocks of 32; with S = 2 lane half h owns one
+template <> struct Unit<5> {
+  static constexpr int NK = 4;
+  __host__ __device__ static constexpr int NKS(int S) { return NK / S; }
+  struct Raw { u32x4 l0, l1; u32x2 h; uint32_t f, dd; };
+  __device__ static int pidx(int h, int p, int S) { return S == 1 ? p : 16 * h + p; }
+  __device__ static void offsets(int64_t u, uint32_t *off) {
+    off[0] = (uint32_t)(u * 32); off[1] = (uint32_t)(u * 8); off[2] = fields_off(u); off[3] = (uint32_t)((u >> 2) * 4);
+  }
+  __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
+    const uint32_t r0 = L.row(0, r);
+    q.l0 = bld4(L.rs[0], L.off[0], r0);
+    q.l1 = bld4(L.rs[0], L.off[0] + 16, r0);
+    q.h = bld2(L.rs[1], L.off[1], L.row(1, r));
+    q.f = fields24(L, 2, r);
+    q.dd = bld1(L.rs[3], L.off[3], L.row(3, r));
+  }
+  // kc layout (S = 1): [start h0, start h1, sum x h0, sum x h1]; (S = 2): [start, sum x]
+  template <int S> __device__ static void prep(const uint32_t *xp, float *kc) {
+#pragma unroll
+    for (int hh = 0; hh < 2 / S; ++hh) {
+      float x1 = 0.f, x16 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x1 = dot2(xp[16 * hh + 4 * i + 0], kOnes, x1);
+        x1 = dot2(xp[16 * hh + 4 * i + 2], kOnes, x1);
+        x16 = dot2(xp[16 * hh + 4 * i + 1], kOnes, x16);
+        x16 = dot2(xp[16 * hh + 4 * i + 3], kOnes, x16);
+      }
+      kc[hh] = -(1024.0f * x1 + 64.0f * x16);
+      kc[2 / S + hh] = x1 + x16;
+    }
+  }
+  template <int M, int S>
+  __device__ static void dot(const Raw &q, int h, const uint32_t (*xp)[32 / S], const float (*kc)[NKS(S)], float *out) {
+    const uint32_t L[8] = {q.l0.x, q.l0.y, q.l0.z, q.l0.w, q.l1.x, q.l1.y, q.l1.z, q.l1.w};
+    const uint32_t f = q.f;
+    const float dv = half_lo(q.dd), dm = half_hi(q.dd);
+#pragma unroll
+    for (int hh = 0; hh < 2 / S; ++hh) {
+      const int sb = S == 1 ? hh : 0;     // sub-block within what this lane owns
+      float a1[M], a16[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) { a1[m] = kc[m][sb]; a16[m] = 0.f; }
+      const uint32_t H = S == 1 ? (hh ? q.h.y : q.h.x) : sel(h, q.h.y, q.h.x);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t P[4];
+        const uint32_t Li = S == 1 ? L[4 * hh + i] : sel(h, L[4 + i], L[i]);
+        nib_pairs<1>(Li, H, i, P);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          a1[m] = dot2(P[0], xp[m][16 * sb + 4 * i + 0], a1[m]);
+          a16[m] = dot2(P[1], xp[m][16 * sb + 4 * i + 1], a16[m]);
+          a1[m] = dot2(P[2], xp[m][16 * sb + 4 * i + 2], a1[m]);
+          a16[m] = dot2(P[3], xp[m][16 * sb + 4 * i + 3], a16[m]);
+        }
+      }
+      // sub-block of the super-block: 2q + (S == 1 ? hh : h); fields [sc0, sc1, m0, m1]
+      const int which = S == 1 ? hh : h;
+      const float scv = (float)((f >> (6 * which)) & 63u), mv = (float)((f >> (12 + 6 * which)) & 63u);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        const float s = __builtin_fmaf(a16[m], 0.0625f, a1[m]);   // sum c x
+        out[m] = __builtin_fmaf(dv * scv, s, __builtin_fmaf(-dm * mv, kc[m][2 / S + sb], out[m]));
+      }
+    }
+  }
+};
+
+// ---- 6-bit super-block: a unit is four sub-blocks of 16; with S = 2 lane half h owns
+// sub-blocks 2h, 2h+1
+template <> struct Unit<6> {
+  static constexpr int NK = 4;
+  __host__ __device__ static constexpr int NKS(int S) { return NK / S; }
+  struct Raw { u32x4 l0, l1, h; uint32_t sc; uint16_t d; };
+  __device__ static int pidx(int h, int p, int S) { return S == 1 ? p : 16 * h + p; }
+  __device__ static void offsets(int64_t u, uint32_t *off) {
+    off[0] = (uint32_t)(u * 32); off[1] = (uint32_t)(u * 16); off[2] = (uint32_t)(u * 4); off[3] = (uint32_t)((u >> 2) * 2);
+  }
+  __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
+    const uint32_t r0 = L.row(0, r);
+    q.l0 = bld4(L.rs[0], L.off[0], r0);
+    q.l1 = bld4(L.rs[0], L.off[0] + 16, r0);
+    q.h = bld4(L.rs[1], L.off[1], L.row(1, r));
+    q.sc = bld1_nt(L.rs[2], L.off[2], L.row(2, r));
+    q.d = bldh(L.rs[3], L.off[3], L.row(3, r));
+  }
+  template <int S> __device__ static void prep(const uint32_t *xp, float *kc) {
+#pragma unroll
+    for (int j = 0; j < 4 / S; ++j) {
+      float x1 = 0.f, x16 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        x1 = dot2(xp[8 * j + 4 * i + 0], kOnes, x1);
+        x1 = dot2(xp[8 * j + 4 * i + 2], kOnes, x1);
+        x16 = dot2(xp[8 * j + 4 * i + 1], kOnes, x16);
+        x16 = dot2(xp[8 * j + 4 * i + 3], kOnes, x16);
+      }
+      kc[j] = -(1056.0f * x1 + 96.0f * x16);   // 1024 + 32 offset, 64 + 32 offset
+    }
+  }
+  template <int M, int S>
+  __device__ static void dot(const Raw &q, int h, const uint32_t (*xp)[32 / S], const float (*kc)[NKS(S)], float *out) {
+    const uint32_t L[8] = {q.l0.x, q.l0.y, q.l0.z, q.l0.w, q.l1.x, q.l1.y, q.l1.z, q.l1.w};
+    const uint32_t Hd[4] = {q.h.x, q.h.y, q.h.z, q.h.w};
+    const float dv = half_bits(q.d);
+#pragma unroll
+    for (int j = 0; j < 4 / S; ++j) {
+      float a1[M], a16[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) { a1[m] = kc[m][j]; a16[m] = 0.f; }
+      const uint32_t H = S == 1 ? Hd[j] : sel(h, Hd[2 + j], Hd[j]);
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        uint32_t P[4];
+        const uint32_t Li = S == 1 ? L[2 * j + ii] : sel(h, L[4 + 2 * j + ii], L[2 * j + ii]);
+        nib_pairs<2>(Li, H, ii, P);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          a1[m] = dot2(P[0], xp[m][8 * j + 4 * ii + 0], a1[m]);
+          a16[m] = dot2(P[1], xp[m][8 * j + 4 * ii + 1], a16[m]);
+          a1[m] = dot2(P[2], xp[m][8 * j + 4 * ii + 2], a1[m]);
+          a16[m] = dot2(P[3], xp[m][8 * j + 4 * ii + 3], a16[m]);
+        }
+      }
+      const int jj = S == 1 ? j : 2 * h + j;
+      const float sj = (float)(int8_t)((q.sc >> (8 * jj)) & 0xFFu);
+#pragma unroll
+      for (int m = 0; m < M; ++m) out[m] = __builtin_fmaf(dv * sj, __builtin_fmaf(a16[m], 0.0625f, a1[m]), out[m]);
+    }
+  }
+};
+
+}  // namespace qg

@@ -136,8 +136,9 @@ int qg_from_device_layout(int fmt, const uint8_t *device_layout, int64_t n, int6
  * x fp16 [k] (16-byte aligned), y fp16 [n]; fp32 accumulation, one fp16 rounding at the end.
  * The packed weights are streamed once with 128-bit loads and decoded in registers; no
  * dequantized weight is ever written to memory (DBHOO-CIM page section 3.3; "二三五六位量化"
- * page section 3.3's gemv_q3 and its Sigma-x rewrite). n == 0 is a no-op; k == 0 writes
- * zeros. Errors: QG_ERR_NULL, QG_ERR_SHAPE, QG_ERR_ALIGN, QG_ERR_FORMAT, QG_ERR_LAUNCH. */
+ * page section 3.3's gemv_q3 and its Sigma-x rewrite). Limits: k <= 2^20 and every plane
+ * of the device layout under 4 GiB. n == 0 is a no-op; k == 0 writes zeros.
+ * Errors: QG_ERR_NULL, QG_ERR_SHAPE, QG_ERR_ALIGN, QG_ERR_FORMAT, QG_ERR_LAUNCH. */
 int dequant_gemv_q4g32(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
 int dequant_gemv_q2sb(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
 int dequant_gemv_q3sb(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
@@ -154,6 +155,28 @@ int qg_gemv(int fmt, const void *w, const uint16_t *x, void *y, int y_f32, int64
  * launch per matrix. */
 int qg_gemv_batched(int fmt, const void *w, int64_t w_stride, const uint16_t *x, int64_t x_stride,
                     void *y, int64_t y_stride, int y_f32, int64_t count, int64_t n, int64_t k, void *stream);
+
+/* ---- dequant GEMM with a few activation rows (device) ------------------------------------
+ * Y[i][r] = sum_c X[i][c] * W_hat[r][c] for i < m, r < n: X fp16 [m][ldx] (16-byte aligned,
+ * ldx >= k and a multiple of 8 when m > 1), Y fp16 [m][ldy] (ldy >= n when m > 1). Batched
+ * decode: the weights are streamed once per launch and each decoded code meets all the
+ * launch's activation rows, up to 8 of them ("二三五六位量化" page section 1.2: decode
+ * batches and prefill are the same contraction with more activation rows; DBHOO-CIM page
+ * section 6: still bandwidth-bound at small batch). Larger m is served 8 rows per launch.
+ * Limits as dequant_gemv_*. m == 0 or n == 0 is a no-op; k == 0 writes zeros. Errors as dequant_gemv_*. */
+int dequant_gemm_q4g32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
+                       int64_t m, int64_t n, int64_t k, void *stream);
+int dequant_gemm_q2sb(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
+                      int64_t m, int64_t n, int64_t k, void *stream);
+int dequant_gemm_q3sb(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
+                      int64_t m, int64_t n, int64_t k, void *stream);
+int dequant_gemm_q5sb(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
+                      int64_t m, int64_t n, int64_t k, void *stream);
+int dequant_gemm_q6sb(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
+                      int64_t m, int64_t n, int64_t k, void *stream);
+/* Generic form; y_f32 != 0 writes fp32 Y (4-byte aligned). */
+int qg_gemm(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int64_t ldy, int y_f32,
+            int64_t m, int64_t n, int64_t k, void *stream);
 
 /* ---- decode to memory (device; for verification, not for inference) ----------------------
  * Writes W_hat as fp32 [n][k] to w_out (if non-NULL) and the integer codes as uint8 [n][k]

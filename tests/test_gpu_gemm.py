@@ -1,0 +1,165 @@
+"""GPU parity tests for the dequant GEMM with a few activation rows, against the oracle.
+
+Bar: every output Y[i, r] within 2e-3 * sum_k |X[i,k] W_hat[r,k]| (fp16 and fp32 output).
+Covers every row count the streaming kernels are built for (1, 2, 4 and 8 rows per launch,
+with the unused rows of a launch masked), more rows than one launch serves, strided X and Y,
+K split over several waves and over several passes, ragged n, and the full-size decode
+workloads with 2, 4 and 8 activation rows on sampled output rows.
+"""
+import numpy as np
+import pytest
+
+import dequant_gemv_q4g32_amd as qg
+from gpu_util import assert_close, device_weights, oracle_decode, oracle_y
+from workloads import WORKLOADS, activations, laplace_weights
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb"]
+MS = [1, 2, 3, 4, 5, 8, 11, 17]
+# (n, k): several row blocks and a ragged tail, K over 1..8 waves, and (5, 28672) over two
+# passes when eight rows share a launch
+SHAPES = [(37, 512), (1001, 1024), (20, 4352), (9, 8192), (5, 28672)]
+
+
+def _run(fmt, wd, x, n, k, out_f32, ldx=None, ldy=None):
+    m = x.shape[0]
+    ldx = ldx or k
+    ldy = ldy or n
+    xbuf = torch.zeros((m, ldx), dtype=torch.float16, device="cuda")
+    xbuf[:, :k] = torch.from_numpy(x).cuda()
+    ybuf = torch.full((m, ldy), 3.0, dtype=torch.float32 if out_f32 else torch.float16, device="cuda")
+    qg.gemm(fmt, wd, xbuf[:, :k], n, k, out=ybuf[:, :n])
+    torch.cuda.synchronize()
+    yb = ybuf.cpu().float().numpy()
+    assert np.all(yb[:, n:] == 3.0), "GEMM wrote outside Y[:, :n]"
+    return yb[:, :n]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n,k", SHAPES)
+def test_gemm_matches_oracle(fmt, n, k):
+    w = laplace_weights(n, k, 0.02, 17 * n + k, outlier_frac=0.001)
+    _, w_hat = oracle_decode(fmt, w)
+    wd = device_weights(fmt, w)
+    for m in MS:
+        x = activations(m, k, 5 * m + k)
+        y_ref, bound = oracle_y(w_hat, x)
+        y32 = _run(fmt, wd, x, n, k, True)
+        assert_close(y32, y_ref, bound, f"{fmt} m={m} {n}x{k} f32")
+        if m in (2, 8):
+            y16 = _run(fmt, wd, x, n, k, False)
+            assert_close(y16, y_ref, bound, f"{fmt} m={m} {n}x{k} f16")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_strided_x_and_y(fmt):
+    n, k = 70, 2048
+    w = laplace_weights(n, k, 0.02, 123)
+    _, w_hat = oracle_decode(fmt, w)
+    wd = device_weights(fmt, w)
+    for m in (2, 6):
+        x = activations(m, k, 44 + m)
+        y_ref, bound = oracle_y(w_hat, x)
+        y = _run(fmt, wd, x, n, k, True, ldx=k + 24, ldy=n + 5)
+        assert_close(y, y_ref, bound, f"{fmt} m={m} strided")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("m", [1, 2, 4, 8])
+def test_gemm_many_k_passes(fmt, m):
+    """K = 73728: 1152 units, more waves along K than one workgroup holds for every row count,
+    so partial sums are carried across passes in LDS."""
+    n, k = 3, 73728
+    w = laplace_weights(n, k, 0.02, 555 + m)
+    _, w_hat = oracle_decode(fmt, w)
+    x = activations(m, k, 77 + m)
+    y_ref, bound = oracle_y(w_hat, x)
+    y = _run(fmt, device_weights(fmt, w), x, n, k, True)
+    assert_close(y, y_ref, bound, f"{fmt} m={m} {n}x{k}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_q4g32_ragged_k(fmt):
+    """q4g32 with K an odd multiple of 32 (a half unit at the end), for every row count."""
+    if fmt != "q4g32":
+        pytest.skip("ragged K is a q4g32 case")
+    for n, k in ((7, 96), (9, 4128), (4, 160)):
+        w = laplace_weights(n, k, 0.02, k + 9)
+        _, w_hat = oracle_decode(fmt, w)
+        wd = device_weights(fmt, w)
+        for m in (1, 2, 3, 8):
+            x = activations(m, k, k + m)
+            y_ref, bound = oracle_y(w_hat, x)
+            assert_close(_run(fmt, wd, x, n, k, True), y_ref, bound, f"q4g32 m={m} {n}x{k}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_rows_are_independent(fmt):
+    """Row i of X = e_c for distinct columns c: each output row is one column of W_hat, so a
+    mixed-up activation row or output row shows as a wrong column."""
+    n, k = 24, 512
+    w = laplace_weights(n, k, 0.02, 321)
+    _, w_hat = oracle_decode(fmt, w)
+    wd = device_weights(fmt, w)
+    cols = np.array([5, 130, 257, 511, 0, 64, 300, 449])
+    x = np.zeros((8, k), np.float16)
+    x[np.arange(8), cols] = 1.0
+    y = _run(fmt, wd, x, n, k, True)
+    want = w_hat[:, cols].T
+    assert np.all(np.abs(y - want) <= 2e-3 * np.abs(want))
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_gemm_zero_and_empty(fmt):
+    n, k = 10, 1024
+    wd = device_weights(fmt, laplace_weights(n, k, 0.02, 5))
+    y = _run(fmt, wd, np.zeros((4, k), np.float16), n, k, True)
+    assert np.all(y == 0)
+    ybuf = torch.full((3, n), 7.0, dtype=torch.float16, device="cuda")
+    dummy = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    qg.gemm(fmt, dummy, torch.zeros((3, 8), dtype=torch.float16, device="cuda"), n, 0, out=ybuf)
+    assert torch.all(ybuf == 0).item()
+    ybuf.fill_(7.0)
+    qg.gemm(fmt, wd, torch.zeros((0, k), dtype=torch.float16, device="cuda"), n, k, out=ybuf[:0])
+    assert torch.all(ybuf == 7.0).item()
+
+
+def _sampled_rows(n, seed, count=32):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, n - 1], rng.choice(n, size=min(n, count), replace=False)]))
+
+
+def _full_cases():
+    """(format, shape index, [workload names]) for the decode-batch workloads, grouped so that
+    the workloads that share a weight matrix (same format, shapes and seed) upload it once."""
+    groups = {}
+    for name, wl in WORKLOADS.items():
+        if wl.m < 2 or wl.m > 8:
+            continue
+        for i in range(len(wl.shapes)):
+            groups.setdefault((wl.fmt, wl.shapes, wl.seed, i), []).append(name)
+    return [(key[0], key[3], names) for key, names in groups.items()]
+
+
+FULL = _full_cases()
+
+
+@pytest.mark.parametrize("fmt,i,names", FULL, ids=[f"{f}-{i}" for f, i, _ in FULL])
+def test_full_size_small_m_sampled_rows(fmt, i, names):
+    """Full-size decode-batch matrices with 2, 4 and 8 activation rows, in the launch
+    configuration the library uses for them; the oracle recomputes sampled output rows."""
+    wl0 = WORKLOADS[names[0]]
+    n, k = wl0.shapes[i]
+    w = wl0.weights(i)
+    wd = device_weights(fmt, w)
+    rows = _sampled_rows(n, i)
+    _, w_hat = oracle_decode(fmt, w[rows])
+    del w
+    for name in names:
+        x = WORKLOADS[name].x(i)
+        y = qg.gemm(fmt, wd, torch.from_numpy(x).cuda(), n, k)
+        y_ref, bound = oracle_y(w_hat, x)
+        torch.cuda.synchronize()
+        assert_close(y.cpu().float().numpy()[:, rows], y_ref, bound, f"{name}[{i}]")

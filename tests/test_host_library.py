@@ -146,7 +146,18 @@ def test_device_entry_points_validate_without_launching():
     assert L.qg_gemv(3, 256, 16, 3, 0, 4, 256, None) == -3                # y misaligned
     assert L.qg_gemv(3, 257, 16, 2, 0, 4, 256, None) == -3                # w misaligned
     assert L.qg_gemv(3, 256, 18, 2, 0, 4, 256, None) == -3                # x misaligned
-    assert L.qg_gemv(3, 256, 16, 2, 0, 4, 256 * 1025, None) == -2         # k too long
+    assert L.qg_gemv(3, 256, 16, 2, 0, 4, (1 << 20) + 256, None) == -2    # k too long
+    assert L.qg_gemv(4, 256, 16, 2, 0, (1 << 23) + 1, 1024, None) == -2   # 4 GiB code plane
     assert L.qg_dequantize(3, None, None, None, 4, 256, None) == -1
     assert L.qg_dequantize(5, 256, None, 16, 4, 100, None) == -2
     assert L.qg_gemv_batched(2, 256, 100, 16, 0, 2, 4, 0, 3, 4, 256, None) == -3   # w stride
+    # qg_gemm(fmt, w, X, ldx, Y, ldy, y_f32, m, n, k, stream)
+    assert L.qg_gemm(3, 256, 16, 256, 2, 4, 0, 0, 4, 256, None) == 0      # m == 0: no-op
+    assert L.qg_gemm(3, 256, 16, 256, 2, 4, 0, -1, 4, 256, None) == -2    # m < 0
+    assert L.qg_gemm(3, 256, 16, 128, 2, 4, 0, 2, 4, 256, None) == -2     # ldx < k
+    assert L.qg_gemm(3, 256, 16, 256, 2, 3, 0, 2, 4, 256, None) == -2     # ldy < n
+    assert L.qg_gemm(3, 256, 16, 260, 2, 4, 0, 2, 4, 256, None) == -3     # ldx % 8
+    assert L.qg_gemm(3, None, 16, 256, 2, 4, 0, 2, 4, 256, None) == -1    # null w
+    assert L.qg_gemm(5, 256, 16, 256, 2, 4, 0, 2, 4, 100, None) == -2     # k % 256
+    assert L.qg_gemm(8, 256, 16, 256, 2, 4, 0, 2, 4, 256, None) == -6     # format
+    assert L.dequant_gemm_q6sb(256, 16, 256, 3, 4, 2, 4, 256, None) == -3  # Y misaligned
