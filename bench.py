@@ -44,7 +44,42 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-single", action="store_true", help="skip the one-matrix-per-launch timing")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 512 MiB device copy (the reference kernel for HBM counters)")
     return ap.parse_args()
+
+
+SOURCES = ["dequant_gemv_q4g32_amd/csrc/gemv.hip", "dequant_gemv_q4g32_amd/csrc/units.h",
+           "dequant_gemv_q4g32_amd/csrc/device_common.h", "dequant_gemv_q4g32_amd/csrc/layout.h"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per launch of the timed kernel from the committed counter summary
+    (FETCH_SIZE and WRITE_SIZE per dispatch, each scaled by the same counter's reading for a
+    plain copy of known size), or None if there is none or the kernel sources changed since."""
+    path = os.path.join(ROOT, "profiles", f"hbm_traffic_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                key, val = line.split(":", 1)
+                kv[key.strip()] = val.strip()
+    if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    fetch = float(kv["fetch_kib_per_dispatch"]) * 1024 * float(kv["copy_fetch_factor"])
+    write = float(kv["write_kib_per_dispatch"]) * 1024 * float(kv["copy_write_factor"])
+    return fetch + write
 
 
 def cpu_baseline(fmt, canonical, n, k, x, seconds):
@@ -183,12 +218,23 @@ def main():
                   "us_per_gemv_graph": round(us_graph, 3), "GBps_graph": round(alg / us_graph / 1e3, 1)}
         log(f"[bench] single launch: stream {us_stream:.2f} us, graph {us_graph:.2f} us per GEMV")
 
+    if args.calibrate_copy:
+        # a plain device copy of known size: its FETCH_SIZE / WRITE_SIZE readings give the
+        # factors that turn those counters into bytes
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("[bench] ran 5 copies of 512 MiB for counter calibration")
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host ...")
         cpu = cpu_baseline(fmt, canonical, n, k, wl.x(0)[0], args.cpu_seconds)
         log(f"[bench] oracle: {cpu['value']} GB/s ({cpu['sample']})")
 
+    traffic = measured_traffic(args.workload)
     out = {
         "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
@@ -197,7 +243,8 @@ def main():
                    "fmt": fmt, "n": n, "k": k, "batch": 1, "matrices_per_launch": G,
                    "algorithmic_bytes_per_matrix": alg, "resident_GB": round(copies * stride / 1e9, 3)},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+                     "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic},
+        "algorithmic_bytes_per_launch": G * alg,
         "read_ceiling_GBps": round(ceiling, 1),
         "frac_of_read_ceiling": round(gbps / ceiling, 4),
         "single_launch": single,
