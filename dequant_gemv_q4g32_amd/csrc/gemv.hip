@@ -17,6 +17,7 @@
 
 #include "../../include/qgemv.h"
 #include "device_common.h"
+#include "launch.h"
 #include "layout.h"
 #include "units.h"
 
@@ -353,19 +354,6 @@ bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p
 
 thread_local hipError_t g_last_hip_error = hipSuccess;
 
-// hipLaunchKernel returns the launch status itself, so a stale error left in the runtime's
-// last-error slot by an unrelated earlier call cannot be mistaken for a failed launch.
-template <typename... KArgs, typename... Args>
-int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shm, hipStream_t s, Args... args) {
-  void *ptrs[] = {static_cast<void *>(&args)...};
-  hipError_t e = hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, ptrs, shm, s);
-  if (e != hipSuccess) {
-    g_last_hip_error = e;
-    return QG_ERR_LAUNCH;
-  }
-  return QG_OK;
-}
-
 namespace {
 
 constexpr int64_t kMaxK = int64_t(1) << 20;   // at most 64 K passes in every configuration
@@ -532,18 +520,15 @@ int qg_gemm(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int
   GemvArgs a{};
   int st = fill_args(fmt, w, n, k, a);
   if (st != QG_OK) return st;
+  // more rows than one streaming launch serves: LDS-staged fp16 tiles on the matrix cores
+  if (m > kMaxM) return launch_prefill(fmt, w, X, ldx, Y, ldy, y_f32, m, n, k, s);
+  a.x = X;
   a.ldx = ldx;
+  a.y = Y;
   a.ldy = ldy;
   a.y_f32 = y_f32;
-  // each launch serves up to kMaxM activation rows and streams the weights once
-  for (int64_t i0 = 0; i0 < m; i0 += kMaxM) {
-    a.x = X + i0 * ldx;
-    a.y = static_cast<char *>(Y) + i0 * ldy * esz;
-    a.m = m - i0 < kMaxM ? m - i0 : kMaxM;
-    st = launch_mv_fmt(fmt, a, 1, s);
-    if (st != QG_OK) return st;
-  }
-  return QG_OK;
+  a.m = m;
+  return launch_mv_fmt(fmt, a, 1, s);
 }
 
 int dequant_gemv_q4g32(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(4, w, x, y, 0, n, k, s); }

@@ -1,0 +1,198 @@
+// Dequant GEMM for prefill-sized m, gfx950: Y = X * W_hat^T with W_hat tiles dequantized to
+// fp16 in LDS and multiplied on the matrix cores (v_mfma_f32_32x32x16_f16, fp32 accumulate).
+//
+// Method: "二三五六位量化" page section 1.2 (prefill multiplies the same low-bit weights by
+// many activation rows, so the work is a dense contraction; the dequantized weights are fp16)
+// and DBHOO-CIM page section 6 (large batches become compute-bound). The codes are turned
+// into fp16 w_hat by the same per-format unit decode as the GEMV (units.h, `wide`), written
+// once per K step into an LDS tile that every wave of the workgroup reads.
+//
+// Tiling: a workgroup of 4 waves computes a 128 x 128 tile of Y (128 activation rows x 128
+// weight rows) and walks K in steps of one 64-weight unit. Each step, every thread loads
+// half a unit of one weight row and 64 bytes of one activation row (the loads for step u+1
+// are issued before the MFMAs of step u), decodes its half unit to 16 fp16 pairs and stores
+// both into LDS. Each wave then runs 2 x 2 MFMA tiles of 32 x 32 over the step's 4 K-slices
+// of 16. Workgroups are numbered so that the M tiles sharing a weight tile run on one XCD
+// and share its L2.
+#include <hip/hip_runtime.h>
+
+#include "../../include/qgemv.h"
+#include "device_common.h"
+#include "launch.h"
+#include "layout.h"
+#include "units.h"
+
+namespace qg {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+struct PrefillArgs {
+  const uint8_t *w;
+  int64_t poff[4];
+  int64_t prb[4];
+  int64_t n, k, units;
+  const uint16_t *x;
+  int64_t ldx;
+  void *y;
+  int64_t ldy;
+  int64_t m;
+  int y_f32;
+  int mtiles, ntiles, per_xcd;
+};
+
+constexpr int kBM = 128;                 // activation rows per workgroup tile
+constexpr int kBN = 128;                 // weight rows per workgroup tile
+constexpr int kLdsRow = kUnit + 8;       // halfs per LDS row: 64 + 8 of padding (bank spread)
+
+template <int F>
+__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+  using U = Unit<F>;
+  using Raw = typename U::Raw;
+  __shared__ __attribute__((aligned(16))) _Float16 xs[kBM * kLdsRow];
+  __shared__ __attribute__((aligned(16))) _Float16 ws[kBN * kLdsRow];
+
+  // Workgroups are dispatched round-robin over the 8 XCDs; tile numbers are assigned so that
+  // consecutive tiles (the M tiles of one weight tile) fall on the same XCD.
+  const int bid = blockIdx.x;
+  const int tile = (bid & 7) * a.per_xcd + (bid >> 3);
+  if (tile >= a.mtiles * a.ntiles) return;
+  const int mt = tile % a.mtiles, nt = tile / a.mtiles;
+  const int64_t m0 = (int64_t)mt * kBM, r0 = (int64_t)nt * kBN;
+
+  const int t = threadIdx.x;
+  const int lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int wm = wave & 1, wn = wave >> 1;         // this wave's 64 x 64 quarter of the tile
+
+  // loader role: LDS row t >> 1 of both tiles, half h = t & 1 of the unit
+  const int lrow = t >> 1, h = t & 1;
+  const int64_t wrow = r0 + lrow < a.n ? r0 + lrow : a.n - 1;   // rows past n are not stored
+  const bool xlive = m0 + lrow < a.m;
+  const uint16_t *xrow = a.x + (xlive ? m0 + lrow : 0) * a.ldx;
+
+  Lane L;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    L.rs[p] = make_rsrc(a.w + a.poff[p], (uint32_t)(a.prb[p] * a.n));
+    L.prb[p] = (uint32_t)a.prb[p];
+  }
+
+  Raw q;
+  u32x4 xv[4];
+  auto gload = [&](int64_t u) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) L.off[p] = 0;
+    U::offsets(u, L.off);
+    L.sh = fields_sh(u);
+    const bool half = (F == 4) && (u == a.units - 1) && (a.k % 64 != 0);
+    U::load(q, L, wrow, half);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t kk = u * kUnit + 32 * h + 8 * i;
+      xv[i] = (xlive && kk < a.k) ? ld4(reinterpret_cast<const uint8_t *>(xrow + kk)) : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto lds_store = [&]() {
+    uint32_t pr[16];
+    U::wide(q, h, pr);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      // local pairs 4i..4i+3 are the unit's consecutive pairs pidx(h, 4i).. (k = 2 * pair)
+      const int g = U::pidx(h, 4 * i, 2);
+      *reinterpret_cast<u32x4 *>(&ws[lrow * kLdsRow + 2 * g]) = u32x4{pr[4 * i], pr[4 * i + 1], pr[4 * i + 2], pr[4 * i + 3]};
+      *reinterpret_cast<u32x4 *>(&xs[lrow * kLdsRow + 32 * h + 8 * i]) = xv[i];
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+
+  gload(0);
+  lds_store();
+  __syncthreads();
+  const int arow = lane & 31, akoff = 8 * (lane >> 5);
+  for (int64_t u = 0; u < a.units; ++u) {
+    const bool more = u + 1 < a.units;
+    if (more) gload(u + 1);
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      half8_t A[2], B[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        A[i] = *reinterpret_cast<const half8_t *>(&xs[(wm * 64 + 32 * i + arow) * kLdsRow + 16 * s + akoff]);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        B[j] = *reinterpret_cast<const half8_t *>(&ws[(wn * 64 + 32 * j + arow) * kLdsRow + 16 * s + akoff]);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i], B[j], acc[i][j], 0, 0, 0);
+    }
+    __syncthreads();                   // every wave is done reading this step's tiles
+    if (more) {
+      lds_store();
+      __syncthreads();
+    }
+  }
+
+  // D of a 32 x 32 MFMA: lane l holds column l % 32 and rows 8 (e / 4) + 4 (l / 32) + e % 4
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t row = m0 + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int64_t col = r0 + wn * 64 + 32 * j + (lane & 31);
+        if (row < a.m && col < a.n) {
+          const int64_t idx = row * a.ldy + col;
+          if (a.y_f32) reinterpret_cast<float *>(a.y)[idx] = acc[i][j][e];
+          else reinterpret_cast<_Float16 *>(a.y)[idx] = (_Float16)acc[i][j][e];
+        }
+      }
+}
+
+int launch_prefill(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int64_t ldy, int y_f32,
+                   int64_t m, int64_t n, int64_t k, hipStream_t s) {
+  qg_layout lay;
+  int st = qg_device_layout(fmt, n, k, &lay);
+  if (st != QG_OK) return st;
+  PrefillArgs a{};
+  a.w = static_cast<const uint8_t *>(w);
+  for (int p = 0; p < 4; ++p) {
+    a.poff[p] = lay.plane_offset[p];
+    a.prb[p] = lay.plane_row_bytes[p];
+  }
+  a.n = n;
+  a.k = k;
+  a.units = (k + kUnit - 1) / kUnit;
+  a.x = X;
+  a.ldx = ldx;
+  a.y = Y;
+  a.ldy = ldy;
+  a.m = m;
+  a.y_f32 = y_f32;
+  const int64_t mtiles = (m + kBM - 1) / kBM, ntiles = (n + kBN - 1) / kBN;
+  const int64_t total = mtiles * ntiles;
+  if (total > (int64_t(1) << 30)) return QG_ERR_SHAPE;
+  a.mtiles = (int)mtiles;
+  a.ntiles = (int)ntiles;
+  a.per_xcd = (int)((total + 7) / 8);
+  const dim3 grid((unsigned)(8 * a.per_xcd)), block(256);
+  switch (fmt) {
+    case 2: return launch(prefill_kernel<2>, grid, block, 0, s, a);
+    case 3: return launch(prefill_kernel<3>, grid, block, 0, s, a);
+    case 4: return launch(prefill_kernel<4>, grid, block, 0, s, a);
+    case 5: return launch(prefill_kernel<5>, grid, block, 0, s, a);
+    case 6: return launch(prefill_kernel<6>, grid, block, 0, s, a);
+  }
+  return QG_ERR_FORMAT;
+}
+
+}  // namespace qg

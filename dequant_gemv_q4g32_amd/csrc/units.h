@@ -42,6 +42,24 @@ __device__ __forceinline__ uint32_t fields24(const Lane &L, int p, int64_t r) {
 
 __device__ __forceinline__ uint32_t sel(bool c, uint32_t a, uint32_t b) { return c ? a : b; }
 
+// ---- decode to fp16 weights (for the MFMA path): from a code pair P = (1024 + p*c_a,
+// 1024 + p*c_b) to the fp16 pair of w_hat.
+// Symmetric formats: w_hat = step * (c - o) = (P - (1024 + p*o)) * (step / p). The subtraction
+// is exact (small integers); the product is one fp16 rounding of a value whose factor step/p
+// was itself rounded to fp16 once.
+__device__ __forceinline__ uint32_t sym_pair(uint32_t P, _Float16 off, _Float16 mul) {
+  const h2_t v = __builtin_bit_cast(h2_t, P);
+  const h2_t o = {off, off}, m = {mul, mul};
+  return __builtin_bit_cast(uint32_t, (v + o) * m);
+}
+// Asymmetric formats: w_hat = step * c - off = P * (step / p) + add, add = -(1024 step / p + off),
+// in fp32 (so that the cancellation of 1024 * step / p is exact up to fp32 rounding of add),
+// then one rounding to fp16.
+__device__ __forceinline__ uint32_t asym_pair(uint32_t P, float mul, float add) {
+  const h2_t r = {(_Float16)__builtin_fmaf(half_lo(P), mul, add), (_Float16)__builtin_fmaf(half_hi(P), mul, add)};
+  return __builtin_bit_cast(uint32_t, r);
+}
+
 template <int F> struct Unit;
 
 // ---- INT4 group-32: a unit is two groups; with S = 2 a lane owns one group
@@ -103,6 +121,21 @@ template <> struct Unit<4> {
       }
 #pragma unroll
       for (int m = 0; m < M; ++m) out[m] = __builtin_fmaf(scale, __builtin_fmaf(a16[m], 0.0625f, a1[m]), out[m]);
+    }
+  }
+  // fp16 w_hat of the 16 pairs of half h (group h), in local pair order
+  __device__ static void wide(const Raw &q, int h, uint32_t *out) {
+    const u32x4 c = h ? q.c1 : q.c0;
+    const float scale = h ? q.s1 : q.s0;
+    const _Float16 m1 = (_Float16)scale, m16 = (_Float16)(scale * 0.0625f);
+    const uint32_t d[4] = {c.x, c.y, c.z, c.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t v = d[i], v8 = v >> 8;
+      out[4 * i + 0] = sym_pair(pick(v, QG_SMASK(0x000F000Fu)), (_Float16)-1032.0f, m1);
+      out[4 * i + 1] = sym_pair(pick(v, QG_SMASK(0x00F000F0u)), (_Float16)-1152.0f, m16);
+      out[4 * i + 2] = sym_pair(pick(v8, QG_SMASK(0x000F000Fu)), (_Float16)-1032.0f, m1);
+      out[4 * i + 3] = sym_pair(pick(v8, QG_SMASK(0x00F000F0u)), (_Float16)-1152.0f, m16);
     }
   }
 };
@@ -175,6 +208,27 @@ template <> struct Unit<2> {
         acc = __builtin_fmaf(-cj[j], kc[m][j], acc);
       }
       out[m] = acc;
+    }
+  }
+  // fp16 w_hat of the 16 pairs of half h (dwords 2h, 2h+1), in local pair order
+  __device__ static void wide(const Raw &q, int h, uint32_t *out) {
+    const uint32_t d[4] = {q.c.x, q.c.y, q.c.z, q.c.w};
+    const float inv4[4] = {1.0f, 0.25f, 0.0625f, 0.015625f};
+    const float dv = half_lo(q.dd), dm = half_hi(q.dd);
+    float mul[4], add[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      mul[j] = dv * (float)((q.sc >> (8 * j)) & 15u) * inv4[j];
+      add[j] = -__builtin_fmaf(1024.0f, mul[j], dm * (float)((q.sc >> (8 * j + 4)) & 15u));
+    }
+#pragma unroll
+    for (int ii = 0; ii < 2; ++ii) {
+      const uint32_t v = sel(h, d[2 + ii], d[ii]), v8 = v >> 8;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        out[4 * j + 2 * ii] = asym_pair(pick(v, QG_SMASK(0x00030003u << (2 * j))), mul[j], add[j]);
+        out[4 * j + 2 * ii + 1] = asym_pair(pick(v8, QG_SMASK(0x00030003u << (2 * j))), mul[j], add[j]);
+      }
     }
   }
 };
@@ -284,6 +338,24 @@ template <> struct Unit<3> {
       }
     }
   }
+  // fp16 w_hat of the 16 pairs of chunk h (sub-blocks a = 2h, b = 2h + 1 of the unit)
+  __device__ static void wide(const Raw &q, int h, uint32_t *out) {
+    uint32_t P[16];
+    chunk_pairs(sel(h, q.a.w, q.a.x), sel(h, q.b.x, q.a.y), sel(h, q.b.y, q.a.z), P);
+    const uint32_t fh = q.f >> (12 * h);
+    const float dv = half_bits(q.d);
+    const float sa = dv * (float)(fh & 63u), sb = dv * (float)((fh >> 6) & 63u);
+    const _Float16 a1 = (_Float16)sa, a8 = (_Float16)(sa * 0.125f);
+    const _Float16 b8 = (_Float16)(sb * 0.125f), b64 = (_Float16)(sb * 0.015625f);
+#pragma unroll
+    for (int r = 0; r < 6; ++r) out[r] = sym_pair(P[r], (_Float16)-1028.0f, a1);
+    out[6] = sym_pair(P[6], (_Float16)-1056.0f, a8);
+    out[7] = sym_pair(P[7], (_Float16)-1056.0f, a8);
+#pragma unroll
+    for (int r = 8; r < 12; ++r) out[r] = sym_pair(P[r], (_Float16)-1056.0f, b8);
+#pragma unroll
+    for (int r = 12; r < 16; ++r) out[r] = sym_pair(P[r], (_Float16)-1280.0f, b64);
+  }
 };
 
 // ---- nibble plane + high-bit plane (q5sb: 1 high bit, 32-weight sub-blocks;
@@ -369,6 +441,24 @@ template <> struct Unit<5> {
       }
     }
   }
+  // fp16 w_hat of the 16 pairs of half h (sub-block h of the unit)
+  __device__ static void wide(const Raw &q, int h, uint32_t *out) {
+    const uint32_t L[8] = {q.l0.x, q.l0.y, q.l0.z, q.l0.w, q.l1.x, q.l1.y, q.l1.z, q.l1.w};
+    const uint32_t H = sel(h, q.h.y, q.h.x);
+    const float dv = half_lo(q.dd), dm = half_hi(q.dd);
+    const float step = dv * (float)((q.f >> (6 * h)) & 63u), off = dm * (float)((q.f >> (12 + 6 * h)) & 63u);
+    const float mul1 = step, add1 = -__builtin_fmaf(1024.0f, step, off);
+    const float mul16 = step * 0.0625f, add16 = -__builtin_fmaf(64.0f, step, off);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t P[4];
+      nib_pairs<1>(sel(h, L[4 + i], L[i]), H, i, P);
+      out[4 * i + 0] = asym_pair(P[0], mul1, add1);
+      out[4 * i + 1] = asym_pair(P[1], mul16, add16);
+      out[4 * i + 2] = asym_pair(P[2], mul1, add1);
+      out[4 * i + 3] = asym_pair(P[3], mul16, add16);
+    }
+  }
 };
 
 // ---- 6-bit super-block: a unit is four sub-blocks of 16; with S = 2 lane half h owns
@@ -431,6 +521,27 @@ template <> struct Unit<6> {
       const float sj = (float)(int8_t)((q.sc >> (8 * jj)) & 0xFFu);
 #pragma unroll
       for (int m = 0; m < M; ++m) out[m] = __builtin_fmaf(dv * sj, __builtin_fmaf(a16[m], 0.0625f, a1[m]), out[m]);
+    }
+  }
+  // fp16 w_hat of the 16 pairs of half h (sub-blocks 2h, 2h + 1 of the unit)
+  __device__ static void wide(const Raw &q, int h, uint32_t *out) {
+    const uint32_t L[8] = {q.l0.x, q.l0.y, q.l0.z, q.l0.w, q.l1.x, q.l1.y, q.l1.z, q.l1.w};
+    const uint32_t Hd[4] = {q.h.x, q.h.y, q.h.z, q.h.w};
+    const float dv = half_bits(q.d);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const float step = dv * (float)(int8_t)((q.sc >> (8 * (2 * h + j))) & 0xFFu);
+      const _Float16 m1 = (_Float16)step, m16 = (_Float16)(step * 0.0625f);
+      const uint32_t H = sel(h, Hd[2 + j], Hd[j]);
+#pragma unroll
+      for (int ii = 0; ii < 2; ++ii) {
+        uint32_t P[4];
+        nib_pairs<2>(sel(h, L[4 + 2 * j + ii], L[2 * j + ii]), H, ii, P);
+        out[8 * j + 4 * ii + 0] = sym_pair(P[0], (_Float16)-1056.0f, m1);
+        out[8 * j + 4 * ii + 1] = sym_pair(P[1], (_Float16)-1536.0f, m16);
+        out[8 * j + 4 * ii + 2] = sym_pair(P[2], (_Float16)-1056.0f, m1);
+        out[8 * j + 4 * ii + 3] = sym_pair(P[3], (_Float16)-1536.0f, m16);
+      }
     }
   }
 };

@@ -1,0 +1,112 @@
+"""GPU parity tests for the prefill dequant GEMM (m > 8: fp16 tiles in LDS, MFMA), against
+the oracle.
+
+Bar: every output Y[i, r] within 2e-3 * sum_k |X[i,k] W_hat[r,k]|. The fp16 dequantized
+weights carry at most two fp16 roundings (about 1e-3 of |w_hat|), inside that bound.
+Covers m not a multiple of the 128-row tile, n not a multiple of the 128-row weight tile,
+K over one and many steps, ragged q4g32 K, strided X and Y, fp16 and fp32 output, and the
+full-size 512 x 11008 x 4096 prefill workloads on sampled weight rows.
+"""
+import numpy as np
+import pytest
+
+import dequant_gemv_q4g32_amd as qg
+from gpu_util import assert_close, device_weights, oracle_decode, oracle_y
+from workloads import WORKLOADS, activations, laplace_weights
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb"]
+SHAPES = [(37, 256), (300, 1024), (130, 4352)]
+MS = [9, 64, 128, 200]
+
+
+def _run(fmt, wd, x, n, k, out_f32, ldx=None, ldy=None):
+    m = x.shape[0]
+    ldx = ldx or k
+    ldy = ldy or n
+    xbuf = torch.zeros((m, ldx), dtype=torch.float16, device="cuda")
+    xbuf[:, :k] = torch.from_numpy(x).cuda()
+    ybuf = torch.full((m, ldy), 3.0, dtype=torch.float32 if out_f32 else torch.float16, device="cuda")
+    qg.gemm(fmt, wd, xbuf[:, :k], n, k, out=ybuf[:, :n])
+    torch.cuda.synchronize()
+    yb = ybuf.cpu().float().numpy()
+    assert np.all(yb[:, n:] == 3.0), "GEMM wrote outside Y[:, :n]"
+    return yb[:, :n]
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("n,k", SHAPES)
+def test_prefill_matches_oracle(fmt, n, k):
+    w = laplace_weights(n, k, 0.02, 13 * n + k, outlier_frac=0.001)
+    _, w_hat = oracle_decode(fmt, w)
+    wd = device_weights(fmt, w)
+    for m in MS:
+        x = activations(m, k, 3 * m + k)
+        y_ref, bound = oracle_y(w_hat, x)
+        assert_close(_run(fmt, wd, x, n, k, True), y_ref, bound, f"{fmt} m={m} {n}x{k} f32")
+        if m == 200:
+            assert_close(_run(fmt, wd, x, n, k, False), y_ref, bound, f"{fmt} m={m} {n}x{k} f16")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_prefill_strided(fmt):
+    n, k, m = 150, 512, 70
+    w = laplace_weights(n, k, 0.02, 4242)
+    _, w_hat = oracle_decode(fmt, w)
+    x = activations(m, k, 11)
+    y_ref, bound = oracle_y(w_hat, x)
+    y = _run(fmt, device_weights(fmt, w), x, n, k, True, ldx=k + 40, ldy=n + 3)
+    assert_close(y, y_ref, bound, f"{fmt} strided")
+
+
+def test_prefill_q4g32_ragged_k():
+    for n, k in ((40, 96), (130, 4128)):
+        w = laplace_weights(n, k, 0.02, k + 5)
+        _, w_hat = oracle_decode("q4g32", w)
+        x = activations(33, k, k)
+        y_ref, bound = oracle_y(w_hat, x)
+        assert_close(_run("q4g32", device_weights("q4g32", w), x, n, k, True), y_ref, bound, f"q4g32 {n}x{k}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_prefill_one_hot_rows(fmt):
+    """X rows are unit vectors e_c: output row i is column c_i of W_hat, which pins where every
+    decoded weight lands in the LDS tile and in the MFMA operands."""
+    n, k = 136, 256
+    w = laplace_weights(n, k, 0.02, 77)
+    _, w_hat = oracle_decode(fmt, w)
+    m = 40
+    cols = (np.arange(m) * 37 + 3) % k
+    x = np.zeros((m, k), np.float16)
+    x[np.arange(m), cols] = 1.0
+    y = _run(fmt, device_weights(fmt, w), x, n, k, True)
+    want = w_hat[:, cols].T
+    # one fp16 rounding of the dequantized weight (and of step / p for symmetric formats); the
+    # absolute term covers the fp32 rounding of an asymmetric weight whose two parts cancel
+    tol = 1.2e-3 * np.abs(want) + 1e-6
+    assert np.all(np.abs(y - want) <= tol), np.argwhere(np.abs(y - want) > tol)[:5]
+
+
+def _prefill_cases():
+    return [name for name, wl in WORKLOADS.items() if wl.m > 8]
+
+
+@pytest.mark.parametrize("name", _prefill_cases())
+def test_full_size_prefill_sampled_rows(name):
+    """The full prefill shape (512 x 4096 activations, 11008 x 4096 weights) in the launch
+    configuration the library uses for it; the oracle recomputes sampled weight rows (output
+    columns) for all 512 activation rows."""
+    wl = WORKLOADS[name]
+    n, k = wl.shapes[0]
+    w = wl.weights(0)
+    x = wl.x(0)
+    wd = device_weights(wl.fmt, w)
+    y = qg.gemm(wl.fmt, wd, torch.from_numpy(x).cuda(), n, k)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([[0, 127, 128, n - 1], rng.choice(n, 28, replace=False)]))
+    _, w_hat = oracle_decode(wl.fmt, w[rows])
+    y_ref, bound = oracle_y(w_hat, x)
+    torch.cuda.synchronize()
+    assert_close(y.cpu().float().numpy()[:, rows], y_ref, bound, name)
