@@ -86,6 +86,10 @@ __device__ __forceinline__ rsrc_t make_rsrc(const void *p, uint32_t bytes) {
 __device__ __forceinline__ u32x4 bld4(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, kNT));
 }
+// cached 128-bit load; an offset past the resource's range returns zeros
+__device__ __forceinline__ u32x4 bld4c(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0));
+}
 __device__ __forceinline__ u32x2 bld2(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kNT));
 }

@@ -9,9 +9,9 @@
 //
 // Tiling: a workgroup of 4 waves computes a 128 x 128 tile of Y (128 activation rows x 128
 // weight rows) and walks K in steps of one 64-weight unit. Each step, every thread loads
-// half a unit of one weight row and 64 bytes of one activation row (the loads for step u+1
-// are issued before the MFMAs of step u), decodes its half unit to 16 fp16 pairs and stores
-// both into LDS. Each wave then runs 2 x 2 MFMA tiles of 32 x 32 over the step's 4 K-slices
+// half a unit of one weight row and 64 bytes of one activation row (two steps ahead, into
+// one of two register stages), decodes its half unit to 16 fp16 pairs and stores both into
+// one of two LDS buffers. Each wave then runs 2 x 2 MFMA tiles of 32 x 32 over the step's 4 K-slices
 // of 16. Workgroups are numbered so that the M tiles sharing a weight tile run on one XCD
 // and share its L2.
 #include <hip/hip_runtime.h>
@@ -44,20 +44,26 @@ struct PrefillArgs {
 constexpr int kBM = 128;                 // activation rows per workgroup tile
 constexpr int kBN = 128;                 // weight rows per workgroup tile
 constexpr int kLdsRow = kUnit + 8;       // halfs per LDS row: 64 + 8 of padding (bank spread)
+constexpr uint32_t kXRange = 0x7FFFFFF0u; // activation buffer range; offsets at or past it read 0
 
 template <int F>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   using U = Unit<F>;
   using Raw = typename U::Raw;
-  __shared__ __attribute__((aligned(16))) _Float16 xs[kBM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) _Float16 ws[kBN * kLdsRow];
+  // two LDS buffers per operand: the MFMAs of step u read one while step u+1 is stored into
+  // the other, so one barrier per step suffices
+  __shared__ __attribute__((aligned(16))) _Float16 xs[2][kBM * kLdsRow];
+  __shared__ __attribute__((aligned(16))) _Float16 ws[2][kBN * kLdsRow];
 
   // Workgroups are dispatched round-robin over the 8 XCDs; tile numbers are assigned so that
   // consecutive tiles (the M tiles of one weight tile) fall on the same XCD.
   const int bid = blockIdx.x;
   const int tile = (bid & 7) * a.per_xcd + (bid >> 3);
   if (tile >= a.mtiles * a.ntiles) return;
-  const int mt = tile % a.mtiles, nt = tile / a.mtiles;
+  // (integer division runs on the vector unit; readfirstlane keeps the tile indices scalar,
+  // so that the buffer resources built from them stay in scalar registers)
+  const int mt = __builtin_amdgcn_readfirstlane(tile % a.mtiles);
+  const int nt = __builtin_amdgcn_readfirstlane(tile / a.mtiles);
   const int64_t m0 = (int64_t)mt * kBM, r0 = (int64_t)nt * kBN;
 
   const int t = threadIdx.x;
@@ -69,7 +75,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int lrow = t >> 1, h = t & 1;
   const int64_t wrow = r0 + lrow < a.n ? r0 + lrow : a.n - 1;   // rows past n are not stored
   const bool xlive = m0 + lrow < a.m;
-  const uint16_t *xrow = a.x + (xlive ? m0 + lrow : 0) * a.ldx;
+  // activations through a buffer resource based at this tile's first row: a dead row or the
+  // missing half of a ragged q4g32 unit gets an offset past the range, which loads zeros (a
+  // select on the loaded data instead would make every step wait for its own loads)
+  const rsrc_t xr = make_rsrc(a.x + m0 * a.ldx, kXRange);
+  const uint32_t xrow_off = (uint32_t)(lrow * a.ldx * 2);
 
   Lane L;
 #pragma unroll
@@ -78,30 +88,38 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     L.prb[p] = (uint32_t)a.prb[p];
   }
 
-  Raw q;
-  u32x4 xv[4];
-  auto gload = [&](int64_t u) {
+  // Global loads of step u into one register stage. Steps past the end re-load the last
+  // step, so that every step issues the same loads and waits only for the older stage.
+  auto gload = [&](Raw &q, u32x4 *xv, int64_t u) {
+    u = u < a.units ? u : a.units - 1;
 #pragma unroll
     for (int p = 0; p < 4; ++p) L.off[p] = 0;
     U::offsets(u, L.off);
     L.sh = fields_sh(u);
+    // the weight row differs per lane here, so it goes into the per-lane offset (a row in
+    // the scalar offset would force one load per distinct row)
+#pragma unroll
+    for (int p = 0; p < 4; ++p) L.off[p] += (uint32_t)wrow * L.prb[p];
     const bool half = (F == 4) && (u == a.units - 1) && (a.k % 64 != 0);
-    U::load(q, L, wrow, half);
+    U::load(q, L, 0, half);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int64_t kk = u * kUnit + 32 * h + 8 * i;
-      xv[i] = (xlive && kk < a.k) ? ld4(reinterpret_cast<const uint8_t *>(xrow + kk)) : u32x4{0u, 0u, 0u, 0u};
+      const bool ok = xlive && kk < a.k;
+      xv[i] = bld4c(xr, ok ? xrow_off + (uint32_t)(kk * 2) : kXRange, 0);
     }
   };
-  auto lds_store = [&]() {
+  // decode a register stage to fp16 and store it, with its activations, into LDS buffer b
+  auto lds_store = [&](const Raw &q, const u32x4 *xv, int b) {
     uint32_t pr[16];
     U::wide(q, h, pr);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       // local pairs 4i..4i+3 are the unit's consecutive pairs pidx(h, 4i).. (k = 2 * pair)
       const int g = U::pidx(h, 4 * i, 2);
-      *reinterpret_cast<u32x4 *>(&ws[lrow * kLdsRow + 2 * g]) = u32x4{pr[4 * i], pr[4 * i + 1], pr[4 * i + 2], pr[4 * i + 3]};
-      *reinterpret_cast<u32x4 *>(&xs[lrow * kLdsRow + 32 * h + 8 * i]) = xv[i];
+      *reinterpret_cast<u32x4 *>(&ws[b][lrow * kLdsRow + 2 * g]) =
+          u32x4{pr[4 * i], pr[4 * i + 1], pr[4 * i + 2], pr[4 * i + 3]};
+      *reinterpret_cast<u32x4 *>(&xs[b][lrow * kLdsRow + 32 * h + 8 * i]) = xv[i];
     }
   };
 
@@ -113,33 +131,46 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-  gload(0);
-  lds_store();
-  __syncthreads();
   const int arow = lane & 31, akoff = 8 * (lane >> 5);
-  for (int64_t u = 0; u < a.units; ++u) {
-    const bool more = u + 1 < a.units;
-    if (more) gload(u + 1);
+  auto mfma_step = [&](int b) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       half8_t A[2], B[2];
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        A[i] = *reinterpret_cast<const half8_t *>(&xs[(wm * 64 + 32 * i + arow) * kLdsRow + 16 * s + akoff]);
+        A[i] = *reinterpret_cast<const half8_t *>(&xs[b][(wm * 64 + 32 * i + arow) * kLdsRow + 16 * s + akoff]);
 #pragma unroll
       for (int j = 0; j < 2; ++j)
-        B[j] = *reinterpret_cast<const half8_t *>(&ws[(wn * 64 + 32 * j + arow) * kLdsRow + 16 * s + akoff]);
+        B[j] = *reinterpret_cast<const half8_t *>(&ws[b][(wn * 64 + 32 * j + arow) * kLdsRow + 16 * s + akoff]);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i], B[j], acc[i][j], 0, 0, 0);
     }
-    __syncthreads();                   // every wave is done reading this step's tiles
-    if (more) {
-      lds_store();
-      __syncthreads();
-    }
+  };
+
+  // Pipeline: at step u, LDS buffer u & 1 holds step u, one register stage holds step u + 1
+  // (loaded during step u - 1) and the other is free, so it receives the loads of step u + 2.
+  Raw q0, q1;
+  u32x4 x0[4], x1[4];
+  gload(q0, x0, 0);
+  gload(q1, x1, 1);
+  lds_store(q0, x0, 0);
+  __syncthreads();
+  // No branches inside a step: past the last step the stage and LDS buffer written are never
+  // read. Two steps per iteration keep the stages in fixed registers.
+  auto body = [&](Raw &ql, u32x4 *xl, const Raw &qs, const u32x4 *xs_, int b, int64_t u) {
+    gload(ql, xl, u + 2);
+    mfma_step(b);
+    lds_store(qs, xs_, b ^ 1);
+    __syncthreads();
+  };
+  int64_t u = 0;
+  for (; u + 2 <= a.units; u += 2) {
+    body(q0, x0, q1, x1, 0, u);
+    body(q1, x1, q0, x0, 1, u + 1);
   }
+  if (u < a.units) body(q0, x0, q1, x1, 0, u);
 
   // D of a 32 x 32 MFMA: lane l holds column l % 32 and rows 8 (e / 4) + 4 (l / 32) + e % 4
 #pragma unroll
@@ -178,6 +209,7 @@ int launch_prefill(int fmt, const void *w, const uint16_t *X, int64_t ldx, void 
   a.ldy = ldy;
   a.m = m;
   a.y_f32 = y_f32;
+  if (kBM * ldx * 2 >= (int64_t)kXRange) return QG_ERR_SHAPE;     // 32-bit activation offsets
   const int64_t mtiles = (m + kBM - 1) / kBM, ntiles = (n + kBN - 1) / kBN;
   const int64_t total = mtiles * ntiles;
   if (total > (int64_t(1) << 30)) return QG_ERR_SHAPE;
