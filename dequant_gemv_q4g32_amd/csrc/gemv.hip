@@ -48,8 +48,20 @@ struct GemvArgs {
 // GEMV), S lanes per 64-weight unit (1, or 2 to halve the activation registers when M is
 // large), R rows per pipelined batch, MP more than one pass over K.
 
+#ifndef QG_GEMV_DEPTH
+#define QG_GEMV_DEPTH 2
+#endif
+#ifndef QG_MV_THREADS
+#define QG_MV_THREADS 1024
+#endif
+
+// Largest workgroup of the streaming kernels: it bounds their registers (a workgroup must fit
+// on the 4 SIMDs of one CU) and the waves along K of one pass.
+template <int M> constexpr int mv_threads() { return M > 4 && QG_MV_THREADS > 512 ? 512 : QG_MV_THREADS; }
+
 template <int F, int M, int S, int R, bool MP>
-__global__ __launch_bounds__(M > 4 ? 512 : 1024) void mv_kernel(GemvArgs a) {
+__global__ __launch_bounds__(mv_threads<M>()) void mv_kernel(GemvArgs a) {
+  constexpr int D = M == 1 ? QG_GEMV_DEPTH : 2;   // pipeline stages
   using U = Unit<F>;
   using Raw = typename U::Raw;
   static_assert(R == 1 || R == 2, "rows per batch");
@@ -76,7 +88,18 @@ __global__ __launch_bounds__(M > 4 ? 512 : 1024) void mv_kernel(GemvArgs a) {
 
   // this row group's rows: nb consecutive batches of R rows; rows past n re-read row n-1
   const int rows_here = R * a.nb;
+#ifndef QG_ROW_INTERLEAVE
+#define QG_ROW_INTERLEAVE 0
+#endif
+#if QG_ROW_INTERLEAVE
+  // batch j of row group g covers rows (j G + g) R .. + R - 1 (G row groups in the grid): the
+  // row groups walk the matrix side by side, so concurrent loads stay close together
+  const int64_t grp = (int64_t)blockIdx.x * a.wr + wr, ngrp = (int64_t)gridDim.x * a.wr;
+  auto row_of = [&](int j, int i) -> int64_t { return ((int64_t)j * ngrp + grp) * R + i; };
+#else
   const int64_t row_begin = ((int64_t)blockIdx.x * a.wr + wr) * rows_here;
+  auto row_of = [&](int j, int i) -> int64_t { return row_begin + (int64_t)j * R + i; };
+#endif
   auto store_y = [&](int mm, int64_t r, float v) {
     const int64_t i = b * a.y_bstride + (int64_t)mm * a.ldy + r;
     if (a.y_f32) reinterpret_cast<float *>(a.y)[i] = v;
@@ -95,13 +118,18 @@ __global__ __launch_bounds__(M > 4 ? 512 : 1024) void mv_kernel(GemvArgs a) {
     for (int p = 0; p < 4; ++p) L.off[p] = 0;
     U::offsets(u, L.off);
     L.sh = fields_sh(u);
+    L.set_halves(a.units);
 
     auto load_batch = [&](Raw *q, int64_t r0) {
 #pragma unroll
       for (int i = 0; i < R; ++i) U::load(q[i], L, r0 + i < a.n ? r0 + i : a.n - 1, half);
     };
-    Raw qa[R], qb[R];
-    load_batch(qa, row_begin);                 // weights first: their latency covers the x work
+    // D register stages: the loads of D - 1 batches are in flight while one is computed.
+    // Prefetches past this row group's last batch re-load that batch (no extra HBM traffic).
+    Raw qs[D][R];
+    auto load_batch_j = [&](Raw *q, int jb) { load_batch(q, row_of(jb < a.nb ? jb : a.nb - 1, 0)); };
+#pragma unroll
+    for (int d = 0; d + 1 < D; ++d) load_batch_j(qs[d], d);   // weights first: their latency covers the x work
 
     // The lane's activation pairs, 16 bytes (4 pairs) at a time: local pairs 4i..4i+3 are the
     // unit's pairs pidx(h, 4i).. (consecutive), i.e. bytes 4 * pidx(h, 4i) of its 128.
@@ -129,7 +157,7 @@ __global__ __launch_bounds__(M > 4 ? 512 : 1024) void mv_kernel(GemvArgs a) {
     for (int mm = 0; mm < M; ++mm) U::template prep<S>(xp[mm], kc[mm]);
 
     auto finish_batch = [&](const Raw *q, int j) {
-      const int64_t r0 = row_begin + (int64_t)j * R;
+      const int64_t r0 = row_of(j, 0);
       float part[R][M];
 #pragma unroll
       for (int i = 0; i < R; ++i) {
@@ -156,22 +184,16 @@ __global__ __launch_bounds__(M > 4 ? 512 : 1024) void mv_kernel(GemvArgs a) {
       }
     };
 
-    // Software pipeline: the next batch's loads are in flight while this one is computed.
-    // Loads inside the steady-state loop are unconditional, so the wait before each compute
-    // covers only the older batch (a conditional prefetch would force a wait for everything).
-    int j = 0;
-    for (; j + 2 < a.nb; j += 2) {
-      load_batch(qb, row_begin + (int64_t)(j + 1) * R);
-      finish_batch(qa, j);
-      load_batch(qa, row_begin + (int64_t)(j + 2) * R);
-      finish_batch(qb, j + 1);
-    }
-    if (j + 1 < a.nb) {
-      load_batch(qb, row_begin + (int64_t)(j + 1) * R);
-      finish_batch(qa, j);
-      finish_batch(qb, j + 1);
-    } else {
-      finish_batch(qa, j);
+    // Software pipeline, D batches per iteration so that every stage stays in fixed registers.
+    // Loads are unconditional, so the wait before each compute covers only the oldest stage
+    // (a conditional prefetch would force a wait for everything in flight).
+    for (int j = 0; j < a.nb; j += D) {
+#pragma unroll
+      for (int d = 0; d < D; ++d) {
+        if (j + d >= a.nb) break;
+        load_batch_j(qs[(d + D - 1) % D], j + d + D - 1);
+        finish_batch(qs[d], j + d);
+      }
     }
   }
   if (a.wk == 1) return;
@@ -180,7 +202,7 @@ __global__ __launch_bounds__(M > 4 ? 512 : 1024) void mv_kernel(GemvArgs a) {
   __syncthreads();
   if (wk == 0) {
     for (int i = lane; i < rows_here * M; i += 64) {
-      const int64_t r = row_begin + i / M;
+      const int64_t r = row_of(i / M / R, i / M % R);
       const int mm = i % M;
       float sum = 0.f;
       for (int jj = 0; jj < a.wk; ++jj) sum += red[(wr * rows_here * M + i) * a.wk + jj];
@@ -226,14 +248,14 @@ __device__ void decode_unit(const GemvArgs &a, const uint8_t *w, int64_t r, int6
   uint8_t c[64];
   float step[4] = {0, 0, 0, 0}, off[4] = {0, 0, 0, 0};
   if (F == 4) {
-    const uint8_t *pc = w + a.poff[0] + r * a.prb[0] + u * 32;
-    const uint8_t *ps = w + a.poff[1] + r * a.prb[1] + u * 8;
+    const uint8_t *pc = w + a.poff[0] + r * a.prb[0];
+    const uint8_t *ps = w + a.poff[1] + r * a.prb[1];
     for (int i = 0; i < 8; ++i) {
-      uint32_t v = (i < 4 || nvalid > 32) ? ld1(pc + 4 * i) : 0u;
+      uint32_t v = (i < 4 || nvalid > 32) ? ld1(pc + split_off(a.units, u, i >> 2, 16) + 4 * (i & 3)) : 0u;
       for (int e = 0; e < 8; ++e) c[8 * i + e] = (v >> (4 * ((e >> 1) + 4 * (e & 1)))) & 15u;
     }
-    float s0 = __builtin_bit_cast(float, ld1(ps));
-    float s1 = nvalid > 32 ? __builtin_bit_cast(float, ld1(ps + 4)) : 0.f;
+    float s0 = __builtin_bit_cast(float, ld1(ps + split_off(a.units, u, 0, 4)));
+    float s1 = nvalid > 32 ? __builtin_bit_cast(float, ld1(ps + split_off(a.units, u, 1, 4))) : 0.f;
     for (int i = 0; i < nvalid; ++i) {
       codes[i] = c[i];
       vals[i] = (float)((int)c[i] - 8) * (i < 32 ? s0 : s1);
@@ -292,9 +314,9 @@ __device__ void decode_unit(const GemvArgs &a, const uint8_t *w, int64_t r, int6
     return;
   }
   // q5sb / q6sb
-  const uint8_t *pl = w + a.poff[0] + r * a.prb[0] + u * 32;
+  const uint8_t *pl = w + a.poff[0] + r * a.prb[0];
   uint32_t L[8], H[4];
-  for (int i = 0; i < 8; ++i) L[i] = ld1(pl + 4 * i);
+  for (int i = 0; i < 8; ++i) L[i] = ld1(pl + split_off(a.units, u, i >> 2, 16) + 4 * (i & 3));
   const int hbytes = F == 5 ? 8 : 16;
   const uint8_t *ph = w + a.poff[1] + r * a.prb[1] + u * hbytes;
   for (int i = 0; i < hbytes / 4; ++i) H[i] = ld1(ph + 4 * i);
@@ -375,7 +397,6 @@ int fill_args(int fmt, const void *w, int64_t n, int64_t k, GemvArgs &a) {
   return QG_OK;
 }
 
-constexpr int kMaxWk = 16;                 // waves along K in one workgroup (1024 threads)
 constexpr int64_t kSimds = 1024;           // 256 CUs x 4 SIMDs
 constexpr int kMaxBatches = 32;
 constexpr int kMaxM = 8;                   // activation rows one streaming launch serves
@@ -410,7 +431,7 @@ int launch_mv(GemvArgs a, int64_t count, hipStream_t s) {
 template <int F, int M, int S>
 int launch_mv_s(GemvArgs a, int64_t count, hipStream_t s) {
   constexpr int UPW = 64 / S;
-  constexpr int max_wk = M > 4 ? kMaxWk / 2 : kMaxWk;        // the kernel's block-size bound
+  constexpr int max_wk = mv_threads<M>() / 64;                // the kernel's block-size bound
   const int64_t waves_k = (a.units + UPW - 1) / UPW;
   const int64_t passes = (waves_k + max_wk - 1) / max_wk;
   if (passes > 64) return QG_ERR_SHAPE;
@@ -419,7 +440,10 @@ int launch_mv_s(GemvArgs a, int64_t count, hipStream_t s) {
   a.wk = wk;
   a.wr = wk >= 4 ? 1 : 4 / wk;
   if (passes > 1) return launch_mv<F, M, S, 1, true>(a, count, s);
-  if constexpr (M <= 2) {
+#ifndef QG_GEMV_R2
+#define QG_GEMV_R2 1
+#endif
+  if constexpr (M <= 2 && QG_GEMV_R2) {
     const int64_t rows = a.n * count, target = kSimds * 4 / wk;
     if (rows >= 2 * target) return launch_mv<F, M, S, 2, false>(a, count, s);
   }

@@ -310,14 +310,16 @@ void row_to_device(int fmt, const uint8_t *canon, int64_t k, int64_t r, int64_t 
     const uint8_t *cr = canon + r * (k / 2);
     for (int64_t i = 0; i < k; ++i) codes[(size_t)i] = (cr[i >> 1] >> (4 * (i & 1))) & 15;
     const uint8_t *sr = canon + n * (k / 2) + r * (k / 32) * 4;
-    std::memcpy(P.p[1] + r * P.rb[1], sr, (size_t)((k / 32) * 4));
+    uint8_t *ds = P.p[1] + r * P.rb[1];
+    for (int64_t g = 0; g < k / 32; ++g)             // group 2u + h -> half h of unit u
+      std::memcpy(ds + split_off(units, g >> 1, (int)(g & 1), 4), sr + g * 4, 4);
     uint8_t *dst = P.p[0] + r * P.rb[0];
     for (int64_t u = 0; u < units; ++u) {
       uint32_t wv[8] = {0};
       for (int kk = 0; kk < kUnit; ++kk)
         for (int b = 0; b < 4; ++b) setbit(wv, code_pos(4, kk, b), (codes[(size_t)(u * kUnit + kk)] >> b) & 1u);
-      int64_t nbytes = std::min<int64_t>(32, k / 2 - u * 32);
-      std::memcpy(dst + u * 32, wv, (size_t)nbytes);
+      std::memcpy(dst + split_off(units, u, 0, 16), wv, 16);
+      if (k / 2 - u * 32 > 16) std::memcpy(dst + split_off(units, u, 1, 16), wv + 4, 16);
     }
     return;
   }
@@ -375,7 +377,7 @@ void row_to_device(int fmt, const uint8_t *canon, int64_t k, int64_t r, int64_t 
         for (int b = 0; b < nh; ++b) setbit(hb, hi_pos(fmt, kk, b), (cv >> (4 + b)) & 1u);
       }
     }
-    uint8_t *d0 = P.p[0] + r * P.rb[0] + u * fp.unit_bytes[0];
+    uint8_t *d0 = P.p[0] + r * P.rb[0] + u * fp.unit_bytes[0];   // (q2sb, q3sb)
     uint8_t *d1 = P.p[1] + r * P.rb[1] + u * fp.unit_bytes[1];
     if (fmt == 2) {
       std::memcpy(d0, a, 16);
@@ -383,7 +385,9 @@ void row_to_device(int fmt, const uint8_t *canon, int64_t k, int64_t r, int64_t 
       std::memcpy(d0, a, 16);
       std::memcpy(d1, a + 4, 8);
     } else {
-      std::memcpy(d0, a, 32);
+      uint8_t *row0 = P.p[0] + r * P.rb[0];
+      std::memcpy(row0 + split_off(units, u, 0, 16), a, 16);
+      std::memcpy(row0 + split_off(units, u, 1, 16), a + 4, 16);
       std::memcpy(d1, hb, (size_t)fp.unit_bytes[1]);
     }
   }
@@ -397,15 +401,16 @@ void row_from_device(int fmt, const uint8_t *const *pl, const int64_t *rb, int64
   for (int64_t u = 0; u < units; ++u) {
     uint32_t a[8] = {0}, hb[4] = {0};
     if (fmt == 4) {
-      int64_t nbytes = std::min<int64_t>(32, k / 2 - u * 32);
-      std::memcpy(a, pl[0] + r * rb[0] + u * 32, (size_t)nbytes);
+      std::memcpy(a, pl[0] + r * rb[0] + split_off(units, u, 0, 16), 16);
+      if (k / 2 - u * 32 > 16) std::memcpy(a + 4, pl[0] + r * rb[0] + split_off(units, u, 1, 16), 16);
     } else if (fmt == 2) {
       std::memcpy(a, pl[0] + r * rb[0] + u * 16, 16);
     } else if (fmt == 3) {
       std::memcpy(a, pl[0] + r * rb[0] + u * 16, 16);
       std::memcpy(a + 4, pl[1] + r * rb[1] + u * 8, 8);
     } else {
-      std::memcpy(a, pl[0] + r * rb[0] + u * 32, 32);
+      std::memcpy(a, pl[0] + r * rb[0] + split_off(units, u, 0, 16), 16);
+      std::memcpy(a + 4, pl[0] + r * rb[0] + split_off(units, u, 1, 16), 16);
       std::memcpy(hb, pl[1] + r * rb[1] + u * fp.unit_bytes[1], (size_t)fp.unit_bytes[1]);
     }
     for (int kk = 0; kk < kUnit; ++kk) {
@@ -422,7 +427,8 @@ void row_from_device(int fmt, const uint8_t *const *pl, const int64_t *rb, int64
   if (fmt == 4) {
     uint8_t *cr = canon + r * (k / 2);
     for (int64_t i = 0; i < k; i += 2) cr[i / 2] = (uint8_t)(codes[(size_t)i] | (codes[(size_t)i + 1] << 4));
-    std::memcpy(canon + n * (k / 2) + r * (k / 32) * 4, pl[1] + r * rb[1], (size_t)((k / 32) * 4));
+    for (int64_t g = 0; g < k / 32; ++g)
+      std::memcpy(canon + n * (k / 2) + r * (k / 32) * 4 + g * 4, pl[1] + r * rb[1] + split_off(units, g >> 1, (int)(g & 1), 4), 4);
     return;
   }
   SB s;

@@ -15,6 +15,12 @@
 //
 //  q4g32  plane 0 codes: 8 dwords/unit, dword i holds weights 8i..8i+7, weight 8i+e in
 //         nibble slot (e>>1) + 4*(e&1); plane 1 fp32 scales (one per group of 32).
+//         Split halves (also the q5sb/q6sb nibble planes): a row of a 32-byte-per-unit plane
+//         stores the first 16 bytes of every unit, then the second 16 bytes of every unit
+//         (dwords 0-3 of unit u at 16u, dwords 4-7 at 16 units + 16u); the q4g32 scale plane
+//         likewise stores every unit's first scale, then every unit's second scale. Each
+//         128-bit (32-bit) load of a wave then reads one contiguous run of 1 KB (256 B).
+//         A ragged q4g32 row (k % 64 == 32) has no second half for its last unit.
 //  q2sb   plane 0 codes: 4 dwords/unit (a quarter super-block, 4 sub-blocks j of 16).
 //         Pair t of sub-block j = t>>3, r = t&7 sits in dword r>>1 at bit 2j + 8*(r&1)
 //         (+16 for the high half). Extraction mask 0x00030003 << 2j, class p = 4^j.
@@ -44,6 +50,15 @@ namespace qg {
 constexpr int kUnit = 64;          // weights per lane unit
 constexpr int kQK = 256;           // weights per super-block
 constexpr int64_t kPlaneAlign = 256;
+
+// Byte offset, within a row of a split-halves plane, of half `second` of unit u (each half
+// `hb` bytes; `units` units per row). Shared by the host packer and the device decoder.
+#if defined(__HIP__)
+#define QG_HOST_DEVICE __host__ __device__
+#else
+#define QG_HOST_DEVICE
+#endif
+QG_HOST_DEVICE inline int64_t split_off(int64_t units, int64_t u, int second, int hb) { return (second ? units * hb : 0) + u * hb; }
 
 // Bytes per lane unit of each plane, and the number of planes.
 struct FmtPlanes {

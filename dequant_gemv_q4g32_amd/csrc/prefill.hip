@@ -96,6 +96,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     for (int p = 0; p < 4; ++p) L.off[p] = 0;
     U::offsets(u, L.off);
     L.sh = fields_sh(u);
+    L.set_halves(a.units);
     // the weight row differs per lane here, so it goes into the per-lane offset (a row in
     // the scalar offset would force one load per distinct row)
 #pragma unroll

@@ -21,7 +21,13 @@ struct Lane {
   uint32_t prb[4];
   uint32_t off[4];
   uint32_t sh;              // bit offset of this unit's 6-bit fields in its 8-byte window
+  uint32_t half16;          // offset of the second halves in a split 16-byte-half plane row
+  uint32_t half4;           // same for the split q4g32 scale plane
   __device__ uint32_t row(int p, int64_t r) const { return (uint32_t)r * prb[p]; }
+  __device__ void set_halves(int64_t units) {
+    half16 = (uint32_t)(units * 16);
+    half4 = (uint32_t)(units * 4);
+  }
 };
 
 // 6-bit sub-scale fields (12 bytes per super-block; a unit owns 3 of them, bytes 3q..3q+2 for
@@ -69,17 +75,17 @@ template <> struct Unit<4> {
   __host__ __device__ static constexpr int NKS(int S) { return NK / S; }
   struct Raw { u32x4 c0, c1; float s0, s1; };
   __device__ static int pidx(int h, int p, int S) { return S == 1 ? p : 16 * h + p; }
-  __device__ static void offsets(int64_t u, uint32_t *off) { off[0] = (uint32_t)(u * 32); off[1] = (uint32_t)(u * 8); }
+  __device__ static void offsets(int64_t u, uint32_t *off) { off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 4); }
   __device__ static void load(Raw &q, const Lane &L, int64_t r, bool half) {
     const uint32_t r0 = L.row(0, r), r1 = L.row(1, r);
     q.c0 = bld4(L.rs[0], L.off[0], r0);
     // a half unit (k % 64 == 32) has one group; its second group's activations are zero
-    q.c1 = bld4(L.rs[0], L.off[0] + (half ? 0u : 16u), r0);
+    q.c1 = bld4(L.rs[0], L.off[0] + (half ? 0u : L.half16), r0);
     // Two 32-bit loads, not one 64-bit load: this toolchain narrows a multi-dword buffer load
     // whose elements are bit-cast to float to its first dword and reuses that dword for the
     // second element (vectors used in integer arithmetic, like the code words, are unaffected).
     q.s0 = __builtin_bit_cast(float, bld1(L.rs[1], L.off[1], r1));
-    q.s1 = __builtin_bit_cast(float, bld1(L.rs[1], L.off[1] + (half ? 0u : 4u), r1));
+    q.s1 = __builtin_bit_cast(float, bld1(L.rs[1], L.off[1] + (half ? 0u : L.half4), r1));
   }
   // xp: the lane's pairs (32 / S); kc: NK / S constants
   template <int S> __device__ static void prep(const uint32_t *xp, float *kc) {
@@ -380,12 +386,12 @@ template <> struct Unit<5> {
   struct Raw { u32x4 l0, l1; u32x2 h; uint32_t f, dd; };
   __device__ static int pidx(int h, int p, int S) { return S == 1 ? p : 16 * h + p; }
   __device__ static void offsets(int64_t u, uint32_t *off) {
-    off[0] = (uint32_t)(u * 32); off[1] = (uint32_t)(u * 8); off[2] = fields_off(u); off[3] = (uint32_t)((u >> 2) * 4);
+    off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 8); off[2] = fields_off(u); off[3] = (uint32_t)((u >> 2) * 4);
   }
   __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
     const uint32_t r0 = L.row(0, r);
     q.l0 = bld4(L.rs[0], L.off[0], r0);
-    q.l1 = bld4(L.rs[0], L.off[0] + 16, r0);
+    q.l1 = bld4(L.rs[0], L.off[0] + L.half16, r0);
     q.h = bld2(L.rs[1], L.off[1], L.row(1, r));
     q.f = fields24(L, 2, r);
     q.dd = bld1(L.rs[3], L.off[3], L.row(3, r));
@@ -469,12 +475,12 @@ template <> struct Unit<6> {
   struct Raw { u32x4 l0, l1, h; uint32_t sc; uint16_t d; };
   __device__ static int pidx(int h, int p, int S) { return S == 1 ? p : 16 * h + p; }
   __device__ static void offsets(int64_t u, uint32_t *off) {
-    off[0] = (uint32_t)(u * 32); off[1] = (uint32_t)(u * 16); off[2] = (uint32_t)(u * 4); off[3] = (uint32_t)((u >> 2) * 2);
+    off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 16); off[2] = (uint32_t)(u * 4); off[3] = (uint32_t)((u >> 2) * 2);
   }
   __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
     const uint32_t r0 = L.row(0, r);
     q.l0 = bld4(L.rs[0], L.off[0], r0);
-    q.l1 = bld4(L.rs[0], L.off[0] + 16, r0);
+    q.l1 = bld4(L.rs[0], L.off[0] + L.half16, r0);
     q.h = bld4(L.rs[1], L.off[1], L.row(1, r));
     q.sc = bld1_nt(L.rs[2], L.off[2], L.row(2, r));
     q.d = bldh(L.rs[3], L.off[3], L.row(3, r));
