@@ -88,7 +88,7 @@ template <> struct Unit<4> {
     q.s1 = __builtin_bit_cast(float, bld1(L.rs[1], L.off[1] + (half ? 0u : L.half4), r1));
   }
   // xp: the lane's pairs (32 / S); kc: NK / S constants
-  template <int S> __device__ static void prep(const uint32_t *xp, float *kc) {
+  template <int S> __device__ static void prep(uint32_t *xp, float *kc) {
 #pragma unroll
     for (int g = 0; g < 2 / S; ++g) {
       float x1 = 0.f, x16 = 0.f;
@@ -163,7 +163,7 @@ template <> struct Unit<2> {
     q.dd = bld1(L.rs[2], L.off[2], L.row(2, r));
   }
   // kc[j]: sum of x over the lane's part of sub-block j (local pairs (8/S) j .. (8/S) j + 8/S - 1)
-  template <int S> __device__ static void prep(const uint32_t *xp, float *kc) {
+  template <int S> __device__ static void prep(uint32_t *xp, float *kc) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       float s = 0.f;
@@ -255,10 +255,17 @@ template <> struct Unit<3> {
     q.f = fields24(L, 2, r);
     q.d = bldh(L.rs[3], L.off[3], L.row(3, r));
   }
-  template <int S> __device__ static void prep(const uint32_t *xp, float *kc) {
+  // The pairs of sub-block a sit at classes 1 (pairs 0..5) and 8 (6, 7), those of b at
+  // classes 8 (8..11) and 64 (12..15). prep divides the activations of the class-8 and
+  // class-64 pairs by 8 and 64 (exact in fp16 down to 2^-11 and 2^-8 of |x|, below which the
+  // quotient is subnormal and rounds by at most 2^-25), so that each sub-block accumulates
+  // in one register: sum P x = sum c x + 1024 X1 + 128 X8 (a), sum c x + 128 X8 + 16 X64 (b)
+  // with X the sums of the original x over each class.
+  template <int S> __device__ static void prep(uint32_t *xp, float *kc) {
+    const h2_t s8 = {(_Float16)0.125f, (_Float16)0.125f}, s64 = {(_Float16)0.015625f, (_Float16)0.015625f};
 #pragma unroll
     for (int c = 0; c < 2 / S; ++c) {
-      const uint32_t *x = xp + 16 * c;
+      uint32_t *x = xp + 16 * c;
       float a1 = 0.f, a8 = 0.f, b8 = 0.f, b64 = 0.f;
 #pragma unroll
       for (int r = 0; r < 6; ++r) a1 = dot2(x[r], kOnes, a1);
@@ -268,8 +275,12 @@ template <> struct Unit<3> {
       for (int r = 8; r < 12; ++r) b8 = dot2(x[r], kOnes, b8);
 #pragma unroll
       for (int r = 12; r < 16; ++r) b64 = dot2(x[r], kOnes, b64);
-      kc[2 * c] = -(1028.0f * a1 + 132.0f * a8);            // start of a's class-1 sum
-      kc[2 * c + 1] = -8.0f * (132.0f * b8 + 20.0f * b64);  // start of b's class-8 sum
+      kc[2 * c] = -(1028.0f * a1 + 132.0f * a8);       // start of a: sum (c - 4) x
+      kc[2 * c + 1] = -(132.0f * b8 + 20.0f * b64);    // start of b: sum (c - 4) x
+#pragma unroll
+      for (int r = 6; r < 12; ++r) x[r] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, x[r]) * s8);
+#pragma unroll
+      for (int r = 12; r < 16; ++r) x[r] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, x[r]) * s64);
     }
   }
   // One chunk: three dwords e0..e2 holding 32 codes -> the 16 fp16 pairs of its two
@@ -295,19 +306,15 @@ template <> struct Unit<3> {
     t = keep(pick_or(e1 >> 8, QG_SMASK(0x00800080u), t));    // bit 15 of e1 -> 7
     P[15] = pick_or(e2 >> 7, QG_SMASK(0x01000100u), t);      // bit 15 of e2 -> 8
   }
-  // sum (c - 4) x over sub-block a (sa) and 8 x that over b (sb) for one activation row
+  // sum (c - 4) x over sub-block a (sa) and over b (sb) for one activation row (x prepared)
   __device__ static void chunk_dot(const uint32_t *P, const uint32_t *x, float ka, float kb, float &sa, float &sb) {
-    float a1 = ka, a8 = 0.f, b8 = kb, b64 = 0.f;
+    float a = ka, b = kb;
 #pragma unroll
-    for (int r = 0; r < 6; ++r) a1 = dot2(P[r], x[r], a1);
-    a8 = dot2(P[6], x[6], a8);
-    a8 = dot2(P[7], x[7], a8);
+    for (int r = 0; r < 8; ++r) a = dot2(P[r], x[r], a);
 #pragma unroll
-    for (int r = 8; r < 12; ++r) b8 = dot2(P[r], x[r], b8);
-#pragma unroll
-    for (int r = 12; r < 16; ++r) b64 = dot2(P[r], x[r], b64);
-    sa = __builtin_fmaf(a8, 0.125f, a1);
-    sb = __builtin_fmaf(b64, 0.125f, b8);
+    for (int r = 8; r < 16; ++r) b = dot2(P[r], x[r], b);
+    sa = a;
+    sb = b;
   }
   template <int M, int S>
   __device__ static void dot(const Raw &q, int h, const uint32_t (*xp)[32 / S], const float (*kc)[NKS(S)], float *out) {
@@ -317,8 +324,8 @@ template <> struct Unit<3> {
       uint32_t P0[16], P1[16];
       chunk_pairs(q.a.x, q.a.y, q.a.z, P0);
       chunk_pairs(q.a.w, q.b.x, q.b.y, P1);
-      const float s0 = (float)(f & 63u), s1 = (float)((f >> 6) & 63u) * 0.125f;
-      const float s2 = (float)((f >> 12) & 63u), s3 = (float)((f >> 18) & 63u) * 0.125f;
+      const float s0 = (float)(f & 63u), s1 = (float)((f >> 6) & 63u);
+      const float s2 = (float)((f >> 12) & 63u), s3 = (float)((f >> 18) & 63u);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         float sa0, sb0, sa1, sb1;
@@ -335,7 +342,7 @@ template <> struct Unit<3> {
       uint32_t P[16];
       chunk_pairs(sel(h, q.a.w, q.a.x), sel(h, q.b.x, q.a.y), sel(h, q.b.y, q.a.z), P);
       const uint32_t fh = f >> (12 * h);
-      const float s0 = (float)(fh & 63u), s1 = (float)((fh >> 6) & 63u) * 0.125f;
+      const float s0 = (float)(fh & 63u), s1 = (float)((fh >> 6) & 63u);
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         float sa, sb;
@@ -397,7 +404,7 @@ template <> struct Unit<5> {
     q.dd = bld1(L.rs[3], L.off[3], L.row(3, r));
   }
   // kc layout (S = 1): [start h0, start h1, sum x h0, sum x h1]; (S = 2): [start, sum x]
-  template <int S> __device__ static void prep(const uint32_t *xp, float *kc) {
+  template <int S> __device__ static void prep(uint32_t *xp, float *kc) {
 #pragma unroll
     for (int hh = 0; hh < 2 / S; ++hh) {
       float x1 = 0.f, x16 = 0.f;
@@ -485,7 +492,7 @@ template <> struct Unit<6> {
     q.sc = bld1_nt(L.rs[2], L.off[2], L.row(2, r));
     q.d = bldh(L.rs[3], L.off[3], L.row(3, r));
   }
-  template <int S> __device__ static void prep(const uint32_t *xp, float *kc) {
+  template <int S> __device__ static void prep(uint32_t *xp, float *kc) {
 #pragma unroll
     for (int j = 0; j < 4 / S; ++j) {
       float x1 = 0.f, x16 = 0.f;
