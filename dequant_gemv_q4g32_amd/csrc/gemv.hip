@@ -399,6 +399,7 @@ int fill_args(int fmt, const void *w, int64_t n, int64_t k, GemvArgs &a) {
 
 constexpr int64_t kSimds = 1024;           // 256 CUs x 4 SIMDs
 constexpr int kMaxBatches = 32;
+constexpr int kMinBatches = 4;
 constexpr int kMaxM = 8;                   // activation rows one streaming launch serves
 
 // Resident waves per SIMD that a kernel's register and LDS use allow (asked once per kernel).
@@ -414,8 +415,11 @@ int launch_mv(GemvArgs a, int64_t count, hipStream_t s) {
   static const int wps = waves_per_simd(reinterpret_cast<const void *>(kern));
   const int64_t groups_per_matrix = (a.n + R - 1) / R;          // batches of R rows
   const int64_t target = kSimds * wps / a.wk;                   // row groups resident at once
+  // Batches per row group: enough to fill the resident slots once, but at least kMinBatches,
+  // so that a wave's activation load and first load latency are spread over several rows
+  // (a grid with fewer, longer waves beats a full one of very short waves).
   int64_t nb = (groups_per_matrix * count) / target;
-  nb = nb < 1 ? 1 : (nb > kMaxBatches ? kMaxBatches : nb);
+  nb = nb < kMinBatches ? kMinBatches : (nb > kMaxBatches ? kMaxBatches : nb);
   a.nb = (int)nb;
   const int64_t rows_per_block = (int64_t)a.wr * R * nb;
   dim3 grid((unsigned)((a.n + rows_per_block - 1) / rows_per_block), (unsigned)count);
