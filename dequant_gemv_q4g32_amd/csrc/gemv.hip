@@ -401,6 +401,7 @@ constexpr int64_t kSimds = 1024;           // 256 CUs x 4 SIMDs
 constexpr int kMaxBatches = 32;
 constexpr int kMinBatches = 4;
 constexpr int kMaxM = 8;                   // activation rows one streaming launch serves
+constexpr int kSkinnyMaxM = 16;            // activation rows of the matrix-core decode kernel
 
 // Resident waves per SIMD that a kernel's register and LDS use allow (asked once per kernel).
 int waves_per_simd(const void *kernel) {
@@ -548,7 +549,12 @@ int qg_gemm(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int
   GemvArgs a{};
   int st = fill_args(fmt, w, n, k, a);
   if (st != QG_OK) return st;
-  // more rows than one streaming launch serves: LDS-staged fp16 tiles on the matrix cores
+  // a decode batch of a few rows: fp16 w_hat on the matrix cores, one weight stream;
+  // more rows: LDS-staged fp16 tiles on the matrix cores
+#ifndef QG_SKINNY_MIN_M
+#define QG_SKINNY_MIN_M 5
+#endif
+  if (m >= QG_SKINNY_MIN_M && m <= kSkinnyMaxM) return launch_skinny(fmt, w, X, ldx, Y, ldy, y_f32, m, n, k, s);
   if (m > kMaxM) return launch_prefill(fmt, w, X, ldx, Y, ldy, y_f32, m, n, k, s);
   a.x = X;
   a.ldx = ldx;

@@ -1,0 +1,218 @@
+// Dequant GEMM for a few activation rows (2 <= m <= 16) on the matrix cores, gfx950.
+//
+// Method: "二三五六位量化" page section 1.2 and DBHOO-CIM page section 6 (a decode batch is
+// the GEMV with several activation rows, still bound by the weight stream). On the vector
+// units every code pair costs one v_dot2 per activation row, so 8 rows need about 300 TFLOP/s
+// at 8 TB/s, twice what v_dot2 delivers. Here each code is decoded once to fp16 w_hat (the
+// per-format `wide` decode of units.h, as in the prefill kernel) and the products with all
+// activation rows (padded to 16) come from v_mfma_f32_16x16x32_f16 with fp32 accumulation.
+//
+// Mapping: a wave covers 16 weight rows and 4 * DW units of K per pass. Lane l serves weight
+// row l % 16 (the MFMA's N index) and lane group g = l / 16 serves unit g of each group of 4
+// consecutive units: it decodes those 64 weights to 32 fp16 pairs, which are the B operands
+// of 8 MFMAs (4 pairs each). The A operands are the activations of the same k indices for
+// activation row l % 16, loaded once per pass into registers and reused for every row tile
+// of the wave. Waves of a workgroup split K and add their partial 16 x 16 tiles into one LDS
+// tile per row tile (LDS float atomics: the order of those fp32 additions, and so the last
+// bits of the result, can differ from run to run).
+#include <hip/hip_runtime.h>
+
+#include "../../include/qgemv.h"
+#include "device_common.h"
+#include "launch.h"
+#include "layout.h"
+#include "units.h"
+
+namespace qg {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+struct SkinnyArgs {
+  const uint8_t *w;
+  int64_t poff[4];
+  int64_t prb[4];
+  int64_t n, k, units;
+  const uint16_t *x;
+  int64_t ldx;
+  void *y;
+  int64_t ldy;
+  int m;
+  int y_f32;
+  int wk;            // waves along K in a workgroup
+  int kpasses;       // passes over K
+  int nb;            // row tiles (16 rows each) per workgroup
+};
+
+constexpr int kDW = 1;                     // steps of 4 units per wave and pass
+#ifndef QG_SKINNY_STAGES
+#define QG_SKINNY_STAGES 2
+#endif
+constexpr int kStages = QG_SKINNY_STAGES;
+constexpr int kSkinnyMaxWk = 16;
+constexpr int kSkinnyMaxNb = 32;           // LDS: nb * 256 floats (a multiple of every kStages)
+constexpr uint32_t kSkX = 0x7FFFFFF0u;     // activation buffer range; offsets past it read 0
+#ifndef QG_SKINNY_WAVES
+#define QG_SKINNY_WAVES 4096
+#endif
+constexpr int64_t kSkinnyWaves = QG_SKINNY_WAVES;
+
+template <int F>
+__global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs a) {
+  using U = Unit<F>;
+  using Raw = typename U::Raw;
+  extern __shared__ float red[];           // [nb][256] output tiles
+  const int lane = threadIdx.x & 63;
+  const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int rl = lane & 15, g = lane >> 4;
+  const int64_t tile0 = (int64_t)blockIdx.x * a.nb;
+
+  Lane L;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    L.rs[p] = make_rsrc(a.w + a.poff[p], (uint32_t)(a.prb[p] * a.n));
+    L.prb[p] = (uint32_t)a.prb[p];
+  }
+  L.set_halves(a.units);
+  for (int i = threadIdx.x; i < a.nb * 256; i += blockDim.x) red[i] = 0.f;
+  __syncthreads();
+  const rsrc_t xr = make_rsrc(a.x, kSkX);
+  const bool mlive = rl < a.m;
+  const uint32_t xrow = (uint32_t)(rl * a.ldx * 2);
+
+  for (int kp = 0; kp < a.kpasses; ++kp) {
+    // This wave's units in this pass: kDW steps of 4 consecutive units; lane group g takes
+    // unit 4 * step + g, so a load instruction reads 4 units (64 B or more) of each of its
+    // 16 rows contiguously.
+    const int64_t step0 = ((int64_t)kp * a.wk + wk) * kDW;
+    int64_t unit[kDW];
+    bool ulive[kDW];
+#pragma unroll
+    for (int d = 0; d < kDW; ++d) {
+      const int64_t u = 4 * (step0 + d) + g;
+      ulive[d] = u < a.units;
+      unit[d] = ulive[d] ? u : a.units - 1;
+    }
+    // activations (A operands): for MFMA s of a unit, local pairs 4 (s & 3).. of half s >> 2
+    half8_t A[kDW][8];
+#pragma unroll
+    for (int d = 0; d < kDW; ++d)
+#pragma unroll
+      for (int s8 = 0; s8 < 8; ++s8) {
+        const int64_t kk = unit[d] * kUnit + 2 * U::pidx(s8 >> 2, 4 * (s8 & 3), 2);
+        const bool ok = mlive && ulive[d] && kk < a.k;
+        A[d][s8] = __builtin_bit_cast(half8_t, bld4c(xr, ok ? xrow + (uint32_t)(kk * 2) : kSkX, 0));
+      }
+
+    auto load = [&](Raw *q, int j) {
+      const int64_t t = tile0 + (j < a.nb ? j : a.nb - 1);
+      int64_t row = t * 16 + rl;
+      row = row < a.n ? row : a.n - 1;
+#pragma unroll
+      for (int d = 0; d < kDW; ++d) {
+        Lane Ld = L;
+#pragma unroll
+        for (int p = 0; p < 4; ++p) Ld.off[p] = 0;
+        U::offsets(unit[d], Ld.off);
+        Ld.sh = fields_sh(unit[d]);
+#pragma unroll
+        for (int p = 0; p < 4; ++p) Ld.off[p] += (uint32_t)row * Ld.prb[p];
+        const bool half = (F == 4) && (unit[d] == a.units - 1) && (a.k % 64 != 0);
+        U::load(q[d], Ld, 0, half);
+      }
+    };
+    auto finish = [&](const Raw *q, int j) {
+      // two accumulators (one per unit half), so that consecutive MFMAs are independent
+      f32x4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+      for (int d = 0; d < kDW; ++d)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          uint32_t pr[16];
+          U::wide(q[d], hh, pr);
+#pragma unroll
+          for (int s = 0; s < 4; ++s) {
+            const half8_t B = __builtin_bit_cast(half8_t, u32x4{pr[4 * s], pr[4 * s + 1], pr[4 * s + 2], pr[4 * s + 3]});
+            acc2[s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[d][4 * hh + s], B, acc2[s & 1], 0, 0, 0);
+          }
+        }
+      const f32x4 acc = acc2[0] + acc2[1];
+      // D of a 16 x 16 MFMA: lane l holds column l % 16 (weight row) and rows 4 (l / 16) + e
+      // (activation rows); tile index m * 16 + n
+#pragma unroll
+      for (int e = 0; e < 4; ++e) atomicAdd(&red[j * 256 + (4 * g + e) * 16 + rl], acc[e]);
+    };
+    // kStages register stages over the row tiles (loads of kStages - 1 tiles in flight while
+    // one is computed); prefetches past the last tile re-load it
+    Raw qs[kStages][kDW];
+#pragma unroll
+    for (int d = 0; d + 1 < kStages; ++d) load(qs[d], d);
+    // (nb is a multiple of kStages, so the body has no branch and each wait covers only the
+    // oldest stage)
+    for (int j = 0; j < a.nb; j += kStages) {
+#pragma unroll
+      for (int d = 0; d < kStages; ++d) {
+        load(qs[(d + kStages - 1) % kStages], j + d + kStages - 1);
+        finish(qs[d], j + d);
+      }
+    }
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < a.nb * 256; i += blockDim.x) {
+    const int j = i >> 8, idx = i & 255, mm = idx >> 4;
+    const int64_t row = (tile0 + j) * 16 + (idx & 15);
+    if (mm >= a.m || row >= a.n) continue;
+    const float sum = red[i];
+    const int64_t o = (int64_t)mm * a.ldy + row;
+    if (a.y_f32) reinterpret_cast<float *>(a.y)[o] = sum;
+    else reinterpret_cast<_Float16 *>(a.y)[o] = (_Float16)sum;
+  }
+}
+
+int launch_skinny(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int64_t ldy, int y_f32,
+                  int64_t m, int64_t n, int64_t k, hipStream_t s) {
+  qg_layout lay;
+  int st = qg_device_layout(fmt, n, k, &lay);
+  if (st != QG_OK) return st;
+  if (m < 1 || m > 16) return QG_ERR_SHAPE;
+  if (16 * ldx * 2 >= (int64_t)kSkX) return QG_ERR_SHAPE;         // 32-bit activation offsets
+  SkinnyArgs a{};
+  a.w = static_cast<const uint8_t *>(w);
+  for (int p = 0; p < 4; ++p) {
+    a.poff[p] = lay.plane_offset[p];
+    a.prb[p] = lay.plane_row_bytes[p];
+  }
+  a.n = n;
+  a.k = k;
+  a.units = (k + kUnit - 1) / kUnit;
+  a.x = X;
+  a.ldx = ldx;
+  a.y = Y;
+  a.ldy = ldy;
+  a.m = (int)m;
+  a.y_f32 = y_f32;
+  const int64_t waves_k = (a.units + 4 * kDW - 1) / (4 * kDW);
+  const int64_t passes = (waves_k + kSkinnyMaxWk - 1) / kSkinnyMaxWk;
+  a.kpasses = (int)passes;
+  a.wk = (int)((waves_k + passes - 1) / passes);
+  const int64_t tiles = (n + 15) / 16;
+  // Row tiles per workgroup: each wave reuses its activation registers for every tile, so
+  // more tiles per wave means less activation traffic per weight byte; the grid is kept at
+  // about kSkinnyWaves waves so that the CUs stay busy.
+  int64_t nb = tiles * a.wk / kSkinnyWaves;
+  nb = nb < 1 ? 1 : (nb > kSkinnyMaxNb ? kSkinnyMaxNb : nb);
+  nb = (nb + kStages - 1) / kStages * kStages;      // whole pipeline rounds; extra tiles are past n
+  a.nb = (int)nb;
+  const dim3 grid((unsigned)((tiles + nb - 1) / nb)), block((unsigned)(64 * a.wk));
+  const size_t shm = (size_t)nb * 256 * sizeof(float);
+  switch (fmt) {
+    case 2: return launch(skinny_kernel<2>, grid, block, shm, s, a);
+    case 3: return launch(skinny_kernel<3>, grid, block, shm, s, a);
+    case 4: return launch(skinny_kernel<4>, grid, block, shm, s, a);
+    case 5: return launch(skinny_kernel<5>, grid, block, shm, s, a);
+    case 6: return launch(skinny_kernel<6>, grid, block, shm, s, a);
+  }
+  return QG_ERR_FORMAT;
+}
+
+}  // namespace qg
