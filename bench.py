@@ -9,8 +9,15 @@ Workload (default): the 3-bit super-block matrix 4096 x 4096 (Laplace(0, 0.02) w
 N(0, 1) activations, batch 1). One step is one launch of G independent batch-1 GEMVs of that
 shape (default G = 32, 230 MB of packed weights), each with its own matrix copy and its own
 activation vector. Steps rotate over enough copies (>= 1.2 GB) that every step reads its
-weights from HBM, not from the 256 MB last-level cache. A single 7.2 MB matrix per launch is
-also timed ("single_launch"): at ~1 us of streaming it is bound by launch cadence, not HBM.
+weights from HBM, not from the 256 MB last-level cache. The K timed steps are captured in one
+HIP graph; after W eager warmup steps and one untimed replay (which uploads the graph and lets
+the clocks settle) the graph is replayed between two synchronizes. A single 7.2 MB matrix per launch is also
+timed ("single_launch"): at ~1 us of streaming it is bound by launch cadence, not HBM.
+
+"other_workloads" measures the remaining workloads the same way (HBM-resident rotation,
+graph-timed): INT4 group-32 4096^2, the 7B-like layer set per super-block format (same-shape
+projections batched into one launch), the 70B-like layer set at batch 1, 2, 4 and 8, and the
+512-row prefill GEMM (TFLOP/s and fraction of the 2.5 PFLOP/s dense fp16 MFMA peak).
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -36,14 +43,19 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=400)
     ap.add_argument("--workload", default="q3sb_gemv_4096")
     ap.add_argument("--group", type=int, default=32, help="independent batch-1 GEMVs per launch")
     ap.add_argument("--footprint-gb", type=float, default=1.2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-single", action="store_true", help="skip the one-matrix-per-launch timing")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other workloads (INT4 4096^2, layer sets, decode batches, prefill)")
+    ap.add_argument("--profile-workload", default=None, metavar="NAME",
+                    help="only launch the first matrix of workload NAME --steps times (for profiler runs); "
+                         "prints no JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (the reference kernel for HBM counters)")
     return ap.parse_args()
@@ -115,6 +127,129 @@ def cpu_baseline(fmt, canonical, n, k, x, seconds):
                       f"canonical encoding + fp64 matvec, one thread, {dt:.1f} s"}
 
 
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+
+def _graph_time_us(fn, rounds, reps=3):
+    """Median over reps of the per-round time of `rounds` calls of fn(i), captured in one graph."""
+    import torch
+    fn(0)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(reps):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(rounds):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        times.append(e0.elapsed_time(e1) * 1e3 / rounds)
+        del g
+    return sorted(times)[len(times) // 2]
+
+
+def measure_set(qg, fmt, canon_shapes, m, dev, footprint_gb=1.2, rounds=24):
+    """One decode step over a set of matrices (batch m), with the weights rotated over enough
+    copies that every round reads them from HBM. At batch 1 consecutive matrices of one shape
+    go out as one strided batched launch (q/k/v/o, or gate/up, of a layer); otherwise one
+    launch per matrix. Returns (algorithmic bytes per round, microseconds per round)."""
+    import numpy as np
+    import torch
+    from workloads import activations
+    lays = [qg.device_layout(fmt, n, k) for _, n, k in canon_shapes]
+    strides = [(l.total_bytes + 255) // 256 * 256 for l in lays]
+    set_bytes = sum(strides)
+    alg = sum(l.algorithmic_bytes for l in lays)
+    copies = max(2, int(np.ceil(footprint_gb * 1e9 / set_bytes)))
+    buf = torch.empty(copies * set_bytes, dtype=torch.uint8, device=dev)
+    offs = np.concatenate([[0], np.cumsum(strides)[:-1]]).astype(np.int64)
+    for j, (canon, n, k) in enumerate(canon_shapes):
+        one = torch.from_numpy(qg.to_device_layout(fmt, canon, n, k)).to(dev)
+        for c in range(copies):
+            o = c * set_bytes + int(offs[j])
+            buf[o:o + lays[j].total_bytes].copy_(one)
+        del one
+    # groups of consecutive same-shape matrices: (first index, count, n, k)
+    groups = []
+    for j, (_, n, k) in enumerate(canon_shapes):
+        if m == 1 and groups and tuple(groups[-1][2:]) == (n, k):
+            groups[-1][1] += 1
+        else:
+            groups.append([j, 1, n, k])
+    xs = [torch.from_numpy(activations(max(m, cnt), k, 11 + j)).to(dev) for j, cnt, n, k in groups]
+    ys = [torch.empty((max(m, cnt), n), dtype=torch.float16, device=dev) for j, cnt, n, k in groups]
+
+    def rnd(i):
+        c = i % copies
+        for (j, cnt, n, k), x, y in zip(groups, xs, ys):
+            w = buf[c * set_bytes + int(offs[j]):]
+            if m == 1:
+                qg.gemv_batched(fmt, w, strides[j], x, y, cnt, n, k)
+            else:
+                qg.gemm(fmt, w, x, n, k, out=y)
+
+    us = _graph_time_us(rnd, rounds)
+    del buf
+    torch.cuda.empty_cache()
+    return alg, us
+
+
+def extra_configs(qg, dev):
+    """The other workloads on this one GPU: INT4 4096^2 at batch 1, the 7B-like layer set
+    (q/k/v/o, gate/up, down) per super-block format, the 70B-like set at batch 1, 2, 4 and 8,
+    and the 512-row prefill GEMM."""
+    from workloads import WORKLOADS, activations
+    out = {}
+    # INT4 group-32 4096 x 4096, batch 1: grouped like the headline, and as a single launch
+    wl = WORKLOADS["q4g32_gemv_4096"]
+    canon = qg.quantize("q4g32", wl.weights(0))
+    alg, us = measure_set(qg, "q4g32", [(canon, 4096, 4096)] * 32, 1, dev, rounds=16)
+    alg1, us1 = measure_set(qg, "q4g32", [(canon, 4096, 4096)], 1, dev, rounds=200)
+    out["q4g32_gemv_4096"] = {"GBps_32_per_launch": round(alg / us / 1e3, 1), "frac": round(alg / us / 1e3 / HBM_PEAK_GBPS, 4),
+                              "GBps_single_launch": round(alg1 / us1 / 1e3, 1), "us_single_launch": round(us1, 2)}
+    log(f"[bench] q4g32 4096^2: {out['q4g32_gemv_4096']}")
+    # 7B-like layer set, batch 1, each format (the four share one set of fp32 weights)
+    wl = WORKLOADS["q3sb_7b_layer_set"]
+    w7 = [wl.weights(i) for i in range(len(wl.shapes))]
+    for fmt in ("q2sb", "q3sb", "q5sb", "q6sb"):
+        cs = [(qg.quantize(fmt, w), w.shape[0], w.shape[1]) for w in w7]
+        alg, us = measure_set(qg, fmt, cs, 1, dev)
+        out[f"{fmt}_7b_layer_set"] = {"GBps": round(alg / us / 1e3, 1), "frac": round(alg / us / 1e3 / HBM_PEAK_GBPS, 4),
+                                      "us_per_set": round(us, 2), "bytes_per_set": alg}
+        log(f"[bench] {fmt} 7B layer set: {out[f'{fmt}_7b_layer_set']}")
+    del w7
+    # 70B-like layer set at batch 1, 2, 4, 8 (q3sb and q5sb share the fp32 weights)
+    wl = WORKLOADS["q3sb_70b_layer_set_m1"]
+    w70 = [wl.weights(i) for i in range(len(wl.shapes))]
+    for fmt in ("q3sb", "q5sb"):
+        cs = [(qg.quantize(fmt, w), w.shape[0], w.shape[1]) for w in w70]
+        for m in (1, 2, 4, 8):
+            alg, us = measure_set(qg, fmt, cs, m, dev, rounds=12)
+            flops = 2 * m * sum(n * k for _, n, k in cs)
+            out[f"{fmt}_70b_layer_set_m{m}"] = {"GBps": round(alg / us / 1e3, 1),
+                                                "frac": round(alg / us / 1e3 / HBM_PEAK_GBPS, 4),
+                                                "us_per_set": round(us, 2), "TFLOPs": round(flops / us / 1e6, 2)}
+            log(f"[bench] {fmt} 70B layer set m={m}: {out[f'{fmt}_70b_layer_set_m{m}']}")
+        del cs
+    del w70
+    # prefill: 512 x 4096 activations times 11008 x 4096 weights (MFMA bound)
+    for fmt in ("q4g32", "q5sb"):
+        wl = WORKLOADS[f"{fmt}_prefill_512"]
+        n, k = wl.shapes[0]
+        canon = qg.quantize(fmt, wl.weights(0))
+        alg, us = measure_set(qg, fmt, [(canon, n, k)], 512, dev, rounds=10)
+        tf = 2 * 512 * n * k / us / 1e6
+        out[f"{fmt}_prefill_512"] = {"TFLOPs": round(tf, 1), "mfma_frac_of_fp16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                                     "us": round(us, 2), "weight_GBps": round(alg / us / 1e3, 1)}
+        log(f"[bench] {fmt} prefill 512: {out[f'{fmt}_prefill_512']}")
+    return out
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -129,6 +264,20 @@ def main():
 
     import dequant_gemv_q4g32_amd as qg
     from workloads import WORKLOADS
+
+    if args.profile_workload:
+        wl = WORKLOADS[args.profile_workload]
+        n, k = wl.shapes[0]
+        wd = torch.from_numpy(qg.to_device_layout(wl.fmt, qg.quantize(wl.fmt, wl.weights(0)), n, k)).to("cuda:0")
+        X = torch.from_numpy(wl.x(0)).to("cuda:0")
+        for _ in range(args.steps):
+            if wl.m == 1:
+                qg.gemv(wl.fmt, wd, X[0], n, k)
+            else:
+                qg.gemm(wl.fmt, wd, X, n, k)
+        torch.cuda.synchronize()
+        log(f"[bench] profiled {args.profile_workload}: {args.steps} launches of {wl.fmt} {wl.m}x{n}x{k}")
+        return
 
     wl = WORKLOADS[args.workload]
     fmt = wl.fmt
@@ -158,16 +307,25 @@ def main():
         s = i % sets
         qg.gemv_batched(fmt, buf[s * G * stride:], stride, xs[s * G:], ys[s * G:], G, n, k)
 
+    # The K timed steps are captured in one HIP graph (so that host launch overhead cannot
+    # leave the GPU idle between 50 us steps). After the W warmup steps the graph is replayed
+    # once untimed (its first replay uploads it), then timed between two synchronizes.
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for i in range(args.steps):
+            step(args.warmup + i)
+    graph.replay()
+    torch.cuda.synchronize()
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
-    for i in range(args.steps):
-        step(args.warmup + i)
+    graph.replay()
     ev1.record()
     torch.cuda.synchronize()
     ms = ev0.elapsed_time(ev1) / args.steps
+    del graph
     gbps = G * alg / (ms * 1e-3) / 1e9
     log(f"[bench] grouped: {ms * 1e3:.2f} us per launch, {gbps:.0f} GB/s")
 
@@ -228,6 +386,10 @@ def main():
         torch.cuda.synchronize()
         log("[bench] ran 5 copies of 512 MiB for counter calibration")
 
+    extra = None
+    if not args.no_extra:
+        extra = extra_configs(qg, dev)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("[bench] timing the oracle on the host ...")
@@ -249,6 +411,7 @@ def main():
         "frac_of_read_ceiling": round(gbps / ceiling, 4),
         "single_launch": single,
         "cpu_baseline": cpu,
+        "other_workloads": extra,
     }
     print(json.dumps(out), flush=True)
 
