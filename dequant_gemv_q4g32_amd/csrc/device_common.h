@@ -93,6 +93,16 @@ __device__ __forceinline__ u32x4 bld4c(rsrc_t r, uint32_t voff, uint32_t soff) {
 __device__ __forceinline__ u32x2 bld2(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, kNT));
 }
+// the same with the cache policy as a template argument (AUX = kNT streams, 0 caches)
+template <int AUX> __device__ __forceinline__ u32x4 bldx4(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, AUX));
+}
+template <int AUX> __device__ __forceinline__ u32x2 bldx2(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_bit_cast(u32x2, __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, AUX));
+}
+template <int AUX> __device__ __forceinline__ uint32_t bldx1(rsrc_t r, uint32_t voff, uint32_t soff) {
+  return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, AUX);
+}
 __device__ __forceinline__ uint32_t bld1_nt(rsrc_t r, uint32_t voff, uint32_t soff) {
   return __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, kNT);
 }

@@ -9,9 +9,9 @@
 //
 // Tiling: a workgroup of 4 waves computes a 128 x 128 tile of Y (128 activation rows x 128
 // weight rows) and walks K in steps of one 64-weight unit. Each step, every thread loads
-// half a unit of one weight row and 64 bytes of one activation row (two steps ahead, into
-// one of two register stages), decodes its half unit to 16 fp16 pairs and stores both into
-// one of two LDS buffers. Each wave then runs 2 x 2 MFMA tiles of 32 x 32 over the step's 4 K-slices
+// half a unit of one weight row and 16 bytes of each of 4 activation rows (two steps ahead,
+// into one of two register stages), decodes its half unit to 16 fp16 pairs and stores both
+// into one of two LDS buffers. Each wave then runs 2 x 2 MFMA tiles of 32 x 32 over the step's 4 K-slices
 // of 16. Workgroups are numbered so that the M tiles sharing a weight tile run on one XCD
 // and share its L2.
 #include <hip/hip_runtime.h>
@@ -71,15 +71,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave & 1, wn = wave >> 1;         // this wave's 64 x 64 quarter of the tile
 
-  // loader role: LDS row t >> 1 of both tiles, half h = t & 1 of the unit
+  // weight loader role: LDS row t >> 1 of the weight tile, half h = t & 1 of the unit
   const int lrow = t >> 1, h = t & 1;
   const int64_t wrow = r0 + lrow < a.n ? r0 + lrow : a.n - 1;   // rows past n are not stored
-  const bool xlive = m0 + lrow < a.m;
+  // activation loader role: rows (t >> 3) + 32 i, 16-byte chunk t & 7 of the step's 128 bytes,
+  // so that 8 consecutive lanes read one row's 128 bytes (whole cache lines)
+  const int xr0 = t >> 3, xc = t & 7;
   // activations through a buffer resource based at this tile's first row: a dead row or the
   // missing half of a ragged q4g32 unit gets an offset past the range, which loads zeros (a
   // select on the loaded data instead would make every step wait for its own loads)
   const rsrc_t xr = make_rsrc(a.x + m0 * a.ldx, kXRange);
-  const uint32_t xrow_off = (uint32_t)(lrow * a.ldx * 2);
 
   Lane L;
 #pragma unroll
@@ -102,12 +103,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) L.off[p] += (uint32_t)wrow * L.prb[p];
     const bool half = (F == 4) && (u == a.units - 1) && (a.k % 64 != 0);
-    U::load(q, L, 0, half);
+    // cached: the weight tile is read again by the workgroups of the other M tiles
+    U::template load<0>(q, L, 0, half);
+    const int64_t kk = u * kUnit + 8 * xc;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t kk = u * kUnit + 32 * h + 8 * i;
-      const bool ok = xlive && kk < a.k;
-      xv[i] = bld4c(xr, ok ? xrow_off + (uint32_t)(kk * 2) : kXRange, 0);
+      const int xrow = xr0 + 32 * i;
+      const bool ok = m0 + xrow < a.m && kk < a.k;
+      xv[i] = bld4c(xr, ok ? (uint32_t)(xrow * a.ldx * 2 + kk * 2) : kXRange, 0);
     }
   };
   // decode a register stage to fp16 and store it, with its activations, into LDS buffer b
@@ -120,7 +123,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       const int g = U::pidx(h, 4 * i, 2);
       *reinterpret_cast<u32x4 *>(&ws[b][lrow * kLdsRow + 2 * g]) =
           u32x4{pr[4 * i], pr[4 * i + 1], pr[4 * i + 2], pr[4 * i + 3]};
-      *reinterpret_cast<u32x4 *>(&xs[b][lrow * kLdsRow + 32 * h + 8 * i]) = xv[i];
+      *reinterpret_cast<u32x4 *>(&xs[b][(xr0 + 32 * i) * kLdsRow + 8 * xc]) = xv[i];
     }
   };
 

@@ -76,11 +76,11 @@ template <> struct Unit<4> {
   struct Raw { u32x4 c0, c1; float s0, s1; };
   __device__ static int pidx(int h, int p, int S) { return S == 1 ? p : 16 * h + p; }
   __device__ static void offsets(int64_t u, uint32_t *off) { off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 4); }
-  __device__ static void load(Raw &q, const Lane &L, int64_t r, bool half) {
+  template <int AUX = kNT> __device__ static void load(Raw &q, const Lane &L, int64_t r, bool half) {
     const uint32_t r0 = L.row(0, r), r1 = L.row(1, r);
-    q.c0 = bld4(L.rs[0], L.off[0], r0);
+    q.c0 = bldx4<AUX>(L.rs[0], L.off[0], r0);
     // a half unit (k % 64 == 32) has one group; its second group's activations are zero
-    q.c1 = bld4(L.rs[0], L.off[0] + (half ? 0u : L.half16), r0);
+    q.c1 = bldx4<AUX>(L.rs[0], L.off[0] + (half ? 0u : L.half16), r0);
     // Two 32-bit loads, not one 64-bit load: this toolchain narrows a multi-dword buffer load
     // whose elements are bit-cast to float to its first dword and reuses that dword for the
     // second element (vectors used in integer arithmetic, like the code words, are unaffected).
@@ -157,9 +157,9 @@ template <> struct Unit<2> {
   __device__ static void offsets(int64_t u, uint32_t *off) {
     off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 4); off[2] = (uint32_t)((u >> 2) * 4);
   }
-  __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
-    q.c = bld4(L.rs[0], L.off[0], L.row(0, r));
-    q.sc = bld1_nt(L.rs[1], L.off[1], L.row(1, r));
+  template <int AUX = kNT> __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
+    q.c = bldx4<AUX>(L.rs[0], L.off[0], L.row(0, r));
+    q.sc = bldx1<AUX>(L.rs[1], L.off[1], L.row(1, r));
     q.dd = bld1(L.rs[2], L.off[2], L.row(2, r));
   }
   // kc[j]: sum of x over the lane's part of sub-block j (local pairs (8/S) j .. (8/S) j + 8/S - 1)
@@ -249,9 +249,9 @@ template <> struct Unit<3> {
   __device__ static void offsets(int64_t u, uint32_t *off) {
     off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 8); off[2] = fields_off(u); off[3] = (uint32_t)((u >> 2) * 2);
   }
-  __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
-    q.a = bld4(L.rs[0], L.off[0], L.row(0, r));
-    q.b = bld2(L.rs[1], L.off[1], L.row(1, r));
+  template <int AUX = kNT> __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
+    q.a = bldx4<AUX>(L.rs[0], L.off[0], L.row(0, r));
+    q.b = bldx2<AUX>(L.rs[1], L.off[1], L.row(1, r));
     q.f = fields24(L, 2, r);
     q.d = bldh(L.rs[3], L.off[3], L.row(3, r));
   }
@@ -395,11 +395,11 @@ template <> struct Unit<5> {
   __device__ static void offsets(int64_t u, uint32_t *off) {
     off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 8); off[2] = fields_off(u); off[3] = (uint32_t)((u >> 2) * 4);
   }
-  __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
+  template <int AUX = kNT> __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
     const uint32_t r0 = L.row(0, r);
-    q.l0 = bld4(L.rs[0], L.off[0], r0);
-    q.l1 = bld4(L.rs[0], L.off[0] + L.half16, r0);
-    q.h = bld2(L.rs[1], L.off[1], L.row(1, r));
+    q.l0 = bldx4<AUX>(L.rs[0], L.off[0], r0);
+    q.l1 = bldx4<AUX>(L.rs[0], L.off[0] + L.half16, r0);
+    q.h = bldx2<AUX>(L.rs[1], L.off[1], L.row(1, r));
     q.f = fields24(L, 2, r);
     q.dd = bld1(L.rs[3], L.off[3], L.row(3, r));
   }
@@ -484,12 +484,12 @@ template <> struct Unit<6> {
   __device__ static void offsets(int64_t u, uint32_t *off) {
     off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 16); off[2] = (uint32_t)(u * 4); off[3] = (uint32_t)((u >> 2) * 2);
   }
-  __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
+  template <int AUX = kNT> __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
     const uint32_t r0 = L.row(0, r);
-    q.l0 = bld4(L.rs[0], L.off[0], r0);
-    q.l1 = bld4(L.rs[0], L.off[0] + L.half16, r0);
-    q.h = bld4(L.rs[1], L.off[1], L.row(1, r));
-    q.sc = bld1_nt(L.rs[2], L.off[2], L.row(2, r));
+    q.l0 = bldx4<AUX>(L.rs[0], L.off[0], r0);
+    q.l1 = bldx4<AUX>(L.rs[0], L.off[0] + L.half16, r0);
+    q.h = bldx4<AUX>(L.rs[1], L.off[1], L.row(1, r));
+    q.sc = bldx1<AUX>(L.rs[2], L.off[2], L.row(2, r));
     q.d = bldh(L.rs[3], L.off[3], L.row(3, r));
   }
   template <int S> __device__ static void prep(uint32_t *xp, float *kc) {
