@@ -15,9 +15,11 @@ the clocks settle) the graph is replayed between two synchronizes. A single 7.2 
 timed ("single_launch"): at ~1 us of streaming it is bound by launch cadence, not HBM.
 
 "other_workloads" measures the remaining workloads the same way (HBM-resident rotation,
-graph-timed): INT4 group-32 4096^2, the 7B-like layer set per super-block format (same-shape
-projections batched into one launch), the 70B-like layer set at batch 1, 2, 4 and 8, and the
-512-row prefill GEMM (TFLOP/s and fraction of the 2.5 PFLOP/s dense fp16 MFMA peak).
+graph-timed): INT4 group-32 4096^2, the 7B-like layer set per super-block format (all seven
+matrices in one grouped launch, and in the launches a decode step's data dependencies
+allow), the 70B-like layer set at batch 1, 2, 4 and 8 (one launch per matrix, and one
+grouped launch), and the 512-row prefill GEMM (TFLOP/s and fraction of the 2.5 PFLOP/s
+dense fp16 MFMA peak).
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -153,11 +155,12 @@ def _graph_time_us(fn, rounds, reps=3):
     return sorted(times)[len(times) // 2]
 
 
-def measure_set(qg, fmt, canon_shapes, m, dev, footprint_gb=1.2, rounds=24):
-    """One decode step over a set of matrices (batch m), with the weights rotated over enough
-    copies that every round reads them from HBM. At batch 1 consecutive matrices of one shape
-    go out as one strided batched launch (q/k/v/o, or gate/up, of a layer); otherwise one
-    launch per matrix. Returns (algorithmic bytes per round, microseconds per round)."""
+def measure_set(qg, fmt, canon_shapes, m, dev, plan, footprint_gb=1.2, rounds=24):
+    """One pass over a set of matrices (batch m), with the weights rotated over enough copies
+    that every round reads them from HBM. `plan` lists the launches of a round: ("group",
+    [i, ...]) is one grouped launch of those matrices (any shapes), ("batched", [i, ...]) one
+    strided batched launch of consecutive same-shape matrices (m = 1), ("single", [i]) one
+    qg_gemm (qg_gemv at m = 1). Returns (algorithmic bytes per round, microseconds per round)."""
     import numpy as np
     import torch
     from workloads import activations
@@ -174,24 +177,33 @@ def measure_set(qg, fmt, canon_shapes, m, dev, footprint_gb=1.2, rounds=24):
             o = c * set_bytes + int(offs[j])
             buf[o:o + lays[j].total_bytes].copy_(one)
         del one
-    # groups of consecutive same-shape matrices: (first index, count, n, k)
-    groups = []
-    for j, (_, n, k) in enumerate(canon_shapes):
-        if m == 1 and groups and tuple(groups[-1][2:]) == (n, k):
-            groups[-1][1] += 1
+    shapes = [(n, k) for _, n, k in canon_shapes]
+    launches = []
+    for kind, idx in plan:
+        if kind == "batched":
+            n, k = shapes[idx[0]]
+            X = torch.from_numpy(activations(len(idx), k, 11 + idx[0])).to(dev)
+            Y = torch.empty((len(idx), n), dtype=torch.float16, device=dev)
         else:
-            groups.append([j, 1, n, k])
-    xs = [torch.from_numpy(activations(max(m, cnt), k, 11 + j)).to(dev) for j, cnt, n, k in groups]
-    ys = [torch.empty((max(m, cnt), n), dtype=torch.float16, device=dev) for j, cnt, n, k in groups]
+            X = [torch.from_numpy(activations(m, shapes[i][1], 11 + i)).to(dev) for i in idx]
+            Y = [torch.empty((m, shapes[i][0]), dtype=torch.float16, device=dev) for i in idx]
+        launches.append((kind, idx, X, Y))
 
-    def rnd(i):
-        c = i % copies
-        for (j, cnt, n, k), x, y in zip(groups, xs, ys):
-            w = buf[c * set_bytes + int(offs[j]):]
-            if m == 1:
-                qg.gemv_batched(fmt, w, strides[j], x, y, cnt, n, k)
+    def rnd(r):
+        base = (r % copies) * set_bytes
+        for kind, idx, X, Y in launches:
+            if kind == "batched":
+                n, k = shapes[idx[0]]
+                qg.gemv_batched(fmt, buf[base + int(offs[idx[0]]):], strides[idx[0]], X, Y, len(idx), n, k)
+            elif kind == "group":
+                qg.gemm_grouped(fmt, [buf[base + int(offs[i]):] for i in idx], X, [shapes[i] for i in idx], outs=Y)
             else:
-                qg.gemm(fmt, w, x, n, k, out=y)
+                (i,) = idx
+                n, k = shapes[i]
+                if m == 1:
+                    qg.gemv(fmt, buf[base + int(offs[i]):], X[0][0], n, k, out=Y[0][0])
+                else:
+                    qg.gemm(fmt, buf[base + int(offs[i]):], X[0], n, k, out=Y[0])
 
     us = _graph_time_us(rnd, rounds)
     del buf
@@ -199,41 +211,52 @@ def measure_set(qg, fmt, canon_shapes, m, dev, footprint_gb=1.2, rounds=24):
     return alg, us
 
 
+def _rate(alg, us):
+    return {"GBps": round(alg / us / 1e3, 1), "frac": round(alg / us / 1e3 / HBM_PEAK_GBPS, 4), "us": round(us, 2)}
+
+
 def extra_configs(qg, dev):
-    """The other workloads on this one GPU: INT4 4096^2 at batch 1, the 7B-like layer set
-    (q/k/v/o, gate/up, down) per super-block format, the 70B-like set at batch 1, 2, 4 and 8,
-    and the 512-row prefill GEMM."""
-    from workloads import WORKLOADS, activations
+    """The other workloads on this one GPU: INT4 group-32 4096^2 at batch 1, the 7B-like layer
+    set (q/k/v/o, gate/up, down) per super-block format, the 70B-like set at batch 1, 2, 4
+    and 8, and the 512-row prefill GEMM."""
+    from workloads import WORKLOADS
     out = {}
-    # INT4 group-32 4096 x 4096, batch 1: grouped like the headline, and as a single launch
+    # INT4 group-32 4096 x 4096, batch 1: 32 per launch like the headline, and one per launch
     wl = WORKLOADS["q4g32_gemv_4096"]
     canon = qg.quantize("q4g32", wl.weights(0))
-    alg, us = measure_set(qg, "q4g32", [(canon, 4096, 4096)] * 32, 1, dev, rounds=16)
-    alg1, us1 = measure_set(qg, "q4g32", [(canon, 4096, 4096)], 1, dev, rounds=200)
+    alg, us = measure_set(qg, "q4g32", [(canon, 4096, 4096)] * 32, 1, dev, [("batched", list(range(32)))], rounds=16)
+    alg1, us1 = measure_set(qg, "q4g32", [(canon, 4096, 4096)], 1, dev, [("single", [0])], rounds=200)
     out["q4g32_gemv_4096"] = {"GBps_32_per_launch": round(alg / us / 1e3, 1), "frac": round(alg / us / 1e3 / HBM_PEAK_GBPS, 4),
                               "GBps_single_launch": round(alg1 / us1 / 1e3, 1), "us_single_launch": round(us1, 2)}
     log(f"[bench] q4g32 4096^2: {out['q4g32_gemv_4096']}")
-    # 7B-like layer set, batch 1, each format (the four share one set of fp32 weights)
+    # 7B-like layer set, batch 1, each format (the four share one set of fp32 weights). Matrices
+    # 0-3 are q, k, v, o; 4, 5 gate, up; 6 down. "one_launch": all seven in one grouped launch;
+    # "decode_order": the launches a decode step can issue given its data dependencies
+    # ({q, k, v} share x; o waits for attention; {gate, up} share x; down waits for both).
     wl = WORKLOADS["q3sb_7b_layer_set"]
     w7 = [wl.weights(i) for i in range(len(wl.shapes))]
     for fmt in ("q2sb", "q3sb", "q5sb", "q6sb"):
         cs = [(qg.quantize(fmt, w), w.shape[0], w.shape[1]) for w in w7]
-        alg, us = measure_set(qg, fmt, cs, 1, dev)
-        out[f"{fmt}_7b_layer_set"] = {"GBps": round(alg / us / 1e3, 1), "frac": round(alg / us / 1e3 / HBM_PEAK_GBPS, 4),
-                                      "us_per_set": round(us, 2), "bytes_per_set": alg}
+        alg, us = measure_set(qg, fmt, cs, 1, dev, [("group", list(range(7)))])
+        alg2, us2 = measure_set(qg, fmt, cs, 1, dev, [("group", [0, 1, 2]), ("single", [3]), ("group", [4, 5]),
+                                                      ("single", [6])])
+        out[f"{fmt}_7b_layer_set"] = {**_rate(alg, us), "bytes_per_set": alg,
+                                      "decode_order": _rate(alg2, us2)}
         log(f"[bench] {fmt} 7B layer set: {out[f'{fmt}_7b_layer_set']}")
     del w7
-    # 70B-like layer set at batch 1, 2, 4, 8 (q3sb and q5sb share the fp32 weights)
+    # 70B-like layer set at batch 1, 2, 4, 8 (q3sb and q5sb share the fp32 weights): one launch
+    # per matrix (the matrices depend on each other in a decode step), and all three in one
+    # grouped launch
     wl = WORKLOADS["q3sb_70b_layer_set_m1"]
     w70 = [wl.weights(i) for i in range(len(wl.shapes))]
     for fmt in ("q3sb", "q5sb"):
         cs = [(qg.quantize(fmt, w), w.shape[0], w.shape[1]) for w in w70]
         for m in (1, 2, 4, 8):
-            alg, us = measure_set(qg, fmt, cs, m, dev, rounds=12)
+            alg, us = measure_set(qg, fmt, cs, m, dev, [("single", [0]), ("single", [1]), ("single", [2])], rounds=12)
+            alg2, us2 = measure_set(qg, fmt, cs, m, dev, [("group", [0, 1, 2])], rounds=12)
             flops = 2 * m * sum(n * k for _, n, k in cs)
-            out[f"{fmt}_70b_layer_set_m{m}"] = {"GBps": round(alg / us / 1e3, 1),
-                                                "frac": round(alg / us / 1e3 / HBM_PEAK_GBPS, 4),
-                                                "us_per_set": round(us, 2), "TFLOPs": round(flops / us / 1e6, 2)}
+            out[f"{fmt}_70b_layer_set_m{m}"] = {**_rate(alg, us), "TFLOPs": round(flops / us / 1e6, 2),
+                                                "one_launch": _rate(alg2, us2)}
             log(f"[bench] {fmt} 70B layer set m={m}: {out[f'{fmt}_70b_layer_set_m{m}']}")
         del cs
     del w70
@@ -242,7 +265,7 @@ def extra_configs(qg, dev):
         wl = WORKLOADS[f"{fmt}_prefill_512"]
         n, k = wl.shapes[0]
         canon = qg.quantize(fmt, wl.weights(0))
-        alg, us = measure_set(qg, fmt, [(canon, n, k)], 512, dev, rounds=10)
+        alg, us = measure_set(qg, fmt, [(canon, n, k)], 512, dev, [("single", [0])], rounds=10)
         tf = 2 * 512 * n * k / us / 1e6
         out[f"{fmt}_prefill_512"] = {"TFLOPs": round(tf, 1), "mfma_frac_of_fp16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
                                      "us": round(us, 2), "weight_GBps": round(alg / us / 1e3, 1)}

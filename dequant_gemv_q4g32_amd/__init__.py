@@ -66,6 +66,7 @@ def _load() -> ctypes.CDLL:
         "qg_gemv": ([i32, vp, vp, vp, i32, i64, i64, vp], i32),
         "qg_gemv_batched": ([i32, vp, i64, vp, i64, vp, i64, i32, i64, i64, i64, vp], i32),
         "qg_gemm": ([i32, vp, vp, i64, vp, i64, i32, i64, i64, i64, vp], i32),
+        "qg_gemm_grouped": ([i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp], i32),
         "qg_dequantize": ([i32, vp, vp, vp, i64, i64, vp], i32),
         "qg_read_probe": ([vp, i64, vp, vp], i32),
     }
@@ -224,6 +225,29 @@ def gemm(fmt, w, X, n: int, k: int, out=None, out_f32: bool = False, stream=None
     _check(_lib.qg_gemm(_fmt(fmt), w.data_ptr(), X.data_ptr(), X.stride(0), out.data_ptr(), out.stride(0),
                         int(out.dtype == torch.float32), m, n, k, _stream(stream)), "qg_gemm")
     return out
+
+
+def gemm_grouped(fmt, ws, Xs, shapes, outs=None, out_f32: bool = False, stream=None):
+    """One launch over several matrices: outs[g] = Xs[g] W_hat_g^T for W_g of shapes[g] = (n, k)
+    at ws[g] (device layout). Every Xs[g] is fp16 [m, k_g] (one m, at most 8, row stride
+    X.stride(0)) or [k_g] for m = 1; outs[g] is [m, n_g] (or [n_g]), allocated when None."""
+    torch = _torch()
+    count = len(ws)
+    if not (len(Xs) == len(shapes) == count):
+        raise ValueError("ws, Xs and shapes must have one entry per matrix")
+    vec = Xs[0].dim() == 1
+    m = 1 if vec else Xs[0].shape[0]
+    dt = torch.float32 if out_f32 else torch.float16
+    if outs is None:
+        outs = [torch.empty((n,) if vec else (m, n), dtype=dt, device=X.device) for X, (n, _) in zip(Xs, shapes)]
+    arr = lambda ctype, vals: (ctype * max(count, 1))(*vals)
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+    _check(_lib.qg_gemm_grouped(
+        _fmt(fmt), count, arr(vp, [w.data_ptr() for w in ws]), arr(vp, [X.data_ptr() for X in Xs]),
+        arr(i64, [X.stride(0) if X.dim() == 2 else X.shape[0] for X in Xs]), arr(vp, [y.data_ptr() for y in outs]),
+        arr(i64, [y.stride(0) if y.dim() == 2 else y.shape[0] for y in outs]), arr(i64, [n for n, _ in shapes]),
+        arr(i64, [k for _, k in shapes]), m, int(outs[0].dtype == torch.float32), _stream(stream)), "qg_gemm_grouped")
+    return outs
 
 
 def dequantize(fmt, w, n: int, k: int, values: bool = True, codes: bool = True, stream=None):

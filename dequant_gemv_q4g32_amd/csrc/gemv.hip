@@ -39,7 +39,9 @@ struct GemvArgs {
   int wk;                   // waves per workgroup along K
   int wr;                   // row groups per workgroup
   int kpasses;              // passes over K (wk > 1 whenever kpasses > 1)
-  int nb;                   // row batches per row group (each R rows)
+  int nb;                   // most row batches (each R rows) of any row group
+  int64_t groups;           // row batches per matrix
+  int64_t rgroups;          // row groups per matrix (gridDim.x * wr); they split the batches evenly
 };
 
 // ------------------------------------------------------------------ GEMV / small-M kernel -
@@ -59,8 +61,11 @@ struct GemvArgs {
 // on the 4 SIMDs of one CU) and the waves along K of one pass.
 template <int M> constexpr int mv_threads() { return M > 4 && QG_MV_THREADS > 512 ? 512 : QG_MV_THREADS; }
 
+// One workgroup of the streaming kernel over matrix b of a (block bx along the rows). Waves
+// past wk * wr (a grouped launch whose workgroup is sized for another matrix) have no rows
+// but still reach the barrier.
 template <int F, int M, int S, int R, bool MP>
-__global__ __launch_bounds__(mv_threads<M>()) void mv_kernel(GemvArgs a) {
+__device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b) {
   constexpr int D = M == 1 ? QG_GEMV_DEPTH : 2;   // pipeline stages
   using U = Unit<F>;
   using Raw = typename U::Raw;
@@ -75,7 +80,6 @@ __global__ __launch_bounds__(mv_threads<M>()) void mv_kernel(GemvArgs a) {
   const int wr = wave / a.wk;
   const int h = S == 1 ? 0 : (lane & 1);
 
-  const int64_t b = blockIdx.y;
   const uint8_t *w = a.w + b * a.w_bstride;
   const uint16_t *x = a.x + b * a.x_bstride;
 
@@ -86,20 +90,15 @@ __global__ __launch_bounds__(mv_threads<M>()) void mv_kernel(GemvArgs a) {
     L.prb[p] = (uint32_t)a.prb[p];
   }
 
-  // this row group's rows: nb consecutive batches of R rows; rows past n re-read row n-1
-  const int rows_here = R * a.nb;
-#ifndef QG_ROW_INTERLEAVE
-#define QG_ROW_INTERLEAVE 0
-#endif
-#if QG_ROW_INTERLEAVE
-  // batch j of row group g covers rows (j G + g) R .. + R - 1 (G row groups in the grid): the
-  // row groups walk the matrix side by side, so concurrent loads stay close together
-  const int64_t grp = (int64_t)blockIdx.x * a.wr + wr, ngrp = (int64_t)gridDim.x * a.wr;
-  auto row_of = [&](int j, int i) -> int64_t { return ((int64_t)j * ngrp + grp) * R + i; };
-#else
-  const int64_t row_begin = ((int64_t)blockIdx.x * a.wr + wr) * rows_here;
-  auto row_of = [&](int j, int i) -> int64_t { return row_begin + (int64_t)j * R + i; };
-#endif
+  // This row group's rows: batches [begin, end) of R rows, an even split of the matrix's
+  // batches over the grid's row groups (they differ by at most one batch); rows past n
+  // re-read row n-1.
+  const int64_t grp = bx * a.wr + wr;
+  const bool idle = wr >= a.wr;
+  const int64_t begin = idle ? 0 : grp * a.groups / a.rgroups, end = idle ? 0 : (grp + 1) * a.groups / a.rgroups;
+  const int nbh = (int)(end - begin);          // batches of this row group (0 only for tiny n)
+  const int rows_max = R * a.nb;               // LDS stride of a row group: a.nb >= every nbh
+  auto row_of = [&](int j, int i) -> int64_t { return (begin + j) * R + i; };
   auto store_y = [&](int mm, int64_t r, float v) {
     const int64_t i = b * a.y_bstride + (int64_t)mm * a.ldy + r;
     if (a.y_f32) reinterpret_cast<float *>(a.y)[i] = v;
@@ -110,6 +109,7 @@ __global__ __launch_bounds__(mv_threads<M>()) void mv_kernel(GemvArgs a) {
   // pass (long K with many activation rows) each wave accumulates its partial sums in LDS.
   const int passes = MP ? a.kpasses : 1;
   for (int kp = 0; kp < passes; ++kp) {
+    if (nbh == 0) break;                       // wave-uniform: a row group past the last batch
     const int64_t u_raw = ((int64_t)kp * a.wk + wk) * UPW + (S == 1 ? lane : lane >> 1);
     const bool act = u_raw < a.units;
     const int64_t u = act ? u_raw : 0;         // inactive lanes read unit 0 and contribute 0
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(mv_threads<M>()) void mv_kernel(GemvArgs a) {
     // D register stages: the loads of D - 1 batches are in flight while one is computed.
     // Prefetches past this row group's last batch re-load that batch (no extra HBM traffic).
     Raw qs[D][R];
-    auto load_batch_j = [&](Raw *q, int jb) { load_batch(q, row_of(jb < a.nb ? jb : a.nb - 1, 0)); };
+    auto load_batch_j = [&](Raw *q, int jb) { load_batch(q, row_of(jb < nbh ? jb : nbh - 1, 0)); };
 #pragma unroll
     for (int d = 0; d + 1 < D; ++d) load_batch_j(qs[d], d);   // weights first: their latency covers the x work
 
@@ -177,7 +177,7 @@ __global__ __launch_bounds__(mv_threads<M>()) void mv_kernel(GemvArgs a) {
             if (a.wk == 1) {
               if (r0 + i < a.n) store_y(mm, r0 + i, part[i][mm]);
             } else {
-              float &slot = red[((wr * rows_here + j * R + i) * M + mm) * a.wk + wk];
+              float &slot = red[((wr * rows_max + j * R + i) * M + mm) * a.wk + wk];
               slot = (MP && kp) ? slot + part[i][mm] : part[i][mm];
             }
           }
@@ -187,10 +187,10 @@ __global__ __launch_bounds__(mv_threads<M>()) void mv_kernel(GemvArgs a) {
     // Software pipeline, D batches per iteration so that every stage stays in fixed registers.
     // Loads are unconditional, so the wait before each compute covers only the oldest stage
     // (a conditional prefetch would force a wait for everything in flight).
-    for (int j = 0; j < a.nb; j += D) {
+    for (int j = 0; j < nbh; j += D) {
 #pragma unroll
       for (int d = 0; d < D; ++d) {
-        if (j + d >= a.nb) break;
+        if (j + d >= nbh) break;
         load_batch_j(qs[(d + D - 1) % D], j + d + D - 1);
         finish_batch(qs[d], j + d);
       }
@@ -201,14 +201,36 @@ __global__ __launch_bounds__(mv_threads<M>()) void mv_kernel(GemvArgs a) {
   // partial sums of all its (row, m) outputs and writes them (one output per lane)
   __syncthreads();
   if (wk == 0) {
-    for (int i = lane; i < rows_here * M; i += 64) {
+    for (int i = lane; i < R * nbh * M; i += 64) {
       const int64_t r = row_of(i / M / R, i / M % R);
       const int mm = i % M;
       float sum = 0.f;
-      for (int jj = 0; jj < a.wk; ++jj) sum += red[(wr * rows_here * M + i) * a.wk + jj];
+      for (int jj = 0; jj < a.wk; ++jj) sum += red[(wr * rows_max * M + i) * a.wk + jj];
       if (r < a.n && mm < a.m) store_y(mm, r, sum);
     }
   }
+}
+
+template <int F, int M, int S, int R, bool MP>
+__global__ __launch_bounds__(mv_threads<M>()) void mv_kernel(GemvArgs a) {
+  mv_body<F, M, S, R, MP>(a, blockIdx.x, blockIdx.y);
+}
+
+// Several matrices (any shapes, one activation-row count) in one launch: blocks
+// [block_end[g-1], block_end[g]) serve matrix g.
+constexpr int kMaxGroup = 8;
+struct GemvGroup {
+  int count;
+  int64_t block_end[kMaxGroup];
+  GemvArgs g[kMaxGroup];
+};
+
+template <int F, int M, int S, int R, bool MP>
+__global__ __launch_bounds__(mv_threads<M>()) void mv_group_kernel(GemvGroup G) {
+  const int64_t bx = blockIdx.x;
+  int gi = 0;
+  while (gi + 1 < G.count && bx >= G.block_end[gi]) ++gi;
+  mv_body<F, M, S, R, MP>(G.g[gi], bx - (gi ? G.block_end[gi - 1] : 0), 0);
 }
 
 __global__ void fill_zero_kernel(void *y, int64_t count, int f32, int64_t bstride, int64_t n) {
@@ -399,7 +421,10 @@ int fill_args(int fmt, const void *w, int64_t n, int64_t k, GemvArgs &a) {
 
 constexpr int64_t kSimds = 1024;           // 256 CUs x 4 SIMDs
 constexpr int kMaxBatches = 32;
-constexpr int kMinBatches = 4;
+#ifndef QG_MV_MIN_BATCHES
+#define QG_MV_MIN_BATCHES 4
+#endif
+constexpr int kMinBatches = QG_MV_MIN_BATCHES;
 constexpr int kMaxM = 8;                   // activation rows one streaming launch serves
 constexpr int kSkinnyMaxM = 16;            // activation rows of the matrix-core decode kernel
 
@@ -410,49 +435,154 @@ int waves_per_simd(const void *kernel) {
   return blocks / 4 > 8 ? 8 : blocks / 4;
 }
 
+// Row groups of one matrix: about nbt batches (of R rows) each, at most kMaxBatches (the
+// partial sums of a row group fit in LDS), whole workgroups of wr row groups, batches split
+// evenly. Returns the workgroups along the rows.
+int64_t split_rows(GemvArgs &a, int R, int64_t nbt) {
+  const int64_t groups = (a.n + R - 1) / R;
+  int64_t rg = groups / nbt;
+  const int64_t rg_cap = (groups + kMaxBatches - 1) / kMaxBatches;
+  rg = rg < rg_cap ? rg_cap : rg;
+  rg = rg < 1 ? 1 : (rg > groups ? groups : rg);
+  const int64_t blocks = (rg + a.wr - 1) / a.wr;
+  a.groups = groups;
+  a.rgroups = blocks * a.wr;
+  a.nb = (int)((groups + a.rgroups - 1) / a.rgroups);
+  return blocks;
+}
+
+size_t red_bytes(const GemvArgs &a, int R, int M) {
+  return a.wk > 1 ? (size_t)a.wr * R * a.nb * M * a.wk * sizeof(float) : 0;
+}
+
+// Launch shape of the streaming kernel over `ng` matrix shapes (count[g] matrices of n[g]
+// rows and wk[g] waves along K each). Every workgroup has W waves; matrix g gets
+// wr_g = W / wk_g row groups per workgroup, and waves past wr_g * wk_g idle until the
+// workgroup's barrier. Whole workgroups fit a CU's wave slots floor(slots / W) times. Row
+// groups take nbt batches each: one resident round of waves (no tail round), but at least
+// kMinBatches, so that a wave's activation load and first load latency are spread over
+// several rows (fewer, longer waves beat a full grid of very short ones here). W is chosen
+// for the fewest wasted wave slots, times the fraction of the 256 CUs that get a workgroup
+// at all (a small matrix in large workgroups would leave most CUs idle); the smaller W on
+// ties (idle waves and coarse workgroups cost more than the score shows).
+struct MvPlan {
+  int W;
+  int64_t nbt;
+};
+MvPlan plan_mv(int ng, const int64_t *n, const int *wk, const int64_t *count, int R, int wps, int max_w) {
+  const int slots = 4 * wps;
+  int64_t work[kMaxGroup], total = 0;
+  int wk_max = 1;
+  for (int g = 0; g < ng; ++g) {
+    work[g] = (n[g] + R - 1) / R * wk[g] * count[g];           // row batches x waves along K
+    total += work[g];
+    wk_max = wk[g] > wk_max ? wk[g] : wk_max;
+  }
+  MvPlan best{wk_max, kMinBatches};
+  double best_score = -1.0;
+  for (int W = wk_max; W <= max_w && W <= slots; ++W) {
+    double used = 0.0;
+    for (int g = 0; g < ng; ++g) used += (double)work[g] * (W / wk[g] * wk[g]) / W;
+    const int64_t per_cu = slots / W;
+    const int64_t resident = (int64_t)256 * per_cu * W;
+    int64_t nbt = (total + resident - 1) / resident;
+    nbt = nbt < kMinBatches ? kMinBatches : nbt;
+    int64_t blocks = 0;
+    for (int g = 0; g < ng; ++g) {
+      const int64_t groups = (n[g] + R - 1) / R;
+      int64_t rg = groups / nbt;
+      const int64_t rg_cap = (groups + kMaxBatches - 1) / kMaxBatches;
+      rg = rg < rg_cap ? rg_cap : rg;
+      rg = rg < 1 ? 1 : (rg > groups ? groups : rg);
+      blocks += count[g] * ((rg + W / wk[g] - 1) / (W / wk[g]));
+    }
+    const double score = used / (double)total * (double)(per_cu * W) / slots *
+                         (blocks >= 256 ? 1.0 : (double)blocks / 256);
+    if (score > best_score + 1e-9) {
+      best_score = score;
+      best = {W, nbt};
+    }
+  }
+  return best;
+}
+
 template <int F, int M, int S, int R, bool MP>
 int launch_mv(GemvArgs a, int64_t count, hipStream_t s) {
   void (*kern)(GemvArgs) = mv_kernel<F, M, S, R, MP>;
   static const int wps = waves_per_simd(reinterpret_cast<const void *>(kern));
-  const int64_t groups_per_matrix = (a.n + R - 1) / R;          // batches of R rows
-  const int64_t target = kSimds * wps / a.wk;                   // row groups resident at once
-  // Batches per row group: enough to fill the resident slots once, but at least kMinBatches,
-  // so that a wave's activation load and first load latency are spread over several rows
-  // (a grid with fewer, longer waves beats a full one of very short waves).
-  int64_t nb = (groups_per_matrix * count) / target;
-  nb = nb < kMinBatches ? kMinBatches : (nb > kMaxBatches ? kMaxBatches : nb);
-  a.nb = (int)nb;
-  const int64_t rows_per_block = (int64_t)a.wr * R * nb;
-  dim3 grid((unsigned)((a.n + rows_per_block - 1) / rows_per_block), (unsigned)count);
-  dim3 block((unsigned)(64 * a.wk * a.wr));
-  size_t shm = a.wk > 1 ? (size_t)a.wr * R * nb * M * a.wk * sizeof(float) : 0;
-  return launch(kern, grid, block, shm, s, a);
+  const MvPlan P = plan_mv(1, &a.n, &a.wk, &count, R, wps, mv_threads<M>() / 64);
+  a.wr = P.W / a.wk;
+  const int64_t blocks = split_rows(a, R, P.nbt);
+  dim3 grid((unsigned)blocks, (unsigned)count);
+  return launch(kern, grid, dim3((unsigned)(64 * P.W)), red_bytes(a, R, M), s, a);
 }
 
-// Waves along K: one per 64 / S units. Rows per batch: 2 (double-buffered, so four rows of
-// loads per wave in flight without spilling) when there are enough rows to keep every SIMD
-// busy, else 1: small problems are bound by latency and get as many waves as possible. With
-// M > 2 the activation registers leave room for one row per batch only.
-template <int F, int M, int S>
-int launch_mv_s(GemvArgs a, int64_t count, hipStream_t s) {
+template <int F, int M, int S, int R, bool MP>
+int launch_mv_group(GemvGroup &G, hipStream_t s) {
+  void (*kern)(GemvGroup) = mv_group_kernel<F, M, S, R, MP>;
+  static const int wps = waves_per_simd(reinterpret_cast<const void *>(kern));
+  int64_t n[kMaxGroup], count[kMaxGroup];
+  int wk[kMaxGroup];
+  for (int g = 0; g < G.count; ++g) {
+    n[g] = G.g[g].n;
+    wk[g] = G.g[g].wk;
+    count[g] = 1;
+  }
+  const MvPlan P = plan_mv(G.count, n, wk, count, R, wps, mv_threads<M>() / 64);
+  int64_t blocks = 0;
+  size_t shm = 0;
+  for (int g = 0; g < G.count; ++g) {
+    G.g[g].wr = P.W / G.g[g].wk;
+    blocks += split_rows(G.g[g], R, P.nbt);
+    G.block_end[g] = blocks;
+    const size_t r = red_bytes(G.g[g], R, M);
+    shm = r > shm ? r : shm;
+  }
+  if (blocks > 0x7FFFFFFF) return QG_ERR_SHAPE;
+  return launch(kern, dim3((unsigned)blocks), dim3((unsigned)(64 * P.W)), shm, s, G);
+}
+
+// Waves along K: one per 64 / S units, in passes of at most the workgroup's waves.
+template <int M, int S>
+int set_k_split(GemvArgs &a) {
   constexpr int UPW = 64 / S;
   constexpr int max_wk = mv_threads<M>() / 64;                // the kernel's block-size bound
   const int64_t waves_k = (a.units + UPW - 1) / UPW;
   const int64_t passes = (waves_k + max_wk - 1) / max_wk;
   if (passes > 64) return QG_ERR_SHAPE;
-  const int wk = (int)((waves_k + passes - 1) / passes);
   a.kpasses = (int)passes;
-  a.wk = wk;
-  a.wr = wk >= 4 ? 1 : 4 / wk;
-  if (passes > 1) return launch_mv<F, M, S, 1, true>(a, count, s);
-#ifndef QG_GEMV_R2
-#define QG_GEMV_R2 1
-#endif
-  if constexpr (M <= 2 && QG_GEMV_R2) {
-    const int64_t rows = a.n * count, target = kSimds * 4 / wk;
-    if (rows >= 2 * target) return launch_mv<F, M, S, 2, false>(a, count, s);
-  }
+  a.wk = (int)((waves_k + passes - 1) / passes);
+  return QG_OK;
+}
+
+// Rows per batch: 2 (double-buffered, so four rows of loads per wave in flight without
+// spilling) when there are enough rows to keep every SIMD busy, else 1: small problems are
+// bound by latency and get as many waves as possible. With M > 2 the activation registers
+// leave room for one row per batch only.
+template <int F, int M, int S>
+int launch_mv_s(GemvArgs a, int64_t count, hipStream_t s) {
+  int st = set_k_split<M, S>(a);
+  if (st != QG_OK) return st;
+  if (a.kpasses > 1) return launch_mv<F, M, S, 1, true>(a, count, s);
+  if constexpr (M <= 2)
+    if (a.n * count * a.wk >= 2 * kSimds * 4) return launch_mv<F, M, S, 2, false>(a, count, s);
   return launch_mv<F, M, S, 1, false>(a, count, s);
+}
+
+template <int F, int M, int S>
+int launch_mv_group_s(GemvGroup &G, hipStream_t s) {
+  int64_t rows = 0;
+  bool mp = false;
+  for (int g = 0; g < G.count; ++g) {
+    int st = set_k_split<M, S>(G.g[g]);
+    if (st != QG_OK) return st;
+    mp = mp || G.g[g].kpasses > 1;
+    rows += G.g[g].n * G.g[g].wk;
+  }
+  if (mp) return launch_mv_group<F, M, S, 1, true>(G, s);
+  if constexpr (M <= 2)
+    if (rows >= 2 * kSimds * 4) return launch_mv_group<F, M, S, 2, false>(G, s);
+  return launch_mv_group<F, M, S, 1, false>(G, s);
 }
 
 // M = 1: a lane owns a whole unit (32 activation VGPRs). M = 2..8: two lanes share a unit, so
@@ -468,6 +598,17 @@ int launch_mv_f(GemvArgs a, int64_t count, hipStream_t s) {
   }
 }
 
+template <int F>
+int launch_mv_group_f(GemvGroup &G, hipStream_t s) {
+  switch (G.g[0].m) {
+    case 1: return launch_mv_group_s<F, 1, 1>(G, s);
+    case 2: return launch_mv_group_s<F, 2, 2>(G, s);
+    case 3:
+    case 4: return launch_mv_group_s<F, 4, 2>(G, s);
+    default: return launch_mv_group_s<F, 8, 2>(G, s);
+  }
+}
+
 int launch_mv_fmt(int fmt, GemvArgs a, int64_t count, hipStream_t s) {
   if (a.m < 1 || a.m > kMaxM) return QG_ERR_SHAPE;
   switch (fmt) {
@@ -480,6 +621,16 @@ int launch_mv_fmt(int fmt, GemvArgs a, int64_t count, hipStream_t s) {
   return QG_ERR_FORMAT;
 }
 
+int launch_mv_group_fmt(int fmt, GemvGroup &G, hipStream_t s) {
+  switch (fmt) {
+    case 2: return launch_mv_group_f<2>(G, s);
+    case 3: return launch_mv_group_f<3>(G, s);
+    case 4: return launch_mv_group_f<4>(G, s);
+    case 5: return launch_mv_group_f<5>(G, s);
+    case 6: return launch_mv_group_f<6>(G, s);
+  }
+  return QG_ERR_FORMAT;
+}
 
 }  // namespace
 
@@ -563,6 +714,51 @@ int qg_gemm(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int
   a.y_f32 = y_f32;
   a.m = m;
   return launch_mv_fmt(fmt, a, 1, s);
+}
+
+int qg_gemm_grouped(int fmt, int count, const void *const *w, const uint16_t *const *X, const int64_t *ldx,
+                    void *const *Y, const int64_t *ldy, const int64_t *n, const int64_t *k, int64_t m, int y_f32,
+                    void *stream) {
+  if (!fmt_valid(fmt)) return QG_ERR_FORMAT;
+  if (count < 0 || count > kMaxGroup || m < 0 || m > kMaxM) return QG_ERR_SHAPE;
+  if (count > 0 && (!w || !X || !Y || !n || !k || (m > 1 && (!ldx || !ldy)))) return QG_ERR_NULL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const size_t esz = y_f32 ? 4 : 2;
+  GemvGroup G{};
+  // every matrix is checked before anything is launched
+  for (int g = 0; g < count; ++g) {
+    const int64_t lx = m > 1 ? ldx[g] : k[g], ly = m > 1 ? ldy[g] : n[g];
+    if (n[g] < 0 || k[g] < 0) return QG_ERR_SHAPE;
+    if ((fmt == 4 && k[g] % 32) || (fmt != 4 && k[g] % kQK)) return QG_ERR_SHAPE;
+    if (m > 1 && (lx < k[g] || ly < n[g])) return QG_ERR_SHAPE;
+    if (k[g] > kMaxK) return QG_ERR_SHAPE;
+    if (n[g] == 0 || m == 0) continue;
+    if (!Y[g] || (k[g] > 0 && (!w[g] || !X[g]))) return QG_ERR_NULL;
+    if (!aligned(Y[g], esz)) return QG_ERR_ALIGN;
+    if (k[g] == 0) continue;
+    if (!aligned(w[g], 256) || !aligned(X[g], 16) || (m > 1 && lx % 8)) return QG_ERR_ALIGN;
+    GemvArgs &a = G.g[G.count];
+    int st = fill_args(fmt, w[g], n[g], k[g], a);
+    if (st != QG_OK) return st;
+    a.x = X[g];
+    a.ldx = lx;
+    a.y = Y[g];
+    a.ldy = ly;
+    a.y_f32 = y_f32;
+    a.m = m;
+    ++G.count;
+  }
+  for (int g = 0; g < count && m > 0; ++g) {
+    if (n[g] == 0 || k[g] != 0) continue;
+    for (int64_t i = 0; i < m; ++i) {
+      const int64_t ly = m > 1 ? ldy[g] : n[g];
+      int st = launch(fill_zero_kernel, dim3((unsigned)((n[g] + 255) / 256)), dim3(256), 0, s,
+                      static_cast<void *>(static_cast<char *>(Y[g]) + i * ly * esz), n[g], y_f32, (int64_t)0, n[g]);
+      if (st != QG_OK) return st;
+    }
+  }
+  if (G.count == 0) return QG_OK;
+  return launch_mv_group_fmt(fmt, G, s);
 }
 
 int dequant_gemv_q4g32(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(4, w, x, y, 0, n, k, s); }

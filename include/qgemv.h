@@ -162,8 +162,13 @@ int qg_gemv_batched(int fmt, const void *w, int64_t w_stride, const uint16_t *x,
  * decode: the weights are streamed once per launch and each decoded code meets all the
  * launch's activation rows, up to 8 of them ("二三五六位量化" page section 1.2: decode
  * batches and prefill are the same contraction with more activation rows; DBHOO-CIM page
- * section 6: still bandwidth-bound at small batch). Larger m is served 8 rows per launch.
- * Limits as dequant_gemv_*. m == 0 or n == 0 is a no-op; k == 0 writes zeros. Errors as dequant_gemv_*. */
+ * section 6: still bandwidth-bound at small batch, compute-bound at large batch). Any m >= 1:
+ * m <= 4 runs on the vector units (each decoded code pair meets every activation row in a
+ * v_dot2), 5 <= m <= 16 decodes each code once to fp16 and multiplies on the matrix cores
+ * in the same single weight stream, and m > 16 (prefill) stages fp16 weight and activation
+ * tiles in LDS for 32x32 matrix-core tiles. Limits as dequant_gemv_*; for m > 4 also
+ * ldx < 2^23 (32-bit activation offsets within a 128-row tile). m == 0 or n == 0 is a no-op; k == 0 writes
+ * zeros. Errors as dequant_gemv_*. */
 int dequant_gemm_q4g32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
                        int64_t m, int64_t n, int64_t k, void *stream);
 int dequant_gemm_q2sb(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
@@ -177,6 +182,21 @@ int dequant_gemm_q6sb(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y
 /* Generic form; y_f32 != 0 writes fp32 Y (4-byte aligned). */
 int qg_gemm(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int64_t ldy, int y_f32,
             int64_t m, int64_t n, int64_t k, void *stream);
+
+/* Several matrices of any shapes, one activation-row count m (0..8), in one launch: for
+ * g < count (at most 8), Y_g [m][ldy[g]] = X_g [m][ldx[g]] * W_hat_g^T with W_g of n[g] x k[g]
+ * at w[g]. The arrays are host arrays read during the call; ldx and ldy are read only when
+ * m > 1 (else the rows are dense). Each matrix is checked as by qg_gemm (for m <= 8) before
+ * anything is launched; a matrix with n[g] == 0 is skipped and one with k[g] == 0 gets
+ * zeros. Every matrix runs on the streaming vector-unit kernel of qg_gemv and shares its
+ * numerics. This serves the projections of a decode step that read one activation (q, k and
+ * v; gate and up) or simply follow each other, with one launch's start and drain instead
+ * of one per matrix ("二三五六位量化" page section 1.2: the decode pass is one weight stream
+ * bound by bandwidth). Errors: QG_ERR_SHAPE (count > 8, m > 8, or a matrix's shape),
+ * QG_ERR_NULL, QG_ERR_ALIGN, QG_ERR_FORMAT, QG_ERR_LAUNCH. */
+int qg_gemm_grouped(int fmt, int count, const void *const *w, const uint16_t *const *X, const int64_t *ldx,
+                    void *const *Y, const int64_t *ldy, const int64_t *n, const int64_t *k, int64_t m, int y_f32,
+                    void *stream);
 
 /* ---- decode to memory (device; for verification, not for inference) ----------------------
  * Writes W_hat as fp32 [n][k] to w_out (if non-NULL) and the integer codes as uint8 [n][k]

@@ -161,3 +161,37 @@ def test_device_entry_points_validate_without_launching():
     assert L.qg_gemm(5, 256, 16, 256, 2, 4, 0, 2, 4, 100, None) == -2     # k % 256
     assert L.qg_gemm(8, 256, 16, 256, 2, 4, 0, 2, 4, 256, None) == -6     # format
     assert L.dequant_gemm_q6sb(256, 16, 256, 3, 4, 2, 4, 256, None) == -3  # Y misaligned
+
+
+def test_grouped_entry_point_validates_every_matrix_first():
+    """qg_gemm_grouped checks all matrices before launching anything: an error in the last
+    matrix is returned even though the first ones are valid (no GPU needed)."""
+    import ctypes
+    L = qg.lib
+    vp, i64 = ctypes.c_void_p, ctypes.c_int64
+
+    def call(fmt, ws, xs, ys, ns, ks, m=1, ldx=None, ldy=None, count=None):
+        c = len(ws) if count is None else count
+        arr = lambda t, v: (t * max(len(v), 1))(*v)
+        return L.qg_gemm_grouped(fmt, c, arr(vp, ws), arr(vp, xs), arr(i64, ldx or ks), arr(vp, ys),
+                                 arr(i64, ldy or ns), arr(i64, ns), arr(i64, ks), m, 0, None)
+
+    ok = dict(ws=[256, 512], xs=[16, 32], ys=[2, 4], ns=[4, 8], ks=[256, 512])
+    assert call(3, **{**ok, "ks": [256, 100]}) == -2                      # k % 256 in matrix 1
+    assert call(4, **{**ok, "ks": [256, 48]}) == -2                       # k % 32
+    assert call(3, **{**ok, "ws": [256, 300]}) == -3                      # w misaligned
+    assert call(3, **{**ok, "xs": [16, 18]}) == -3                        # x misaligned
+    assert call(3, **{**ok, "ys": [2, 3]}) == -3                          # y misaligned
+    assert call(3, **{**ok, "ws": [256, 0]}) == -1                        # null w
+    assert call(3, **{**ok, "ks": [256, (1 << 20) + 256]}) == -2          # k too long
+    assert call(3, **ok, m=9) == -2                                       # m > 8
+    assert call(3, **ok, m=-1) == -2
+    assert call(3, **ok, m=2, ldx=[256, 500]) == -2                       # ldx < k
+    assert call(3, **ok, m=2, ldy=[4, 7]) == -2                           # ldy < n
+    assert call(3, **ok, m=2, ldx=[260, 512]) == -3                       # ldx % 8
+    assert call(7, **ok) == -6                                            # format
+    assert call(3, [256] * 9, [16] * 9, [2] * 9, [4] * 9, [256] * 9) == -2   # more than 8
+    assert call(3, **ok, m=0) == 0                                        # m == 0: no-op
+    assert call(3, **{**ok, "ns": [0, 0]}) == 0                           # n == 0: no-op
+    assert L.qg_gemm_grouped(3, 0, None, None, None, None, None, None, None, 1, 0, None) == 0
+    assert L.qg_gemm_grouped(3, 1, None, None, None, None, None, None, None, 1, 0, None) == -1
