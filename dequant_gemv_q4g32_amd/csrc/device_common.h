@@ -58,15 +58,61 @@ __device__ __forceinline__ float dpp_move(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xF, false));
 }
 
-// Sum over the 64 lanes of a wave; the total lands in lane 63 (other lanes hold partials).
-__device__ __forceinline__ float wave_sum_to_63(float v) {
+// Cross-lane swaps of gfx950 (VOP1 v_permlane32_swap / v_permlane16_swap). permlane32: the
+// upper 32 lanes of a trade places with the lower 32 lanes of b, so a = [a_lo, b_lo] and
+// b = [a_hi, b_hi]. permlane16: the odd 16-lane rows of a trade places with the even rows of
+// b, so a = [a0, b0, a2, b2] and b = [a1, b1, a3, b3]. Written as inline assembly: the
+// compiler's builtins for them return one of the two swapped registers twice here. The
+// instruction must not read a VGPR within 2 wait states of the VALU write to it (4 after a
+// v_cmpx writes exec), which the compiler does not see inside the asm, so the asm waits 4;
+// the trailing wait keeps a following DPP read of the results clear of the same rule.
+__device__ __forceinline__ void lane_swap32(float &a, float &b) {
+  asm volatile("s_nop 3\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ void lane_swap16(float &a, float &b) {
+  asm volatile("s_nop 3\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 1" : "+v"(a), "+v"(b));
+}
+
+// Sum over each 16-lane row; every lane of a row ends with the row's sum.
+__device__ __forceinline__ float row_sum16(float v) {
   v += dpp_move<0xB1, 0xF>(v);    // quad_perm [1,0,3,2]
   v += dpp_move<0x4E, 0xF>(v);    // quad_perm [2,3,0,1]
   v += dpp_move<0x141, 0xF>(v);   // row_half_mirror
-  v += dpp_move<0x140, 0xF>(v);   // row_mirror: every lane of a row holds the row sum
-  v += dpp_move<0x142, 0xA>(v);   // row_bcast:15 into rows 1 and 3
-  v += dpp_move<0x143, 0xC>(v);   // row_bcast:31 into rows 2 and 3
+  v += dpp_move<0x140, 0xF>(v);   // row_mirror
   return v;
+}
+
+// Wave sums of T = 1, 2, 4 or 8 values per lane at once. Halving the lanes and the values
+// together (permlane32, then permlane16 swaps, each followed by one add per pair) costs
+// T/2 + T/4 swaps and adds before the per-row DPP sums, instead of six DPP steps per value.
+// Every value is summed in the same order whatever T is, ((v[l] + v[l+32]) + (v[l+16] +
+// v[l+48])) and then the 16-lane DPP tree (T = 1 and 2 swap with copies of themselves),
+// so a row's result does not depend on how many rows or activation rows share a wave.
+// Afterwards lane l holds total wave_sum_value(T, l, j) in v[j]:
+//   T = 1: every lane holds value 0 in v[0];
+//   T = 2: rows 0 and 1 (lanes 0-31) hold value 0, rows 2 and 3 value 1, in v[0];
+//   T >= 4: for j < T/4, every lane of row r = l/16 holds value 4j + {0, 2, 1, 3}[r] in v[j].
+template <int T>
+__device__ __forceinline__ void wave_sums(float *v) {
+  static_assert(T == 1 || T == 2 || T == 4 || T == 8, "values per lane");
+  if constexpr (T <= 2) {
+    float a = v[0], b = T == 2 ? v[1] : v[0];
+    lane_swap32(a, b);
+    float c = a + b, d = c;                    // lanes 0-31: value 0, lanes 32-63: value T - 1
+    lane_swap16(c, d);
+    v[0] = row_sum16(c + d);
+  } else {
+#pragma unroll
+    for (int p = 0; p < T / 2; ++p) {
+      lane_swap32(v[2 * p], v[2 * p + 1]);
+      v[p] = v[2 * p] + v[2 * p + 1];          // lanes 0-31: value 2p, lanes 32-63: 2p + 1
+    }
+#pragma unroll
+    for (int q = 0; q < T / 4; ++q) {
+      lane_swap16(v[2 * q], v[2 * q + 1]);
+      v[q] = row_sum16(v[2 * q] + v[2 * q + 1]);
+    }
+  }
 }
 
 // Raw buffer loads: the plane base lives in a buffer resource (scalar registers), the row

@@ -119,10 +119,11 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
     U::offsets(u, L.off);
     L.sh = fields_sh(u);
     L.set_halves(a.units);
+    L.h = h;
 
     auto load_batch = [&](Raw *q, int64_t r0) {
 #pragma unroll
-      for (int i = 0; i < R; ++i) U::load(q[i], L, r0 + i < a.n ? r0 + i : a.n - 1, half);
+      for (int i = 0; i < R; ++i) U::template load<kNT, S>(q[i], L, r0 + i < a.n ? r0 + i : a.n - 1, half);
     };
     // D register stages: the loads of D - 1 batches are in flight while one is computed.
     // Prefetches past this row group's last batch re-load that batch (no extra HBM traffic).
@@ -158,7 +159,9 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
 
     auto finish_batch = [&](const Raw *q, int j) {
       const int64_t r0 = row_of(j, 0);
-      float part[R][M];
+      // the batch's R x M partial sums, reduced over the wave together
+      constexpr int T = R * M;
+      float v[T];
 #pragma unroll
       for (int i = 0; i < R; ++i) {
         float o[M];
@@ -166,21 +169,29 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
         for (int mm = 0; mm < M; ++mm) o[mm] = 0.f;
         U::template dot<M, S>(q[i], h, xp, kc, o);
 #pragma unroll
-        for (int mm = 0; mm < M; ++mm) part[i][mm] = wave_sum_to_63(act ? o[mm] : 0.f);
+        for (int mm = 0; mm < M; ++mm) v[i * M + mm] = act ? o[mm] : 0.f;
       }
-      if (lane == 63) {
+      wave_sums<T>(v);
+      auto emit = [&](float val, int vi) {
+        const int i = vi / M, mm = vi % M;
+        if (mm >= a.m) return;
+        if (a.wk == 1) {
+          if (r0 + i < a.n) store_y(mm, r0 + i, val);
+        } else {
+          float &slot = red[((wr * rows_max + j * R + i) * M + mm) * a.wk + wk];
+          slot = (MP && kp) ? slot + val : val;
+        }
+      };
+      if constexpr (T == 1) {
+        if (lane == 63) emit(v[0], 0);
+      } else if constexpr (T == 2) {
+        if ((lane & 31) == 31) emit(v[0], lane >> 5);
+      } else {
+        if ((lane & 15) == 15) {
+          const int r = lane >> 4, pr = r == 1 ? 2 : (r == 2 ? 1 : r);
 #pragma unroll
-        for (int i = 0; i < R; ++i)
-#pragma unroll
-          for (int mm = 0; mm < M; ++mm) {
-            if (mm >= a.m) continue;
-            if (a.wk == 1) {
-              if (r0 + i < a.n) store_y(mm, r0 + i, part[i][mm]);
-            } else {
-              float &slot = red[((wr * rows_max + j * R + i) * M + mm) * a.wk + wk];
-              slot = (MP && kp) ? slot + part[i][mm] : part[i][mm];
-            }
-          }
+          for (int jj = 0; jj < T / 4; ++jj) emit(v[jj], 4 * jj + pr);
+        }
       }
     };
 

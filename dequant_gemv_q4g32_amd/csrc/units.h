@@ -23,6 +23,7 @@ struct Lane {
   uint32_t sh;              // bit offset of this unit's 6-bit fields in its 8-byte window
   uint32_t half16;          // offset of the second halves in a split 16-byte-half plane row
   uint32_t half4;           // same for the split q4g32 scale plane
+  int h = 0;                // the lane's half of its unit when two lanes share a unit
   __device__ uint32_t row(int p, int64_t r) const { return (uint32_t)r * prb[p]; }
   __device__ void set_halves(int64_t units) {
     half16 = (uint32_t)(units * 16);
@@ -76,8 +77,17 @@ template <> struct Unit<4> {
   struct Raw { u32x4 c0, c1; float s0, s1; };
   __device__ static int pidx(int h, int p, int S) { return S == 1 ? p : 16 * h + p; }
   __device__ static void offsets(int64_t u, uint32_t *off) { off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 4); }
-  template <int AUX = kNT> __device__ static void load(Raw &q, const Lane &L, int64_t r, bool half) {
+  // S = 2: the lane's own group only (half L.h of the unit), into c0 and s0
+  template <int AUX = kNT, int S = 1> __device__ static void load(Raw &q, const Lane &L, int64_t r, bool half) {
     const uint32_t r0 = L.row(0, r), r1 = L.row(1, r);
+    if constexpr (S == 2) {
+      // a half unit (k % 64 == 32) has no second group: that lane re-reads the first and
+      // meets zero activations
+      const bool second = L.h && !half;
+      q.c0 = bldx4<AUX>(L.rs[0], L.off[0] + (second ? L.half16 : 0u), r0);
+      q.s0 = __builtin_bit_cast(float, bld1(L.rs[1], L.off[1] + (second ? L.half4 : 0u), r1));
+      return;
+    }
     q.c0 = bldx4<AUX>(L.rs[0], L.off[0], r0);
     // a half unit (k % 64 == 32) has one group; its second group's activations are zero
     q.c1 = bldx4<AUX>(L.rs[0], L.off[0] + (half ? 0u : L.half16), r0);
@@ -106,8 +116,9 @@ template <> struct Unit<4> {
   __device__ static void dot(const Raw &q, int h, const uint32_t (*xp)[32 / S], const float (*kc)[NKS(S)], float *out) {
 #pragma unroll
     for (int g = 0; g < 2 / S; ++g) {
-      const u32x4 c = S == 1 ? (g ? q.c1 : q.c0) : (h ? q.c1 : q.c0);
-      const float scale = S == 1 ? (g ? q.s1 : q.s0) : (h ? q.s1 : q.s0);
+      // (S = 2 loaded the lane's own group into c0, s0)
+      const u32x4 c = S == 1 && g ? q.c1 : q.c0;
+      const float scale = S == 1 && g ? q.s1 : q.s0;
       float a1[M], a16[M];
 #pragma unroll
       for (int m = 0; m < M; ++m) { a1[m] = kc[m][g]; a16[m] = 0.f; }
@@ -157,8 +168,15 @@ template <> struct Unit<2> {
   __device__ static void offsets(int64_t u, uint32_t *off) {
     off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 4); off[2] = (uint32_t)((u >> 2) * 4);
   }
-  template <int AUX = kNT> __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
-    q.c = bldx4<AUX>(L.rs[0], L.off[0], L.row(0, r));
+  // S = 2: only the lane's own code dwords 2h, 2h+1, into c.x, c.y
+  template <int AUX = kNT, int S = 1> __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
+    if constexpr (S == 2) {
+      const u32x2 c = bldx2<AUX>(L.rs[0], L.off[0] + 8u * L.h, L.row(0, r));
+      q.c.x = c.x;
+      q.c.y = c.y;
+    } else {
+      q.c = bldx4<AUX>(L.rs[0], L.off[0], L.row(0, r));
+    }
     q.sc = bldx1<AUX>(L.rs[1], L.off[1], L.row(1, r));
     q.dd = bld1(L.rs[2], L.off[2], L.row(2, r));
   }
@@ -184,7 +202,7 @@ template <> struct Unit<2> {
     const uint32_t d[4] = {q.c.x, q.c.y, q.c.z, q.c.w};
 #pragma unroll
     for (int ii = 0; ii < 4 / S; ++ii) {
-      const uint32_t v = S == 1 ? d[ii] : sel(h, d[2 + ii], d[ii]);
+      const uint32_t v = d[ii];                // (S = 2 loaded the lane's dwords into d[0], d[1])
       const uint32_t v8 = v >> 8;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -249,7 +267,7 @@ template <> struct Unit<3> {
   __device__ static void offsets(int64_t u, uint32_t *off) {
     off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 8); off[2] = fields_off(u); off[3] = (uint32_t)((u >> 2) * 2);
   }
-  template <int AUX = kNT> __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
+  template <int AUX = kNT, int S = 1> __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
     q.a = bldx4<AUX>(L.rs[0], L.off[0], L.row(0, r));
     q.b = bldx2<AUX>(L.rs[1], L.off[1], L.row(1, r));
     q.f = fields24(L, 2, r);
@@ -395,11 +413,17 @@ template <> struct Unit<5> {
   __device__ static void offsets(int64_t u, uint32_t *off) {
     off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 8); off[2] = fields_off(u); off[3] = (uint32_t)((u >> 2) * 4);
   }
-  template <int AUX = kNT> __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
+  // S = 2: only the lane's own sub-block h: its nibble half into l0, its high-bit word into h.x
+  template <int AUX = kNT, int S = 1> __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
     const uint32_t r0 = L.row(0, r);
-    q.l0 = bldx4<AUX>(L.rs[0], L.off[0], r0);
-    q.l1 = bldx4<AUX>(L.rs[0], L.off[0] + L.half16, r0);
-    q.h = bldx2<AUX>(L.rs[1], L.off[1], L.row(1, r));
+    if constexpr (S == 2) {
+      q.l0 = bldx4<AUX>(L.rs[0], L.off[0] + (L.h ? L.half16 : 0u), r0);
+      q.h.x = bldx1<AUX>(L.rs[1], L.off[1] + 4u * L.h, L.row(1, r));
+    } else {
+      q.l0 = bldx4<AUX>(L.rs[0], L.off[0], r0);
+      q.l1 = bldx4<AUX>(L.rs[0], L.off[0] + L.half16, r0);
+      q.h = bldx2<AUX>(L.rs[1], L.off[1], L.row(1, r));
+    }
     q.f = fields24(L, 2, r);
     q.dd = bld1(L.rs[3], L.off[3], L.row(3, r));
   }
@@ -421,7 +445,9 @@ template <> struct Unit<5> {
   }
   template <int M, int S>
   __device__ static void dot(const Raw &q, int h, const uint32_t (*xp)[32 / S], const float (*kc)[NKS(S)], float *out) {
-    const uint32_t L[8] = {q.l0.x, q.l0.y, q.l0.z, q.l0.w, q.l1.x, q.l1.y, q.l1.z, q.l1.w};
+    // (S = 2 loaded the lane's own nibble half into l0 and its high-bit word into h.x)
+    const uint32_t L[8] = {q.l0.x, q.l0.y, q.l0.z, q.l0.w, S == 1 ? q.l1.x : 0u, S == 1 ? q.l1.y : 0u,
+                           S == 1 ? q.l1.z : 0u, S == 1 ? q.l1.w : 0u};
     const uint32_t f = q.f;
     const float dv = half_lo(q.dd), dm = half_hi(q.dd);
 #pragma unroll
@@ -430,12 +456,11 @@ template <> struct Unit<5> {
       float a1[M], a16[M];
 #pragma unroll
       for (int m = 0; m < M; ++m) { a1[m] = kc[m][sb]; a16[m] = 0.f; }
-      const uint32_t H = S == 1 ? (hh ? q.h.y : q.h.x) : sel(h, q.h.y, q.h.x);
+      const uint32_t H = S == 1 && hh ? q.h.y : q.h.x;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint32_t P[4];
-        const uint32_t Li = S == 1 ? L[4 * hh + i] : sel(h, L[4 + i], L[i]);
-        nib_pairs<1>(Li, H, i, P);
+        nib_pairs<1>(L[4 * hh + i], H, i, P);
 #pragma unroll
         for (int m = 0; m < M; ++m) {
           a1[m] = dot2(P[0], xp[m][16 * sb + 4 * i + 0], a1[m]);
@@ -484,11 +509,20 @@ template <> struct Unit<6> {
   __device__ static void offsets(int64_t u, uint32_t *off) {
     off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 16); off[2] = (uint32_t)(u * 4); off[3] = (uint32_t)((u >> 2) * 2);
   }
-  template <int AUX = kNT> __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
+  // S = 2: only the lane's own sub-blocks 2h, 2h+1: its nibble half into l0, its two
+  // high-field dwords into h.x, h.y
+  template <int AUX = kNT, int S = 1> __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
     const uint32_t r0 = L.row(0, r);
-    q.l0 = bldx4<AUX>(L.rs[0], L.off[0], r0);
-    q.l1 = bldx4<AUX>(L.rs[0], L.off[0] + L.half16, r0);
-    q.h = bldx4<AUX>(L.rs[1], L.off[1], L.row(1, r));
+    if constexpr (S == 2) {
+      q.l0 = bldx4<AUX>(L.rs[0], L.off[0] + (L.h ? L.half16 : 0u), r0);
+      const u32x2 hh = bldx2<AUX>(L.rs[1], L.off[1] + 8u * L.h, L.row(1, r));
+      q.h.x = hh.x;
+      q.h.y = hh.y;
+    } else {
+      q.l0 = bldx4<AUX>(L.rs[0], L.off[0], r0);
+      q.l1 = bldx4<AUX>(L.rs[0], L.off[0] + L.half16, r0);
+      q.h = bldx4<AUX>(L.rs[1], L.off[1], L.row(1, r));
+    }
     q.sc = bldx1<AUX>(L.rs[2], L.off[2], L.row(2, r));
     q.d = bldh(L.rs[3], L.off[3], L.row(3, r));
   }
@@ -508,20 +542,21 @@ template <> struct Unit<6> {
   }
   template <int M, int S>
   __device__ static void dot(const Raw &q, int h, const uint32_t (*xp)[32 / S], const float (*kc)[NKS(S)], float *out) {
-    const uint32_t L[8] = {q.l0.x, q.l0.y, q.l0.z, q.l0.w, q.l1.x, q.l1.y, q.l1.z, q.l1.w};
-    const uint32_t Hd[4] = {q.h.x, q.h.y, q.h.z, q.h.w};
+    // (S = 2 loaded the lane's own nibble half into l0 and its high-field dwords into h.x, h.y)
+    const uint32_t L[8] = {q.l0.x, q.l0.y, q.l0.z, q.l0.w, S == 1 ? q.l1.x : 0u, S == 1 ? q.l1.y : 0u,
+                           S == 1 ? q.l1.z : 0u, S == 1 ? q.l1.w : 0u};
+    const uint32_t Hd[4] = {q.h.x, q.h.y, S == 1 ? q.h.z : 0u, S == 1 ? q.h.w : 0u};
     const float dv = half_bits(q.d);
 #pragma unroll
     for (int j = 0; j < 4 / S; ++j) {
       float a1[M], a16[M];
 #pragma unroll
       for (int m = 0; m < M; ++m) { a1[m] = kc[m][j]; a16[m] = 0.f; }
-      const uint32_t H = S == 1 ? Hd[j] : sel(h, Hd[2 + j], Hd[j]);
+      const uint32_t H = Hd[j];
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii) {
         uint32_t P[4];
-        const uint32_t Li = S == 1 ? L[2 * j + ii] : sel(h, L[4 + 2 * j + ii], L[2 * j + ii]);
-        nib_pairs<2>(Li, H, ii, P);
+        nib_pairs<2>(L[2 * j + ii], H, ii, P);
 #pragma unroll
         for (int m = 0; m < M; ++m) {
           a1[m] = dot2(P[0], xp[m][8 * j + 4 * ii + 0], a1[m]);

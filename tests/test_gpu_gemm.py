@@ -163,3 +163,32 @@ def test_full_size_small_m_sampled_rows(fmt, i, names):
         y_ref, bound = oracle_y(w_hat, x)
         torch.cuda.synchronize()
         assert_close(y.cpu().float().numpy()[:, rows], y_ref, bound, f"{name}[{i}]")
+
+
+@pytest.mark.parametrize("fmt", ["q4g32", "q3sb", "q6sb"])
+def test_row_results_do_not_depend_on_launch_shape(fmt):
+    """A row's output is the same fp32 sum, bit for bit, whether its wave carries one row or
+    two rows per batch (large launches) and however many matrices share the launch: the
+    wave reduction adds the lanes in one fixed order. The first 64 rows of an 8192-row matrix
+    are quantized exactly like a 64-row matrix of the same weights (quantization is row-local)."""
+    n, k = 8192, 4096
+    w = laplace_weights(n, k, 0.02, 2024)
+    big, small = device_weights(fmt, w), device_weights(fmt, w[:64])
+    for m in (1, 2):
+        x = torch.from_numpy(activations(m, k, 31 + m)).cuda()
+        y_big = qg.gemm(fmt, big, x, n, k, out_f32=True)           # two rows per batch
+        y_small = qg.gemm(fmt, small, x, 64, k, out_f32=True)      # one row per batch
+        torch.cuda.synchronize()
+        assert torch.equal(y_big[:, :64], y_small), f"{fmt} m={m}"
+    # batch-1 strided batch of 8 copies (two rows per batch) against one launch per copy
+    lay = qg.device_layout(fmt, n, k)
+    stride = (lay.total_bytes + 255) // 256 * 256
+    buf = torch.zeros(8 * stride, dtype=torch.uint8, device="cuda")
+    for c in range(8):
+        buf[c * stride:c * stride + lay.total_bytes].copy_(big)
+    xs = torch.from_numpy(activations(8, k, 77)).cuda()
+    ys = torch.empty((8, n), dtype=torch.float32, device="cuda")
+    qg.gemv_batched(fmt, buf, stride, xs, ys, 8, n, k)
+    y0 = qg.gemv(fmt, small, xs[3], 64, k, out_f32=True)
+    torch.cuda.synchronize()
+    assert torch.equal(ys[3, :64], y0), f"{fmt} batched"
