@@ -475,7 +475,10 @@ size_t red_bytes(const GemvArgs &a, int R, int M) {
 // several rows (fewer, longer waves beat a full grid of very short ones here). W is chosen
 // for the fewest wasted wave slots, times the fraction of the 256 CUs that get a workgroup
 // at all (a small matrix in large workgroups would leave most CUs idle); the smaller W on
-// ties (idle waves and coarse workgroups cost more than the score shows).
+// ties, and no more than kMaxPlanW waves unless one matrix needs more along K (idle waves
+// and coarse workgroups cost more than the score shows: workgroups of 10 to 16 waves
+// measured up to 40% slower than 3 to 8 on the same grouped launch).
+constexpr int kMaxPlanW = 8;
 struct MvPlan {
   int W;
   int64_t nbt;
@@ -491,7 +494,7 @@ MvPlan plan_mv(int ng, const int64_t *n, const int *wk, const int64_t *count, in
   }
   MvPlan best{wk_max, kMinBatches};
   double best_score = -1.0;
-  for (int W = wk_max; W <= max_w && W <= slots; ++W) {
+  for (int W = wk_max; W <= max_w && W <= slots && (W <= kMaxPlanW || W == wk_max); ++W) {
     double used = 0.0;
     for (int g = 0; g < ng; ++g) used += (double)work[g] * (W / wk[g] * wk[g]) / W;
     const int64_t per_cu = slots / W;
@@ -711,13 +714,11 @@ int qg_gemm(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int
   GemvArgs a{};
   int st = fill_args(fmt, w, n, k, a);
   if (st != QG_OK) return st;
-  // a decode batch of a few rows: fp16 w_hat on the matrix cores, one weight stream;
-  // more rows: LDS-staged fp16 tiles on the matrix cores
-#ifndef QG_SKINNY_MIN_M
-#define QG_SKINNY_MIN_M 5
-#endif
-  if (m >= QG_SKINNY_MIN_M && m <= kSkinnyMaxM) return launch_skinny(fmt, w, X, ldx, Y, ldy, y_f32, m, n, k, s);
-  if (m > kMaxM) return launch_prefill(fmt, w, X, ldx, Y, ldy, y_f32, m, n, k, s);
+  // up to 8 activation rows: the streaming kernel (every decoded code pair meets each row in
+  // a v_dot2); 9 to 16: fp16 w_hat on the matrix cores in one weight stream; more rows:
+  // LDS-staged fp16 tiles on the matrix cores
+  if (m > kMaxM && m <= kSkinnyMaxM) return launch_skinny(fmt, w, X, ldx, Y, ldy, y_f32, m, n, k, s);
+  if (m > kSkinnyMaxM) return launch_prefill(fmt, w, X, ldx, Y, ldy, y_f32, m, n, k, s);
   a.x = X;
   a.ldx = ldx;
   a.y = Y;

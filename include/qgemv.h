@@ -163,10 +163,10 @@ int qg_gemv_batched(int fmt, const void *w, int64_t w_stride, const uint16_t *x,
  * launch's activation rows, up to 8 of them ("二三五六位量化" page section 1.2: decode
  * batches and prefill are the same contraction with more activation rows; DBHOO-CIM page
  * section 6: still bandwidth-bound at small batch, compute-bound at large batch). Any m >= 1:
- * m <= 4 runs on the vector units (each decoded code pair meets every activation row in a
- * v_dot2), 5 <= m <= 16 decodes each code once to fp16 and multiplies on the matrix cores
+ * m <= 8 runs on the vector units (each decoded code pair meets every activation row in a
+ * v_dot2), 9 <= m <= 16 decodes each code once to fp16 and multiplies on the matrix cores
  * in the same single weight stream, and m > 16 (prefill) stages fp16 weight and activation
- * tiles in LDS for 32x32 matrix-core tiles. Limits as dequant_gemv_*; for m > 4 also
+ * tiles in LDS for 32x32 matrix-core tiles. Limits as dequant_gemv_*; for m > 8 also
  * ldx < 2^23 (32-bit activation offsets within a 128-row tile). m == 0 or n == 0 is a no-op; k == 0 writes
  * zeros. Errors as dequant_gemv_*. */
 int dequant_gemm_q4g32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
