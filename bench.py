@@ -18,8 +18,8 @@ timed ("single_launch"): at ~1 us of streaming it is bound by launch cadence, no
 graph-timed): INT4 group-32 4096^2, the 7B-like layer set per super-block format (all seven
 matrices in one grouped launch, and in the launches a decode step's data dependencies
 allow), the 70B-like layer set at batch 1, 2, 4 and 8 (one launch per matrix, and one
-grouped launch), and the 512-row prefill GEMM (TFLOP/s and fraction of the 2.5 PFLOP/s
-dense fp16 MFMA peak).
+grouped launch), act-order INT4 on the 70B-like set, and the 512-row prefill GEMM (TFLOP/s
+and fraction of the 2.5 PFLOP/s dense fp16 MFMA peak).
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -160,7 +160,8 @@ def measure_set(qg, fmt, canon_shapes, m, dev, plan, footprint_gb=1.2, rounds=24
     that every round reads them from HBM. `plan` lists the launches of a round: ("group",
     [i, ...]) is one grouped launch of those matrices (any shapes), ("batched", [i, ...]) one
     strided batched launch of consecutive same-shape matrices (m = 1), ("single", [i]) one
-    qg_gemm (qg_gemv at m = 1). Returns (algorithmic bytes per round, microseconds per round)."""
+    qg_gemm (qg_gemv at m = 1), ("act_order", [i]) one qg_gemm_act_order with a random column
+    permutation. Returns (algorithmic bytes per round, microseconds per round)."""
     import numpy as np
     import torch
     from workloads import activations
@@ -187,12 +188,18 @@ def measure_set(qg, fmt, canon_shapes, m, dev, plan, footprint_gb=1.2, rounds=24
         else:
             X = [torch.from_numpy(activations(m, shapes[i][1], 11 + i)).to(dev) for i in idx]
             Y = [torch.empty((m, shapes[i][0]), dtype=torch.float16, device=dev) for i in idx]
-        launches.append((kind, idx, X, Y))
+        P = None
+        if kind == "act_order":
+            P = torch.from_numpy(np.random.default_rng(idx[0]).permutation(shapes[idx[0]][1]).astype(np.int32)).to(dev)
+        launches.append((kind, idx, X, Y, P))
 
     def rnd(r):
         base = (r % copies) * set_bytes
-        for kind, idx, X, Y in launches:
-            if kind == "batched":
+        for kind, idx, X, Y, P in launches:
+            if kind == "act_order":
+                (i,) = idx
+                qg.gemm_act_order(fmt, buf[base + int(offs[i]):], X[0], P, shapes[i][0], shapes[i][1], out=Y[0])
+            elif kind == "batched":
                 n, k = shapes[idx[0]]
                 qg.gemv_batched(fmt, buf[base + int(offs[idx[0]]):], strides[idx[0]], X, Y, len(idx), n, k)
             elif kind == "group":
@@ -260,6 +267,15 @@ def extra_configs(qg, dev):
             log(f"[bench] {fmt} 70B layer set m={m}: {out[f'{fmt}_70b_layer_set_m{m}']}")
         del cs
     del w70
+    # act-order INT4 (GPTQ-style column permutation, the gather fused into the kernel) on the
+    # 70B-like set at batch 1, against the same launches without the permutation
+    cs = [(qg.quantize("q4g32", w), w.shape[0], w.shape[1]) for w in
+          (WORKLOADS["q3sb_70b_layer_set_m1"].weights(i) for i in range(3))]
+    alg, us = measure_set(qg, "q4g32", cs, 1, dev, [("act_order", [0]), ("act_order", [1]), ("act_order", [2])], rounds=12)
+    alg2, us2 = measure_set(qg, "q4g32", cs, 1, dev, [("single", [0]), ("single", [1]), ("single", [2])], rounds=12)
+    out["q4g32_70b_layer_set_act_order_m1"] = {**_rate(alg, us), "without_permutation": _rate(alg2, us2)}
+    log(f"[bench] q4g32 70B layer set, act-order, m=1: {out['q4g32_70b_layer_set_act_order_m1']}")
+    del cs
     # prefill: 512 x 4096 activations times 11008 x 4096 weights (MFMA bound)
     for fmt in ("q4g32", "q5sb"):
         wl = WORKLOADS[f"{fmt}_prefill_512"]

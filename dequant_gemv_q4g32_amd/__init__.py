@@ -67,6 +67,7 @@ def _load() -> ctypes.CDLL:
         "qg_gemv_batched": ([i32, vp, i64, vp, i64, vp, i64, i32, i64, i64, i64, vp], i32),
         "qg_gemm": ([i32, vp, vp, i64, vp, i64, i32, i64, i64, i64, vp], i32),
         "qg_gemm_grouped": ([i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp], i32),
+        "qg_gemm_act_order": ([i32, vp, vp, i64, vp, vp, i64, i32, i64, i64, i64, vp], i32),
         "qg_dequantize": ([i32, vp, vp, vp, i64, i64, vp], i32),
         "qg_read_probe": ([vp, i64, vp, vp], i32),
     }
@@ -224,6 +225,22 @@ def gemm(fmt, w, X, n: int, k: int, out=None, out_f32: bool = False, stream=None
         out = torch.empty((m, n), dtype=torch.float32 if out_f32 else torch.float16, device=X.device)
     _check(_lib.qg_gemm(_fmt(fmt), w.data_ptr(), X.data_ptr(), X.stride(0), out.data_ptr(), out.stride(0),
                         int(out.dtype == torch.float32), m, n, k, _stream(stream)), "qg_gemm")
+    return out
+
+
+def gemm_act_order(fmt, w, X, perm, n: int, k: int, out=None, out_f32: bool = False, stream=None):
+    """Y = X[:, perm] W_hat^T for weights quantized with their columns permuted (stored column c
+    is original column perm[c]). X: fp16 [m, k] (m <= 8) or [k]; perm: int32 [k] on the device."""
+    torch = _torch()
+    vec = X.dim() == 1
+    m = 1 if vec else X.shape[0]
+    if out is None:
+        out = torch.empty((n,) if vec else (m, n), dtype=torch.float32 if out_f32 else torch.float16, device=X.device)
+    if perm.dtype != torch.int32:
+        raise TypeError("perm must be int32")
+    _check(_lib.qg_gemm_act_order(_fmt(fmt), w.data_ptr(), X.data_ptr(), k if vec else X.stride(0), perm.data_ptr(),
+                                  out.data_ptr(), n if vec else out.stride(0), int(out.dtype == torch.float32), m, n, k,
+                                  _stream(stream)), "qg_gemm_act_order")
     return out
 
 

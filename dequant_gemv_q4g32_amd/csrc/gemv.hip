@@ -34,6 +34,8 @@ struct GemvArgs {
   int64_t poff[4];
   int64_t prb[4];
   int64_t m;                // activation rows (1 for the GEMV)
+  const int32_t *perm;      // act-order column permutation (k entries) or null
+  int64_t xl_off;           // act-order: float offset of the activations staged in LDS, or -1
   int64_t ldx, ldy;         // elements between activation rows / output rows
   int y_f32;
   int wk;                   // waves per workgroup along K
@@ -107,6 +109,20 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
 
   // K passes: the wk waves of a row group cover wk * UPW units per pass. With more than one
   // pass (long K with many activation rows) each wave accumulates its partial sums in LDS.
+  // Act-order with the activations staged in LDS: the workgroup copies its m rows of x
+  // (contiguous 16-byte loads) once, so that each lane's gather by the permutation reads LDS
+  // instead of issuing 2-byte global loads that touch a cache line each.
+  const uint16_t *xl = a.xl_off >= 0 ? reinterpret_cast<const uint16_t *>(red + a.xl_off) : nullptr;
+  if (a.perm && xl) {
+    uint16_t *xw = reinterpret_cast<uint16_t *>(red + a.xl_off);
+    const int64_t chunks = a.k / 8;                          // 16-byte chunks per row
+    for (int64_t i = threadIdx.x; i < a.m * chunks; i += blockDim.x) {
+      const int64_t mm = i / chunks, c = i % chunks;
+      *reinterpret_cast<u32x4 *>(xw + mm * a.k + 8 * c) = ld4(reinterpret_cast<const uint8_t *>(x + mm * a.ldx + 8 * c));
+    }
+    __syncthreads();
+  }
+
   const int passes = MP ? a.kpasses : 1;
   for (int kp = 0; kp < passes; ++kp) {
     if (nbh == 0) break;                       // wave-uniform: a row group past the last batch
@@ -134,23 +150,55 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
 
     // The lane's activation pairs, 16 bytes (4 pairs) at a time: local pairs 4i..4i+3 are the
     // unit's pairs pidx(h, 4i).. (consecutive), i.e. bytes 4 * pidx(h, 4i) of its 128.
+    // With an act-order permutation, the activation of stored column c is x[perm[c]]: the
+    // lane gathers its 8 activations per group of 4 pairs through 32-bit buffer loads of the
+    // indices and 16-bit buffer loads of x (an index outside [0, k) reads 0, never past x).
     uint32_t xp[M][NP];
-#pragma unroll
-    for (int mm = 0; mm < M; ++mm) {
-      const bool live = mm < a.m;
-      const uint8_t *px =
-          reinterpret_cast<const uint8_t *>(x + (int64_t)(live ? mm : 0) * a.ldx) + (uint32_t)(u * 128);
+    if (a.perm) {
+      const rsrc_t pr = make_rsrc(a.perm, (uint32_t)(a.k * 4));
 #pragma unroll
       for (int i = 0; i < NP / 4; ++i) {
         uint32_t off = 4u * (uint32_t)U::pidx(h, 4 * i, S);
-        bool keepx = live;
-        // a half unit (k % 64 == 32) has only 32 activations: re-read the first half, zero it
+        bool keepx = true;
         if (F == 4 && half && off >= 64) { off -= 64; keepx = false; }
-        const u32x4 v = ld4(px + off);
-        xp[mm][4 * i + 0] = keepx ? v.x : 0u;
-        xp[mm][4 * i + 1] = keepx ? v.y : 0u;
-        xp[mm][4 * i + 2] = keepx ? v.z : 0u;
-        xp[mm][4 * i + 3] = keepx ? v.w : 0u;
+        const uint32_t kb = (uint32_t)(u * kUnit) + off / 2;   // first of the 8 stored columns
+        const u32x4 i0 = bld4c(pr, kb * 4, 0), i1 = bld4c(pr, kb * 4 + 16, 0);
+        const uint32_t idx[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+#pragma unroll
+        for (int mm = 0; mm < M; ++mm) {
+          const bool live = mm < a.m && keepx;
+          const int64_t row = mm < a.m ? mm : 0;
+          uint32_t hv[8];
+          if (xl) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) hv[j] = idx[j] < (uint32_t)a.k ? xl[row * a.k + idx[j]] : 0u;
+          } else {
+            const rsrc_t xr = make_rsrc(x + row * a.ldx, (uint32_t)(a.k * 2));
+#pragma unroll
+            for (int j = 0; j < 8; ++j) hv[j] = bldh(xr, idx[j] * 2, 0);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) xp[mm][4 * i + r] = live ? (hv[2 * r] | (hv[2 * r + 1] << 16)) : 0u;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int mm = 0; mm < M; ++mm) {
+        const bool live = mm < a.m;
+        const uint8_t *px =
+            reinterpret_cast<const uint8_t *>(x + (int64_t)(live ? mm : 0) * a.ldx) + (uint32_t)(u * 128);
+#pragma unroll
+        for (int i = 0; i < NP / 4; ++i) {
+          uint32_t off = 4u * (uint32_t)U::pidx(h, 4 * i, S);
+          bool keepx = live;
+          // a half unit (k % 64 == 32) has only 32 activations: re-read the first half, zero it
+          if (F == 4 && half && off >= 64) { off -= 64; keepx = false; }
+          const u32x4 v = ld4(px + off);
+          xp[mm][4 * i + 0] = keepx ? v.x : 0u;
+          xp[mm][4 * i + 1] = keepx ? v.y : 0u;
+          xp[mm][4 * i + 2] = keepx ? v.z : 0u;
+          xp[mm][4 * i + 3] = keepx ? v.w : 0u;
+        }
       }
     }
     float kc[M][NK];
@@ -432,6 +480,7 @@ int fill_args(int fmt, const void *w, int64_t n, int64_t k, GemvArgs &a) {
 
 constexpr int64_t kSimds = 1024;           // 256 CUs x 4 SIMDs
 constexpr int kMaxBatches = 32;
+constexpr int64_t kActOrderLds = 64 * 1024;   // most activation bytes an act-order launch stages in LDS
 #ifndef QG_MV_MIN_BATCHES
 #define QG_MV_MIN_BATCHES 4
 #endif
@@ -479,11 +528,13 @@ size_t red_bytes(const GemvArgs &a, int R, int M) {
 // and coarse workgroups cost more than the score shows: workgroups of 10 to 16 waves
 // measured up to 40% slower than 3 to 8 on the same grouped launch).
 constexpr int kMaxPlanW = 8;
+constexpr int64_t kLdsPerCu = 160 * 1024;   // LDS bytes per CU on gfx950
 struct MvPlan {
   int W;
   int64_t nbt;
 };
-MvPlan plan_mv(int ng, const int64_t *n, const int *wk, const int64_t *count, int R, int wps, int max_w) {
+MvPlan plan_mv(int ng, const int64_t *n, const int *wk, const int64_t *count, int R, int wps, int max_w,
+               int64_t lds_block = 0) {
   const int slots = 4 * wps;
   int64_t work[kMaxGroup], total = 0;
   int wk_max = 1;
@@ -494,10 +545,11 @@ MvPlan plan_mv(int ng, const int64_t *n, const int *wk, const int64_t *count, in
   }
   MvPlan best{wk_max, kMinBatches};
   double best_score = -1.0;
-  for (int W = wk_max; W <= max_w && W <= slots && (W <= kMaxPlanW || W == wk_max); ++W) {
+  for (int W = wk_max; W <= max_w && W <= slots && (W <= kMaxPlanW || W == wk_max || lds_block > 0); ++W) {
     double used = 0.0;
     for (int g = 0; g < ng; ++g) used += (double)work[g] * (W / wk[g] * wk[g]) / W;
-    const int64_t per_cu = slots / W;
+    int64_t per_cu = slots / W;
+    if (lds_block > 0 && kLdsPerCu / lds_block < per_cu) per_cu = kLdsPerCu / lds_block;
     const int64_t resident = (int64_t)256 * per_cu * W;
     int64_t nbt = (total + resident - 1) / resident;
     nbt = nbt < kMinBatches ? kMinBatches : nbt;
@@ -524,11 +576,20 @@ template <int F, int M, int S, int R, bool MP>
 int launch_mv(GemvArgs a, int64_t count, hipStream_t s) {
   void (*kern)(GemvArgs) = mv_kernel<F, M, S, R, MP>;
   static const int wps = waves_per_simd(reinterpret_cast<const void *>(kern));
-  const MvPlan P = plan_mv(1, &a.n, &a.wk, &count, R, wps, mv_threads<M>() / 64);
+  // act-order activations staged in LDS when they fit beside the partial sums
+  const int64_t xl_bytes = a.perm ? a.m * a.k * 2 : 0;
+  const bool stage = a.perm && xl_bytes <= kActOrderLds;
+  const MvPlan P = plan_mv(1, &a.n, &a.wk, &count, R, wps, mv_threads<M>() / 64, stage ? xl_bytes : 0);
   a.wr = P.W / a.wk;
   const int64_t blocks = split_rows(a, R, P.nbt);
+  size_t shm = red_bytes(a, R, M);
+  a.xl_off = -1;
+  if (stage) {
+    a.xl_off = (int64_t)((shm + 15) / 16 * 4);
+    shm = (size_t)a.xl_off * 4 + (size_t)xl_bytes;
+  }
   dim3 grid((unsigned)blocks, (unsigned)count);
-  return launch(kern, grid, dim3((unsigned)(64 * P.W)), red_bytes(a, R, M), s, a);
+  return launch(kern, grid, dim3((unsigned)(64 * P.W)), shm, s, a);
 }
 
 template <int F, int M, int S, int R, bool MP>
@@ -546,6 +607,7 @@ int launch_mv_group(GemvGroup &G, hipStream_t s) {
   int64_t blocks = 0;
   size_t shm = 0;
   for (int g = 0; g < G.count; ++g) {
+    G.g[g].xl_off = -1;
     G.g[g].wr = P.W / G.g[g].wk;
     blocks += split_rows(G.g[g], R, P.nbt);
     G.block_end[g] = blocks;
@@ -725,6 +787,32 @@ int qg_gemm(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int
   a.ldy = ldy;
   a.y_f32 = y_f32;
   a.m = m;
+  return launch_mv_fmt(fmt, a, 1, s);
+}
+
+int qg_gemm_act_order(int fmt, const void *w, const uint16_t *X, int64_t ldx, const int32_t *perm, void *Y,
+                      int64_t ldy, int y_f32, int64_t m, int64_t n, int64_t k, void *stream) {
+  if (!fmt_valid(fmt)) return QG_ERR_FORMAT;
+  if (n < 0 || k < 0 || m < 0 || m > kMaxM) return QG_ERR_SHAPE;
+  if ((fmt == 4 && k % 32) || (fmt != 4 && k % kQK)) return QG_ERR_SHAPE;
+  if (m > 1 && (ldx < k || ldy < n)) return QG_ERR_SHAPE;
+  if (k > kMaxK) return QG_ERR_SHAPE;
+  if (n == 0 || m == 0) return QG_OK;
+  if (!Y || (k > 0 && (!w || !X || !perm))) return QG_ERR_NULL;
+  if (!aligned(Y, y_f32 ? 4 : 2)) return QG_ERR_ALIGN;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (k == 0) return qg_gemm(fmt, w, X, ldx, Y, ldy, y_f32, m, n, k, stream);
+  if (!aligned(w, 256) || !aligned(X, 16) || !aligned(perm, 16) || (m > 1 && ldx % 8)) return QG_ERR_ALIGN;
+  GemvArgs a{};
+  int st = fill_args(fmt, w, n, k, a);
+  if (st != QG_OK) return st;
+  a.x = X;
+  a.ldx = m > 1 ? ldx : k;
+  a.y = Y;
+  a.ldy = m > 1 ? ldy : n;
+  a.y_f32 = y_f32;
+  a.m = m;
+  a.perm = perm;
   return launch_mv_fmt(fmt, a, 1, s);
 }
 

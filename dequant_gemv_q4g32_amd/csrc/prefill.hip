@@ -88,6 +88,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     L.rs[p] = make_rsrc(a.w + a.poff[p], (uint32_t)(a.prb[p] * a.n));
     L.prb[p] = (uint32_t)a.prb[p];
   }
+  L.h = h;
 
   // Global loads of step u into one register stage. Steps past the end re-load the last
   // step, so that every step issues the same loads and waits only for the older stage.
@@ -103,8 +104,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) L.off[p] += (uint32_t)wrow * L.prb[p];
     const bool half = (F == 4) && (u == a.units - 1) && (a.k % 64 != 0);
-    // cached: the weight tile is read again by the workgroups of the other M tiles
-    U::template load<0>(q, L, 0, half);
+    // only this thread's half of the unit; cached: the weight tile is read again by the
+    // workgroups of the other M tiles
+    U::template load<0, 2>(q, L, 0, half);
     const int64_t kk = u * kUnit + 8 * xc;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -116,7 +118,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   // decode a register stage to fp16 and store it, with its activations, into LDS buffer b
   auto lds_store = [&](const Raw &q, const u32x4 *xv, int b) {
     uint32_t pr[16];
-    U::wide(q, h, pr);
+    U::template wide<2>(q, h, pr);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       // local pairs 4i..4i+3 are the unit's consecutive pairs pidx(h, 4i).. (k = 2 * pair)

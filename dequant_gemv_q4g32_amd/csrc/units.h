@@ -140,10 +140,11 @@ template <> struct Unit<4> {
       for (int m = 0; m < M; ++m) out[m] = __builtin_fmaf(scale, __builtin_fmaf(a16[m], 0.0625f, a1[m]), out[m]);
     }
   }
-  // fp16 w_hat of the 16 pairs of half h (group h), in local pair order
-  __device__ static void wide(const Raw &q, int h, uint32_t *out) {
-    const u32x4 c = h ? q.c1 : q.c0;
-    const float scale = h ? q.s1 : q.s0;
+  // fp16 w_hat of the 16 pairs of half h (group h), in local pair order; S = 2: q holds only
+  // that half (loaded by load<AUX, 2>)
+  template <int S = 1> __device__ static void wide(const Raw &q, int h, uint32_t *out) {
+    const u32x4 c = S == 1 && h ? q.c1 : q.c0;
+    const float scale = S == 1 && h ? q.s1 : q.s0;
     const _Float16 m1 = (_Float16)scale, m16 = (_Float16)(scale * 0.0625f);
     const uint32_t d[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
@@ -234,8 +235,9 @@ template <> struct Unit<2> {
       out[m] = acc;
     }
   }
-  // fp16 w_hat of the 16 pairs of half h (dwords 2h, 2h+1), in local pair order
-  __device__ static void wide(const Raw &q, int h, uint32_t *out) {
+  // fp16 w_hat of the 16 pairs of half h (dwords 2h, 2h+1), in local pair order; S = 2: q
+  // holds only those dwords, in c.x and c.y
+  template <int S = 1> __device__ static void wide(const Raw &q, int h, uint32_t *out) {
     const uint32_t d[4] = {q.c.x, q.c.y, q.c.z, q.c.w};
     const float inv4[4] = {1.0f, 0.25f, 0.0625f, 0.015625f};
     const float dv = half_lo(q.dd), dm = half_hi(q.dd);
@@ -247,7 +249,7 @@ template <> struct Unit<2> {
     }
 #pragma unroll
     for (int ii = 0; ii < 2; ++ii) {
-      const uint32_t v = sel(h, d[2 + ii], d[ii]), v8 = v >> 8;
+      const uint32_t v = S == 1 ? sel(h, d[2 + ii], d[ii]) : d[ii], v8 = v >> 8;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         out[4 * j + 2 * ii] = asym_pair(pick(v, QG_SMASK(0x00030003u << (2 * j))), mul[j], add[j]);
@@ -370,7 +372,7 @@ template <> struct Unit<3> {
     }
   }
   // fp16 w_hat of the 16 pairs of chunk h (sub-blocks a = 2h, b = 2h + 1 of the unit)
-  __device__ static void wide(const Raw &q, int h, uint32_t *out) {
+  template <int S = 1> __device__ static void wide(const Raw &q, int h, uint32_t *out) {
     uint32_t P[16];
     chunk_pairs(sel(h, q.a.w, q.a.x), sel(h, q.b.x, q.a.y), sel(h, q.b.y, q.a.z), P);
     const uint32_t fh = q.f >> (12 * h);
@@ -479,10 +481,12 @@ template <> struct Unit<5> {
       }
     }
   }
-  // fp16 w_hat of the 16 pairs of half h (sub-block h of the unit)
-  __device__ static void wide(const Raw &q, int h, uint32_t *out) {
-    const uint32_t L[8] = {q.l0.x, q.l0.y, q.l0.z, q.l0.w, q.l1.x, q.l1.y, q.l1.z, q.l1.w};
-    const uint32_t H = sel(h, q.h.y, q.h.x);
+  // fp16 w_hat of the 16 pairs of half h (sub-block h of the unit); S = 2: q holds only that
+  // sub-block's nibbles (l0) and high bits (h.x)
+  template <int S = 1> __device__ static void wide(const Raw &q, int h, uint32_t *out) {
+    const uint32_t L[8] = {q.l0.x, q.l0.y, q.l0.z, q.l0.w, S == 1 ? q.l1.x : 0u, S == 1 ? q.l1.y : 0u,
+                           S == 1 ? q.l1.z : 0u, S == 1 ? q.l1.w : 0u};
+    const uint32_t H = S == 1 ? sel(h, q.h.y, q.h.x) : q.h.x;
     const float dv = half_lo(q.dd), dm = half_hi(q.dd);
     const float step = dv * (float)((q.f >> (6 * h)) & 63u), off = dm * (float)((q.f >> (12 + 6 * h)) & 63u);
     const float mul1 = step, add1 = -__builtin_fmaf(1024.0f, step, off);
@@ -490,7 +494,7 @@ template <> struct Unit<5> {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       uint32_t P[4];
-      nib_pairs<1>(sel(h, L[4 + i], L[i]), H, i, P);
+      nib_pairs<1>(S == 1 ? sel(h, L[4 + i], L[i]) : L[i], H, i, P);
       out[4 * i + 0] = asym_pair(P[0], mul1, add1);
       out[4 * i + 1] = asym_pair(P[1], mul16, add16);
       out[4 * i + 2] = asym_pair(P[2], mul1, add1);
@@ -571,20 +575,22 @@ template <> struct Unit<6> {
       for (int m = 0; m < M; ++m) out[m] = __builtin_fmaf(dv * sj, __builtin_fmaf(a16[m], 0.0625f, a1[m]), out[m]);
     }
   }
-  // fp16 w_hat of the 16 pairs of half h (sub-blocks 2h, 2h + 1 of the unit)
-  __device__ static void wide(const Raw &q, int h, uint32_t *out) {
-    const uint32_t L[8] = {q.l0.x, q.l0.y, q.l0.z, q.l0.w, q.l1.x, q.l1.y, q.l1.z, q.l1.w};
-    const uint32_t Hd[4] = {q.h.x, q.h.y, q.h.z, q.h.w};
+  // fp16 w_hat of the 16 pairs of half h (sub-blocks 2h, 2h + 1 of the unit); S = 2: q holds
+  // only those sub-blocks' nibbles (l0) and high fields (h.x, h.y)
+  template <int S = 1> __device__ static void wide(const Raw &q, int h, uint32_t *out) {
+    const uint32_t L[8] = {q.l0.x, q.l0.y, q.l0.z, q.l0.w, S == 1 ? q.l1.x : 0u, S == 1 ? q.l1.y : 0u,
+                           S == 1 ? q.l1.z : 0u, S == 1 ? q.l1.w : 0u};
+    const uint32_t Hd[4] = {q.h.x, q.h.y, S == 1 ? q.h.z : 0u, S == 1 ? q.h.w : 0u};
     const float dv = half_bits(q.d);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const float step = dv * (float)(int8_t)((q.sc >> (8 * (2 * h + j))) & 0xFFu);
       const _Float16 m1 = (_Float16)step, m16 = (_Float16)(step * 0.0625f);
-      const uint32_t H = sel(h, Hd[2 + j], Hd[j]);
+      const uint32_t H = S == 1 ? sel(h, Hd[2 + j], Hd[j]) : Hd[j];
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii) {
         uint32_t P[4];
-        nib_pairs<2>(sel(h, L[4 + 2 * j + ii], L[2 * j + ii]), H, ii, P);
+        nib_pairs<2>(S == 1 ? sel(h, L[4 + 2 * j + ii], L[2 * j + ii]) : L[2 * j + ii], H, ii, P);
         out[8 * j + 4 * ii + 0] = sym_pair(P[0], (_Float16)-1056.0f, m1);
         out[8 * j + 4 * ii + 1] = sym_pair(P[1], (_Float16)-1536.0f, m16);
         out[8 * j + 4 * ii + 2] = sym_pair(P[2], (_Float16)-1056.0f, m1);

@@ -183,6 +183,18 @@ int dequant_gemm_q6sb(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y
 int qg_gemm(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int64_t ldy, int y_f32,
             int64_t m, int64_t n, int64_t k, void *stream);
 
+/* Act-order weights ("二三五六位量化" page section 2.4 and section 3.2, stage 3: GPTQ
+ * quantizes the columns in an activation-dependent order and stores that permutation, which
+ * inference must apply): W was quantized with its columns permuted, stored column c being
+ * original column perm[c], so Y[i][r] = sum_c X[i][perm[c]] * W_hat[r][c]. perm: int32 [k] on
+ * the device (16-byte aligned), entries in [0, k) (an entry outside that range reads an
+ * activation of 0; it never reads outside X). The gather is fused into the streaming
+ * kernel's activation load, so the result equals qg_gemm on the gathered activations bit for
+ * bit. m: 0..8 activation rows (the streaming kernel); other arguments, limits and errors as
+ * qg_gemm. */
+int qg_gemm_act_order(int fmt, const void *w, const uint16_t *X, int64_t ldx, const int32_t *perm, void *Y,
+                      int64_t ldy, int y_f32, int64_t m, int64_t n, int64_t k, void *stream);
+
 /* Several matrices of any shapes, one activation-row count m (0..8), in one launch: for
  * g < count (at most 8), Y_g [m][ldy[g]] = X_g [m][ldx[g]] * W_hat_g^T with W_g of n[g] x k[g]
  * at w[g]. The arrays are host arrays read during the call; ldx and ldy are read only when

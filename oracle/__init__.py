@@ -17,7 +17,9 @@ What it defines, following the two source pages:
     scale = max|w|/8, q = clamp(round(w/scale), -8, 7), groups of 32 along the input
     dimension), section 3.2 (two codes per byte, low nibble first, stored as unsigned 0..15),
     section 4.1 (fp32 scales in a separate array), section 4.4 (effective bandwidth = weight
-    bytes / latency).
+    bytes / latency);
+  * act-order weights ("二三五六位量化" sections 2.4 and 3.2, stage 3: columns quantized in
+    a stored permuted order, restored at inference), in ``actorder``.
 
 Readings taken where the pages are silent or garbled are listed in each module's docstring.
 Floating point is fp64 throughout except where the pages fix another precision (the INT4

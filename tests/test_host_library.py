@@ -195,3 +195,15 @@ def test_grouped_entry_point_validates_every_matrix_first():
     assert call(3, **{**ok, "ns": [0, 0]}) == 0                           # n == 0: no-op
     assert L.qg_gemm_grouped(3, 0, None, None, None, None, None, None, None, 1, 0, None) == 0
     assert L.qg_gemm_grouped(3, 1, None, None, None, None, None, None, None, 1, 0, None) == -1
+
+
+def test_act_order_entry_point_validates_without_launching():
+    L = qg.lib
+    # qg_gemm_act_order(fmt, w, X, ldx, perm, Y, ldy, y_f32, m, n, k, stream)
+    assert L.qg_gemm_act_order(3, 256, 16, 256, None, 2, 4, 0, 1, 4, 256, None) == -1    # null perm
+    assert L.qg_gemm_act_order(3, 256, 16, 256, 52, 2, 4, 0, 1, 4, 256, None) == -3      # perm misaligned
+    assert L.qg_gemm_act_order(3, 256, 16, 256, 32, 2, 4, 0, 9, 4, 256, None) == -2      # m > 8
+    assert L.qg_gemm_act_order(3, 256, 16, 256, 32, 2, 4, 0, 1, 4, 100, None) == -2      # k % 256
+    assert L.qg_gemm_act_order(3, 256, 16, 128, 32, 2, 4, 0, 2, 4, 256, None) == -2      # ldx < k
+    assert L.qg_gemm_act_order(9, 256, 16, 256, 32, 2, 4, 0, 1, 4, 256, None) == -6      # format
+    assert L.qg_gemm_act_order(3, 256, 16, 256, 32, 2, 4, 0, 0, 4, 256, None) == 0       # m == 0
