@@ -19,7 +19,9 @@ What it defines, following the two source pages:
     section 4.1 (fp32 scales in a separate array), section 4.4 (effective bandwidth = weight
     bytes / latency);
   * act-order weights ("二三五六位量化" sections 2.4 and 3.2, stage 3: columns quantized in
-    a stored permuted order, restored at inference), in ``actorder``.
+    a stored permuted order, restored at inference), in ``actorder``;
+  * the 8-bit KV-cache group codec ("二三五六位量化" section 4.1: one fp16 scale per 32
+    elements, about 1.06 bytes per element), in ``kvcache``.
 
 Readings taken where the pages are silent or garbled are listed in each module's docstring.
 Floating point is fp64 throughout except where the pages fix another precision (the INT4
