@@ -18,8 +18,9 @@ timed ("single_launch"): at ~1 us of streaming it is bound by launch cadence, no
 graph-timed): INT4 group-32 4096^2, the 7B-like layer set per super-block format (all seven
 matrices in one grouped launch, and in the launches a decode step's data dependencies
 allow), the 70B-like layer set at batch 1, 2, 4 and 8 (one launch per matrix, and one
-grouped launch), act-order INT4 on the 70B-like set, and the 512-row prefill GEMM (TFLOP/s
-and fraction of the 2.5 PFLOP/s dense fp16 MFMA peak).
+grouped launch), act-order INT4 on the 70B-like set, the 8-bit KV-cache codec on the
+7B-like cache, and the 512-row prefill GEMM (TFLOP/s and fraction of the 2.5 PFLOP/s dense
+fp16 MFMA peak).
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -276,6 +277,28 @@ def extra_configs(qg, dev):
     out["q4g32_70b_layer_set_act_order_m1"] = {**_rate(alg, us), "without_permutation": _rate(alg2, us2)}
     log(f"[bench] q4g32 70B layer set, act-order, m=1: {out['q4g32_70b_layer_set_act_order_m1']}")
     del cs
+    # 8-bit KV-cache codec on the 7B-like cache (32 layers x K and V x 8 KV heads x 128, 8192
+    # tokens = 536,870,912 elements): bytes moved = 2 (fp16) + 1.0625 (codes and scales) per
+    # element; and the per-token append of a decode step (64 rows of 1024)
+    import torch
+    from workloads import activations
+    rows, cols = 2 * 32 * 8192, 8 * 128
+    x = torch.empty((rows, cols), dtype=torch.float16, device=dev)
+    x.copy_(torch.from_numpy(activations(1024, cols, 3)).to(dev).repeat(rows // 1024, 1))
+    codes = torch.empty((rows, cols), dtype=torch.int8, device=dev)
+    scales = torch.empty((rows, cols // 32), dtype=torch.float16, device=dev)
+    moved = rows * cols * 3.0625
+    us_q = _graph_time_us(lambda i: qg.kv_quantize(x, codes, scales), 4)
+    us_d = _graph_time_us(lambda i: qg.kv_dequantize(codes, scales, out=x), 4)
+    xa, ca, sa = x[:64], codes[:64], scales[:64]
+    us_a = _graph_time_us(lambda i: qg.kv_quantize(xa, ca, sa), 200)
+    out["kv_cache_int8_7b_8192"] = {"quantize_GBps": round(moved / us_q / 1e3, 1), "quantize_us": round(us_q, 1),
+                                    "dequantize_GBps": round(moved / us_d / 1e3, 1), "dequantize_us": round(us_d, 1),
+                                    "frac": round(max(moved / us_q, moved / us_d) / 1e3 / HBM_PEAK_GBPS, 4),
+                                    "append_one_token_us": round(us_a, 2)}
+    log(f"[bench] KV cache int8 codec: {out['kv_cache_int8_7b_8192']}")
+    del x, codes, scales
+    torch.cuda.empty_cache()
     # prefill: 512 x 4096 activations times 11008 x 4096 weights (MFMA bound)
     for fmt in ("q4g32", "q5sb"):
         wl = WORKLOADS[f"{fmt}_prefill_512"]

@@ -68,6 +68,8 @@ def _load() -> ctypes.CDLL:
         "qg_gemm": ([i32, vp, vp, i64, vp, i64, i32, i64, i64, i64, vp], i32),
         "qg_gemm_grouped": ([i32, i32, vp, vp, vp, vp, vp, vp, vp, i64, i32, vp], i32),
         "qg_gemm_act_order": ([i32, vp, vp, i64, vp, vp, i64, i32, i64, i64, i64, vp], i32),
+        "qg_kv_quantize": ([vp, i64, i64, i64, vp, vp, vp], i32),
+        "qg_kv_dequantize": ([vp, vp, i64, i64, vp, i64, vp], i32),
         "qg_dequantize": ([i32, vp, vp, vp, i64, i64, vp], i32),
         "qg_read_probe": ([vp, i64, vp, vp], i32),
     }
@@ -265,6 +267,31 @@ def gemm_grouped(fmt, ws, Xs, shapes, outs=None, out_f32: bool = False, stream=N
         arr(i64, [y.stride(0) if y.dim() == 2 else y.shape[0] for y in outs]), arr(i64, [n for n, _ in shapes]),
         arr(i64, [k for _, k in shapes]), m, int(outs[0].dtype == torch.float32), _stream(stream)), "qg_gemm_grouped")
     return outs
+
+
+def kv_quantize(x, codes=None, scales=None, stream=None):
+    """8-bit KV-cache groups: fp16 [rows, cols] (row stride x.stride(0), cols % 32 == 0) ->
+    (int8 codes [rows, cols], fp16 scales [rows, cols / 32])."""
+    torch = _torch()
+    rows, cols = x.shape
+    if codes is None:
+        codes = torch.empty((rows, cols), dtype=torch.int8, device=x.device)
+    if scales is None:
+        scales = torch.empty((rows, cols // 32), dtype=torch.float16, device=x.device)
+    _check(_lib.qg_kv_quantize(x.data_ptr(), x.stride(0), rows, cols, codes.data_ptr(), scales.data_ptr(),
+                               _stream(stream)), "qg_kv_quantize")
+    return codes, scales
+
+
+def kv_dequantize(codes, scales, out=None, stream=None):
+    """int8 codes [rows, cols] and fp16 scales [rows, cols / 32] -> fp16 [rows, cols]."""
+    torch = _torch()
+    rows, cols = codes.shape
+    if out is None:
+        out = torch.empty((rows, cols), dtype=torch.float16, device=codes.device)
+    _check(_lib.qg_kv_dequantize(codes.data_ptr(), scales.data_ptr(), rows, cols, out.data_ptr(), out.stride(0),
+                                 _stream(stream)), "qg_kv_dequantize")
+    return out
 
 
 def dequantize(fmt, w, n: int, k: int, values: bool = True, codes: bool = True, stream=None):

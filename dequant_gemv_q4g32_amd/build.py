@@ -21,7 +21,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqgemv.so")
 
 HOST_SOURCES = ["host.cpp"]
-DEVICE_SOURCES = ["gemv.hip", "prefill.hip", "skinny.hip"]
+DEVICE_SOURCES = ["gemv.hip", "prefill.hip", "skinny.hip", "kvcache.hip"]
 ARCH = "gfx950"
 
 

@@ -210,6 +210,25 @@ int qg_gemm_grouped(int fmt, int count, const void *const *w, const uint16_t *co
                     void *const *Y, const int64_t *ldy, const int64_t *n, const int64_t *k, int64_t m, int y_f32,
                     void *stream);
 
+/* ---- 8-bit KV-cache group codec (device) --------------------------------------------------
+ * "二三五六位量化" page section 4.1: the KV cache quantized to 8 bits, every 32 elements
+ * sharing one fp16 scale (about 1.06 bytes per element, half of fp16). Codes are symmetric
+ * int8 in [-127, 127]; the scale d of a group is the smallest fp16 >= max|x| / 127 (fp32
+ * arithmetic), q = rint(x * fp32(1 / d)) half-to-even, an all-zero group has d = 0 and q = 0,
+ * and every element is within d/2 (up to an fp32 ulp) of fp32(d) * q.
+ *
+ * qg_kv_quantize (on append): src fp16 [rows][ld_src] (first cols used; 16-byte aligned,
+ * ld_src a multiple of 8 when rows > 1) -> codes int8 [rows][cols] (8-byte aligned) and scales
+ * fp16 [rows][cols/32] (2-byte aligned). qg_kv_dequantize (on read): codes and scales ->
+ * dst fp16 [rows][ld_dst] (16-byte aligned, ld_dst a multiple of 8 when rows > 1), each value
+ * fp32(d) * q rounded once to fp16. cols must be a multiple of 32. Inputs must be finite
+ * (a NaN or Inf gives unspecified codes for its group). rows == 0 or cols == 0 is a no-op.
+ * Errors: QG_ERR_SHAPE, QG_ERR_NULL, QG_ERR_ALIGN, QG_ERR_LAUNCH. */
+int qg_kv_quantize(const uint16_t *src, int64_t ld_src, int64_t rows, int64_t cols, int8_t *codes, uint16_t *scales,
+                   void *stream);
+int qg_kv_dequantize(const int8_t *codes, const uint16_t *scales, int64_t rows, int64_t cols, uint16_t *dst,
+                     int64_t ld_dst, void *stream);
+
 /* ---- decode to memory (device; for verification, not for inference) ----------------------
  * Writes W_hat as fp32 [n][k] to w_out (if non-NULL) and the integer codes as uint8 [n][k]
  * to codes_out (if non-NULL; q4g32 writes the unsigned nibble u = q + 8). fp32 values are

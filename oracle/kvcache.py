@@ -16,8 +16,11 @@ Readings (the page gives the group size, the code width and the scale type only)
     super-block scales);
   * the code decision is made in fp32, the precision a GPU kernel computes it in (the page
     fixes none): t = fp32(max|x|) / 127 (one fp32 division), d = fp16_ceil(t),
-    q = clamp(rint(fp32(x) / fp32(d)), -127, 127) with rint half-to-even; an all-zero group
-    has d = 0 and q = 0;
+    inv = fp32(1 / d) (one fp32 division per group), q = clamp(rint(fp32(x) * inv), -127, 127)
+    with rint half-to-even; an all-zero group has d = 0, inv = 0 and q = 0. (A multiply by
+    the group's reciprocal rather than a division per element: it can move a code by one only
+    where x / d lies within an ulp of a half-integer, and keeps the error within d/2 up to
+    that ulp.)
   * decode: x_hat = fp32(d) * q (exact in fp32: 11 x 7 significant bits), rounded once to
     fp16 for the fp16 output.
 
@@ -57,8 +60,9 @@ def quantize(x: np.ndarray):
     t = (amax / np.float32(QMAX)).astype(np.float32)                  # one fp32 division
     d = fp16_ceil_array(t.astype(np.float64))                         # smallest fp16 >= t
     d32 = d.astype(np.float32)[:, :, None]
-    with np.errstate(divide="ignore", invalid="ignore"):
-        r = np.where(d32 > 0, g / np.where(d32 > 0, d32, np.float32(1)), np.float32(0)).astype(np.float32)
+    with np.errstate(divide="ignore"):
+        inv = np.where(d32 > 0, np.float32(1) / np.where(d32 > 0, d32, np.float32(1)), np.float32(0)).astype(np.float32)
+    r = (g * inv).astype(np.float32)                                  # one fp32 multiply
     q = np.clip(np.rint(r), -QMAX, QMAX).astype(np.int8)
     return q.reshape(rows, cols), d
 

@@ -207,3 +207,20 @@ def test_act_order_entry_point_validates_without_launching():
     assert L.qg_gemm_act_order(3, 256, 16, 128, 32, 2, 4, 0, 2, 4, 256, None) == -2      # ldx < k
     assert L.qg_gemm_act_order(9, 256, 16, 256, 32, 2, 4, 0, 1, 4, 256, None) == -6      # format
     assert L.qg_gemm_act_order(3, 256, 16, 256, 32, 2, 4, 0, 0, 4, 256, None) == 0       # m == 0
+
+
+def test_kv_codec_entry_points_validate_without_launching():
+    L = qg.lib
+    # qg_kv_quantize(src, ld_src, rows, cols, codes, scales, stream)
+    assert L.qg_kv_quantize(16, 64, 2, 48, 8, 2, None) == -2          # cols % 32
+    assert L.qg_kv_quantize(16, 16, 2, 32, 8, 2, None) == -2          # ld_src < cols
+    assert L.qg_kv_quantize(18, 64, 2, 64, 8, 2, None) == -3          # src misaligned
+    assert L.qg_kv_quantize(16, 68, 2, 64, 8, 2, None) == -3          # ld_src % 8
+    assert L.qg_kv_quantize(16, 64, 2, 64, 12, 2, None) == -3         # codes misaligned
+    assert L.qg_kv_quantize(None, 64, 2, 64, 8, 2, None) == -1
+    assert L.qg_kv_quantize(16, 64, 0, 64, 8, 2, None) == 0           # no rows: no-op
+    # qg_kv_dequantize(codes, scales, rows, cols, dst, ld_dst, stream)
+    assert L.qg_kv_dequantize(8, 2, 2, 40, 16, 64, None) == -2
+    assert L.qg_kv_dequantize(8, 3, 2, 64, 16, 64, None) == -3        # scales misaligned
+    assert L.qg_kv_dequantize(8, 2, 2, 64, None, 64, None) == -1
+    assert L.qg_kv_dequantize(8, 2, -1, 64, 16, 64, None) == -2
