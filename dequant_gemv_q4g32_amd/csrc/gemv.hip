@@ -52,23 +52,21 @@ struct GemvArgs {
 // GEMV), S lanes per 64-weight unit (1, or 2 to halve the activation registers when M is
 // large), R rows per pipelined batch, MP more than one pass over K.
 
-#ifndef QG_GEMV_DEPTH
-#define QG_GEMV_DEPTH 2
-#endif
-#ifndef QG_MV_THREADS
-#define QG_MV_THREADS 1024
-#endif
+// Register pipeline stages over row batches. Deeper pipelines spill or lose occupancy and
+// measured no faster.
+constexpr int kGemvDepth = 2;
 
 // Largest workgroup of the streaming kernels: it bounds their registers (a workgroup must fit
-// on the 4 SIMDs of one CU) and the waves along K of one pass.
-template <int M> constexpr int mv_threads() { return M > 4 && QG_MV_THREADS > 512 ? 512 : QG_MV_THREADS; }
+// on the 4 SIMDs of one CU) and the waves along K of one pass. Eight activation rows need
+// more than the 128 VGPRs a 1024-thread bound leaves.
+template <int M> constexpr int mv_threads() { return M > 4 ? 512 : 1024; }
 
 // One workgroup of the streaming kernel over matrix b of a (block bx along the rows). Waves
 // past wk * wr (a grouped launch whose workgroup is sized for another matrix) have no rows
 // but still reach the barrier.
 template <int F, int M, int S, int R, bool MP>
 __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b) {
-  constexpr int D = M == 1 ? QG_GEMV_DEPTH : 2;   // pipeline stages
+  constexpr int D = kGemvDepth;                // pipeline stages
   using U = Unit<F>;
   using Raw = typename U::Raw;
   static_assert(R == 1 || R == 2, "rows per batch");
@@ -481,10 +479,7 @@ int fill_args(int fmt, const void *w, int64_t n, int64_t k, GemvArgs &a) {
 constexpr int64_t kSimds = 1024;           // 256 CUs x 4 SIMDs
 constexpr int kMaxBatches = 32;
 constexpr int64_t kActOrderLds = 64 * 1024;   // most activation bytes an act-order launch stages in LDS
-#ifndef QG_MV_MIN_BATCHES
-#define QG_MV_MIN_BATCHES 4
-#endif
-constexpr int kMinBatches = QG_MV_MIN_BATCHES;
+constexpr int kMinBatches = 4;
 constexpr int kMaxM = 8;                   // activation rows one streaming launch serves
 constexpr int kSkinnyMaxM = 16;            // activation rows of the matrix-core decode kernel
 

@@ -45,17 +45,11 @@ struct SkinnyArgs {
 };
 
 constexpr int kDW = 1;                     // steps of 4 units per wave and pass
-#ifndef QG_SKINNY_STAGES
-#define QG_SKINNY_STAGES 2
-#endif
-constexpr int kStages = QG_SKINNY_STAGES;
+constexpr int kStages = 2;                  // register stages over row tiles (3 and 4 measured slower)
 constexpr int kSkinnyMaxWk = 16;
 constexpr int kSkinnyMaxNb = 32;           // LDS: nb * 256 floats (a multiple of every kStages)
 constexpr uint32_t kSkX = 0x7FFFFFF0u;     // activation buffer range; offsets past it read 0
-#ifndef QG_SKINNY_WAVES
-#define QG_SKINNY_WAVES 4096
-#endif
-constexpr int64_t kSkinnyWaves = QG_SKINNY_WAVES;
+constexpr int64_t kSkinnyWaves = 4096;     // about 4 waves per SIMD
 
 template <int F>
 __global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs a) {
