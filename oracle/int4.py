@@ -1,4 +1,5 @@
-"""INT4 symmetric group-32 format ("q4g32").
+"""INT4 symmetric group formats: group 32 ("q4g32"), and groups of 16, 64 and 128 ("q4g16",
+"q4g64", "q4g128").
 
 Source: DBHOO-CIM page.
   * Section 2.1 / 3.1: symmetric quantization with scale = max|w| / 8 per group and
@@ -20,7 +21,13 @@ Readings:
     and the round therefore happen in fp32 here too, so that every integer decision is
     taken in the page's precision. A group whose max|w| / 8 is below 1e-12 gets the
     scale fp32(1e-12), as the page's max(scale, 1e-12) gives.
-  * K must be a multiple of 32 (the page's flattened reshape would otherwise straddle rows).
+  * K must be a multiple of the group (the page's flattened reshape would otherwise straddle
+    rows).
+  * Other group sizes: section 5.1 of the same page advises groups of 16 when a model has
+    many outlier weights (a smaller group confines an outlier's scale to fewer weights);
+    groups of 64 and 128 are the coarser end of the same trade. Everything else is the
+    group-32 format with G in place of 32: codes are packed the same way and each group has
+    one fp32 scale max|w| / 8, so a group costs G/2 + 4 bytes.
   * With scale = max|w| / 8, a group's largest positive weight maps to +8 and clamps to 7,
     so its error is a full scale; the page's section 3.1 remarks on this asymmetry.
     Everything else is within half a scale.
@@ -34,20 +41,23 @@ import numpy as np
 from . import bitstream
 
 GROUP = 32
+GROUPS = (16, 32, 64, 128)
 SCALE_FLOOR = np.float32(1e-12)
 
 
-def quantize(w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
-    """fp32 W [n, k] -> (q int8 [n, k] in [-8, 7], scale fp32 [n, k/32])."""
+def quantize(w: np.ndarray, group: int = GROUP) -> Tuple[np.ndarray, np.ndarray]:
+    """fp32 W [n, k] -> (q int8 [n, k] in [-8, 7], scale fp32 [n, k/group])."""
     w = np.asarray(w)
     if w.dtype != np.float32 or w.ndim != 2:
         raise TypeError("W must be a 2-D float32 array")
+    if group not in GROUPS:
+        raise ValueError("group must be 16, 32, 64 or 128")
     n, k = w.shape
-    if k % GROUP:
-        raise ValueError("K must be a multiple of 32")
+    if k % group:
+        raise ValueError("K must be a multiple of the group")
     if not np.all(np.isfinite(w)):
         raise ValueError("non-finite weight")
-    g = w.reshape(n, k // GROUP, GROUP)
+    g = w.reshape(n, k // group, group)
     amax = np.abs(g).max(axis=2) if k else np.zeros((n, 0), np.float32)
     scale = (amax / np.float32(8.0)).astype(np.float32)
     scale = np.maximum(scale, SCALE_FLOOR)
@@ -86,16 +96,18 @@ def unpack_codes(codes: np.ndarray, k: int) -> np.ndarray:
     return (bitstream.unpack_bits(codes, 4, k).astype(np.int16) - 8).astype(np.int8)
 
 
-def encode(w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
-    """fp32 W -> canonical (codes uint8 [n, k/2], scales fp32 [n, k/32])."""
-    q, s = quantize(w)
+def encode(w: np.ndarray, group: int = GROUP) -> Tuple[np.ndarray, np.ndarray]:
+    """fp32 W -> canonical (codes uint8 [n, k/2], scales fp32 [n, k/group])."""
+    q, s = quantize(w, group)
     return pack_codes(q), s
 
 
 def dequantize(q: np.ndarray, scale: np.ndarray) -> np.ndarray:
-    """W_hat[r, c] = q[r, c] * scale[r, c // 32] in fp64 (exact: 4-bit x 24-bit)."""
+    """W_hat[r, c] = q[r, c] * scale[r, c // G] in fp64 (exact: 4-bit x 24-bit); the group G
+    is k / scale.shape[1]."""
     n, k = q.shape
-    s = np.repeat(scale.astype(np.float64), GROUP, axis=1)
+    group = k // scale.shape[1] if scale.shape[1] else GROUP
+    s = np.repeat(scale.astype(np.float64), group, axis=1)
     return q.astype(np.float64) * s
 
 
@@ -104,6 +116,6 @@ def decode(codes: np.ndarray, scales: np.ndarray, k: int) -> np.ndarray:
     return dequantize(unpack_codes(codes, k), scales)
 
 
-def algorithmic_bytes(n: int, k: int) -> int:
-    """16 bytes of codes + 4 bytes of fp32 scale per group of 32."""
-    return n * (k // GROUP) * (16 + 4)
+def algorithmic_bytes(n: int, k: int, group: int = GROUP) -> int:
+    """group/2 bytes of codes + 4 bytes of fp32 scale per group."""
+    return n * (k // group) * (group // 2 + 4)
