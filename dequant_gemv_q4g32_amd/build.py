@@ -2,7 +2,10 @@
 
 Host code (quantizers, layouts) is compiled as plain C++ with -ffp-contract=off so that no
 multiply-add is fused in the quantizers' integer decisions. Device code is compiled for
-gfx950 only, with packed fp32 instructions disabled.
+gfx950 only, with packed fp32 instructions disabled and also with -ffp-contract=off: every
+fused multiply-add in the kernels is written out (fmaf, v_dot2), so that a kernel's
+arithmetic, and a row's result, does not depend on which instantiation computes it (the
+compiler would otherwise pick which product of a*b + c*d to fuse from the surrounding code).
 
 Usage: python dequant_gemv_q4g32_amd/build.py  (a plain script: it must not import the package,
 whose import loads the library it builds).
@@ -57,7 +60,7 @@ def build(verbose: bool = False) -> str:
         if not os.path.exists(path):
             continue
         obj = os.path.join(BUILD, src + ".o")
-        _run([hipcc, f"--offload-arch={ARCH}", "-O3", *common,
+        _run([hipcc, f"--offload-arch={ARCH}", "-O3", "-ffp-contract=off", *common,
               "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
               "-c", path, "-o", obj], verbose)
         objs.append(obj)

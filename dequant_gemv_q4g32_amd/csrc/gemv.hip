@@ -64,7 +64,7 @@ template <int M> constexpr int mv_threads() { return M > 4 ? 512 : 1024; }
 // One workgroup of the streaming kernel over matrix b of a (block bx along the rows). Waves
 // past wk * wr (a grouped launch whose workgroup is sized for another matrix) have no rows
 // but still reach the barrier.
-template <int F, int M, int S, int R, bool MP>
+template <int F, int M, int S, int R, bool MP, bool PERM = false>
 __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b) {
   constexpr int D = kGemvDepth;                // pipeline stages
   using U = Unit<F>;
@@ -111,7 +111,7 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
   // (contiguous 16-byte loads) once, so that each lane's gather by the permutation reads LDS
   // instead of issuing 2-byte global loads that touch a cache line each.
   const uint16_t *xl = a.xl_off >= 0 ? reinterpret_cast<const uint16_t *>(red + a.xl_off) : nullptr;
-  if (a.perm && xl) {
+  if (PERM && xl) {
     uint16_t *xw = reinterpret_cast<uint16_t *>(red + a.xl_off);
     const int64_t chunks = a.k / 8;                          // 16-byte chunks per row
     for (int64_t i = threadIdx.x; i < a.m * chunks; i += blockDim.x) {
@@ -152,31 +152,33 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
     // lane gathers its 8 activations per group of 4 pairs through 32-bit buffer loads of the
     // indices and 16-bit buffer loads of x (an index outside [0, k) reads 0, never past x).
     uint32_t xp[M][NP];
-    if (a.perm) {
+    // (a separate instantiation: the gather's registers at the branch made the register
+    // allocator spill the kernels with 4 and 8 activation rows)
+    if constexpr (PERM) {
+      // one pair of stored columns at a time (two indices, two gathered halves per row), so
+      // that the gather adds only a few registers to the activation registers it fills
       const rsrc_t pr = make_rsrc(a.perm, (uint32_t)(a.k * 4));
 #pragma unroll
-      for (int i = 0; i < NP / 4; ++i) {
-        uint32_t off = 4u * (uint32_t)U::pidx(h, 4 * i, S);
+      for (int t = 0; t < NP; ++t) {
+        uint32_t off = 4u * (uint32_t)(U::pidx(h, 4 * (t >> 2), S) + (t & 3));
         bool keepx = true;
         if (F == 4 && half && off >= 64) { off -= 64; keepx = false; }
-        const uint32_t kb = (uint32_t)(u * kUnit) + off / 2;   // first of the 8 stored columns
-        const u32x4 i0 = bld4c(pr, kb * 4, 0), i1 = bld4c(pr, kb * 4 + 16, 0);
-        const uint32_t idx[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+        const uint32_t kb = (uint32_t)(u * kUnit) + off / 2;   // the pair's first stored column
+        const u32x2 ix = bldx2<0>(pr, kb * 4, 0);
 #pragma unroll
         for (int mm = 0; mm < M; ++mm) {
           const bool live = mm < a.m && keepx;
           const int64_t row = mm < a.m ? mm : 0;
-          uint32_t hv[8];
+          uint32_t lo, hi;
           if (xl) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) hv[j] = idx[j] < (uint32_t)a.k ? xl[row * a.k + idx[j]] : 0u;
+            lo = ix.x < (uint32_t)a.k ? xl[row * a.k + ix.x] : 0u;
+            hi = ix.y < (uint32_t)a.k ? xl[row * a.k + ix.y] : 0u;
           } else {
             const rsrc_t xr = make_rsrc(x + row * a.ldx, (uint32_t)(a.k * 2));
-#pragma unroll
-            for (int j = 0; j < 8; ++j) hv[j] = bldh(xr, idx[j] * 2, 0);
+            lo = bldh(xr, ix.x * 2, 0);
+            hi = bldh(xr, ix.y * 2, 0);
           }
-#pragma unroll
-          for (int r = 0; r < 4; ++r) xp[mm][4 * i + r] = live ? (hv[2 * r] | (hv[2 * r + 1] << 16)) : 0u;
+          xp[mm][t] = live ? (lo | (hi << 16)) : 0u;
         }
       }
     } else {
@@ -268,9 +270,9 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
   }
 }
 
-template <int F, int M, int S, int R, bool MP>
+template <int F, int M, int S, int R, bool MP, bool PERM>
 __global__ __launch_bounds__(mv_threads<M>()) void mv_kernel(GemvArgs a) {
-  mv_body<F, M, S, R, MP>(a, blockIdx.x, blockIdx.y);
+  mv_body<F, M, S, R, MP, PERM>(a, blockIdx.x, blockIdx.y);
 }
 
 // Several matrices (any shapes, one activation-row count) in one launch: blocks
@@ -326,18 +328,18 @@ __device__ void decode_unit(const GemvArgs &a, const uint8_t *w, int64_t r, int6
                             int nvalid) {
   uint8_t c[64];
   float step[4] = {0, 0, 0, 0}, off[4] = {0, 0, 0, 0};
-  if (F == 4) {
+  if constexpr (q4_group(F) != 0) {
+    constexpr int G = q4_group(F);
     const uint8_t *pc = w + a.poff[0] + r * a.prb[0];
     const uint8_t *ps = w + a.poff[1] + r * a.prb[1];
     for (int i = 0; i < 8; ++i) {
       uint32_t v = (i < 4 || nvalid > 32) ? ld1(pc + split_off(a.units, u, i >> 2, 16) + 4 * (i & 3)) : 0u;
       for (int e = 0; e < 8; ++e) c[8 * i + e] = (v >> (4 * ((e >> 1) + 4 * (e & 1)))) & 15u;
     }
-    float s0 = __builtin_bit_cast(float, ld1(ps + split_off(a.units, u, 0, 4)));
-    float s1 = nvalid > 32 ? __builtin_bit_cast(float, ld1(ps + split_off(a.units, u, 1, 4))) : 0.f;
     for (int i = 0; i < nvalid; ++i) {
+      const int64_t g = (u * kUnit + i) / G;
       codes[i] = c[i];
-      vals[i] = (float)((int)c[i] - 8) * (i < 32 ? s0 : s1);
+      vals[i] = (float)((int)c[i] - 8) * __builtin_bit_cast(float, ld1(ps + q4_scale_off(G, a.units, g)));
     }
     return;
   }
@@ -567,9 +569,9 @@ MvPlan plan_mv(int ng, const int64_t *n, const int *wk, const int64_t *count, in
   return best;
 }
 
-template <int F, int M, int S, int R, bool MP>
-int launch_mv(GemvArgs a, int64_t count, hipStream_t s) {
-  void (*kern)(GemvArgs) = mv_kernel<F, M, S, R, MP>;
+template <int F, int M, int S, int R, bool MP, bool PERM>
+int launch_mv_k(GemvArgs a, int64_t count, hipStream_t s) {
+  void (*kern)(GemvArgs) = mv_kernel<F, M, S, R, MP, PERM>;
   static const int wps = waves_per_simd(reinterpret_cast<const void *>(kern));
   // act-order activations staged in LDS when they fit beside the partial sums
   const int64_t xl_bytes = a.perm ? a.m * a.k * 2 : 0;
@@ -585,6 +587,11 @@ int launch_mv(GemvArgs a, int64_t count, hipStream_t s) {
   }
   dim3 grid((unsigned)blocks, (unsigned)count);
   return launch(kern, grid, dim3((unsigned)(64 * P.W)), shm, s, a);
+}
+
+template <int F, int M, int S, int R, bool MP>
+int launch_mv(GemvArgs a, int64_t count, hipStream_t s) {
+  return a.perm ? launch_mv_k<F, M, S, R, MP, true>(a, count, s) : launch_mv_k<F, M, S, R, MP, false>(a, count, s);
 }
 
 template <int F, int M, int S, int R, bool MP>
@@ -688,6 +695,9 @@ int launch_mv_fmt(int fmt, GemvArgs a, int64_t count, hipStream_t s) {
     case 4: return launch_mv_f<4>(a, count, s);
     case 5: return launch_mv_f<5>(a, count, s);
     case 6: return launch_mv_f<6>(a, count, s);
+    case 7: return launch_mv_f<7>(a, count, s);
+    case 8: return launch_mv_f<8>(a, count, s);
+    case 9: return launch_mv_f<9>(a, count, s);
   }
   return QG_ERR_FORMAT;
 }
@@ -699,6 +709,9 @@ int launch_mv_group_fmt(int fmt, GemvGroup &G, hipStream_t s) {
     case 4: return launch_mv_group_f<4>(G, s);
     case 5: return launch_mv_group_f<5>(G, s);
     case 6: return launch_mv_group_f<6>(G, s);
+    case 7: return launch_mv_group_f<7>(G, s);
+    case 8: return launch_mv_group_f<8>(G, s);
+    case 9: return launch_mv_group_f<9>(G, s);
   }
   return QG_ERR_FORMAT;
 }
@@ -715,7 +728,7 @@ int qg_gemv_batched(int fmt, const void *w, int64_t w_stride, const uint16_t *x,
                     int64_t y_stride, int y_f32, int64_t count, int64_t n, int64_t k, void *stream) {
   if (!fmt_valid(fmt)) return QG_ERR_FORMAT;
   if (n < 0 || k < 0 || count < 0) return QG_ERR_SHAPE;
-  if ((fmt == 4 && k % 32) || (fmt != 4 && k % kQK)) return QG_ERR_SHAPE;
+  if (k % k_multiple(fmt)) return QG_ERR_SHAPE;
   if (k > kMaxK) return QG_ERR_SHAPE;
   if (count > 65535) return QG_ERR_SHAPE;
   if (n == 0 || count == 0) return QG_OK;
@@ -751,7 +764,7 @@ int qg_gemm(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int
             int64_t n, int64_t k, void *stream) {
   if (!fmt_valid(fmt)) return QG_ERR_FORMAT;
   if (n < 0 || k < 0 || m < 0) return QG_ERR_SHAPE;
-  if ((fmt == 4 && k % 32) || (fmt != 4 && k % kQK)) return QG_ERR_SHAPE;
+  if (k % k_multiple(fmt)) return QG_ERR_SHAPE;
   if (m > 1 && (ldx < k || ldy < n)) return QG_ERR_SHAPE;
   if (k > kMaxK) return QG_ERR_SHAPE;
   if (n == 0 || m == 0) return QG_OK;
@@ -789,7 +802,7 @@ int qg_gemm_act_order(int fmt, const void *w, const uint16_t *X, int64_t ldx, co
                       int64_t ldy, int y_f32, int64_t m, int64_t n, int64_t k, void *stream) {
   if (!fmt_valid(fmt)) return QG_ERR_FORMAT;
   if (n < 0 || k < 0 || m < 0 || m > kMaxM) return QG_ERR_SHAPE;
-  if ((fmt == 4 && k % 32) || (fmt != 4 && k % kQK)) return QG_ERR_SHAPE;
+  if (k % k_multiple(fmt)) return QG_ERR_SHAPE;
   if (m > 1 && (ldx < k || ldy < n)) return QG_ERR_SHAPE;
   if (k > kMaxK) return QG_ERR_SHAPE;
   if (n == 0 || m == 0) return QG_OK;
@@ -824,7 +837,7 @@ int qg_gemm_grouped(int fmt, int count, const void *const *w, const uint16_t *co
   for (int g = 0; g < count; ++g) {
     const int64_t lx = m > 1 ? ldx[g] : k[g], ly = m > 1 ? ldy[g] : n[g];
     if (n[g] < 0 || k[g] < 0) return QG_ERR_SHAPE;
-    if ((fmt == 4 && k[g] % 32) || (fmt != 4 && k[g] % kQK)) return QG_ERR_SHAPE;
+    if (k[g] % k_multiple(fmt)) return QG_ERR_SHAPE;
     if (m > 1 && (lx < k[g] || ly < n[g])) return QG_ERR_SHAPE;
     if (k[g] > kMaxK) return QG_ERR_SHAPE;
     if (n[g] == 0 || m == 0) continue;
@@ -861,6 +874,9 @@ int dequant_gemv_q2sb(const void *w, const uint16_t *x, uint16_t *y, int64_t n, 
 int dequant_gemv_q3sb(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(3, w, x, y, 0, n, k, s); }
 int dequant_gemv_q5sb(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(5, w, x, y, 0, n, k, s); }
 int dequant_gemv_q6sb(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(6, w, x, y, 0, n, k, s); }
+int dequant_gemv_q4g16(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(7, w, x, y, 0, n, k, s); }
+int dequant_gemv_q4g64(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(8, w, x, y, 0, n, k, s); }
+int dequant_gemv_q4g128(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(9, w, x, y, 0, n, k, s); }
 int dequant_gemm_q4g32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m, int64_t n,
                        int64_t k, void *s) {
   return qg_gemm(4, w, X, ldx, Y, ldy, 0, m, n, k, s);
@@ -881,10 +897,22 @@ int dequant_gemm_q6sb(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y
                       int64_t k, void *s) {
   return qg_gemm(6, w, X, ldx, Y, ldy, 0, m, n, k, s);
 }
+int dequant_gemm_q4g16(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m, int64_t n,
+                      int64_t k, void *s) {
+  return qg_gemm(7, w, X, ldx, Y, ldy, 0, m, n, k, s);
+}
+int dequant_gemm_q4g64(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m, int64_t n,
+                      int64_t k, void *s) {
+  return qg_gemm(8, w, X, ldx, Y, ldy, 0, m, n, k, s);
+}
+int dequant_gemm_q4g128(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m, int64_t n,
+                      int64_t k, void *s) {
+  return qg_gemm(9, w, X, ldx, Y, ldy, 0, m, n, k, s);
+}
 
 int qg_dequantize(int fmt, const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream) {
   if (!fmt_valid(fmt)) return QG_ERR_FORMAT;
-  if (n < 0 || k < 0 || (fmt == 4 && k % 32) || (fmt != 4 && k % kQK)) return QG_ERR_SHAPE;
+  if (n < 0 || k < 0 || k % k_multiple(fmt)) return QG_ERR_SHAPE;
   if (n == 0 || k == 0) return QG_OK;
   if (!w || (!w_out && !codes_out)) return QG_ERR_NULL;
   if (!aligned(w, 256) || (w_out && !aligned(w_out, 4))) return QG_ERR_ALIGN;
@@ -900,6 +928,9 @@ int qg_dequantize(int fmt, const void *w, float *w_out, uint8_t *codes_out, int6
     case 4: return launch(dequant_kernel<4>, grid, block, 0, s, a, w_out, codes_out);
     case 5: return launch(dequant_kernel<5>, grid, block, 0, s, a, w_out, codes_out);
     case 6: return launch(dequant_kernel<6>, grid, block, 0, s, a, w_out, codes_out);
+    case 7: return launch(dequant_kernel<7>, grid, block, 0, s, a, w_out, codes_out);
+    case 8: return launch(dequant_kernel<8>, grid, block, 0, s, a, w_out, codes_out);
+    case 9: return launch(dequant_kernel<9>, grid, block, 0, s, a, w_out, codes_out);
   }
   return QG_ERR_FORMAT;
 }
@@ -921,5 +952,8 @@ int dequantize_q2sb(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, v
 int dequantize_q3sb(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(3, w, o, c, n, k, s); }
 int dequantize_q5sb(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(5, w, o, c, n, k, s); }
 int dequantize_q6sb(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(6, w, o, c, n, k, s); }
+int dequantize_q4g16(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(7, w, o, c, n, k, s); }
+int dequantize_q4g64(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(8, w, o, c, n, k, s); }
+int dequantize_q4g128(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(9, w, o, c, n, k, s); }
 
 }  // extern "C"

@@ -95,11 +95,11 @@ bool sb_spec(int fmt, SB *s) {
 // ---------------------------------------------------------------- quantizers -------------
 
 // One INT4 row: codes (k/2 bytes, canonical nibble order) and fp32 scales (k/32).
-int quantize_row_q4(const float *w, int64_t k, uint8_t *codes, float *scales) {
-  for (int64_t g = 0; g < k / 32; ++g) {
-    const float *v = w + g * 32;
+int quantize_row_q4(const float *w, int64_t k, int G, uint8_t *codes, float *scales) {
+  for (int64_t g = 0; g < k / G; ++g) {
+    const float *v = w + g * G;
     float amax = 0.0f;
-    for (int i = 0; i < 32; ++i) {
+    for (int i = 0; i < G; ++i) {
       if (!std::isfinite(v[i])) return QG_ERR_NONFINITE;
       float a = std::fabs(v[i]);
       if (a > amax) amax = a;
@@ -107,7 +107,7 @@ int quantize_row_q4(const float *w, int64_t k, uint8_t *codes, float *scales) {
     float scale = amax / 8.0f;
     if (scale < 1e-12f) scale = 1e-12f;
     scales[g] = scale;
-    for (int i = 0; i < 32; i += 2) {
+    for (int i = 0; i < G; i += 2) {
       int u[2];
       for (int t = 0; t < 2; ++t) {
         float r = v[i + t] / scale;                  // fp32 quotient
@@ -116,7 +116,7 @@ int quantize_row_q4(const float *w, int64_t k, uint8_t *codes, float *scales) {
         if (q > 7.0f) q = 7.0f;
         u[t] = (int)q + 8;
       }
-      codes[(g * 32 + i) / 2] = (uint8_t)(u[0] | (u[1] << 4));
+      codes[(g * G + i) / 2] = (uint8_t)(u[0] | (u[1] << 4));
     }
   }
   return QG_OK;
@@ -254,8 +254,7 @@ int parallel_rows(int64_t n, int64_t work_per_row, F f) {
 
 bool shape_ok(int fmt, int64_t n, int64_t k) {
   if (n < 0 || k < 0) return false;
-  if (fmt == 4) return k % 32 == 0;
-  return k % kQK == 0;
+  return k % k_multiple(fmt) == 0;
 }
 
 // ---------------------------------------------------------------- device layout ----------
@@ -267,7 +266,7 @@ inline uint32_t getbit(const uint32_t *w, int pos) { return (w[pos >> 5] >> (pos
 // at unit position k, for the code planes of each format. For q5sb/q6sb this is the low
 // nibble (b < 4) in the nibble dwords; high bits are placed by hi_pos().
 int code_pos(int fmt, int k, int b) {
-  if (fmt == 4 || fmt == 5 || fmt == 6) {            // nibble dwords
+  if (q4_group(fmt) || fmt == 5 || fmt == 6) {        // nibble dwords
     int i = k >> 3, e = k & 7;
     return i * 32 + q4_slot(e) * 4 + b;
   }
@@ -306,13 +305,13 @@ struct Planes {
 void row_to_device(int fmt, const uint8_t *canon, int64_t k, int64_t r, int64_t n, Planes P) {
   const int64_t units = (k + kUnit - 1) / kUnit;
   std::vector<uint8_t> codes((size_t)(units * kUnit), 0);
-  if (fmt == 4) {
+  if (q4_group(fmt)) {
+    const int G = q4_group(fmt);
     const uint8_t *cr = canon + r * (k / 2);
     for (int64_t i = 0; i < k; ++i) codes[(size_t)i] = (cr[i >> 1] >> (4 * (i & 1))) & 15;
-    const uint8_t *sr = canon + n * (k / 2) + r * (k / 32) * 4;
+    const uint8_t *sr = canon + n * (k / 2) + r * (k / G) * 4;
     uint8_t *ds = P.p[1] + r * P.rb[1];
-    for (int64_t g = 0; g < k / 32; ++g)             // group 2u + h -> half h of unit u
-      std::memcpy(ds + split_off(units, g >> 1, (int)(g & 1), 4), sr + g * 4, 4);
+    for (int64_t g = 0; g < k / G; ++g) std::memcpy(ds + q4_scale_off(G, units, g), sr + g * 4, 4);
     uint8_t *dst = P.p[0] + r * P.rb[0];
     for (int64_t u = 0; u < units; ++u) {
       uint32_t wv[8] = {0};
@@ -400,7 +399,7 @@ void row_from_device(int fmt, const uint8_t *const *pl, const int64_t *rb, int64
   std::vector<uint8_t> codes((size_t)(units * kUnit), 0);
   for (int64_t u = 0; u < units; ++u) {
     uint32_t a[8] = {0}, hb[4] = {0};
-    if (fmt == 4) {
+    if (q4_group(fmt)) {
       std::memcpy(a, pl[0] + r * rb[0] + split_off(units, u, 0, 16), 16);
       if (k / 2 - u * 32 > 16) std::memcpy(a + 4, pl[0] + r * rb[0] + split_off(units, u, 1, 16), 16);
     } else if (fmt == 2) {
@@ -424,11 +423,12 @@ void row_from_device(int fmt, const uint8_t *const *pl, const int64_t *rb, int64
       codes[(size_t)(u * kUnit + kk)] = (uint8_t)cv;
     }
   }
-  if (fmt == 4) {
+  if (q4_group(fmt)) {
+    const int G = q4_group(fmt);
     uint8_t *cr = canon + r * (k / 2);
     for (int64_t i = 0; i < k; i += 2) cr[i / 2] = (uint8_t)(codes[(size_t)i] | (codes[(size_t)i + 1] << 4));
-    for (int64_t g = 0; g < k / 32; ++g)
-      std::memcpy(canon + n * (k / 2) + r * (k / 32) * 4 + g * 4, pl[1] + r * rb[1] + split_off(units, g >> 1, (int)(g & 1), 4), 4);
+    for (int64_t g = 0; g < k / G; ++g)
+      std::memcpy(canon + n * (k / 2) + r * (k / G) * 4 + g * 4, pl[1] + r * rb[1] + q4_scale_off(G, units, g), 4);
     return;
   }
   SB s;
@@ -503,7 +503,7 @@ const char *qg_strerror(int status) {
   switch (status) {
     case QG_OK: return "ok";
     case QG_ERR_NULL: return "a required pointer is NULL";
-    case QG_ERR_SHAPE: return "n, k or m out of range (k must be a multiple of 256, or of 32 for q4g32)";
+    case QG_ERR_SHAPE: return "n, k or m out of range (k must be a multiple of 256 for the super-block formats, of 32 for q4g32, 64 for q4g16 and q4g64, 128 for q4g128)";
     case QG_ERR_ALIGN: return "misaligned device pointer or leading dimension";
     case QG_ERR_NONFINITE: return "a weight is NaN or infinite";
     case QG_ERR_RANGE: return "a super-block scale does not fit fp16, or a code does not fit its width";
@@ -518,7 +518,7 @@ int qg_canonical_bytes(int fmt, int64_t n, int64_t k, int64_t *bytes) {
   if (!bytes) return QG_ERR_NULL;
   if (!fmt_valid(fmt)) return QG_ERR_FORMAT;
   if (!shape_ok(fmt, n, k)) return QG_ERR_SHAPE;
-  if (fmt == 4) { *bytes = n * (k / 2) + n * (k / 32) * 4; return QG_OK; }
+  if (q4_group(fmt)) { *bytes = n * (k / 2) + n * (k / q4_group(fmt)) * 4; return QG_OK; }
   SB s;
   sb_spec(fmt, &s);
   *bytes = n * (k / kQK) * s.rec;
@@ -555,13 +555,14 @@ int qg_quantize(int fmt, const float *w, int64_t n, int64_t k, int64_t ldw, uint
   if (!shape_ok(fmt, n, k) || ldw < k) return QG_ERR_SHAPE;
   if (n == 0 || k == 0) return QG_OK;
   if (!w || !canonical) return QG_ERR_NULL;
-  if (fmt == 4) {
+  if (q4_group(fmt)) {
+    const int G = q4_group(fmt);
     uint8_t *codes = canonical;
     float *scales = reinterpret_cast<float *>(canonical + n * (k / 2));
     // scales start at n*k/2 bytes, a multiple of 16: aligned for float
     return parallel_rows(n, k, [&](int64_t r0, int64_t r1) {
       for (int64_t r = r0; r < r1; ++r) {
-        int st = quantize_row_q4(w + r * ldw, k, codes + r * (k / 2), scales + r * (k / 32));
+        int st = quantize_row_q4(w + r * ldw, k, G, codes + r * (k / 2), scales + r * (k / G));
         if (st != QG_OK) return st;
       }
       return (int)QG_OK;
@@ -581,6 +582,9 @@ int qg_quantize(int fmt, const float *w, int64_t n, int64_t k, int64_t ldw, uint
 }
 
 int quantize_q4g32(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(4, w, n, k, ldw, c); }
+int quantize_q4g16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(7, w, n, k, ldw, c); }
+int quantize_q4g64(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(8, w, n, k, ldw, c); }
+int quantize_q4g128(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(9, w, n, k, ldw, c); }
 int quantize_q2sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(2, w, n, k, ldw, c); }
 int quantize_q3sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(3, w, n, k, ldw, c); }
 int quantize_q5sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(5, w, n, k, ldw, c); }

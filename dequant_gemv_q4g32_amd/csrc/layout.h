@@ -60,6 +60,14 @@ constexpr int64_t kPlaneAlign = 256;
 #endif
 QG_HOST_DEVICE inline int64_t split_off(int64_t units, int64_t u, int second, int hb) { return (second ? units * hb : 0) + u * hb; }
 
+// Byte offset, within a row of an INT4 group format's scale plane, of the fp32 scale of
+// group g (G weights per group; units lane units per row).
+QG_HOST_DEVICE inline int64_t q4_scale_off(int G, int64_t units, int64_t g) {
+  if (G == 32) return split_off(units, g >> 1, (int)(g & 1), 4);
+  if (G == 16) return split_off(units, g >> 2, (int)((g >> 1) & 1), 8) + 4 * (g & 1);
+  return 4 * g;                                     // groups of 64 and 128: in order
+}
+
 // Bytes per lane unit of each plane, and the number of planes.
 struct FmtPlanes {
   int nplanes;
@@ -67,7 +75,21 @@ struct FmtPlanes {
   int sb_bytes[4];     // bytes per 256-weight super-block (when unit_bytes == 0)
 };
 
-inline bool fmt_valid(int fmt) { return fmt == 2 || fmt == 3 || fmt == 4 || fmt == 5 || fmt == 6; }
+// INT4 symmetric group formats: group size of the format code (0 for the super-block formats).
+// Codes 7, 8 and 9 are groups of 16, 64 and 128; they share q4g32's code plane (units of 64
+// weights, split halves) and differ only in the fp32 scale plane: 4 scales per unit in split
+// halves of 8 bytes (group 16; half h of unit u holds groups 4u + 2h, 4u + 2h + 1), one per
+// unit (group 64), one per two units (group 128).
+QG_HOST_DEVICE constexpr int q4_group(int fmt) { return fmt == 4 ? 32 : fmt == 7 ? 16 : fmt == 8 ? 64 : fmt == 9 ? 128 : 0; }
+
+inline bool fmt_valid(int fmt) { return (fmt >= 2 && fmt <= 6) || q4_group(fmt) != 0; }
+
+// K must be a multiple of this: 32 for q4g32 (a row may end in half a unit), whole units
+// (64) for q4g16 and q4g64, 128 for q4g128, a super-block (256) for the other formats.
+inline int64_t k_multiple(int fmt) {
+  const int G = q4_group(fmt);
+  return G == 32 ? 32 : G ? (G > kUnit ? G : kUnit) : kQK;
+}
 
 inline FmtPlanes fmt_planes(int fmt) {
   switch (fmt) {
@@ -76,14 +98,19 @@ inline FmtPlanes fmt_planes(int fmt) {
     case 3: return {4, {16, 8, 0, 0}, {0, 0, 12, 2}};         // codes A, codes B, sc, d
     case 5: return {4, {32, 8, 0, 0}, {0, 0, 12, 4}};         // lo, hi, sc/m, (d, dmin)
     case 6: return {4, {32, 16, 4, 0}, {0, 0, 0, 2}};         // lo, hi, sc, d
+    case 7: return {2, {32, 16, 0, 0}, {0, 0, 0, 0}};         // codes, 4 fp32 scales per unit
+    case 8: return {2, {32, 4, 0, 0}, {0, 0, 0, 0}};          // codes, 1 fp32 scale per unit
+    case 9: return {2, {32, 2, 0, 0}, {0, 0, 0, 0}};          // codes, 1 fp32 scale per 2 units
     default: return {0, {0, 0, 0, 0}, {0, 0, 0, 0}};
   }
 }
 
-// Row bytes of plane p for a row of k weights (k a multiple of 256, or of 32 for q4g32).
+// Row bytes of plane p for a row of k weights (k a multiple of 256 for the super-block
+// formats, of 32 for q4g32, of 64 for q4g16 and q4g64, of 128 for q4g128).
 inline int64_t plane_row_bytes(int fmt, int p, int64_t k) {
   FmtPlanes f = fmt_planes(fmt);
   if (fmt == 4) return p == 0 ? k / 2 : (k / 32) * 4;
+  if (q4_group(fmt)) return p == 0 ? k / 2 : (k / q4_group(fmt)) * 4;
   if (f.unit_bytes[p]) return (k / kUnit) * f.unit_bytes[p];
   return (k / kQK) * f.sb_bytes[p];
 }

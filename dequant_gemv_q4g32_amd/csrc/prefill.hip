@@ -229,6 +229,9 @@ int launch_prefill(int fmt, const void *w, const uint16_t *X, int64_t ldx, void 
     case 4: return launch(prefill_kernel<4>, grid, block, 0, s, a);
     case 5: return launch(prefill_kernel<5>, grid, block, 0, s, a);
     case 6: return launch(prefill_kernel<6>, grid, block, 0, s, a);
+    case 7: return launch(prefill_kernel<7>, grid, block, 0, s, a);
+    case 8: return launch(prefill_kernel<8>, grid, block, 0, s, a);
+    case 9: return launch(prefill_kernel<9>, grid, block, 0, s, a);
   }
   return QG_ERR_FORMAT;
 }

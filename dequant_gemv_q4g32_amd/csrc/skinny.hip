@@ -205,6 +205,9 @@ int launch_skinny(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *
     case 4: return launch(skinny_kernel<4>, grid, block, shm, s, a);
     case 5: return launch(skinny_kernel<5>, grid, block, shm, s, a);
     case 6: return launch(skinny_kernel<6>, grid, block, shm, s, a);
+    case 7: return launch(skinny_kernel<7>, grid, block, shm, s, a);
+    case 8: return launch(skinny_kernel<8>, grid, block, shm, s, a);
+    case 9: return launch(skinny_kernel<9>, grid, block, shm, s, a);
   }
   return QG_ERR_FORMAT;
 }

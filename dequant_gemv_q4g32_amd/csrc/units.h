@@ -23,11 +23,13 @@ struct Lane {
   uint32_t sh;              // bit offset of this unit's 6-bit fields in its 8-byte window
   uint32_t half16;          // offset of the second halves in a split 16-byte-half plane row
   uint32_t half4;           // same for the split q4g32 scale plane
+  uint32_t half8;           // same for the split q4g16 scale plane (8-byte halves)
   int h = 0;                // the lane's half of its unit when two lanes share a unit
   __device__ uint32_t row(int p, int64_t r) const { return (uint32_t)r * prb[p]; }
   __device__ void set_halves(int64_t units) {
     half16 = (uint32_t)(units * 16);
     half4 = (uint32_t)(units * 4);
+    half8 = (uint32_t)(units * 8);
   }
 };
 
@@ -69,87 +71,133 @@ __device__ __forceinline__ uint32_t asym_pair(uint32_t P, float mul, float add) 
 
 template <int F> struct Unit;
 
-// ---- INT4 group-32: a unit is two groups; with S = 2 a lane owns one group
-// NKS(S): per-lane constants per activation row, for S lanes per unit.
-template <> struct Unit<4> {
-  static constexpr int NK = 2;                    // constants per activation row (S = 1)
-  __host__ __device__ static constexpr int NKS(int S) { return NK / S; }
-  struct Raw { u32x4 c0, c1; float s0, s1; };
+// ---- INT4 groups of G = 16, 32, 64 or 128 weights, one fp32 scale each. A unit (64
+// weights, 8 code dwords; dword i holds weights 8i..8i+7) spans 64 / G groups, or half a
+// group of 128. With S = 2 a lane owns half a unit (4 dwords, loaded alone). The lane's
+// groups ("lane groups") cover its dwords in runs of G / 8 (at most its 8 / S dwords); their
+// scales are loaded into s[0..], in order.
+// NKS(S): per-lane constants per activation row, one per lane group.
+template <int G> struct UnitQ4 {
+  static_assert(G == 16 || G == 32 || G == 64 || G == 128, "INT4 group size");
+  static constexpr int NG = G <= 64 ? 64 / G : 1;   // scales a unit touches
+  static constexpr int NK = NG;                     // constants per activation row (S = 1)
+  __host__ __device__ static constexpr int NKS(int S) { return NG / S > 0 ? NG / S : 1; }
+  static constexpr int DPG = G / 8;                 // code dwords per group
+  template <int S> static constexpr int dpl() { return DPG < 8 / S ? DPG : 8 / S; }   // dwords per lane group
+  struct Raw { u32x4 c0, c1; float s[NG]; };
   __device__ static int pidx(int h, int p, int S) { return S == 1 ? p : 16 * h + p; }
-  __device__ static void offsets(int64_t u, uint32_t *off) { off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 4); }
-  // S = 2: the lane's own group only (half L.h of the unit), into c0 and s0
+  __device__ static void offsets(int64_t u, uint32_t *off) {
+    off[0] = (uint32_t)(u * 16);
+    off[1] = (uint32_t)(G == 16 ? u * 8 : G == 128 ? (u >> 1) * 4 : u * 4);
+  }
+  // S = 2: the lane's own half only (half L.h of the unit), into c0 and s[0..NKS(2))
   template <int AUX = kNT, int S = 1> __device__ static void load(Raw &q, const Lane &L, int64_t r, bool half) {
     const uint32_t r0 = L.row(0, r), r1 = L.row(1, r);
     if constexpr (S == 2) {
-      // a half unit (k % 64 == 32) has no second group: that lane re-reads the first and
-      // meets zero activations
+      // (q4g32) a half unit (k % 64 == 32) has no second group: that lane re-reads the first
+      // and meets zero activations
       const bool second = L.h && !half;
       q.c0 = bldx4<AUX>(L.rs[0], L.off[0] + (second ? L.half16 : 0u), r0);
-      q.s0 = __builtin_bit_cast(float, bld1(L.rs[1], L.off[1] + (second ? L.half4 : 0u), r1));
-      return;
+    } else {
+      q.c0 = bldx4<AUX>(L.rs[0], L.off[0], r0);
+      // (q4g32) a half unit has one group; its second group's activations are zero
+      q.c1 = bldx4<AUX>(L.rs[0], L.off[0] + (half ? 0u : L.half16), r0);
     }
-    q.c0 = bldx4<AUX>(L.rs[0], L.off[0], r0);
-    // a half unit (k % 64 == 32) has one group; its second group's activations are zero
-    q.c1 = bldx4<AUX>(L.rs[0], L.off[0] + (half ? 0u : L.half16), r0);
-    // Two 32-bit loads, not one 64-bit load: this toolchain narrows a multi-dword buffer load
-    // whose elements are bit-cast to float to its first dword and reuses that dword for the
-    // second element (vectors used in integer arithmetic, like the code words, are unaffected).
-    q.s0 = __builtin_bit_cast(float, bld1(L.rs[1], L.off[1], r1));
-    q.s1 = __builtin_bit_cast(float, bld1(L.rs[1], L.off[1] + (half ? 0u : L.half4), r1));
-  }
-  // xp: the lane's pairs (32 / S); kc: NK / S constants
-  template <int S> __device__ static void prep(uint32_t *xp, float *kc) {
+    // Scales as separate 32-bit loads or as integer pairs passed through keep(): this
+    // toolchain narrows a multi-dword buffer load whose elements are bit-cast to float to its
+    // first dword and reuses that dword for the second element.
+    if constexpr (G == 32) {
+      if constexpr (S == 2) {
+        q.s[0] = __builtin_bit_cast(float, bld1(L.rs[1], L.off[1] + (L.h && !half ? L.half4 : 0u), r1));
+      } else {
+        q.s[0] = __builtin_bit_cast(float, bld1(L.rs[1], L.off[1], r1));
+        q.s[1] = __builtin_bit_cast(float, bld1(L.rs[1], L.off[1] + (half ? 0u : L.half4), r1));
+      }
+    } else if constexpr (G == 16) {
 #pragma unroll
-    for (int g = 0; g < 2 / S; ++g) {
+      for (int hh = 0; hh < 2 / S; ++hh) {
+        const uint32_t o = L.off[1] + (S == 2 ? (L.h ? L.half8 : 0u) : (hh ? L.half8 : 0u));
+        const u32x2 v = bldx2<0>(L.rs[1], o, r1);
+        q.s[2 * hh] = __builtin_bit_cast(float, keep(v.x));
+        q.s[2 * hh + 1] = __builtin_bit_cast(float, keep(v.y));
+      }
+    } else {
+      q.s[0] = __builtin_bit_cast(float, bld1(L.rs[1], L.off[1], r1));
+    }
+  }
+  // xp: the lane's pairs (32 / S; dword i's pairs are 4i..4i+3, classes 1, 16, 1, 16);
+  // kc: one constant per lane group
+  template <int S> __device__ static void prep(uint32_t *xp, float *kc) {
+    constexpr int D = dpl<S>();
+#pragma unroll
+    for (int g = 0; g < NKS(S); ++g) {
       float x1 = 0.f, x16 = 0.f;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        x1 = dot2(xp[16 * g + 4 * i + 0], kOnes, x1);
-        x1 = dot2(xp[16 * g + 4 * i + 2], kOnes, x1);
-        x16 = dot2(xp[16 * g + 4 * i + 1], kOnes, x16);
-        x16 = dot2(xp[16 * g + 4 * i + 3], kOnes, x16);
+      for (int i = D * g; i < D * (g + 1); ++i) {
+        x1 = dot2(xp[4 * i + 0], kOnes, x1);
+        x1 = dot2(xp[4 * i + 2], kOnes, x1);
+        x16 = dot2(xp[4 * i + 1], kOnes, x16);
+        x16 = dot2(xp[4 * i + 3], kOnes, x16);
       }
       kc[g] = -(1032.0f * x1 + 72.0f * x16);   // sum (u - 8) x = A1 + A16/16, A1 starting here
     }
   }
   template <int M, int S>
   __device__ static void dot(const Raw &q, int h, const uint32_t (*xp)[32 / S], const float (*kc)[NKS(S)], float *out) {
+    constexpr int D = dpl<S>();
+    // (S = 2 loaded the lane's own half into c0)
+    const uint32_t d[8] = {q.c0.x, q.c0.y, q.c0.z, q.c0.w, S == 1 ? q.c1.x : 0u, S == 1 ? q.c1.y : 0u,
+                           S == 1 ? q.c1.z : 0u, S == 1 ? q.c1.w : 0u};
 #pragma unroll
-    for (int g = 0; g < 2 / S; ++g) {
-      // (S = 2 loaded the lane's own group into c0, s0)
-      const u32x4 c = S == 1 && g ? q.c1 : q.c0;
-      const float scale = S == 1 && g ? q.s1 : q.s0;
+    for (int g = 0; g < NKS(S); ++g) {
       float a1[M], a16[M];
 #pragma unroll
       for (int m = 0; m < M; ++m) { a1[m] = kc[m][g]; a16[m] = 0.f; }
-      const uint32_t d[4] = {c.x, c.y, c.z, c.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
+      for (int i = D * g; i < D * (g + 1); ++i) {
         const uint32_t v = d[i], v8 = v >> 8;
         const uint32_t p0 = pick(v, QG_SMASK(0x000F000Fu)), p1 = pick(v, QG_SMASK(0x00F000F0u));
         const uint32_t p2 = pick(v8, QG_SMASK(0x000F000Fu)), p3 = pick(v8, QG_SMASK(0x00F000F0u));
 #pragma unroll
         for (int m = 0; m < M; ++m) {
-          a1[m] = dot2(p0, xp[m][16 * g + 4 * i + 0], a1[m]);
-          a16[m] = dot2(p1, xp[m][16 * g + 4 * i + 1], a16[m]);
-          a1[m] = dot2(p2, xp[m][16 * g + 4 * i + 2], a1[m]);
-          a16[m] = dot2(p3, xp[m][16 * g + 4 * i + 3], a16[m]);
+          a1[m] = dot2(p0, xp[m][4 * i + 0], a1[m]);
+          a16[m] = dot2(p1, xp[m][4 * i + 1], a16[m]);
+          a1[m] = dot2(p2, xp[m][4 * i + 2], a1[m]);
+          a16[m] = dot2(p3, xp[m][4 * i + 3], a16[m]);
         }
       }
+      const float scale = q.s[g];
 #pragma unroll
       for (int m = 0; m < M; ++m) out[m] = __builtin_fmaf(scale, __builtin_fmaf(a16[m], 0.0625f, a1[m]), out[m]);
     }
   }
-  // fp16 w_hat of the 16 pairs of half h (group h), in local pair order; S = 2: q holds only
-  // that half (loaded by load<AUX, 2>)
+  // fp16 w_hat of the 16 pairs of half h (dwords 4h..4h+3), in local pair order; S = 2: q
+  // holds only that half (loaded by load<AUX, 2>)
   template <int S = 1> __device__ static void wide(const Raw &q, int h, uint32_t *out) {
-    const u32x4 c = S == 1 && h ? q.c1 : q.c0;
-    const float scale = S == 1 && h ? q.s1 : q.s0;
-    const _Float16 m1 = (_Float16)scale, m16 = (_Float16)(scale * 0.0625f);
-    const uint32_t d[4] = {c.x, c.y, c.z, c.w};
+    const u32x4 c0 = q.c0, c1 = S == 1 ? q.c1 : q.c0;
+    const uint32_t dw[4] = {sel(S == 1 && h, c1.x, c0.x), sel(S == 1 && h, c1.y, c0.y), sel(S == 1 && h, c1.z, c0.z),
+                            sel(S == 1 && h, c1.w, c0.w)};
+    float sc[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t v = d[i], v8 = v >> 8;
+      if constexpr (G == 16) {
+        // dwords 0, 1 of the half: group 2h (lane scale 0 when S = 2); dwords 2, 3: 2h + 1
+        const int j = i >> 1;
+        sc[i] = S == 1 ? __builtin_bit_cast(float, sel(h, __builtin_bit_cast(uint32_t, q.s[2 + j]),
+                                                       __builtin_bit_cast(uint32_t, q.s[j])))
+                       : q.s[j];
+      } else if constexpr (G == 32) {
+        sc[i] = S == 1 ? __builtin_bit_cast(float, sel(h, __builtin_bit_cast(uint32_t, q.s[NG - 1]),
+                                                       __builtin_bit_cast(uint32_t, q.s[0])))
+                       : q.s[0];
+      } else {
+        sc[i] = q.s[0];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const _Float16 m1 = (_Float16)sc[i], m16 = (_Float16)(sc[i] * 0.0625f);
+      const uint32_t v = dw[i], v8 = v >> 8;
       out[4 * i + 0] = sym_pair(pick(v, QG_SMASK(0x000F000Fu)), (_Float16)-1032.0f, m1);
       out[4 * i + 1] = sym_pair(pick(v, QG_SMASK(0x00F000F0u)), (_Float16)-1152.0f, m16);
       out[4 * i + 2] = sym_pair(pick(v8, QG_SMASK(0x000F000Fu)), (_Float16)-1032.0f, m1);
@@ -157,6 +205,10 @@ template <> struct Unit<4> {
     }
   }
 };
+template <> struct Unit<4> : UnitQ4<32> {};
+template <> struct Unit<7> : UnitQ4<16> {};
+template <> struct Unit<8> : UnitQ4<64> {};
+template <> struct Unit<9> : UnitQ4<128> {};
 
 // ---- 2-bit super-block: a unit is a quarter super-block (4 sub-blocks of 16). Sub-block j
 // sits at class 4^j in every dword; with S = 2 lane half h owns dwords 2h, 2h+1, i.e. pairs

@@ -7,6 +7,9 @@
  *   QG_Q4G32  INT4 symmetric, groups of 32 consecutive weights of a row, fp32 scale per group:
  *             scale = max(max|w| / 8, 1e-12), q = clamp(rint(w / scale), -8, 7) in fp32,
  *             w_hat = q * scale; 16 B of codes + 4 B of scale per group (5.0 bpw).
+ *   QG_Q4G16, QG_Q4G64, QG_Q4G128  the same INT4 code with groups of 16, 64 or 128 weights
+ *             (6.0, 4.5, 4.25 bpw; DBHOO-CIM page section 5.1 advises groups of 16 against
+ *             outlier weights). k must be a multiple of 64 (of 128 for QG_Q4G128).
  *   QG_Q2SB   256-weight super-block, 16 sub-blocks of 16, 2-bit codes c, 4-bit sub-scale sc
  *             and 4-bit sub-min m, fp16 d and dmin: w_hat = d*sc*c - dmin*m  (84 B, 2.625 bpw).
  *   QG_Q3SB   16 sub-blocks of 16, 3-bit codes, 6-bit sc, fp16 d: w_hat = d*sc*(c - 4)
@@ -27,7 +30,7 @@
  *
  * Two encodings of a quantized matrix W [n][k] (W is out_features x in_features):
  *   canonical  the pages' interchange layout. q4g32: codes [n][k/2] (byte = u[2j] | u[2j+1] << 4
- *              with u = q + 8) followed by fp32 scales [n][k/32]. Super-block formats: records
+ *              with u = q + 8) followed by fp32 scales [n][k/32] (q4gG: [n][k/G]). Super-block formats: records
  *              [n][k/256] of 84/110/176/210 bytes; fields in the byte table's column order
  *              (codes [, high-bit plane], sub-scales, d [, dmin]); every bit field is a
  *              little-endian bitstream (code i at bits [b*i, b*i + b), section 2.2's unpack3
@@ -65,7 +68,10 @@ typedef enum qg_format {
   QG_Q3SB = 3,
   QG_Q4G32 = 4,
   QG_Q5SB = 5,
-  QG_Q6SB = 6
+  QG_Q6SB = 6,
+  QG_Q4G16 = 7,
+  QG_Q4G64 = 8,
+  QG_Q4G128 = 9
 } qg_format;
 
 typedef enum qg_status {
@@ -124,6 +130,9 @@ int quantize_q2sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *ca
 int quantize_q3sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
 int quantize_q5sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
 int quantize_q6sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
+int quantize_q4g16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
+int quantize_q4g64(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
+int quantize_q4g128(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
 
 /* Canonical encoding (host) -> device layout (host buffer of qg_device_layout().total_bytes;
  * padding is zeroed). A pure bit permutation. */
@@ -144,6 +153,9 @@ int dequant_gemv_q2sb(const void *w, const uint16_t *x, uint16_t *y, int64_t n, 
 int dequant_gemv_q3sb(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
 int dequant_gemv_q5sb(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
 int dequant_gemv_q6sb(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
+int dequant_gemv_q4g16(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
+int dequant_gemv_q4g64(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
+int dequant_gemv_q4g128(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
 
 /* Generic form: y_f32 != 0 writes fp32 y (4-byte aligned) instead of fp16. */
 int qg_gemv(int fmt, const void *w, const uint16_t *x, void *y, int y_f32, int64_t n, int64_t k, void *stream);
@@ -178,6 +190,12 @@ int dequant_gemm_q3sb(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y
 int dequant_gemm_q5sb(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
                       int64_t m, int64_t n, int64_t k, void *stream);
 int dequant_gemm_q6sb(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
+                      int64_t m, int64_t n, int64_t k, void *stream);
+int dequant_gemm_q4g16(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
+                      int64_t m, int64_t n, int64_t k, void *stream);
+int dequant_gemm_q4g64(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
+                      int64_t m, int64_t n, int64_t k, void *stream);
+int dequant_gemm_q4g128(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
                       int64_t m, int64_t n, int64_t k, void *stream);
 /* Generic form; y_f32 != 0 writes fp32 Y (4-byte aligned). */
 int qg_gemm(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int64_t ldy, int y_f32,
@@ -239,6 +257,9 @@ int dequantize_q2sb(const void *w, float *w_out, uint8_t *codes_out, int64_t n, 
 int dequantize_q3sb(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 int dequantize_q5sb(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 int dequantize_q6sb(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
+int dequantize_q4g16(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
+int dequantize_q4g64(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
+int dequantize_q4g128(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 int qg_dequantize(int fmt, const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 
 /* ---- measurement (device) -----------------------------------------------------------------

@@ -10,8 +10,8 @@ from oracle import superblock as sb
 def oracle_decode(fmt, w):
     """Oracle's own quantization of fp32 W: (logical codes uint8 [n, k], W_hat fp64 [n, k])."""
     n, k = w.shape
-    if fmt == "q4g32":
-        q, s = int4.quantize(w)
+    if fmt in qg.Q4_GROUPS:
+        q, s = int4.quantize(w, qg.Q4_GROUPS[fmt])
         return (q.astype(np.int16) + 8).astype(np.uint8), int4.dequantize(q, s)
     f = sb.quantize(fmt, w)
     return f["codes"].reshape(n, k), sb.dequantize_fields(fmt, f)

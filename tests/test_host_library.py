@@ -1,4 +1,4 @@
-"""CPU tests of libqgemv's host side: symbol exports, bitstreams, the five quantizers against
+"""CPU tests of libqgemv's host side: symbol exports, bitstreams, the eight quantizers against
 the oracle (byte-exact canonical encodings), the device-layout permutation and error codes.
 
 No GPU work is launched here. The oracle and the library share no code: agreement of their
@@ -14,12 +14,12 @@ from oracle import bitstream, int4
 from oracle import superblock as sb
 from workloads import laplace_weights, uniform_codes
 
-FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb"]
+FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb", "q4g16", "q4g64", "q4g128"]
 
 
 def oracle_canonical(fmt, w):
-    if fmt == "q4g32":
-        codes, scales = int4.encode(w)
+    if fmt in qg.Q4_GROUPS:
+        codes, scales = int4.encode(w, qg.Q4_GROUPS[fmt])
         return np.concatenate([codes.reshape(-1), scales.reshape(-1).view(np.uint8)])
     return sb.encode(fmt, w).reshape(-1)
 
@@ -108,7 +108,7 @@ def test_device_layout_q4g32_ragged():
 @pytest.mark.parametrize("fmt", FMTS)
 def test_algorithmic_bytes_match_oracle(fmt):
     n, k = 64, 4096
-    want = int4.algorithmic_bytes(n, k) if fmt == "q4g32" else sb.algorithmic_bytes(fmt, n, k)
+    want = int4.algorithmic_bytes(n, k, qg.Q4_GROUPS[fmt]) if fmt in qg.Q4_GROUPS else sb.algorithmic_bytes(fmt, n, k)
     assert qg.device_layout(fmt, n, k).algorithmic_bytes == want
 
 
@@ -129,7 +129,7 @@ def test_error_codes():
         with pytest.raises(qg.QGError) as e:
             qg.quantize(fmt, big)
         assert e.value.status == -5
-    assert qg.lib.qg_quantize(9, None, 1, 256, 256, None) == -6
+    assert qg.lib.qg_quantize(13, None, 1, 256, 256, None) == -6
     out = ctypes.c_int64()
     assert qg.lib.qg_canonical_bytes(3, 1, 100, ctypes.byref(out)) == -2
     assert qg.lib.qg_canonical_bytes(4, 1, 96, ctypes.byref(out)) == 0 and out.value == 48 + 12
@@ -140,7 +140,7 @@ def test_device_entry_points_validate_without_launching():
     L = qg.lib
     assert L.qg_gemv(3, None, None, None, 0, 4, 100, None) == -2          # k % 256
     assert L.qg_gemv(4, None, None, None, 0, 4, 48, None) == -2           # k % 32
-    assert L.qg_gemv(7, None, None, None, 0, 4, 256, None) == -6          # format
+    assert L.qg_gemv(13, None, None, None, 0, 4, 256, None) == -6          # format
     assert L.qg_gemv(3, None, None, None, 0, 0, 256, None) == 0           # n == 0: no-op
     assert L.qg_gemv(3, None, None, None, 0, 4, 256, None) == -1          # null
     assert L.qg_gemv(3, 256, 16, 3, 0, 4, 256, None) == -3                # y misaligned
@@ -159,7 +159,7 @@ def test_device_entry_points_validate_without_launching():
     assert L.qg_gemm(3, 256, 16, 260, 2, 4, 0, 2, 4, 256, None) == -3     # ldx % 8
     assert L.qg_gemm(3, None, 16, 256, 2, 4, 0, 2, 4, 256, None) == -1    # null w
     assert L.qg_gemm(5, 256, 16, 256, 2, 4, 0, 2, 4, 100, None) == -2     # k % 256
-    assert L.qg_gemm(8, 256, 16, 256, 2, 4, 0, 2, 4, 256, None) == -6     # format
+    assert L.qg_gemm(13, 256, 16, 256, 2, 4, 0, 2, 4, 256, None) == -6     # format
     assert L.dequant_gemm_q6sb(256, 16, 256, 3, 4, 2, 4, 256, None) == -3  # Y misaligned
 
 
@@ -189,7 +189,7 @@ def test_grouped_entry_point_validates_every_matrix_first():
     assert call(3, **ok, m=2, ldx=[256, 500]) == -2                       # ldx < k
     assert call(3, **ok, m=2, ldy=[4, 7]) == -2                           # ldy < n
     assert call(3, **ok, m=2, ldx=[260, 512]) == -3                       # ldx % 8
-    assert call(7, **ok) == -6                                            # format
+    assert call(13, **ok) == -6                                            # format
     assert call(3, [256] * 9, [16] * 9, [2] * 9, [4] * 9, [256] * 9) == -2   # more than 8
     assert call(3, **ok, m=0) == 0                                        # m == 0: no-op
     assert call(3, **{**ok, "ns": [0, 0]}) == 0                           # n == 0: no-op
@@ -205,7 +205,7 @@ def test_act_order_entry_point_validates_without_launching():
     assert L.qg_gemm_act_order(3, 256, 16, 256, 32, 2, 4, 0, 9, 4, 256, None) == -2      # m > 8
     assert L.qg_gemm_act_order(3, 256, 16, 256, 32, 2, 4, 0, 1, 4, 100, None) == -2      # k % 256
     assert L.qg_gemm_act_order(3, 256, 16, 128, 32, 2, 4, 0, 2, 4, 256, None) == -2      # ldx < k
-    assert L.qg_gemm_act_order(9, 256, 16, 256, 32, 2, 4, 0, 1, 4, 256, None) == -6      # format
+    assert L.qg_gemm_act_order(13, 256, 16, 256, 32, 2, 4, 0, 1, 4, 256, None) == -6      # format
     assert L.qg_gemm_act_order(3, 256, 16, 256, 32, 2, 4, 0, 0, 4, 256, None) == 0       # m == 0
 
 
