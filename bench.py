@@ -18,7 +18,8 @@ timed ("single_launch"): at ~1 us of streaming it is bound by launch cadence, no
 graph-timed): INT4 group-32 4096^2, the 7B-like layer set per super-block format (all seven
 matrices in one grouped launch, and in the launches a decode step's data dependencies
 allow), the 70B-like layer set at batch 1, 2, 4 and 8 (one launch per matrix, and one
-grouped launch), act-order INT4 on the 70B-like set, the 8-bit KV-cache codec on the
+grouped launch), INT4 with groups of 16, 32, 64 and 128 and act-order INT4 on the 70B-like
+set, the 8-bit KV-cache codec on the
 7B-like cache, and the 512-row prefill GEMM (TFLOP/s and fraction of the 2.5 PFLOP/s dense
 fp16 MFMA peak).
 
@@ -266,6 +267,15 @@ def extra_configs(qg, dev):
             out[f"{fmt}_70b_layer_set_m{m}"] = {**_rate(alg, us), "TFLOPs": round(flops / us / 1e6, 2),
                                                 "one_launch": _rate(alg2, us2)}
             log(f"[bench] {fmt} 70B layer set m={m}: {out[f'{fmt}_70b_layer_set_m{m}']}")
+        del cs
+    del w70
+    # INT4 group sizes (16, 32, 64, 128) on the 70B-like set at batch 1, one launch per matrix
+    w70 = [WORKLOADS["q3sb_70b_layer_set_m1"].weights(i) for i in range(3)]
+    for fmt in ("q4g16", "q4g32", "q4g64", "q4g128"):
+        cs = [(qg.quantize(fmt, w), w.shape[0], w.shape[1]) for w in w70]
+        alg, us = measure_set(qg, fmt, cs, 1, dev, [("single", [0]), ("single", [1]), ("single", [2])], rounds=12)
+        out[f"{fmt}_70b_layer_set_m1"] = {**_rate(alg, us), "bytes_per_set": alg}
+        log(f"[bench] {fmt} 70B layer set m=1: {out[f'{fmt}_70b_layer_set_m1']}")
         del cs
     del w70
     # act-order INT4 (GPTQ-style column permutation, the gather fused into the kernel) on the

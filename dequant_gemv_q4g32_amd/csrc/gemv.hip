@@ -155,30 +155,30 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
     // (a separate instantiation: the gather's registers at the branch made the register
     // allocator spill the kernels with 4 and 8 activation rows)
     if constexpr (PERM) {
-      // one pair of stored columns at a time (two indices, two gathered halves per row), so
-      // that the gather adds only a few registers to the activation registers it fills
       const rsrc_t pr = make_rsrc(a.perm, (uint32_t)(a.k * 4));
 #pragma unroll
-      for (int t = 0; t < NP; ++t) {
-        uint32_t off = 4u * (uint32_t)(U::pidx(h, 4 * (t >> 2), S) + (t & 3));
+      for (int i = 0; i < NP / 4; ++i) {
+        uint32_t off = 4u * (uint32_t)U::pidx(h, 4 * i, S);
         bool keepx = true;
         if (F == 4 && half && off >= 64) { off -= 64; keepx = false; }
-        const uint32_t kb = (uint32_t)(u * kUnit) + off / 2;   // the pair's first stored column
-        const u32x2 ix = bldx2<0>(pr, kb * 4, 0);
+        const uint32_t kb = (uint32_t)(u * kUnit) + off / 2;   // first of the 8 stored columns
+        const u32x4 i0 = bld4c(pr, kb * 4, 0), i1 = bld4c(pr, kb * 4 + 16, 0);
+        const uint32_t idx[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
 #pragma unroll
         for (int mm = 0; mm < M; ++mm) {
           const bool live = mm < a.m && keepx;
           const int64_t row = mm < a.m ? mm : 0;
-          uint32_t lo, hi;
+          uint32_t hv[8];
           if (xl) {
-            lo = ix.x < (uint32_t)a.k ? xl[row * a.k + ix.x] : 0u;
-            hi = ix.y < (uint32_t)a.k ? xl[row * a.k + ix.y] : 0u;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) hv[j] = idx[j] < (uint32_t)a.k ? xl[row * a.k + idx[j]] : 0u;
           } else {
             const rsrc_t xr = make_rsrc(x + row * a.ldx, (uint32_t)(a.k * 2));
-            lo = bldh(xr, ix.x * 2, 0);
-            hi = bldh(xr, ix.y * 2, 0);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) hv[j] = bldh(xr, idx[j] * 2, 0);
           }
-          xp[mm][t] = live ? (lo | (hi << 16)) : 0u;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) xp[mm][4 * i + r] = live ? (hv[2 * r] | (hv[2 * r + 1] << 16)) : 0u;
         }
       }
     } else {
