@@ -119,3 +119,80 @@ def decode(codes: np.ndarray, scales: np.ndarray, k: int) -> np.ndarray:
 def algorithmic_bytes(n: int, k: int, group: int = GROUP) -> int:
     """group/2 bytes of codes + 4 bytes of fp32 scale per group."""
     return n * (k // group) * (group // 2 + 4)
+
+
+# ---- asymmetric INT4, groups of 32 ("q4a32") -----------------------------------------------
+#
+# Source: "二三五六位量化" page, section 2.1 (linear quantization q = round(x / s) + z,
+# x = s (q - z): symmetric sets z = 0, asymmetric keeps the zero point z, which matters more the
+# fewer levels there are) and DBHOO-CIM page, section 5.1 (a layer whose largest weights stand
+# out from the rest may need asymmetric quantization instead of the symmetric grid).
+#
+# Readings (the pages give the formula, not the range rule or the storage):
+#   * the group range includes zero: lo = min(0, min w), hi = max(0, max w), so that a zero
+#     weight decodes to exactly zero; s = max((hi - lo) / 15, 1e-12); z = clamp(rint(-lo / s),
+#     0, 15); q = clamp(rint(w / s) + z, 0, 15); w_hat = s * (q - z). All in fp32 with rint
+#     half-to-even, as the symmetric INT4 quantizer computes;
+#   * storage: the unsigned codes q (two per byte, first weight in the low nibble), fp32
+#     scales [n][k/32] and uint8 zero points [n][k/32]: 21 bytes per group (5.25 bpw);
+#   * K a multiple of 64 (whole lane units).
+# Error: within s/2 inside the grid; the rounding of z moves the grid by at most s/2, so a
+# group's extreme weight can be clipped by up to s/2 more (within s).
+
+ASYM_QMAX = 15
+
+
+def quantize_asym(w: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarray]:
+    """fp32 W [n, k] (k % 64 == 0) -> (q uint8 [n, k] in [0, 15], scale fp32 [n, k/32],
+    zero point uint8 [n, k/32])."""
+    w = np.asarray(w)
+    if w.dtype != np.float32 or w.ndim != 2:
+        raise TypeError("W must be a 2-D float32 array")
+    n, k = w.shape
+    if k % 64:
+        raise ValueError("K must be a multiple of 64")
+    if not np.all(np.isfinite(w)):
+        raise ValueError("non-finite weight")
+    g = w.reshape(n, k // GROUP, GROUP)
+    lo = np.minimum(np.float32(0), g.min(axis=2) if k else np.zeros((n, 0), np.float32)).astype(np.float32)
+    hi = np.maximum(np.float32(0), g.max(axis=2) if k else np.zeros((n, 0), np.float32)).astype(np.float32)
+    s = ((hi - lo) / np.float32(ASYM_QMAX)).astype(np.float32)
+    s = np.maximum(s, SCALE_FLOOR)
+    z = np.clip(np.rint((-lo / s).astype(np.float32)), 0, ASYM_QMAX).astype(np.uint8)
+    r = (g / s[..., None]).astype(np.float32)
+    q = np.clip(np.rint(r) + z[..., None].astype(np.float32), 0, ASYM_QMAX).astype(np.uint8)
+    return q.reshape(n, k), s, z
+
+
+def quantize_asym_group_scalar(w32):
+    """One group, element by element (reference for the vectorized quantizer)."""
+    vals = [np.float32(v) for v in w32]
+    lo, hi = np.float32(0.0), np.float32(0.0)
+    for v in vals:
+        lo = min(lo, v)
+        hi = max(hi, v)
+    s = np.float32(np.float32(hi - lo) / np.float32(ASYM_QMAX))
+    if s < SCALE_FLOOR:
+        s = SCALE_FLOOR
+    z = int(min(ASYM_QMAX, max(0, np.rint(np.float32(-lo / s)))))
+    q = [int(min(ASYM_QMAX, max(0, int(np.rint(np.float32(v / s))) + z))) for v in vals]
+    return q, s, z
+
+
+def dequantize_asym(q: np.ndarray, s: np.ndarray, z: np.ndarray) -> np.ndarray:
+    """W_hat = s * (q - z) in fp64 (exact)."""
+    n, k = q.shape
+    ss = np.repeat(s.astype(np.float64), GROUP, axis=1)
+    zz = np.repeat(z.astype(np.float64), GROUP, axis=1)
+    return (q.astype(np.float64) - zz) * ss
+
+
+def encode_asym(w: np.ndarray):
+    """fp32 W -> canonical (codes uint8 [n, k/2], scales fp32 [n, k/32], zeros uint8 [n, k/32])."""
+    q, s, z = quantize_asym(w)
+    return bitstream.pack_bits(q, 4), s, z
+
+
+def algorithmic_bytes_asym(n: int, k: int) -> int:
+    """16 code bytes, a 4-byte scale and a 1-byte zero point per group of 32."""
+    return n * (k // GROUP) * (16 + 4 + 1)
