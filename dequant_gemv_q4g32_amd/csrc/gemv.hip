@@ -343,6 +343,22 @@ __device__ void decode_unit(const GemvArgs &a, const uint8_t *w, int64_t r, int6
     }
     return;
   }
+  if constexpr (F == kQ4A32) {
+    const uint8_t *pc = w + a.poff[0] + r * a.prb[0];
+    const uint8_t *ps = w + a.poff[1] + r * a.prb[1];
+    const uint32_t zz = ldh(w + a.poff[2] + r * a.prb[2] + u * 2);
+    for (int i = 0; i < 8; ++i) {
+      uint32_t v = ld1(pc + split_off(a.units, u, i >> 2, 16) + 4 * (i & 3));
+      for (int e = 0; e < 8; ++e) c[8 * i + e] = (v >> (4 * ((e >> 1) + 4 * (e & 1)))) & 15u;
+    }
+    for (int i = 0; i < nvalid; ++i) {
+      const int gi = i >> 5;                       // group of the unit
+      const int z = (int)((zz >> (8 * gi)) & 0xFFu);
+      codes[i] = c[i];
+      vals[i] = (float)((int)c[i] - z) * __builtin_bit_cast(float, ld1(ps + split_off(a.units, u, gi, 4)));
+    }
+    return;
+  }
   if (F == 2) {
     const uint8_t *pc = w + a.poff[0] + r * a.prb[0] + u * 16;
     uint32_t d[4];
@@ -698,6 +714,7 @@ int launch_mv_fmt(int fmt, GemvArgs a, int64_t count, hipStream_t s) {
     case 7: return launch_mv_f<7>(a, count, s);
     case 8: return launch_mv_f<8>(a, count, s);
     case 9: return launch_mv_f<9>(a, count, s);
+    case 10: return launch_mv_f<10>(a, count, s);
   }
   return QG_ERR_FORMAT;
 }
@@ -712,6 +729,7 @@ int launch_mv_group_fmt(int fmt, GemvGroup &G, hipStream_t s) {
     case 7: return launch_mv_group_f<7>(G, s);
     case 8: return launch_mv_group_f<8>(G, s);
     case 9: return launch_mv_group_f<9>(G, s);
+    case 10: return launch_mv_group_f<10>(G, s);
   }
   return QG_ERR_FORMAT;
 }
@@ -877,6 +895,7 @@ int dequant_gemv_q6sb(const void *w, const uint16_t *x, uint16_t *y, int64_t n, 
 int dequant_gemv_q4g16(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(7, w, x, y, 0, n, k, s); }
 int dequant_gemv_q4g64(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(8, w, x, y, 0, n, k, s); }
 int dequant_gemv_q4g128(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(9, w, x, y, 0, n, k, s); }
+int dequant_gemv_q4a32(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(10, w, x, y, 0, n, k, s); }
 int dequant_gemm_q4g32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m, int64_t n,
                        int64_t k, void *s) {
   return qg_gemm(4, w, X, ldx, Y, ldy, 0, m, n, k, s);
@@ -909,6 +928,10 @@ int dequant_gemm_q4g128(const void *w, const uint16_t *X, int64_t ldx, uint16_t 
                       int64_t k, void *s) {
   return qg_gemm(9, w, X, ldx, Y, ldy, 0, m, n, k, s);
 }
+int dequant_gemm_q4a32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m, int64_t n,
+                       int64_t k, void *s) {
+  return qg_gemm(10, w, X, ldx, Y, ldy, 0, m, n, k, s);
+}
 
 int qg_dequantize(int fmt, const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream) {
   if (!fmt_valid(fmt)) return QG_ERR_FORMAT;
@@ -931,6 +954,7 @@ int qg_dequantize(int fmt, const void *w, float *w_out, uint8_t *codes_out, int6
     case 7: return launch(dequant_kernel<7>, grid, block, 0, s, a, w_out, codes_out);
     case 8: return launch(dequant_kernel<8>, grid, block, 0, s, a, w_out, codes_out);
     case 9: return launch(dequant_kernel<9>, grid, block, 0, s, a, w_out, codes_out);
+    case 10: return launch(dequant_kernel<10>, grid, block, 0, s, a, w_out, codes_out);
   }
   return QG_ERR_FORMAT;
 }
@@ -955,5 +979,6 @@ int dequantize_q6sb(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, v
 int dequantize_q4g16(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(7, w, o, c, n, k, s); }
 int dequantize_q4g64(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(8, w, o, c, n, k, s); }
 int dequantize_q4g128(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(9, w, o, c, n, k, s); }
+int dequantize_q4a32(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(10, w, o, c, n, k, s); }
 
 }  // extern "C"

@@ -122,6 +122,37 @@ int quantize_row_q4(const float *w, int64_t k, int G, uint8_t *codes, float *sca
   return QG_OK;
 }
 
+// One asymmetric INT4 row (groups of 32): unsigned codes (k/2 bytes, canonical nibble order),
+// fp32 scales and uint8 zero points (k/32 each). The group's range is widened to include 0:
+// lo = min(0, min w), hi = max(0, max w), s = max((hi - lo) / 15, 1e-12),
+// z = clamp(rint(-lo / s), 0, 15), c = clamp(rint(w / s) + z, 0, 15); fp32 throughout.
+int quantize_row_q4a(const float *w, int64_t k, uint8_t *codes, float *scales, uint8_t *zeros) {
+  for (int64_t g = 0; g < k / 32; ++g) {
+    const float *v = w + g * 32;
+    float lo = 0.0f, hi = 0.0f;
+    for (int i = 0; i < 32; ++i) {
+      if (!std::isfinite(v[i])) return QG_ERR_NONFINITE;
+      if (v[i] < lo) lo = v[i];
+      if (v[i] > hi) hi = v[i];
+    }
+    float scale = (hi - lo) / 15.0f;
+    if (scale < 1e-12f) scale = 1e-12f;
+    float zf = std::nearbyint(-lo / scale);
+    zf = std::min(15.0f, std::max(0.0f, zf));
+    scales[g] = scale;
+    zeros[g] = (uint8_t)zf;
+    for (int i = 0; i < 32; i += 2) {
+      int u[2];
+      for (int t = 0; t < 2; ++t) {
+        float q = std::nearbyint(v[i + t] / scale) + zf;
+        u[t] = (int)std::min(15.0f, std::max(0.0f, q));
+      }
+      codes[(g * 32 + i) / 2] = (uint8_t)(u[0] | (u[1] << 4));
+    }
+  }
+  return QG_OK;
+}
+
 // One super-block: fp32 w[256] -> canonical record.
 int quantize_block_sb(const SB &s, int fmt, const float *w, uint8_t *rec) {
   const int sub = s.sub(), nsub = s.nsub, cmax = s.cmax();
@@ -266,7 +297,7 @@ inline uint32_t getbit(const uint32_t *w, int pos) { return (w[pos >> 5] >> (pos
 // at unit position k, for the code planes of each format. For q5sb/q6sb this is the low
 // nibble (b < 4) in the nibble dwords; high bits are placed by hi_pos().
 int code_pos(int fmt, int k, int b) {
-  if (q4_group(fmt) || fmt == 5 || fmt == 6) {        // nibble dwords
+  if (q4_group(fmt) || fmt == kQ4A32 || fmt == 5 || fmt == 6) {        // nibble dwords
     int i = k >> 3, e = k & 7;
     return i * 32 + q4_slot(e) * 4 + b;
   }
@@ -305,13 +336,15 @@ struct Planes {
 void row_to_device(int fmt, const uint8_t *canon, int64_t k, int64_t r, int64_t n, Planes P) {
   const int64_t units = (k + kUnit - 1) / kUnit;
   std::vector<uint8_t> codes((size_t)(units * kUnit), 0);
-  if (q4_group(fmt)) {
-    const int G = q4_group(fmt);
+  if (q4_group(fmt) || fmt == kQ4A32) {
+    const int G = fmt == kQ4A32 ? 32 : q4_group(fmt);
     const uint8_t *cr = canon + r * (k / 2);
     for (int64_t i = 0; i < k; ++i) codes[(size_t)i] = (cr[i >> 1] >> (4 * (i & 1))) & 15;
     const uint8_t *sr = canon + n * (k / 2) + r * (k / G) * 4;
     uint8_t *ds = P.p[1] + r * P.rb[1];
     for (int64_t g = 0; g < k / G; ++g) std::memcpy(ds + q4_scale_off(G, units, g), sr + g * 4, 4);
+    if (fmt == kQ4A32)                                   // zero points, in group order
+      std::memcpy(P.p[2] + r * P.rb[2], canon + n * (k / 2) + n * (k / 32) * 4 + r * (k / 32), (size_t)(k / 32));
     uint8_t *dst = P.p[0] + r * P.rb[0];
     for (int64_t u = 0; u < units; ++u) {
       uint32_t wv[8] = {0};
@@ -399,7 +432,7 @@ void row_from_device(int fmt, const uint8_t *const *pl, const int64_t *rb, int64
   std::vector<uint8_t> codes((size_t)(units * kUnit), 0);
   for (int64_t u = 0; u < units; ++u) {
     uint32_t a[8] = {0}, hb[4] = {0};
-    if (q4_group(fmt)) {
+    if (q4_group(fmt) || fmt == kQ4A32) {
       std::memcpy(a, pl[0] + r * rb[0] + split_off(units, u, 0, 16), 16);
       if (k / 2 - u * 32 > 16) std::memcpy(a + 4, pl[0] + r * rb[0] + split_off(units, u, 1, 16), 16);
     } else if (fmt == 2) {
@@ -423,12 +456,14 @@ void row_from_device(int fmt, const uint8_t *const *pl, const int64_t *rb, int64
       codes[(size_t)(u * kUnit + kk)] = (uint8_t)cv;
     }
   }
-  if (q4_group(fmt)) {
-    const int G = q4_group(fmt);
+  if (q4_group(fmt) || fmt == kQ4A32) {
+    const int G = fmt == kQ4A32 ? 32 : q4_group(fmt);
     uint8_t *cr = canon + r * (k / 2);
     for (int64_t i = 0; i < k; i += 2) cr[i / 2] = (uint8_t)(codes[(size_t)i] | (codes[(size_t)i + 1] << 4));
     for (int64_t g = 0; g < k / G; ++g)
       std::memcpy(canon + n * (k / 2) + r * (k / G) * 4 + g * 4, pl[1] + r * rb[1] + q4_scale_off(G, units, g), 4);
+    if (fmt == kQ4A32)
+      std::memcpy(canon + n * (k / 2) + n * (k / 32) * 4 + r * (k / 32), pl[2] + r * rb[2], (size_t)(k / 32));
     return;
   }
   SB s;
@@ -503,7 +538,7 @@ const char *qg_strerror(int status) {
   switch (status) {
     case QG_OK: return "ok";
     case QG_ERR_NULL: return "a required pointer is NULL";
-    case QG_ERR_SHAPE: return "n, k or m out of range (k must be a multiple of 256 for the super-block formats, of 32 for q4g32, 64 for q4g16 and q4g64, 128 for q4g128)";
+    case QG_ERR_SHAPE: return "n, k or m out of range (k must be a multiple of 256 for the super-block formats, of 32 for q4g32, 64 for q4g16, q4g64 and q4a32, 128 for q4g128)";
     case QG_ERR_ALIGN: return "misaligned device pointer or leading dimension";
     case QG_ERR_NONFINITE: return "a weight is NaN or infinite";
     case QG_ERR_RANGE: return "a super-block scale does not fit fp16, or a code does not fit its width";
@@ -519,6 +554,7 @@ int qg_canonical_bytes(int fmt, int64_t n, int64_t k, int64_t *bytes) {
   if (!fmt_valid(fmt)) return QG_ERR_FORMAT;
   if (!shape_ok(fmt, n, k)) return QG_ERR_SHAPE;
   if (q4_group(fmt)) { *bytes = n * (k / 2) + n * (k / q4_group(fmt)) * 4; return QG_OK; }
+  if (fmt == kQ4A32) { *bytes = n * (k / 2) + n * (k / 32) * 5; return QG_OK; }
   SB s;
   sb_spec(fmt, &s);
   *bytes = n * (k / kQK) * s.rec;
@@ -568,6 +604,18 @@ int qg_quantize(int fmt, const float *w, int64_t n, int64_t k, int64_t ldw, uint
       return (int)QG_OK;
     });
   }
+  if (fmt == kQ4A32) {
+    uint8_t *codes = canonical;
+    float *scales = reinterpret_cast<float *>(canonical + n * (k / 2));
+    uint8_t *zeros = canonical + n * (k / 2) + n * (k / 32) * 4;
+    return parallel_rows(n, k, [&](int64_t r0, int64_t r1) {
+      for (int64_t r = r0; r < r1; ++r) {
+        int st = quantize_row_q4a(w + r * ldw, k, codes + r * (k / 2), scales + r * (k / 32), zeros + r * (k / 32));
+        if (st != QG_OK) return st;
+      }
+      return (int)QG_OK;
+    });
+  }
   SB s;
   sb_spec(fmt, &s);
   const int64_t S = k / kQK;
@@ -585,6 +633,7 @@ int quantize_q4g32(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c
 int quantize_q4g16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(7, w, n, k, ldw, c); }
 int quantize_q4g64(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(8, w, n, k, ldw, c); }
 int quantize_q4g128(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(9, w, n, k, ldw, c); }
+int quantize_q4a32(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(10, w, n, k, ldw, c); }
 int quantize_q2sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(2, w, n, k, ldw, c); }
 int quantize_q3sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(3, w, n, k, ldw, c); }
 int quantize_q5sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(5, w, n, k, ldw, c); }

@@ -210,6 +210,102 @@ template <> struct Unit<7> : UnitQ4<16> {};
 template <> struct Unit<8> : UnitQ4<64> {};
 template <> struct Unit<9> : UnitQ4<128> {};
 
+// ---- INT4 asymmetric, groups of 32 (q4a32): the q4g32 code and scale planes with unsigned
+// codes c, and a plane of uint8 zero points z (2 bytes per unit, group order):
+// w_hat = s * (c - z), so a group's sum of w_hat * x is s * (sum c x - z * sum x). With S = 2
+// a lane owns one group (half h of the unit).
+template <> struct Unit<kQ4A32> {
+  static constexpr int NK = 4;
+  __host__ __device__ static constexpr int NKS(int S) { return NK / S; }
+  struct Raw { u32x4 c0, c1; float s[2]; uint32_t z; };
+  __device__ static int pidx(int h, int p, int S) { return S == 1 ? p : 16 * h + p; }
+  __device__ static void offsets(int64_t u, uint32_t *off) {
+    off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 4); off[2] = (uint32_t)(u * 2);
+  }
+  // S = 2: the lane's own group only, into c0 and s[0]
+  template <int AUX = kNT, int S = 1> __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
+    const uint32_t r0 = L.row(0, r), r1 = L.row(1, r);
+    if constexpr (S == 2) {
+      q.c0 = bldx4<AUX>(L.rs[0], L.off[0] + (L.h ? L.half16 : 0u), r0);
+      q.s[0] = __builtin_bit_cast(float, bld1(L.rs[1], L.off[1] + (L.h ? L.half4 : 0u), r1));
+    } else {
+      q.c0 = bldx4<AUX>(L.rs[0], L.off[0], r0);
+      q.c1 = bldx4<AUX>(L.rs[0], L.off[0] + L.half16, r0);
+      q.s[0] = __builtin_bit_cast(float, bld1(L.rs[1], L.off[1], r1));
+      q.s[1] = __builtin_bit_cast(float, bld1(L.rs[1], L.off[1] + L.half4, r1));
+    }
+    q.z = bldh(L.rs[2], L.off[2], L.row(2, r));
+  }
+  // kc layout (S = 1): [start g0, start g1, sum x g0, sum x g1]; (S = 2): [start, sum x]
+  template <int S> __device__ static void prep(uint32_t *xp, float *kc) {
+#pragma unroll
+    for (int g = 0; g < 2 / S; ++g) {
+      float x1 = 0.f, x16 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        x1 = dot2(xp[16 * g + 4 * i + 0], kOnes, x1);
+        x1 = dot2(xp[16 * g + 4 * i + 2], kOnes, x1);
+        x16 = dot2(xp[16 * g + 4 * i + 1], kOnes, x16);
+        x16 = dot2(xp[16 * g + 4 * i + 3], kOnes, x16);
+      }
+      kc[g] = -(1024.0f * x1 + 64.0f * x16);   // A1 + A16 / 16 = sum c x, A1 starting here
+      kc[2 / S + g] = x1 + x16;
+    }
+  }
+  template <int M, int S>
+  __device__ static void dot(const Raw &q, int h, const uint32_t (*xp)[32 / S], const float (*kc)[NKS(S)], float *out) {
+    const uint32_t d[8] = {q.c0.x, q.c0.y, q.c0.z, q.c0.w, S == 1 ? q.c1.x : 0u, S == 1 ? q.c1.y : 0u,
+                           S == 1 ? q.c1.z : 0u, S == 1 ? q.c1.w : 0u};
+#pragma unroll
+    for (int g = 0; g < 2 / S; ++g) {
+      float a1[M], a16[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) { a1[m] = kc[m][g]; a16[m] = 0.f; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t v = d[4 * g + i], v8 = v >> 8;
+        const uint32_t p0 = pick(v, QG_SMASK(0x000F000Fu)), p1 = pick(v, QG_SMASK(0x00F000F0u));
+        const uint32_t p2 = pick(v8, QG_SMASK(0x000F000Fu)), p3 = pick(v8, QG_SMASK(0x00F000F0u));
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          a1[m] = dot2(p0, xp[m][16 * g + 4 * i + 0], a1[m]);
+          a16[m] = dot2(p1, xp[m][16 * g + 4 * i + 1], a16[m]);
+          a1[m] = dot2(p2, xp[m][16 * g + 4 * i + 2], a1[m]);
+          a16[m] = dot2(p3, xp[m][16 * g + 4 * i + 3], a16[m]);
+        }
+      }
+      // s * (sum c x - z * sum x), the difference taken before the scale: a code equal to the
+      // zero point then contributes exactly 0, as its w_hat does
+      const float scale = q.s[g];
+      const float zf = (float)((q.z >> (8 * (S == 1 ? g : h))) & 0xFFu);
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        out[m] = __builtin_fmaf(scale, __builtin_fmaf(-zf, kc[m][2 / S + g], __builtin_fmaf(a16[m], 0.0625f, a1[m])), out[m]);
+    }
+  }
+  // fp16 w_hat of the 16 pairs of half h (group h); S = 2: q holds only that group
+  template <int S = 1> __device__ static void wide(const Raw &q, int h, uint32_t *out) {
+    const u32x4 c0 = q.c0, c1 = S == 1 ? q.c1 : q.c0;
+    const uint32_t dw[4] = {sel(S == 1 && h, c1.x, c0.x), sel(S == 1 && h, c1.y, c0.y), sel(S == 1 && h, c1.z, c0.z),
+                            sel(S == 1 && h, c1.w, c0.w)};
+    const float sc = S == 1 ? __builtin_bit_cast(float, sel(h, __builtin_bit_cast(uint32_t, q.s[1]),
+                                                            __builtin_bit_cast(uint32_t, q.s[0])))
+                            : q.s[0];
+    const float zf = (float)((q.z >> (8 * h)) & 0xFFu);
+    // (P - (1024 + p z)) is p (c - z) exactly; times s / p rounded to fp16
+    const _Float16 m1 = (_Float16)sc, m16 = (_Float16)(sc * 0.0625f);
+    const _Float16 o1 = (_Float16)(-1024.0f - zf), o16 = (_Float16)(-1024.0f - 16.0f * zf);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t v = dw[i], v8 = v >> 8;
+      out[4 * i + 0] = sym_pair(pick(v, QG_SMASK(0x000F000Fu)), o1, m1);
+      out[4 * i + 1] = sym_pair(pick(v, QG_SMASK(0x00F000F0u)), o16, m16);
+      out[4 * i + 2] = sym_pair(pick(v8, QG_SMASK(0x000F000Fu)), o1, m1);
+      out[4 * i + 3] = sym_pair(pick(v8, QG_SMASK(0x00F000F0u)), o16, m16);
+    }
+  }
+};
+
 // ---- 2-bit super-block: a unit is a quarter super-block (4 sub-blocks of 16). Sub-block j
 // sits at class 4^j in every dword; with S = 2 lane half h owns dwords 2h, 2h+1, i.e. pairs
 // r = 4h..4h+3 of every sub-block.

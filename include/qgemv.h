@@ -10,6 +10,13 @@
  *   QG_Q4G16, QG_Q4G64, QG_Q4G128  the same INT4 code with groups of 16, 64 or 128 weights
  *             (6.0, 4.5, 4.25 bpw; DBHOO-CIM page section 5.1 advises groups of 16 against
  *             outlier weights). k must be a multiple of 64 (of 128 for QG_Q4G128).
+ *   QG_Q4A32  INT4 asymmetric, groups of 32, fp32 scale s and uint8 zero point z per group
+ *             ("二三五六位量化" page section 2.1's x = s (q - z); DBHOO-CIM page section 5.1
+ *             keeps asymmetric quantization for layers the symmetric grid serves badly):
+ *             lo = min(0, min w), hi = max(0, max w), s = max((hi - lo) / 15, 1e-12),
+ *             z = clamp(rint(-lo / s), 0, 15), c = clamp(rint(w / s) + z, 0, 15) in fp32,
+ *             w_hat = s * (c - z); 16 B of codes + 4 B of scale + 1 B of zero point per group
+ *             (5.25 bpw). k must be a multiple of 64.
  *   QG_Q2SB   256-weight super-block, 16 sub-blocks of 16, 2-bit codes c, 4-bit sub-scale sc
  *             and 4-bit sub-min m, fp16 d and dmin: w_hat = d*sc*c - dmin*m  (84 B, 2.625 bpw).
  *   QG_Q3SB   16 sub-blocks of 16, 3-bit codes, 6-bit sc, fp16 d: w_hat = d*sc*(c - 4)
@@ -30,7 +37,8 @@
  *
  * Two encodings of a quantized matrix W [n][k] (W is out_features x in_features):
  *   canonical  the pages' interchange layout. q4g32: codes [n][k/2] (byte = u[2j] | u[2j+1] << 4
- *              with u = q + 8) followed by fp32 scales [n][k/32] (q4gG: [n][k/G]). Super-block formats: records
+ *              with u = q + 8) followed by fp32 scales [n][k/32] (q4gG: [n][k/G]). q4a32: codes
+ *              [n][k/2] (u = c), fp32 scales [n][k/32], uint8 zero points [n][k/32]. Super-block formats: records
  *              [n][k/256] of 84/110/176/210 bytes; fields in the byte table's column order
  *              (codes [, high-bit plane], sub-scales, d [, dmin]); every bit field is a
  *              little-endian bitstream (code i at bits [b*i, b*i + b), section 2.2's unpack3
@@ -71,13 +79,14 @@ typedef enum qg_format {
   QG_Q6SB = 6,
   QG_Q4G16 = 7,
   QG_Q4G64 = 8,
-  QG_Q4G128 = 9
+  QG_Q4G128 = 9,
+  QG_Q4A32 = 10
 } qg_format;
 
 typedef enum qg_status {
   QG_OK = 0,
   QG_ERR_NULL = -1,      /* a required pointer is NULL                                      */
-  QG_ERR_SHAPE = -2,     /* n, k or m out of range (k % 256 for super-blocks, k % 32 q4g32)  */
+  QG_ERR_SHAPE = -2,     /* n, k or m out of range (k % 256 super-blocks, % 32 q4g32, ...)   */
   QG_ERR_ALIGN = -3,     /* a device pointer or leading dimension is misaligned              */
   QG_ERR_NONFINITE = -4, /* a weight is NaN or infinite                                     */
   QG_ERR_RANGE = -5,     /* d or dmin does not fit fp16 (section 2.3's overflow warning)     */
@@ -133,6 +142,7 @@ int quantize_q6sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *ca
 int quantize_q4g16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
 int quantize_q4g64(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
 int quantize_q4g128(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
+int quantize_q4a32(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
 
 /* Canonical encoding (host) -> device layout (host buffer of qg_device_layout().total_bytes;
  * padding is zeroed). A pure bit permutation. */
@@ -156,6 +166,7 @@ int dequant_gemv_q6sb(const void *w, const uint16_t *x, uint16_t *y, int64_t n, 
 int dequant_gemv_q4g16(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
 int dequant_gemv_q4g64(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
 int dequant_gemv_q4g128(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
+int dequant_gemv_q4a32(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
 
 /* Generic form: y_f32 != 0 writes fp32 y (4-byte aligned) instead of fp16. */
 int qg_gemv(int fmt, const void *w, const uint16_t *x, void *y, int y_f32, int64_t n, int64_t k, void *stream);
@@ -197,6 +208,8 @@ int dequant_gemm_q4g64(const void *w, const uint16_t *X, int64_t ldx, uint16_t *
                       int64_t m, int64_t n, int64_t k, void *stream);
 int dequant_gemm_q4g128(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
                       int64_t m, int64_t n, int64_t k, void *stream);
+int dequant_gemm_q4a32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
+                       int64_t m, int64_t n, int64_t k, void *stream);
 /* Generic form; y_f32 != 0 writes fp32 Y (4-byte aligned). */
 int qg_gemm(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int64_t ldy, int y_f32,
             int64_t m, int64_t n, int64_t k, void *stream);
@@ -249,9 +262,9 @@ int qg_kv_dequantize(const int8_t *codes, const uint16_t *scales, int64_t rows, 
 
 /* ---- decode to memory (device; for verification, not for inference) ----------------------
  * Writes W_hat as fp32 [n][k] to w_out (if non-NULL) and the integer codes as uint8 [n][k]
- * to codes_out (if non-NULL; q4g32 writes the unsigned nibble u = q + 8). fp32 values are
- * single-rounding products (q*scale, d*sc*(c - o), fma(d*sc, c, -dmin*m)), hence exactly
- * fp32(W_hat). */
+ * to codes_out (if non-NULL; q4g32 writes the unsigned nibble u = q + 8, q4a32 the code c).
+ * fp32 values are single-rounding products (q*scale, (c - z)*s, d*sc*(c - o),
+ * fma(d*sc, c, -dmin*m)), hence exactly fp32(W_hat). */
 int dequantize_q4g32(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 int dequantize_q2sb(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 int dequantize_q3sb(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
@@ -260,6 +273,7 @@ int dequantize_q6sb(const void *w, float *w_out, uint8_t *codes_out, int64_t n, 
 int dequantize_q4g16(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 int dequantize_q4g64(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 int dequantize_q4g128(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
+int dequantize_q4a32(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 int qg_dequantize(int fmt, const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 
 /* ---- measurement (device) -----------------------------------------------------------------

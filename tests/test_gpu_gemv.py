@@ -14,7 +14,7 @@ from workloads import WORKLOADS, activations, laplace_weights
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb", "q4g16", "q4g64", "q4g128"]
+FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb", "q4g16", "q4g64", "q4g128", "q4a32"]
 # (n, k): several tiles, ragged n, K split over 1, 2, 3 and 7 waves
 SHAPES = [(37, 512), (16, 256), (1001, 1024), (64, 4096), (20, 4352), (9, 8192), (33, 11008), (5, 28672)]
 
@@ -158,3 +158,26 @@ def test_full_size_workloads_sampled_rows(name, i):
     y_ref, bound = oracle_y(w_hat, x)
     torch.cuda.synchronize()
     assert_close(y.cpu().float().numpy()[rows][None, :], y_ref, bound, f"{name}[{i}]")
+
+
+def test_q4a32_zero_points_over_their_range():
+    """Asymmetric INT4: groups shifted from all-negative to all-positive, so that the zero
+    points take every value 0..15; decode bit-exact, GEMV (1 and 4 rows) and prefill (64 rows)
+    within the tolerance."""
+    n, k = 48, 2048
+    w = laplace_weights(n, k, 0.01, 404)
+    shift = np.linspace(-0.06, 0.06, n * (k // 32), dtype=np.float32).reshape(n, k // 32)
+    w = (w + np.repeat(shift, 32, axis=1)).astype(np.float32)
+    codes_ref, w_hat = oracle_decode("q4a32", w)
+    from oracle import int4
+    zeros = int4.quantize_asym(w)[2]
+    assert set(np.unique(zeros)) == set(range(16))
+    wd = device_weights("q4a32", w)
+    vals, codes = qg.dequantize("q4a32", wd, n, k)
+    assert np.array_equal(codes.cpu().numpy(), codes_ref)
+    assert np.array_equal(vals.cpu().numpy(), w_hat.astype(np.float32))
+    for m in (1, 4, 64):
+        x = _x(k, 405 + m, m)
+        y_ref, bound = oracle_y(w_hat, x)
+        y = qg.gemm("q4a32", wd, torch.from_numpy(x).cuda(), n, k, out_f32=True)
+        assert_close(y.cpu().numpy(), y_ref, bound, f"q4a32 m={m}")

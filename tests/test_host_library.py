@@ -14,10 +14,13 @@ from oracle import bitstream, int4
 from oracle import superblock as sb
 from workloads import laplace_weights, uniform_codes
 
-FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb", "q4g16", "q4g64", "q4g128"]
+FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb", "q4g16", "q4g64", "q4g128", "q4a32"]
 
 
 def oracle_canonical(fmt, w):
+    if fmt == "q4a32":
+        codes, scales, zeros = int4.encode_asym(w)
+        return np.concatenate([codes.reshape(-1), scales.reshape(-1).view(np.uint8), zeros.reshape(-1)])
     if fmt in qg.Q4_GROUPS:
         codes, scales = int4.encode(w, qg.Q4_GROUPS[fmt])
         return np.concatenate([codes.reshape(-1), scales.reshape(-1).view(np.uint8)])
@@ -108,7 +111,10 @@ def test_device_layout_q4g32_ragged():
 @pytest.mark.parametrize("fmt", FMTS)
 def test_algorithmic_bytes_match_oracle(fmt):
     n, k = 64, 4096
-    want = int4.algorithmic_bytes(n, k, qg.Q4_GROUPS[fmt]) if fmt in qg.Q4_GROUPS else sb.algorithmic_bytes(fmt, n, k)
+    if fmt == "q4a32":
+        want = int4.algorithmic_bytes_asym(n, k)
+    else:
+        want = int4.algorithmic_bytes(n, k, qg.Q4_GROUPS[fmt]) if fmt in qg.Q4_GROUPS else sb.algorithmic_bytes(fmt, n, k)
     assert qg.device_layout(fmt, n, k).algorithmic_bytes == want
 
 
@@ -133,6 +139,8 @@ def test_error_codes():
     out = ctypes.c_int64()
     assert qg.lib.qg_canonical_bytes(3, 1, 100, ctypes.byref(out)) == -2
     assert qg.lib.qg_canonical_bytes(4, 1, 96, ctypes.byref(out)) == 0 and out.value == 48 + 12
+    assert qg.lib.qg_canonical_bytes(10, 2, 128, ctypes.byref(out)) == 0 and out.value == 2 * (64 + 16 + 4)
+    assert qg.lib.qg_canonical_bytes(10, 1, 96, ctypes.byref(out)) == -2
 
 
 def test_device_entry_points_validate_without_launching():
@@ -140,6 +148,7 @@ def test_device_entry_points_validate_without_launching():
     L = qg.lib
     assert L.qg_gemv(3, None, None, None, 0, 4, 100, None) == -2          # k % 256
     assert L.qg_gemv(4, None, None, None, 0, 4, 48, None) == -2           # k % 32
+    assert L.qg_gemv(10, None, None, None, 0, 4, 96, None) == -2          # q4a32: k % 64
     assert L.qg_gemv(13, None, None, None, 0, 4, 256, None) == -6          # format
     assert L.qg_gemv(3, None, None, None, 0, 0, 256, None) == 0           # n == 0: no-op
     assert L.qg_gemv(3, None, None, None, 0, 4, 256, None) == -1          # null
