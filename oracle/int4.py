@@ -196,3 +196,54 @@ def encode_asym(w: np.ndarray):
 def algorithmic_bytes_asym(n: int, k: int) -> int:
     """16 code bytes, a 4-byte scale and a 1-byte zero point per group of 32."""
     return n * (k // GROUP) * (16 + 4 + 1)
+
+
+# ---- INT4 symmetric, groups of 32 with an fp16 scale ("q4g32h") -----------------------------
+#
+# Source: "二三五六位量化" page, section 2.1 (each group of 32 storing its scale in fp16
+# costs 16 bits per 32 weights, 0.5 bpw; the 5- and 6-bit tiers even do with a plain
+# single-level group scale) and the DBHOO-CIM page, sections 2.1 and 3.1 (the INT4 rule).
+#
+# Readings: the INT4 rule with the scale stored as fp16: s32 = max|w| / 8 in fp32, rounded
+# to the nearest fp16 (ties to even); a scale that rounds to 0 is raised to the smallest
+# fp16 subnormal 2^-24 (the fp16 counterpart of the 1e-12 floor); one that overflows fp16
+# is an error. The codes are then taken against the stored scale, q = clamp(rint(w / s),
+# -8, 7) in fp32 with s = float(fp16 scale), so that w_hat = q * s is what was quantized
+# against. 16 + 2 bytes per group (4.5 bpw); K a multiple of 64.
+
+HALF_SCALE_FLOOR = np.float16(2.0 ** -24)
+
+
+def quantize_h(w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """fp32 W [n, k] (k % 64 == 0) -> (q int8 [n, k] in [-8, 7], scale fp16 [n, k/32])."""
+    w = np.asarray(w)
+    if w.dtype != np.float32 or w.ndim != 2:
+        raise TypeError("W must be a 2-D float32 array")
+    n, k = w.shape
+    if k % 64:
+        raise ValueError("K must be a multiple of 64")
+    if not np.all(np.isfinite(w)):
+        raise ValueError("non-finite weight")
+    g = w.reshape(n, k // GROUP, GROUP)
+    amax = np.abs(g).max(axis=2) if k else np.zeros((n, 0), np.float32)
+    s32 = (amax / np.float32(8.0)).astype(np.float32)
+    with np.errstate(over="ignore"):
+        s16 = s32.astype(np.float16)                          # round to nearest even
+    if np.any(np.isinf(s16)):
+        raise OverflowError("a group scale does not fit fp16")
+    s16 = np.where(s16 == 0, HALF_SCALE_FLOOR, s16).astype(np.float16)
+    s = s16.astype(np.float32)
+    ratio = (g / s[..., None]).astype(np.float32)
+    q = np.clip(np.rint(ratio), -8, 7).astype(np.int8)
+    return q.reshape(n, k), s16
+
+
+def encode_h(w: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """fp32 W -> canonical (codes uint8 [n, k/2], scales fp16 [n, k/32])."""
+    q, s = quantize_h(w)
+    return pack_codes(q), s
+
+
+def algorithmic_bytes_h(n: int, k: int) -> int:
+    """16 code bytes and a 2-byte scale per group of 32."""
+    return n * (k // GROUP) * (16 + 2)
