@@ -343,6 +343,19 @@ __device__ void decode_unit(const GemvArgs &a, const uint8_t *w, int64_t r, int6
     }
     return;
   }
+  if constexpr (F == kQ4G32H) {
+    const uint8_t *pc = w + a.poff[0] + r * a.prb[0];
+    const uint32_t sc = ld1(w + a.poff[1] + r * a.prb[1] + u * 4);
+    for (int i = 0; i < 8; ++i) {
+      uint32_t v = ld1(pc + split_off(a.units, u, i >> 2, 16) + 4 * (i & 3));
+      for (int e = 0; e < 8; ++e) c[8 * i + e] = (v >> (4 * ((e >> 1) + 4 * (e & 1)))) & 15u;
+    }
+    for (int i = 0; i < nvalid; ++i) {
+      codes[i] = c[i];
+      vals[i] = (float)((int)c[i] - 8) * (i < 32 ? half_lo(sc) : half_hi(sc));
+    }
+    return;
+  }
   if constexpr (F == kQ4A32) {
     const uint8_t *pc = w + a.poff[0] + r * a.prb[0];
     const uint8_t *ps = w + a.poff[1] + r * a.prb[1];
@@ -715,6 +728,7 @@ int launch_mv_fmt(int fmt, GemvArgs a, int64_t count, hipStream_t s) {
     case 8: return launch_mv_f<8>(a, count, s);
     case 9: return launch_mv_f<9>(a, count, s);
     case 10: return launch_mv_f<10>(a, count, s);
+    case 11: return launch_mv_f<11>(a, count, s);
   }
   return QG_ERR_FORMAT;
 }
@@ -730,6 +744,7 @@ int launch_mv_group_fmt(int fmt, GemvGroup &G, hipStream_t s) {
     case 8: return launch_mv_group_f<8>(G, s);
     case 9: return launch_mv_group_f<9>(G, s);
     case 10: return launch_mv_group_f<10>(G, s);
+    case 11: return launch_mv_group_f<11>(G, s);
   }
   return QG_ERR_FORMAT;
 }
@@ -896,6 +911,7 @@ int dequant_gemv_q4g16(const void *w, const uint16_t *x, uint16_t *y, int64_t n,
 int dequant_gemv_q4g64(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(8, w, x, y, 0, n, k, s); }
 int dequant_gemv_q4g128(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(9, w, x, y, 0, n, k, s); }
 int dequant_gemv_q4a32(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(10, w, x, y, 0, n, k, s); }
+int dequant_gemv_q4g32h(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(11, w, x, y, 0, n, k, s); }
 int dequant_gemm_q4g32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m, int64_t n,
                        int64_t k, void *s) {
   return qg_gemm(4, w, X, ldx, Y, ldy, 0, m, n, k, s);
@@ -932,6 +948,10 @@ int dequant_gemm_q4a32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *
                        int64_t k, void *s) {
   return qg_gemm(10, w, X, ldx, Y, ldy, 0, m, n, k, s);
 }
+int dequant_gemm_q4g32h(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m, int64_t n,
+                        int64_t k, void *s) {
+  return qg_gemm(11, w, X, ldx, Y, ldy, 0, m, n, k, s);
+}
 
 int qg_dequantize(int fmt, const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream) {
   if (!fmt_valid(fmt)) return QG_ERR_FORMAT;
@@ -955,6 +975,7 @@ int qg_dequantize(int fmt, const void *w, float *w_out, uint8_t *codes_out, int6
     case 8: return launch(dequant_kernel<8>, grid, block, 0, s, a, w_out, codes_out);
     case 9: return launch(dequant_kernel<9>, grid, block, 0, s, a, w_out, codes_out);
     case 10: return launch(dequant_kernel<10>, grid, block, 0, s, a, w_out, codes_out);
+    case 11: return launch(dequant_kernel<11>, grid, block, 0, s, a, w_out, codes_out);
   }
   return QG_ERR_FORMAT;
 }
@@ -980,5 +1001,6 @@ int dequantize_q4g16(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, 
 int dequantize_q4g64(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(8, w, o, c, n, k, s); }
 int dequantize_q4g128(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(9, w, o, c, n, k, s); }
 int dequantize_q4a32(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(10, w, o, c, n, k, s); }
+int dequantize_q4g32h(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(11, w, o, c, n, k, s); }
 
 }  // extern "C"

@@ -49,6 +49,26 @@ bool half_ceil(double v, uint16_t *bits) {
   return true;
 }
 
+// Nearest binary16 value to v for finite v >= 0 (ties to even), as bits. Returns false on
+// overflow (v rounds past 65504).
+bool half_rn(double v, uint16_t *bits) {
+  if (!(v >= 0.0)) return false;
+  if (v == 0.0) { *bits = 0; return true; }
+  if (v < std::ldexp(1.0, -14)) {                        // subnormal range: k * 2^-24
+    *bits = (uint16_t)std::nearbyint(std::ldexp(v, 24));   // k == 1024 is 2^-14 = 0x0400
+    return true;
+  }
+  int ex;
+  std::frexp(v, &ex);
+  int e = ex - 1;
+  double k = std::nearbyint(std::ldexp(v, 10 - e));      // in [1024, 2048], ties to even
+  if (k >= 2048.0) { k = 1024.0; e += 1; }
+  int be = e + 15;
+  if (be >= 31) return false;
+  *bits = (uint16_t)((be << 10) | ((int)k - 1024));
+  return true;
+}
+
 // ---------------------------------------------------------------- bitstreams -------------
 
 void pack_le(const uint8_t *codes, int64_t count, int bits, uint8_t *out) {
@@ -117,6 +137,36 @@ int quantize_row_q4(const float *w, int64_t k, int G, uint8_t *codes, float *sca
         u[t] = (int)q + 8;
       }
       codes[(g * G + i) / 2] = (uint8_t)(u[0] | (u[1] << 4));
+    }
+  }
+  return QG_OK;
+}
+
+// One INT4 row with fp16 group scales (groups of 32): the INT4 rule with the scale
+// max|w| / 8 (fp32) rounded to the nearest fp16 (0 raised to 2^-24), the codes taken
+// against that stored scale.
+int quantize_row_q4h(const float *w, int64_t k, uint8_t *codes, uint16_t *scales) {
+  for (int64_t g = 0; g < k / 32; ++g) {
+    const float *v = w + g * 32;
+    float amax = 0.0f;
+    for (int i = 0; i < 32; ++i) {
+      if (!std::isfinite(v[i])) return QG_ERR_NONFINITE;
+      float a = std::fabs(v[i]);
+      if (a > amax) amax = a;
+    }
+    uint16_t sb;
+    if (!half_rn((double)(amax / 8.0f), &sb)) return QG_ERR_RANGE;
+    if (sb == 0) sb = 1;
+    scales[g] = sb;
+    const float scale = (float)half_to_double(sb);
+    for (int i = 0; i < 32; i += 2) {
+      int u[2];
+      for (int t = 0; t < 2; ++t) {
+        float q = std::nearbyint(v[i + t] / scale);
+        q = std::min(7.0f, std::max(-8.0f, q));
+        u[t] = (int)q + 8;
+      }
+      codes[(g * 32 + i) / 2] = (uint8_t)(u[0] | (u[1] << 4));
     }
   }
   return QG_OK;
@@ -297,7 +347,7 @@ inline uint32_t getbit(const uint32_t *w, int pos) { return (w[pos >> 5] >> (pos
 // at unit position k, for the code planes of each format. For q5sb/q6sb this is the low
 // nibble (b < 4) in the nibble dwords; high bits are placed by hi_pos().
 int code_pos(int fmt, int k, int b) {
-  if (q4_group(fmt) || fmt == kQ4A32 || fmt == 5 || fmt == 6) {        // nibble dwords
+  if (q4_group(fmt) || fmt == kQ4A32 || fmt == kQ4G32H || fmt == 5 || fmt == 6) {   // nibble dwords
     int i = k >> 3, e = k & 7;
     return i * 32 + q4_slot(e) * 4 + b;
   }
@@ -336,13 +386,17 @@ struct Planes {
 void row_to_device(int fmt, const uint8_t *canon, int64_t k, int64_t r, int64_t n, Planes P) {
   const int64_t units = (k + kUnit - 1) / kUnit;
   std::vector<uint8_t> codes((size_t)(units * kUnit), 0);
-  if (q4_group(fmt) || fmt == kQ4A32) {
-    const int G = fmt == kQ4A32 ? 32 : q4_group(fmt);
+  if (q4_group(fmt) || fmt == kQ4A32 || fmt == kQ4G32H) {
+    const int G = q4_group(fmt) ? q4_group(fmt) : 32;
     const uint8_t *cr = canon + r * (k / 2);
     for (int64_t i = 0; i < k; ++i) codes[(size_t)i] = (cr[i >> 1] >> (4 * (i & 1))) & 15;
-    const uint8_t *sr = canon + n * (k / 2) + r * (k / G) * 4;
     uint8_t *ds = P.p[1] + r * P.rb[1];
-    for (int64_t g = 0; g < k / G; ++g) std::memcpy(ds + q4_scale_off(G, units, g), sr + g * 4, 4);
+    if (fmt == kQ4G32H) {                                // fp16 scales, in group order
+      std::memcpy(ds, canon + n * (k / 2) + r * (k / 32) * 2, (size_t)(k / 32) * 2);
+    } else {
+      const uint8_t *sr = canon + n * (k / 2) + r * (k / G) * 4;
+      for (int64_t g = 0; g < k / G; ++g) std::memcpy(ds + q4_scale_off(G, units, g), sr + g * 4, 4);
+    }
     if (fmt == kQ4A32)                                   // zero points, in group order
       std::memcpy(P.p[2] + r * P.rb[2], canon + n * (k / 2) + n * (k / 32) * 4 + r * (k / 32), (size_t)(k / 32));
     uint8_t *dst = P.p[0] + r * P.rb[0];
@@ -432,7 +486,7 @@ void row_from_device(int fmt, const uint8_t *const *pl, const int64_t *rb, int64
   std::vector<uint8_t> codes((size_t)(units * kUnit), 0);
   for (int64_t u = 0; u < units; ++u) {
     uint32_t a[8] = {0}, hb[4] = {0};
-    if (q4_group(fmt) || fmt == kQ4A32) {
+    if (q4_group(fmt) || fmt == kQ4A32 || fmt == kQ4G32H) {
       std::memcpy(a, pl[0] + r * rb[0] + split_off(units, u, 0, 16), 16);
       if (k / 2 - u * 32 > 16) std::memcpy(a + 4, pl[0] + r * rb[0] + split_off(units, u, 1, 16), 16);
     } else if (fmt == 2) {
@@ -456,10 +510,14 @@ void row_from_device(int fmt, const uint8_t *const *pl, const int64_t *rb, int64
       codes[(size_t)(u * kUnit + kk)] = (uint8_t)cv;
     }
   }
-  if (q4_group(fmt) || fmt == kQ4A32) {
-    const int G = fmt == kQ4A32 ? 32 : q4_group(fmt);
+  if (q4_group(fmt) || fmt == kQ4A32 || fmt == kQ4G32H) {
+    const int G = q4_group(fmt) ? q4_group(fmt) : 32;
     uint8_t *cr = canon + r * (k / 2);
     for (int64_t i = 0; i < k; i += 2) cr[i / 2] = (uint8_t)(codes[(size_t)i] | (codes[(size_t)i + 1] << 4));
+    if (fmt == kQ4G32H) {
+      std::memcpy(canon + n * (k / 2) + r * (k / 32) * 2, pl[1] + r * rb[1], (size_t)(k / 32) * 2);
+      return;
+    }
     for (int64_t g = 0; g < k / G; ++g)
       std::memcpy(canon + n * (k / 2) + r * (k / G) * 4 + g * 4, pl[1] + r * rb[1] + q4_scale_off(G, units, g), 4);
     if (fmt == kQ4A32)
@@ -538,10 +596,10 @@ const char *qg_strerror(int status) {
   switch (status) {
     case QG_OK: return "ok";
     case QG_ERR_NULL: return "a required pointer is NULL";
-    case QG_ERR_SHAPE: return "n, k or m out of range (k must be a multiple of 256 for the super-block formats, of 32 for q4g32, 64 for q4g16, q4g64 and q4a32, 128 for q4g128)";
+    case QG_ERR_SHAPE: return "n, k or m out of range (k must be a multiple of 256 for the super-block formats, of 32 for q4g32, 64 for q4g16, q4g64, q4a32 and q4g32h, 128 for q4g128)";
     case QG_ERR_ALIGN: return "misaligned device pointer or leading dimension";
     case QG_ERR_NONFINITE: return "a weight is NaN or infinite";
-    case QG_ERR_RANGE: return "a super-block scale does not fit fp16, or a code does not fit its width";
+    case QG_ERR_RANGE: return "a super-block or fp16 group scale does not fit fp16, or a code does not fit its width";
     case QG_ERR_FORMAT: return "unknown format or bit width";
     case QG_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
     case QG_ERR_DEVICE: return "no usable gfx950 device or HIP runtime error";
@@ -555,6 +613,7 @@ int qg_canonical_bytes(int fmt, int64_t n, int64_t k, int64_t *bytes) {
   if (!shape_ok(fmt, n, k)) return QG_ERR_SHAPE;
   if (q4_group(fmt)) { *bytes = n * (k / 2) + n * (k / q4_group(fmt)) * 4; return QG_OK; }
   if (fmt == kQ4A32) { *bytes = n * (k / 2) + n * (k / 32) * 5; return QG_OK; }
+  if (fmt == kQ4G32H) { *bytes = n * (k / 2) + n * (k / 32) * 2; return QG_OK; }
   SB s;
   sb_spec(fmt, &s);
   *bytes = n * (k / kQK) * s.rec;
@@ -604,6 +663,17 @@ int qg_quantize(int fmt, const float *w, int64_t n, int64_t k, int64_t ldw, uint
       return (int)QG_OK;
     });
   }
+  if (fmt == kQ4G32H) {
+    uint8_t *codes = canonical;
+    uint16_t *scales = reinterpret_cast<uint16_t *>(canonical + n * (k / 2));
+    return parallel_rows(n, k, [&](int64_t r0, int64_t r1) {
+      for (int64_t r = r0; r < r1; ++r) {
+        int st = quantize_row_q4h(w + r * ldw, k, codes + r * (k / 2), scales + r * (k / 32));
+        if (st != QG_OK) return st;
+      }
+      return (int)QG_OK;
+    });
+  }
   if (fmt == kQ4A32) {
     uint8_t *codes = canonical;
     float *scales = reinterpret_cast<float *>(canonical + n * (k / 2));
@@ -634,6 +704,7 @@ int quantize_q4g16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c
 int quantize_q4g64(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(8, w, n, k, ldw, c); }
 int quantize_q4g128(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(9, w, n, k, ldw, c); }
 int quantize_q4a32(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(10, w, n, k, ldw, c); }
+int quantize_q4g32h(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(11, w, n, k, ldw, c); }
 int quantize_q2sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(2, w, n, k, ldw, c); }
 int quantize_q3sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(3, w, n, k, ldw, c); }
 int quantize_q5sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(5, w, n, k, ldw, c); }

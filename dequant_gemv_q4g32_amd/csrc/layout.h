@@ -17,6 +17,7 @@
 //         nibble slot (e>>1) + 4*(e&1); plane 1 fp32 scales (one per group of 32).
 //  q4a32  (asymmetric) planes 0 and 1 as q4g32 (unsigned codes), plane 2 uint8 zero points,
 //         2 bytes per unit in group order (not split).
+//  q4g32h plane 0 as q4g32; plane 1 fp16 scales in group order (one dword per unit).
 //         Split halves (also the q5sb/q6sb nibble planes): a row of a 32-byte-per-unit plane
 //         stores the first 16 bytes of every unit, then the second 16 bytes of every unit
 //         (dwords 0-3 of unit u at 16u, dwords 4-7 at 16 units + 16u); the q4g32 scale plane
@@ -84,15 +85,18 @@ struct FmtPlanes {
 // unit (group 64), one per two units (group 128).
 QG_HOST_DEVICE constexpr int q4_group(int fmt) { return fmt == 4 ? 32 : fmt == 7 ? 16 : fmt == 8 ? 64 : fmt == 9 ? 128 : 0; }
 
-// INT4 asymmetric, groups of 32 with a zero point (code 10).
+// INT4 asymmetric, groups of 32 with a zero point (code 10); INT4 symmetric, groups of 32
+// with fp16 scales (code 11).
 constexpr int kQ4A32 = 10;
+constexpr int kQ4G32H = 11;
 
-inline bool fmt_valid(int fmt) { return (fmt >= 2 && fmt <= 6) || q4_group(fmt) != 0 || fmt == kQ4A32; }
+inline bool fmt_valid(int fmt) { return (fmt >= 2 && fmt <= 6) || q4_group(fmt) != 0 || fmt == kQ4A32 || fmt == kQ4G32H; }
 
 // K must be a multiple of this: 32 for q4g32 (a row may end in half a unit), whole units
-// (64) for q4g16, q4g64 and q4a32, 128 for q4g128, a super-block (256) for the other formats.
+// (64) for q4g16, q4g64, q4a32 and q4g32h, 128 for q4g128, a super-block (256) for the
+// other formats.
 inline int64_t k_multiple(int fmt) {
-  if (fmt == kQ4A32) return kUnit;
+  if (fmt == kQ4A32 || fmt == kQ4G32H) return kUnit;
   const int G = q4_group(fmt);
   return G == 32 ? 32 : G ? (G > kUnit ? G : kUnit) : kQK;
 }
@@ -108,16 +112,18 @@ inline FmtPlanes fmt_planes(int fmt) {
     case 8: return {2, {32, 4, 0, 0}, {0, 0, 0, 0}};          // codes, 1 fp32 scale per unit
     case 9: return {2, {32, 2, 0, 0}, {0, 0, 0, 0}};          // codes, 1 fp32 scale per 2 units
     case 10: return {3, {32, 8, 2, 0}, {0, 0, 0, 0}};         // codes, fp32 scales, zero points
+    case 11: return {2, {32, 4, 0, 0}, {0, 0, 0, 0}};         // codes, fp16 scales
     default: return {0, {0, 0, 0, 0}, {0, 0, 0, 0}};
   }
 }
 
 // Row bytes of plane p for a row of k weights (k a multiple of 256 for the super-block
-// formats, of 32 for q4g32, of 64 for q4g16, q4g64 and q4a32, of 128 for q4g128).
+// formats, of 32 for q4g32, of 64 for q4g16, q4g64, q4a32 and q4g32h, of 128 for q4g128).
 inline int64_t plane_row_bytes(int fmt, int p, int64_t k) {
   FmtPlanes f = fmt_planes(fmt);
   if (fmt == 4) return p == 0 ? k / 2 : (k / 32) * 4;
   if (fmt == kQ4A32) return p == 0 ? k / 2 : p == 1 ? (k / 32) * 4 : k / 32;
+  if (fmt == kQ4G32H) return p == 0 ? k / 2 : (k / 32) * 2;
   if (q4_group(fmt)) return p == 0 ? k / 2 : (k / q4_group(fmt)) * 4;
   if (f.unit_bytes[p]) return (k / kUnit) * f.unit_bytes[p];
   return (k / kQK) * f.sb_bytes[p];

@@ -233,6 +233,7 @@ int launch_prefill(int fmt, const void *w, const uint16_t *X, int64_t ldx, void 
     case 8: return launch(prefill_kernel<8>, grid, block, 0, s, a);
     case 9: return launch(prefill_kernel<9>, grid, block, 0, s, a);
     case 10: return launch(prefill_kernel<10>, grid, block, 0, s, a);
+    case 11: return launch(prefill_kernel<11>, grid, block, 0, s, a);
   }
   return QG_ERR_FORMAT;
 }

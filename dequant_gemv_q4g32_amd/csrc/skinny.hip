@@ -209,6 +209,7 @@ int launch_skinny(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *
     case 8: return launch(skinny_kernel<8>, grid, block, shm, s, a);
     case 9: return launch(skinny_kernel<9>, grid, block, shm, s, a);
     case 10: return launch(skinny_kernel<10>, grid, block, shm, s, a);
+    case 11: return launch(skinny_kernel<11>, grid, block, shm, s, a);
   }
   return QG_ERR_FORMAT;
 }

@@ -210,6 +210,32 @@ template <> struct Unit<7> : UnitQ4<16> {};
 template <> struct Unit<8> : UnitQ4<64> {};
 template <> struct Unit<9> : UnitQ4<128> {};
 
+// ---- INT4 groups of 32 with fp16 scales (q4g32h): q4g32's codes and arithmetic; the unit's
+// two scales are one dword of fp16 pairs (group order), which both lanes of a shared unit
+// read.
+template <> struct Unit<kQ4G32H> : UnitQ4<32> {
+  __device__ static void offsets(int64_t u, uint32_t *off) {
+    off[0] = (uint32_t)(u * 16);
+    off[1] = (uint32_t)(u * 4);
+  }
+  template <int AUX = kNT, int S = 1> __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
+    const uint32_t r0 = L.row(0, r);
+    if constexpr (S == 2) {
+      q.c0 = bldx4<AUX>(L.rs[0], L.off[0] + (L.h ? L.half16 : 0u), r0);
+    } else {
+      q.c0 = bldx4<AUX>(L.rs[0], L.off[0], r0);
+      q.c1 = bldx4<AUX>(L.rs[0], L.off[0] + L.half16, r0);
+    }
+    const uint32_t sc = bld1(L.rs[1], L.off[1], L.row(1, r));
+    if constexpr (S == 2) {
+      q.s[0] = L.h ? half_hi(sc) : half_lo(sc);
+    } else {
+      q.s[0] = half_lo(sc);
+      q.s[1] = half_hi(sc);
+    }
+  }
+};
+
 // ---- INT4 asymmetric, groups of 32 (q4a32): the q4g32 code and scale planes with unsigned
 // codes c, and a plane of uint8 zero points z (2 bytes per unit, group order):
 // w_hat = s * (c - z), so a group's sum of w_hat * x is s * (sum c x - z * sum x). With S = 2

@@ -17,6 +17,11 @@
  *             z = clamp(rint(-lo / s), 0, 15), c = clamp(rint(w / s) + z, 0, 15) in fp32,
  *             w_hat = s * (c - z); 16 B of codes + 4 B of scale + 1 B of zero point per group
  *             (5.25 bpw). k must be a multiple of 64.
+ *   QG_Q4G32H INT4 symmetric, groups of 32, fp16 scale ("二三五六位量化" page section 2.1: a
+ *             16-bit scale per group of 32): s = fp16_rn(max|w| / 8 in fp32) (0 raised to
+ *             2^-24; past 65504 QG_ERR_RANGE), q = clamp(rint(w / s), -8, 7) in fp32 against
+ *             that stored s, w_hat = q * s; 16 B of codes + 2 B of scale per group (4.5 bpw).
+ *             k must be a multiple of 64.
  *   QG_Q2SB   256-weight super-block, 16 sub-blocks of 16, 2-bit codes c, 4-bit sub-scale sc
  *             and 4-bit sub-min m, fp16 d and dmin: w_hat = d*sc*c - dmin*m  (84 B, 2.625 bpw).
  *   QG_Q3SB   16 sub-blocks of 16, 3-bit codes, 6-bit sc, fp16 d: w_hat = d*sc*(c - 4)
@@ -38,7 +43,8 @@
  * Two encodings of a quantized matrix W [n][k] (W is out_features x in_features):
  *   canonical  the pages' interchange layout. q4g32: codes [n][k/2] (byte = u[2j] | u[2j+1] << 4
  *              with u = q + 8) followed by fp32 scales [n][k/32] (q4gG: [n][k/G]). q4a32: codes
- *              [n][k/2] (u = c), fp32 scales [n][k/32], uint8 zero points [n][k/32]. Super-block formats: records
+ *              [n][k/2] (u = c), fp32 scales [n][k/32], uint8 zero points [n][k/32]. q4g32h: codes
+ *              as q4g32, then fp16 scales [n][k/32]. Super-block formats: records
  *              [n][k/256] of 84/110/176/210 bytes; fields in the byte table's column order
  *              (codes [, high-bit plane], sub-scales, d [, dmin]); every bit field is a
  *              little-endian bitstream (code i at bits [b*i, b*i + b), section 2.2's unpack3
@@ -80,7 +86,8 @@ typedef enum qg_format {
   QG_Q4G16 = 7,
   QG_Q4G64 = 8,
   QG_Q4G128 = 9,
-  QG_Q4A32 = 10
+  QG_Q4A32 = 10,
+  QG_Q4G32H = 11
 } qg_format;
 
 typedef enum qg_status {
@@ -143,6 +150,7 @@ int quantize_q4g16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c
 int quantize_q4g64(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
 int quantize_q4g128(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
 int quantize_q4a32(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
+int quantize_q4g32h(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
 
 /* Canonical encoding (host) -> device layout (host buffer of qg_device_layout().total_bytes;
  * padding is zeroed). A pure bit permutation. */
@@ -167,6 +175,7 @@ int dequant_gemv_q4g16(const void *w, const uint16_t *x, uint16_t *y, int64_t n,
 int dequant_gemv_q4g64(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
 int dequant_gemv_q4g128(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
 int dequant_gemv_q4a32(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
+int dequant_gemv_q4g32h(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
 
 /* Generic form: y_f32 != 0 writes fp32 y (4-byte aligned) instead of fp16. */
 int qg_gemv(int fmt, const void *w, const uint16_t *x, void *y, int y_f32, int64_t n, int64_t k, void *stream);
@@ -210,6 +219,8 @@ int dequant_gemm_q4g128(const void *w, const uint16_t *X, int64_t ldx, uint16_t 
                       int64_t m, int64_t n, int64_t k, void *stream);
 int dequant_gemm_q4a32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
                        int64_t m, int64_t n, int64_t k, void *stream);
+int dequant_gemm_q4g32h(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
+                        int64_t m, int64_t n, int64_t k, void *stream);
 /* Generic form; y_f32 != 0 writes fp32 Y (4-byte aligned). */
 int qg_gemm(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int64_t ldy, int y_f32,
             int64_t m, int64_t n, int64_t k, void *stream);
@@ -274,6 +285,7 @@ int dequantize_q4g16(const void *w, float *w_out, uint8_t *codes_out, int64_t n,
 int dequantize_q4g64(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 int dequantize_q4g128(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 int dequantize_q4a32(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
+int dequantize_q4g32h(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 int qg_dequantize(int fmt, const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 
 /* ---- measurement (device) -----------------------------------------------------------------

@@ -13,6 +13,9 @@ def oracle_decode(fmt, w):
     if fmt in qg.Q4_GROUPS:
         q, s = int4.quantize(w, qg.Q4_GROUPS[fmt])
         return (q.astype(np.int16) + 8).astype(np.uint8), int4.dequantize(q, s)
+    if fmt == "q4g32h":
+        q, s16 = int4.quantize_h(w)
+        return (q.astype(np.int16) + 8).astype(np.uint8), int4.dequantize(q, s16.astype(np.float32))
     if fmt == "q4a32":
         q, s, z = int4.quantize_asym(w)
         return q, int4.dequantize_asym(q, s, z)

@@ -14,10 +14,13 @@ from oracle import bitstream, int4
 from oracle import superblock as sb
 from workloads import laplace_weights, uniform_codes
 
-FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb", "q4g16", "q4g64", "q4g128", "q4a32"]
+FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb", "q4g16", "q4g64", "q4g128", "q4a32", "q4g32h"]
 
 
 def oracle_canonical(fmt, w):
+    if fmt == "q4g32h":
+        codes, s16 = int4.encode_h(w)
+        return np.concatenate([codes.reshape(-1), s16.reshape(-1).view(np.uint8)])
     if fmt == "q4a32":
         codes, scales, zeros = int4.encode_asym(w)
         return np.concatenate([codes.reshape(-1), scales.reshape(-1).view(np.uint8), zeros.reshape(-1)])
@@ -113,6 +116,8 @@ def test_algorithmic_bytes_match_oracle(fmt):
     n, k = 64, 4096
     if fmt == "q4a32":
         want = int4.algorithmic_bytes_asym(n, k)
+    elif fmt == "q4g32h":
+        want = int4.algorithmic_bytes_h(n, k)
     else:
         want = int4.algorithmic_bytes(n, k, qg.Q4_GROUPS[fmt]) if fmt in qg.Q4_GROUPS else sb.algorithmic_bytes(fmt, n, k)
     assert qg.device_layout(fmt, n, k).algorithmic_bytes == want
@@ -131,7 +136,7 @@ def test_error_codes():
         assert e.value.status == -4
     big = w.copy()
     big[0, 0] = np.float32(1e10)
-    for fmt in ("q2sb", "q3sb", "q5sb", "q6sb"):
+    for fmt in ("q2sb", "q3sb", "q5sb", "q6sb", "q4g32h"):
         with pytest.raises(qg.QGError) as e:
             qg.quantize(fmt, big)
         assert e.value.status == -5
