@@ -21,7 +21,10 @@ What it defines, following the two source pages:
   * act-order weights ("二三五六位量化" sections 2.4 and 3.2, stage 3: columns quantized in
     a stored permuted order, restored at inference), in ``actorder``;
   * the 8-bit KV-cache group codec ("二三五六位量化" section 4.1: one fp16 scale per 32
-    elements, about 1.06 bytes per element), in ``kvcache``.
+    elements, about 1.06 bytes per element), in ``kvcache``;
+  * format variants: INT4 groups of 16/64/128, asymmetric INT4 with a zero point
+    ("二三五六位量化" section 2.1) and INT4 with fp16 group scales (section 2.1) in ``int4``;
+    super-block formats with bf16 super-scales (section 2.3) in ``superblock`` / ``bf16``.
 
 Readings taken where the pages are silent or garbled are listed in each module's docstring.
 Floating point is fp64 throughout except where the pages fix another precision (the INT4

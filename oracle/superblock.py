@@ -46,6 +46,10 @@ Readings (the pages give the layouts but not every field, nor how scales are cho
     |w - w_hat| <= d * sc_j / 2 for every element, which is section 3.4's check with
     "scale" read as the sub-block step d * sc_j. rint is round half to even.
   * A super-scale beyond the fp16 range raises OverflowError (section 2.3 warns of inf).
+  * bf16 super-scales ("q2sb_bf16", "q3sb_bf16", "q5sb_bf16", "q6sb_bf16"): section 2.3's
+    remedy for that overflow, storing the super-block scale as bf16. Read as the same
+    format, record layout and rule with bf16_ceil (smallest bf16 >= v) in place of
+    fp16_ceil for d and dmin, and the two bytes of each holding the bf16 bits.
 """
 from __future__ import annotations
 
@@ -56,6 +60,7 @@ from typing import Dict, List
 import numpy as np
 
 from . import bitstream
+from .bf16 import bf16_bits, bf16_ceil, bf16_ceil_array, bf16_from_le_bytes, bf16_to_le_bytes
 from .fp16 import fp16_ceil, fp16_ceil_array, from_le_bytes, to_le_bytes
 
 QK = 256
@@ -70,6 +75,8 @@ class SBSpec:
     offset: int
     smax: int
     record_bytes: int
+    layout: str = ""           # the base format whose record layout this one shares
+    bf16: bool = False         # super-scales d, dmin stored as bf16 instead of fp16
 
     @property
     def sub(self) -> int:
@@ -81,11 +88,44 @@ class SBSpec:
 
 
 SPECS: Dict[str, SBSpec] = {
-    "q2sb": SBSpec("q2sb", 2, 16, False, 0, 15, 84),
-    "q3sb": SBSpec("q3sb", 3, 16, True, 4, 63, 110),
-    "q5sb": SBSpec("q5sb", 5, 8, False, 0, 63, 176),
-    "q6sb": SBSpec("q6sb", 6, 16, True, 32, 127, 210),
+    "q2sb": SBSpec("q2sb", 2, 16, False, 0, 15, 84, "q2sb"),
+    "q3sb": SBSpec("q3sb", 3, 16, True, 4, 63, 110, "q3sb"),
+    "q5sb": SBSpec("q5sb", 5, 8, False, 0, 63, 176, "q5sb"),
+    "q6sb": SBSpec("q6sb", 6, 16, True, 32, 127, 210, "q6sb"),
 }
+for _b in ("q2sb", "q3sb", "q5sb", "q6sb"):
+    SPECS[_b + "_bf16"] = dataclasses.replace(SPECS[_b], name=_b + "_bf16", bf16=True)
+
+
+# Super-scale codec of a spec: ceil to the stored type, zero, bits, little-endian bytes.
+def _ceil(spec: SBSpec, v: float):
+    return bf16_ceil(v) if spec.bf16 else fp16_ceil(v)
+
+
+def _ceil_array(spec: SBSpec, v: np.ndarray) -> np.ndarray:
+    return bf16_ceil_array(v) if spec.bf16 else fp16_ceil_array(v)
+
+
+def _zero(spec: SBSpec):
+    return np.float32(0.0) if spec.bf16 else np.float16(0.0)
+
+
+def _dtype(spec: SBSpec):
+    return np.float32 if spec.bf16 else np.float16
+
+
+def scale_bits(spec: SBSpec, d) -> np.ndarray:
+    """Stored 16-bit pattern of super-scales (fp16 or bf16 per spec)."""
+    d = np.asarray(d, _dtype(spec))
+    return bf16_bits(d) if spec.bf16 else d.view(np.uint16)
+
+
+def _to_bytes(spec: SBSpec, d) -> np.ndarray:
+    return bf16_to_le_bytes(d) if spec.bf16 else to_le_bytes(d)
+
+
+def _from_bytes(spec: SBSpec, b) -> np.ndarray:
+    return bf16_from_le_bytes(b) if spec.bf16 else from_le_bytes(b)
 
 
 # ---------------------------------------------------------------------------
@@ -106,8 +146,8 @@ def quantize_block_scalar(spec: SBSpec, w256) -> dict:
         t = [max(abs(v) for v in blk) / (o - 0.5) for blk in blocks]
         T = max(t)
         if T == 0.0:
-            return dict(codes=[o] * QK, sc=[0] * nsub, m=None, d=np.float16(0.0), dmin=None)
-        d = fp16_ceil(T / spec.smax)
+            return dict(codes=[o] * QK, sc=[0] * nsub, m=None, d=_zero(spec), dmin=None)
+        d = _ceil(spec, T / spec.smax)
         dd = float(d)
         sc = [min(spec.smax, math.ceil(tj / dd)) for tj in t]
         for j, blk in enumerate(blocks):
@@ -119,19 +159,19 @@ def quantize_block_scalar(spec: SBSpec, w256) -> dict:
     hi = [max(0.0, max(blk)) for blk in blocks]
     L = max(-x for x in lo)
     if L == 0.0:
-        dmin = np.float16(0.0)
+        dmin = _zero(spec)
         m = [0] * nsub
     else:
-        dmin = fp16_ceil(L / spec.smax)
+        dmin = _ceil(spec, L / spec.smax)
         m = [min(spec.smax, math.ceil(-x / float(dmin))) for x in lo]
     off = [float(dmin) * mj for mj in m]
     t = [(hi[j] + off[j]) / cmax for j in range(nsub)]
     T = max(t)
     if T == 0.0:
-        d = np.float16(0.0)
+        d = _zero(spec)
         sc = [0] * nsub
     else:
-        d = fp16_ceil(T / spec.smax)
+        d = _ceil(spec, T / spec.smax)
         sc = [min(spec.smax, math.ceil(tj / float(d))) for tj in t]
     for j, blk in enumerate(blocks):
         step = float(d) * sc[j]
@@ -154,19 +194,19 @@ def dequantize_block_scalar(spec: SBSpec, f: dict) -> List[float]:
 
 def encode_block_scalar(spec: SBSpec, f: dict) -> bytes:
     codes = f["codes"]
-    d = to_le_bytes(np.array(f["d"], np.float16)).tobytes()
-    if spec.name == "q2sb":
+    d = _to_bytes(spec, np.array(f["d"], _dtype(spec))).tobytes()
+    if spec.layout == "q2sb":
         meta = bytes((f["sc"][j] | (f["m"][j] << 4)) for j in range(16))
-        dm = to_le_bytes(np.array(f["dmin"], np.float16)).tobytes()
+        dm = _to_bytes(spec, np.array(f["dmin"], _dtype(spec))).tobytes()
         rec = bitstream.pack_bits_scalar(codes, 2) + meta + d + dm
-    elif spec.name == "q3sb":
+    elif spec.layout == "q3sb":
         rec = bitstream.pack_bits_scalar(codes, 3) + bitstream.pack_bits_scalar(f["sc"], 6) + d
-    elif spec.name == "q5sb":
-        dm = to_le_bytes(np.array(f["dmin"], np.float16)).tobytes()
+    elif spec.layout == "q5sb":
+        dm = _to_bytes(spec, np.array(f["dmin"], _dtype(spec))).tobytes()
         rec = (bitstream.pack_bits_scalar([c & 15 for c in codes], 4)
                + bitstream.pack_bits_scalar([c >> 4 for c in codes], 1)
                + bitstream.pack_bits_scalar(list(f["sc"]) + list(f["m"]), 6) + d + dm)
-    elif spec.name == "q6sb":
+    elif spec.layout == "q6sb":
         rec = (bitstream.pack_bits_scalar([c & 15 for c in codes], 4)
                + bitstream.pack_bits_scalar([c >> 4 for c in codes], 2)
                + bytes((s & 0xFF) for s in f["sc"]) + d)
@@ -181,24 +221,24 @@ def decode_block_scalar(spec: SBSpec, rec: bytes) -> dict:
         raise ValueError("wrong record length")
 
     def half(b):
-        return from_le_bytes(np.frombuffer(b, np.uint8)).reshape(())[()]
+        return _from_bytes(spec, np.frombuffer(b, np.uint8)).reshape(())[()]
 
-    if spec.name == "q2sb":
+    if spec.layout == "q2sb":
         codes = bitstream.unpack_bits_scalar(rec[0:64], 2, QK)
         sc = [b & 15 for b in rec[64:80]]
         m = [b >> 4 for b in rec[64:80]]
         return dict(codes=codes, sc=sc, m=m, d=half(rec[80:82]), dmin=half(rec[82:84]))
-    if spec.name == "q3sb":
+    if spec.layout == "q3sb":
         codes = bitstream.unpack_bits_scalar(rec[0:96], 3, QK)
         sc = bitstream.unpack_bits_scalar(rec[96:108], 6, 16)
         return dict(codes=codes, sc=sc, m=None, d=half(rec[108:110]), dmin=None)
-    if spec.name == "q5sb":
+    if spec.layout == "q5sb":
         lo = bitstream.unpack_bits_scalar(rec[0:128], 4, QK)
         hi = bitstream.unpack_bits_scalar(rec[128:160], 1, QK)
         f6 = bitstream.unpack_bits_scalar(rec[160:172], 6, 16)
         return dict(codes=[a | (b << 4) for a, b in zip(lo, hi)], sc=f6[:8], m=f6[8:],
                     d=half(rec[172:174]), dmin=half(rec[174:176]))
-    if spec.name == "q6sb":
+    if spec.layout == "q6sb":
         lo = bitstream.unpack_bits_scalar(rec[0:128], 4, QK)
         hi = bitstream.unpack_bits_scalar(rec[128:192], 2, QK)
         sc = [b - 256 if b >= 128 else b for b in rec[192:208]]
@@ -229,8 +269,8 @@ def quantize(fmt: str, w: np.ndarray) -> dict:
         o = spec.offset
         t = np.abs(v).max(axis=3) / (o - 0.5) if v.size else np.zeros((n, S, spec.nsub))
         T = t.max(axis=2) if t.size else np.zeros((n, S))
-        d = fp16_ceil_array(T / spec.smax)
-        d = np.where(T == 0.0, np.float16(0.0), d).astype(np.float16)
+        d = _ceil_array(spec, T / spec.smax)
+        d = np.where(T == 0.0, _zero(spec), d).astype(_dtype(spec))
         dd = d.astype(np.float64)[..., None]
         with np.errstate(divide="ignore", invalid="ignore"):
             sc = np.minimum(spec.smax, np.ceil(t / dd))
@@ -243,8 +283,8 @@ def quantize(fmt: str, w: np.ndarray) -> dict:
     lo = np.minimum(0.0, v.min(axis=3)) if v.size else np.zeros((n, S, spec.nsub))
     hi = np.maximum(0.0, v.max(axis=3)) if v.size else np.zeros((n, S, spec.nsub))
     L = (-lo).max(axis=2) if lo.size else np.zeros((n, S))
-    dmin = fp16_ceil_array(L / spec.smax)
-    dmin = np.where(L == 0.0, np.float16(0.0), dmin).astype(np.float16)
+    dmin = _ceil_array(spec, L / spec.smax)
+    dmin = np.where(L == 0.0, _zero(spec), dmin).astype(_dtype(spec))
     dm = dmin.astype(np.float64)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):
         m = np.minimum(spec.smax, np.ceil(-lo / dm))
@@ -252,8 +292,8 @@ def quantize(fmt: str, w: np.ndarray) -> dict:
     off = dm * m
     t = (hi + off) / cmax
     T = t.max(axis=2) if t.size else np.zeros((n, S))
-    d = fp16_ceil_array(T / spec.smax)
-    d = np.where(T == 0.0, np.float16(0.0), d).astype(np.float16)
+    d = _ceil_array(spec, T / spec.smax)
+    d = np.where(T == 0.0, _zero(spec), d).astype(_dtype(spec))
     dd = d.astype(np.float64)[..., None]
     with np.errstate(divide="ignore", invalid="ignore"):
         sc = np.minimum(spec.smax, np.ceil(t / dd))
@@ -271,17 +311,18 @@ def encode_fields(fmt: str, f: dict) -> np.ndarray:
     spec = SPECS[fmt]
     codes = f["codes"]
     n, S, _ = codes.shape
-    d = to_le_bytes(f["d"])
-    if fmt == "q2sb":
+    d = _to_bytes(spec, f["d"])
+    lay = spec.layout
+    if lay == "q2sb":
         meta = (f["sc"].astype(np.uint8) | (f["m"].astype(np.uint8) << 4)).astype(np.uint8)
-        parts = [bitstream.pack_bits(codes, 2), meta, d, to_le_bytes(f["dmin"])]
-    elif fmt == "q3sb":
+        parts = [bitstream.pack_bits(codes, 2), meta, d, _to_bytes(spec, f["dmin"])]
+    elif lay == "q3sb":
         parts = [bitstream.pack_bits(codes, 3), bitstream.pack_bits(f["sc"].astype(np.uint8), 6), d]
-    elif fmt == "q5sb":
+    elif lay == "q5sb":
         f6 = np.concatenate([f["sc"], f["m"]], axis=-1).astype(np.uint8)
         parts = [bitstream.pack_bits(codes & 15, 4), bitstream.pack_bits(codes >> 4, 1),
-                 bitstream.pack_bits(f6, 6), d, to_le_bytes(f["dmin"])]
-    elif fmt == "q6sb":
+                 bitstream.pack_bits(f6, 6), d, _to_bytes(spec, f["dmin"])]
+    elif lay == "q6sb":
         parts = [bitstream.pack_bits(codes & 15, 4), bitstream.pack_bits(codes >> 4, 2),
                  (f["sc"].astype(np.int16) & 0xFF).astype(np.uint8), d]
     else:
@@ -297,26 +338,31 @@ def decode_records(fmt: str, rec: np.ndarray) -> dict:
     rec = np.asarray(rec, np.uint8)
     if rec.shape[-1] != spec.record_bytes:
         raise ValueError("wrong record length")
-    if fmt == "q2sb":
+    lay = spec.layout
+
+    def half(b):
+        return _from_bytes(spec, b)
+
+    if lay == "q2sb":
         codes = bitstream.unpack_bits(rec[..., 0:64], 2, QK)
         meta = rec[..., 64:80]
         return dict(codes=codes, sc=(meta & 15).astype(np.int16), m=(meta >> 4).astype(np.int16),
-                    d=from_le_bytes(rec[..., 80:82]), dmin=from_le_bytes(rec[..., 82:84]))
-    if fmt == "q3sb":
+                    d=half(rec[..., 80:82]), dmin=half(rec[..., 82:84]))
+    if lay == "q3sb":
         return dict(codes=bitstream.unpack_bits(rec[..., 0:96], 3, QK),
                     sc=bitstream.unpack_bits(rec[..., 96:108], 6, 16).astype(np.int16), m=None,
-                    d=from_le_bytes(rec[..., 108:110]), dmin=None)
-    if fmt == "q5sb":
+                    d=half(rec[..., 108:110]), dmin=None)
+    if lay == "q5sb":
         lo = bitstream.unpack_bits(rec[..., 0:128], 4, QK)
         hi = bitstream.unpack_bits(rec[..., 128:160], 1, QK)
         f6 = bitstream.unpack_bits(rec[..., 160:172], 6, 16).astype(np.int16)
         return dict(codes=(lo | (hi << 4)).astype(np.uint8), sc=f6[..., :8], m=f6[..., 8:],
-                    d=from_le_bytes(rec[..., 172:174]), dmin=from_le_bytes(rec[..., 174:176]))
-    if fmt == "q6sb":
+                    d=half(rec[..., 172:174]), dmin=half(rec[..., 174:176]))
+    if lay == "q6sb":
         lo = bitstream.unpack_bits(rec[..., 0:128], 4, QK)
         hi = bitstream.unpack_bits(rec[..., 128:192], 2, QK)
         return dict(codes=(lo | (hi << 4)).astype(np.uint8), sc=rec[..., 192:208].view(np.int8).astype(np.int16),
-                    m=None, d=from_le_bytes(rec[..., 208:210]), dmin=None)
+                    m=None, d=half(rec[..., 208:210]), dmin=None)
     raise KeyError(fmt)
 
 
