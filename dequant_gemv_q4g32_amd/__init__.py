@@ -20,11 +20,13 @@ LIB_PATH = os.path.join(_HERE, "libqgemv.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "qgemv.h")
 
 FORMATS = {"q2sb": 2, "q3sb": 3, "q4g32": 4, "q5sb": 5, "q6sb": 6, "q4g16": 7, "q4g64": 8, "q4g128": 9,
-           "q4a32": 10, "q4g32h": 11}
+           "q4a32": 10, "q4g32h": 11,
+           "q2sb_bf16": 12, "q3sb_bf16": 13, "q5sb_bf16": 15, "q6sb_bf16": 16}
 Q4_GROUPS = {"q4g16": 16, "q4g32": 32, "q4g64": 64, "q4g128": 128}   # symmetric INT4 group sizes
-SUPERBLOCK_FORMATS = ("q2sb", "q3sb", "q5sb", "q6sb")
+SUPERBLOCK_FORMATS = ("q2sb", "q3sb", "q5sb", "q6sb", "q2sb_bf16", "q3sb_bf16", "q5sb_bf16", "q6sb_bf16")
 K_MULTIPLE = {"q4g32": 32, "q2sb": 256, "q3sb": 256, "q5sb": 256, "q6sb": 256, "q4g16": 64, "q4g64": 64, "q4g128": 128,
-              "q4a32": 64, "q4g32h": 64}
+              "q4a32": 64, "q4g32h": 64, "q2sb_bf16": 256, "q3sb_bf16": 256, "q5sb_bf16": 256,
+              "q6sb_bf16": 256}
 
 
 class QGError(RuntimeError):

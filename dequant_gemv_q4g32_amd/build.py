@@ -16,6 +16,7 @@ import os
 import shutil
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -55,15 +56,20 @@ def build(verbose: bool = False) -> str:
         _run([hipcc, "-x", "c++", "-O2", "-ffp-contract=off", *common, "-c", os.path.join(CSRC, src), "-o", obj],
              verbose)
         objs.append(obj)
+    device = []
     for src in DEVICE_SOURCES:
         path = os.path.join(CSRC, src)
         if not os.path.exists(path):
             continue
         obj = os.path.join(BUILD, src + ".o")
-        _run([hipcc, f"--offload-arch={ARCH}", "-O3", "-ffp-contract=off", *common,
-              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-              "-c", path, "-o", obj], verbose)
+        device.append([hipcc, f"--offload-arch={ARCH}", "-O3", "-ffp-contract=off", *common,
+                       "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+                       "-c", path, "-o", obj])
         objs.append(obj)
+    # the device sources compile independently: one compiler process each
+    with ThreadPoolExecutor(max_workers=max(1, min(len(device), os.cpu_count() or 1, 8))) as pool:
+        for f in [pool.submit(_run, cmd, verbose) for cmd in device]:
+            f.result()
     tmp = LIB + ".tmp"
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp, "-lpthread"], verbose)
     os.replace(tmp, LIB)

@@ -372,7 +372,9 @@ __device__ void decode_unit(const GemvArgs &a, const uint8_t *w, int64_t r, int6
     }
     return;
   }
-  if (F == 2) {
+  constexpr int B = sb_base(F);
+  constexpr bool BF = sb_bf16(F);
+  if (B == 2) {
     const uint8_t *pc = w + a.poff[0] + r * a.prb[0] + u * 16;
     uint32_t d[4];
     for (int i = 0; i < 4; ++i) d[i] = ld1(pc + 4 * i);
@@ -382,7 +384,7 @@ __device__ void decode_unit(const GemvArgs &a, const uint8_t *w, int64_t r, int6
     }
     uint32_t s = ld1(w + a.poff[1] + r * a.prb[1] + u * 4);
     uint32_t dd = ld1(w + a.poff[2] + r * a.prb[2] + (u >> 2) * 4);
-    float dv = half_lo(dd), dm = half_hi(dd);
+    float dv = ss_lo<BF>(dd), dm = ss_hi<BF>(dd);
     for (int j = 0; j < 4; ++j) {
       step[j] = dv * (float)((s >> (8 * j)) & 15u);
       off[j] = dm * (float)((s >> (8 * j + 4)) & 15u);
@@ -393,7 +395,7 @@ __device__ void decode_unit(const GemvArgs &a, const uint8_t *w, int64_t r, int6
     }
     return;
   }
-  if (F == 3) {
+  if (B == 3) {
     uint32_t e[6];
     const uint8_t *pa = w + a.poff[0] + r * a.prb[0] + u * 16;
     const uint8_t *pb = w + a.poff[1] + r * a.prb[1] + u * 8;
@@ -415,7 +417,7 @@ __device__ void decode_unit(const GemvArgs &a, const uint8_t *w, int64_t r, int6
       c[k] = (uint8_t)v;
     }
     uint32_t f = load_fields24(w + a.poff[2] + r * a.prb[2] + (u >> 2) * 12, (int)(u & 3));
-    float dv = half_bits(ldh(w + a.poff[3] + r * a.prb[3] + (u >> 2) * 2));
+    float dv = ss_one<BF>(ldh(w + a.poff[3] + r * a.prb[3] + (u >> 2) * 2));
     for (int k = 0; k < 64; ++k) {
       codes[k] = c[k];
       float st = dv * (float)((f >> (6 * (k >> 4))) & 63u);
@@ -427,21 +429,21 @@ __device__ void decode_unit(const GemvArgs &a, const uint8_t *w, int64_t r, int6
   const uint8_t *pl = w + a.poff[0] + r * a.prb[0];
   uint32_t L[8], H[4];
   for (int i = 0; i < 8; ++i) L[i] = ld1(pl + split_off(a.units, u, i >> 2, 16) + 4 * (i & 3));
-  const int hbytes = F == 5 ? 8 : 16;
+  const int hbytes = B == 5 ? 8 : 16;
   const uint8_t *ph = w + a.poff[1] + r * a.prb[1] + u * hbytes;
   for (int i = 0; i < hbytes / 4; ++i) H[i] = ld1(ph + 4 * i);
   const int base[4] = {4, 8, 12, 16};
   for (int k = 0; k < 64; ++k) {
     int i = k >> 3, e = k & 7, pk = e >> 1, h = e & 1;
     uint32_t lo = (L[i] >> (4 * ((e >> 1) + 4 * (e & 1)))) & 15u, hi;
-    if (F == 5) hi = (H[i >> 2] >> ((base[pk] + 16 * h + (i & 3)) & 31)) & 1u;
+    if (B == 5) hi = (H[i >> 2] >> ((base[pk] + 16 * h + (i & 3)) & 31)) & 1u;
     else hi = (H[i >> 1] >> ((base[pk] + 16 * h + 2 * (i & 1)) & 31)) & 3u;
     c[k] = (uint8_t)(lo | (hi << 4));
   }
-  if (F == 5) {
+  if (B == 5) {
     uint32_t f = load_fields24(w + a.poff[2] + r * a.prb[2] + (u >> 2) * 12, (int)(u & 3));
     uint32_t dd = ld1(w + a.poff[3] + r * a.prb[3] + (u >> 2) * 4);
-    float dv = half_lo(dd), dm = half_hi(dd);
+    float dv = ss_lo<BF>(dd), dm = ss_hi<BF>(dd);
     for (int h = 0; h < 2; ++h) {
       step[h] = dv * (float)((f >> (6 * h)) & 63u);
       off[h] = dm * (float)((f >> (12 + 6 * h)) & 63u);
@@ -452,7 +454,7 @@ __device__ void decode_unit(const GemvArgs &a, const uint8_t *w, int64_t r, int6
     }
   } else {
     uint32_t s = ld1(w + a.poff[2] + r * a.prb[2] + u * 4);
-    float dv = half_bits(ldh(w + a.poff[3] + r * a.prb[3] + (u >> 2) * 2));
+    float dv = ss_one<BF>(ldh(w + a.poff[3] + r * a.prb[3] + (u >> 2) * 2));
     for (int k = 0; k < 64; ++k) {
       codes[k] = c[k];
       float st = dv * (float)(int8_t)((s >> (8 * (k >> 4))) & 0xFFu);
@@ -729,6 +731,10 @@ int launch_mv_fmt(int fmt, GemvArgs a, int64_t count, hipStream_t s) {
     case 9: return launch_mv_f<9>(a, count, s);
     case 10: return launch_mv_f<10>(a, count, s);
     case 11: return launch_mv_f<11>(a, count, s);
+    case 12: return launch_mv_f<12>(a, count, s);
+    case 13: return launch_mv_f<13>(a, count, s);
+    case 15: return launch_mv_f<15>(a, count, s);
+    case 16: return launch_mv_f<16>(a, count, s);
   }
   return QG_ERR_FORMAT;
 }
@@ -745,6 +751,10 @@ int launch_mv_group_fmt(int fmt, GemvGroup &G, hipStream_t s) {
     case 9: return launch_mv_group_f<9>(G, s);
     case 10: return launch_mv_group_f<10>(G, s);
     case 11: return launch_mv_group_f<11>(G, s);
+    case 12: return launch_mv_group_f<12>(G, s);
+    case 13: return launch_mv_group_f<13>(G, s);
+    case 15: return launch_mv_group_f<15>(G, s);
+    case 16: return launch_mv_group_f<16>(G, s);
   }
   return QG_ERR_FORMAT;
 }
@@ -912,6 +922,10 @@ int dequant_gemv_q4g64(const void *w, const uint16_t *x, uint16_t *y, int64_t n,
 int dequant_gemv_q4g128(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(9, w, x, y, 0, n, k, s); }
 int dequant_gemv_q4a32(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(10, w, x, y, 0, n, k, s); }
 int dequant_gemv_q4g32h(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(11, w, x, y, 0, n, k, s); }
+int dequant_gemv_q2sb_bf16(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(12, w, x, y, 0, n, k, s); }
+int dequant_gemv_q3sb_bf16(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(13, w, x, y, 0, n, k, s); }
+int dequant_gemv_q5sb_bf16(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(15, w, x, y, 0, n, k, s); }
+int dequant_gemv_q6sb_bf16(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(16, w, x, y, 0, n, k, s); }
 int dequant_gemm_q4g32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m, int64_t n,
                        int64_t k, void *s) {
   return qg_gemm(4, w, X, ldx, Y, ldy, 0, m, n, k, s);
@@ -952,6 +966,22 @@ int dequant_gemm_q4g32h(const void *w, const uint16_t *X, int64_t ldx, uint16_t 
                         int64_t k, void *s) {
   return qg_gemm(11, w, X, ldx, Y, ldy, 0, m, n, k, s);
 }
+int dequant_gemm_q2sb_bf16(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m, int64_t n,
+                            int64_t k, void *s) {
+  return qg_gemm(12, w, X, ldx, Y, ldy, 0, m, n, k, s);
+}
+int dequant_gemm_q3sb_bf16(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m, int64_t n,
+                            int64_t k, void *s) {
+  return qg_gemm(13, w, X, ldx, Y, ldy, 0, m, n, k, s);
+}
+int dequant_gemm_q5sb_bf16(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m, int64_t n,
+                            int64_t k, void *s) {
+  return qg_gemm(15, w, X, ldx, Y, ldy, 0, m, n, k, s);
+}
+int dequant_gemm_q6sb_bf16(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m, int64_t n,
+                            int64_t k, void *s) {
+  return qg_gemm(16, w, X, ldx, Y, ldy, 0, m, n, k, s);
+}
 
 int qg_dequantize(int fmt, const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream) {
   if (!fmt_valid(fmt)) return QG_ERR_FORMAT;
@@ -976,6 +1006,10 @@ int qg_dequantize(int fmt, const void *w, float *w_out, uint8_t *codes_out, int6
     case 9: return launch(dequant_kernel<9>, grid, block, 0, s, a, w_out, codes_out);
     case 10: return launch(dequant_kernel<10>, grid, block, 0, s, a, w_out, codes_out);
     case 11: return launch(dequant_kernel<11>, grid, block, 0, s, a, w_out, codes_out);
+    case 12: return launch(dequant_kernel<12>, grid, block, 0, s, a, w_out, codes_out);
+    case 13: return launch(dequant_kernel<13>, grid, block, 0, s, a, w_out, codes_out);
+    case 15: return launch(dequant_kernel<15>, grid, block, 0, s, a, w_out, codes_out);
+    case 16: return launch(dequant_kernel<16>, grid, block, 0, s, a, w_out, codes_out);
   }
   return QG_ERR_FORMAT;
 }
@@ -1002,5 +1036,9 @@ int dequantize_q4g64(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, 
 int dequantize_q4g128(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(9, w, o, c, n, k, s); }
 int dequantize_q4a32(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(10, w, o, c, n, k, s); }
 int dequantize_q4g32h(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(11, w, o, c, n, k, s); }
+int dequantize_q2sb_bf16(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(12, w, o, c, n, k, s); }
+int dequantize_q3sb_bf16(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(13, w, o, c, n, k, s); }
+int dequantize_q5sb_bf16(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(15, w, o, c, n, k, s); }
+int dequantize_q6sb_bf16(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(16, w, o, c, n, k, s); }
 
 }  // extern "C"

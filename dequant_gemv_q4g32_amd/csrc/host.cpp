@@ -69,6 +69,26 @@ bool half_rn(double v, uint16_t *bits) {
   return true;
 }
 
+// Smallest bfloat16 value >= v for finite v >= 0, as bits. Returns false on overflow.
+bool bf16_ceil(double v, uint16_t *bits) {
+  if (!(v >= 0.0) || !std::isfinite(v)) return false;
+  float f = (float)v;                                    // round to nearest
+  if ((double)f < v) f = std::nextafterf(f, INFINITY);
+  uint32_t u;
+  std::memcpy(&u, &f, 4);
+  if (u & 0xFFFFu) u = (u & 0xFFFF0000u) + 0x10000u;     // round the dropped half up
+  if ((u >> 16) >= 0x7F80u) return false;
+  *bits = (uint16_t)(u >> 16);
+  return true;
+}
+
+double bf16_to_double(uint16_t b) {
+  const uint32_t u = (uint32_t)b << 16;
+  float f;
+  std::memcpy(&f, &u, 4);
+  return (double)f;
+}
+
 // ---------------------------------------------------------------- bitstreams -------------
 
 void pack_le(const uint8_t *codes, int64_t count, int bits, uint8_t *out) {
@@ -98,19 +118,26 @@ inline uint16_t get_half(const uint8_t *p) { return (uint16_t)(p[0] | (p[1] << 8
 
 struct SB {
   int bits, nsub, sym, offset, smax, rec;
+  bool bf16 = false;                                     // super-scales stored as bf16
   int sub() const { return kQK / nsub; }
   int cmax() const { return (1 << bits) - 1; }
 };
 
 bool sb_spec(int fmt, SB *s) {
-  switch (fmt) {
-    case 2: *s = {2, 16, 0, 0, 15, 84}; return true;
-    case 3: *s = {3, 16, 1, 4, 63, 110}; return true;
-    case 5: *s = {5, 8, 0, 0, 63, 176}; return true;
-    case 6: *s = {6, 16, 1, 32, 127, 210}; return true;
+  switch (sb_base(fmt)) {
+    case 2: *s = {2, 16, 0, 0, 15, 84}; break;
+    case 3: *s = {3, 16, 1, 4, 63, 110}; break;
+    case 5: *s = {5, 8, 0, 0, 63, 176}; break;
+    case 6: *s = {6, 16, 1, 32, 127, 210}; break;
     default: return false;
   }
+  s->bf16 = sb_bf16(fmt);
+  return true;
 }
+
+// Super-scale rounding and decoding in the format's 16-bit type (fp16, or bf16).
+bool scale_ceil(const SB &s, double v, uint16_t *bits) { return s.bf16 ? bf16_ceil(v, bits) : half_ceil(v, bits); }
+double scale_value(const SB &s, uint16_t bits) { return s.bf16 ? bf16_to_double(bits) : half_to_double(bits); }
 
 // ---------------------------------------------------------------- quantizers -------------
 
@@ -222,8 +249,8 @@ int quantize_block_sb(const SB &s, int fmt, const float *w, uint8_t *rec) {
     }
     double d = 0.0;
     if (T != 0.0) {
-      if (!half_ceil(T / s.smax, &dbits)) return QG_ERR_RANGE;
-      d = half_to_double(dbits);
+      if (!scale_ceil(s, T / s.smax, &dbits)) return QG_ERR_RANGE;
+      d = scale_value(s, dbits);
       for (int j = 0; j < nsub; ++j) sc[j] = (int)std::min((double)s.smax, std::ceil(t[j] / d));
     }
     for (int j = 0; j < nsub; ++j) {
@@ -251,8 +278,8 @@ int quantize_block_sb(const SB &s, int fmt, const float *w, uint8_t *rec) {
     }
     double dmin = 0.0;
     if (L != 0.0) {
-      if (!half_ceil(L / s.smax, &dminbits)) return QG_ERR_RANGE;
-      dmin = half_to_double(dminbits);
+      if (!scale_ceil(s, L / s.smax, &dminbits)) return QG_ERR_RANGE;
+      dmin = scale_value(s, dminbits);
       for (int j = 0; j < nsub; ++j) m[j] = (int)std::min((double)s.smax, std::ceil(-lo[j] / dmin));
     }
     double T = 0.0;
@@ -263,8 +290,8 @@ int quantize_block_sb(const SB &s, int fmt, const float *w, uint8_t *rec) {
     }
     double d = 0.0;
     if (T != 0.0) {
-      if (!half_ceil(T / s.smax, &dbits)) return QG_ERR_RANGE;
-      d = half_to_double(dbits);
+      if (!scale_ceil(s, T / s.smax, &dbits)) return QG_ERR_RANGE;
+      d = scale_value(s, dbits);
       for (int j = 0; j < nsub; ++j) sc[j] = (int)std::min((double)s.smax, std::ceil(t[j] / d));
     }
     for (int j = 0; j < nsub; ++j) {
@@ -599,7 +626,7 @@ const char *qg_strerror(int status) {
     case QG_ERR_SHAPE: return "n, k or m out of range (k must be a multiple of 256 for the super-block formats, of 32 for q4g32, 64 for q4g16, q4g64, q4a32 and q4g32h, 128 for q4g128)";
     case QG_ERR_ALIGN: return "misaligned device pointer or leading dimension";
     case QG_ERR_NONFINITE: return "a weight is NaN or infinite";
-    case QG_ERR_RANGE: return "a super-block or fp16 group scale does not fit fp16, or a code does not fit its width";
+    case QG_ERR_RANGE: return "a super-block scale does not fit fp16 (or bf16), or an fp16 group scale overflows, or a code does not fit its width";
     case QG_ERR_FORMAT: return "unknown format or bit width";
     case QG_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
     case QG_ERR_DEVICE: return "no usable gfx950 device or HIP runtime error";
@@ -692,7 +719,7 @@ int qg_quantize(int fmt, const float *w, int64_t n, int64_t k, int64_t ldw, uint
   return parallel_rows(n, k, [&](int64_t r0, int64_t r1) {
     for (int64_t r = r0; r < r1; ++r)
       for (int64_t b = 0; b < S; ++b) {
-        int st = quantize_block_sb(s, fmt, w + r * ldw + b * kQK, canonical + (r * S + b) * s.rec);
+        int st = quantize_block_sb(s, sb_base(fmt), w + r * ldw + b * kQK, canonical + (r * S + b) * s.rec);
         if (st != QG_OK) return st;
       }
     return (int)QG_OK;
@@ -705,6 +732,10 @@ int quantize_q4g64(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c
 int quantize_q4g128(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(9, w, n, k, ldw, c); }
 int quantize_q4a32(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(10, w, n, k, ldw, c); }
 int quantize_q4g32h(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(11, w, n, k, ldw, c); }
+int quantize_q2sb_bf16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(12, w, n, k, ldw, c); }
+int quantize_q3sb_bf16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(13, w, n, k, ldw, c); }
+int quantize_q5sb_bf16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(15, w, n, k, ldw, c); }
+int quantize_q6sb_bf16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(16, w, n, k, ldw, c); }
 int quantize_q2sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(2, w, n, k, ldw, c); }
 int quantize_q3sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(3, w, n, k, ldw, c); }
 int quantize_q5sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(5, w, n, k, ldw, c); }
@@ -724,7 +755,7 @@ int qg_to_device_layout(int fmt, const uint8_t *canonical, int64_t n, int64_t k,
     P.rb[p] = L.plane_row_bytes[p];
   }
   return parallel_rows(n, k * 4, [&](int64_t r0, int64_t r1) {
-    for (int64_t r = r0; r < r1; ++r) row_to_device(fmt, canonical, k, r, n, P);
+    for (int64_t r = r0; r < r1; ++r) row_to_device(sb_base(fmt), canonical, k, r, n, P);
     return (int)QG_OK;
   });
 }
@@ -743,7 +774,7 @@ int qg_from_device_layout(int fmt, const uint8_t *dev, int64_t n, int64_t k, uin
     rb[p] = L.plane_row_bytes[p];
   }
   return parallel_rows(n, k * 4, [&](int64_t r0, int64_t r1) {
-    for (int64_t r = r0; r < r1; ++r) row_from_device(fmt, pl, rb, k, r, n, canonical);
+    for (int64_t r = r0; r < r1; ++r) row_from_device(sb_base(fmt), pl, rb, k, r, n, canonical);
     return (int)QG_OK;
   });
 }

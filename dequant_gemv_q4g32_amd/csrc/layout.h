@@ -90,7 +90,15 @@ QG_HOST_DEVICE constexpr int q4_group(int fmt) { return fmt == 4 ? 32 : fmt == 7
 constexpr int kQ4A32 = 10;
 constexpr int kQ4G32H = 11;
 
-inline bool fmt_valid(int fmt) { return (fmt >= 2 && fmt <= 6) || q4_group(fmt) != 0 || fmt == kQ4A32 || fmt == kQ4G32H; }
+// Super-block formats with bf16 super-scales d (and dmin): the base format's code + 10
+// (12, 13, 15, 16 for q2sb, q3sb, q5sb, q6sb). Same records, planes and kernels as the base
+// format; only the 16-bit super-scale fields hold bf16 instead of fp16.
+QG_HOST_DEVICE constexpr bool sb_bf16(int fmt) { return fmt == 12 || fmt == 13 || fmt == 15 || fmt == 16; }
+QG_HOST_DEVICE constexpr int sb_base(int fmt) { return sb_bf16(fmt) ? fmt - 10 : fmt; }
+
+inline bool fmt_valid(int fmt) {
+  return (fmt >= 2 && fmt <= 6) || q4_group(fmt) != 0 || fmt == kQ4A32 || fmt == kQ4G32H || sb_bf16(fmt);
+}
 
 // K must be a multiple of this: 32 for q4g32 (a row may end in half a unit), whole units
 // (64) for q4g16, q4g64, q4a32 and q4g32h, 128 for q4g128, a super-block (256) for the
@@ -102,7 +110,7 @@ inline int64_t k_multiple(int fmt) {
 }
 
 inline FmtPlanes fmt_planes(int fmt) {
-  switch (fmt) {
+  switch (sb_base(fmt)) {
     case 4: return {2, {32, 8, 0, 0}, {0, 0, 0, 0}};          // codes, fp32 scales
     case 2: return {3, {16, 4, 0, 0}, {0, 0, 4, 0}};          // codes, sc|m, (d, dmin)
     case 3: return {4, {16, 8, 0, 0}, {0, 0, 12, 2}};         // codes A, codes B, sc, d

@@ -234,6 +234,10 @@ int launch_prefill(int fmt, const void *w, const uint16_t *X, int64_t ldx, void 
     case 9: return launch(prefill_kernel<9>, grid, block, 0, s, a);
     case 10: return launch(prefill_kernel<10>, grid, block, 0, s, a);
     case 11: return launch(prefill_kernel<11>, grid, block, 0, s, a);
+    case 12: return launch(prefill_kernel<12>, grid, block, 0, s, a);
+    case 13: return launch(prefill_kernel<13>, grid, block, 0, s, a);
+    case 15: return launch(prefill_kernel<15>, grid, block, 0, s, a);
+    case 16: return launch(prefill_kernel<16>, grid, block, 0, s, a);
   }
   return QG_ERR_FORMAT;
 }

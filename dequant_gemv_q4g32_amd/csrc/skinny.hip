@@ -210,6 +210,10 @@ int launch_skinny(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *
     case 9: return launch(skinny_kernel<9>, grid, block, shm, s, a);
     case 10: return launch(skinny_kernel<10>, grid, block, shm, s, a);
     case 11: return launch(skinny_kernel<11>, grid, block, shm, s, a);
+    case 12: return launch(skinny_kernel<12>, grid, block, shm, s, a);
+    case 13: return launch(skinny_kernel<13>, grid, block, shm, s, a);
+    case 15: return launch(skinny_kernel<15>, grid, block, shm, s, a);
+    case 16: return launch(skinny_kernel<16>, grid, block, shm, s, a);
   }
   return QG_ERR_FORMAT;
 }

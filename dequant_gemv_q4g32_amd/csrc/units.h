@@ -71,6 +71,21 @@ __device__ __forceinline__ uint32_t asym_pair(uint32_t P, float mul, float add) 
 
 template <int F> struct Unit;
 
+// Super-scales d, dmin of the super-block formats: fp16 bits, or bf16 bits (the upper half of
+// an fp32) in the "_bf16" variants; both widen to fp32 exactly.
+template <bool BF> __device__ __forceinline__ float ss_lo(uint32_t v) {
+  if constexpr (BF) return __builtin_bit_cast(float, v << 16);
+  else return half_lo(v);
+}
+template <bool BF> __device__ __forceinline__ float ss_hi(uint32_t v) {
+  if constexpr (BF) return __builtin_bit_cast(float, v & 0xFFFF0000u);
+  else return half_hi(v);
+}
+template <bool BF> __device__ __forceinline__ float ss_one(uint16_t v) {
+  if constexpr (BF) return __builtin_bit_cast(float, (uint32_t)v << 16);
+  else return half_bits(v);
+}
+
 // ---- INT4 groups of G = 16, 32, 64 or 128 weights, one fp32 scale each. A unit (64
 // weights, 8 code dwords; dword i holds weights 8i..8i+7) spans 64 / G groups, or half a
 // group of 128. With S = 2 a lane owns half a unit (4 dwords, loaded alone). The lane's
@@ -335,7 +350,7 @@ template <> struct Unit<kQ4A32> {
 // ---- 2-bit super-block: a unit is a quarter super-block (4 sub-blocks of 16). Sub-block j
 // sits at class 4^j in every dword; with S = 2 lane half h owns dwords 2h, 2h+1, i.e. pairs
 // r = 4h..4h+3 of every sub-block.
-template <> struct Unit<2> {
+template <bool BF> struct UnitQ2 {
   static constexpr int NK = 4;
   __host__ __device__ static constexpr int NKS(int) { return 4; }  // every half meets all 4 sub-blocks
   struct Raw { u32x4 c; uint32_t sc, dd; };
@@ -391,7 +406,7 @@ template <> struct Unit<2> {
     }
     const uint32_t s = q.sc;
     const float inv4[4] = {1.0f, 0.25f, 0.0625f, 0.015625f};
-    const float dv = half_lo(q.dd), dm = half_hi(q.dd);
+    const float dv = ss_lo<BF>(q.dd), dm = ss_hi<BF>(q.dd);
     float scj[4], cj[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -414,7 +429,7 @@ template <> struct Unit<2> {
   template <int S = 1> __device__ static void wide(const Raw &q, int h, uint32_t *out) {
     const uint32_t d[4] = {q.c.x, q.c.y, q.c.z, q.c.w};
     const float inv4[4] = {1.0f, 0.25f, 0.0625f, 0.015625f};
-    const float dv = half_lo(q.dd), dm = half_hi(q.dd);
+    const float dv = ss_lo<BF>(q.dd), dm = ss_hi<BF>(q.dd);
     float mul[4], add[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
@@ -432,10 +447,12 @@ template <> struct Unit<2> {
     }
   }
 };
+template <> struct Unit<2> : UnitQ2<false> {};
+template <> struct Unit<12> : UnitQ2<true> {};
 
 // ---- 3-bit super-block: a unit is two chunks of 32 codes (sub-blocks a, b each); with S = 2
 // lane half h owns chunk h.
-template <> struct Unit<3> {
+template <bool BF> struct UnitQ3 {
   static constexpr int NK = 4;
   __host__ __device__ static constexpr int NKS(int S) { return NK / S; }
   struct Raw { u32x4 a; u32x2 b; uint32_t f; uint16_t d; };
@@ -513,7 +530,7 @@ template <> struct Unit<3> {
   template <int M, int S>
   __device__ static void dot(const Raw &q, int h, const uint32_t (*xp)[32 / S], const float (*kc)[NKS(S)], float *out) {
     const uint32_t f = q.f;
-    const float dv = half_bits(q.d);
+    const float dv = ss_one<BF>(q.d);
     if constexpr (S == 1) {
       uint32_t P0[16], P1[16];
       chunk_pairs(q.a.x, q.a.y, q.a.z, P0);
@@ -550,7 +567,7 @@ template <> struct Unit<3> {
     uint32_t P[16];
     chunk_pairs(sel(h, q.a.w, q.a.x), sel(h, q.b.x, q.a.y), sel(h, q.b.y, q.a.z), P);
     const uint32_t fh = q.f >> (12 * h);
-    const float dv = half_bits(q.d);
+    const float dv = ss_one<BF>(q.d);
     const float sa = dv * (float)(fh & 63u), sb = dv * (float)((fh >> 6) & 63u);
     const _Float16 a1 = (_Float16)sa, a8 = (_Float16)(sa * 0.125f);
     const _Float16 b8 = (_Float16)(sb * 0.125f), b64 = (_Float16)(sb * 0.015625f);
@@ -564,6 +581,8 @@ template <> struct Unit<3> {
     for (int r = 12; r < 16; ++r) out[r] = sym_pair(P[r], (_Float16)-1280.0f, b64);
   }
 };
+template <> struct Unit<3> : UnitQ3<false> {};
+template <> struct Unit<13> : UnitQ3<true> {};
 
 // ---- nibble plane + high-bit plane (q5sb: 1 high bit, 32-weight sub-blocks;
 //      q6sb: 2 high bits, 16-weight sub-blocks). Produces the four pairs of one nibble dword.
@@ -581,7 +600,7 @@ __device__ __forceinline__ void nib_pairs(uint32_t L, uint32_t H, int ip, uint32
 }
 
 // ---- 5-bit super-block: a unit is two sub-blocks of 32; with S = 2 lane half h owns one
-template <> struct Unit<5> {
+template <bool BF> struct UnitQ5 {
   static constexpr int NK = 4;
   __host__ __device__ static constexpr int NKS(int S) { return NK / S; }
   struct Raw { u32x4 l0, l1; u32x2 h; uint32_t f, dd; };
@@ -625,7 +644,7 @@ template <> struct Unit<5> {
     const uint32_t L[8] = {q.l0.x, q.l0.y, q.l0.z, q.l0.w, S == 1 ? q.l1.x : 0u, S == 1 ? q.l1.y : 0u,
                            S == 1 ? q.l1.z : 0u, S == 1 ? q.l1.w : 0u};
     const uint32_t f = q.f;
-    const float dv = half_lo(q.dd), dm = half_hi(q.dd);
+    const float dv = ss_lo<BF>(q.dd), dm = ss_hi<BF>(q.dd);
 #pragma unroll
     for (int hh = 0; hh < 2 / S; ++hh) {
       const int sb = S == 1 ? hh : 0;     // sub-block within what this lane owns
@@ -661,7 +680,7 @@ template <> struct Unit<5> {
     const uint32_t L[8] = {q.l0.x, q.l0.y, q.l0.z, q.l0.w, S == 1 ? q.l1.x : 0u, S == 1 ? q.l1.y : 0u,
                            S == 1 ? q.l1.z : 0u, S == 1 ? q.l1.w : 0u};
     const uint32_t H = S == 1 ? sel(h, q.h.y, q.h.x) : q.h.x;
-    const float dv = half_lo(q.dd), dm = half_hi(q.dd);
+    const float dv = ss_lo<BF>(q.dd), dm = ss_hi<BF>(q.dd);
     const float step = dv * (float)((q.f >> (6 * h)) & 63u), off = dm * (float)((q.f >> (12 + 6 * h)) & 63u);
     const float mul1 = step, add1 = -__builtin_fmaf(1024.0f, step, off);
     const float mul16 = step * 0.0625f, add16 = -__builtin_fmaf(64.0f, step, off);
@@ -676,10 +695,12 @@ template <> struct Unit<5> {
     }
   }
 };
+template <> struct Unit<5> : UnitQ5<false> {};
+template <> struct Unit<15> : UnitQ5<true> {};
 
 // ---- 6-bit super-block: a unit is four sub-blocks of 16; with S = 2 lane half h owns
 // sub-blocks 2h, 2h+1
-template <> struct Unit<6> {
+template <bool BF> struct UnitQ6 {
   static constexpr int NK = 4;
   __host__ __device__ static constexpr int NKS(int S) { return NK / S; }
   struct Raw { u32x4 l0, l1, h; uint32_t sc; uint16_t d; };
@@ -724,7 +745,7 @@ template <> struct Unit<6> {
     const uint32_t L[8] = {q.l0.x, q.l0.y, q.l0.z, q.l0.w, S == 1 ? q.l1.x : 0u, S == 1 ? q.l1.y : 0u,
                            S == 1 ? q.l1.z : 0u, S == 1 ? q.l1.w : 0u};
     const uint32_t Hd[4] = {q.h.x, q.h.y, S == 1 ? q.h.z : 0u, S == 1 ? q.h.w : 0u};
-    const float dv = half_bits(q.d);
+    const float dv = ss_one<BF>(q.d);
 #pragma unroll
     for (int j = 0; j < 4 / S; ++j) {
       float a1[M], a16[M];
@@ -755,7 +776,7 @@ template <> struct Unit<6> {
     const uint32_t L[8] = {q.l0.x, q.l0.y, q.l0.z, q.l0.w, S == 1 ? q.l1.x : 0u, S == 1 ? q.l1.y : 0u,
                            S == 1 ? q.l1.z : 0u, S == 1 ? q.l1.w : 0u};
     const uint32_t Hd[4] = {q.h.x, q.h.y, S == 1 ? q.h.z : 0u, S == 1 ? q.h.w : 0u};
-    const float dv = half_bits(q.d);
+    const float dv = ss_one<BF>(q.d);
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const float step = dv * (float)(int8_t)((q.sc >> (8 * (2 * h + j))) & 0xFFu);
@@ -773,5 +794,7 @@ template <> struct Unit<6> {
     }
   }
 };
+template <> struct Unit<6> : UnitQ6<false> {};
+template <> struct Unit<16> : UnitQ6<true> {};
 
 }  // namespace qg

@@ -30,6 +30,12 @@
  *             m, fp16 d and dmin: w_hat = d*sc*c - dmin*m  (176 B, 5.5 bpw).
  *   QG_Q6SB   16 sub-blocks of 16, 6-bit codes (low-4-bit plane + high-2-bit plane), int8 sc,
  *             fp16 d: w_hat = d*sc*(c - 32)  (210 B, 6.5625 bpw).
+ *   QG_Q2SB_BF16, QG_Q3SB_BF16, QG_Q5SB_BF16, QG_Q6SB_BF16  the same four formats with the
+ *             super-scales d (and dmin) stored as bf16 instead of fp16 ("二三五六位量化" page
+ *             section 2.3: against fp16 overflow of the super-scale); same records and sizes,
+ *             bf16_ceil in place of fp16_ceil in the rule below. The GEMM paths for m > 8
+ *             multiply fp16 W_hat on the matrix cores: weights beyond the fp16 range (which
+ *             only bf16 super-scales can express) need m <= 8 there.
  *
  * Super-block scales are chosen by "range-covering round to nearest" (the pages give the
  * layouts, not the rule): with fp16_ceil(v) = smallest fp16 >= v, symmetric formats take
@@ -87,7 +93,11 @@ typedef enum qg_format {
   QG_Q4G64 = 8,
   QG_Q4G128 = 9,
   QG_Q4A32 = 10,
-  QG_Q4G32H = 11
+  QG_Q4G32H = 11,
+  QG_Q2SB_BF16 = 12,
+  QG_Q3SB_BF16 = 13,
+  QG_Q5SB_BF16 = 15,
+  QG_Q6SB_BF16 = 16
 } qg_format;
 
 typedef enum qg_status {
@@ -151,6 +161,10 @@ int quantize_q4g64(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c
 int quantize_q4g128(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
 int quantize_q4a32(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
 int quantize_q4g32h(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
+int quantize_q2sb_bf16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
+int quantize_q3sb_bf16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
+int quantize_q5sb_bf16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
+int quantize_q6sb_bf16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
 
 /* Canonical encoding (host) -> device layout (host buffer of qg_device_layout().total_bytes;
  * padding is zeroed). A pure bit permutation. */
@@ -176,6 +190,10 @@ int dequant_gemv_q4g64(const void *w, const uint16_t *x, uint16_t *y, int64_t n,
 int dequant_gemv_q4g128(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
 int dequant_gemv_q4a32(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
 int dequant_gemv_q4g32h(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
+int dequant_gemv_q2sb_bf16(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
+int dequant_gemv_q3sb_bf16(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
+int dequant_gemv_q5sb_bf16(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
+int dequant_gemv_q6sb_bf16(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
 
 /* Generic form: y_f32 != 0 writes fp32 y (4-byte aligned) instead of fp16. */
 int qg_gemv(int fmt, const void *w, const uint16_t *x, void *y, int y_f32, int64_t n, int64_t k, void *stream);
@@ -221,6 +239,14 @@ int dequant_gemm_q4a32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *
                        int64_t m, int64_t n, int64_t k, void *stream);
 int dequant_gemm_q4g32h(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
                         int64_t m, int64_t n, int64_t k, void *stream);
+int dequant_gemm_q2sb_bf16(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
+                            int64_t m, int64_t n, int64_t k, void *stream);
+int dequant_gemm_q3sb_bf16(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
+                            int64_t m, int64_t n, int64_t k, void *stream);
+int dequant_gemm_q5sb_bf16(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
+                            int64_t m, int64_t n, int64_t k, void *stream);
+int dequant_gemm_q6sb_bf16(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
+                            int64_t m, int64_t n, int64_t k, void *stream);
 /* Generic form; y_f32 != 0 writes fp32 Y (4-byte aligned). */
 int qg_gemm(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int64_t ldy, int y_f32,
             int64_t m, int64_t n, int64_t k, void *stream);
@@ -286,6 +312,10 @@ int dequantize_q4g64(const void *w, float *w_out, uint8_t *codes_out, int64_t n,
 int dequantize_q4g128(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 int dequantize_q4a32(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 int dequantize_q4g32h(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
+int dequantize_q2sb_bf16(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
+int dequantize_q3sb_bf16(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
+int dequantize_q5sb_bf16(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
+int dequantize_q6sb_bf16(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 int qg_dequantize(int fmt, const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 
 /* ---- measurement (device) -----------------------------------------------------------------

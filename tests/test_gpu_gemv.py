@@ -14,7 +14,8 @@ from workloads import WORKLOADS, activations, laplace_weights
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb", "q4g16", "q4g64", "q4g128", "q4a32", "q4g32h"]
+FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb", "q4g16", "q4g64", "q4g128", "q4a32", "q4g32h",
+        "q2sb_bf16", "q3sb_bf16", "q5sb_bf16", "q6sb_bf16"]
 # (n, k): several tiles, ragged n, K split over 1, 2, 3 and 7 waves
 SHAPES = [(37, 512), (16, 256), (1001, 1024), (64, 4096), (20, 4352), (9, 8192), (33, 11008), (5, 28672)]
 
@@ -181,3 +182,25 @@ def test_q4a32_zero_points_over_their_range():
         y_ref, bound = oracle_y(w_hat, x)
         y = qg.gemm("q4a32", wd, torch.from_numpy(x).cuda(), n, k, out_f32=True)
         assert_close(y.cpu().numpy(), y_ref, bound, f"q4a32 m={m}")
+
+
+@pytest.mark.parametrize("fmt", ["q2sb_bf16", "q3sb_bf16", "q5sb_bf16", "q6sb_bf16"])
+def test_bf16_super_scales_past_the_fp16_range(fmt):
+    """bf16 super-scales: rows with super-blocks whose scale would overflow fp16 (weights of
+    order 1e8) beside ordinary ones; decode bit-exact, outputs (fp32) within the tolerance
+    for 1, 4 and 8 activation rows (the streaming kernel: the matrix-core paths for more rows
+    take W_hat through fp16, whose range such weights exceed)."""
+    n, k = 40, 1024
+    w = laplace_weights(n, k, 0.02, 77)
+    w[3, 300] = np.float32(2.0e8)
+    w[17, 5:40] *= np.float32(3.0e9)
+    codes_ref, w_hat = oracle_decode(fmt, w)
+    wd = device_weights(fmt, w)
+    vals, codes = qg.dequantize(fmt, wd, n, k)
+    assert np.array_equal(codes.cpu().numpy(), codes_ref)
+    assert np.array_equal(vals.cpu().numpy(), w_hat.astype(np.float32))
+    for m in (1, 4, 8):
+        x = _x(k, 78 + m, m)
+        y_ref, bound = oracle_y(w_hat, x)
+        y = qg.gemm(fmt, wd, torch.from_numpy(x).cuda(), n, k, out_f32=True)
+        assert_close(y.cpu().numpy(), y_ref, bound, f"{fmt} m={m}")
