@@ -269,11 +269,11 @@ def extra_configs(qg, dev):
             log(f"[bench] {fmt} 70B layer set m={m}: {out[f'{fmt}_70b_layer_set_m{m}']}")
         del cs
     del w70
-    # INT4 group sizes (16, 32, 64, 128), asymmetric groups of 32, fp16-scale groups of 32 and
-    # the bf16 super-scale variants of q3sb and q5sb on the 70B-like set at batch 1, one
-    # launch per matrix
+    # INT4 group sizes (16, 32, 64, 128), asymmetric groups of 32, fp16-scale groups of 32, the
+    # bf16 super-scale variants of q3sb and q5sb, and plain group-wise 3- and 5-bit codes on
+    # the 70B-like set at batch 1, one launch per matrix
     w70 = [WORKLOADS["q3sb_70b_layer_set_m1"].weights(i) for i in range(3)]
-    for fmt in ("q4g16", "q4g32", "q4g64", "q4g128", "q4a32", "q4g32h", "q3sb_bf16", "q5sb_bf16"):
+    for fmt in ("q4g16", "q4g32", "q4g64", "q4g128", "q4a32", "q4g32h", "q3sb_bf16", "q5sb_bf16", "q3g32", "q5g32"):
         cs = [(qg.quantize(fmt, w), w.shape[0], w.shape[1]) for w in w70]
         alg, us = measure_set(qg, fmt, cs, 1, dev, [("single", [0]), ("single", [1]), ("single", [2])], rounds=12)
         out[f"{fmt}_70b_layer_set_m1"] = {**_rate(alg, us), "bytes_per_set": alg}

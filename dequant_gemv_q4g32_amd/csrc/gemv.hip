@@ -323,6 +323,19 @@ __device__ __forceinline__ uint32_t load_fields24(const uint8_t *sb12, int q) {
 // One thread per (row, unit): decodes 64 codes from the device layout by the same bit
 // placement the GEMV kernels use and writes logical-order codes and fp32 W_hat.
 
+// Group-wise formats: w_hat = s * c + m (one rounding), group = the unit's half
+__device__ void gw_values(const GemvArgs &a, const uint8_t *w, int64_t r, int64_t u, const uint8_t *c, uint8_t *codes,
+                          float *vals) {
+  const uint8_t *ps = w + a.poff[2] + r * a.prb[2] + u * 8;
+  const uint8_t *pm = w + a.poff[3] + r * a.prb[3] + u * 8;
+  for (int k = 0; k < 64; ++k) {
+    const int g = k >> 5;
+    codes[k] = c[k];
+    vals[k] = __builtin_fmaf(__builtin_bit_cast(float, ld1(ps + 4 * g)), (float)c[k],
+                             __builtin_bit_cast(float, ld1(pm + 4 * g)));
+  }
+}
+
 template <int F>
 __device__ void decode_unit(const GemvArgs &a, const uint8_t *w, int64_t r, int64_t u, uint8_t *codes, float *vals,
                             int nvalid) {
@@ -372,7 +385,7 @@ __device__ void decode_unit(const GemvArgs &a, const uint8_t *w, int64_t r, int6
     }
     return;
   }
-  constexpr int B = sb_base(F);
+  constexpr int B = F == kQ3G32 ? 3 : F == kQ5G32 ? 5 : sb_base(F);   // code placement
   constexpr bool BF = sb_bf16(F);
   if (B == 2) {
     const uint8_t *pc = w + a.poff[0] + r * a.prb[0] + u * 16;
@@ -416,6 +429,10 @@ __device__ void decode_unit(const GemvArgs &a, const uint8_t *w, int64_t r, int6
       }
       c[k] = (uint8_t)v;
     }
+    if constexpr (F == kQ3G32) {
+      gw_values(a, w, r, u, c, codes, vals);
+      return;
+    }
     uint32_t f = load_fields24(w + a.poff[2] + r * a.prb[2] + (u >> 2) * 12, (int)(u & 3));
     float dv = ss_one<BF>(ldh(w + a.poff[3] + r * a.prb[3] + (u >> 2) * 2));
     for (int k = 0; k < 64; ++k) {
@@ -439,6 +456,10 @@ __device__ void decode_unit(const GemvArgs &a, const uint8_t *w, int64_t r, int6
     if (B == 5) hi = (H[i >> 2] >> ((base[pk] + 16 * h + (i & 3)) & 31)) & 1u;
     else hi = (H[i >> 1] >> ((base[pk] + 16 * h + 2 * (i & 1)) & 31)) & 3u;
     c[k] = (uint8_t)(lo | (hi << 4));
+  }
+  if constexpr (F == kQ5G32) {
+    gw_values(a, w, r, u, c, codes, vals);
+    return;
   }
   if (B == 5) {
     uint32_t f = load_fields24(w + a.poff[2] + r * a.prb[2] + (u >> 2) * 12, (int)(u & 3));
@@ -735,6 +756,8 @@ int launch_mv_fmt(int fmt, GemvArgs a, int64_t count, hipStream_t s) {
     case 13: return launch_mv_f<13>(a, count, s);
     case 15: return launch_mv_f<15>(a, count, s);
     case 16: return launch_mv_f<16>(a, count, s);
+    case 17: return launch_mv_f<17>(a, count, s);
+    case 18: return launch_mv_f<18>(a, count, s);
   }
   return QG_ERR_FORMAT;
 }
@@ -755,6 +778,8 @@ int launch_mv_group_fmt(int fmt, GemvGroup &G, hipStream_t s) {
     case 13: return launch_mv_group_f<13>(G, s);
     case 15: return launch_mv_group_f<15>(G, s);
     case 16: return launch_mv_group_f<16>(G, s);
+    case 17: return launch_mv_group_f<17>(G, s);
+    case 18: return launch_mv_group_f<18>(G, s);
   }
   return QG_ERR_FORMAT;
 }
@@ -926,6 +951,8 @@ int dequant_gemv_q2sb_bf16(const void *w, const uint16_t *x, uint16_t *y, int64_
 int dequant_gemv_q3sb_bf16(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(13, w, x, y, 0, n, k, s); }
 int dequant_gemv_q5sb_bf16(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(15, w, x, y, 0, n, k, s); }
 int dequant_gemv_q6sb_bf16(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(16, w, x, y, 0, n, k, s); }
+int dequant_gemv_q3g32(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(17, w, x, y, 0, n, k, s); }
+int dequant_gemv_q5g32(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(18, w, x, y, 0, n, k, s); }
 int dequant_gemm_q4g32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m, int64_t n,
                        int64_t k, void *s) {
   return qg_gemm(4, w, X, ldx, Y, ldy, 0, m, n, k, s);
@@ -982,6 +1009,14 @@ int dequant_gemm_q6sb_bf16(const void *w, const uint16_t *X, int64_t ldx, uint16
                             int64_t k, void *s) {
   return qg_gemm(16, w, X, ldx, Y, ldy, 0, m, n, k, s);
 }
+int dequant_gemm_q3g32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m, int64_t n,
+                        int64_t k, void *s) {
+  return qg_gemm(17, w, X, ldx, Y, ldy, 0, m, n, k, s);
+}
+int dequant_gemm_q5g32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m, int64_t n,
+                        int64_t k, void *s) {
+  return qg_gemm(18, w, X, ldx, Y, ldy, 0, m, n, k, s);
+}
 
 int qg_dequantize(int fmt, const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream) {
   if (!fmt_valid(fmt)) return QG_ERR_FORMAT;
@@ -1010,6 +1045,8 @@ int qg_dequantize(int fmt, const void *w, float *w_out, uint8_t *codes_out, int6
     case 13: return launch(dequant_kernel<13>, grid, block, 0, s, a, w_out, codes_out);
     case 15: return launch(dequant_kernel<15>, grid, block, 0, s, a, w_out, codes_out);
     case 16: return launch(dequant_kernel<16>, grid, block, 0, s, a, w_out, codes_out);
+    case 17: return launch(dequant_kernel<17>, grid, block, 0, s, a, w_out, codes_out);
+    case 18: return launch(dequant_kernel<18>, grid, block, 0, s, a, w_out, codes_out);
   }
   return QG_ERR_FORMAT;
 }
@@ -1040,5 +1077,7 @@ int dequantize_q2sb_bf16(const void *w, float *o, uint8_t *c, int64_t n, int64_t
 int dequantize_q3sb_bf16(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(13, w, o, c, n, k, s); }
 int dequantize_q5sb_bf16(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(15, w, o, c, n, k, s); }
 int dequantize_q6sb_bf16(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(16, w, o, c, n, k, s); }
+int dequantize_q3g32(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(17, w, o, c, n, k, s); }
+int dequantize_q5g32(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(18, w, o, c, n, k, s); }
 
 }  // extern "C"

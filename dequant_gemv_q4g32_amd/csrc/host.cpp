@@ -169,6 +169,37 @@ int quantize_row_q4(const float *w, int64_t k, int G, uint8_t *codes, float *sca
   return QG_OK;
 }
 
+// One row of plain group-wise b-bit codes (b = 3 or 5) with an fp32 scale and min per group
+// of 32: m = min w, s = max((max w - min w) / (2^b - 1), 1e-12), c = clamp(rint((w - m) / s),
+// 0, 2^b - 1), the difference and the quotient in fp32; codes packed as one little-endian
+// bitstream (k*b/8 bytes).
+int quantize_row_gw(const float *w, int64_t k, int b, uint8_t *codes, float *scales, float *mins) {
+  const int qmax = (1 << b) - 1;
+  std::vector<uint8_t> c((size_t)k);
+  for (int64_t g = 0; g < k / 32; ++g) {
+    const float *v = w + g * 32;
+    float lo = v[0], hi = v[0];
+    for (int i = 0; i < 32; ++i) {
+      if (!std::isfinite(v[i])) return QG_ERR_NONFINITE;
+      if (v[i] < lo) lo = v[i];
+      if (v[i] > hi) hi = v[i];
+    }
+    float scale = (hi - lo) / (float)qmax;
+    if (!std::isfinite(scale)) return QG_ERR_RANGE;
+    if (scale < 1e-12f) scale = 1e-12f;
+    scales[g] = scale;
+    mins[g] = lo;
+    for (int i = 0; i < 32; ++i) {
+      const float diff = v[i] - lo;
+      float q = std::nearbyint(diff / scale);
+      q = std::min((float)qmax, std::max(0.0f, q));
+      c[(size_t)(g * 32 + i)] = (uint8_t)q;
+    }
+  }
+  pack_le(c.data(), k, b, codes);
+  return QG_OK;
+}
+
 // One INT4 row with fp16 group scales (groups of 32): the INT4 rule with the scale
 // max|w| / 8 (fp32) rounded to the nearest fp16 (0 raised to 2^-24), the codes taken
 // against that stored scale.
@@ -436,6 +467,15 @@ void row_to_device(int fmt, const uint8_t *canon, int64_t k, int64_t r, int64_t 
     }
     return;
   }
+  int pf = fmt;                                         // code placement: a super-block format
+  if (gw_bits(fmt)) {
+    const int b = gw_bits(fmt);
+    unpack_le(canon + r * (k * b / 8), k, b, codes.data());
+    const uint8_t *meta = canon + n * (k * b / 8);        // scales [n][k/32], then mins
+    std::memcpy(P.p[2] + r * P.rb[2], meta + r * (k / 32) * 4, (size_t)(k / 32) * 4);
+    std::memcpy(P.p[3] + r * P.rb[3], meta + n * (k / 32) * 4 + r * (k / 32) * 4, (size_t)(k / 32) * 4);
+    pf = b == 3 ? 3 : 5;
+  } else {
   SB s;
   sb_spec(fmt, &s);
   const int64_t S = k / kQK;
@@ -474,27 +514,28 @@ void row_to_device(int fmt, const uint8_t *canon, int64_t k, int64_t r, int64_t 
       std::memcpy(P.p[3] + r * P.rb[3] + sbi * 2, rec + 208, 2);
     }
   }
+  }
   FmtPlanes fp = fmt_planes(fmt);
   for (int64_t u = 0; u < units; ++u) {
     const uint8_t *cu = &codes[(size_t)(u * kUnit)];
     uint32_t a[8] = {0}, hb[4] = {0};
     for (int kk = 0; kk < kUnit; ++kk) {
       uint32_t cv = cu[kk];
-      if (fmt == 2) {
+      if (pf == 2) {
         for (int b = 0; b < 2; ++b) setbit(a, code_pos(2, kk, b), (cv >> b) & 1u);
-      } else if (fmt == 3) {
+      } else if (pf == 3) {
         for (int b = 0; b < 3; ++b) setbit(a, code_pos(3, kk, b), (cv >> b) & 1u);
       } else {
-        for (int b = 0; b < 4; ++b) setbit(a, code_pos(fmt, kk, b), (cv >> b) & 1u);
-        int nh = fmt == 5 ? 1 : 2;
-        for (int b = 0; b < nh; ++b) setbit(hb, hi_pos(fmt, kk, b), (cv >> (4 + b)) & 1u);
+        for (int b = 0; b < 4; ++b) setbit(a, code_pos(pf, kk, b), (cv >> b) & 1u);
+        int nh = pf == 5 ? 1 : 2;
+        for (int b = 0; b < nh; ++b) setbit(hb, hi_pos(pf, kk, b), (cv >> (4 + b)) & 1u);
       }
     }
     uint8_t *d0 = P.p[0] + r * P.rb[0] + u * fp.unit_bytes[0];   // (q2sb, q3sb)
     uint8_t *d1 = P.p[1] + r * P.rb[1] + u * fp.unit_bytes[1];
-    if (fmt == 2) {
+    if (pf == 2) {
       std::memcpy(d0, a, 16);
-    } else if (fmt == 3) {
+    } else if (pf == 3) {
       std::memcpy(d0, a, 16);
       std::memcpy(d1, a + 4, 8);
     } else {
@@ -510,15 +551,16 @@ void row_from_device(int fmt, const uint8_t *const *pl, const int64_t *rb, int64
                      uint8_t *canon) {
   const int64_t units = (k + kUnit - 1) / kUnit;
   FmtPlanes fp = fmt_planes(fmt);
+  const int pf = gw_bits(fmt) == 3 ? 3 : gw_bits(fmt) == 5 ? 5 : fmt;   // code placement
   std::vector<uint8_t> codes((size_t)(units * kUnit), 0);
   for (int64_t u = 0; u < units; ++u) {
     uint32_t a[8] = {0}, hb[4] = {0};
-    if (q4_group(fmt) || fmt == kQ4A32 || fmt == kQ4G32H) {
+    if (q4_group(pf) || pf == kQ4A32 || pf == kQ4G32H) {
       std::memcpy(a, pl[0] + r * rb[0] + split_off(units, u, 0, 16), 16);
       if (k / 2 - u * 32 > 16) std::memcpy(a + 4, pl[0] + r * rb[0] + split_off(units, u, 1, 16), 16);
-    } else if (fmt == 2) {
+    } else if (pf == 2) {
       std::memcpy(a, pl[0] + r * rb[0] + u * 16, 16);
-    } else if (fmt == 3) {
+    } else if (pf == 3) {
       std::memcpy(a, pl[0] + r * rb[0] + u * 16, 16);
       std::memcpy(a + 4, pl[1] + r * rb[1] + u * 8, 8);
     } else {
@@ -528,14 +570,22 @@ void row_from_device(int fmt, const uint8_t *const *pl, const int64_t *rb, int64
     }
     for (int kk = 0; kk < kUnit; ++kk) {
       uint32_t cv = 0;
-      int nb = fmt == 2 ? 2 : fmt == 3 ? 3 : 4;
-      for (int b = 0; b < nb; ++b) cv |= getbit(a, code_pos(fmt, kk, b)) << b;
-      if (fmt == 5 || fmt == 6) {
-        int nh = fmt == 5 ? 1 : 2;
-        for (int b = 0; b < nh; ++b) cv |= getbit(hb, hi_pos(fmt, kk, b)) << (4 + b);
+      int nb = pf == 2 ? 2 : pf == 3 ? 3 : 4;
+      for (int b = 0; b < nb; ++b) cv |= getbit(a, code_pos(pf, kk, b)) << b;
+      if (pf == 5 || pf == 6) {
+        int nh = pf == 5 ? 1 : 2;
+        for (int b = 0; b < nh; ++b) cv |= getbit(hb, hi_pos(pf, kk, b)) << (4 + b);
       }
       codes[(size_t)(u * kUnit + kk)] = (uint8_t)cv;
     }
+  }
+  if (gw_bits(fmt)) {
+    const int b = gw_bits(fmt);
+    pack_le(codes.data(), k, b, canon + r * (k * b / 8));
+    uint8_t *meta = canon + n * (k * b / 8);
+    std::memcpy(meta + r * (k / 32) * 4, pl[2] + r * rb[2], (size_t)(k / 32) * 4);
+    std::memcpy(meta + n * (k / 32) * 4 + r * (k / 32) * 4, pl[3] + r * rb[3], (size_t)(k / 32) * 4);
+    return;
   }
   if (q4_group(fmt) || fmt == kQ4A32 || fmt == kQ4G32H) {
     const int G = q4_group(fmt) ? q4_group(fmt) : 32;
@@ -623,7 +673,7 @@ const char *qg_strerror(int status) {
   switch (status) {
     case QG_OK: return "ok";
     case QG_ERR_NULL: return "a required pointer is NULL";
-    case QG_ERR_SHAPE: return "n, k or m out of range (k must be a multiple of 256 for the super-block formats, of 32 for q4g32, 64 for q4g16, q4g64, q4a32 and q4g32h, 128 for q4g128)";
+    case QG_ERR_SHAPE: return "n, k or m out of range (k must be a multiple of 256 for the super-block formats, of 32 for q4g32, 64 for q4g16, q4g64, q4a32, q4g32h, q3g32 and q5g32, 128 for q4g128)";
     case QG_ERR_ALIGN: return "misaligned device pointer or leading dimension";
     case QG_ERR_NONFINITE: return "a weight is NaN or infinite";
     case QG_ERR_RANGE: return "a super-block scale does not fit fp16 (or bf16), or an fp16 group scale overflows, or a code does not fit its width";
@@ -641,6 +691,7 @@ int qg_canonical_bytes(int fmt, int64_t n, int64_t k, int64_t *bytes) {
   if (q4_group(fmt)) { *bytes = n * (k / 2) + n * (k / q4_group(fmt)) * 4; return QG_OK; }
   if (fmt == kQ4A32) { *bytes = n * (k / 2) + n * (k / 32) * 5; return QG_OK; }
   if (fmt == kQ4G32H) { *bytes = n * (k / 2) + n * (k / 32) * 2; return QG_OK; }
+  if (gw_bits(fmt)) { *bytes = n * (k * gw_bits(fmt) / 8) + n * (k / 32) * 8; return QG_OK; }
   SB s;
   sb_spec(fmt, &s);
   *bytes = n * (k / kQK) * s.rec;
@@ -685,6 +736,18 @@ int qg_quantize(int fmt, const float *w, int64_t n, int64_t k, int64_t ldw, uint
     return parallel_rows(n, k, [&](int64_t r0, int64_t r1) {
       for (int64_t r = r0; r < r1; ++r) {
         int st = quantize_row_q4(w + r * ldw, k, G, codes + r * (k / 2), scales + r * (k / G));
+        if (st != QG_OK) return st;
+      }
+      return (int)QG_OK;
+    });
+  }
+  if (gw_bits(fmt)) {
+    const int b = gw_bits(fmt);
+    float *scales = reinterpret_cast<float *>(canonical + n * (k * b / 8));   // k % 64: 4-byte aligned
+    float *mins = scales + n * (k / 32);
+    return parallel_rows(n, k, [&](int64_t r0, int64_t r1) {
+      for (int64_t r = r0; r < r1; ++r) {
+        int st = quantize_row_gw(w + r * ldw, k, b, canonical + r * (k * b / 8), scales + r * (k / 32), mins + r * (k / 32));
         if (st != QG_OK) return st;
       }
       return (int)QG_OK;
@@ -736,6 +799,8 @@ int quantize_q2sb_bf16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_
 int quantize_q3sb_bf16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(13, w, n, k, ldw, c); }
 int quantize_q5sb_bf16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(15, w, n, k, ldw, c); }
 int quantize_q6sb_bf16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(16, w, n, k, ldw, c); }
+int quantize_q3g32(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(17, w, n, k, ldw, c); }
+int quantize_q5g32(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(18, w, n, k, ldw, c); }
 int quantize_q2sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(2, w, n, k, ldw, c); }
 int quantize_q3sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(3, w, n, k, ldw, c); }
 int quantize_q5sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(5, w, n, k, ldw, c); }

@@ -18,6 +18,10 @@
 //  q4a32  (asymmetric) planes 0 and 1 as q4g32 (unsigned codes), plane 2 uint8 zero points,
 //         2 bytes per unit in group order (not split).
 //  q4g32h plane 0 as q4g32; plane 1 fp16 scales in group order (one dword per unit).
+//  q3g32  planes 0 and 1 as q3sb (a unit's two chunks of 32 codes are its two groups);
+//         planes 2 and 3 fp32 scales and fp32 mins, two per unit in group order.
+//  q5g32  planes 0 and 1 as q5sb (a unit's two sub-blocks of 32 are its two groups); planes
+//         2 and 3 fp32 scales and fp32 mins, two per unit in group order.
 //         Split halves (also the q5sb/q6sb nibble planes): a row of a 32-byte-per-unit plane
 //         stores the first 16 bytes of every unit, then the second 16 bytes of every unit
 //         (dwords 0-3 of unit u at 16u, dwords 4-7 at 16 units + 16u); the q4g32 scale plane
@@ -96,15 +100,22 @@ constexpr int kQ4G32H = 11;
 QG_HOST_DEVICE constexpr bool sb_bf16(int fmt) { return fmt == 12 || fmt == 13 || fmt == 15 || fmt == 16; }
 QG_HOST_DEVICE constexpr int sb_base(int fmt) { return sb_bf16(fmt) ? fmt - 10 : fmt; }
 
+// Plain group-wise codes with an fp32 scale and min per group of 32: 3-bit (code 17) and
+// 5-bit (code 18); code bits of the format (0 for the others).
+constexpr int kQ3G32 = 17;
+constexpr int kQ5G32 = 18;
+QG_HOST_DEVICE constexpr int gw_bits(int fmt) { return fmt == kQ3G32 ? 3 : fmt == kQ5G32 ? 5 : 0; }
+
 inline bool fmt_valid(int fmt) {
-  return (fmt >= 2 && fmt <= 6) || q4_group(fmt) != 0 || fmt == kQ4A32 || fmt == kQ4G32H || sb_bf16(fmt);
+  return (fmt >= 2 && fmt <= 6) || q4_group(fmt) != 0 || fmt == kQ4A32 || fmt == kQ4G32H || sb_bf16(fmt) ||
+         gw_bits(fmt) != 0;
 }
 
 // K must be a multiple of this: 32 for q4g32 (a row may end in half a unit), whole units
-// (64) for q4g16, q4g64, q4a32 and q4g32h, 128 for q4g128, a super-block (256) for the
-// other formats.
+// (64) for q4g16, q4g64, q4a32, q4g32h, q3g32 and q5g32, 128 for q4g128, a super-block
+// (256) for the other formats.
 inline int64_t k_multiple(int fmt) {
-  if (fmt == kQ4A32 || fmt == kQ4G32H) return kUnit;
+  if (fmt == kQ4A32 || fmt == kQ4G32H || gw_bits(fmt)) return kUnit;
   const int G = q4_group(fmt);
   return G == 32 ? 32 : G ? (G > kUnit ? G : kUnit) : kQK;
 }
@@ -121,12 +132,15 @@ inline FmtPlanes fmt_planes(int fmt) {
     case 9: return {2, {32, 2, 0, 0}, {0, 0, 0, 0}};          // codes, 1 fp32 scale per 2 units
     case 10: return {3, {32, 8, 2, 0}, {0, 0, 0, 0}};         // codes, fp32 scales, zero points
     case 11: return {2, {32, 4, 0, 0}, {0, 0, 0, 0}};         // codes, fp16 scales
+    case 17: return {4, {16, 8, 8, 8}, {0, 0, 0, 0}};         // codes A, codes B, scales, mins
+    case 18: return {4, {32, 8, 8, 8}, {0, 0, 0, 0}};         // lo, hi, scales, mins
     default: return {0, {0, 0, 0, 0}, {0, 0, 0, 0}};
   }
 }
 
 // Row bytes of plane p for a row of k weights (k a multiple of 256 for the super-block
-// formats, of 32 for q4g32, of 64 for q4g16, q4g64, q4a32 and q4g32h, of 128 for q4g128).
+// formats, of 32 for q4g32, of 64 for q4g16, q4g64, q4a32, q4g32h, q3g32 and q5g32, of 128
+// for q4g128).
 inline int64_t plane_row_bytes(int fmt, int p, int64_t k) {
   FmtPlanes f = fmt_planes(fmt);
   if (fmt == 4) return p == 0 ? k / 2 : (k / 32) * 4;

@@ -238,6 +238,8 @@ int launch_prefill(int fmt, const void *w, const uint16_t *X, int64_t ldx, void 
     case 13: return launch(prefill_kernel<13>, grid, block, 0, s, a);
     case 15: return launch(prefill_kernel<15>, grid, block, 0, s, a);
     case 16: return launch(prefill_kernel<16>, grid, block, 0, s, a);
+    case 17: return launch(prefill_kernel<17>, grid, block, 0, s, a);
+    case 18: return launch(prefill_kernel<18>, grid, block, 0, s, a);
   }
   return QG_ERR_FORMAT;
 }

@@ -214,6 +214,8 @@ int launch_skinny(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *
     case 13: return launch(skinny_kernel<13>, grid, block, shm, s, a);
     case 15: return launch(skinny_kernel<15>, grid, block, shm, s, a);
     case 16: return launch(skinny_kernel<16>, grid, block, shm, s, a);
+    case 17: return launch(skinny_kernel<17>, grid, block, shm, s, a);
+    case 18: return launch(skinny_kernel<18>, grid, block, shm, s, a);
   }
   return QG_ERR_FORMAT;
 }

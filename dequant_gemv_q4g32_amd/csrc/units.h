@@ -584,6 +584,102 @@ template <bool BF> struct UnitQ3 {
 template <> struct Unit<3> : UnitQ3<false> {};
 template <> struct Unit<13> : UnitQ3<true> {};
 
+// ---- plain group-wise 3-bit codes with an fp32 scale s and min m per group of 32 (q3g32):
+// q3sb's code planes (a chunk of 32 codes is one group), scale and min planes of two fp32 per
+// unit. w_hat = s c + m, so a group's sum is s * sum(c x) + m * sum(x). With S = 2 lane half
+// h owns chunk (group) h.
+template <> struct Unit<kQ3G32> : UnitQ3<false> {
+  static constexpr int NK = 4;
+  __host__ __device__ static constexpr int NKS(int S) { return NK / S; }
+  struct Raw { u32x4 a; u32x2 b; float s[2]; float mn[2]; };
+  __device__ static void offsets(int64_t u, uint32_t *off) {
+    off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 8); off[2] = (uint32_t)(u * 8); off[3] = (uint32_t)(u * 8);
+  }
+  template <int AUX = kNT, int S = 1> __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
+    q.a = bldx4<AUX>(L.rs[0], L.off[0], L.row(0, r));
+    q.b = bldx2<AUX>(L.rs[1], L.off[1], L.row(1, r));
+    // (integer pairs through keep(): see the INT4 scale loads)
+    const u32x2 sv = bldx2<0>(L.rs[2], L.off[2], L.row(2, r));
+    const u32x2 mv = bldx2<0>(L.rs[3], L.off[3], L.row(3, r));
+    q.s[0] = __builtin_bit_cast(float, keep(sv.x));
+    q.s[1] = __builtin_bit_cast(float, keep(sv.y));
+    q.mn[0] = __builtin_bit_cast(float, keep(mv.x));
+    q.mn[1] = __builtin_bit_cast(float, keep(mv.y));
+  }
+  // Per chunk: the start of its accumulator (sum P x = sum c x + 1024 X1 + 128 X8a + 128 X8b
+  // + 16 X64, with the class-8 and class-64 activations divided as for q3sb) and sum x.
+  // kc layout (S = 1): [start g0, start g1, sum x g0, sum x g1]; (S = 2): [start, sum x]
+  template <int S> __device__ static void prep(uint32_t *xp, float *kc) {
+    const h2_t s8 = {(_Float16)0.125f, (_Float16)0.125f}, s64 = {(_Float16)0.015625f, (_Float16)0.015625f};
+#pragma unroll
+    for (int c = 0; c < 2 / S; ++c) {
+      uint32_t *x = xp + 16 * c;
+      float a1 = 0.f, a8 = 0.f, b8 = 0.f, b64 = 0.f;
+#pragma unroll
+      for (int r = 0; r < 6; ++r) a1 = dot2(x[r], kOnes, a1);
+#pragma unroll
+      for (int r = 6; r < 8; ++r) a8 = dot2(x[r], kOnes, a8);
+#pragma unroll
+      for (int r = 8; r < 12; ++r) b8 = dot2(x[r], kOnes, b8);
+#pragma unroll
+      for (int r = 12; r < 16; ++r) b64 = dot2(x[r], kOnes, b64);
+      kc[c] = -(1024.0f * a1 + 128.0f * (a8 + b8) + 16.0f * b64);
+      kc[2 / S + c] = (a1 + a8) + (b8 + b64);
+#pragma unroll
+      for (int r = 6; r < 12; ++r) x[r] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, x[r]) * s8);
+#pragma unroll
+      for (int r = 12; r < 16; ++r) x[r] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, x[r]) * s64);
+    }
+  }
+  template <int M, int S>
+  __device__ static void dot(const Raw &q, int h, const uint32_t (*xp)[32 / S], const float (*kc)[NKS(S)], float *out) {
+    if constexpr (S == 1) {
+      uint32_t P0[16], P1[16];
+      chunk_pairs(q.a.x, q.a.y, q.a.z, P0);
+      chunk_pairs(q.a.w, q.b.x, q.b.y, P1);
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float a0 = kc[m][0], a1 = kc[m][1];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a0 = dot2(P0[r], xp[m][r], a0);
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a1 = dot2(P1[r], xp[m][16 + r], a1);
+        out[m] = __builtin_fmaf(q.s[0], a0, __builtin_fmaf(q.mn[0], kc[m][2], out[m]));
+        out[m] = __builtin_fmaf(q.s[1], a1, __builtin_fmaf(q.mn[1], kc[m][3], out[m]));
+      }
+    } else {
+      uint32_t P[16];
+      chunk_pairs(sel(h, q.a.w, q.a.x), sel(h, q.b.x, q.a.y), sel(h, q.b.y, q.a.z), P);
+      const float sc = __builtin_bit_cast(float, sel(h, __builtin_bit_cast(uint32_t, q.s[1]), __builtin_bit_cast(uint32_t, q.s[0])));
+      const float mn = __builtin_bit_cast(float, sel(h, __builtin_bit_cast(uint32_t, q.mn[1]), __builtin_bit_cast(uint32_t, q.mn[0])));
+#pragma unroll
+      for (int m = 0; m < M; ++m) {
+        float a = kc[m][0];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) a = dot2(P[r], xp[m][r], a);
+        out[m] = __builtin_fmaf(sc, a, __builtin_fmaf(mn, kc[m][1], out[m]));
+      }
+    }
+  }
+  // fp16 w_hat of the 16 pairs of chunk h: P * (s / p) + (m - 1024 s / p) for class p, in fp32,
+  // then one rounding
+  template <int S = 1> __device__ static void wide(const Raw &q, int h, uint32_t *out) {
+    uint32_t P[16];
+    chunk_pairs(sel(h, q.a.w, q.a.x), sel(h, q.b.x, q.a.y), sel(h, q.b.y, q.a.z), P);
+    const float sc = __builtin_bit_cast(float, sel(h, __builtin_bit_cast(uint32_t, q.s[1]), __builtin_bit_cast(uint32_t, q.s[0])));
+    const float mn = __builtin_bit_cast(float, sel(h, __builtin_bit_cast(uint32_t, q.mn[1]), __builtin_bit_cast(uint32_t, q.mn[0])));
+    const float mul1 = sc, add1 = __builtin_fmaf(-1024.0f, sc, mn);
+    const float mul8 = sc * 0.125f, add8 = __builtin_fmaf(-128.0f, sc, mn);
+    const float mul64 = sc * 0.015625f, add64 = __builtin_fmaf(-16.0f, sc, mn);
+#pragma unroll
+    for (int r = 0; r < 6; ++r) out[r] = asym_pair(P[r], mul1, add1);
+#pragma unroll
+    for (int r = 6; r < 12; ++r) out[r] = asym_pair(P[r], mul8, add8);
+#pragma unroll
+    for (int r = 12; r < 16; ++r) out[r] = asym_pair(P[r], mul64, add64);
+  }
+};
+
 // ---- nibble plane + high-bit plane (q5sb: 1 high bit, 32-weight sub-blocks;
 //      q6sb: 2 high bits, 16-weight sub-blocks). Produces the four pairs of one nibble dword.
 template <int HB>
@@ -697,6 +793,85 @@ template <bool BF> struct UnitQ5 {
 };
 template <> struct Unit<5> : UnitQ5<false> {};
 template <> struct Unit<15> : UnitQ5<true> {};
+
+// ---- plain group-wise 5-bit codes with an fp32 scale s and min m per group of 32 (q5g32):
+// q5sb's code planes (a sub-block of 32 is one group), scale and min planes of two fp32 per
+// unit; w_hat = s c + m. prep is q5sb's (start and sum x per group). With S = 2 lane half h
+// owns group h.
+template <> struct Unit<kQ5G32> : UnitQ5<false> {
+  struct Raw { u32x4 l0, l1; u32x2 h; float s[2]; float mn[2]; };
+  __device__ static void offsets(int64_t u, uint32_t *off) {
+    off[0] = (uint32_t)(u * 16); off[1] = (uint32_t)(u * 8); off[2] = (uint32_t)(u * 8); off[3] = (uint32_t)(u * 8);
+  }
+  template <int AUX = kNT, int S = 1> __device__ static void load(Raw &q, const Lane &L, int64_t r, bool) {
+    const uint32_t r0 = L.row(0, r);
+    if constexpr (S == 2) {
+      q.l0 = bldx4<AUX>(L.rs[0], L.off[0] + (L.h ? L.half16 : 0u), r0);
+      q.h.x = bldx1<AUX>(L.rs[1], L.off[1] + 4u * L.h, L.row(1, r));
+    } else {
+      q.l0 = bldx4<AUX>(L.rs[0], L.off[0], r0);
+      q.l1 = bldx4<AUX>(L.rs[0], L.off[0] + L.half16, r0);
+      q.h = bldx2<AUX>(L.rs[1], L.off[1], L.row(1, r));
+    }
+    const u32x2 sv = bldx2<0>(L.rs[2], L.off[2], L.row(2, r));
+    const u32x2 mv = bldx2<0>(L.rs[3], L.off[3], L.row(3, r));
+    q.s[0] = __builtin_bit_cast(float, keep(sv.x));
+    q.s[1] = __builtin_bit_cast(float, keep(sv.y));
+    q.mn[0] = __builtin_bit_cast(float, keep(mv.x));
+    q.mn[1] = __builtin_bit_cast(float, keep(mv.y));
+  }
+  template <int M, int S>
+  __device__ static void dot(const Raw &q, int h, const uint32_t (*xp)[32 / S], const float (*kc)[NKS(S)], float *out) {
+    const uint32_t L[8] = {q.l0.x, q.l0.y, q.l0.z, q.l0.w, S == 1 ? q.l1.x : 0u, S == 1 ? q.l1.y : 0u,
+                           S == 1 ? q.l1.z : 0u, S == 1 ? q.l1.w : 0u};
+#pragma unroll
+    for (int hh = 0; hh < 2 / S; ++hh) {
+      const int sb = S == 1 ? hh : 0;
+      float a1[M], a16[M];
+#pragma unroll
+      for (int m = 0; m < M; ++m) { a1[m] = kc[m][sb]; a16[m] = 0.f; }
+      const uint32_t H = S == 1 && hh ? q.h.y : q.h.x;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        uint32_t P[4];
+        nib_pairs<1>(L[4 * hh + i], H, i, P);
+#pragma unroll
+        for (int m = 0; m < M; ++m) {
+          a1[m] = dot2(P[0], xp[m][16 * sb + 4 * i + 0], a1[m]);
+          a16[m] = dot2(P[1], xp[m][16 * sb + 4 * i + 1], a16[m]);
+          a1[m] = dot2(P[2], xp[m][16 * sb + 4 * i + 2], a1[m]);
+          a16[m] = dot2(P[3], xp[m][16 * sb + 4 * i + 3], a16[m]);
+        }
+      }
+      const float sc = S == 1 ? q.s[hh]
+                              : __builtin_bit_cast(float, sel(h, __builtin_bit_cast(uint32_t, q.s[1]), __builtin_bit_cast(uint32_t, q.s[0])));
+      const float mn = S == 1 ? q.mn[hh]
+                              : __builtin_bit_cast(float, sel(h, __builtin_bit_cast(uint32_t, q.mn[1]), __builtin_bit_cast(uint32_t, q.mn[0])));
+#pragma unroll
+      for (int m = 0; m < M; ++m)
+        out[m] = __builtin_fmaf(sc, __builtin_fmaf(a16[m], 0.0625f, a1[m]), __builtin_fmaf(mn, kc[m][2 / S + sb], out[m]));
+    }
+  }
+  // fp16 w_hat of the 16 pairs of half h (group h); S = 2: q holds only that group's codes
+  template <int S = 1> __device__ static void wide(const Raw &q, int h, uint32_t *out) {
+    const uint32_t L[8] = {q.l0.x, q.l0.y, q.l0.z, q.l0.w, S == 1 ? q.l1.x : 0u, S == 1 ? q.l1.y : 0u,
+                           S == 1 ? q.l1.z : 0u, S == 1 ? q.l1.w : 0u};
+    const uint32_t H = S == 1 ? sel(h, q.h.y, q.h.x) : q.h.x;
+    const float sc = __builtin_bit_cast(float, sel(h, __builtin_bit_cast(uint32_t, q.s[1]), __builtin_bit_cast(uint32_t, q.s[0])));
+    const float mn = __builtin_bit_cast(float, sel(h, __builtin_bit_cast(uint32_t, q.mn[1]), __builtin_bit_cast(uint32_t, q.mn[0])));
+    const float mul1 = sc, add1 = __builtin_fmaf(-1024.0f, sc, mn);
+    const float mul16 = sc * 0.0625f, add16 = __builtin_fmaf(-64.0f, sc, mn);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t P[4];
+      nib_pairs<1>(S == 1 ? sel(h, L[4 + i], L[i]) : L[i], H, i, P);
+      out[4 * i + 0] = asym_pair(P[0], mul1, add1);
+      out[4 * i + 1] = asym_pair(P[1], mul16, add16);
+      out[4 * i + 2] = asym_pair(P[2], mul1, add1);
+      out[4 * i + 3] = asym_pair(P[3], mul16, add16);
+    }
+  }
+};
 
 // ---- 6-bit super-block: a unit is four sub-blocks of 16; with S = 2 lane half h owns
 // sub-blocks 2h, 2h+1

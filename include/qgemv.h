@@ -36,6 +36,11 @@
  *             bf16_ceil in place of fp16_ceil in the rule below. The GEMM paths for m > 8
  *             multiply fp16 W_hat on the matrix cores: weights beyond the fp16 range (which
  *             only bf16 super-scales can express) need m <= 8 there.
+ *   QG_Q3G32, QG_Q5G32  plain group-wise 3- and 5-bit codes c with an fp32 scale s and an fp32
+ *             min m per group of 32 (the form of "二三五六位量化" page section 3.3's gemv_q3:
+ *             w_hat = s*c + m): m = min w, s = max((max w - min w) / (2^b - 1), 1e-12),
+ *             c = clamp(rint((w - m) / s), 0, 2^b - 1), difference and quotient in fp32.
+ *             12 or 20 B of codes + 8 B per group (5.0 and 7.0 bpw). k a multiple of 64.
  *
  * Super-block scales are chosen by "range-covering round to nearest" (the pages give the
  * layouts, not the rule): with fp16_ceil(v) = smallest fp16 >= v, symmetric formats take
@@ -50,7 +55,9 @@
  *   canonical  the pages' interchange layout. q4g32: codes [n][k/2] (byte = u[2j] | u[2j+1] << 4
  *              with u = q + 8) followed by fp32 scales [n][k/32] (q4gG: [n][k/G]). q4a32: codes
  *              [n][k/2] (u = c), fp32 scales [n][k/32], uint8 zero points [n][k/32]. q4g32h: codes
- *              as q4g32, then fp16 scales [n][k/32]. Super-block formats: records
+ *              as q4g32, then fp16 scales [n][k/32]. q3g32 / q5g32: each row's codes as one
+ *              little-endian b-bit stream [n][k*b/8], then fp32 scales [n][k/32], then fp32
+ *              mins [n][k/32]. Super-block formats: records
  *              [n][k/256] of 84/110/176/210 bytes; fields in the byte table's column order
  *              (codes [, high-bit plane], sub-scales, d [, dmin]); every bit field is a
  *              little-endian bitstream (code i at bits [b*i, b*i + b), section 2.2's unpack3
@@ -97,7 +104,9 @@ typedef enum qg_format {
   QG_Q2SB_BF16 = 12,
   QG_Q3SB_BF16 = 13,
   QG_Q5SB_BF16 = 15,
-  QG_Q6SB_BF16 = 16
+  QG_Q6SB_BF16 = 16,
+  QG_Q3G32 = 17,
+  QG_Q5G32 = 18
 } qg_format;
 
 typedef enum qg_status {
@@ -165,6 +174,8 @@ int quantize_q2sb_bf16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_
 int quantize_q3sb_bf16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
 int quantize_q5sb_bf16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
 int quantize_q6sb_bf16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
+int quantize_q3g32(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
+int quantize_q5g32(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
 
 /* Canonical encoding (host) -> device layout (host buffer of qg_device_layout().total_bytes;
  * padding is zeroed). A pure bit permutation. */
@@ -194,6 +205,8 @@ int dequant_gemv_q2sb_bf16(const void *w, const uint16_t *x, uint16_t *y, int64_
 int dequant_gemv_q3sb_bf16(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
 int dequant_gemv_q5sb_bf16(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
 int dequant_gemv_q6sb_bf16(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
+int dequant_gemv_q3g32(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
+int dequant_gemv_q5g32(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
 
 /* Generic form: y_f32 != 0 writes fp32 y (4-byte aligned) instead of fp16. */
 int qg_gemv(int fmt, const void *w, const uint16_t *x, void *y, int y_f32, int64_t n, int64_t k, void *stream);
@@ -247,6 +260,10 @@ int dequant_gemm_q5sb_bf16(const void *w, const uint16_t *X, int64_t ldx, uint16
                             int64_t m, int64_t n, int64_t k, void *stream);
 int dequant_gemm_q6sb_bf16(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
                             int64_t m, int64_t n, int64_t k, void *stream);
+int dequant_gemm_q3g32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
+                        int64_t m, int64_t n, int64_t k, void *stream);
+int dequant_gemm_q5g32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
+                        int64_t m, int64_t n, int64_t k, void *stream);
 /* Generic form; y_f32 != 0 writes fp32 Y (4-byte aligned). */
 int qg_gemm(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int64_t ldy, int y_f32,
             int64_t m, int64_t n, int64_t k, void *stream);
@@ -301,7 +318,7 @@ int qg_kv_dequantize(const int8_t *codes, const uint16_t *scales, int64_t rows, 
  * Writes W_hat as fp32 [n][k] to w_out (if non-NULL) and the integer codes as uint8 [n][k]
  * to codes_out (if non-NULL; q4g32 writes the unsigned nibble u = q + 8, q4a32 the code c).
  * fp32 values are single-rounding products (q*scale, (c - z)*s, d*sc*(c - o),
- * fma(d*sc, c, -dmin*m)), hence exactly fp32(W_hat). */
+ * fma(d*sc, c, -dmin*m), fma(s, c, m)), hence exactly fp32(W_hat). */
 int dequantize_q4g32(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 int dequantize_q2sb(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 int dequantize_q3sb(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
@@ -316,6 +333,8 @@ int dequantize_q2sb_bf16(const void *w, float *w_out, uint8_t *codes_out, int64_
 int dequantize_q3sb_bf16(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 int dequantize_q5sb_bf16(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 int dequantize_q6sb_bf16(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
+int dequantize_q3g32(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
+int dequantize_q5g32(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 int qg_dequantize(int fmt, const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 
 /* ---- measurement (device) -----------------------------------------------------------------

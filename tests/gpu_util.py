@@ -3,6 +3,7 @@ import numpy as np
 
 import dequant_gemv_q4g32_amd as qg
 from oracle import gemv as ogemv
+from oracle import groupwise as gw
 from oracle import int4
 from oracle import superblock as sb
 
@@ -16,6 +17,9 @@ def oracle_decode(fmt, w):
     if fmt == "q4g32h":
         q, s16 = int4.quantize_h(w)
         return (q.astype(np.int16) + 8).astype(np.uint8), int4.dequantize(q, s16.astype(np.float32))
+    if fmt in gw.BITS:
+        q, s, m = gw.quantize(fmt, w)
+        return q, gw.dequantize(q, s, m)
     if fmt == "q4a32":
         q, s, z = int4.quantize_asym(w)
         return q, int4.dequantize_asym(q, s, z)

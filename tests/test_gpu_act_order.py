@@ -18,7 +18,7 @@ from workloads import activations, laplace_weights
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb", "q4g16", "q4g128", "q4a32", "q4g32h", "q3sb_bf16", "q5sb_bf16"]
+FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb", "q4g16", "q4g128", "q4a32", "q4g32h", "q3sb_bf16", "q5sb_bf16", "q3g32", "q5g32"]
 SHAPES = [(37, 512), (300, 4352), (9, 8192)]
 
 

@@ -19,7 +19,7 @@ from workloads import WORKLOADS, activations, laplace_weights
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb", "q4g16", "q4g128", "q4a32", "q4g32h", "q3sb_bf16", "q5sb_bf16"]
+FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb", "q4g16", "q4g128", "q4a32", "q4g32h", "q3sb_bf16", "q5sb_bf16", "q3g32", "q5g32"]
 # K over 1, 2, 5 and 7 waves; ragged n; (7, 28672) takes two passes over K at m = 8
 SHAPES = [(37, 512), (300, 4352), (9, 8192), (130, 1024), (7, 28672), (64, 4352)]
 

@@ -11,14 +11,18 @@ import pytest
 
 import dequant_gemv_q4g32_amd as qg
 from oracle import bitstream, int4
+from oracle import groupwise as gw
 from oracle import superblock as sb
 from workloads import laplace_weights, uniform_codes
 
 FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb", "q4g16", "q4g64", "q4g128", "q4a32", "q4g32h",
-        "q2sb_bf16", "q3sb_bf16", "q5sb_bf16", "q6sb_bf16"]
+        "q2sb_bf16", "q3sb_bf16", "q5sb_bf16", "q6sb_bf16", "q3g32", "q5g32"]
 
 
 def oracle_canonical(fmt, w):
+    if fmt in gw.BITS:
+        codes, s, m = gw.encode(fmt, w)
+        return np.concatenate([codes.reshape(-1), s.reshape(-1).view(np.uint8), m.reshape(-1).view(np.uint8)])
     if fmt == "q4g32h":
         codes, s16 = int4.encode_h(w)
         return np.concatenate([codes.reshape(-1), s16.reshape(-1).view(np.uint8)])
@@ -119,6 +123,8 @@ def test_algorithmic_bytes_match_oracle(fmt):
         want = int4.algorithmic_bytes_asym(n, k)
     elif fmt == "q4g32h":
         want = int4.algorithmic_bytes_h(n, k)
+    elif fmt in gw.BITS:
+        want = gw.algorithmic_bytes(fmt, n, k)
     else:
         want = int4.algorithmic_bytes(n, k, qg.Q4_GROUPS[fmt]) if fmt in qg.Q4_GROUPS else sb.algorithmic_bytes(fmt, n, k)
     assert qg.device_layout(fmt, n, k).algorithmic_bytes == want
@@ -142,7 +148,7 @@ def test_error_codes():
             qg.quantize(fmt, big)
         assert e.value.status == -5
     assert qg.lib.qg_quantize(14, None, 1, 256, 256, None) == -6
-    assert qg.lib.qg_quantize(17, None, 1, 256, 256, None) == -6
+    assert qg.lib.qg_quantize(19, None, 1, 256, 256, None) == -6
     for fmt in ("q2sb_bf16", "q3sb_bf16", "q5sb_bf16", "q6sb_bf16"):      # bf16 covers 1e10
         assert np.array_equal(qg.quantize(fmt, big), oracle_canonical(fmt, big))
     out = ctypes.c_int64()
