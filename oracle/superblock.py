@@ -46,6 +46,11 @@ Readings (the pages give the layouts but not every field, nor how scales are cho
     |w - w_hat| <= d * sc_j / 2 for every element, which is section 3.4's check with
     "scale" read as the sub-block step d * sc_j. rint is round half to even.
   * A super-scale beyond the fp16 range raises OverflowError (section 2.3 warns of inf).
+  * "q3sb_planes": section 2.3's advice for widths that do not divide a byte (split the code
+    into byte-friendly planes instead of interleaving, as the 5- and 6-bit records do) applied
+    to the 3-bit record: the same fields and rule as q3sb, with the 96 code bytes stored as a
+    64-byte plane of the low 2 bits (2-bit little-endian stream) followed by a 32-byte plane
+    of the high bit (1-bit stream); 110 bytes as before.
   * bf16 super-scales ("q2sb_bf16", "q3sb_bf16", "q5sb_bf16", "q6sb_bf16"): section 2.3's
     remedy for that overflow, storing the super-block scale as bf16. Read as the same
     format, record layout and rule with bf16_ceil (smallest bf16 >= v) in place of
@@ -95,6 +100,7 @@ SPECS: Dict[str, SBSpec] = {
 }
 for _b in ("q2sb", "q3sb", "q5sb", "q6sb"):
     SPECS[_b + "_bf16"] = dataclasses.replace(SPECS[_b], name=_b + "_bf16", bf16=True)
+SPECS["q3sb_planes"] = dataclasses.replace(SPECS["q3sb"], name="q3sb_planes", layout="q3sb_planes")
 
 
 # Super-scale codec of a spec: ceil to the stored type, zero, bits, little-endian bytes.
@@ -201,6 +207,10 @@ def encode_block_scalar(spec: SBSpec, f: dict) -> bytes:
         rec = bitstream.pack_bits_scalar(codes, 2) + meta + d + dm
     elif spec.layout == "q3sb":
         rec = bitstream.pack_bits_scalar(codes, 3) + bitstream.pack_bits_scalar(f["sc"], 6) + d
+    elif spec.layout == "q3sb_planes":
+        rec = (bitstream.pack_bits_scalar([c & 3 for c in codes], 2)
+               + bitstream.pack_bits_scalar([c >> 2 for c in codes], 1)
+               + bitstream.pack_bits_scalar(f["sc"], 6) + d)
     elif spec.layout == "q5sb":
         dm = _to_bytes(spec, np.array(f["dmin"], _dtype(spec))).tobytes()
         rec = (bitstream.pack_bits_scalar([c & 15 for c in codes], 4)
@@ -228,6 +238,11 @@ def decode_block_scalar(spec: SBSpec, rec: bytes) -> dict:
         sc = [b & 15 for b in rec[64:80]]
         m = [b >> 4 for b in rec[64:80]]
         return dict(codes=codes, sc=sc, m=m, d=half(rec[80:82]), dmin=half(rec[82:84]))
+    if spec.layout == "q3sb_planes":
+        lo = bitstream.unpack_bits_scalar(rec[0:64], 2, QK)
+        hi = bitstream.unpack_bits_scalar(rec[64:96], 1, QK)
+        sc = bitstream.unpack_bits_scalar(rec[96:108], 6, 16)
+        return dict(codes=[a | (b << 2) for a, b in zip(lo, hi)], sc=sc, m=None, d=half(rec[108:110]), dmin=None)
     if spec.layout == "q3sb":
         codes = bitstream.unpack_bits_scalar(rec[0:96], 3, QK)
         sc = bitstream.unpack_bits_scalar(rec[96:108], 6, 16)
@@ -318,6 +333,9 @@ def encode_fields(fmt: str, f: dict) -> np.ndarray:
         parts = [bitstream.pack_bits(codes, 2), meta, d, _to_bytes(spec, f["dmin"])]
     elif lay == "q3sb":
         parts = [bitstream.pack_bits(codes, 3), bitstream.pack_bits(f["sc"].astype(np.uint8), 6), d]
+    elif lay == "q3sb_planes":
+        parts = [bitstream.pack_bits(codes & 3, 2), bitstream.pack_bits(codes >> 2, 1),
+                 bitstream.pack_bits(f["sc"].astype(np.uint8), 6), d]
     elif lay == "q5sb":
         f6 = np.concatenate([f["sc"], f["m"]], axis=-1).astype(np.uint8)
         parts = [bitstream.pack_bits(codes & 15, 4), bitstream.pack_bits(codes >> 4, 1),
@@ -348,6 +366,12 @@ def decode_records(fmt: str, rec: np.ndarray) -> dict:
         meta = rec[..., 64:80]
         return dict(codes=codes, sc=(meta & 15).astype(np.int16), m=(meta >> 4).astype(np.int16),
                     d=half(rec[..., 80:82]), dmin=half(rec[..., 82:84]))
+    if lay == "q3sb_planes":
+        lo = bitstream.unpack_bits(rec[..., 0:64], 2, QK)
+        hi = bitstream.unpack_bits(rec[..., 64:96], 1, QK)
+        return dict(codes=(lo | (hi << 2)).astype(np.uint8),
+                    sc=bitstream.unpack_bits(rec[..., 96:108], 6, 16).astype(np.int16), m=None,
+                    d=half(rec[..., 108:110]), dmin=None)
     if lay == "q3sb":
         return dict(codes=bitstream.unpack_bits(rec[..., 0:96], 3, QK),
                     sc=bitstream.unpack_bits(rec[..., 96:108], 6, 16).astype(np.int16), m=None,
