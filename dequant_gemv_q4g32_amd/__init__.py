@@ -21,13 +21,16 @@ HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "qgemv.h")
 
 FORMATS = {"q2sb": 2, "q3sb": 3, "q4g32": 4, "q5sb": 5, "q6sb": 6, "q4g16": 7, "q4g64": 8, "q4g128": 9,
            "q4a32": 10, "q4g32h": 11,
-           "q2sb_bf16": 12, "q3sb_bf16": 13, "q5sb_bf16": 15, "q6sb_bf16": 16, "q3g32": 17, "q5g32": 18}
+           "q2sb_bf16": 12, "q3sb_bf16": 13, "q5sb_bf16": 15, "q6sb_bf16": 16, "q3g32": 17, "q5g32": 18,
+           "q3sb_planes": 14}
 GROUPWISE_FORMATS = ("q3g32", "q5g32")   # plain group-wise codes, fp32 scale and min per 32
 Q4_GROUPS = {"q4g16": 16, "q4g32": 32, "q4g64": 64, "q4g128": 128}   # symmetric INT4 group sizes
-SUPERBLOCK_FORMATS = ("q2sb", "q3sb", "q5sb", "q6sb", "q2sb_bf16", "q3sb_bf16", "q5sb_bf16", "q6sb_bf16")
+SUPERBLOCK_FORMATS = ("q2sb", "q3sb", "q5sb", "q6sb", "q2sb_bf16", "q3sb_bf16", "q5sb_bf16", "q6sb_bf16",
+                      "q3sb_planes")
 K_MULTIPLE = {"q4g32": 32, "q2sb": 256, "q3sb": 256, "q5sb": 256, "q6sb": 256, "q4g16": 64, "q4g64": 64, "q4g128": 128,
               "q4a32": 64, "q4g32h": 64, "q2sb_bf16": 256, "q3sb_bf16": 256, "q5sb_bf16": 256,
-              "q6sb_bf16": 256, "q3g32": 64, "q5g32": 64}
+              "q6sb_bf16": 256, "q3g32": 64, "q5g32": 64,
+              "q3sb_planes": 256}
 
 
 class QGError(RuntimeError):

@@ -754,6 +754,7 @@ int launch_mv_fmt(int fmt, GemvArgs a, int64_t count, hipStream_t s) {
     case 11: return launch_mv_f<11>(a, count, s);
     case 12: return launch_mv_f<12>(a, count, s);
     case 13: return launch_mv_f<13>(a, count, s);
+    case 14: return launch_mv_f<3>(a, count, s);   // q3sb's device layout
     case 15: return launch_mv_f<15>(a, count, s);
     case 16: return launch_mv_f<16>(a, count, s);
     case 17: return launch_mv_f<17>(a, count, s);
@@ -776,6 +777,7 @@ int launch_mv_group_fmt(int fmt, GemvGroup &G, hipStream_t s) {
     case 11: return launch_mv_group_f<11>(G, s);
     case 12: return launch_mv_group_f<12>(G, s);
     case 13: return launch_mv_group_f<13>(G, s);
+    case 14: return launch_mv_group_f<3>(G, s);   // q3sb's device layout
     case 15: return launch_mv_group_f<15>(G, s);
     case 16: return launch_mv_group_f<16>(G, s);
     case 17: return launch_mv_group_f<17>(G, s);
@@ -953,6 +955,7 @@ int dequant_gemv_q5sb_bf16(const void *w, const uint16_t *x, uint16_t *y, int64_
 int dequant_gemv_q6sb_bf16(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(16, w, x, y, 0, n, k, s); }
 int dequant_gemv_q3g32(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(17, w, x, y, 0, n, k, s); }
 int dequant_gemv_q5g32(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(18, w, x, y, 0, n, k, s); }
+int dequant_gemv_q3sb_planes(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *s) { return qg_gemv(14, w, x, y, 0, n, k, s); }
 int dequant_gemm_q4g32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m, int64_t n,
                        int64_t k, void *s) {
   return qg_gemm(4, w, X, ldx, Y, ldy, 0, m, n, k, s);
@@ -1017,6 +1020,10 @@ int dequant_gemm_q5g32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *
                         int64_t k, void *s) {
   return qg_gemm(18, w, X, ldx, Y, ldy, 0, m, n, k, s);
 }
+int dequant_gemm_q3sb_planes(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy, int64_t m,
+                              int64_t n, int64_t k, void *s) {
+  return qg_gemm(14, w, X, ldx, Y, ldy, 0, m, n, k, s);
+}
 
 int qg_dequantize(int fmt, const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream) {
   if (!fmt_valid(fmt)) return QG_ERR_FORMAT;
@@ -1043,6 +1050,7 @@ int qg_dequantize(int fmt, const void *w, float *w_out, uint8_t *codes_out, int6
     case 11: return launch(dequant_kernel<11>, grid, block, 0, s, a, w_out, codes_out);
     case 12: return launch(dequant_kernel<12>, grid, block, 0, s, a, w_out, codes_out);
     case 13: return launch(dequant_kernel<13>, grid, block, 0, s, a, w_out, codes_out);
+    case 14: return launch(dequant_kernel<3>, grid, block, 0, s, a, w_out, codes_out);   // q3sb's device layout
     case 15: return launch(dequant_kernel<15>, grid, block, 0, s, a, w_out, codes_out);
     case 16: return launch(dequant_kernel<16>, grid, block, 0, s, a, w_out, codes_out);
     case 17: return launch(dequant_kernel<17>, grid, block, 0, s, a, w_out, codes_out);
@@ -1079,5 +1087,6 @@ int dequantize_q5sb_bf16(const void *w, float *o, uint8_t *c, int64_t n, int64_t
 int dequantize_q6sb_bf16(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(16, w, o, c, n, k, s); }
 int dequantize_q3g32(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(17, w, o, c, n, k, s); }
 int dequantize_q5g32(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(18, w, o, c, n, k, s); }
+int dequantize_q3sb_planes(const void *w, float *o, uint8_t *c, int64_t n, int64_t k, void *s) { return qg_dequantize(14, w, o, c, n, k, s); }
 
 }  // extern "C"

@@ -344,8 +344,15 @@ int quantize_block_sb(const SB &s, int fmt, const float *w, uint8_t *rec) {
     for (int j = 0; j < 16; ++j) rec[64 + j] = (uint8_t)(sc[j] | (m[j] << 4));
     put_half(rec + 80, dbits);
     put_half(rec + 82, dminbits);
-  } else if (fmt == 3) {
-    pack_le(c, 256, 3, rec);
+  } else if (fmt == 3 || fmt == kQ3SBPlanes) {
+    if (fmt == 3) {
+      pack_le(c, 256, 3, rec);
+    } else {                                             // 2-bit plane, then 1-bit plane
+      uint8_t lo2[256], hi1[256];
+      for (int i = 0; i < 256; ++i) { lo2[i] = c[i] & 3; hi1[i] = c[i] >> 2; }
+      pack_le(lo2, 256, 2, rec);
+      pack_le(hi1, 256, 1, rec + 64);
+    }
     uint8_t f[16];
     for (int j = 0; j < 16; ++j) f[j] = (uint8_t)sc[j];
     pack_le(f, 16, 6, rec + 96);
@@ -476,6 +483,7 @@ void row_to_device(int fmt, const uint8_t *canon, int64_t k, int64_t r, int64_t 
     std::memcpy(P.p[3] + r * P.rb[3], meta + n * (k / 32) * 4 + r * (k / 32) * 4, (size_t)(k / 32) * 4);
     pf = b == 3 ? 3 : 5;
   } else {
+  if (fmt == kQ3SBPlanes) pf = 3;
   SB s;
   sb_spec(fmt, &s);
   const int64_t S = k / kQK;
@@ -487,8 +495,15 @@ void row_to_device(int fmt, const uint8_t *canon, int64_t k, int64_t r, int64_t 
       unpack_le(rec, 256, 2, c);
       std::memcpy(P.p[1] + r * P.rb[1] + sbi * 16, rec + 64, 16);
       std::memcpy(P.p[2] + r * P.rb[2] + sbi * 4, rec + 80, 4);
-    } else if (fmt == 3) {
-      unpack_le(rec, 256, 3, c);
+    } else if (fmt == 3 || fmt == kQ3SBPlanes) {
+      if (fmt == 3) {
+        unpack_le(rec, 256, 3, c);
+      } else {
+        uint8_t lo2[256], hi1[256];
+        unpack_le(rec, 256, 2, lo2);
+        unpack_le(rec + 64, 256, 1, hi1);
+        for (int i = 0; i < 256; ++i) c[i] = (uint8_t)(lo2[i] | (hi1[i] << 2));
+      }
       std::memcpy(P.p[2] + r * P.rb[2] + sbi * 12, rec + 96, 12);
       std::memcpy(P.p[3] + r * P.rb[3] + sbi * 2, rec + 108, 2);
     } else if (fmt == 5) {
@@ -551,7 +566,7 @@ void row_from_device(int fmt, const uint8_t *const *pl, const int64_t *rb, int64
                      uint8_t *canon) {
   const int64_t units = (k + kUnit - 1) / kUnit;
   FmtPlanes fp = fmt_planes(fmt);
-  const int pf = gw_bits(fmt) == 3 ? 3 : gw_bits(fmt) == 5 ? 5 : fmt;   // code placement
+  const int pf = gw_bits(fmt) == 3 || fmt == kQ3SBPlanes ? 3 : gw_bits(fmt) == 5 ? 5 : fmt;   // code placement
   std::vector<uint8_t> codes((size_t)(units * kUnit), 0);
   for (int64_t u = 0; u < units; ++u) {
     uint32_t a[8] = {0}, hb[4] = {0};
@@ -612,8 +627,15 @@ void row_from_device(int fmt, const uint8_t *const *pl, const int64_t *rb, int64
       pack_le(c, 256, 2, rec);
       std::memcpy(rec + 64, pl[1] + r * rb[1] + sbi * 16, 16);
       std::memcpy(rec + 80, pl[2] + r * rb[2] + sbi * 4, 4);
-    } else if (fmt == 3) {
-      pack_le(c, 256, 3, rec);
+    } else if (fmt == 3 || fmt == kQ3SBPlanes) {
+      if (fmt == 3) {
+        pack_le(c, 256, 3, rec);
+      } else {
+        uint8_t lo2[256], hi1[256];
+        for (int i = 0; i < 256; ++i) { lo2[i] = c[i] & 3; hi1[i] = c[i] >> 2; }
+        pack_le(lo2, 256, 2, rec);
+        pack_le(hi1, 256, 1, rec + 64);
+      }
       std::memcpy(rec + 96, pl[2] + r * rb[2] + sbi * 12, 12);
       std::memcpy(rec + 108, pl[3] + r * rb[3] + sbi * 2, 2);
     } else if (fmt == 5) {
@@ -782,7 +804,8 @@ int qg_quantize(int fmt, const float *w, int64_t n, int64_t k, int64_t ldw, uint
   return parallel_rows(n, k, [&](int64_t r0, int64_t r1) {
     for (int64_t r = r0; r < r1; ++r)
       for (int64_t b = 0; b < S; ++b) {
-        int st = quantize_block_sb(s, sb_base(fmt), w + r * ldw + b * kQK, canonical + (r * S + b) * s.rec);
+        int st = quantize_block_sb(s, fmt == kQ3SBPlanes ? fmt : sb_base(fmt), w + r * ldw + b * kQK,
+                                   canonical + (r * S + b) * s.rec);
         if (st != QG_OK) return st;
       }
     return (int)QG_OK;
@@ -800,6 +823,7 @@ int quantize_q3sb_bf16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_
 int quantize_q5sb_bf16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(15, w, n, k, ldw, c); }
 int quantize_q6sb_bf16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(16, w, n, k, ldw, c); }
 int quantize_q3g32(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(17, w, n, k, ldw, c); }
+int quantize_q3sb_planes(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(14, w, n, k, ldw, c); }
 int quantize_q5g32(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(18, w, n, k, ldw, c); }
 int quantize_q2sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(2, w, n, k, ldw, c); }
 int quantize_q3sb(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c) { return qg_quantize(3, w, n, k, ldw, c); }
@@ -820,7 +844,7 @@ int qg_to_device_layout(int fmt, const uint8_t *canonical, int64_t n, int64_t k,
     P.rb[p] = L.plane_row_bytes[p];
   }
   return parallel_rows(n, k * 4, [&](int64_t r0, int64_t r1) {
-    for (int64_t r = r0; r < r1; ++r) row_to_device(sb_base(fmt), canonical, k, r, n, P);
+    for (int64_t r = r0; r < r1; ++r) row_to_device(fmt == kQ3SBPlanes ? fmt : sb_base(fmt), canonical, k, r, n, P);
     return (int)QG_OK;
   });
 }
@@ -839,7 +863,7 @@ int qg_from_device_layout(int fmt, const uint8_t *dev, int64_t n, int64_t k, uin
     rb[p] = L.plane_row_bytes[p];
   }
   return parallel_rows(n, k * 4, [&](int64_t r0, int64_t r1) {
-    for (int64_t r = r0; r < r1; ++r) row_from_device(sb_base(fmt), pl, rb, k, r, n, canonical);
+    for (int64_t r = r0; r < r1; ++r) row_from_device(fmt == kQ3SBPlanes ? fmt : sb_base(fmt), pl, rb, k, r, n, canonical);
     return (int)QG_OK;
   });
 }

@@ -97,8 +97,11 @@ constexpr int kQ4G32H = 11;
 // Super-block formats with bf16 super-scales d (and dmin): the base format's code + 10
 // (12, 13, 15, 16 for q2sb, q3sb, q5sb, q6sb). Same records, planes and kernels as the base
 // format; only the 16-bit super-scale fields hold bf16 instead of fp16.
+// q3sb_planes (code 14) is q3sb with the record's codes in a 2-bit and a 1-bit plane: its
+// device layout is q3sb's.
+constexpr int kQ3SBPlanes = 14;
 QG_HOST_DEVICE constexpr bool sb_bf16(int fmt) { return fmt == 12 || fmt == 13 || fmt == 15 || fmt == 16; }
-QG_HOST_DEVICE constexpr int sb_base(int fmt) { return sb_bf16(fmt) ? fmt - 10 : fmt; }
+QG_HOST_DEVICE constexpr int sb_base(int fmt) { return sb_bf16(fmt) ? fmt - 10 : fmt == kQ3SBPlanes ? 3 : fmt; }
 
 // Plain group-wise codes with an fp32 scale and min per group of 32: 3-bit (code 17) and
 // 5-bit (code 18); code bits of the format (0 for the others).
@@ -108,7 +111,7 @@ QG_HOST_DEVICE constexpr int gw_bits(int fmt) { return fmt == kQ3G32 ? 3 : fmt =
 
 inline bool fmt_valid(int fmt) {
   return (fmt >= 2 && fmt <= 6) || q4_group(fmt) != 0 || fmt == kQ4A32 || fmt == kQ4G32H || sb_bf16(fmt) ||
-         gw_bits(fmt) != 0;
+         gw_bits(fmt) != 0 || fmt == kQ3SBPlanes;
 }
 
 // K must be a multiple of this: 32 for q4g32 (a row may end in half a unit), whole units

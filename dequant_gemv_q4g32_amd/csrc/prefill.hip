@@ -236,6 +236,7 @@ int launch_prefill(int fmt, const void *w, const uint16_t *X, int64_t ldx, void 
     case 11: return launch(prefill_kernel<11>, grid, block, 0, s, a);
     case 12: return launch(prefill_kernel<12>, grid, block, 0, s, a);
     case 13: return launch(prefill_kernel<13>, grid, block, 0, s, a);
+    case 14: return launch(prefill_kernel<3>, grid, block, 0, s, a);   // q3sb's device layout
     case 15: return launch(prefill_kernel<15>, grid, block, 0, s, a);
     case 16: return launch(prefill_kernel<16>, grid, block, 0, s, a);
     case 17: return launch(prefill_kernel<17>, grid, block, 0, s, a);

@@ -212,6 +212,7 @@ int launch_skinny(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *
     case 11: return launch(skinny_kernel<11>, grid, block, shm, s, a);
     case 12: return launch(skinny_kernel<12>, grid, block, shm, s, a);
     case 13: return launch(skinny_kernel<13>, grid, block, shm, s, a);
+    case 14: return launch(skinny_kernel<3>, grid, block, shm, s, a);   // q3sb's device layout
     case 15: return launch(skinny_kernel<15>, grid, block, shm, s, a);
     case 16: return launch(skinny_kernel<16>, grid, block, shm, s, a);
     case 17: return launch(skinny_kernel<17>, grid, block, shm, s, a);

@@ -36,6 +36,10 @@
  *             bf16_ceil in place of fp16_ceil in the rule below. The GEMM paths for m > 8
  *             multiply fp16 W_hat on the matrix cores: weights beyond the fp16 range (which
  *             only bf16 super-scales can express) need m <= 8 there.
+ *   QG_Q3SB_PLANES  q3sb with the record's 96 code bytes stored as a 64-byte plane of the low
+ *             2 bits (2-bit stream) and a 32-byte plane of the high bit (1-bit stream)
+ *             ("二三五六位量化" page section 2.3: split widths that do not divide a byte into
+ *             planes); same fields, rule and device layout as QG_Q3SB (110 B, 3.4375 bpw).
  *   QG_Q3G32, QG_Q5G32  plain group-wise 3- and 5-bit codes c with an fp32 scale s and an fp32
  *             min m per group of 32 (the form of "二三五六位量化" page section 3.3's gemv_q3:
  *             w_hat = s*c + m): m = min w, s = max((max w - min w) / (2^b - 1), 1e-12),
@@ -59,7 +63,8 @@
  *              little-endian b-bit stream [n][k*b/8], then fp32 scales [n][k/32], then fp32
  *              mins [n][k/32]. Super-block formats: records
  *              [n][k/256] of 84/110/176/210 bytes; fields in the byte table's column order
- *              (codes [, high-bit plane], sub-scales, d [, dmin]); every bit field is a
+ *              (codes [, high-bit plane], sub-scales, d [, dmin]; q3sb_planes: low-2-bit plane,
+ *              high-bit plane, sub-scales, d); every bit field is a
  *              little-endian bitstream (code i at bits [b*i, b*i + b), section 2.2's unpack3
  *              and unpack5); q2sb sub-block byte = sc | m << 4; q5sb's 12 bytes hold sixteen
  *              6-bit fields sc0..sc7, m0..m7; fp16 values little-endian.
@@ -103,6 +108,7 @@ typedef enum qg_format {
   QG_Q4G32H = 11,
   QG_Q2SB_BF16 = 12,
   QG_Q3SB_BF16 = 13,
+  QG_Q3SB_PLANES = 14,
   QG_Q5SB_BF16 = 15,
   QG_Q6SB_BF16 = 16,
   QG_Q3G32 = 17,
@@ -176,6 +182,7 @@ int quantize_q5sb_bf16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_
 int quantize_q6sb_bf16(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
 int quantize_q3g32(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
 int quantize_q5g32(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
+int quantize_q3sb_planes(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
 
 /* Canonical encoding (host) -> device layout (host buffer of qg_device_layout().total_bytes;
  * padding is zeroed). A pure bit permutation. */
@@ -207,6 +214,7 @@ int dequant_gemv_q5sb_bf16(const void *w, const uint16_t *x, uint16_t *y, int64_
 int dequant_gemv_q6sb_bf16(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
 int dequant_gemv_q3g32(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
 int dequant_gemv_q5g32(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
+int dequant_gemv_q3sb_planes(const void *w, const uint16_t *x, uint16_t *y, int64_t n, int64_t k, void *stream);
 
 /* Generic form: y_f32 != 0 writes fp32 y (4-byte aligned) instead of fp16. */
 int qg_gemv(int fmt, const void *w, const uint16_t *x, void *y, int y_f32, int64_t n, int64_t k, void *stream);
@@ -264,6 +272,8 @@ int dequant_gemm_q3g32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *
                         int64_t m, int64_t n, int64_t k, void *stream);
 int dequant_gemm_q5g32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
                         int64_t m, int64_t n, int64_t k, void *stream);
+int dequant_gemm_q3sb_planes(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
+                              int64_t m, int64_t n, int64_t k, void *stream);
 /* Generic form; y_f32 != 0 writes fp32 Y (4-byte aligned). */
 int qg_gemm(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int64_t ldy, int y_f32,
             int64_t m, int64_t n, int64_t k, void *stream);
@@ -335,6 +345,7 @@ int dequantize_q5sb_bf16(const void *w, float *w_out, uint8_t *codes_out, int64_
 int dequantize_q6sb_bf16(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 int dequantize_q3g32(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 int dequantize_q5g32(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
+int dequantize_q3sb_planes(const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 int qg_dequantize(int fmt, const void *w, float *w_out, uint8_t *codes_out, int64_t n, int64_t k, void *stream);
 
 /* ---- measurement (device) -----------------------------------------------------------------

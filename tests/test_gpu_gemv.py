@@ -15,7 +15,7 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb", "q4g16", "q4g64", "q4g128", "q4a32", "q4g32h",
-        "q2sb_bf16", "q3sb_bf16", "q5sb_bf16", "q6sb_bf16", "q3g32", "q5g32"]
+        "q2sb_bf16", "q3sb_bf16", "q5sb_bf16", "q6sb_bf16", "q3g32", "q5g32", "q3sb_planes"]
 # (n, k): several tiles, ragged n, K split over 1, 2, 3 and 7 waves
 SHAPES = [(37, 512), (16, 256), (1001, 1024), (64, 4096), (20, 4352), (9, 8192), (33, 11008), (5, 28672)]
 

@@ -16,7 +16,7 @@ from oracle import superblock as sb
 from workloads import laplace_weights, uniform_codes
 
 FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb", "q4g16", "q4g64", "q4g128", "q4a32", "q4g32h",
-        "q2sb_bf16", "q3sb_bf16", "q5sb_bf16", "q6sb_bf16", "q3g32", "q5g32"]
+        "q2sb_bf16", "q3sb_bf16", "q5sb_bf16", "q6sb_bf16", "q3g32", "q5g32", "q3sb_planes"]
 
 
 def oracle_canonical(fmt, w):
@@ -147,7 +147,6 @@ def test_error_codes():
         with pytest.raises(qg.QGError) as e:
             qg.quantize(fmt, big)
         assert e.value.status == -5
-    assert qg.lib.qg_quantize(14, None, 1, 256, 256, None) == -6
     assert qg.lib.qg_quantize(19, None, 1, 256, 256, None) == -6
     for fmt in ("q2sb_bf16", "q3sb_bf16", "q5sb_bf16", "q6sb_bf16"):      # bf16 covers 1e10
         assert np.array_equal(qg.quantize(fmt, big), oracle_canonical(fmt, big))
@@ -164,7 +163,7 @@ def test_device_entry_points_validate_without_launching():
     assert L.qg_gemv(3, None, None, None, 0, 4, 100, None) == -2          # k % 256
     assert L.qg_gemv(4, None, None, None, 0, 4, 48, None) == -2           # k % 32
     assert L.qg_gemv(10, None, None, None, 0, 4, 96, None) == -2          # q4a32: k % 64
-    assert L.qg_gemv(14, None, None, None, 0, 4, 256, None) == -6          # format
+    assert L.qg_gemv(19, None, None, None, 0, 4, 256, None) == -6          # format
     assert L.qg_gemv(3, None, None, None, 0, 0, 256, None) == 0           # n == 0: no-op
     assert L.qg_gemv(3, None, None, None, 0, 4, 256, None) == -1          # null
     assert L.qg_gemv(3, 256, 16, 3, 0, 4, 256, None) == -3                # y misaligned
@@ -183,7 +182,7 @@ def test_device_entry_points_validate_without_launching():
     assert L.qg_gemm(3, 256, 16, 260, 2, 4, 0, 2, 4, 256, None) == -3     # ldx % 8
     assert L.qg_gemm(3, None, 16, 256, 2, 4, 0, 2, 4, 256, None) == -1    # null w
     assert L.qg_gemm(5, 256, 16, 256, 2, 4, 0, 2, 4, 100, None) == -2     # k % 256
-    assert L.qg_gemm(14, 256, 16, 256, 2, 4, 0, 2, 4, 256, None) == -6     # format
+    assert L.qg_gemm(19, 256, 16, 256, 2, 4, 0, 2, 4, 256, None) == -6     # format
     assert L.dequant_gemm_q6sb(256, 16, 256, 3, 4, 2, 4, 256, None) == -3  # Y misaligned
 
 
@@ -213,7 +212,7 @@ def test_grouped_entry_point_validates_every_matrix_first():
     assert call(3, **ok, m=2, ldx=[256, 500]) == -2                       # ldx < k
     assert call(3, **ok, m=2, ldy=[4, 7]) == -2                           # ldy < n
     assert call(3, **ok, m=2, ldx=[260, 512]) == -3                       # ldx % 8
-    assert call(14, **ok) == -6                                            # format
+    assert call(19, **ok) == -6                                            # format
     assert call(3, [256] * 9, [16] * 9, [2] * 9, [4] * 9, [256] * 9) == -2   # more than 8
     assert call(3, **ok, m=0) == 0                                        # m == 0: no-op
     assert call(3, **{**ok, "ns": [0, 0]}) == 0                           # n == 0: no-op
@@ -229,7 +228,7 @@ def test_act_order_entry_point_validates_without_launching():
     assert L.qg_gemm_act_order(3, 256, 16, 256, 32, 2, 4, 0, 9, 4, 256, None) == -2      # m > 8
     assert L.qg_gemm_act_order(3, 256, 16, 256, 32, 2, 4, 0, 1, 4, 100, None) == -2      # k % 256
     assert L.qg_gemm_act_order(3, 256, 16, 128, 32, 2, 4, 0, 2, 4, 256, None) == -2      # ldx < k
-    assert L.qg_gemm_act_order(14, 256, 16, 256, 32, 2, 4, 0, 1, 4, 256, None) == -6      # format
+    assert L.qg_gemm_act_order(19, 256, 16, 256, 32, 2, 4, 0, 1, 4, 256, None) == -6      # format
     assert L.qg_gemm_act_order(3, 256, 16, 256, 32, 2, 4, 0, 0, 4, 256, None) == 0       # m == 0
 
 
