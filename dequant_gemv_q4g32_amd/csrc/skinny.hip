@@ -12,9 +12,9 @@
 // consecutive units: it decodes those 64 weights to 32 fp16 pairs, which are the B operands
 // of 8 MFMAs (4 pairs each). The A operands are the activations of the same k indices for
 // activation row l % 16, loaded once per pass into registers and reused for every row tile
-// of the wave. Waves of a workgroup split K and add their partial 16 x 16 tiles into one LDS
-// tile per row tile (LDS float atomics: the order of those fp32 additions, and so the last
-// bits of the result, can differ from run to run).
+// of the wave. Waves of a workgroup split K; each keeps its partial 16 x 16 tiles in its own
+// LDS slots (summed over its passes), and after one barrier the slots are added in wave
+// order, so the result does not depend on timing.
 #include <hip/hip_runtime.h>
 
 #include "../../include/qgemv.h"
@@ -47,7 +47,8 @@ struct SkinnyArgs {
 constexpr int kDW = 1;                     // steps of 4 units per wave and pass
 constexpr int kStages = 2;                  // register stages over row tiles (3 and 4 measured slower)
 constexpr int kSkinnyMaxWk = 16;
-constexpr int kSkinnyMaxNb = 32;           // LDS: nb * 256 floats (a multiple of every kStages)
+constexpr int kSkinnyMaxNb = 32;           // row tiles per workgroup (a multiple of kStages)
+constexpr int64_t kSkinnyLds = 64 * 1024;  // LDS for the partial tiles: wk * nb * 256 floats
 constexpr uint32_t kSkX = 0x7FFFFFF0u;     // activation buffer range; offsets past it read 0
 constexpr int64_t kSkinnyWaves = 4096;     // about 4 waves per SIMD
 
@@ -55,7 +56,7 @@ template <int F>
 __global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs a) {
   using U = Unit<F>;
   using Raw = typename U::Raw;
-  extern __shared__ float red[];           // [nb][256] output tiles
+  extern __shared__ float red[];           // [wk][nb][256] partial output tiles
   const int lane = threadIdx.x & 63;
   const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rl = lane & 15, g = lane >> 4;
@@ -68,8 +69,7 @@ __global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs a) {
     L.prb[p] = (uint32_t)a.prb[p];
   }
   L.set_halves(a.units);
-  for (int i = threadIdx.x; i < a.nb * 256; i += blockDim.x) red[i] = 0.f;
-  __syncthreads();
+  float *slots = red + (size_t)wk * a.nb * 256;      // this wave's partial tiles
   const rsrc_t xr = make_rsrc(a.x, kSkX);
   const bool mlive = rl < a.m;
   const uint32_t xrow = (uint32_t)(rl * a.ldx * 2);
@@ -133,8 +133,12 @@ __global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs a) {
       const f32x4 acc = acc2[0] + acc2[1];
       // D of a 16 x 16 MFMA: lane l holds column l % 16 (weight row) and rows 4 (l / 16) + e
       // (activation rows); tile index m * 16 + n
+      // (each lane owns 4 of the tile's 256 sums; the first pass stores, later passes add)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) atomicAdd(&red[j * 256 + (4 * g + e) * 16 + rl], acc[e]);
+      for (int e = 0; e < 4; ++e) {
+        float &slot = slots[j * 256 + (4 * g + e) * 16 + rl];
+        slot = kp == 0 ? acc[e] : slot + acc[e];
+      }
     };
     // kStages register stages over the row tiles (loads of kStages - 1 tiles in flight while
     // one is computed); prefetches past the last tile re-load it
@@ -156,7 +160,8 @@ __global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs a) {
     const int j = i >> 8, idx = i & 255, mm = idx >> 4;
     const int64_t row = (tile0 + j) * 16 + (idx & 15);
     if (mm >= a.m || row >= a.n) continue;
-    const float sum = red[i];
+    float sum = red[i];
+    for (int w = 1; w < a.wk; ++w) sum += red[(size_t)w * a.nb * 256 + i];
     const int64_t o = (int64_t)mm * a.ldy + row;
     if (a.y_f32) reinterpret_cast<float *>(a.y)[o] = sum;
     else reinterpret_cast<_Float16 *>(a.y)[o] = (_Float16)sum;
@@ -196,9 +201,11 @@ int launch_skinny(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *
   int64_t nb = tiles * a.wk / kSkinnyWaves;
   nb = nb < 1 ? 1 : (nb > kSkinnyMaxNb ? kSkinnyMaxNb : nb);
   nb = (nb + kStages - 1) / kStages * kStages;      // whole pipeline rounds; extra tiles are past n
+  const int64_t nb_lds = kSkinnyLds / (a.wk * 256 * (int64_t)sizeof(float)) / kStages * kStages;
+  if (nb > nb_lds) nb = nb_lds;                     // every wave's partial tiles fit in LDS
   a.nb = (int)nb;
   const dim3 grid((unsigned)((tiles + nb - 1) / nb)), block((unsigned)(64 * a.wk));
-  const size_t shm = (size_t)nb * 256 * sizeof(float);
+  const size_t shm = (size_t)a.wk * nb * 256 * sizeof(float);
   switch (fmt) {
     case 2: return launch(skinny_kernel<2>, grid, block, shm, s, a);
     case 3: return launch(skinny_kernel<3>, grid, block, shm, s, a);
