@@ -536,6 +536,7 @@ constexpr int64_t kActOrderLds = 64 * 1024;   // most activation bytes an act-or
 constexpr int kMinBatches = 4;
 constexpr int kMaxM = 8;                   // activation rows one streaming launch serves
 constexpr int kSkinnyMaxM = 16;            // activation rows of the matrix-core decode kernel
+constexpr int kGemmStreamMaxM = 4;         // qg_gemm's streaming rows (grouped and act-order: kMaxM)
 
 // Resident waves per SIMD that a kernel's register and LDS use allow (asked once per kernel).
 int waves_per_simd(const void *kernel) {
@@ -854,10 +855,11 @@ int qg_gemm(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int
   GemvArgs a{};
   int st = fill_args(fmt, w, n, k, a);
   if (st != QG_OK) return st;
-  // up to 8 activation rows: the streaming kernel (every decoded code pair meets each row in
-  // a v_dot2); 9 to 16: fp16 w_hat on the matrix cores in one weight stream; more rows:
-  // LDS-staged fp16 tiles on the matrix cores
-  if (m > kMaxM && m <= kSkinnyMaxM) return launch_skinny(fmt, w, X, ldx, Y, ldy, y_f32, m, n, k, s);
+  // up to 4 activation rows: the streaming kernel (every decoded code pair meets each row in
+  // a v_dot2); 5 to 16: fp16 w_hat on the matrix cores in one weight stream (from 5 rows
+  // on, the v_dot2 per row and code pair cost more than the decode that the matrix cores
+  // need once); more rows: LDS-staged fp16 tiles on the matrix cores
+  if (m > kGemmStreamMaxM && m <= kSkinnyMaxM) return launch_skinny(fmt, w, X, ldx, Y, ldy, y_f32, m, n, k, s);
   if (m > kSkinnyMaxM) return launch_prefill(fmt, w, X, ldx, Y, ldy, y_f32, m, n, k, s);
   a.x = X;
   a.ldx = ldx;

@@ -1,4 +1,4 @@
-// Dequant GEMM for a decode batch of 9 to 16 activation rows on the matrix cores, gfx950.
+// Dequant GEMM for a decode batch of 5 to 16 activation rows on the matrix cores, gfx950.
 //
 // Method: "二三五六位量化" page section 1.2 and DBHOO-CIM page section 6 (a decode batch is
 // the GEMV with several activation rows, still bound by the weight stream). On the vector

@@ -33,9 +33,10 @@
  *   QG_Q2SB_BF16, QG_Q3SB_BF16, QG_Q5SB_BF16, QG_Q6SB_BF16  the same four formats with the
  *             super-scales d (and dmin) stored as bf16 instead of fp16 ("二三五六位量化" page
  *             section 2.3: against fp16 overflow of the super-scale); same records and sizes,
- *             bf16_ceil in place of fp16_ceil in the rule below. The GEMM paths for m > 8
+ *             bf16_ceil in place of fp16_ceil in the rule below. The GEMM paths for m > 4
  *             multiply fp16 W_hat on the matrix cores: weights beyond the fp16 range (which
- *             only bf16 super-scales can express) need m <= 8 there.
+ *             only bf16 super-scales can express) need the streaming kernel (qg_gemm with
+ *             m <= 4, qg_gemm_grouped or qg_gemm_act_order with m <= 8).
  *   QG_Q3SB_PLANES  q3sb with the record's 96 code bytes stored as a 64-byte plane of the low
  *             2 bits (2-bit stream) and a 32-byte plane of the high bit (1-bit stream)
  *             ("二三五六位量化" page section 2.3: split widths that do not divide a byte into
@@ -231,14 +232,15 @@ int qg_gemv_batched(int fmt, const void *w, int64_t w_stride, const uint16_t *x,
  * Y[i][r] = sum_c X[i][c] * W_hat[r][c] for i < m, r < n: X fp16 [m][ldx] (16-byte aligned,
  * ldx >= k and a multiple of 8 when m > 1), Y fp16 [m][ldy] (ldy >= n when m > 1). Batched
  * decode: the weights are streamed once per launch and each decoded code meets all the
- * launch's activation rows, up to 8 of them ("二三五六位量化" page section 1.2: decode
+ * launch's activation rows, up to 16 of them ("二三五六位量化" page section 1.2: decode
  * batches and prefill are the same contraction with more activation rows; DBHOO-CIM page
  * section 6: still bandwidth-bound at small batch, compute-bound at large batch). Any m >= 1:
- * m <= 8 runs on the vector units (each decoded code pair meets every activation row in a
- * v_dot2), 9 <= m <= 16 decodes each code once to fp16 and multiplies on the matrix cores
- * in the same single weight stream, and m > 16 (prefill) stages fp16 weight and activation
- * tiles in LDS for 32x32 matrix-core tiles. Limits as dequant_gemv_*; for m > 8 also
- * ldx < 2^23 (32-bit activation offsets within a 128-row tile). m == 0 or n == 0 is a no-op; k == 0 writes
+ * m <= 4 runs on the vector units (each decoded code pair meets every activation row in a
+ * v_dot2; the kernel of qg_gemv, qg_gemm_grouped and qg_gemm_act_order), 5 <= m <= 16
+ * decodes each code once to fp16 and multiplies on the matrix cores in the same single
+ * weight stream, and m > 16 (prefill) stages fp16 weight and activation tiles in LDS for
+ * 32x32 matrix-core tiles. Limits as dequant_gemv_*; for m > 4 also ldx < 2^23 (32-bit
+ * activation offsets within a 128-row tile). m == 0 or n == 0 is a no-op; k == 0 writes
  * zeros. Errors as dequant_gemv_*. */
 int dequant_gemm_q4g32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
                        int64_t m, int64_t n, int64_t k, void *stream);
@@ -284,9 +286,9 @@ int qg_gemm(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int
  * original column perm[c], so Y[i][r] = sum_c X[i][perm[c]] * W_hat[r][c]. perm: int32 [k] on
  * the device (16-byte aligned), entries in [0, k) (an entry outside that range reads an
  * activation of 0; it never reads outside X). The gather is fused into the streaming
- * kernel's activation load, so the result equals qg_gemm on the gathered activations bit for
- * bit. m: 0..8 activation rows (the streaming kernel); other arguments, limits and errors as
- * qg_gemm. */
+ * kernel's activation load, so the result equals that kernel's on the gathered activations
+ * bit for bit (qg_gemm_grouped's for any m, qg_gemm's for m <= 4). m: 0..8 activation rows
+ * (the streaming kernel); other arguments, limits and errors as qg_gemm. */
 int qg_gemm_act_order(int fmt, const void *w, const uint16_t *X, int64_t ldx, const int32_t *perm, void *Y,
                       int64_t ldy, int y_f32, int64_t m, int64_t n, int64_t k, void *stream);
 
@@ -296,7 +298,8 @@ int qg_gemm_act_order(int fmt, const void *w, const uint16_t *X, int64_t ldx, co
  * m > 1 (else the rows are dense). Each matrix is checked as by qg_gemm (for m <= 8) before
  * anything is launched; a matrix with n[g] == 0 is skipped and one with k[g] == 0 gets
  * zeros. Every matrix runs on the streaming vector-unit kernel of qg_gemv and shares its
- * numerics. This serves the projections of a decode step that read one activation (q, k and
+ * numerics (qg_gemm's for m <= 4; for 5 <= m <= 8 qg_gemm uses the matrix cores and agrees
+ * within the tolerance, not bit for bit). This serves the projections of a decode step that read one activation (q, k and
  * v; gate and up) or simply follow each other, with one launch's start and drain instead
  * of one per matrix ("二三五六位量化" page section 1.2: the decode pass is one weight stream
  * bound by bandwidth). Errors: QG_ERR_SHAPE (count > 8, m > 8, or a matrix's shape),

@@ -77,8 +77,16 @@ def test_gemm_many_k_passes(fmt, m):
     _, w_hat = oracle_decode(fmt, w)
     x = activations(m, k, 77 + m)
     y_ref, bound = oracle_y(w_hat, x)
-    y = _run(fmt, device_weights(fmt, w), x, n, k, True)
+    wd = device_weights(fmt, w)
+    y = _run(fmt, wd, x, n, k, True)
     assert_close(y, y_ref, bound, f"{fmt} m={m} {n}x{k}")
+    if m > 4:
+        # qg_gemm takes the matrix-core kernel from 5 rows; the streaming kernel's passes
+        # over K at 8 rows are reached through the grouped entry point
+        yg = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        qg.gemm_grouped(fmt, [wd], [torch.from_numpy(x).cuda()], [(n, k)], outs=[yg])
+        torch.cuda.synchronize()
+        assert_close(yg.cpu().numpy(), y_ref, bound, f"{fmt} m={m} {n}x{k} streaming")
 
 
 @pytest.mark.parametrize("fmt", FMTS)

@@ -188,8 +188,9 @@ def test_q4a32_zero_points_over_their_range():
 def test_bf16_super_scales_past_the_fp16_range(fmt):
     """bf16 super-scales: rows with super-blocks whose scale would overflow fp16 (weights of
     order 1e8) beside ordinary ones; decode bit-exact, outputs (fp32) within the tolerance
-    for 1, 4 and 8 activation rows (the streaming kernel: the matrix-core paths for more rows
-    take W_hat through fp16, whose range such weights exceed)."""
+    for 1, 2 and 4 activation rows through qg_gemm and 8 through the grouped entry point (the
+    streaming kernel: the matrix-core paths take W_hat through fp16, whose range such weights
+    exceed)."""
     n, k = 40, 1024
     w = laplace_weights(n, k, 0.02, 77)
     w[3, 300] = np.float32(2.0e8)
@@ -199,8 +200,12 @@ def test_bf16_super_scales_past_the_fp16_range(fmt):
     vals, codes = qg.dequantize(fmt, wd, n, k)
     assert np.array_equal(codes.cpu().numpy(), codes_ref)
     assert np.array_equal(vals.cpu().numpy(), w_hat.astype(np.float32))
-    for m in (1, 4, 8):
+    for m in (1, 2, 4, 8):
         x = _x(k, 78 + m, m)
         y_ref, bound = oracle_y(w_hat, x)
-        y = qg.gemm(fmt, wd, torch.from_numpy(x).cuda(), n, k, out_f32=True)
+        if m <= 4:
+            y = qg.gemm(fmt, wd, torch.from_numpy(x).cuda(), n, k, out_f32=True)
+        else:
+            y = torch.empty((m, n), dtype=torch.float32, device="cuda")
+            qg.gemm_grouped(fmt, [wd], [torch.from_numpy(x).cuda()], [(n, k)], outs=[y])
         assert_close(y.cpu().numpy(), y_ref, bound, f"{fmt} m={m}")
