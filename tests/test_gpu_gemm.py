@@ -1,10 +1,11 @@
 """GPU parity tests for the dequant GEMM with a few activation rows, against the oracle.
 
 Bar: every output Y[i, r] within 2e-3 * sum_k |X[i,k] W_hat[r,k]| (fp16 and fp32 output).
-Covers every row count the streaming kernels are built for (1, 2, 4 and 8 rows per launch,
-with the unused rows of a launch masked), more rows than one launch serves, strided X and Y,
-K split over several waves and over several passes, ragged n, and the full-size decode
-workloads with 2, 4 and 8 activation rows on sampled output rows.
+Covers the three kernels qg_gemm routes to (the streaming kernel for 1-4 rows, built for 1,
+2 and 4 rows per launch with the unused rows masked; the matrix-core decode kernel for 5-16;
+the prefill kernel beyond), strided X and Y, K split over several waves and over several
+passes (the streaming kernel's passes at 8 rows through the grouped entry point), ragged n,
+and the full-size decode workloads with 2, 4 and 8 activation rows on sampled output rows.
 """
 import numpy as np
 import pytest
@@ -20,7 +21,7 @@ FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb", "q4g16", "q4g64", "q4g128", "q4
         "q2sb_bf16", "q3sb_bf16", "q5sb_bf16", "q6sb_bf16", "q3g32", "q5g32", "q3sb_planes"]
 MS = [1, 2, 3, 4, 5, 8, 11, 17]
 # (n, k): several row blocks and a ragged tail, K over 1..8 waves, and (5, 28672) over two
-# passes when eight rows share a launch
+# passes
 SHAPES = [(37, 512), (1001, 1024), (20, 4352), (9, 8192), (5, 28672)]
 
 
