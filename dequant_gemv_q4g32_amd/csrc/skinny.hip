@@ -46,17 +46,21 @@ struct SkinnyArgs {
 
 constexpr int kDW = 1;                     // steps of 4 units per wave and pass
 constexpr int kStages = 2;                  // register stages over row tiles (3 and 4 measured slower)
-constexpr int kSkinnyMaxWk = 16;
+constexpr int kSkinnyMaxWk = 8;
 constexpr int kSkinnyMaxNb = 32;           // row tiles per workgroup (a multiple of kStages)
-constexpr int64_t kSkinnyLds = 64 * 1024;  // LDS for the partial tiles: wk * nb * 256 floats
+constexpr int kStageLine = 144;            // bytes per staged activation line (128 + 16 of padding)
+constexpr int64_t kStageBytes = 64 * kStageLine;   // one wave's staged activations
+constexpr int64_t kSkinnyLds = 128 * 1024; // LDS: staging for every wave, then wk * nb * 256 floats
 constexpr uint32_t kSkX = 0x7FFFFFF0u;     // activation buffer range; offsets past it read 0
 constexpr int64_t kSkinnyWaves = 4096;     // about 4 waves per SIMD
 
 template <int F>
-__global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs a) {
+__global__ __launch_bounds__(64 * kSkinnyMaxWk) void skinny_kernel(SkinnyArgs a) {
   using U = Unit<F>;
   using Raw = typename U::Raw;
-  extern __shared__ float red[];           // [wk][nb][256] partial output tiles
+  static_assert(kDW == 1, "one step of 4 units per wave and pass");
+  // [wk][64 lines of kStageLine bytes] staged activations, then [wk][nb][256] partial tiles
+  extern __shared__ float red[];
   const int lane = threadIdx.x & 63;
   const int wk = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int rl = lane & 15, g = lane >> 4;
@@ -69,10 +73,11 @@ __global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs a) {
     L.prb[p] = (uint32_t)a.prb[p];
   }
   L.set_halves(a.units);
-  float *slots = red + (size_t)wk * a.nb * 256;      // this wave's partial tiles
+  uint8_t *stage = reinterpret_cast<uint8_t *>(red) + wk * kStageBytes;   // this wave's lines
+  float *const tiles = red + (a.wk * kStageBytes) / 4;                    // every wave's partial tiles
+  float *slots = tiles + (size_t)wk * a.nb * 256;                          // this wave's
   const rsrc_t xr = make_rsrc(a.x, kSkX);
-  const bool mlive = rl < a.m;
-  const uint32_t xrow = (uint32_t)(rl * a.ldx * 2);
+  const int cl = lane & 7, li = lane >> 3;         // staging loads: chunk, line within 8
 
   for (int kp = 0; kp < a.kpasses; ++kp) {
     // This wave's units in this pass: kDW steps of 4 consecutive units; lane group g takes
@@ -87,16 +92,26 @@ __global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs a) {
       ulive[d] = u < a.units;
       unit[d] = ulive[d] ? u : a.units - 1;
     }
-    // activations (A operands): for MFMA s of a unit, local pairs 4 (s & 3).. of half s >> 2
+    // activations (A operands): lane (rl, g) needs the 128 bytes of activation row rl in unit
+    // g, the "line" rl + 16 g. Loaded with 8 consecutive lanes per line (instruction j reads
+    // lines 8j..8j+7, one cache line each) into this wave's LDS lines, then each lane reads
+    // its own line: for MFMA s of a unit, local pairs 4 (s & 3).. of half s >> 2.
     half8_t A[kDW][8];
+    {
+      u32x4 v[8];
 #pragma unroll
-    for (int d = 0; d < kDW; ++d)
-#pragma unroll
-      for (int s8 = 0; s8 < 8; ++s8) {
-        const int64_t kk = unit[d] * kUnit + 2 * U::pidx(s8 >> 2, 4 * (s8 & 3), 2);
-        const bool ok = mlive && ulive[d] && kk < a.k;
-        A[d][s8] = __builtin_bit_cast(half8_t, bld4c(xr, ok ? xrow + (uint32_t)(kk * 2) : kSkX, 0));
+      for (int j = 0; j < 8; ++j) {
+        const int line = 8 * j + li, arow = line & 15;
+        const int64_t u = 4 * step0 + (line >> 4), kk = u * kUnit + 8 * cl;
+        const bool ok = arow < a.m && u < a.units && kk < a.k;
+        v[j] = bld4c(xr, ok ? (uint32_t)(arow * a.ldx * 2 + kk * 2) : kSkX, 0);
       }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4 *>(stage + (8 * j + li) * kStageLine + 16 * cl) = v[j];
+#pragma unroll
+      for (int s8 = 0; s8 < 8; ++s8)
+        A[0][s8] = *reinterpret_cast<const half8_t *>(stage + lane * kStageLine + 4 * U::pidx(s8 >> 2, 4 * (s8 & 3), 2));
+    }
 
     auto load = [&](Raw *q, int j) {
       const int64_t t = tile0 + (j < a.nb ? j : a.nb - 1);
@@ -160,8 +175,8 @@ __global__ __launch_bounds__(1024) void skinny_kernel(SkinnyArgs a) {
     const int j = i >> 8, idx = i & 255, mm = idx >> 4;
     const int64_t row = (tile0 + j) * 16 + (idx & 15);
     if (mm >= a.m || row >= a.n) continue;
-    float sum = red[i];
-    for (int w = 1; w < a.wk; ++w) sum += red[(size_t)w * a.nb * 256 + i];
+    float sum = tiles[i];
+    for (int w = 1; w < a.wk; ++w) sum += tiles[(size_t)w * a.nb * 256 + i];
     const int64_t o = (int64_t)mm * a.ldy + row;
     if (a.y_f32) reinterpret_cast<float *>(a.y)[o] = sum;
     else reinterpret_cast<_Float16 *>(a.y)[o] = (_Float16)sum;
@@ -201,11 +216,11 @@ int launch_skinny(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *
   int64_t nb = tiles * a.wk / kSkinnyWaves;
   nb = nb < 1 ? 1 : (nb > kSkinnyMaxNb ? kSkinnyMaxNb : nb);
   nb = (nb + kStages - 1) / kStages * kStages;      // whole pipeline rounds; extra tiles are past n
-  const int64_t nb_lds = kSkinnyLds / (a.wk * 256 * (int64_t)sizeof(float)) / kStages * kStages;
-  if (nb > nb_lds) nb = nb_lds;                     // every wave's partial tiles fit in LDS
+  const int64_t nb_lds = (kSkinnyLds - a.wk * kStageBytes) / (a.wk * 256 * (int64_t)sizeof(float)) / kStages * kStages;
+  if (nb > nb_lds) nb = nb_lds;                     // staging and every wave's partial tiles fit in LDS
   a.nb = (int)nb;
   const dim3 grid((unsigned)((tiles + nb - 1) / nb)), block((unsigned)(64 * a.wk));
-  const size_t shm = (size_t)a.wk * nb * 256 * sizeof(float);
+  const size_t shm = (size_t)a.wk * kStageBytes + (size_t)a.wk * nb * 256 * sizeof(float);
   switch (fmt) {
     case 2: return launch(skinny_kernel<2>, grid, block, shm, s, a);
     case 3: return launch(skinny_kernel<3>, grid, block, shm, s, a);
