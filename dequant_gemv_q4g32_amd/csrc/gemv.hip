@@ -52,13 +52,9 @@ struct GemvArgs {
 // GEMV), S lanes per 64-weight unit (1, or 2 to halve the activation registers when M is
 // large), R rows per pipelined batch, MP more than one pass over K.
 
-// Register pipeline stages over row batches: two, and three for the single-row kernels of the
-// formats whose units are small enough to keep three batches in registers without losing
-// occupancy (measured on 32 GEMVs of 4096 x 4096 per launch: q4g32 +5%, q4g64 +3%, q4g128
-// +4%, q4g32h +2%, q2sb +1%; the other formats lost 2-200% to spills or occupancy).
-template <int F, int M> constexpr int gemv_depth() {
-  return M == 1 && (F == 2 || F == 4 || F == 8 || F == 9 || F == 11 || F == 12) ? 3 : 2;
-}
+// Register pipeline stages over row batches. Deeper pipelines spill or lose occupancy and
+// measured no faster.
+constexpr int kGemvDepth = 2;
 
 // Largest workgroup of the streaming kernels: it bounds their registers (a workgroup must fit
 // on the 4 SIMDs of one CU) and the waves along K of one pass. Eight activation rows need
@@ -70,7 +66,7 @@ template <int M> constexpr int mv_threads() { return M > 4 ? 512 : 1024; }
 // but still reach the barrier.
 template <int F, int M, int S, int R, bool MP, bool PERM = false>
 __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b) {
-  constexpr int D = gemv_depth<F, M>();         // pipeline stages
+  constexpr int D = kGemvDepth;                // pipeline stages
   using U = Unit<F>;
   using Raw = typename U::Raw;
   static_assert(R == 1 || R == 2, "rows per batch");
