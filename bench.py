@@ -238,6 +238,28 @@ def extra_configs(qg, dev):
     out["q4g32_gemv_4096"] = {"GBps_32_per_launch": round(alg / us / 1e3, 1), "frac": round(alg / us / 1e3 / HBM_PEAK_GBPS, 4),
                               "GBps_single_launch": round(alg1 / us1 / 1e3, 1), "us_single_launch": round(us1, 2)}
     log(f"[bench] q4g32 4096^2: {out['q4g32_gemv_4096']}")
+    # context only: the same 32 GEMVs of 4096 x 4096 with dense fp16 weights (33.5 MB each, the
+    # traffic the quantized formats avoid), one torch bmm per launch over contiguous operands
+    import torch
+    sets = 2
+    wd = torch.randn((sets, 32, 4096, 4096), dtype=torch.float16, device=dev)
+    xd = torch.randn((32, 4096, 1), dtype=torch.float16, device=dev)
+    yd = torch.empty((32, 4096, 1), dtype=torch.float16, device=dev)
+    for i in range(4):
+        torch.bmm(wd[i % sets], xd, out=yd)             # (eager: a library GEMM stays out of graphs)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(20):
+        torch.bmm(wd[i % sets], xd, out=yd)
+    e1.record()
+    torch.cuda.synchronize()
+    us_d = e0.elapsed_time(e1) * 1e3 / 20
+    dense_bytes = 32 * 4096 * 4096 * 2
+    out["dense_fp16_gemv_4096_x32"] = {"us": round(us_d, 2), "weight_GBps": round(dense_bytes / us_d / 1e3, 1)}
+    log(f"[bench] dense fp16 context, 32 x 4096^2 GEMV per launch: {out['dense_fp16_gemv_4096_x32']}")
+    del wd, xd, yd
+    torch.cuda.empty_cache()
     # 7B-like layer set, batch 1, each format (the four share one set of fp32 weights). Matrices
     # 0-3 are q, k, v, o; 4, 5 gate, up; 6 down. "one_launch": all seven in one grouped launch;
     # "decode_order": the launches a decode step can issue given its data dependencies

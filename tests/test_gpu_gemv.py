@@ -209,3 +209,29 @@ def test_bf16_super_scales_past_the_fp16_range(fmt):
             y = torch.empty((m, n), dtype=torch.float32, device="cuda")
             qg.gemm_grouped(fmt, [wd], [torch.from_numpy(x).cuda()], [(n, k)], outs=[y])
         assert_close(y.cpu().numpy(), y_ref, bound, f"{fmt} m={m}")
+
+
+def test_headline_launch_configuration_sampled_rows():
+    """The benchmark's exact launch: 32 independent q3sb 4096 x 4096 GEMVs in one strided
+    batch (each with its own activations); sampled rows of several members against the
+    oracle."""
+    wl = WORKLOADS["q3sb_gemv_4096"]
+    n, k = wl.shapes[0]
+    w = wl.weights(0)
+    wd = device_weights(wl.fmt, w)
+    lay = qg.device_layout(wl.fmt, n, k)
+    stride = (lay.total_bytes + 255) // 256 * 256
+    count = 32
+    buf = torch.zeros(count * stride, dtype=torch.uint8, device="cuda")
+    for c in range(count):
+        buf[c * stride:c * stride + lay.total_bytes].copy_(wd)
+    xs = activations(count, k, 4242)
+    ys = torch.empty((count, n), dtype=torch.float16, device="cuda")
+    qg.gemv_batched(wl.fmt, buf, stride, torch.from_numpy(xs).cuda(), ys, count, n, k)
+    rows = _sampled_rows(n, 0)
+    _, w_hat = oracle_decode(wl.fmt, w[rows])
+    torch.cuda.synchronize()
+    y = ys.cpu().float().numpy()
+    for b in (0, 17, 31):
+        y_ref, bound = oracle_y(w_hat, xs[b:b + 1])
+        assert_close(y[b, rows][None, :], y_ref, bound, f"member {b}")
