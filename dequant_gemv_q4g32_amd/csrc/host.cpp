@@ -170,9 +170,9 @@ int quantize_row_q4(const float *w, int64_t k, int G, uint8_t *codes, float *sca
 }
 
 // One row of plain group-wise b-bit codes (b = 3 or 5) with an fp32 scale and min per group
-// of 32: m = min w, s = max((max w - min w) / (2^b - 1), 1e-12), c = clamp(rint((w - m) / s),
-// 0, 2^b - 1), the difference and the quotient in fp32; codes packed as one little-endian
-// bitstream (k*b/8 bytes).
+// of 32: m = min w (a zero minimum stored as +0), s = max((max w - min w) / (2^b - 1), 1e-12),
+// c = clamp(rint((w - m) / s), 0, 2^b - 1), the difference and the quotient in fp32; codes
+// packed as one little-endian bitstream (k*b/8 bytes).
 int quantize_row_gw(const float *w, int64_t k, int b, uint8_t *codes, float *scales, float *mins) {
   const int qmax = (1 << b) - 1;
   std::vector<uint8_t> c((size_t)k);
@@ -187,6 +187,7 @@ int quantize_row_gw(const float *w, int64_t k, int b, uint8_t *codes, float *sca
     float scale = (hi - lo) / (float)qmax;
     if (!std::isfinite(scale)) return QG_ERR_RANGE;
     if (scale < 1e-12f) scale = 1e-12f;
+    lo = lo + 0.0f;                                      // a zero minimum is stored as +0
     scales[g] = scale;
     mins[g] = lo;
     for (int i = 0; i < 32; ++i) {

@@ -43,7 +43,7 @@
  *             planes); same fields, rule and device layout as QG_Q3SB (110 B, 3.4375 bpw).
  *   QG_Q3G32, QG_Q5G32  plain group-wise 3- and 5-bit codes c with an fp32 scale s and an fp32
  *             min m per group of 32 (the form of "二三五六位量化" page section 3.3's gemv_q3:
- *             w_hat = s*c + m): m = min w, s = max((max w - min w) / (2^b - 1), 1e-12),
+ *             w_hat = s*c + m): m = min w (+0 for a zero minimum), s = max((max w - min w) / (2^b - 1), 1e-12),
  *             c = clamp(rint((w - m) / s), 0, 2^b - 1), difference and quotient in fp32.
  *             12 or 20 B of codes + 8 B per group (5.0 and 7.0 bpw). k a multiple of 64.
  *

@@ -18,7 +18,8 @@ Readings (the page gives the decoding, not the quantizer):
     every other quantizer on the pages uses.
   * Min-max rule in fp32 (the listing's float scales): m = min w, s = (max w - min w) / (2^b - 1)
     floored at 1e-12 (the INT4 page's floor), q = clamp(rint((w - m) / s), 0, 2^b - 1) with the
-    difference and the quotient each rounded to fp32. w_hat = s * q + m (computed exactly in
+    difference and the quotient each rounded to fp32. A group whose minimum is a zero stores
+    +0 (m + 0 in fp32): the minimum of +0 and -0 is otherwise either, by reduction order. w_hat = s * q + m (computed exactly in
     fp64 here). Every weight is then within s / 2 of w_hat, up to the fp32 rounding of the
     difference and the quotient.
   * Canonical encoding: the codes of a row as one little-endian bitstream of b-bit codes
@@ -57,10 +58,11 @@ def quantize(fmt: str, w: np.ndarray) -> Tuple[np.ndarray, np.ndarray, np.ndarra
     if not np.all(np.isfinite(s)):
         raise OverflowError("a group's range does not fit fp32")
     s = np.maximum(s, SCALE_FLOOR)
+    lo = (lo + np.float32(0.0)).astype(np.float32)       # -0 -> +0
     diff = (g - lo[..., None]).astype(np.float32)
     r = (diff / s[..., None]).astype(np.float32)
     q = np.clip(np.rint(r), 0, qmax).astype(np.uint8)
-    return q.reshape(n, k), s, lo.astype(np.float32)
+    return q.reshape(n, k), s, lo
 
 
 def quantize_group_scalar(fmt: str, w32) -> Tuple[List[int], np.float32, np.float32]:
@@ -74,6 +76,7 @@ def quantize_group_scalar(fmt: str, w32) -> Tuple[List[int], np.float32, np.floa
     s = np.float32(np.float32(hi - lo) / np.float32(qmax))
     if s < SCALE_FLOOR:
         s = SCALE_FLOOR
+    lo = np.float32(lo + np.float32(0.0))
     q = []
     for v in vals:
         r = np.float32(np.float32(v - lo) / s)

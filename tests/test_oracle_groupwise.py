@@ -77,6 +77,22 @@ def test_listing_byte_layout_3bit():
     assert [(int(v) >> (3 * i)) & 7 for i in range(8)] == list(range(8))[::-1]
 
 
+def test_zero_minimum_is_stored_as_positive_zero():
+    """A group whose minimum is a zero stores +0, whichever signed zero came first."""
+    w = np.zeros((2, 64), np.float32)
+    w[0, :32] = np.float32(-0.0)
+    w[0, 5] = np.float32(0.25)
+    w[1, 40] = np.float32(-0.0)
+    w[1, 41] = np.float32(0.5)
+    for fmt in FMTS:
+        _, s, m = gw.quantize(fmt, w)
+        assert np.all(m.view(np.uint32) == 0), (fmt, m)
+        for r in range(2):
+            for g in range(2):
+                _, ss, ms = gw.quantize_group_scalar(fmt, w[r, 32 * g:32 * g + 32])
+                assert np.float32(ms).view(np.uint32) == 0
+
+
 def test_bytes_and_errors():
     assert gw.algorithmic_bytes("q3g32", 2, 128) == 2 * (48 + 32)
     assert gw.algorithmic_bytes("q5g32", 2, 128) == 2 * (80 + 32)
