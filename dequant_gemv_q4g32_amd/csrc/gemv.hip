@@ -579,12 +579,23 @@ size_t red_bytes(const GemvArgs &a, int R, int M) {
 // measured up to 40% slower than 3 to 8 on the same grouped launch).
 constexpr int kMaxPlanW = 8;
 constexpr int64_t kLdsPerCu = 160 * 1024;   // LDS bytes per CU on gfx950
+// Large single-row launches: every wave first loads its activation slice (8 KB for a whole
+// wave of units), which a full grid of short waves re-reads from L2 thousands of times.
+// When there is enough work, waves take more batches so that about kLongWaves of them
+// (two per SIMD) cover it, up to a per-format cap: the 2- and 3-bit decodes spend about twice
+// the VALU per weight byte and need the wave slots to hide it (cap 16 batches), the others
+// stream best with the longest waves (32).
+constexpr int64_t kLongWaves = 2048;
+template <int F> constexpr int long_nbt() {
+  // q2sb, q3sb, their bf16-scale forms and q3g32
+  return (F == 2 || F == 3 || F == 12 || F == 13 || F == kQ3G32) ? 16 : kMaxBatches;
+}
 struct MvPlan {
   int W;
   int64_t nbt;
 };
 MvPlan plan_mv(int ng, const int64_t *n, const int *wk, const int64_t *count, int R, int wps, int max_w,
-               int64_t lds_block = 0) {
+               int64_t lds_block = 0, int long_cap = 0) {
   const int slots = 4 * wps;
   int64_t work[kMaxGroup], total = 0;
   int wk_max = 1;
@@ -593,6 +604,19 @@ MvPlan plan_mv(int ng, const int64_t *n, const int *wk, const int64_t *count, in
     total += work[g];
     wk_max = wk[g] > wk_max ? wk[g] : wk_max;
   }
+  // workgroups of W waves when row groups take nbt batches (split_rows' split)
+  auto blocks_for = [&](int W, int64_t nbt) {
+    int64_t blocks = 0;
+    for (int g = 0; g < ng; ++g) {
+      const int64_t groups = (n[g] + R - 1) / R;
+      int64_t rg = groups / nbt;
+      const int64_t rg_cap = (groups + kMaxBatches - 1) / kMaxBatches;
+      rg = rg < rg_cap ? rg_cap : rg;
+      rg = rg < 1 ? 1 : (rg > groups ? groups : rg);
+      blocks += count[g] * ((rg + W / wk[g] - 1) / (W / wk[g]));
+    }
+    return blocks;
+  };
   MvPlan best{wk_max, kMinBatches};
   double best_score = -1.0;
   for (int W = wk_max; W <= max_w && W <= slots && (W <= kMaxPlanW || W == wk_max || lds_block > 0); ++W) {
@@ -603,21 +627,24 @@ MvPlan plan_mv(int ng, const int64_t *n, const int *wk, const int64_t *count, in
     const int64_t resident = (int64_t)256 * per_cu * W;
     int64_t nbt = (total + resident - 1) / resident;
     nbt = nbt < kMinBatches ? kMinBatches : nbt;
-    int64_t blocks = 0;
-    for (int g = 0; g < ng; ++g) {
-      const int64_t groups = (n[g] + R - 1) / R;
-      int64_t rg = groups / nbt;
-      const int64_t rg_cap = (groups + kMaxBatches - 1) / kMaxBatches;
-      rg = rg < rg_cap ? rg_cap : rg;
-      rg = rg < 1 ? 1 : (rg > groups ? groups : rg);
-      blocks += count[g] * ((rg + W / wk[g] - 1) / (W / wk[g]));
-    }
+    const int64_t blocks = blocks_for(W, nbt);
     const double score = used / (double)total * (double)(per_cu * W) / slots *
                          (blocks >= 256 ? 1.0 : (double)blocks / 256);
     if (score > best_score + 1e-9) {
       best_score = score;
       best = {W, nbt};
     }
+  }
+  // Long waves (single-row kernels): about kLongWaves waves, i.e. bpc workgroups of W waves
+  // on every CU, each row group taking nbt_long batches, when that is longer than the plan's
+  // and within the format's cap. Taken only if the workgroups still fit one even round
+  // (blocks <= 256 * bpc): a grid a little larger than that leaves some CUs a second round.
+  if (long_cap > 0) {
+    const int64_t per_wave_slots = kLongWaves / 256;                  // waves per CU
+    const int64_t bpc = best.W < per_wave_slots ? per_wave_slots / best.W : 1;
+    const int64_t denom = (int64_t)256 * best.W * bpc;
+    const int64_t nbt_long = (total + denom - 1) / denom;
+    if (nbt_long > best.nbt && nbt_long <= long_cap && blocks_for(best.W, nbt_long) <= 256 * bpc) best.nbt = nbt_long;
   }
   return best;
 }
@@ -629,7 +656,8 @@ int launch_mv_k(GemvArgs a, int64_t count, hipStream_t s) {
   // act-order activations staged in LDS when they fit beside the partial sums
   const int64_t xl_bytes = a.perm ? a.m * a.k * 2 : 0;
   const bool stage = a.perm && xl_bytes <= kActOrderLds;
-  const MvPlan P = plan_mv(1, &a.n, &a.wk, &count, R, wps, mv_threads<M>() / 64, stage ? xl_bytes : 0);
+  const MvPlan P = plan_mv(1, &a.n, &a.wk, &count, R, wps, mv_threads<M>() / 64, stage ? xl_bytes : 0,
+                           M == 1 ? long_nbt<F>() : 0);
   a.wr = P.W / a.wk;
   const int64_t blocks = split_rows(a, R, P.nbt);
   size_t shm = red_bytes(a, R, M);
@@ -658,7 +686,7 @@ int launch_mv_group(GemvGroup &G, hipStream_t s) {
     wk[g] = G.g[g].wk;
     count[g] = 1;
   }
-  const MvPlan P = plan_mv(G.count, n, wk, count, R, wps, mv_threads<M>() / 64);
+  const MvPlan P = plan_mv(G.count, n, wk, count, R, wps, mv_threads<M>() / 64, 0, M == 1 ? long_nbt<F>() : 0);
   int64_t blocks = 0;
   size_t shm = 0;
   for (int g = 0; g < G.count; ++g) {
