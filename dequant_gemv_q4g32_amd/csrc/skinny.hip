@@ -218,6 +218,12 @@ int launch_skinny(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *
   nb = (nb + kStages - 1) / kStages * kStages;      // whole pipeline rounds; extra tiles are past n
   const int64_t nb_lds = (kSkinnyLds - a.wk * kStageBytes) / (a.wk * 256 * (int64_t)sizeof(float)) / kStages * kStages;
   if (nb > nb_lds) nb = nb_lds;                     // staging and every wave's partial tiles fit in LDS
+  // A grid a little over one workgroup per CU gives most CUs one workgroup and a few two,
+  // and every workgroup re-reads all the activation rows of its K range: twice the tiles per
+  // workgroup instead, while that still keeps half the CUs busy (11008 x 4096 with 8 or 16
+  // rows: 344 workgroups of 2 tiles 16.4 us, 172 of 4 tiles 13.1 us, measured on one MI355X).
+  const int64_t wgs = (tiles + nb - 1) / nb, nb2 = nb + kStages;
+  if (wgs > 256 && wgs < 384 && nb2 <= kSkinnyMaxNb && nb2 <= nb_lds && (tiles + nb2 - 1) / nb2 >= 128) nb = nb2;
   a.nb = (int)nb;
   const dim3 grid((unsigned)((tiles + nb - 1) / nb)), block((unsigned)(64 * a.wk));
   const size_t shm = (size_t)a.wk * kStageBytes + (size_t)a.wk * nb * 256 * sizeof(float);
