@@ -314,5 +314,5 @@ def dequantize(fmt, w, n: int, k: int, values: bool = True, codes: bool = True, 
 
 
 def read_probe(buf, nbytes: int, sink, stream=None) -> None:
-    """Stream nbytes of a device buffer through 128-bit loads (read-ceiling measurement)."""
+    """Stream nbytes of a device buffer through non-temporal 128-bit loads (read-ceiling measurement)."""
     _check(_lib.qg_read_probe(buf.data_ptr(), nbytes, sink.data_ptr(), _stream(stream)), "qg_read_probe")

@@ -235,3 +235,18 @@ def test_headline_launch_configuration_sampled_rows():
     for b in (0, 17, 31):
         y_ref, bound = oracle_y(w_hat, xs[b:b + 1])
         assert_close(y[b, rows][None, :], y_ref, bound, f"member {b}")
+
+
+def test_read_probe_streams_without_writing():
+    """The read-ceiling probe reads any multiple of 16 bytes (one-shot and grid-stride sizes,
+    a ragged tail of 16-byte chunks) and leaves the sink alone (zeros xor to 0); bad sizes
+    are rejected."""
+    buf = torch.zeros(64 << 20, dtype=torch.uint8, device="cuda")
+    sink = torch.full((1,), 7, dtype=torch.int32, device="cuda")
+    for nbytes in (16, 16 * 1023, 16 * 1025, 48 << 20, (64 << 20) - 16 * 37):
+        qg.read_probe(buf, nbytes, sink)
+    torch.cuda.synchronize()
+    assert sink.item() == 7
+    for bad in (8, -16):
+        with pytest.raises(Exception):
+            qg.read_probe(buf, bad, sink)
