@@ -583,7 +583,8 @@ size_t red_bytes(const GemvArgs &a, int R, int M) {
 // workgroup's barrier. Whole workgroups fit a CU's wave slots floor(slots / W) times. Row
 // groups take nbt batches each: one resident round of waves (no tail round), but at least
 // kMinBatches, so that a wave's activation load and first load latency are spread over
-// several rows (fewer, longer waves beat a full grid of very short ones here). W is chosen
+// several rows (fewer, longer waves beat a full grid of very short ones here), and longer
+// still for large single-row launches (kLongWaves below). W is chosen
 // for the fewest wasted wave slots, times the fraction of the 256 CUs that get a workgroup
 // at all (a small matrix in large workgroups would leave most CUs idle); the smaller W on
 // ties, and no more than kMaxPlanW waves unless one matrix needs more along K (idle waves

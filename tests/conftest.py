@@ -11,4 +11,4 @@ GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
 
 
 def pytest_configure(config):
-    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU; run on the GPU box")
+    config.addinivalue_line("markers", "gpu: needs an MI355X (gfx950) GPU")
