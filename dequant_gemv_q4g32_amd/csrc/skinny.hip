@@ -158,15 +158,21 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWk) void skinny_kernel(SkinnyArgs a)
     // kStages register stages over the row tiles (loads of kStages - 1 tiles in flight while
     // one is computed); prefetches past the last tile re-load it
     Raw qs[kStages][kDW];
+    if (a.nb == 1) {
+      // one tile per workgroup (small grids): nothing to pipeline
+      load(qs[0], 0);
+      finish(qs[0], 0);
+    } else {
 #pragma unroll
-    for (int d = 0; d + 1 < kStages; ++d) load(qs[d], d);
-    // (nb is a multiple of kStages, so the body has no branch and each wait covers only the
-    // oldest stage)
-    for (int j = 0; j < a.nb; j += kStages) {
+      for (int d = 0; d + 1 < kStages; ++d) load(qs[d], d);
+      // (nb is a multiple of kStages, so the body has no branch and each wait covers only
+      // the oldest stage)
+      for (int j = 0; j < a.nb; j += kStages) {
 #pragma unroll
-      for (int d = 0; d < kStages; ++d) {
-        load(qs[(d + kStages - 1) % kStages], j + d + kStages - 1);
-        finish(qs[d], j + d);
+        for (int d = 0; d < kStages; ++d) {
+          load(qs[(d + kStages - 1) % kStages], j + d + kStages - 1);
+          finish(qs[d], j + d);
+        }
       }
     }
   }
@@ -224,6 +230,9 @@ int launch_skinny(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *
   // rows: 344 workgroups of 2 tiles 16.4 us, 172 of 4 tiles 13.1 us, measured on one MI355X).
   const int64_t wgs = (tiles + nb - 1) / nb, nb2 = nb + kStages;
   if (wgs > 256 && wgs < 384 && nb2 <= kSkinnyMaxNb && nb2 <= nb_lds && (tiles + nb2 - 1) / nb2 >= 128) nb = nb2;
+  // At most 256 tiles: two tiles per workgroup would leave at least half the CUs idle, so
+  // each workgroup takes one (an unpipelined tile).
+  if (nb == kStages && tiles <= 256) nb = 1;
   a.nb = (int)nb;
   const dim3 grid((unsigned)((tiles + nb - 1) / nb)), block((unsigned)(64 * a.wk));
   const size_t shm = (size_t)a.wk * kStageBytes + (size_t)a.wk * nb * 256 * sizeof(float);
