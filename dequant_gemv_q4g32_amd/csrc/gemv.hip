@@ -599,16 +599,20 @@ constexpr int64_t kLdsPerCu = 160 * 1024;   // LDS bytes per CU on gfx950
 // the VALU per weight byte and need the wave slots to hide it (cap 16 batches), the others
 // stream best with the longest waves (32).
 constexpr int64_t kLongWaves = 2048;
-template <int F> constexpr int long_nbt() {
-  // q2sb, q3sb, their bf16-scale forms and q3g32
-  return (F == 2 || F == 3 || F == 12 || F == 13 || F == kQ3G32) ? 16 : kMaxBatches;
+template <int F> constexpr bool light_bits() {   // q2sb, q3sb, their bf16-scale forms and q3g32
+  return F == 2 || F == 3 || F == 12 || F == 13 || F == kQ3G32;
 }
+template <int F> constexpr int long_nbt() { return light_bits<F>() ? 16 : kMaxBatches; }
+// Among equally scored workgroup sizes, the 2- and 3-bit single-row kernels take 4 waves when
+// that still gives every CU at least 4 workgroups: measured 1.3% (q3sb) and 4% (q2sb) faster
+// than 1 on 32 4096^2 GEMVs per launch; the other formats were as fast or up to 2% slower.
+template <int F> constexpr int prefer_w() { return light_bits<F>() ? 4 : 0; }
 struct MvPlan {
   int W;
   int64_t nbt;
 };
 MvPlan plan_mv(int ng, const int64_t *n, const int *wk, const int64_t *count, int R, int wps, int max_w,
-               int64_t lds_block = 0, int long_cap = 0) {
+               int64_t lds_block = 0, int long_cap = 0, int prefer_w = 0) {
   const int slots = 4 * wps;
   int64_t work[kMaxGroup], total = 0;
   int wk_max = 1;
@@ -643,7 +647,7 @@ MvPlan plan_mv(int ng, const int64_t *n, const int *wk, const int64_t *count, in
     const int64_t blocks = blocks_for(W, nbt);
     const double score = used / (double)total * (double)(per_cu * W) / slots *
                          (blocks >= 256 ? 1.0 : (double)blocks / 256);
-    if (score > best_score + 1e-9) {
+    if (score > best_score + 1e-9 || (W == prefer_w && score > best_score - 1e-9 && blocks >= 4 * 256)) {
       best_score = score;
       best = {W, nbt};
     }
@@ -670,7 +674,7 @@ int launch_mv_k(GemvArgs a, int64_t count, hipStream_t s) {
   const int64_t xl_bytes = a.perm ? a.m * a.k * 2 : 0;
   const bool stage = a.perm && xl_bytes <= kActOrderLds;
   const MvPlan P = plan_mv(1, &a.n, &a.wk, &count, R, wps, mv_threads<M>() / 64, stage ? xl_bytes : 0,
-                           M == 1 ? long_nbt<F>() : 0);
+                           M == 1 ? long_nbt<F>() : 0, M == 1 && !PERM ? prefer_w<F>() : 0);
   a.wr = P.W / a.wk;
   const int64_t blocks = split_rows(a, R, P.nbt);
   size_t shm = red_bytes(a, R, M);
