@@ -7,13 +7,14 @@
 // into fp16 w_hat by the same per-format unit decode as the GEMV (units.h, `wide`), written
 // once per K step into an LDS tile that every wave of the workgroup reads.
 //
-// Tiling: a workgroup of 4 waves computes a 128 x 128 tile of Y (128 activation rows x 128
-// weight rows) and walks K in steps of one 64-weight unit. Each step, every thread loads
-// half a unit of one weight row and 16 bytes of each of 4 activation rows (two steps ahead,
-// into one of two register stages), decodes its half unit to 16 fp16 pairs and stores both
-// into one of two LDS buffers. Each wave then runs 2 x 2 MFMA tiles of 32 x 32 over the step's 4 K-slices
-// of 16. Workgroups are numbered so that the M tiles sharing a weight tile run on one XCD
-// and share its L2.
+// Tiling: a workgroup of 4 waves computes a 128 x BN tile of Y (128 activation rows x BN =
+// 128 or 96 weight rows) and walks K in steps of one 64-weight unit. Each step, every thread
+// loads half a unit of one weight row (the first 2 * BN threads) and 16 bytes of each of 4
+// activation rows (two steps ahead, into one of two register stages), decodes its half unit
+// to 16 fp16 pairs and stores both into one of two LDS buffers. Each wave then runs 2 x 2
+// (BN = 128) or 1 x 3 (BN = 96) MFMA tiles of 32 x 32 over the step's 4 K-slices of 16.
+// Workgroups are numbered so that the M tiles sharing a weight tile run on one XCD and share
+// its L2.
 #include <hip/hip_runtime.h>
 
 #include "../../include/qgemv.h"
@@ -42,18 +43,22 @@ struct PrefillArgs {
 };
 
 constexpr int kBM = 128;                 // activation rows per workgroup tile
-constexpr int kBN = 128;                 // weight rows per workgroup tile
+// Weight rows per workgroup tile, BN: 128 (4 waves as 2 x 2 of 64 x 64) or 96 (4 waves along
+// M, each 32 x 96). The launch takes the one whose busiest CU has the fewest weight rows.
 constexpr int kLdsRow = kUnit + 8;       // halfs per LDS row: 64 + 8 of padding (bank spread)
 constexpr uint32_t kXRange = 0x7FFFFFF0u; // activation buffer range; offsets at or past it read 0
 
-template <int F>
+template <int F, int BN>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   using U = Unit<F>;
   using Raw = typename U::Raw;
+  static_assert(BN == 128 || BN == 96, "weight rows per tile");
+  constexpr int WM = BN == 128 ? 2 : 4;                   // waves along M
+  constexpr int TM = kBM / WM / 32, TN = BN / (4 / WM) / 32;   // 32 x 32 MFMA tiles per wave
   // two LDS buffers per operand: the MFMAs of step u read one while step u+1 is stored into
   // the other, so one barrier per step suffices
   __shared__ __attribute__((aligned(16))) _Float16 xs[2][kBM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) _Float16 ws[2][kBN * kLdsRow];
+  __shared__ __attribute__((aligned(16))) _Float16 ws[2][BN * kLdsRow];
 
   // Workgroups are dispatched round-robin over the 8 XCDs; tile numbers are assigned so that
   // consecutive tiles (the M tiles of one weight tile) fall on the same XCD.
@@ -64,15 +69,16 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   // so that the buffer resources built from them stay in scalar registers)
   const int mt = __builtin_amdgcn_readfirstlane(tile % a.mtiles);
   const int nt = __builtin_amdgcn_readfirstlane(tile / a.mtiles);
-  const int64_t m0 = (int64_t)mt * kBM, r0 = (int64_t)nt * kBN;
+  const int64_t m0 = (int64_t)mt * kBM, r0 = (int64_t)nt * BN;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = wave & 1, wn = wave >> 1;         // this wave's 64 x 64 quarter of the tile
+  const int wm = wave % WM, wn = wave / WM;        // this wave's (TM x 32) x (TN x 32) block
 
   // weight loader role: LDS row t >> 1 of the weight tile, half h = t & 1 of the unit
   const int lrow = t >> 1, h = t & 1;
+  const bool wload = BN == 128 || lrow < BN;       // wave-uniform: threads 2 * BN.. load no weights
   const int64_t wrow = r0 + lrow < a.n ? r0 + lrow : a.n - 1;   // rows past n are not stored
   // activation loader role: rows (t >> 3) + 32 i, 16-byte chunk t & 7 of the step's 128 bytes,
   // so that 8 consecutive lanes read one row's 128 bytes (whole cache lines)
@@ -106,7 +112,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     const bool half = (F == 4) && (u == a.units - 1) && (a.k % 64 != 0);
     // only this thread's half of the unit; cached: the weight tile is read again by the
     // workgroups of the other M tiles
-    U::template load<0, 2>(q, L, 0, half);
+    if (wload) U::template load<0, 2>(q, L, 0, half);
     const int64_t kk = u * kUnit + 8 * xc;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -117,23 +123,26 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   };
   // decode a register stage to fp16 and store it, with its activations, into LDS buffer b
   auto lds_store = [&](const Raw &q, const u32x4 *xv, int b) {
-    uint32_t pr[16];
-    U::template wide<2>(q, h, pr);
+    if (wload) {
+      uint32_t pr[16];
+      U::template wide<2>(q, h, pr);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      // local pairs 4i..4i+3 are the unit's consecutive pairs pidx(h, 4i).. (k = 2 * pair)
-      const int g = U::pidx(h, 4 * i, 2);
-      *reinterpret_cast<u32x4 *>(&ws[b][lrow * kLdsRow + 2 * g]) =
-          u32x4{pr[4 * i], pr[4 * i + 1], pr[4 * i + 2], pr[4 * i + 3]};
-      *reinterpret_cast<u32x4 *>(&xs[b][(xr0 + 32 * i) * kLdsRow + 8 * xc]) = xv[i];
+      for (int i = 0; i < 4; ++i) {
+        // local pairs 4i..4i+3 are the unit's consecutive pairs pidx(h, 4i).. (k = 2 * pair)
+        const int g = U::pidx(h, 4 * i, 2);
+        *reinterpret_cast<u32x4 *>(&ws[b][lrow * kLdsRow + 2 * g]) =
+            u32x4{pr[4 * i], pr[4 * i + 1], pr[4 * i + 2], pr[4 * i + 3]};
+      }
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4 *>(&xs[b][(xr0 + 32 * i) * kLdsRow + 8 * xc]) = xv[i];
   };
 
-  f32x16 acc[2][2];
+  f32x16 acc[TM][TN];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
@@ -141,17 +150,17 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   auto mfma_step = [&](int b) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      half8_t A[2], B[2];
+      half8_t A[TM], B[TN];
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        A[i] = *reinterpret_cast<const half8_t *>(&xs[b][(wm * 64 + 32 * i + arow) * kLdsRow + 16 * s + akoff]);
+      for (int i = 0; i < TM; ++i)
+        A[i] = *reinterpret_cast<const half8_t *>(&xs[b][(wm * TM * 32 + 32 * i + arow) * kLdsRow + 16 * s + akoff]);
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        B[j] = *reinterpret_cast<const half8_t *>(&ws[b][(wn * 64 + 32 * j + arow) * kLdsRow + 16 * s + akoff]);
+      for (int j = 0; j < TN; ++j)
+        B[j] = *reinterpret_cast<const half8_t *>(&ws[b][(wn * TN * 32 + 32 * j + arow) * kLdsRow + 16 * s + akoff]);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i], B[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i], B[j], acc[i][j], 0, 0, 0);
     }
   };
 
@@ -180,13 +189,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 
   // D of a 32 x 32 MFMA: lane l holds column l % 32 and rows 8 (e / 4) + 4 (l / 32) + e % 4
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < TN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * 64 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const int64_t col = r0 + wn * 64 + 32 * j + (lane & 31);
+        const int64_t row = m0 + wm * TM * 32 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int64_t col = r0 + wn * TN * 32 + 32 * j + (lane & 31);
         if (row < a.m && col < a.n) {
           const int64_t idx = row * a.ldy + col;
           if (a.y_f32) reinterpret_cast<float *>(a.y)[idx] = acc[i][j][e];
@@ -216,31 +225,40 @@ int launch_prefill(int fmt, const void *w, const uint16_t *X, int64_t ldx, void 
   a.m = m;
   a.y_f32 = y_f32;
   if (kBM * ldx * 2 >= (int64_t)kXRange) return QG_ERR_SHAPE;     // 32-bit activation offsets
-  const int64_t mtiles = (m + kBM - 1) / kBM, ntiles = (n + kBN - 1) / kBN;
+  // weight rows on the busiest CU: ceil(tiles / 256) tiles of BN rows (the workgroups go out one
+  // per CU first); 96-row tiles when they leave it fewer rows (512 x 11008: 460 tiles, 192 rows
+  // against 344 tiles and 256 rows)
+  const int64_t mtiles = (m + kBM - 1) / kBM;
+  const int64_t t128 = mtiles * ((n + 127) / 128), t96 = mtiles * ((n + 95) / 96);
+  const int BN = (t96 + 255) / 256 * 96 < (t128 + 255) / 256 * 128 ? 96 : 128;
+  const int64_t ntiles = (n + BN - 1) / BN;
   const int64_t total = mtiles * ntiles;
   if (total > (int64_t(1) << 30)) return QG_ERR_SHAPE;
   a.mtiles = (int)mtiles;
   a.ntiles = (int)ntiles;
   a.per_xcd = (int)((total + 7) / 8);
   const dim3 grid((unsigned)(8 * a.per_xcd)), block(256);
+  auto go = [&](auto kern128, auto kern96) {
+    return BN == 96 ? launch(kern96, grid, block, 0, s, a) : launch(kern128, grid, block, 0, s, a);
+  };
   switch (fmt) {
-    case 2: return launch(prefill_kernel<2>, grid, block, 0, s, a);
-    case 3: return launch(prefill_kernel<3>, grid, block, 0, s, a);
-    case 4: return launch(prefill_kernel<4>, grid, block, 0, s, a);
-    case 5: return launch(prefill_kernel<5>, grid, block, 0, s, a);
-    case 6: return launch(prefill_kernel<6>, grid, block, 0, s, a);
-    case 7: return launch(prefill_kernel<7>, grid, block, 0, s, a);
-    case 8: return launch(prefill_kernel<8>, grid, block, 0, s, a);
-    case 9: return launch(prefill_kernel<9>, grid, block, 0, s, a);
-    case 10: return launch(prefill_kernel<10>, grid, block, 0, s, a);
-    case 11: return launch(prefill_kernel<11>, grid, block, 0, s, a);
-    case 12: return launch(prefill_kernel<12>, grid, block, 0, s, a);
-    case 13: return launch(prefill_kernel<13>, grid, block, 0, s, a);
-    case 14: return launch(prefill_kernel<3>, grid, block, 0, s, a);   // q3sb's device layout
-    case 15: return launch(prefill_kernel<15>, grid, block, 0, s, a);
-    case 16: return launch(prefill_kernel<16>, grid, block, 0, s, a);
-    case 17: return launch(prefill_kernel<17>, grid, block, 0, s, a);
-    case 18: return launch(prefill_kernel<18>, grid, block, 0, s, a);
+    case 2: return go(prefill_kernel<2, 128>, prefill_kernel<2, 96>);
+    case 3: return go(prefill_kernel<3, 128>, prefill_kernel<3, 96>);
+    case 4: return go(prefill_kernel<4, 128>, prefill_kernel<4, 96>);
+    case 5: return go(prefill_kernel<5, 128>, prefill_kernel<5, 96>);
+    case 6: return go(prefill_kernel<6, 128>, prefill_kernel<6, 96>);
+    case 7: return go(prefill_kernel<7, 128>, prefill_kernel<7, 96>);
+    case 8: return go(prefill_kernel<8, 128>, prefill_kernel<8, 96>);
+    case 9: return go(prefill_kernel<9, 128>, prefill_kernel<9, 96>);
+    case 10: return go(prefill_kernel<10, 128>, prefill_kernel<10, 96>);
+    case 11: return go(prefill_kernel<11, 128>, prefill_kernel<11, 96>);
+    case 12: return go(prefill_kernel<12, 128>, prefill_kernel<12, 96>);
+    case 13: return go(prefill_kernel<13, 128>, prefill_kernel<13, 96>);
+    case 14: return go(prefill_kernel<3, 128>, prefill_kernel<3, 96>);   // q3sb's device layout
+    case 15: return go(prefill_kernel<15, 128>, prefill_kernel<15, 96>);
+    case 16: return go(prefill_kernel<16, 128>, prefill_kernel<16, 96>);
+    case 17: return go(prefill_kernel<17, 128>, prefill_kernel<17, 96>);
+    case 18: return go(prefill_kernel<18, 128>, prefill_kernel<18, 96>);
   }
   return QG_ERR_FORMAT;
 }
