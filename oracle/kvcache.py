@@ -11,27 +11,32 @@ fp16 scale shared by every 32 elements costs about 1.06 bytes per element (8 + 1
 Readings (the page gives the group size, the code width and the scale type only):
   * symmetric int8 codes in [-127, 127] (no zero point: K and V entries are centred, and the
     page mentions only a scale); groups are 32 consecutive elements of a row;
-  * the scale d is the smallest fp16 >= max|x| / 127, so the fp16 grid covers the group and
-    every element is within d/2 of its decoded value (the same range-covering rule as the
-    super-block scales);
-  * the code decision is made in fp32, the precision a GPU kernel computes it in (the page
-    fixes none): t = fp32(max|x|) / 127 (one fp32 division), d = fp16_ceil(t),
-    inv = fp32(1 / d) (one fp32 division per group), q = clamp(rint(fp32(x) * inv), -127, 127)
-    with rint half-to-even; an all-zero group has d = 0, inv = 0 and q = 0. (A multiply by
-    the group's reciprocal rather than a division per element: it can move a code by one only
-    where x / d lies within an ulp of a half-integer, and keeps the error within d/2 up to
-    that ulp.)
-  * decode: x_hat = fp32(d) * q (exact in fp32: 11 x 7 significant bits), rounded once to
-    fp16 for the fp16 output.
+  * the scale d is the smallest fp16 >= max|x| / 127 (exact quotient), so the fp16 grid covers
+    the group (the same range-covering rule as the super-block scales);
+  * the code is the plain definition q = clamp(rint(x / d), -127, 127) on the exact quotient,
+    rint rounding halves to even; an all-zero group has d = 0 and q = 0;
+  * decode: x_hat = d * q (exact: 11 x 7 significant bits). The fp16 decode rounds it once to
+    the nearest fp16 and saturates at +-65504: the one group whose d exceeds 65504 / 127 (a
+    group maximum above 65469, d = 516) would otherwise decode code +-127 (+-65532) to inf.
+    Saturation keeps every decoded element within d/2 of its input there, since such inputs
+    are at most 65504.
+
+Both divisions are carried out in fp64, and neither rounding can change a decision: the
+operands are fp16, so a quotient that is not exactly an fp16 value (for d) or a half-integer
+(for q) stays at least 2^-20 of its own size away from one (11-bit operands, quotients below
+2^7), while an fp64 quotient is within 2^-53 of its size of the exact one. Exact
+half-integers (x = 1.5 d, ...) come out exact and go to the even code.
 
 Parity status: pinned by tests/test_oracle_kvcache.py (the page's byte arithmetic, hand-worked
-groups in tests/golden/kvcache_groups.json, the d/2 error bound, all-zero and one-hot groups).
+groups in tests/golden/kvcache_groups.json, including exact ties that a reciprocal multiply
+decides the other way, the d/2 error bound, saturation at the fp16 maximum, exact rational
+brute force of the code decision, all-zero and one-hot groups).
 """
 from __future__ import annotations
 
 import numpy as np
 
-from .fp16 import fp16_ceil_array
+from .fp16 import FP16_MAX, fp16_ceil_array
 
 GROUP = 32
 QMAX = 127
@@ -55,15 +60,13 @@ def quantize(x: np.ndarray):
         raise ValueError("cols must be a multiple of 32")
     if not np.all(np.isfinite(x)):
         raise ValueError("non-finite input")
-    g = x.astype(np.float32).reshape(rows, cols // GROUP, GROUP)
-    amax = np.max(np.abs(g), axis=2)                                  # exact (fp16 values)
-    t = (amax / np.float32(QMAX)).astype(np.float32)                  # one fp32 division
-    d = fp16_ceil_array(t.astype(np.float64))                         # smallest fp16 >= t
-    d32 = d.astype(np.float32)[:, :, None]
-    with np.errstate(divide="ignore"):
-        inv = np.where(d32 > 0, np.float32(1) / np.where(d32 > 0, d32, np.float32(1)), np.float32(0)).astype(np.float32)
-    r = (g * inv).astype(np.float32)                                  # one fp32 multiply
-    q = np.clip(np.rint(r), -QMAX, QMAX).astype(np.int8)
+    g = x.astype(np.float64).reshape(rows, cols // GROUP, GROUP)
+    amax = np.max(np.abs(g), axis=2)
+    d = fp16_ceil_array(amax / QMAX)                                  # smallest fp16 >= max|x| / 127
+    d64 = d.astype(np.float64)[:, :, None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        quotient = np.where(d64 > 0, g / np.where(d64 > 0, d64, 1.0), 0.0)
+    q = np.clip(np.rint(quotient), -QMAX, QMAX).astype(np.int8)      # np.rint: halves to even
     return q.reshape(rows, cols), d
 
 
@@ -73,3 +76,9 @@ def dequantize(q: np.ndarray, d: np.ndarray) -> np.ndarray:
     rows, cols = q.shape
     d32 = np.asarray(d, dtype=np.float16).astype(np.float32)
     return (q.astype(np.float32).reshape(rows, cols // GROUP, GROUP) * d32[:, :, None]).reshape(rows, cols)
+
+
+def dequantize_fp16(q: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """The fp16 decode: d * q rounded once to the nearest fp16, saturated at +-65504."""
+    v = dequantize(q, d).astype(np.float64)
+    return np.clip(v, -FP16_MAX, FP16_MAX).astype(np.float16)
