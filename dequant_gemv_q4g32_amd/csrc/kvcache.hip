@@ -2,9 +2,10 @@
 //
 // Method: "二三五六位量化" page section 4.1 (the KV cache quantized to 8 bits with one fp16
 // scale per 32 elements, about 1.06 bytes per element, half of fp16). Symmetric int8 codes in
-// [-127, 127]; the scale d is the smallest fp16 at or above max|x| / 127 (computed in fp32),
-// so every element is within d/2 of its decoded value; q = rint(x * fp32(1 / d)) (an all-zero
-// group has d = 0 and q = 0); decode is fp32(d) * q rounded once to fp16.
+// [-127, 127]; the scale d is the smallest fp16 at or above max|x| / 127, so every element is
+// within d/2 of its decoded value; q = rint(x / d) on the exact quotient, halves to even (an
+// all-zero group has d = 0 and q = 0); decode is d * q rounded once to fp16 and saturated at
+// +-65504 (only d = 516, the scale of a group whose maximum is above 65469, reaches past it).
 //
 // Both kernels are streaming and HBM-bound: a lane handles 8 consecutive elements of a row
 // (one 16-byte fp16 load or store, one 8-byte code load or store), so a wave moves 1 KB of
@@ -64,16 +65,29 @@ __global__ __launch_bounds__(kKvThreads) void kv_quant_kernel(const uint16_t *sr
     amax = fmaxf(amax, fmaxf(fabsf(f[2 * j]), fabsf(f[2 * j + 1])));
   }
   amax = quad_max(amax);
-  // d = smallest fp16 >= amax / 127 (t is finite and non-negative, at most 65504 / 127)
+  // d = smallest fp16 >= amax / 127 (t is finite and non-negative, at most 65504 / 127). The
+  // fp32 quotient cannot cross an fp16 value: amax is fp16, so the exact quotient lies either
+  // on an fp16 number or at least 2^-18 of its size away from every one, far beyond fp32's
+  // rounding.
   const float t = amax / 127.0f;
   _Float16 h = (_Float16)t;
   if ((float)h < t) h = __builtin_bit_cast(_Float16, (uint16_t)(__builtin_bit_cast(uint16_t, h) + 1));
   const float d = (float)h;
-  const float inv = d > 0.f ? 1.0f / d : 0.f;   // one division per group; codes = rint(x * inv)
+  const float inv = d > 0.f ? 1.0f / d : 0.f;   // one division per group
   uint32_t packed[2] = {0u, 0u};
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
+    // q0 = rint(x * inv) is within one of rint(x / d) (|x / d| <= 127, inv within an ulp).
+    // The remainder e = x - q0 d is exact in fp32: x and d are fp16, |q0| <= 127, and for
+    // q0 != 0 |x| >= d / 2, so e is a multiple of half of d's last-place unit and below
+    // 1.5 d (13 bits). Comparing 2e with +-d then moves q0 to the exact quotient's nearest
+    // integer, ties (2e == +-d) to the even one.
     float q = __builtin_rintf(f[j] * inv);
+    const float e2 = 2.0f * __builtin_fmaf(-q, d, f[j]);
+    const bool odd = ((int32_t)q & 1) != 0;
+    const bool up = e2 > d || (e2 == d && odd);
+    const bool dn = e2 < -d || (e2 == -d && odd);
+    q += up ? 1.0f : (dn ? -1.0f : 0.0f);
     q = fminf(fmaxf(q, -127.f), 127.f);
     packed[j >> 2] |= ((uint32_t)(int32_t)q & 0xFFu) << (8 * (j & 3));
   }
@@ -96,7 +110,9 @@ __global__ __launch_bounds__(kKvThreads) void kv_dequant_kernel(const int8_t *co
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const uint32_t word = qw[j >> 1] >> (16 * (j & 1));
-    const float a = (float)(int8_t)(word & 0xFFu) * d, b = (float)(int8_t)((word >> 8) & 0xFFu) * d;
+    // d * q is exact in fp32; only 127 * 516 = 65532 lies past the fp16 maximum, saturated
+    const float a = fminf(fmaxf((float)(int8_t)(word & 0xFFu) * d, -65504.f), 65504.f);
+    const float b = fminf(fmaxf((float)(int8_t)((word >> 8) & 0xFFu) * d, -65504.f), 65504.f);
     out[j] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) | ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
   }
   *reinterpret_cast<u32x4 *>(dst + strided_offset(i, per_row, ld, lanes < (int64_t(1) << 32))) =

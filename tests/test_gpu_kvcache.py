@@ -1,12 +1,16 @@
 """GPU parity tests for the 8-bit KV-cache group codec (qg_kv_quantize / qg_kv_dequantize)
 against the oracle ("二三五六位量化" page section 4.1; readings in oracle/kvcache.py).
 
-Bar: bit-exact. The codes and fp16 scales are integer decisions taken in fp32 on both sides,
-and the decoded value fp32(d) * q is exact before its one rounding to fp16, so every code,
-scale and decoded fp16 must equal the oracle's. Covers one group, ragged row counts, strided
-fp16 rows, all-zero groups, values near the fp16 maximum and subnormal ones, and one full
-layer of the 7B-like cache (8192 tokens x 8 KV heads x 128).
+Bar: bit-exact. The codes and fp16 scales are integer decisions with one correct answer (the
+oracle takes them on exact quotients), and the decoded value d * q is exact before its one
+saturating rounding to fp16, so every code, scale and decoded fp16 must equal the oracle's.
+Covers one group, ragged row counts, strided fp16 rows, all-zero groups, exact ties of x / d
+(the golden groups), values at the fp16 maximum (finite decode within d/2) and subnormal ones,
+and one full layer of the 7B-like cache (8192 tokens x 8 KV heads x 128).
 """
+import json
+import os
+
 import numpy as np
 import pytest
 
@@ -46,7 +50,7 @@ def test_kv_codec_bit_exact_against_oracle(rows, cols, ld):
     q_ref, d_ref = kvcache.quantize(x)
     assert np.array_equal(d.view(np.uint16), d_ref.view(np.uint16)), "scales differ"
     assert np.array_equal(q, q_ref), f"codes differ at {np.argwhere(q != q_ref)[:5]}"
-    xh_ref = kvcache.dequantize(q_ref, d_ref).astype(np.float16)
+    xh_ref = kvcache.dequantize_fp16(q_ref, d_ref)
     assert np.array_equal(xh.view(np.uint16), xh_ref.view(np.uint16)), "decoded values differ"
 
 
@@ -62,8 +66,32 @@ def test_kv_codec_special_groups():
     q_ref, d_ref = kvcache.quantize(x)
     assert np.array_equal(d.view(np.uint16), d_ref.view(np.uint16))
     assert np.array_equal(q, q_ref)
-    assert np.array_equal(xh.view(np.uint16), kvcache.dequantize(q_ref, d_ref).astype(np.float16).view(np.uint16))
+    assert np.array_equal(xh.view(np.uint16), kvcache.dequantize_fp16(q_ref, d_ref).view(np.uint16))
     assert np.all(q[3] == 0) and np.all(d[3] == 0) and np.all(xh[3] == 0)
+    # the fp16-maximum group decodes finite, within d/2 of its inputs
+    assert np.all(np.isfinite(xh.astype(np.float32)))
+    err = np.abs(xh[0, :32].astype(np.float64) - x[0, :32].astype(np.float64))
+    assert float(d[0, 0]) == 516.0 and np.all(err <= 516.0 / 2)
+    assert xh[0, 0] == np.float16(65504.0) and xh[0, 33] == np.float16(-65504.0)
+
+
+def test_kv_codec_golden_groups_and_ties():
+    """Hand-worked groups, among them exact ties x = (k + 1/2) d that go to the even code."""
+    golden = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "kvcache_groups.json")))["groups"]
+    x = np.zeros((len(golden), 32), np.float16)
+    for gi, grp in enumerate(golden):
+        for i, v in grp["values"].items():
+            x[gi, int(i)] = v
+    q, d, xh = _roundtrip(x)
+    for gi, grp in enumerate(golden):
+        assert d[gi, 0].view(np.uint16) == int(grp["scale_bits"], 16), grp
+        want = np.zeros(32, np.int8)
+        for i, c in grp["codes"].items():
+            want[int(i)] = c
+        assert np.array_equal(q[gi], want), (gi, q[gi], want)
+        for i, bits in grp.get("fp16_decode_bits", {}).items():
+            assert xh[gi, int(i)].view(np.uint16) == int(bits, 16)
+    assert np.all(np.isfinite(xh.astype(np.float32)))
 
 
 def test_kv_codec_full_layer_of_7b_cache():
