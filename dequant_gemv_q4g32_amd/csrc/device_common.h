@@ -11,6 +11,13 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // fp16 0x6400 is 1024.0; OR-ing a field n < 1024 into the mantissa gives 1024 + n exactly.
 constexpr uint32_t kMagic = 0x64006400u;
+// The same trick with the exponent lowered by a code's bit offset gives the code itself with
+// unit weight: a code c at mantissa bits 3.. under 128.0 (0x5800) is 128 + c, at bits 4..
+// under 64.0 (0x5400) is 64 + c, at bits 6.. under 16.0 (0x4C00) is 16 + c (all exact in fp16),
+// so no activation or step has to be divided by the bit position's power of two.
+constexpr uint32_t kMagic128 = 0x58005800u;
+constexpr uint32_t kMagic64 = 0x54005400u;
+constexpr uint32_t kMagic16 = 0x4C004C00u;
 constexpr uint32_t kOnes = 0x3C003C00u;   // (1.0, 1.0) in fp16
 
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
@@ -32,9 +39,10 @@ __device__ __forceinline__ uint32_t vreg(uint32_t v) {
   return r;
 }
 #define QG_SMASK(v) ::qg::sreg(v)
-// (v & mask) | t, and (v & mask) | 0x6400 in both fp16 halves.
+// (v & mask) | t, and (v & mask) | magic (1024.0 by default) in both fp16 halves.
 __device__ __forceinline__ uint32_t pick_or(uint32_t v, uint32_t mask, uint32_t t) { return (v & mask) | t; }
-__device__ __forceinline__ uint32_t pick(uint32_t v, uint32_t mask) { return (v & mask) | vreg(kMagic); }
+template <uint32_t MG = kMagic>
+__device__ __forceinline__ uint32_t pick(uint32_t v, uint32_t mask) { return (v & mask) | vreg(MG); }
 // Keeps v as computed: stops the compiler from re-associating (a & m) | ((b & m') | c) into
 // and, and, or3 (three instructions) instead of two v_and_or_b32.
 __device__ __forceinline__ uint32_t keep(uint32_t v) {

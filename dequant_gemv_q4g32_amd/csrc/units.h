@@ -51,11 +51,11 @@ __device__ __forceinline__ uint32_t fields24(const Lane &L, int p, int64_t r) {
 
 __device__ __forceinline__ uint32_t sel(bool c, uint32_t a, uint32_t b) { return c ? a : b; }
 
-// ---- decode to fp16 weights (for the MFMA path): from a code pair P = (1024 + p*c_a,
-// 1024 + p*c_b) to the fp16 pair of w_hat.
-// Symmetric formats: w_hat = step * (c - o) = (P - (1024 + p*o)) * (step / p). The subtraction
-// is exact (small integers); the product is one fp16 rounding of a value whose factor step/p
-// was itself rounded to fp16 once.
+// ---- decode to fp16 weights (for the MFMA path): from a code pair P = (B + c_a, B + c_b)
+// (a class magic B: 1024, 128, 64 or 16) to the fp16 pair of w_hat.
+// Symmetric formats: w_hat = step * (c - o) = (P - (B + o)) * step. The subtraction is exact
+// (small integers); the product is one fp16 rounding of a value whose factor step was itself
+// rounded to fp16 once. A step below 2^-14 (an fp16 subnormal) keeps only 2^-25 absolute.
 __device__ __forceinline__ uint32_t sym_pair(uint32_t P, _Float16 off, _Float16 mul) {
   const h2_t v = __builtin_bit_cast(h2_t, P);
   const h2_t o = {off, off}, m = {mul, mul};
@@ -211,12 +211,12 @@ template <int G> struct UnitQ4 {
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const _Float16 m1 = (_Float16)sc[i], m16 = (_Float16)(sc[i] * 0.0625f);
+      const _Float16 m1 = (_Float16)sc[i];
       const uint32_t v = dw[i], v8 = v >> 8;
       out[4 * i + 0] = sym_pair(pick(v, QG_SMASK(0x000F000Fu)), (_Float16)-1032.0f, m1);
-      out[4 * i + 1] = sym_pair(pick(v, QG_SMASK(0x00F000F0u)), (_Float16)-1152.0f, m16);
+      out[4 * i + 1] = sym_pair(pick<kMagic64>(v, QG_SMASK(0x00F000F0u)), (_Float16)-72.0f, m1);
       out[4 * i + 2] = sym_pair(pick(v8, QG_SMASK(0x000F000Fu)), (_Float16)-1032.0f, m1);
-      out[4 * i + 3] = sym_pair(pick(v8, QG_SMASK(0x00F000F0u)), (_Float16)-1152.0f, m16);
+      out[4 * i + 3] = sym_pair(pick<kMagic64>(v8, QG_SMASK(0x00F000F0u)), (_Float16)-72.0f, m1);
     }
   }
 };
@@ -333,16 +333,16 @@ template <> struct Unit<kQ4A32> {
                                                             __builtin_bit_cast(uint32_t, q.s[0])))
                             : q.s[0];
     const float zf = (float)((q.z >> (8 * h)) & 0xFFu);
-    // (P - (1024 + p z)) is p (c - z) exactly; times s / p rounded to fp16
-    const _Float16 m1 = (_Float16)sc, m16 = (_Float16)(sc * 0.0625f);
-    const _Float16 o1 = (_Float16)(-1024.0f - zf), o16 = (_Float16)(-1024.0f - 16.0f * zf);
+    // (P - (B + z)) is c - z exactly; times s rounded to fp16
+    const _Float16 m1 = (_Float16)sc;
+    const _Float16 o1 = (_Float16)(-1024.0f - zf), o16 = (_Float16)(-64.0f - zf);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const uint32_t v = dw[i], v8 = v >> 8;
       out[4 * i + 0] = sym_pair(pick(v, QG_SMASK(0x000F000Fu)), o1, m1);
-      out[4 * i + 1] = sym_pair(pick(v, QG_SMASK(0x00F000F0u)), o16, m16);
+      out[4 * i + 1] = sym_pair(pick<kMagic64>(v, QG_SMASK(0x00F000F0u)), o16, m1);
       out[4 * i + 2] = sym_pair(pick(v8, QG_SMASK(0x000F000Fu)), o1, m1);
-      out[4 * i + 3] = sym_pair(pick(v8, QG_SMASK(0x00F000F0u)), o16, m16);
+      out[4 * i + 3] = sym_pair(pick<kMagic64>(v8, QG_SMASK(0x00F000F0u)), o16, m1);
     }
   }
 };
@@ -466,14 +466,12 @@ template <bool BF> struct UnitQ3 {
     q.f = fields24(L, 2, r);
     q.d = bldh(L.rs[3], L.off[3], L.row(3, r));
   }
-  // The pairs of sub-block a sit at classes 1 (pairs 0..5) and 8 (6, 7), those of b at
-  // classes 8 (8..11) and 64 (12..15). prep divides the activations of the class-8 and
-  // class-64 pairs by 8 and 64 (exact in fp16 down to 2^-11 and 2^-8 of |x|, below which the
-  // quotient is subnormal and rounds by at most 2^-25), so that each sub-block accumulates
-  // in one register: sum P x = sum c x + 1024 X1 + 128 X8 (a), sum c x + 128 X8 + 16 X64 (b)
-  // with X the sums of the original x over each class.
+  // The pairs of sub-block a sit at bit classes 1 (pairs 0..5) and 8 (6, 7), those of b at
+  // classes 8 (8..11) and 64 (12..15). Each class has its own magic (1024, 128, 16), so every
+  // pair decodes to (B + c_a, B + c_b) with unit weight and each sub-block accumulates in one
+  // register from the activations as given: sum P x = sum c x + 1024 X1 + 128 X8 (a),
+  // sum c x + 128 X8 + 16 X64 (b), with X the sums of x over each class.
   template <int S> __device__ static void prep(uint32_t *xp, float *kc) {
-    const h2_t s8 = {(_Float16)0.125f, (_Float16)0.125f}, s64 = {(_Float16)0.015625f, (_Float16)0.015625f};
 #pragma unroll
     for (int c = 0; c < 2 / S; ++c) {
       uint32_t *x = xp + 16 * c;
@@ -488,14 +486,11 @@ template <bool BF> struct UnitQ3 {
       for (int r = 12; r < 16; ++r) b64 = dot2(x[r], kOnes, b64);
       kc[2 * c] = -(1028.0f * a1 + 132.0f * a8);       // start of a: sum (c - 4) x
       kc[2 * c + 1] = -(132.0f * b8 + 20.0f * b64);    // start of b: sum (c - 4) x
-#pragma unroll
-      for (int r = 6; r < 12; ++r) x[r] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, x[r]) * s8);
-#pragma unroll
-      for (int r = 12; r < 16; ++r) x[r] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, x[r]) * s64);
     }
   }
   // One chunk: three dwords e0..e2 holding 32 codes -> the 16 fp16 pairs of its two
-  // sub-blocks (a: P[0..7], classes 1 x6 and 8 x2; b: P[8..15], classes 8 x4 and 64 x4).
+  // sub-blocks (a: P[0..7], classes 1 x6 and 8 x2; b: P[8..15], classes 8 x4 and 64 x4),
+  // each (B + c_a, B + c_b) with B = 1024, 128, 16 for classes 1, 8, 64.
   __device__ static void chunk_pairs(uint32_t e0, uint32_t e1, uint32_t e2, uint32_t *P) {
     const uint32_t e09 = e0 >> 9, e19 = e1 >> 9, e29 = e2 >> 9;
     P[0] = pick(e0, QG_SMASK(0x00070007u));
@@ -504,16 +499,16 @@ template <bool BF> struct UnitQ3 {
     P[3] = pick(e19, QG_SMASK(0x00070007u));
     P[4] = pick(e2, QG_SMASK(0x00070007u));
     P[5] = pick(e29, QG_SMASK(0x00070007u));
-    P[6] = pick(e0, QG_SMASK(0x00380038u));
-    P[7] = pick(e09, QG_SMASK(0x00380038u));
-    P[8] = pick(e1, QG_SMASK(0x00380038u));
-    P[9] = pick(e19, QG_SMASK(0x00380038u));
-    P[10] = pick(e2, QG_SMASK(0x00380038u));
-    P[11] = pick(e29, QG_SMASK(0x00380038u));
-    P[12] = pick(e0, QG_SMASK(0x01C001C0u));
-    P[13] = pick(e1, QG_SMASK(0x01C001C0u));
-    P[14] = pick(e2, QG_SMASK(0x01C001C0u));
-    uint32_t t = keep(pick(e09, QG_SMASK(0x00400040u)));    // bit 15 of e0 -> 6, bit 31 -> 22
+    P[6] = pick<kMagic128>(e0, QG_SMASK(0x00380038u));
+    P[7] = pick<kMagic128>(e09, QG_SMASK(0x00380038u));
+    P[8] = pick<kMagic128>(e1, QG_SMASK(0x00380038u));
+    P[9] = pick<kMagic128>(e19, QG_SMASK(0x00380038u));
+    P[10] = pick<kMagic128>(e2, QG_SMASK(0x00380038u));
+    P[11] = pick<kMagic128>(e29, QG_SMASK(0x00380038u));
+    P[12] = pick<kMagic16>(e0, QG_SMASK(0x01C001C0u));
+    P[13] = pick<kMagic16>(e1, QG_SMASK(0x01C001C0u));
+    P[14] = pick<kMagic16>(e2, QG_SMASK(0x01C001C0u));
+    uint32_t t = keep(pick<kMagic16>(e09, QG_SMASK(0x00400040u)));    // bit 15 of e0 -> 6, bit 31 -> 22
     t = keep(pick_or(e1 >> 8, QG_SMASK(0x00800080u), t));    // bit 15 of e1 -> 7
     P[15] = pick_or(e2 >> 7, QG_SMASK(0x01000100u), t);      // bit 15 of e2 -> 8
   }
@@ -569,16 +564,15 @@ template <bool BF> struct UnitQ3 {
     const uint32_t fh = q.f >> (12 * h);
     const float dv = ss_one<BF>(q.d);
     const float sa = dv * (float)(fh & 63u), sb = dv * (float)((fh >> 6) & 63u);
-    const _Float16 a1 = (_Float16)sa, a8 = (_Float16)(sa * 0.125f);
-    const _Float16 b8 = (_Float16)(sb * 0.125f), b64 = (_Float16)(sb * 0.015625f);
+    const _Float16 a1 = (_Float16)sa, b1 = (_Float16)sb;
 #pragma unroll
     for (int r = 0; r < 6; ++r) out[r] = sym_pair(P[r], (_Float16)-1028.0f, a1);
-    out[6] = sym_pair(P[6], (_Float16)-1056.0f, a8);
-    out[7] = sym_pair(P[7], (_Float16)-1056.0f, a8);
+    out[6] = sym_pair(P[6], (_Float16)-132.0f, a1);
+    out[7] = sym_pair(P[7], (_Float16)-132.0f, a1);
 #pragma unroll
-    for (int r = 8; r < 12; ++r) out[r] = sym_pair(P[r], (_Float16)-1056.0f, b8);
+    for (int r = 8; r < 12; ++r) out[r] = sym_pair(P[r], (_Float16)-132.0f, b1);
 #pragma unroll
-    for (int r = 12; r < 16; ++r) out[r] = sym_pair(P[r], (_Float16)-1280.0f, b64);
+    for (int r = 12; r < 16; ++r) out[r] = sym_pair(P[r], (_Float16)-20.0f, b1);
   }
 };
 template <> struct Unit<3> : UnitQ3<false> {};
@@ -607,10 +601,9 @@ template <> struct Unit<kQ3G32> : UnitQ3<false> {
     q.mn[1] = __builtin_bit_cast(float, keep(mv.y));
   }
   // Per chunk: the start of its accumulator (sum P x = sum c x + 1024 X1 + 128 X8a + 128 X8b
-  // + 16 X64, with the class-8 and class-64 activations divided as for q3sb) and sum x.
+  // + 16 X64, with q3sb's class magics) and sum x.
   // kc layout (S = 1): [start g0, start g1, sum x g0, sum x g1]; (S = 2): [start, sum x]
   template <int S> __device__ static void prep(uint32_t *xp, float *kc) {
-    const h2_t s8 = {(_Float16)0.125f, (_Float16)0.125f}, s64 = {(_Float16)0.015625f, (_Float16)0.015625f};
 #pragma unroll
     for (int c = 0; c < 2 / S; ++c) {
       uint32_t *x = xp + 16 * c;
@@ -625,10 +618,6 @@ template <> struct Unit<kQ3G32> : UnitQ3<false> {
       for (int r = 12; r < 16; ++r) b64 = dot2(x[r], kOnes, b64);
       kc[c] = -(1024.0f * a1 + 128.0f * (a8 + b8) + 16.0f * b64);
       kc[2 / S + c] = (a1 + a8) + (b8 + b64);
-#pragma unroll
-      for (int r = 6; r < 12; ++r) x[r] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, x[r]) * s8);
-#pragma unroll
-      for (int r = 12; r < 16; ++r) x[r] = __builtin_bit_cast(uint32_t, __builtin_bit_cast(h2_t, x[r]) * s64);
     }
   }
   template <int M, int S>
@@ -661,38 +650,39 @@ template <> struct Unit<kQ3G32> : UnitQ3<false> {
       }
     }
   }
-  // fp16 w_hat of the 16 pairs of chunk h: P * (s / p) + (m - 1024 s / p) for class p, in fp32,
-  // then one rounding
+  // fp16 w_hat of the 16 pairs of chunk h: P * s + (m - B s) for class magic B, in fp32, then
+  // one rounding
   template <int S = 1> __device__ static void wide(const Raw &q, int h, uint32_t *out) {
     uint32_t P[16];
     chunk_pairs(sel(h, q.a.w, q.a.x), sel(h, q.b.x, q.a.y), sel(h, q.b.y, q.a.z), P);
     const float sc = __builtin_bit_cast(float, sel(h, __builtin_bit_cast(uint32_t, q.s[1]), __builtin_bit_cast(uint32_t, q.s[0])));
     const float mn = __builtin_bit_cast(float, sel(h, __builtin_bit_cast(uint32_t, q.mn[1]), __builtin_bit_cast(uint32_t, q.mn[0])));
     const float mul1 = sc, add1 = __builtin_fmaf(-1024.0f, sc, mn);
-    const float mul8 = sc * 0.125f, add8 = __builtin_fmaf(-128.0f, sc, mn);
-    const float mul64 = sc * 0.015625f, add64 = __builtin_fmaf(-16.0f, sc, mn);
+    const float add8 = __builtin_fmaf(-128.0f, sc, mn), add64 = __builtin_fmaf(-16.0f, sc, mn);
 #pragma unroll
     for (int r = 0; r < 6; ++r) out[r] = asym_pair(P[r], mul1, add1);
 #pragma unroll
-    for (int r = 6; r < 12; ++r) out[r] = asym_pair(P[r], mul8, add8);
+    for (int r = 6; r < 12; ++r) out[r] = asym_pair(P[r], mul1, add8);
 #pragma unroll
-    for (int r = 12; r < 16; ++r) out[r] = asym_pair(P[r], mul64, add64);
+    for (int r = 12; r < 16; ++r) out[r] = asym_pair(P[r], mul1, add64);
   }
 };
 
 // ---- nibble plane + high-bit plane (q5sb: 1 high bit, 32-weight sub-blocks;
 //      q6sb: 2 high bits, 16-weight sub-blocks). Produces the four pairs of one nibble dword.
-template <int HB>
+// The class-16 pairs take magic M16: 1024 (1024 + 16 c, for the fp32-combined dot) or 64
+// (64 + c, for the fp16 decode).
+template <int HB, uint32_t M16 = kMagic>
 __device__ __forceinline__ void nib_pairs(uint32_t L, uint32_t H, int ip, uint32_t *P) {
   constexpr uint32_t m1 = HB == 1 ? 0x00100010u : 0x00300030u;
   constexpr uint32_t m16 = HB == 1 ? 0x01000100u : 0x03000300u;
   const int ra = HB * ip, rb = 8 + HB * ip;
   const uint32_t ha = ra ? rotr(H, ra) : H, hb = rotr(H, rb);
   const uint32_t L8 = L >> 8;
-  P[0] = pick_or(L, QG_SMASK(0x000F000Fu), keep(pick(ha, QG_SMASK(m1))));    // class 1
-  P[1] = pick_or(L, QG_SMASK(0x00F000F0u), keep(pick(ha, QG_SMASK(m16))));   // class 16
-  P[2] = pick_or(L8, QG_SMASK(0x000F000Fu), keep(pick(hb, QG_SMASK(m1))));   // class 1
-  P[3] = pick_or(L8, QG_SMASK(0x00F000F0u), keep(pick(hb, QG_SMASK(m16))));  // class 16
+  P[0] = pick_or(L, QG_SMASK(0x000F000Fu), keep(pick(ha, QG_SMASK(m1))));         // class 1
+  P[1] = pick_or(L, QG_SMASK(0x00F000F0u), keep(pick<M16>(ha, QG_SMASK(m16))));   // class 16
+  P[2] = pick_or(L8, QG_SMASK(0x000F000Fu), keep(pick(hb, QG_SMASK(m1))));        // class 1
+  P[3] = pick_or(L8, QG_SMASK(0x00F000F0u), keep(pick<M16>(hb, QG_SMASK(m16))));  // class 16
 }
 
 // ---- 5-bit super-block: a unit is two sub-blocks of 32; with S = 2 lane half h owns one
@@ -955,16 +945,20 @@ template <bool BF> struct UnitQ6 {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const float step = dv * (float)(int8_t)((q.sc >> (8 * (2 * h + j))) & 0xFFu);
-      const _Float16 m1 = (_Float16)step, m16 = (_Float16)(step * 0.0625f);
+      // The 6-bit codes' step is about max|w| / 31.5, small enough to fall below fp16's normal
+      // range on small layers, so it stays fp32: P * step + add is exact in fp32 (step has at
+      // most 19 significant bits, 1056 = 33 * 32 and 96 = 3 * 32 keep add exact, and
+      // (c - 32) * step fits 24 bits), and the one rounding is to fp16.
+      const float add1 = -1056.0f * step, add16 = -96.0f * step;
       const uint32_t H = S == 1 ? sel(h, Hd[2 + j], Hd[j]) : Hd[j];
 #pragma unroll
       for (int ii = 0; ii < 2; ++ii) {
         uint32_t P[4];
-        nib_pairs<2>(S == 1 ? sel(h, L[4 + 2 * j + ii], L[2 * j + ii]) : L[2 * j + ii], H, ii, P);
-        out[8 * j + 4 * ii + 0] = sym_pair(P[0], (_Float16)-1056.0f, m1);
-        out[8 * j + 4 * ii + 1] = sym_pair(P[1], (_Float16)-1536.0f, m16);
-        out[8 * j + 4 * ii + 2] = sym_pair(P[2], (_Float16)-1056.0f, m1);
-        out[8 * j + 4 * ii + 3] = sym_pair(P[3], (_Float16)-1536.0f, m16);
+        nib_pairs<2, kMagic64>(S == 1 ? sel(h, L[4 + 2 * j + ii], L[2 * j + ii]) : L[2 * j + ii], H, ii, P);
+        out[8 * j + 4 * ii + 0] = asym_pair(P[0], step, add1);
+        out[8 * j + 4 * ii + 1] = asym_pair(P[1], step, add16);
+        out[8 * j + 4 * ii + 2] = asym_pair(P[2], step, add1);
+        out[8 * j + 4 * ii + 3] = asym_pair(P[3], step, add16);
       }
     }
   }
