@@ -5,6 +5,10 @@ PyTorch supplies device memory and streams: device arguments are torch tensors o
 device, and work is enqueued on torch's current stream unless ``stream`` is given.
 Importing this module fails if the shared library has not been built
 (``python dequant_gemv_q4g32_amd/build.py``); there is no fallback implementation.
+
+QGEMV_HOST_ONLY_LIBRARY=<path> loads a build of the host code alone instead (the sanitizer
+build of ``build.build_host_sanitized``): only the host functions are bound then, and every
+device entry point is absent, so calling one raises instead of running anywhere else.
 """
 from __future__ import annotations
 
@@ -16,7 +20,12 @@ from typing import Optional
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libqgemv.so")
+HOST_ONLY_LIB = os.environ.get("QGEMV_HOST_ONLY_LIBRARY")
+LIB_PATH = HOST_ONLY_LIB or os.path.join(_HERE, "libqgemv.so")
+# exported by the host code (host.cpp); everything else is device code
+HOST_FUNCTIONS = ("qg_abi_version", "qg_strerror", "qg_canonical_bytes", "qg_device_layout",
+                  "qg_packed_bytes", "qg_pack_bits", "qg_unpack_bits", "qg_quantize", "qg_to_device_layout",
+                  "qg_from_device_layout")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "qgemv.h")
 
 FORMATS = {"q2sb": 2, "q3sb": 3, "q4g32": 4, "q5sb": 5, "q6sb": 6, "q4g16": 7, "q4g64": 8, "q4g128": 9,
@@ -53,10 +62,11 @@ def _load() -> ctypes.CDLL:
     # makes libqgemv bind to that one runtime; loading libqgemv first would map a second HIP
     # and HSA runtime into the process, which then finds no device, and torch's streams and
     # device pointers would mean nothing to it anyway.
-    try:
-        import torch  # noqa: F401
-    except ImportError:
-        pass
+    if not HOST_ONLY_LIB:
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
     if not os.path.exists(LIB_PATH):
         raise ImportError(f"{LIB_PATH} is not built; run `python dequant_gemv_q4g32_amd/build.py`")
     lib = ctypes.CDLL(LIB_PATH)
@@ -67,6 +77,7 @@ def _load() -> ctypes.CDLL:
         "qg_last_hip_error": ([], ctypes.c_char_p),
         "qg_canonical_bytes": ([i32, i64, i64, ctypes.POINTER(i64)], i32),
         "qg_device_layout": ([i32, i64, i64, ctypes.POINTER(Layout)], i32),
+        "qg_packed_bytes": ([i32, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)], i32),
         "qg_pack_bits": ([i32, vp, i64, vp], i32),
         "qg_unpack_bits": ([i32, vp, i64, vp], i32),
         "qg_quantize": ([i32, vp, i64, i64, i64, vp], i32),
@@ -88,6 +99,8 @@ def _load() -> ctypes.CDLL:
         sig[f"dequant_gemm_{f}"] = ([vp, vp, i64, vp, i64, i64, i64, i64, vp], i32)
         sig[f"dequantize_{f}"] = ([vp, vp, vp, i64, i64, vp], i32)
     for name, (args, res) in sig.items():
+        if HOST_ONLY_LIB and not (name in HOST_FUNCTIONS or name.startswith("quantize_")):
+            continue
         fn = getattr(lib, name)
         fn.argtypes = args
         fn.restype = res

@@ -25,7 +25,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libqgemv.so")
 
 HOST_SOURCES = ["host.cpp"]
-DEVICE_SOURCES = ["gemv.hip", "prefill.hip", "skinny.hip", "kvcache.hip"]
+DEVICE_SOURCES = ["gemv.hip", "prefill.hip", "skinny.hip", "kvcache.hip"] + sorted(
+    f for f in os.listdir(CSRC) if f.startswith("mv_") and f.endswith(".hip"))   # streaming launchers per format
 ARCH = "gfx950"
 
 
@@ -76,5 +77,26 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def build_host_sanitized(verbose: bool = False) -> str:
+    """The host code alone (quantizers, bitstreams, layouts) as a CPU shared library built by g++
+    with AddressSanitizer and UndefinedBehaviorSanitizer, aborting on the first report. It is
+    loaded through QGEMV_HOST_ONLY_LIBRARY by the host tests (see the package docstring); a
+    process that loads it must preload the ASan runtime (g++ -print-file-name=libasan.so)."""
+    gxx = shutil.which("g++")
+    if not gxx:
+        raise RuntimeError("g++ not found")
+    os.makedirs(BUILD, exist_ok=True)
+    out = os.path.join(BUILD, "libqgemv_host_san.so")
+    tmp = out + ".tmp"
+    _run([gxx, "-std=c++17", "-O1", "-g", "-fno-omit-frame-pointer", "-ffp-contract=off", "-fPIC", "-shared",
+          "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", f"-I{ROOT}/include",
+          os.path.join(CSRC, "host.cpp"), "-o", tmp, "-lpthread"], verbose)
+    os.replace(tmp, out)
+    return out
+
+
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    if "--host-sanitized" in sys.argv:
+        print(build_host_sanitized(verbose="-v" in sys.argv))
+    else:
+        print(build(verbose="-v" in sys.argv))

@@ -728,6 +728,15 @@ int qg_device_layout(int fmt, int64_t n, int64_t k, qg_layout *out) {
   return qg::layout(fmt, n, k, out);
 }
 
+int qg_packed_bytes(int fmt, int64_t n, int64_t k, int64_t *total, int64_t *algorithmic) {
+  qg_layout l;
+  const int st = qg_device_layout(fmt, n, k, &l);
+  if (st != QG_OK) return st;
+  if (total) *total = l.total_bytes;
+  if (algorithmic) *algorithmic = l.algorithmic_bytes;
+  return QG_OK;
+}
+
 int qg_pack_bits(int bits, const uint8_t *codes, int64_t count, uint8_t *out) {
   if (bits < 1 || bits > 8) return QG_ERR_FORMAT;
   if (count < 0) return QG_ERR_SHAPE;

@@ -3,7 +3,7 @@
 //
 // Method: "二三五六位量化" page section 1.2 (prefill multiplies the same low-bit weights by
 // many activation rows, so the work is a dense contraction; the dequantized weights are fp16)
-// and DBHOO-CIM page section 6 (large batches become compute-bound). The codes are turned
+// and DBHOO-CIM page section 5.2 (large prefill batches turn compute-bound). The codes are turned
 // into fp16 w_hat by the same per-format unit decode as the GEMV (units.h, `wide`), written
 // once per K step into an LDS tile that every wave of the workgroup reads.
 //

@@ -1,6 +1,6 @@
 // Dequant GEMM for a decode batch of 5 to 16 activation rows on the matrix cores, gfx950.
 //
-// Method: "二三五六位量化" page section 1.2 and DBHOO-CIM page section 6 (a decode batch is
+// Method: "二三五六位量化" page section 1.2 and DBHOO-CIM page section 5.2 (a decode batch is
 // the GEMV with several activation rows, still bound by the weight stream). On the vector
 // units every code pair costs one v_dot2 per activation row, so 8 rows need about 300 TFLOP/s
 // at 8 TB/s, twice what v_dot2 delivers. Here each code is decoded once to fp16 w_hat (the

@@ -147,10 +147,21 @@ const char *qg_last_hip_error(void);
 
 /* ---- sizes and layouts (host) ------------------------------------------------------- */
 
-/* Bytes of the canonical encoding of an n x k matrix. */
+/* Bytes of the canonical encoding of an n x k matrix: n * k / 256 records of 84 / 110 / 176 /
+ * 210 bytes for the super-block formats ("二三五六位量化" page section 2.3, byte table), and
+ * for INT4 16 bytes of codes plus the scale bytes per group (DBHOO-CIM page sections 3.2, 4.1).
+ * Errors: QG_ERR_NULL, QG_ERR_FORMAT, QG_ERR_SHAPE. */
 int qg_canonical_bytes(int fmt, int64_t n, int64_t k, int64_t *bytes);
-/* Device layout of an n x k matrix. */
+/* Device layout of an n x k matrix: the planes (codes, high-bit planes, sub-scales,
+ * super-scales) kept apart, as the pages advise for the scales (DBHOO-CIM page section 4.1,
+ * "二三五六位量化" page section 2.3), with their offsets and row strides; algorithmic_bytes
+ * equals the canonical size. Errors: QG_ERR_NULL, QG_ERR_FORMAT, QG_ERR_SHAPE. */
 int qg_device_layout(int fmt, int64_t n, int64_t k, qg_layout *out);
+/* The two sizes a caller needs, in one call: *total = bytes to allocate for the device layout
+ * (planes and padding), *algorithmic = the bytes one dequant GEMV reads (the canonical size,
+ * which the effective-bandwidth figure of DBHOO-CIM page section 4.4 divides by the time).
+ * Either pointer may be NULL. Errors: QG_ERR_FORMAT, QG_ERR_SHAPE. */
+int qg_packed_bytes(int fmt, int64_t n, int64_t k, int64_t *total, int64_t *algorithmic);
 
 /* ---- bitstreams (host; "二三五六位量化" page section 2.2) ---------------------------- */
 
@@ -186,9 +197,13 @@ int quantize_q5g32(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *c
 int quantize_q3sb_planes(const float *w, int64_t n, int64_t k, int64_t ldw, uint8_t *canonical);
 
 /* Canonical encoding (host) -> device layout (host buffer of qg_device_layout().total_bytes;
- * padding is zeroed). A pure bit permutation. */
+ * padding is zeroed). A pure bit permutation: the scales move to planes of their own
+ * (DBHOO-CIM page section 4.1 keeps scales in a separate array) and the codes to planes of
+ * whole bit fields ("二三五六位量化" page section 2.3 splits 5- and 6-bit codes into a low
+ * plane and a high-bit plane). Errors: QG_ERR_NULL, QG_ERR_FORMAT, QG_ERR_SHAPE. */
 int qg_to_device_layout(int fmt, const uint8_t *canonical, int64_t n, int64_t k, uint8_t *device_layout);
-/* Device layout (host copy) -> canonical encoding. Inverse of qg_to_device_layout. */
+/* Device layout (host copy) -> canonical encoding. Inverse of qg_to_device_layout; same
+ * errors. */
 int qg_from_device_layout(int fmt, const uint8_t *device_layout, int64_t n, int64_t k, uint8_t *canonical);
 
 /* ---- dequant GEMV, batch 1 (device) ------------------------------------------------------
@@ -224,7 +239,9 @@ int qg_gemv(int fmt, const void *w, const uint16_t *x, void *y, int y_f32, int64
  * y_b = W_b x_b with W_b at w + b*w_stride (bytes, multiple of 256), x_b at x + b*x_stride
  * and y_b at y + b*y_stride (elements; x_stride a multiple of 8). Same numerics as qg_gemv.
  * This is how a decode step issues several same-shape projections (or experts) without a
- * launch per matrix. */
+ * launch per matrix ("二三五六位量化" page section 1.2: decode reads every weight once per
+ * token, one stream bound by bandwidth). count == 0 is a no-op. Errors as qg_gemv, and
+ * QG_ERR_SHAPE for count < 0, QG_ERR_ALIGN for a misaligned stride. */
 int qg_gemv_batched(int fmt, const void *w, int64_t w_stride, const uint16_t *x, int64_t x_stride,
                     void *y, int64_t y_stride, int y_f32, int64_t count, int64_t n, int64_t k, void *stream);
 
@@ -234,7 +251,7 @@ int qg_gemv_batched(int fmt, const void *w, int64_t w_stride, const uint16_t *x,
  * decode: the weights are streamed once per launch and each decoded code meets all the
  * launch's activation rows, up to 16 of them ("二三五六位量化" page section 1.2: decode
  * batches and prefill are the same contraction with more activation rows; DBHOO-CIM page
- * section 6: still bandwidth-bound at small batch, compute-bound at large batch). Any m >= 1:
+ * section 5.2: still bandwidth-bound at small batch, compute-bound at large batch). Any m >= 1:
  * m <= 4 runs on the vector units (each decoded code pair meets every activation row in a
  * v_dot2; the kernel of qg_gemv, qg_gemm_grouped and qg_gemm_act_order), 5 <= m <= 16
  * decodes each code once to fp16 and multiplies on the matrix cores in the same single
@@ -311,15 +328,17 @@ int qg_gemm_grouped(int fmt, int count, const void *const *w, const uint16_t *co
 /* ---- 8-bit KV-cache group codec (device) --------------------------------------------------
  * "二三五六位量化" page section 4.1: the KV cache quantized to 8 bits, every 32 elements
  * sharing one fp16 scale (about 1.06 bytes per element, half of fp16). Codes are symmetric
- * int8 in [-127, 127]; the scale d of a group is the smallest fp16 >= max|x| / 127 (fp32
- * arithmetic), q = rint(x * fp32(1 / d)) half-to-even, an all-zero group has d = 0 and q = 0,
- * and every element is within d/2 (up to an fp32 ulp) of fp32(d) * q.
+ * int8 in [-127, 127]; the scale d of a group is the smallest fp16 >= max|x| / 127, q is
+ * rint(x / d) on the exact quotient (halves to even), an all-zero group has d = 0 and q = 0,
+ * and every element is within d/2 of d * q.
  *
  * qg_kv_quantize (on append): src fp16 [rows][ld_src] (first cols used; 16-byte aligned,
  * ld_src a multiple of 8 when rows > 1) -> codes int8 [rows][cols] (8-byte aligned) and scales
  * fp16 [rows][cols/32] (2-byte aligned). qg_kv_dequantize (on read): codes and scales ->
  * dst fp16 [rows][ld_dst] (16-byte aligned, ld_dst a multiple of 8 when rows > 1), each value
- * fp32(d) * q rounded once to fp16. cols must be a multiple of 32. Inputs must be finite
+ * d * q rounded once to fp16 and saturated at +-65504 (d * q exceeds it only for code
+ * +-127 at d = 516, the scale of a group whose maximum is above 65469; the saturated value
+ * is still within d/2 of the input). cols must be a multiple of 32. Inputs must be finite
  * (a NaN or Inf gives unspecified codes for its group). rows == 0 or cols == 0 is a no-op.
  * Errors: QG_ERR_SHAPE, QG_ERR_NULL, QG_ERR_ALIGN, QG_ERR_LAUNCH. */
 int qg_kv_quantize(const uint16_t *src, int64_t ld_src, int64_t rows, int64_t cols, int8_t *codes, uint16_t *scales,

@@ -157,6 +157,20 @@ def test_error_codes():
     assert qg.lib.qg_canonical_bytes(10, 1, 96, ctypes.byref(out)) == -2
 
 
+def test_packed_bytes_gives_both_sizes():
+    """qg_packed_bytes: the allocation size of the device layout and the algorithmic bytes (the
+    canonical size: the byte table's 110 B per 256 weights for q3sb, 20 B per 32 INT4 weights)."""
+    tot, alg = ctypes.c_int64(), ctypes.c_int64()
+    assert qg.lib.qg_packed_bytes(3, 4096, 4096, ctypes.byref(tot), ctypes.byref(alg)) == 0
+    assert alg.value == 4096 * 16 * 110
+    lay = qg.device_layout("q3sb", 4096, 4096)
+    assert tot.value == lay.total_bytes and alg.value == lay.algorithmic_bytes
+    assert qg.lib.qg_packed_bytes(4, 4096, 4096, None, ctypes.byref(alg)) == 0 and alg.value == 4096 * 128 * 20
+    assert qg.lib.qg_packed_bytes(4, 4096, 4096, ctypes.byref(tot), None) == 0
+    assert qg.lib.qg_packed_bytes(3, 1, 100, ctypes.byref(tot), ctypes.byref(alg)) == -2
+    assert qg.lib.qg_packed_bytes(19, 1, 256, ctypes.byref(tot), ctypes.byref(alg)) == -6
+
+
 def test_device_entry_points_validate_without_launching():
     """Argument errors are returned before any HIP call, so they are checkable without a GPU."""
     L = qg.lib
