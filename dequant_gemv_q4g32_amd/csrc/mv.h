@@ -56,7 +56,12 @@ struct GemvArgs {
 // GEMV), S lanes per 64-weight unit (1, or 2 to halve the activation registers when M is
 // large), R rows per pipelined batch, MP more than one pass over K, ONE a single batch of R
 // (2 or 4) rows per row group with no pipeline: launches that fit one resident round of
-// waves, where a second round trip to memory, not the stream rate, would set the time.
+// waves, where a second round trip to memory, not the stream rate, would set the time. DYN
+// (K in one wave): the row batches of a workgroup are handed to its waves one at a time from
+// an LDS counter instead of in fixed runs. Waves of one CU that run the same number of
+// batches were measured to end up to 10 us apart in a 41 us launch (the CU's memory
+// pipeline serves them unevenly), so that each CU ran its last quarter with few loads in
+// flight; with a shared queue the waves of a workgroup end within about one batch.
 
 // Register pipeline stages over row batches. Deeper pipelines spill or lose occupancy and
 // measured no faster.
@@ -70,13 +75,14 @@ template <int M> constexpr int mv_threads() { return M > 4 ? 512 : 1024; }
 // One workgroup of the streaming kernel over matrix b of a (block bx along the rows). Waves
 // past wk * wr (a grouped launch whose workgroup is sized for another matrix) have no rows
 // but still reach the barrier.
-template <int F, int M, int S, int R, bool MP, bool PERM = false, bool ONE = false>
+template <int F, int M, int S, int R, bool MP, bool PERM = false, bool ONE = false, bool DYN = false>
 __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b) {
   constexpr int D = ONE ? 1 : kGemvDepth;      // pipeline stages
   using U = Unit<F>;
   using Raw = typename U::Raw;
   static_assert(R == 1 || R == 2 || (ONE && R == 4), "rows per batch");
   static_assert(!ONE || (!MP && !PERM), "one-shot batches: a single pass, no permutation");
+  static_assert(!DYN || (!MP && !PERM && !ONE && D == 2), "shared batch queue: one pass, K in one wave");
   constexpr int UPW = 64 / S;                  // units per wave
   constexpr int NP = 32 / S;                   // activation pairs per lane and row
   constexpr int NK = U::NKS(S);
@@ -106,6 +112,23 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
   const int nbh = (int)(end - begin);          // batches of this row group (0 only for tiny n)
   const int rows_max = R * a.nb;               // LDS stride of a row group: a.nb >= every nbh
   auto row_of = [&](int j, int i) -> int64_t { return (begin + j) * R + i; };
+  // DYN: the workgroup's batches [dyn_begin, dyn_begin + dyn_total), handed out by dyn_next
+  __shared__ uint32_t dyn_next;
+  int64_t dyn_begin = 0;
+  int dyn_total = 0;
+  if constexpr (DYN) {
+    dyn_begin = bx * a.wr * a.groups / a.rgroups;
+    dyn_total = (int)((bx * a.wr + a.wr) * a.groups / a.rgroups - dyn_begin);
+    if (threadIdx.x == 0) dyn_next = 0;
+    __syncthreads();
+  }
+  auto claim = [&]() -> int {                  // the next batch of the workgroup (wave-uniform)
+    uint32_t v = 0;
+    if (lane == 0) v = __hip_atomic_fetch_add(&dyn_next, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return (int)__builtin_amdgcn_readfirstlane(v);
+  };
+  // first row of batch c (a batch past the end re-reads the last one; its results are dropped)
+  auto dyn_row = [&](int c) -> int64_t { return (dyn_begin + (c < dyn_total ? c : dyn_total - 1)) * R; };
   auto store_y = [&](int mm, int64_t r, float v) {
     const int64_t i = b * a.y_bstride + (int64_t)mm * a.ldy + r;
     if (a.y_f32) reinterpret_cast<float *>(a.y)[i] = v;
@@ -130,7 +153,7 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
 
   const int passes = MP ? a.kpasses : 1;
   for (int kp = 0; kp < passes; ++kp) {
-    if (nbh == 0) break;                       // wave-uniform: a row group past the last batch
+    if (DYN ? dyn_total == 0 : nbh == 0) break;   // wave-uniform: no batch for this wave
     const int64_t u_raw = ((int64_t)kp * a.wk + wk) * UPW + (S == 1 ? lane : lane >> 1);
     const bool act = u_raw < a.units;
     const int64_t u = act ? u_raw : 0;         // inactive lanes read unit 0 and contribute 0
@@ -214,9 +237,13 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
     // ahead of the first wait; without it the scheduler moved most weight loads behind the
     // wait for the activations, so that a wave paid two round trips to memory before its
     // first row instead of one.
+    int dyn_c0 = 0;
+    if constexpr (DYN) dyn_c0 = claim();
     load_x();
     if constexpr (ONE) {
       load_batch(qs[0], row_of(0, 0));
+    } else if constexpr (DYN) {
+      load_batch(qs[0], dyn_row(dyn_c0));
     } else {
 #pragma unroll
       for (int d = 0; d + 1 < D; ++d) load_batch_j(qs[d], d);
@@ -226,8 +253,7 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
 #pragma unroll
     for (int mm = 0; mm < M; ++mm) U::template prep<S>(xp[mm], kc[mm]);
 
-    auto finish_batch = [&](const Raw *q, int j) {
-      const int64_t r0 = row_of(j, 0);
+    auto finish_batch = [&](const Raw *q, int64_t r0, int j) {
       // the batch's R x M partial sums, reduced over the wave together
       constexpr int T = R * M;
       float v[T];
@@ -268,7 +294,22 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
     // Loads are unconditional, so the wait before each compute covers only the oldest stage
     // (a conditional prefetch would force a wait for everything in flight).
     if constexpr (ONE) {
-      finish_batch(qs[0], 0);                  // the row group's only batch (nbh == 1)
+      finish_batch(qs[0], row_of(0, 0), 0);    // the row group's only batch (nbh == 1)
+      continue;
+    }
+    if constexpr (DYN) {
+      // two stages as below; each prefetch claims the next batch of the workgroup
+      int c0 = dyn_c0;
+      for (;;) {
+        const int c1 = claim();
+        load_batch(qs[1], dyn_row(c1));
+        if (c0 >= dyn_total) break;
+        finish_batch(qs[0], dyn_row(c0), 0);
+        c0 = claim();
+        load_batch(qs[0], dyn_row(c0));
+        if (c1 >= dyn_total) break;
+        finish_batch(qs[1], dyn_row(c1), 0);
+      }
       continue;
     }
     for (int j = 0; j < nbh; j += D) {
@@ -276,7 +317,7 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
       for (int d = 0; d < D; ++d) {
         if (j + d >= nbh) break;
         load_batch_j(qs[(d + D - 1) % D], j + d + D - 1);
-        finish_batch(qs[d], j + d);
+        finish_batch(qs[d], row_of(j + d, 0), j + d);
       }
     }
   }
@@ -295,9 +336,9 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
   }
 }
 
-template <int F, int M, int S, int R, bool MP, bool PERM, bool ONE = false>
+template <int F, int M, int S, int R, bool MP, bool PERM, bool ONE = false, bool DYN = false>
 __global__ __launch_bounds__(mv_threads<M>()) void mv_kernel(GemvArgs a) {
-  mv_body<F, M, S, R, MP, PERM, ONE>(a, blockIdx.x, blockIdx.y);
+  mv_body<F, M, S, R, MP, PERM, ONE, DYN>(a, blockIdx.x, blockIdx.y);
 }
 
 // Several matrices (any shapes, one activation-row count) in one launch: blocks
@@ -309,12 +350,12 @@ struct GemvGroup {
   GemvArgs g[kMaxGroup];
 };
 
-template <int F, int M, int S, int R, bool MP, bool ONE = false>
+template <int F, int M, int S, int R, bool MP, bool ONE = false, bool DYN = false>
 __global__ __launch_bounds__(mv_threads<M>()) void mv_group_kernel(GemvGroup G) {
   const int64_t bx = blockIdx.x;
   int gi = 0;
   while (gi + 1 < G.count && bx >= G.block_end[gi]) ++gi;
-  mv_body<F, M, S, R, MP, false, ONE>(G.g[gi], bx - (gi ? G.block_end[gi - 1] : 0), 0);
+  mv_body<F, M, S, R, MP, false, ONE, DYN>(G.g[gi], bx - (gi ? G.block_end[gi - 1] : 0), 0);
 }
 
 // ------------------------------------------------------------------ launch planning ------
@@ -431,8 +472,8 @@ inline MvPlan plan_mv(int ng, const int64_t *n, const int *wk, const int64_t *co
     }
     return blocks;
   };
-  MvPlan best{wk_max, kMinBatches};
-  double best_score = -1.0;
+  MvPlan best{wk_max, kMinBatches}, best_plain{wk_max, kMinBatches};
+  double best_score = -1.0, plain_score = -1.0;
   for (int W = wk_max; W <= max_w && W <= slots && (W <= kMaxPlanW || W == wk_max || lds_block > 0); ++W) {
     double used = 0.0;
     for (int g = 0; g < ng; ++g) used += (double)work[g] * (W / wk[g] * wk[g]) / W;
@@ -448,24 +489,55 @@ inline MvPlan plan_mv(int ng, const int64_t *n, const int *wk, const int64_t *co
       best_score = score;
       best = {W, nbt};
     }
+    if (score > plain_score + 1e-9) {
+      plain_score = score;
+      best_plain = {W, nbt};
+    }
   }
   // Long waves (single-row kernels): about kLongWaves waves, i.e. bpc workgroups of W waves
   // on every CU, each row group taking nbt_long batches, when that is longer than the plan's
   // and within the format's cap. Taken only if the workgroups still fit one even round
   // (blocks <= 256 * bpc): a grid a little larger than that leaves some CUs a second round.
-  if (long_cap > 0) {
-    const int64_t per_wave_slots = kLongWaves / 256;                  // waves per CU
-    const int64_t bpc = best.W < per_wave_slots ? per_wave_slots / best.W : 1;
-    const int64_t denom = (int64_t)256 * best.W * bpc;
-    const int64_t nbt_long = (total + denom - 1) / denom;
-    if (nbt_long > best.nbt && nbt_long <= long_cap && blocks_for(best.W, nbt_long) <= 256 * bpc) best.nbt = nbt_long;
-  }
+  auto lengthen = [&](MvPlan p) {
+    if (long_cap > 0) {
+      const int64_t per_wave_slots = kLongWaves / 256;                  // waves per CU
+      const int64_t bpc = p.W < per_wave_slots ? per_wave_slots / p.W : 1;
+      const int64_t denom = (int64_t)256 * p.W * bpc;
+      const int64_t nbt_long = (total + denom - 1) / denom;
+      if (nbt_long > p.nbt && nbt_long <= long_cap && blocks_for(p.W, nbt_long) <= 256 * bpc) p.nbt = nbt_long;
+    }
+    return p;
+  };
+  best = lengthen(best);
+  // the preferred workgroup size only where the final plan still gives every CU 4 workgroups
+  if (best.W == prefer_w && blocks_for(best.W, best.nbt) < 4 * 256) best = lengthen(best_plain);
   return best;
 }
 
-template <int F, int M, int S, int R, bool MP, bool PERM, bool ONE>
+// Shared batch queues (DYN): workgroups of dyn_waves<F>() waves (fewer if the kernel's
+// registers leave fewer wave slots per CU), exactly one resident round of them, every row
+// group taking an even share of the batches (its workgroup's waves then share them
+// dynamically). Taken for single-row launches with K in one wave and at least kDynMinBatches
+// batches. Measured on the benchmark's launch of 32 4096^2 GEMVs over 1.2 GB of rotating
+// copies, against the fixed runs (three alternating runs, medians): q3sb 40.7 -> 39.1 us with
+// workgroups of 16 waves (40.0 with 8), q4g32 54.4 -> 52.8 with 8 (53.7 with 16), q5sb
+// 59.1 -> 59.6 (within noise). With fewer than about 8 batches per wave of one resident round
+// the claims cost more than the balance gains (the 7B gate and up projections in one launch,
+// 11008 batches: 11.8 -> 13.6 us).
+template <int F> constexpr int dyn_waves() { return light_bits<F>() ? 16 : 8; }
+constexpr int64_t kDynMinBatches = 4 * kSimds * 8;
+inline MvPlan plan_dyn(const int64_t *n, int ng, int64_t count, int R, int wps, int max_w) {
+  const int W = 4 * wps < max_w ? 4 * wps : max_w;
+  const int64_t per_cu = (4 * wps) / W;
+  int64_t batches = 0;
+  for (int g = 0; g < ng; ++g) batches += (n[g] + R - 1) / R * count;
+  const int64_t round = (int64_t)256 * per_cu * W;
+  return {W, (batches + round - 1) / round};
+}
+
+template <int F, int M, int S, int R, bool MP, bool PERM, bool ONE, bool DYN = false>
 int launch_mv_k(GemvArgs a, int64_t count, hipStream_t s) {
-  void (*kern)(GemvArgs) = mv_kernel<F, M, S, R, MP, PERM, ONE>;
+  void (*kern)(GemvArgs) = mv_kernel<F, M, S, R, MP, PERM, ONE, DYN>;
   static const int wps = waves_per_simd(reinterpret_cast<const void *>(kern));
   // act-order activations staged in LDS when they fit beside the partial sums
   const int64_t xl_bytes = a.perm ? a.m * a.k * 2 : 0;
@@ -473,6 +545,7 @@ int launch_mv_k(GemvArgs a, int64_t count, hipStream_t s) {
   MvPlan P = plan_mv(1, &a.n, &a.wk, &count, R, wps, mv_threads<M>() / 64, stage ? xl_bytes : 0,
                      M == 1 && !ONE ? long_nbt<F>() : 0, M == 1 && !PERM && !ONE ? prefer_w<F>() : 0);
   if (ONE) P.nbt = 1;
+  if (DYN) P = plan_dyn(&a.n, 1, count, R, wps, dyn_waves<F>());
   a.wr = P.W / a.wk;
   const int64_t blocks = split_rows(a, R, P.nbt);
   size_t shm = red_bytes(a, R, M);
@@ -485,16 +558,17 @@ int launch_mv_k(GemvArgs a, int64_t count, hipStream_t s) {
   return launch(kern, grid, dim3((unsigned)(64 * P.W)), shm, s, a);
 }
 
-template <int F, int M, int S, int R, bool MP, bool ONE = false>
+template <int F, int M, int S, int R, bool MP, bool ONE = false, bool DYN = false>
 int launch_mv(GemvArgs a, int64_t count, hipStream_t s) {
   if constexpr (ONE) return launch_mv_k<F, M, S, R, MP, false, true>(a, count, s);
+  else if constexpr (DYN) return launch_mv_k<F, M, S, R, MP, false, false, true>(a, count, s);
   else return a.perm ? launch_mv_k<F, M, S, R, MP, true, false>(a, count, s)
                      : launch_mv_k<F, M, S, R, MP, false, false>(a, count, s);
 }
 
-template <int F, int M, int S, int R, bool MP, bool ONE = false>
+template <int F, int M, int S, int R, bool MP, bool ONE = false, bool DYN = false>
 int launch_mv_group(GemvGroup &G, hipStream_t s) {
-  void (*kern)(GemvGroup) = mv_group_kernel<F, M, S, R, MP, ONE>;
+  void (*kern)(GemvGroup) = mv_group_kernel<F, M, S, R, MP, ONE, DYN>;
   static const int wps = waves_per_simd(reinterpret_cast<const void *>(kern));
   int64_t n[kMaxGroup], count[kMaxGroup];
   int wk[kMaxGroup];
@@ -505,6 +579,7 @@ int launch_mv_group(GemvGroup &G, hipStream_t s) {
   }
   MvPlan P = plan_mv(G.count, n, wk, count, R, wps, mv_threads<M>() / 64, 0, M == 1 && !ONE ? long_nbt<F>() : 0);
   if (ONE) P.nbt = 1;
+  if (DYN) P = plan_dyn(n, G.count, 1, R, wps, dyn_waves<F>());
   int64_t blocks = 0;
   size_t shm = 0;
   for (int g = 0; g < G.count; ++g) {
@@ -554,7 +629,12 @@ int launch_mv_s(GemvArgs a, int64_t count, hipStream_t s) {
   if constexpr (M == 1)
     if (!a.perm && one_shot(a.n * count, a.wk)) return launch_mv<F, M, S, kOneRows, false, true>(a, count, s);
   if constexpr (M <= 2)
-    if (a.n * count * a.wk >= 2 * kSimds * 4) return launch_mv<F, M, S, 2, false>(a, count, s);
+    if (a.n * count * a.wk >= 2 * kSimds * 4) {
+      if constexpr (M == 1)
+        if (!a.perm && a.wk == 1 && (a.n + 1) / 2 * count >= kDynMinBatches)
+          return launch_mv<F, M, S, 2, false, false, true>(a, count, s);
+      return launch_mv<F, M, S, 2, false>(a, count, s);
+    }
   return launch_mv<F, M, S, 1, false>(a, count, s);
 }
 
@@ -575,7 +655,11 @@ int launch_mv_group_s(GemvGroup &G, hipStream_t s) {
   if constexpr (M == 1)
     if (one_shot(rows_1, wk_max)) return launch_mv_group<F, M, S, kOneRows, false, true>(G, s);
   if constexpr (M <= 2)
-    if (rows >= 2 * kSimds * 4) return launch_mv_group<F, M, S, 2, false>(G, s);
+    if (rows >= 2 * kSimds * 4) {
+      if constexpr (M == 1)
+        if (wk_max == 1 && (rows_1 + G.count) / 2 >= kDynMinBatches) return launch_mv_group<F, M, S, 2, false, false, true>(G, s);
+      return launch_mv_group<F, M, S, 2, false>(G, s);
+    }
   return launch_mv_group<F, M, S, 1, false>(G, s);
 }
 
