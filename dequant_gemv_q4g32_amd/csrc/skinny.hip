@@ -79,101 +79,114 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWk) void skinny_kernel(SkinnyArgs a)
   const rsrc_t xr = make_rsrc(a.x, kSkX);
   const int cl = lane & 7, li = lane >> 3;         // staging loads: chunk, line within 8
 
-  for (int kp = 0; kp < a.kpasses; ++kp) {
-    // This wave's units in this pass: kDW steps of 4 consecutive units; lane group g takes
-    // unit 4 * step + g, so a load instruction reads 4 units (64 B or more) of each of its
-    // 16 rows contiguously.
-    const int64_t step0 = ((int64_t)kp * a.wk + wk) * kDW;
-    int64_t unit[kDW];
-    bool ulive[kDW];
+  // This wave's units in pass kp: 4 consecutive units; lane group g takes unit 4 * step + g,
+  // so a load instruction reads 4 units (64 B or more) of each of its 16 rows contiguously.
+  auto step_of = [&](int kp) -> int64_t { return (int64_t)kp * a.wk + wk; };
+  auto unit_of = [&](int kp) -> int64_t {
+    const int64_t u = 4 * step_of(kp) + g;
+    return u < a.units ? u : a.units - 1;
+  };
+  // activations (A operands) of pass kp: lane (rl, g) needs the 128 bytes of activation row
+  // rl in unit g, the "line" rl + 16 g. Loaded with 8 consecutive lanes per line (instruction
+  // j reads lines 8j..8j+7, one cache line each), written to this wave's LDS lines, and each
+  // lane reads its own line back: for MFMA s of a unit, local pairs 4 (s & 3).. of half s >> 2.
+  half8_t A[kDW][8];
+  auto a_load = [&](u32x4 *v, int kp) {
+    const int64_t step0 = step_of(kp);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int line = 8 * j + li, arow = line & 15;
+      const int64_t u = 4 * step0 + (line >> 4), kk = u * kUnit + 8 * cl;
+      const bool ok = arow < a.m && u < a.units && kk < a.k;
+      v[j] = bld4c(xr, ok ? (uint32_t)(arow * a.ldx * 2 + kk * 2) : kSkX, 0);
+    }
+  };
+  auto a_stage = [&](const u32x4 *v) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4 *>(stage + (8 * j + li) * kStageLine + 16 * cl) = v[j];
+#pragma unroll
+    for (int s8 = 0; s8 < 8; ++s8)
+      A[0][s8] = *reinterpret_cast<const half8_t *>(stage + lane * kStageLine + 4 * U::pidx(s8 >> 2, 4 * (s8 & 3), 2));
+  };
+
+  // weights of row tile j in pass kp (a tile past the workgroup's last re-loads that one)
+  auto load = [&](Raw *q, int kp, int j) {
+    const int64_t t = tile0 + (j < a.nb ? j : a.nb - 1);
+    int64_t row = t * 16 + rl;
+    row = row < a.n ? row : a.n - 1;
+    const int64_t unit = unit_of(kp);
 #pragma unroll
     for (int d = 0; d < kDW; ++d) {
-      const int64_t u = 4 * (step0 + d) + g;
-      ulive[d] = u < a.units;
-      unit[d] = ulive[d] ? u : a.units - 1;
-    }
-    // activations (A operands): lane (rl, g) needs the 128 bytes of activation row rl in unit
-    // g, the "line" rl + 16 g. Loaded with 8 consecutive lanes per line (instruction j reads
-    // lines 8j..8j+7, one cache line each) into this wave's LDS lines, then each lane reads
-    // its own line: for MFMA s of a unit, local pairs 4 (s & 3).. of half s >> 2.
-    half8_t A[kDW][8];
-    {
-      u32x4 v[8];
+      Lane Ld = L;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int line = 8 * j + li, arow = line & 15;
-        const int64_t u = 4 * step0 + (line >> 4), kk = u * kUnit + 8 * cl;
-        const bool ok = arow < a.m && u < a.units && kk < a.k;
-        v[j] = bld4c(xr, ok ? (uint32_t)(arow * a.ldx * 2 + kk * 2) : kSkX, 0);
+      for (int p = 0; p < 4; ++p) Ld.off[p] = 0;
+      U::offsets(unit, Ld.off);
+      Ld.sh = fields_sh(unit);
+#pragma unroll
+      for (int p = 0; p < 4; ++p) Ld.off[p] += (uint32_t)row * Ld.prb[p];
+      const bool half = (F == 4) && (unit == a.units - 1) && (a.k % 64 != 0);
+      U::load(q[d], Ld, 0, half);
+    }
+  };
+  auto finish = [&](const Raw *q, int kp, int j) {
+    // two accumulators (one per unit half), so that consecutive MFMAs are independent
+    f32x4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int d = 0; d < kDW; ++d)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        uint32_t pr[16];
+        U::wide(q[d], hh, pr);
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const half8_t B = __builtin_bit_cast(half8_t, u32x4{pr[4 * s], pr[4 * s + 1], pr[4 * s + 2], pr[4 * s + 3]});
+          acc2[s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[d][4 * hh + s], B, acc2[s & 1], 0, 0, 0);
+        }
       }
+    const f32x4 acc = acc2[0] + acc2[1];
+    // D of a 16 x 16 MFMA: lane l holds column l % 16 (weight row) and rows 4 (l / 16) + e
+    // (activation rows); tile index m * 16 + n
+    // (each lane owns 4 of the tile's 256 sums; the first pass stores, later passes add)
 #pragma unroll
-      for (int j = 0; j < 8; ++j) *reinterpret_cast<u32x4 *>(stage + (8 * j + li) * kStageLine + 16 * cl) = v[j];
-#pragma unroll
-      for (int s8 = 0; s8 < 8; ++s8)
-        A[0][s8] = *reinterpret_cast<const half8_t *>(stage + lane * kStageLine + 4 * U::pidx(s8 >> 2, 4 * (s8 & 3), 2));
+    for (int e = 0; e < 4; ++e) {
+      float &slot = slots[j * 256 + (4 * g + e) * 16 + rl];
+      slot = kp == 0 ? acc[e] : slot + acc[e];
     }
+  };
 
-    auto load = [&](Raw *q, int j) {
-      const int64_t t = tile0 + (j < a.nb ? j : a.nb - 1);
-      int64_t row = t * 16 + rl;
-      row = row < a.n ? row : a.n - 1;
-#pragma unroll
-      for (int d = 0; d < kDW; ++d) {
-        Lane Ld = L;
-#pragma unroll
-        for (int p = 0; p < 4; ++p) Ld.off[p] = 0;
-        U::offsets(unit[d], Ld.off);
-        Ld.sh = fields_sh(unit[d]);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) Ld.off[p] += (uint32_t)row * Ld.prb[p];
-        const bool half = (F == 4) && (unit[d] == a.units - 1) && (a.k % 64 != 0);
-        U::load(q[d], Ld, 0, half);
+  u32x4 v[8];
+  Raw qa[kDW], qb[kDW];
+  if (a.nb == 1) {
+    // one tile per workgroup (small grids): nothing to pipeline
+    for (int kp = 0; kp < a.kpasses; ++kp) {
+      a_load(v, kp);
+      load(qa, kp, 0);
+      a_stage(v);
+      finish(qa, kp, 0);
+    }
+  } else {
+    // Two register stages over the (pass, tile) sequence, without a drain at the pass
+    // boundaries: the last two tiles of a pass also issue the next pass's activation loads
+    // and its first tile's weight loads, and the activations are staged after the pass's
+    // last MFMAs. (nb is even; every load is unconditional, the last pass "prefetching"
+    // itself, so that each wait covers only the oldest stage.)
+    a_load(v, 0);
+    load(qa, 0, 0);
+    a_stage(v);
+    for (int kp = 0; kp < a.kpasses; ++kp) {
+      const int kn = kp + 1 < a.kpasses ? kp + 1 : kp;
+      for (int j = 0; j + 2 < a.nb; j += 2) {
+        load(qb, kp, j + 1);
+        finish(qa, kp, j);
+        load(qa, kp, j + 2);
+        finish(qb, kp, j + 1);
       }
-    };
-    auto finish = [&](const Raw *q, int j) {
-      // two accumulators (one per unit half), so that consecutive MFMAs are independent
-      f32x4 acc2[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-      for (int d = 0; d < kDW; ++d)
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          uint32_t pr[16];
-          U::wide(q[d], hh, pr);
-#pragma unroll
-          for (int s = 0; s < 4; ++s) {
-            const half8_t B = __builtin_bit_cast(half8_t, u32x4{pr[4 * s], pr[4 * s + 1], pr[4 * s + 2], pr[4 * s + 3]});
-            acc2[s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[d][4 * hh + s], B, acc2[s & 1], 0, 0, 0);
-          }
-        }
-      const f32x4 acc = acc2[0] + acc2[1];
-      // D of a 16 x 16 MFMA: lane l holds column l % 16 (weight row) and rows 4 (l / 16) + e
-      // (activation rows); tile index m * 16 + n
-      // (each lane owns 4 of the tile's 256 sums; the first pass stores, later passes add)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float &slot = slots[j * 256 + (4 * g + e) * 16 + rl];
-        slot = kp == 0 ? acc[e] : slot + acc[e];
-      }
-    };
-    // kStages register stages over the row tiles (loads of kStages - 1 tiles in flight while
-    // one is computed); prefetches past the last tile re-load it
-    Raw qs[kStages][kDW];
-    if (a.nb == 1) {
-      // one tile per workgroup (small grids): nothing to pipeline
-      load(qs[0], 0);
-      finish(qs[0], 0);
-    } else {
-#pragma unroll
-      for (int d = 0; d + 1 < kStages; ++d) load(qs[d], d);
-      // (nb is a multiple of kStages, so the body has no branch and each wait covers only
-      // the oldest stage)
-      for (int j = 0; j < a.nb; j += kStages) {
-#pragma unroll
-        for (int d = 0; d < kStages; ++d) {
-          load(qs[(d + kStages - 1) % kStages], j + d + kStages - 1);
-          finish(qs[d], j + d);
-        }
-      }
+      load(qb, kp, a.nb - 1);
+      finish(qa, kp, a.nb - 2);
+      a_load(v, kn);
+      load(qa, kn, 0);
+      finish(qb, kp, a.nb - 1);
+      a_stage(v);
     }
   }
   __syncthreads();
