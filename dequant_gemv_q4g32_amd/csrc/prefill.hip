@@ -7,14 +7,25 @@
 // into fp16 w_hat by the same per-format unit decode as the GEMV (units.h, `wide`), written
 // once per K step into an LDS tile that every wave of the workgroup reads.
 //
-// Tiling: a workgroup of 4 waves computes a 128 x BN tile of Y (128 activation rows x BN =
-// 128 or 96 weight rows) and walks K in steps of one 64-weight unit. Each step, every thread
-// loads half a unit of one weight row (the first 2 * BN threads) and 16 bytes of each of 4
-// activation rows (two steps ahead, into one of two register stages), decodes its half unit
-// to 16 fp16 pairs and stores both into one of two LDS buffers. Each wave then runs 2 x 2
-// (BN = 128) or 1 x 3 (BN = 96) MFMA tiles of 32 x 32 over the step's 4 K-slices of 16.
-// Workgroups are numbered so that the M tiles sharing a weight tile run on one XCD and share
-// its L2.
+// Tiling: a workgroup of 4 waves computes a BM x BN tile of Y and walks K in steps of one
+// 64-weight unit. Two shapes:
+//   * 256 x 64 (each wave a 64 x 64 block of 2 x 2 MFMA tiles): each weight is decoded once
+//     per 256 activation rows, and the 32 KB of activations a step brings in feed 2 MFLOP;
+//   * 128 x 32 (each wave one 32 x 32 MFMA tile) where 256 x 64 tiles would leave CUs without
+//     a workgroup (512 x 4096 has 128 of them, 128 x 11008 has 172): four times the tiles.
+// Roles per step:
+//   * waves 2 and 3 stream the next step's activation tile (BM rows x 128 bytes) straight
+//     into LDS with buffer_load ... lds (no registers, no LDS store instructions);
+//   * the first 2 BN threads (waves 0 and 1, or wave 0) load the weights two steps ahead
+//     (thread t: half t & 1 of the unit of weight row t >> 1) and decode the next step's to
+//     fp16 into the LDS weight tile;
+//   * all four waves run the current step's MFMAs (4 K-slices of 16).
+// Both tiles are double-buffered in four distinct LDS arrays, so that the compiler can see
+// that the loads into one buffer do not alias the reads of the other, and one barrier per
+// step separates them. Rows are stored with their 16-byte chunks XOR-swizzled by the row's
+// low 3 bits, so that the 32 rows an MFMA operand read touches fall on different banks.
+// Workgroups are numbered so that each XCD works through the tiles of one M tile, whose
+// activation rows then stay in its L2.
 #include <hip/hip_runtime.h>
 
 #include "../../include/qgemv.h"
@@ -27,6 +38,7 @@ namespace qg {
 
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void_t;
 
 struct PrefillArgs {
   const uint8_t *w;
@@ -42,52 +54,46 @@ struct PrefillArgs {
   int mtiles, ntiles, per_xcd;
 };
 
-constexpr int kBM = 128;                 // activation rows per workgroup tile
-// Weight rows per workgroup tile, BN: 128 (4 waves as 2 x 2 of 64 x 64) or 96 (4 waves along
-// M, each 32 x 96). The launch takes the one whose busiest CU has the fewest weight rows.
-constexpr int kLdsRow = kUnit + 8;       // halfs per LDS row: 64 + 8 of padding (bank spread)
-constexpr uint32_t kXRange = 0x7FFFFFF0u; // activation buffer range; offsets at or past it read 0
+constexpr int kMaxBM = 256;                   // activation rows per workgroup tile (256 or 128)
+constexpr int kRowBytes = kUnit * 2;          // one K step of one row in fp16: 128 bytes
+constexpr uint32_t kXRange = 0x7FFFFFF0u;    // activation buffer range; offsets at or past it read 0
 
-template <int F, int BN>
+// byte offset of 16-byte chunk c of row r in a swizzled tile
+__device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t c) { return r * kRowBytes + 16u * (c ^ (r & 7u)); }
+
+template <int F, int BM, int BN>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   using U = Unit<F>;
   using Raw = typename U::Raw;
-  static_assert(BN == 128 || BN == 96, "weight rows per tile");
-  constexpr int WM = BN == 128 ? 2 : 4;                   // waves along M
-  constexpr int TM = kBM / WM / 32, TN = BN / (4 / WM) / 32;   // 32 x 32 MFMA tiles per wave
-  // two LDS buffers per operand: the MFMAs of step u read one while step u+1 is stored into
-  // the other, so one barrier per step suffices
-  __shared__ __attribute__((aligned(16))) _Float16 xs[2][kBM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) _Float16 ws[2][BN * kLdsRow];
+  static_assert((BM == 256 && BN == 64) || (BM == 128 && BN == 32), "tile shape");
+  constexpr int TM = BM / 128;                  // 32-row MFMA tiles per wave (rows BM / 4)
+  constexpr int WN = BN / 32;                   // 32-column MFMA tiles per wave
+  constexpr int NX = BM / 16;                   // 1 KB activation DMA instructions per x-wave
+  __shared__ __attribute__((aligned(16))) uint8_t X0[BM * kRowBytes], X1[BM * kRowBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t W0[BN * kRowBytes], W1[BN * kRowBytes];
 
   // Workgroups are dispatched round-robin over the 8 XCDs; tile numbers are assigned so that
-  // consecutive tiles (the M tiles of one weight tile) fall on the same XCD.
+  // each XCD runs a contiguous range of tiles, M tile major: an XCD's L2 then holds the
+  // activation rows of one M tile (2 MB at K = 4096 and BM = 256), which every step of every
+  // tile reads BM x 128 bytes of, while a weight tile (BN rows of one unit) is read once per M
+  // tile.
   const int bid = blockIdx.x;
   const int tile = (bid & 7) * a.per_xcd + (bid >> 3);
   if (tile >= a.mtiles * a.ntiles) return;
-  // (integer division runs on the vector unit; readfirstlane keeps the tile indices scalar,
-  // so that the buffer resources built from them stay in scalar registers)
-  const int mt = __builtin_amdgcn_readfirstlane(tile % a.mtiles);
-  const int nt = __builtin_amdgcn_readfirstlane(tile / a.mtiles);
-  const int64_t m0 = (int64_t)mt * kBM, r0 = (int64_t)nt * BN;
+  // (integer division runs on the vector unit; readfirstlane keeps the tile indices scalar)
+  const int mt = __builtin_amdgcn_readfirstlane(tile / a.ntiles);
+  const int nt = __builtin_amdgcn_readfirstlane(tile % a.ntiles);
+  const int64_t m0 = (int64_t)mt * BM, r0 = (int64_t)nt * BN;
 
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int wm = wave % WM, wn = wave / WM;        // this wave's (TM x 32) x (TN x 32) block
+  const bool xwave = wave >= 2;                 // wave-uniform role
 
-  // weight loader role: LDS row t >> 1 of the weight tile, half h = t & 1 of the unit
-  const int lrow = t >> 1, h = t & 1;
-  const bool wload = BN == 128 || lrow < BN;       // wave-uniform: threads 2 * BN.. load no weights
+  // ---- weights (waves 0, 1): thread t < 2 BN decodes half t & 1 of weight row t >> 1
+  const bool wload = t < 2 * BN;                // wave-uniform
+  const int lrow = (t & 127) >> 1, h = t & 1;
   const int64_t wrow = r0 + lrow < a.n ? r0 + lrow : a.n - 1;   // rows past n are not stored
-  // activation loader role: rows (t >> 3) + 32 i, 16-byte chunk t & 7 of the step's 128 bytes,
-  // so that 8 consecutive lanes read one row's 128 bytes (whole cache lines)
-  const int xr0 = t >> 3, xc = t & 7;
-  // activations through a buffer resource based at this tile's first row: a dead row or the
-  // missing half of a ragged q4g32 unit gets an offset past the range, which loads zeros (a
-  // select on the loaded data instead would make every step wait for its own loads)
-  const rsrc_t xr = make_rsrc(a.x + m0 * a.ldx, kXRange);
-
   Lane L;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
@@ -95,113 +101,155 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     L.prb[p] = (uint32_t)a.prb[p];
   }
   L.h = h;
-
-  // Global loads of step u into one register stage. Steps past the end re-load the last
-  // step, so that every step issues the same loads and waits only for the older stage.
-  auto gload = [&](Raw &q, u32x4 *xv, int64_t u) {
+  // global loads of step u (steps past the end re-load the last one, never read)
+  auto gload = [&](Raw &q, int64_t u) {
+    if (!wload) return;
     u = u < a.units ? u : a.units - 1;
 #pragma unroll
     for (int p = 0; p < 4; ++p) L.off[p] = 0;
     U::offsets(u, L.off);
     L.sh = fields_sh(u);
     L.set_halves(a.units);
-    // the weight row differs per lane here, so it goes into the per-lane offset (a row in
-    // the scalar offset would force one load per distinct row)
+    // the weight row differs per lane, so it goes into the per-lane offset
 #pragma unroll
     for (int p = 0; p < 4; ++p) L.off[p] += (uint32_t)wrow * L.prb[p];
     const bool half = (F == 4) && (u == a.units - 1) && (a.k % 64 != 0);
-    // only this thread's half of the unit; cached: the weight tile is read again by the
-    // workgroups of the other M tiles
-    if (wload) U::template load<0, 2>(q, L, 0, half);
-    const int64_t kk = u * kUnit + 8 * xc;
+    // cached: the workgroups of the other M tiles read the same weight tile
+    U::template load<0, 2>(q, L, 0, half);
+  };
+  // decode a register stage to fp16 and store it into the weight tile W
+  auto wstore = [&](const Raw &q, uint8_t *W) {
+    if (!wload) return;
+    uint32_t pr[16];
+    U::template wide<2>(q, h, pr);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int xrow = xr0 + 32 * i;
-      const bool ok = m0 + xrow < a.m && kk < a.k;
-      xv[i] = bld4c(xr, ok ? (uint32_t)(xrow * a.ldx * 2 + kk * 2) : kXRange, 0);
+      // local pairs 4i..4i+3 are the unit's consecutive pairs pidx(h, 4i).. (k = 2 * pair), so
+      // they fill 16-byte chunk pidx / 4 of the row
+      const int c = U::pidx(h, 4 * i, 2) >> 2;
+      *reinterpret_cast<u32x4 *>(W + swz(lrow, c)) = u32x4{pr[4 * i], pr[4 * i + 1], pr[4 * i + 2], pr[4 * i + 3]};
     }
-  };
-  // decode a register stage to fp16 and store it, with its activations, into LDS buffer b
-  auto lds_store = [&](const Raw &q, const u32x4 *xv, int b) {
-    if (wload) {
-      uint32_t pr[16];
-      U::template wide<2>(q, h, pr);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // local pairs 4i..4i+3 are the unit's consecutive pairs pidx(h, 4i).. (k = 2 * pair)
-        const int g = U::pidx(h, 4 * i, 2);
-        *reinterpret_cast<u32x4 *>(&ws[b][lrow * kLdsRow + 2 * g]) =
-            u32x4{pr[4 * i], pr[4 * i + 1], pr[4 * i + 2], pr[4 * i + 3]};
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<u32x4 *>(&xs[b][(xr0 + 32 * i) * kLdsRow + 8 * xc]) = xv[i];
   };
 
-  f32x16 acc[TM][TN];
+  // ---- activations (waves 2, 3): instruction i of x-wave xw fills tile rows 8 (NX xw + i) ..
+  // + 7 (1 KB); lane l loads row + (l >> 3), chunk (l & 7) ^ (l >> 3) of the step's 128 bytes,
+  // which lands at LDS position l & 7 of that row: the swizzled layout. A dead row, or the
+  // missing half of a ragged q4g32 unit, gets an offset past the range and reads zeros.
+  const int xw = wave & 1;
+  const int xrow_l = lane >> 3, xc = (lane & 7) ^ (lane >> 3);
+  const rsrc_t xr = make_rsrc(a.x + m0 * a.ldx, kXRange);
+  auto xdma = [&](int64_t u, uint8_t *X) {
+    u = u < a.units ? u : a.units - 1;
+    const int64_t kk = u * kUnit + 8 * xc;
+#pragma unroll
+    for (int i = 0; i < NX; ++i) {
+      const int row = 8 * (NX * xw + i) + xrow_l;
+      const bool ok = m0 + row < a.m && kk < a.k;
+      const uint32_t voff = ok ? (uint32_t)(row * a.ldx * 2 + kk * 2) : kXRange;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t *)(X + (NX * xw + i) * 1024), 16, voff, 0, 0, 0);
+    }
+  };
+
+  // ---- MFMAs of one step: wave w covers tile rows BM w / 4 .., each of its TM 32-row blocks
+  // against every 32-column block of the weight tile
+  f32x16 acc[TM][WN];
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < WN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-  const int arow = lane & 31, akoff = 8 * (lane >> 5);
-  auto mfma_step = [&](int b) {
+  const uint32_t arow = (uint32_t)(BM / 4 * wave + (lane & 31)), brow = (uint32_t)(lane & 31), kh = (uint32_t)(lane >> 5);
+  auto mfma_step = [&](const uint8_t *X, const uint8_t *W) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      half8_t A[TM], B[TN];
+      half8_t A[TM], B[WN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) A[i] = *reinterpret_cast<const half8_t *>(X + swz(arow + 32 * i, 2 * s + kh));
+#pragma unroll
+      for (int j = 0; j < WN; ++j) B[j] = *reinterpret_cast<const half8_t *>(W + swz(brow + 32 * j, 2 * s + kh));
 #pragma unroll
       for (int i = 0; i < TM; ++i)
-        A[i] = *reinterpret_cast<const half8_t *>(&xs[b][(wm * TM * 32 + 32 * i + arow) * kLdsRow + 16 * s + akoff]);
 #pragma unroll
-      for (int j = 0; j < TN; ++j)
-        B[j] = *reinterpret_cast<const half8_t *>(&ws[b][(wn * TN * 32 + 32 * j + arow) * kLdsRow + 16 * s + akoff]);
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i], B[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < WN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i], B[j], acc[i][j], 0, 0, 0);
     }
   };
+  // x-waves: their LDS loads of this step are complete before they reach the barrier
+  auto xwait = [&]() { __builtin_amdgcn_s_waitcnt(0); };
 
-  // Pipeline: at step u, LDS buffer u & 1 holds step u, one register stage holds step u + 1
-  // (loaded during step u - 1) and the other is free, so it receives the loads of step u + 2.
-  Raw q0, q1;
-  u32x4 x0[4], x1[4];
-  gload(q0, x0, 0);
-  gload(q1, x1, 1);
-  lds_store(q0, x0, 0);
-  __syncthreads();
-  // No branches inside a step: past the last step the stage and LDS buffer written are never
-  // read. Two steps per iteration keep the stages in fixed registers.
-  auto body = [&](Raw &ql, u32x4 *xl, const Raw &qs, const u32x4 *xs_, int b, int64_t u) {
-    gload(ql, xl, u + 2);
-    mfma_step(b);
-    lds_store(qs, xs_, b ^ 1);
+  // Pipeline, two steps per iteration so that every buffer and register stage is fixed:
+  // step u computes from X_{u&1}, W_{u&1}; the x-waves fill X_{(u+1)&1}, the weight waves store
+  // the decoded step u + 1 into W_{(u+1)&1} and load step u + 2.
+  const int64_t units = a.units;
+  if (xwave) {
+    xdma(0, X0);
+    xwait();
     __syncthreads();
-  };
-  int64_t u = 0;
-  for (; u + 2 <= a.units; u += 2) {
-    body(q0, x0, q1, x1, 0, u);
-    body(q1, x1, q0, x0, 1, u + 1);
+    int64_t u = 0;
+    for (; u + 2 <= units; u += 2) {
+      xdma(u + 1, X1);
+      mfma_step(X0, W0);
+      xwait();
+      __syncthreads();
+      xdma(u + 2, X0);
+      mfma_step(X1, W1);
+      xwait();
+      __syncthreads();
+    }
+    if (u < units) {
+      xdma(u + 1, X1);
+      mfma_step(X0, W0);
+      xwait();
+      __syncthreads();
+    }
+  } else {
+    Raw q0, q1;
+    gload(q0, 0);
+    gload(q1, 1);
+    wstore(q0, W0);
+    __syncthreads();
+    int64_t u = 0;
+    for (; u + 2 <= units; u += 2) {
+      gload(q0, u + 2);
+      mfma_step(X0, W0);
+      wstore(q1, W1);
+      __syncthreads();
+      gload(q1, u + 3);
+      mfma_step(X1, W1);
+      wstore(q0, W0);
+      __syncthreads();
+    }
+    if (u < units) {
+      gload(q0, u + 2);
+      mfma_step(X0, W0);
+      wstore(q1, W1);
+      __syncthreads();
+    }
   }
-  if (u < a.units) body(q0, x0, q1, x1, 0, u);
 
   // D of a 32 x 32 MFMA: lane l holds column l % 32 and rows 8 (e / 4) + 4 (l / 32) + e % 4
 #pragma unroll
   for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int j = 0; j < TN; ++j)
+    for (int j = 0; j < WN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + wm * TM * 32 + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
-        const int64_t col = r0 + wn * TN * 32 + 32 * j + (lane & 31);
+        const int64_t row = m0 + BM / 4 * wave + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int64_t col = r0 + 32 * j + (lane & 31);
         if (row < a.m && col < a.n) {
           const int64_t idx = row * a.ldy + col;
           if (a.y_f32) reinterpret_cast<float *>(a.y)[idx] = acc[i][j][e];
           else reinterpret_cast<_Float16 *>(a.y)[idx] = (_Float16)acc[i][j][e];
         }
       }
+}
+
+// Tile shape for m x n: 256 x 64 when that gives every CU a workgroup; else 128 x 32, four
+// times the tiles (each K step of a tile is then short, and more of them run at once).
+void prefill_tile(int64_t m, int64_t n, int *bm, int *bn) {
+  const bool big = (m + 255) / 256 * ((n + 63) / 64) >= 256;
+  *bm = big ? 256 : 128;
+  *bn = big ? 64 : 32;
 }
 
 int launch_prefill(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int64_t ldy, int y_f32,
@@ -224,13 +272,10 @@ int launch_prefill(int fmt, const void *w, const uint16_t *X, int64_t ldx, void 
   a.ldy = ldy;
   a.m = m;
   a.y_f32 = y_f32;
-  if (kBM * ldx * 2 >= (int64_t)kXRange) return QG_ERR_SHAPE;     // 32-bit activation offsets
-  // weight rows on the busiest CU: ceil(tiles / 256) tiles of BN rows (the workgroups go out one
-  // per CU first); 96-row tiles when they leave it fewer rows (512 x 11008: 460 tiles, 192 rows
-  // against 344 tiles and 256 rows)
-  const int64_t mtiles = (m + kBM - 1) / kBM;
-  const int64_t t128 = mtiles * ((n + 127) / 128), t96 = mtiles * ((n + 95) / 96);
-  const int BN = (t96 + 255) / 256 * 96 < (t128 + 255) / 256 * 128 ? 96 : 128;
+  if (kMaxBM * ldx * 2 >= (int64_t)kXRange) return QG_ERR_SHAPE;     // 32-bit activation offsets
+  int BM, BN;
+  prefill_tile(m, n, &BM, &BN);
+  const int64_t mtiles = (m + BM - 1) / BM;
   const int64_t ntiles = (n + BN - 1) / BN;
   const int64_t total = mtiles * ntiles;
   if (total > (int64_t(1) << 30)) return QG_ERR_SHAPE;
@@ -238,28 +283,30 @@ int launch_prefill(int fmt, const void *w, const uint16_t *X, int64_t ldx, void 
   a.ntiles = (int)ntiles;
   a.per_xcd = (int)((total + 7) / 8);
   const dim3 grid((unsigned)(8 * a.per_xcd)), block(256);
-  auto go = [&](auto kern128, auto kern96) {
-    return BN == 96 ? launch(kern96, grid, block, 0, s, a) : launch(kern128, grid, block, 0, s, a);
+  auto go = [&](auto big, auto small) {
+    return BM == 256 ? launch(big, grid, block, 0, s, a) : launch(small, grid, block, 0, s, a);
   };
+#define QG_PF(F) go(prefill_kernel<F, 256, 64>, prefill_kernel<F, 128, 32>)
   switch (fmt) {
-    case 2: return go(prefill_kernel<2, 128>, prefill_kernel<2, 96>);
-    case 3: return go(prefill_kernel<3, 128>, prefill_kernel<3, 96>);
-    case 4: return go(prefill_kernel<4, 128>, prefill_kernel<4, 96>);
-    case 5: return go(prefill_kernel<5, 128>, prefill_kernel<5, 96>);
-    case 6: return go(prefill_kernel<6, 128>, prefill_kernel<6, 96>);
-    case 7: return go(prefill_kernel<7, 128>, prefill_kernel<7, 96>);
-    case 8: return go(prefill_kernel<8, 128>, prefill_kernel<8, 96>);
-    case 9: return go(prefill_kernel<9, 128>, prefill_kernel<9, 96>);
-    case 10: return go(prefill_kernel<10, 128>, prefill_kernel<10, 96>);
-    case 11: return go(prefill_kernel<11, 128>, prefill_kernel<11, 96>);
-    case 12: return go(prefill_kernel<12, 128>, prefill_kernel<12, 96>);
-    case 13: return go(prefill_kernel<13, 128>, prefill_kernel<13, 96>);
-    case 14: return go(prefill_kernel<3, 128>, prefill_kernel<3, 96>);   // q3sb's device layout
-    case 15: return go(prefill_kernel<15, 128>, prefill_kernel<15, 96>);
-    case 16: return go(prefill_kernel<16, 128>, prefill_kernel<16, 96>);
-    case 17: return go(prefill_kernel<17, 128>, prefill_kernel<17, 96>);
-    case 18: return go(prefill_kernel<18, 128>, prefill_kernel<18, 96>);
+    case 2: return QG_PF(2);
+    case 3: return QG_PF(3);
+    case 4: return QG_PF(4);
+    case 5: return QG_PF(5);
+    case 6: return QG_PF(6);
+    case 7: return QG_PF(7);
+    case 8: return QG_PF(8);
+    case 9: return QG_PF(9);
+    case 10: return QG_PF(10);
+    case 11: return QG_PF(11);
+    case 12: return QG_PF(12);
+    case 13: return QG_PF(13);
+    case 14: return QG_PF(3);   // q3sb's device layout
+    case 15: return QG_PF(15);
+    case 16: return QG_PF(16);
+    case 17: return QG_PF(17);
+    case 18: return QG_PF(18);
   }
+#undef QG_PF
   return QG_ERR_FORMAT;
 }
 
