@@ -10,14 +10,16 @@ N(0, 1) activations, batch 1). One step is one launch of G independent batch-1 G
 shape (default G = 32, 230 MB of packed weights), each with its own matrix copy and its own
 activation vector. Steps rotate over enough copies (>= 1.2 GB) that every step reads its
 weights from HBM, not from the 256 MB last-level cache. The K timed steps are captured in one
-HIP graph; after W eager warmup steps and one untimed replay (which uploads the graph and lets
-the clocks settle) the graph is replayed between two synchronizes. A single 7.2 MB matrix per launch is also
-timed ("single_launch"): at ~1 us of streaming it is bound by launch cadence, not HBM.
+HIP graph; after W eager warmup steps, one untimed replay (which uploads the graph) and 0.15 s
+of back-to-back untimed replays (the clocks ramp under sustained load), the graph is replayed
+between two synchronizes. A single 7.2 MB matrix per launch is also timed ("single_launch"),
+and reported with the INT4 one under "batch1_one_matrix_per_launch": at ~1 us of streaming
+it is bound by launch cadence, not HBM.
 
 "other_workloads" measures the remaining workloads the same way (HBM-resident rotation,
 graph-timed): INT4 group-32 4096^2, the 7B-like layer set per super-block format (all seven
 matrices in one grouped launch, and in the launches a decode step's data dependencies
-allow), the 70B-like layer set at batch 1, 2, 4 and 8 (one launch per matrix, and one
+allow), the 70B-like layer set at batch 1, 2, 4, 8 and 16 (one launch per matrix, and one
 grouped launch), INT4 with groups of 16, 32, 64 and 128 and act-order INT4 on the 70B-like
 set, the 8-bit KV-cache codec on the
 7B-like cache, and the 512-row prefill GEMM (TFLOP/s and fraction of the 2.5 PFLOP/s dense
@@ -53,20 +55,24 @@ def parse():
     ap.add_argument("--group", type=int, default=32, help="independent batch-1 GEMVs per launch")
     ap.add_argument("--footprint-gb", type=float, default=1.2)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-single", action="store_true", help="skip the one-matrix-per-launch timing")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other workloads (INT4 4096^2, layer sets, decode batches, prefill)")
     ap.add_argument("--profile-workload", default=None, metavar="NAME",
-                    help="only launch the first matrix of workload NAME --steps times (for profiler runs); "
-                         "prints no JSON line")
+                    help="only run --steps rounds over the matrices of workload NAME, rotated over >= 1.2 GB "
+                         "of copies, eagerly (for profiler runs); prints no JSON line")
+    ap.add_argument("--profile-plan", choices=("single", "group"), default="single",
+                    help="one launch per matrix, or all matrices in one grouped launch")
+    ap.add_argument("--profile-m", type=int, default=None, help="batch (activation rows) instead of the workload's")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (the reference kernel for HBM counters)")
     return ap.parse_args()
 
 
-SOURCES = ["dequant_gemv_q4g32_amd/csrc/gemv.hip", "dequant_gemv_q4g32_amd/csrc/units.h",
-           "dequant_gemv_q4g32_amd/csrc/device_common.h", "dequant_gemv_q4g32_amd/csrc/layout.h"]
+SOURCES = ["dequant_gemv_q4g32_amd/csrc/gemv.hip", "dequant_gemv_q4g32_amd/csrc/mv.h",
+           "dequant_gemv_q4g32_amd/csrc/units.h", "dequant_gemv_q4g32_amd/csrc/device_common.h",
+           "dequant_gemv_q4g32_amd/csrc/layout.h"]
 
 
 def kernel_source_hash():
@@ -98,9 +104,26 @@ def measured_traffic(workload):
     return fetch + write
 
 
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(fmt, canonical, n, k, x, seconds):
-    """The oracle as it stands (NumPy decode + fp64 matvec), single-threaded, on a bounded
-    sample of rows of the same matrix; returns GB/s of packed weights processed."""
+    """The oracle as it stands (NumPy decode + fp64 matvec) on a bounded sample of rows of the
+    same matrix, timed twice: on one thread, and on one thread per available core (at most 16)
+    with each thread taking 64-row chunks in turn (NumPy releases the interpreter lock inside
+    its array operations; BLAS is held to one thread per caller). Returns GB/s of packed
+    weights processed; `value` is the all-core figure."""
+    import threading
+
     import numpy as np
     from threadpoolctl import threadpool_limits
 
@@ -109,61 +132,100 @@ def cpu_baseline(fmt, canonical, n, k, x, seconds):
     from oracle import superblock as sb
 
     chunk = 64
-    done = 0
-    with threadpool_limits(1):
-        t0 = time.perf_counter()
-        while time.perf_counter() - t0 < seconds:
-            r0 = done % n
-            r1 = min(n, r0 + chunk)
-            if fmt == "q4g32":
-                codes = canonical[: n * k // 2].reshape(n, k // 2)[r0:r1]
-                scales = canonical[n * k // 2:].view(np.float32).reshape(n, k // 32)[r0:r1]
-                w_hat = int4.decode(codes, scales, k)
-            else:
-                rec = canonical.reshape(n, k // 256, -1)[r0:r1]
-                w_hat = sb.decode(fmt, rec)
-            ogemv.gemv(w_hat, x)
-            done += r1 - r0
-        dt = time.perf_counter() - t0
     row_bytes = canonical.size // n
-    return {"value": round(done * row_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": f"{done} rows ({done / n:.2f} passes) of the {n}x{k} {fmt} matrix: NumPy decode of the "
-                      f"canonical encoding + fp64 matvec, one thread, {dt:.1f} s"}
+
+    def rows(r0, r1):
+        if fmt == "q4g32":
+            codes = canonical[: n * k // 2].reshape(n, k // 2)[r0:r1]
+            scales = canonical[n * k // 2:].view(np.float32).reshape(n, k // 32)[r0:r1]
+            w_hat = int4.decode(codes, scales, k)
+        else:
+            w_hat = sb.decode(fmt, canonical.reshape(n, k // 256, -1)[r0:r1])
+        ogemv.gemv(w_hat, x)
+
+    def run(threads):
+        lock = threading.Lock()
+        state = {"next": 0, "done": 0}
+        t0 = time.perf_counter()
+
+        def worker():
+            while time.perf_counter() - t0 < seconds:
+                with lock:
+                    r0 = state["next"] % n
+                    state["next"] = r0 + chunk
+                r1 = min(n, r0 + chunk)
+                rows(r0, r1)
+                with lock:
+                    state["done"] += r1 - r0
+
+        ts = [threading.Thread(target=worker) for _ in range(threads)]
+        for t in ts:
+            t.start()
+        for t in ts:
+            t.join()
+        dt = time.perf_counter() - t0
+        return state["done"], dt
+
+    affinity = len(os.sched_getaffinity(0))
+    threads = max(1, min(16, affinity))
+    with threadpool_limits(1):
+        done1, dt1 = run(1)
+        done, dt = run(threads)
+    one = round(done1 * row_bytes / dt1 / 1e9, 4)
+    return {"value": round(done * row_bytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "one_thread_value": one, "cpu_model": _cpu_model(), "sched_getaffinity_cpus": affinity,
+            "sample": f"{done} rows ({done / n:.2f} passes) of the {n}x{k} {fmt} matrix on {threads} threads in "
+                      f"{dt:.1f} s, and {done1} rows on one thread in {dt1:.1f} s: NumPy decode of the canonical "
+                      f"encoding + fp64 matvec"}
 
 
 MFMA_F16_PEAK_TFLOPS = 2500.0
 
 
+WARM_S = 0.15     # sustained load before a timed replay: the clocks drop within a second of idle
+
+
+def _warm(replay, seconds=WARM_S):
+    """Run replay() back to back for `seconds`: after the idle of host-side set-up the GPU
+    clocks take tens of milliseconds of load to ramp (a 512-row prefill launch measures 93 us
+    right after a second of idle and 80 us after 50 ms of load)."""
+    import torch
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds:
+        replay()
+        torch.cuda.synchronize()
+
+
 def _graph_time_us(fn, rounds, reps=3):
-    """Median over reps of the per-round time of `rounds` calls of fn(i), captured in one graph."""
+    """Median over reps of the per-round time of `rounds` calls of fn(i), captured in one graph
+    and replayed after WARM_S seconds of back-to-back replays."""
     import torch
     fn(0)
     torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for i in range(rounds):
+            fn(i)
+    _warm(g.replay)
     times = []
     for _ in range(reps):
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(rounds):
-                fn(i)
-        g.replay()
-        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         g.replay()
         e1.record()
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1) * 1e3 / rounds)
-        del g
+    del g
     return sorted(times)[len(times) // 2]
 
 
-def measure_set(qg, fmt, canon_shapes, m, dev, plan, footprint_gb=1.2, rounds=24):
-    """One pass over a set of matrices (batch m), with the weights rotated over enough copies
-    that every round reads them from HBM. `plan` lists the launches of a round: ("group",
-    [i, ...]) is one grouped launch of those matrices (any shapes), ("batched", [i, ...]) one
-    strided batched launch of consecutive same-shape matrices (m = 1), ("single", [i]) one
-    qg_gemm (qg_gemv at m = 1), ("act_order", [i]) one qg_gemm_act_order with a random column
-    permutation. Returns (algorithmic bytes per round, microseconds per round)."""
+def build_set(qg, fmt, canon_shapes, m, dev, plan, footprint_gb=1.2):
+    """Device buffers for passes over a set of matrices (batch m), with the weights rotated over
+    enough copies that every round reads them from HBM. `plan` lists the launches of a round:
+    ("group", [i, ...]) is one grouped launch of those matrices (any shapes), ("batched",
+    [i, ...]) one strided batched launch of consecutive same-shape matrices (m = 1), ("single",
+    [i]) one qg_gemm (qg_gemv at m = 1), ("act_order", [i]) one qg_gemm_act_order with a random
+    column permutation. Returns (algorithmic bytes per round, rnd) where rnd(r) issues round r."""
     import numpy as np
     import torch
     from workloads import activations
@@ -214,8 +276,15 @@ def measure_set(qg, fmt, canon_shapes, m, dev, plan, footprint_gb=1.2, rounds=24
                 else:
                     qg.gemm(fmt, buf[base + int(offs[i]):], X[0], n, k, out=Y[0])
 
+    return alg, rnd
+
+
+def measure_set(qg, fmt, canon_shapes, m, dev, plan, footprint_gb=1.2, rounds=24):
+    """build_set, then the graph-timed microseconds per round: (algorithmic bytes, us)."""
+    import torch
+    alg, rnd = build_set(qg, fmt, canon_shapes, m, dev, plan, footprint_gb)
     us = _graph_time_us(rnd, rounds)
-    del buf
+    del rnd
     torch.cuda.empty_cache()
     return alg, us
 
@@ -226,8 +295,8 @@ def _rate(alg, us):
 
 def extra_configs(qg, dev):
     """The other workloads on this one GPU: INT4 group-32 4096^2 at batch 1, the 7B-like layer
-    set (q/k/v/o, gate/up, down) per super-block format, the 70B-like set at batch 1, 2, 4
-    and 8, and the 512-row prefill GEMM."""
+    set (q/k/v/o, gate/up, down) per super-block format, the 70B-like set at batch 1, 2, 4, 8
+    and 16, and the 512-row prefill GEMM (with 2048 rows as context)."""
     from workloads import WORKLOADS
     out = {}
     # INT4 group-32 4096 x 4096, batch 1: 32 per launch like the headline, and one per launch
@@ -275,19 +344,20 @@ def extra_configs(qg, dev):
                                       "decode_order": _rate(alg2, us2)}
         log(f"[bench] {fmt} 7B layer set: {out[f'{fmt}_7b_layer_set']}")
     del w7
-    # 70B-like layer set at batch 1, 2, 4, 8 (q3sb and q5sb share the fp32 weights): one launch
+    # 70B-like layer set at batch 1, 2, 4, 8, 16 (q3sb and q5sb share the fp32 weights): one launch
     # per matrix (the matrices depend on each other in a decode step), and all three in one
-    # grouped launch
+    # grouped launch (up to batch 8)
     wl = WORKLOADS["q3sb_70b_layer_set_m1"]
     w70 = [wl.weights(i) for i in range(len(wl.shapes))]
     for fmt in ("q3sb", "q5sb"):
         cs = [(qg.quantize(fmt, w), w.shape[0], w.shape[1]) for w in w70]
-        for m in (1, 2, 4, 8):
+        for m in (1, 2, 4, 8, 16):
             alg, us = measure_set(qg, fmt, cs, m, dev, [("single", [0]), ("single", [1]), ("single", [2])], rounds=12)
-            alg2, us2 = measure_set(qg, fmt, cs, m, dev, [("group", [0, 1, 2])], rounds=12)
             flops = 2 * m * sum(n * k for _, n, k in cs)
-            out[f"{fmt}_70b_layer_set_m{m}"] = {**_rate(alg, us), "TFLOPs": round(flops / us / 1e6, 2),
-                                                "one_launch": _rate(alg2, us2)}
+            out[f"{fmt}_70b_layer_set_m{m}"] = {**_rate(alg, us), "TFLOPs": round(flops / us / 1e6, 2)}
+            if m <= 8:      # grouped launches take up to 8 activation rows
+                alg2, us2 = measure_set(qg, fmt, cs, m, dev, [("group", [0, 1, 2])], rounds=12)
+                out[f"{fmt}_70b_layer_set_m{m}"]["one_launch"] = _rate(alg2, us2)
             log(f"[bench] {fmt} 70B layer set m={m}: {out[f'{fmt}_70b_layer_set_m{m}']}")
         del cs
     del w70
@@ -333,16 +403,19 @@ def extra_configs(qg, dev):
     log(f"[bench] KV cache int8 codec: {out['kv_cache_int8_7b_8192']}")
     del x, codes, scales
     torch.cuda.empty_cache()
-    # prefill: 512 x 4096 activations times 11008 x 4096 weights (MFMA bound)
+    # prefill: 512 x 4096 activations times 11008 x 4096 weights (MFMA bound), and 2048 rows
+    # of activations as context
     for fmt in ("q4g32", "q5sb"):
         wl = WORKLOADS[f"{fmt}_prefill_512"]
         n, k = wl.shapes[0]
         canon = qg.quantize(fmt, wl.weights(0))
-        alg, us = measure_set(qg, fmt, [(canon, n, k)], 512, dev, [("single", [0])], rounds=10)
-        tf = 2 * 512 * n * k / us / 1e6
-        out[f"{fmt}_prefill_512"] = {"TFLOPs": round(tf, 1), "mfma_frac_of_fp16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
-                                     "us": round(us, 2), "weight_GBps": round(alg / us / 1e3, 1)}
-        log(f"[bench] {fmt} prefill 512: {out[f'{fmt}_prefill_512']}")
+        for m in (512, 2048):
+            alg, us = measure_set(qg, fmt, [(canon, n, k)], m, dev, [("single", [0])], rounds=10)
+            tf = 2 * m * n * k / us / 1e6
+            key = f"{fmt}_prefill_512" if m == 512 else f"{fmt}_prefill_{m}_context"
+            out[key] = {"TFLOPs": round(tf, 1), "mfma_frac_of_fp16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                        "us": round(us, 2), "weight_GBps": round(alg / us / 1e3, 1)}
+            log(f"[bench] {fmt} prefill {m}: {out[key]}")
     return out
 
 
@@ -363,16 +436,23 @@ def main():
 
     if args.profile_workload:
         wl = WORKLOADS[args.profile_workload]
-        n, k = wl.shapes[0]
-        wd = torch.from_numpy(qg.to_device_layout(wl.fmt, qg.quantize(wl.fmt, wl.weights(0)), n, k)).to("cuda:0")
-        X = torch.from_numpy(wl.x(0)).to("cuda:0")
-        for _ in range(args.steps):
-            if wl.m == 1:
-                qg.gemv(wl.fmt, wd, X[0], n, k)
-            else:
-                qg.gemm(wl.fmt, wd, X, n, k)
+        m = args.profile_m or wl.m
+        cs = [(qg.quantize(wl.fmt, wl.weights(i)), n, k) for i, (n, k) in enumerate(wl.shapes)]
+        idx = list(range(len(cs)))
+        plan = [("group", idx)] if args.profile_plan == "group" else [("single", [i]) for i in idx]
+        alg, rnd = build_set(qg, wl.fmt, cs, m, torch.device("cuda:0"), plan, args.footprint_gb)
+        state = {"r": 0}
+
+        def one():
+            rnd(state["r"])
+            state["r"] += 1
+        _warm(one)          # rounds before the last --steps: clock ramp, not measured
+        warm_rounds = state["r"]
+        for r in range(args.steps):
+            one()
         torch.cuda.synchronize()
-        log(f"[bench] profiled {args.profile_workload}: {args.steps} launches of {wl.fmt} {wl.m}x{n}x{k}")
+        log(f"[bench] profiled {args.profile_workload}: {args.steps} rounds of {len(plan)} launches after "
+            f"{warm_rounds} warm-up rounds, {wl.fmt} m={m}, shapes {list(wl.shapes)}, {alg} algorithmic bytes per round")
         return
 
     wl = WORKLOADS[args.workload]
@@ -405,7 +485,8 @@ def main():
 
     # The K timed steps are captured in one HIP graph (so that host launch overhead cannot
     # leave the GPU idle between 50 us steps). After the W warmup steps the graph is replayed
-    # once untimed (its first replay uploads it), then timed between two synchronizes.
+    # once untimed (its first replay uploads it) and back to back for WARM_S seconds, then
+    # timed between two synchronizes.
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -415,6 +496,7 @@ def main():
             step(args.warmup + i)
     graph.replay()
     torch.cuda.synchronize()
+    _warm(graph.replay)
     ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     ev0.record()
     graph.replay()
@@ -448,21 +530,18 @@ def main():
     single = None
     if not args.no_single:
         iters = 400
-        for i in range(20):
-            qg.gemv(fmt, buf[(i % copies) * stride:], xs[i % copies], n, k, out=ys[i % copies])
-        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(iters):
+                qg.gemv(fmt, buf[(i % copies) * stride:], xs[i % copies], n, k, out=ys[i % copies])
+        _warm(g.replay)
         ev0.record()
         for i in range(iters):
             qg.gemv(fmt, buf[(i % copies) * stride:], xs[i % copies], n, k, out=ys[i % copies])
         ev1.record()
         torch.cuda.synchronize()
         us_stream = ev0.elapsed_time(ev1) / iters * 1e3
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(iters):
-                qg.gemv(fmt, buf[(i % copies) * stride:], xs[i % copies], n, k, out=ys[i % copies])
-        g.replay()
-        torch.cuda.synchronize()
+        _warm(g.replay, 0.05)
         ev0.record()
         g.replay()
         ev1.record()
@@ -493,6 +572,17 @@ def main():
         log(f"[bench] oracle: {cpu['value']} GB/s ({cpu['sample']})")
 
     traffic = measured_traffic(args.workload)
+    # one matrix per launch at batch 1 (the headline packs 32 independent GEMVs into a launch),
+    # and the 7B-like layer set in the launches a decode step's dependencies allow
+    per_matrix = {f"{args.workload}": single}
+    decode_order = None
+    if extra:
+        q4 = extra["q4g32_gemv_4096"]
+        per_matrix["q4g32_gemv_4096"] = {"us_per_gemv_graph": q4["us_single_launch"], "GBps_graph": q4["GBps_single_launch"]}
+        decode_order = {f: extra[f"{f}_7b_layer_set"]["decode_order"]["frac"] for f in ("q2sb", "q3sb", "q5sb", "q6sb")}
+    for v in per_matrix.values():
+        if v:
+            v["frac_graph"] = round(v["GBps_graph"] / HBM_PEAK_GBPS, 4)
     out = {
         "metric": METRIC, "value": round(gbps, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
@@ -502,6 +592,9 @@ def main():
                    "algorithmic_bytes_per_matrix": alg, "resident_GB": round(copies * stride / 1e9, 3)},
         "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": traffic},
+        "headline_kind": f"multi-matrix throughput: {G} independent batch-1 GEMVs per launch",
+        "batch1_one_matrix_per_launch": per_matrix,
+        "layer_set_7b_decode_order_frac": decode_order,
         "algorithmic_bytes_per_launch": G * alg,
         "read_ceiling_GBps": round(ceiling, 1),
         "frac_of_read_ceiling": round(gbps / ceiling, 4),

@@ -22,8 +22,8 @@
 //   * all four waves run the current step's MFMAs (4 K-slices of 16).
 // Both tiles are double-buffered in four distinct LDS arrays, so that the compiler can see
 // that the loads into one buffer do not alias the reads of the other, and one barrier per
-// step separates them. Rows are stored with their 16-byte chunks XOR-swizzled by the row's
-// low 3 bits, so that the 32 rows an MFMA operand read touches fall on different banks.
+// step separates them. Rows are stored with their 16-byte chunks XOR-swizzled (swz below), so
+// that the rows an MFMA operand read touches fall on different banks.
 // Workgroups are numbered so that each XCD works through the tiles of one M tile, whose
 // activation rows then stay in its L2.
 #include <hip/hip_runtime.h>
@@ -58,8 +58,12 @@ constexpr int kMaxBM = 256;                   // activation rows per workgroup t
 constexpr int kRowBytes = kUnit * 2;          // one K step of one row in fp16: 128 bytes
 constexpr uint32_t kXRange = 0x7FFFFFF0u;    // activation buffer range; offsets at or past it read 0
 
-// byte offset of 16-byte chunk c of row r in a swizzled tile
-__device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t c) { return r * kRowBytes + 16u * (c ^ (r & 7u)); }
+// Byte offset of 16-byte chunk c of row r in a swizzled tile: the chunk goes to position
+// c ^ f(r) of its row, f(r) = (r ^ (r >> 3)) & 7. A 128-bit LDS read serves 16 lanes per
+// cycle (256 bytes, 64 banks): an MFMA operand read has those lanes on 16 consecutive rows
+// at one chunk, and f is one-to-one on the even and on the odd rows of any 16 aligned rows
+// (and on any 8 aligned rows), so those reads hit 16 distinct 16-byte bank groups.
+__device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t c) { return r * kRowBytes + 16u * (c ^ ((r ^ (r >> 3)) & 7u)); }
 
 template <int F, int BM, int BN>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
@@ -131,19 +135,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  // ---- activations (waves 2, 3): instruction i of x-wave xw fills tile rows 8 (NX xw + i) ..
-  // + 7 (1 KB); lane l loads row + (l >> 3), chunk (l & 7) ^ (l >> 3) of the step's 128 bytes,
-  // which lands at LDS position l & 7 of that row: the swizzled layout. A dead row, or the
-  // missing half of a ragged q4g32 unit, gets an offset past the range and reads zeros.
+  // ---- activations (waves 2, 3): instruction i of x-wave xw fills tile rows 8 R .. 8 R + 7,
+  // R = NX xw + i (1 KB, written in lane order); lane l loads row 8 R + (l >> 3), chunk
+  // (l & 7) ^ f(row) of the step's 128 bytes, which lands at LDS position l & 7 of that row:
+  // the swizzled layout (f(8 R + j) = (j ^ R) & 7). A dead row, or the missing half of a ragged
+  // q4g32 unit, gets an offset past the range and reads zeros.
   const int xw = wave & 1;
-  const int xrow_l = lane >> 3, xc = (lane & 7) ^ (lane >> 3);
+  const int xrow_l = lane >> 3;
   const rsrc_t xr = make_rsrc(a.x + m0 * a.ldx, kXRange);
   auto xdma = [&](int64_t u, uint8_t *X) {
     u = u < a.units ? u : a.units - 1;
-    const int64_t kk = u * kUnit + 8 * xc;
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
       const int row = 8 * (NX * xw + i) + xrow_l;
+      const int xc = (lane & 7) ^ ((xrow_l ^ (NX * xw + i)) & 7);
+      const int64_t kk = u * kUnit + 8 * xc;
       const bool ok = m0 + row < a.m && kk < a.k;
       const uint32_t voff = ok ? (uint32_t)(row * a.ldx * 2 + kk * 2) : kXRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t *)(X + (NX * xw + i) * 1024), 16, voff, 0, 0, 0);
