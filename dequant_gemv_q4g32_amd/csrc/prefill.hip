@@ -143,16 +143,43 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int xw = wave & 1;
   const int xrow_l = lane >> 3;
   const rsrc_t xr = make_rsrc(a.x + m0 * a.ldx, kXRange);
-  auto xdma = [&](int64_t u, uint8_t *X) {
-    u = u < a.units ? u : a.units - 1;
+  // 256-row tiles: each instruction's lane offset is fixed (row and chunk) and the step adds
+  // u * 128 bytes as the scalar offset; xcs marks the lanes whose chunk is in the second half
+  // of a unit, which a ragged q4g32 K (k % 64 == 32) leaves past k in the last unit. 128-row
+  // tiles compute each offset per step instead. (Measured in one session: the fixed offsets
+  // took 4-7% off the 256 x 64 launches and added 7-9% to the q3sb and q5sb 128 x 32 ones.)
+  uint32_t xoff[NX];
+  uint32_t xcs = 0;
+  if constexpr (BM == 256) {
 #pragma unroll
     for (int i = 0; i < NX; ++i) {
       const int row = 8 * (NX * xw + i) + xrow_l;
       const int xc = (lane & 7) ^ ((xrow_l ^ (NX * xw + i)) & 7);
-      const int64_t kk = u * kUnit + 8 * xc;
-      const bool ok = m0 + row < a.m && kk < a.k;
-      const uint32_t voff = ok ? (uint32_t)(row * a.ldx * 2 + kk * 2) : kXRange;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t *)(X + (NX * xw + i) * 1024), 16, voff, 0, 0, 0);
+      xoff[i] = m0 + row < a.m ? (uint32_t)(row * a.ldx * 2 + 16 * xc) : kXRange;
+      xcs |= (xc >= 4 ? 1u : 0u) << i;
+    }
+  }
+  const bool ragged = (F == 4) && (a.k % 64 != 0);
+  auto xdma = [&](int64_t u, uint8_t *X) {
+    u = u < a.units ? u : a.units - 1;
+    if constexpr (BM == 256) {
+      const uint32_t so = (uint32_t)(u * kRowBytes);
+      const bool cut = ragged && u == a.units - 1;
+#pragma unroll
+      for (int i = 0; i < NX; ++i) {
+        const uint32_t voff = cut && ((xcs >> i) & 1u) ? kXRange : xoff[i];
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t *)(X + (NX * xw + i) * 1024), 16, voff, so, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < NX; ++i) {
+        const int row = 8 * (NX * xw + i) + xrow_l;
+        const int xc = (lane & 7) ^ ((xrow_l ^ (NX * xw + i)) & 7);
+        const int64_t kk = u * kUnit + 8 * xc;
+        const bool ok = m0 + row < a.m && kk < a.k;
+        const uint32_t voff = ok ? (uint32_t)(row * a.ldx * 2 + kk * 2) : kXRange;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (lds_void_t *)(X + (NX * xw + i) * 1024), 16, voff, 0, 0, 0);
+      }
     }
   };
 

@@ -256,9 +256,16 @@ int qg_gemv_batched(int fmt, const void *w, int64_t w_stride, const uint16_t *x,
  * v_dot2; the kernel of qg_gemv, qg_gemm_grouped and qg_gemm_act_order), 5 <= m <= 16
  * decodes each code once to fp16 and multiplies on the matrix cores in the same single
  * weight stream, and m > 16 (prefill) stages fp16 weight and activation tiles in LDS for
- * 32x32 matrix-core tiles. Limits as dequant_gemv_*; for m > 4 also ldx < 2^23 (32-bit
- * activation offsets within a 128-row tile). m == 0 or n == 0 is a no-op; k == 0 writes
- * zeros. Errors as dequant_gemv_*. */
+ * 32x32 matrix-core tiles. Limits as dequant_gemv_*; also ldx < 2^26 for 5 <= m <= 16 and
+ * ldx < 2^22 for m > 16 (32-bit activation offsets within a 16-row or a 256-row tile).
+ * m == 0 or n == 0 is a no-op; k == 0 writes zeros. Errors as dequant_gemv_*.
+ * Precision: m <= 4 works on the codes in fp32 (the 2e-3 * sum |W_hat x| bound holds at any
+ * weight and activation scale). The matrix-core paths (m > 4) round each decoded weight to
+ * fp16, which keeps 11 significant bits down to 2^-14 only: they hold the bound while the
+ * quantization steps (an INT4 group scale, a super-block's d * sc) are at least 2^-14 and
+ * the weights stay within +-65504; smaller steps lose relative precision (fp16 subnormals)
+ * and weights beyond the fp16 range (the _bf16 formats only) are not representable. Such
+ * layers take m <= 4 launches, or qg_gemm_grouped / qg_gemm_act_order up to 8 rows. */
 int dequant_gemm_q4g32(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,
                        int64_t m, int64_t n, int64_t k, void *stream);
 int dequant_gemm_q2sb(const void *w, const uint16_t *X, int64_t ldx, uint16_t *Y, int64_t ldy,

@@ -194,6 +194,8 @@ def test_device_entry_points_validate_without_launching():
     assert L.qg_gemm(3, 256, 16, 128, 2, 4, 0, 2, 4, 256, None) == -2     # ldx < k
     assert L.qg_gemm(3, 256, 16, 256, 2, 3, 0, 2, 4, 256, None) == -2     # ldy < n
     assert L.qg_gemm(3, 256, 16, 260, 2, 4, 0, 2, 4, 256, None) == -3     # ldx % 8
+    assert L.qg_gemm(3, 256, 16, 1 << 22, 2, 4, 0, 20, 4, 256, None) == -2    # prefill: ldx >= 2^22
+    assert L.qg_gemm(3, 256, 16, 1 << 26, 2, 4, 0, 8, 4, 256, None) == -2     # 5..16 rows: ldx >= 2^26
     assert L.qg_gemm(3, None, 16, 256, 2, 4, 0, 2, 4, 256, None) == -1    # null w
     assert L.qg_gemm(5, 256, 16, 256, 2, 4, 0, 2, 4, 100, None) == -2     # k % 256
     assert L.qg_gemm(19, 256, 16, 256, 2, 4, 0, 2, 4, 256, None) == -6     # format
