@@ -16,14 +16,18 @@ between two synchronizes. A single 7.2 MB matrix per launch is also timed ("sing
 and reported with the INT4 one under "batch1_one_matrix_per_launch": at ~1 us of streaming
 it is bound by launch cadence, not HBM.
 
+Beside the headline: the same steps launched eagerly on the stream ("stream_ms_per_step"),
+the bytes of activations and outputs per launch (not counted in the metric), and the time of
+the host quantizer (C++) for the headline matrix, as context.
+
 "other_workloads" measures the remaining workloads the same way (HBM-resident rotation,
-graph-timed): INT4 group-32 4096^2, the 7B-like layer set per super-block format (all seven
-matrices in one grouped launch, and in the launches a decode step's data dependencies
-allow), the 70B-like layer set at batch 1, 2, 4, 8 and 16 (one launch per matrix, and one
-grouped launch), INT4 with groups of 16, 32, 64 and 128 and act-order INT4 on the 70B-like
-set, the 8-bit KV-cache codec on the
-7B-like cache, and the 512-row prefill GEMM (TFLOP/s and fraction of the 2.5 PFLOP/s dense
-fp16 MFMA peak).
+graph-timed): INT4 group-32 4096^2; the 7B-like layer set per super-block format (all seven
+matrices in one grouped launch, and in the launches a decode step's data dependencies allow;
+rotated over 32 copies, a 32-layer model's decode pass); the 70B-like layer set at batch 1,
+2, 4, 8 and 16 (one launch per matrix, and one grouped launch); INT4 with groups of 16, 32,
+64 and 128, the other format variants and act-order INT4 on the 70B-like set; the 8-bit
+KV-cache codec on the 7B-like cache; and the 512-row prefill GEMM (TFLOP/s and fraction of
+the 2.5 PFLOP/s dense fp16 MFMA peak), with 2048 rows as context.
 
 Prints one JSON line on stdout; progress goes to stderr.
 """
@@ -219,13 +223,14 @@ def _graph_time_us(fn, rounds, reps=3):
     return sorted(times)[len(times) // 2]
 
 
-def build_set(qg, fmt, canon_shapes, m, dev, plan, footprint_gb=1.2):
+def build_set(qg, fmt, canon_shapes, m, dev, plan, footprint_gb=1.2, min_copies=2):
     """Device buffers for passes over a set of matrices (batch m), with the weights rotated over
     enough copies that every round reads them from HBM. `plan` lists the launches of a round:
     ("group", [i, ...]) is one grouped launch of those matrices (any shapes), ("batched",
     [i, ...]) one strided batched launch of consecutive same-shape matrices (m = 1), ("single",
     [i]) one qg_gemm (qg_gemv at m = 1), ("act_order", [i]) one qg_gemm_act_order with a random
-    column permutation. Returns (algorithmic bytes per round, rnd) where rnd(r) issues round r."""
+    column permutation. At least min_copies copies (a model's layer count). Returns (algorithmic
+    bytes per round, rnd) where rnd(r) issues round r."""
     import numpy as np
     import torch
     from workloads import activations
@@ -233,7 +238,7 @@ def build_set(qg, fmt, canon_shapes, m, dev, plan, footprint_gb=1.2):
     strides = [(l.total_bytes + 255) // 256 * 256 for l in lays]
     set_bytes = sum(strides)
     alg = sum(l.algorithmic_bytes for l in lays)
-    copies = max(2, int(np.ceil(footprint_gb * 1e9 / set_bytes)))
+    copies = max(min_copies, int(np.ceil(footprint_gb * 1e9 / set_bytes)))
     buf = torch.empty(copies * set_bytes, dtype=torch.uint8, device=dev)
     offs = np.concatenate([[0], np.cumsum(strides)[:-1]]).astype(np.int64)
     for j, (canon, n, k) in enumerate(canon_shapes):
@@ -279,10 +284,10 @@ def build_set(qg, fmt, canon_shapes, m, dev, plan, footprint_gb=1.2):
     return alg, rnd
 
 
-def measure_set(qg, fmt, canon_shapes, m, dev, plan, footprint_gb=1.2, rounds=24):
+def measure_set(qg, fmt, canon_shapes, m, dev, plan, footprint_gb=1.2, rounds=24, min_copies=2):
     """build_set, then the graph-timed microseconds per round: (algorithmic bytes, us)."""
     import torch
-    alg, rnd = build_set(qg, fmt, canon_shapes, m, dev, plan, footprint_gb)
+    alg, rnd = build_set(qg, fmt, canon_shapes, m, dev, plan, footprint_gb, min_copies)
     us = _graph_time_us(rnd, rounds)
     del rnd
     torch.cuda.empty_cache()
@@ -333,13 +338,15 @@ def extra_configs(qg, dev):
     # 0-3 are q, k, v, o; 4, 5 gate, up; 6 down. "one_launch": all seven in one grouped launch;
     # "decode_order": the launches a decode step can issue given its data dependencies
     # ({q, k, v} share x; o waits for attention; {gate, up} share x; down waits for both).
+    # The weights rotate over 32 copies of the set at least: one round is one layer of a
+    # 32-layer 7B-class model, so 32 rounds are one token's decode pass.
     wl = WORKLOADS["q3sb_7b_layer_set"]
     w7 = [wl.weights(i) for i in range(len(wl.shapes))]
     for fmt in ("q2sb", "q3sb", "q5sb", "q6sb"):
         cs = [(qg.quantize(fmt, w), w.shape[0], w.shape[1]) for w in w7]
-        alg, us = measure_set(qg, fmt, cs, 1, dev, [("group", list(range(7)))])
+        alg, us = measure_set(qg, fmt, cs, 1, dev, [("group", list(range(7)))], rounds=32, min_copies=32)
         alg2, us2 = measure_set(qg, fmt, cs, 1, dev, [("group", [0, 1, 2]), ("single", [3]), ("group", [4, 5]),
-                                                      ("single", [6])])
+                                                      ("single", [6])], rounds=32, min_copies=32)
         out[f"{fmt}_7b_layer_set"] = {**_rate(alg, us), "bytes_per_set": alg,
                                       "decode_order": _rate(alg2, us2)}
         log(f"[bench] {fmt} 7B layer set: {out[f'{fmt}_7b_layer_set']}")
@@ -462,7 +469,15 @@ def main():
     log(f"[bench] {args.workload}: {fmt} {n}x{k}, {args.group} GEMVs per launch")
 
     w = wl.weights(0)
-    canonical = qg.quantize(fmt, w)
+    # the host quantizer (C++, synchronous; offline in a deployment, timed here as context)
+    tq = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        canonical = qg.quantize(fmt, w)
+        tq.append(time.perf_counter() - t0)
+    host_quantize = {"s_per_matrix": round(sorted(tq)[1], 4),
+                     "Mweights_per_s": round(n * k / sorted(tq)[1] / 1e6, 1),
+                     "what": f"qg_quantize of the {n}x{k} fp32 matrix to {fmt} records, one host thread"}
     lay = qg.device_layout(fmt, n, k)
     alg = lay.algorithmic_bytes
     stride = (lay.total_bytes + 255) // 256 * 256
@@ -506,6 +521,15 @@ def main():
     del graph
     gbps = G * alg / (ms * 1e-3) / 1e9
     log(f"[bench] grouped: {ms * 1e3:.2f} us per launch, {gbps:.0f} GB/s")
+    # the same steps launched eagerly, back to back on the stream (host launch overhead can
+    # leave gaps between launches)
+    ns = min(args.steps, 200)
+    ev0.record()
+    for i in range(ns):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    ms_stream = ev0.elapsed_time(ev1) / ns
 
     # check the timed outputs of one set against a single-matrix launch (same kernels)
     ref = qg.gemv(fmt, one, xs[0], n, k)
@@ -596,6 +620,10 @@ def main():
         "batch1_one_matrix_per_launch": per_matrix,
         "layer_set_7b_decode_order_frac": decode_order,
         "algorithmic_bytes_per_launch": G * alg,
+        "activation_and_output_bytes_per_launch": G * (k + n) * 2,
+        "stream_ms_per_step": round(ms_stream, 5),
+        "stream_GBps": round(G * alg / (ms_stream * 1e-3) / 1e9, 1),
+        "host_quantize": host_quantize,
         "read_ceiling_GBps": round(ceiling, 1),
         "frac_of_read_ceiling": round(gbps / ceiling, 4),
         "single_launch": single,
