@@ -125,7 +125,11 @@ __global__ __launch_bounds__(64 * kSkinnyMaxWk) void skinny_kernel(SkinnyArgs a)
 #pragma unroll
       for (int p = 0; p < 4; ++p) Ld.off[p] += (uint32_t)row * Ld.prb[p];
       const bool half = (F == 4) && (unit == a.units - 1) && (a.k % 64 != 0);
-      U::load(q[d], Ld, 0, half);
+      // default cache policy: a load reads 64 bytes of each of its 16 rows, and the other half
+      // of those 128-byte lines belongs to the next wave's units in the same pass; with the
+      // non-temporal hint the lines were often gone by then (HBM fetch 1.25 x the weight bytes
+      // on 28672 x 8192, and 3-10% slower)
+      U::template load<0>(q[d], Ld, 0, half);
     }
   };
   auto finish = [&](const Raw *q, int kp, int j) {
