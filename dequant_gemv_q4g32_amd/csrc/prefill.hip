@@ -8,17 +8,19 @@
 // once per K step into an LDS tile that every wave of the workgroup reads.
 //
 // Tiling: a workgroup of 4 waves computes a BM x BN tile of Y and walks K in steps of one
-// 64-weight unit. Two shapes:
+// 64-weight unit. Three shapes:
 //   * 256 x 64 (each wave a 64 x 64 block of 2 x 2 MFMA tiles): each weight is decoded once
 //     per 256 activation rows, and the 32 KB of activations a step brings in feed 2 MFLOP;
+//   * 256 x 96 (each wave 64 x 96) where 256 x 64 tiles come to just over one per CU;
 //   * 128 x 32 (each wave one 32 x 32 MFMA tile) where 256 x 64 tiles would leave CUs without
 //     a workgroup (512 x 4096 has 128 of them, 128 x 11008 has 172): four times the tiles.
 // Roles per step:
-//   * waves 2 and 3 stream the next step's activation tile (BM rows x 128 bytes) straight
-//     into LDS with buffer_load ... lds (no registers, no LDS store instructions);
-//   * the first 2 BN threads (waves 0 and 1, or wave 0) load the weights two steps ahead
-//     (thread t: half t & 1 of the unit of weight row t >> 1) and decode the next step's to
-//     fp16 into the LDS weight tile;
+//   * the last waves (2 and 3; wave 3 alone for 96 columns) stream the next step's activation
+//     tile (BM rows x 128 bytes) straight into LDS with buffer_load ... lds (no registers, no
+//     LDS store instructions);
+//   * the first 2 BN threads (waves 0 and 1, waves 0-2, or wave 0) load the weights two steps
+//     ahead (thread t: half t & 1 of the unit of weight row t >> 1) and decode the next
+//     step's to fp16 into the LDS weight tile;
 //   * all four waves run the current step's MFMAs (4 K-slices of 16).
 // Both tiles are double-buffered in four distinct LDS arrays, so that the compiler can see
 // that the loads into one buffer do not alias the reads of the other, and one barrier per
@@ -69,10 +71,11 @@ template <int F, int BM, int BN>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   using U = Unit<F>;
   using Raw = typename U::Raw;
-  static_assert((BM == 256 && BN == 64) || (BM == 128 && BN == 32), "tile shape");
+  static_assert((BM == 256 && (BN == 64 || BN == 96)) || (BM == 128 && BN == 32), "tile shape");
   constexpr int TM = BM / 128;                  // 32-row MFMA tiles per wave (rows BM / 4)
   constexpr int WN = BN / 32;                   // 32-column MFMA tiles per wave
-  constexpr int NX = BM / 16;                   // 1 KB activation DMA instructions per x-wave
+  constexpr int XW0 = BN == 96 ? 3 : 2;         // first x-wave: 2 BN threads decode weights
+  constexpr int NX = BM / 8 / (4 - XW0);        // 1 KB activation DMA instructions per x-wave
   __shared__ __attribute__((aligned(16))) uint8_t X0[BM * kRowBytes], X1[BM * kRowBytes];
   __shared__ __attribute__((aligned(16))) uint8_t W0[BN * kRowBytes], W1[BN * kRowBytes];
 
@@ -92,11 +95,11 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int t = threadIdx.x;
   const int lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const bool xwave = wave >= 2;                 // wave-uniform role
+  const bool xwave = wave >= XW0;               // wave-uniform role
 
   // ---- weights (waves 0, 1): thread t < 2 BN decodes half t & 1 of weight row t >> 1
   const bool wload = t < 2 * BN;                // wave-uniform
-  const int lrow = (t & 127) >> 1, h = t & 1;
+  const int lrow = (t >> 1) < BN ? t >> 1 : 0, h = t & 1;
   const int64_t wrow = r0 + lrow < a.n ? r0 + lrow : a.n - 1;   // rows past n are not stored
   Lane L;
 #pragma unroll
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   // (l & 7) ^ f(row) of the step's 128 bytes, which lands at LDS position l & 7 of that row:
   // the swizzled layout (f(8 R + j) = (j ^ R) & 7). A dead row, or the missing half of a ragged
   // q4g32 unit, gets an offset past the range and reads zeros.
-  const int xw = wave & 1;
+  const int xw = wave - XW0 < 0 ? 0 : wave - XW0;
   const int xrow_l = lane >> 3;
   const rsrc_t xr = make_rsrc(a.x + m0 * a.ldx, kXRange);
   // 256-row tiles: each instruction's lane offset is fixed (row and chunk) and the step adds
@@ -278,11 +281,15 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
 }
 
 // Tile shape for m x n: 256 x 64 when that gives every CU a workgroup; else 128 x 32, four
-// times the tiles (each K step of a tile is then short, and more of them run at once).
+// times the tiles (each K step of a tile is then short, and more of them run at once). Where
+// 256 x 64 tiles come to just over one per CU (257 to 384) and 256 x 96 tiles fit in one round,
+// the wider tiles: 512 x 11008 has 344 of the first (88 CUs run two) and 230 of the second
+// (measured 2-8% faster; everywhere else the 96-row tiles were slower).
 void prefill_tile(int64_t m, int64_t n, int *bm, int *bn) {
-  const bool big = (m + 255) / 256 * ((n + 63) / 64) >= 256;
+  const int64_t mt = (m + 255) / 256, t64 = mt * ((n + 63) / 64), t96 = mt * ((n + 95) / 96);
+  const bool big = t64 >= 256;
   *bm = big ? 256 : 128;
-  *bn = big ? 64 : 32;
+  *bn = !big ? 32 : (t64 <= 384 && t96 <= 256 ? 96 : 64);
 }
 
 int launch_prefill(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int64_t ldy, int y_f32,
@@ -316,10 +323,11 @@ int launch_prefill(int fmt, const void *w, const uint16_t *X, int64_t ldx, void 
   a.ntiles = (int)ntiles;
   a.per_xcd = (int)((total + 7) / 8);
   const dim3 grid((unsigned)(8 * a.per_xcd)), block(256);
-  auto go = [&](auto big, auto small) {
-    return BM == 256 ? launch(big, grid, block, 0, s, a) : launch(small, grid, block, 0, s, a);
+  auto go = [&](auto big, auto small, auto wide) {
+    if (BM == 128) return launch(small, grid, block, 0, s, a);
+    return BN == 96 ? launch(wide, grid, block, 0, s, a) : launch(big, grid, block, 0, s, a);
   };
-#define QG_PF(F) go(prefill_kernel<F, 256, 64>, prefill_kernel<F, 128, 32>)
+#define QG_PF(F) go(prefill_kernel<F, 256, 64>, prefill_kernel<F, 128, 32>, prefill_kernel<F, 256, 96>)
   switch (fmt) {
     case 2: return QG_PF(2);
     case 3: return QG_PF(3);
