@@ -77,18 +77,18 @@ __global__ __launch_bounds__(kKvThreads) void kv_quant_kernel(const uint16_t *sr
   uint32_t packed[2] = {0u, 0u};
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    // q0 = rint(x * inv) is within one of rint(x / d) (|x / d| <= 127, inv within an ulp).
-    // The remainder e = x - q0 d is exact in fp32: x and d are fp16, |q0| <= 127, and for
-    // q0 != 0 |x| >= d / 2, so e is a multiple of half of d's last-place unit and below
-    // 1.5 d (13 bits). Comparing 2e with +-d then moves q0 to the exact quotient's nearest
-    // integer, ties (2e == +-d) to the even one.
+    // x = a 2^i and d = b 2^k with a, b integers below 2^11 (fp16), so x / d is either a
+    // half-integer or at least 1 / (2 b) >= 2^-12 away from every one, which is 1.9e-6 of the
+    // largest quotient, 127.5. x * inv (inv = 1 / d rounded once) is within 2^-23 of x / d
+    // relative, so q0 = rint(x * inv) is already the nearest integer except at an exact tie,
+    // where it may be the odd neighbour. The remainder e = x - q0 d is exact in fp32 (x and d
+    // are fp16, |q0| <= 127, and for q0 != 0 |x| >= d / 2, so e is a multiple of half of d's
+    // last-place unit below 1.5 d: 13 bits); a tie is 2e = +-d, and then the even code is
+    // q0 + sign(e). |x| <= 127 d keeps q within [-127, 127]. (d = 0: inv = 0, q = 0, e = 0.)
     float q = __builtin_rintf(f[j] * inv);
     const float e2 = 2.0f * __builtin_fmaf(-q, d, f[j]);
-    const bool odd = ((int32_t)q & 1) != 0;
-    const bool up = e2 > d || (e2 == d && odd);
-    const bool dn = e2 < -d || (e2 == -d && odd);
-    q += up ? 1.0f : (dn ? -1.0f : 0.0f);
-    q = fminf(fmaxf(q, -127.f), 127.f);
+    const bool fix = __builtin_fabsf(e2) == d && ((int32_t)q & 1) != 0;
+    q += fix ? __builtin_copysignf(1.0f, e2) : 0.0f;
     packed[j >> 2] |= ((uint32_t)(int32_t)q & 0xFFu) << (8 * (j & 3));
   }
   if (!live) return;
