@@ -381,7 +381,7 @@ int qg_dequantize(int fmt, const void *w, float *w_out, uint8_t *codes_out, int6
  * Streams `bytes` bytes (a multiple of 16; buf 16-byte aligned) through non-temporal 128-bit
  * loads (a grid-stride loop, four loads in flight per thread) and writes nothing except, with
  * negligible probability, one word of `sink`: the achievable HBM
- * read rate against which the GEMV kernels are judged (the DBHOO-CIM page, section 5.3,
+ * read rate the GEMV kernels are measured against (the DBHOO-CIM page, section 5.3,
  * measures the machine's ceiling with STREAM first). */
 int qg_read_probe(const void *buf, int64_t bytes, uint32_t *sink, void *stream);
 
