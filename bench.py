@@ -423,6 +423,31 @@ def extra_configs(qg, dev):
             out[key] = {"TFLOPs": round(tf, 1), "mfma_frac_of_fp16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
                         "us": round(us, 2), "weight_GBps": round(alg / us / 1e3, 1)}
             log(f"[bench] {fmt} prefill {m}: {out[key]}")
+    # context only: the same 512 x 4096 x 11008 product with dense fp16 weights through torch's
+    # GEMM (the vendor library; timed eagerly after the clocks ramp, library GEMMs stay out of
+    # graphs), the work the low-bit formats add a decode to
+    import torch
+    n, k = WORKLOADS["q4g32_prefill_512"].shapes[0]
+    xa = torch.randn((512, k), dtype=torch.float16, device=dev)
+    wts = [torch.randn((k, n), dtype=torch.float16, device=dev) for _ in range(8)]   # 8 x 90 MB, past the LLC
+    ya = torch.empty((512, n), dtype=torch.float16, device=dev)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < WARM_S:
+        torch.matmul(xa, wts[0], out=ya)
+        torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(40):
+        torch.matmul(xa, wts[i % 8], out=ya)
+    e1.record()
+    torch.cuda.synchronize()
+    us_m = e0.elapsed_time(e1) * 1e3 / 40
+    tf = 2 * 512 * n * k / us_m / 1e6
+    out["dense_fp16_prefill_512_context"] = {"TFLOPs": round(tf, 1), "mfma_frac_of_fp16_peak": round(tf / MFMA_F16_PEAK_TFLOPS, 4),
+                                             "us": round(us_m, 2)}
+    log(f"[bench] dense fp16 prefill context: {out['dense_fp16_prefill_512_context']}")
+    del xa, wts, ya
+    torch.cuda.empty_cache()
     return out
 
 
