@@ -351,6 +351,33 @@ def extra_configs(qg, dev):
                                       "decode_order": _rate(alg2, us2)}
         log(f"[bench] {fmt} 7B layer set: {out[f'{fmt}_7b_layer_set']}")
     del w7
+    # context: the read probe alone over the same launch pattern (q3sb byte counts), i.e. the
+    # rate at which launches of these sizes can stream at all: the decode-order rounds (qkv,
+    # o, gate+up, down as 4 probe launches per round) and one 4096^2 matrix per launch
+    import torch
+    lay4, lay11, layd = (qg.device_layout("q3sb", n, k) for n, k in ((4096, 4096), (11008, 4096), (4096, 11008)))
+    sizes = [3 * lay4.algorithmic_bytes, lay4.algorithmic_bytes, 2 * lay11.algorithmic_bytes, layd.algorithmic_bytes]
+    sizes = [(b + 15) // 16 * 16 for b in sizes]
+    span = (sum(sizes) + 255) // 256 * 256
+    copies = int(1.2e9 // span) + 1
+    pbuf = torch.zeros(copies * span, dtype=torch.uint8, device=dev)
+    sink = torch.zeros(1, dtype=torch.int32, device=dev)
+    offs = [0, sizes[0], sizes[0] + sizes[1], sizes[0] + sizes[1] + sizes[2]]
+
+    def probe_round(r):
+        base = (r % copies) * span
+        for o, b in zip(offs, sizes):
+            qg.read_probe(pbuf[base + o:], b, sink)
+    us_p = _graph_time_us(probe_round, 32)
+    one = (lay4.algorithmic_bytes + 255) // 256 * 256
+    n1 = int(1.2e9 // one)
+    us_1 = _graph_time_us(lambda r: qg.read_probe(pbuf[(r % n1) * one:], lay4.algorithmic_bytes // 16 * 16, sink), 200)
+    out["read_probe_launch_patterns_context"] = {
+        "decode_order_7b_q3sb": _rate(sum(sizes), us_p),
+        "one_4096sq_q3sb_matrix": _rate(lay4.algorithmic_bytes, us_1)}
+    log(f"[bench] read probe over the same launch patterns: {out['read_probe_launch_patterns_context']}")
+    del pbuf
+    torch.cuda.empty_cache()
     # 70B-like layer set at batch 1, 2, 4, 8, 16 (q3sb and q5sb share the fp32 weights): one launch
     # per matrix (the matrices depend on each other in a decode step), and all three in one
     # grouped launch (up to batch 8)
