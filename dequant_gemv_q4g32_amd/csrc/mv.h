@@ -47,7 +47,9 @@ struct GemvArgs {
   int kpasses;              // passes over K (wk > 1 whenever kpasses > 1)
   int nb;                   // most row batches (each R rows) of any row group
   int64_t groups;           // row batches per matrix
-  int64_t rgroups;          // row groups per matrix (gridDim.x * wr); they split the batches evenly
+  int64_t rgroups;          // row groups per matrix (gridDim.x * wr); they split the batches evenly:
+  int64_t gq, gr;           // row group g starts at batch g * gq + min(g, gr) (gq = groups / rgroups,
+                            // gr = groups % rgroups), so the first gr groups take one batch more
 };
 
 // ------------------------------------------------------------------ GEMV / small-M kernel -
@@ -108,7 +110,8 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
   // re-read row n-1.
   const int64_t grp = bx * a.wr + wr;
   const bool idle = wr >= a.wr;
-  const int64_t begin = idle ? 0 : grp * a.groups / a.rgroups, end = idle ? 0 : (grp + 1) * a.groups / a.rgroups;
+  auto gbegin = [&](int64_t g) -> int64_t { return g * a.gq + (g < a.gr ? g : a.gr); };
+  const int64_t begin = idle ? 0 : gbegin(grp), end = idle ? 0 : gbegin(grp + 1);
   const int nbh = (int)(end - begin);          // batches of this row group (0 only for tiny n)
   const int rows_max = R * a.nb;               // LDS stride of a row group: a.nb >= every nbh
   auto row_of = [&](int j, int i) -> int64_t { return (begin + j) * R + i; };
@@ -117,8 +120,8 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
   int64_t dyn_begin = 0;
   int dyn_total = 0;
   if constexpr (DYN) {
-    dyn_begin = bx * a.wr * a.groups / a.rgroups;
-    dyn_total = (int)((bx * a.wr + a.wr) * a.groups / a.rgroups - dyn_begin);
+    dyn_begin = gbegin(bx * a.wr);
+    dyn_total = (int)(gbegin(bx * a.wr + a.wr) - dyn_begin);
     if (threadIdx.x == 0) dyn_next = 0;
     __syncthreads();
   }
@@ -407,6 +410,8 @@ inline int64_t split_rows(GemvArgs &a, int R, int64_t nbt) {
   const int64_t blocks = (rg + a.wr - 1) / a.wr;
   a.groups = groups;
   a.rgroups = blocks * a.wr;
+  a.gq = groups / a.rgroups;
+  a.gr = groups % a.rgroups;
   a.nb = (int)((groups + a.rgroups - 1) / a.rgroups);
   return blocks;
 }
