@@ -15,20 +15,25 @@
 //   * 128 x 32 (each wave one 32 x 32 MFMA tile) where 256 x 64 tiles would leave CUs without
 //     a workgroup (512 x 4096 has 128 of them, 128 x 11008 has 172): four times the tiles.
 // Roles per step:
-//   * the last waves (2 and 3; wave 3 alone for 96 columns) stream the next step's activation
+//   * the last waves (2 and 3; wave 3 alone for 96 columns) stream a later step's activation
 //     tile (BM rows x 128 bytes) straight into LDS with buffer_load ... lds (no registers, no
 //     LDS store instructions);
-//   * the first 2 BN threads (waves 0 and 1, waves 0-2, or wave 0) load the weights two steps
-//     ahead (thread t: half t & 1 of the unit of weight row t >> 1) and decode the next
-//     step's to fp16 into the LDS weight tile;
+//   * the first 2 BN threads (waves 0 and 1, waves 0-2, or wave 0; for 32 columns wave 1
+//     loads and decodes too but stores nothing) load a later step's weights (thread t: half
+//     t & 1 of the unit of weight row t >> 1) and decode the next step's to fp16 into the LDS
+//     weight tile;
 //   * all four waves run the current step's MFMAs (4 K-slices of 16).
-// Both tiles are double-buffered in four distinct LDS arrays, so that the compiler can see
-// that the loads into one buffer do not alias the reads of the other, and one barrier per
-// step separates them. Rows are stored with their 16-byte chunks XOR-swizzled (swz below), so
+// P stages of both tiles in distinct LDS arrays (so that the compiler can see that the
+// loads into one buffer do not alias the reads of another) and one barrier per step: the
+// 256 x 64 tiles take two (two workgroups fit on a CU, each hiding the other's waits), the
+// 256 x 96 and 128 x 32 tiles three, so that an activation DMA and a weight load each have
+// two steps to arrive. Rows are stored with their 16-byte chunks XOR-swizzled (swz below), so
 // that the rows an MFMA operand read touches fall on different banks.
 // Workgroups are numbered so that each XCD works through the tiles of one M tile, whose
 // activation rows then stay in its L2.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "../../include/qgemv.h"
 #include "device_common.h"
@@ -67,6 +72,12 @@ constexpr uint32_t kXRange = 0x7FFFFFF0u;    // activation buffer range; offsets
 // (and on any 8 aligned rows), so those reads hit 16 distinct 16-byte bank groups.
 __device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t c) { return r * kRowBytes + 16u * (c ^ ((r ^ (r >> 3)) & 7u)); }
 
+// s_waitcnt: wait until at most N vector memory loads of this wave are in flight
+template <int N> __device__ __forceinline__ void vm_wait() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 template <int F, int BM, int BN>
 __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   using U = Unit<F>;
@@ -76,8 +87,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   constexpr int WN = BN / 32;                   // 32-column MFMA tiles per wave
   constexpr int XW0 = BN == 96 ? 3 : 2;         // first x-wave: 2 BN threads decode weights
   constexpr int NX = BM / 8 / (4 - XW0);        // 1 KB activation DMA instructions per x-wave
-  __shared__ __attribute__((aligned(16))) uint8_t X0[BM * kRowBytes], X1[BM * kRowBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t W0[BN * kRowBytes], W1[BN * kRowBytes];
+  constexpr int P = BN == 64 ? 2 : 3;           // pipeline stages
+  __shared__ __attribute__((aligned(16))) uint8_t X0[BM * kRowBytes], X1[BM * kRowBytes], X2[P > 2 ? BM * kRowBytes : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t W0[BN * kRowBytes], W1[BN * kRowBytes], W2[P > 2 ? BN * kRowBytes : 16];
 
   // Workgroups are dispatched round-robin over the 8 XCDs; tile numbers are assigned so that
   // each XCD runs a contiguous range of tiles, M tile major: an XCD's L2 then holds the
@@ -97,8 +109,12 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const bool xwave = wave >= XW0;               // wave-uniform role
 
-  // ---- weights (waves 0, 1): thread t < 2 BN decodes half t & 1 of weight row t >> 1
-  const bool wload = t < 2 * BN;                // wave-uniform
+  // ---- weights (waves 0, 1): thread t < 2 BN decodes half t & 1 of weight row t >> 1. The
+  // loads and the decode run in every thread of the weight waves (threads past 2 BN, only
+  // in the 32-column tiles, re-read the tile's first row); only the stores depend on wload.
+  // With no branch around them, the compiler counts the loads in flight exactly, and the
+  // wait before a decode covers only the stage it reads.
+  const bool wload = 64 * XW0 <= 2 * BN || t < 2 * BN;   // wave-uniform; always true for BN >= 64
   const int lrow = (t >> 1) < BN ? t >> 1 : 0, h = t & 1;
   const int64_t wrow = r0 + lrow < a.n ? r0 + lrow : a.n - 1;   // rows past n are not stored
   Lane L;
@@ -110,7 +126,6 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   L.h = h;
   // global loads of step u (steps past the end re-load the last one, never read)
   auto gload = [&](Raw &q, int64_t u) {
-    if (!wload) return;
     u = u < a.units ? u : a.units - 1;
 #pragma unroll
     for (int p = 0; p < 4; ++p) L.off[p] = 0;
@@ -126,9 +141,9 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   };
   // decode a register stage to fp16 and store it into the weight tile W
   auto wstore = [&](const Raw &q, uint8_t *W) {
-    if (!wload) return;
     uint32_t pr[16];
     U::template wide<2>(q, h, pr);
+    if (!wload) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       // local pairs 4i..4i+3 are the unit's consecutive pairs pidx(h, 4i).. (k = 2 * pair), so
@@ -210,56 +225,122 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
         for (int j = 0; j < WN; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(A[i], B[j], acc[i][j], 0, 0, 0);
     }
   };
-  // x-waves: their LDS loads of this step are complete before they reach the barrier
-  auto xwait = [&]() { __builtin_amdgcn_s_waitcnt(0); };
-
-  // Pipeline, two steps per iteration so that every buffer and register stage is fixed:
-  // step u computes from X_{u&1}, W_{u&1}; the x-waves fill X_{(u+1)&1}, the weight waves store
-  // the decoded step u + 1 into W_{(u+1)&1} and load step u + 2.
   const int64_t units = a.units;
-  if (xwave) {
-    xdma(0, X0);
-    xwait();
-    __syncthreads();
-    int64_t u = 0;
-    for (; u + 2 <= units; u += 2) {
-      xdma(u + 1, X1);
-      mfma_step(X0, W0);
+  if constexpr (P == 2) {
+    // x-waves: their LDS loads of this step are complete before they reach the barrier
+    auto xwait = [&]() { __builtin_amdgcn_s_waitcnt(0); };
+
+    // Two stages, two steps per iteration so that every buffer and register stage is fixed:
+    // step u computes from X_{u&1}, W_{u&1}; the x-waves fill X_{(u+1)&1}, the weight waves store
+    // the decoded step u + 1 into W_{(u+1)&1} and load step u + 2.
+    if (xwave) {
+      xdma(0, X0);
       xwait();
       __syncthreads();
-      xdma(u + 2, X0);
-      mfma_step(X1, W1);
-      xwait();
-      __syncthreads();
-    }
-    if (u < units) {
-      xdma(u + 1, X1);
-      mfma_step(X0, W0);
-      xwait();
-      __syncthreads();
-    }
-  } else {
-    Raw q0, q1;
-    gload(q0, 0);
-    gload(q1, 1);
-    wstore(q0, W0);
-    __syncthreads();
-    int64_t u = 0;
-    for (; u + 2 <= units; u += 2) {
-      gload(q0, u + 2);
-      mfma_step(X0, W0);
-      wstore(q1, W1);
-      __syncthreads();
-      gload(q1, u + 3);
-      mfma_step(X1, W1);
+      int64_t u = 0;
+      for (; u + 2 <= units; u += 2) {
+        xdma(u + 1, X1);
+        mfma_step(X0, W0);
+        xwait();
+        __syncthreads();
+        xdma(u + 2, X0);
+        mfma_step(X1, W1);
+        xwait();
+        __syncthreads();
+      }
+      if (u < units) {
+        xdma(u + 1, X1);
+        mfma_step(X0, W0);
+        xwait();
+        __syncthreads();
+      }
+    } else {
+      Raw q0, q1;
+      gload(q0, 0);
+      gload(q1, 1);
       wstore(q0, W0);
       __syncthreads();
+      int64_t u = 0;
+      for (; u + 2 <= units; u += 2) {
+        gload(q0, u + 2);
+        mfma_step(X0, W0);
+        wstore(q1, W1);
+        __syncthreads();
+        gload(q1, u + 3);
+        mfma_step(X1, W1);
+        wstore(q0, W0);
+        __syncthreads();
+      }
+      if (u < units) {
+        gload(q0, u + 2);
+        mfma_step(X0, W0);
+        wstore(q1, W1);
+        __syncthreads();
+      }
     }
-    if (u < units) {
-      gload(q0, u + 2);
-      mfma_step(X0, W0);
-      wstore(q1, W1);
-      __syncthreads();
+  } else {
+    // Three stages, three steps per iteration: step u computes from X_{u%3}, W_{u%3}; at its
+    // start the x-waves issue the DMA of step u + 2 and the weight waves the loads of step u + 3
+    // (into the register stage decoded at step u - 1); at its end the weight waves decode step
+    // u + 1, loaded two steps earlier, and the x-waves wait for the DMA of step u + 1 only. The
+    // barrier is s_barrier after the wave's own LDS writes: __syncthreads would add a fence that
+    // also waits for the DMA still in flight. (The memory clobber keeps every LDS access on its
+    // side of the barrier.)
+    auto wg_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    auto XB = [&](auto J) -> uint8_t * {
+      if constexpr (decltype(J)::value == 0) return X0;
+      else if constexpr (decltype(J)::value == 1) return X1;
+      else return X2;
+    };
+    auto WB = [&](auto J) -> uint8_t * {
+      if constexpr (decltype(J)::value == 0) return W0;
+      else if constexpr (decltype(J)::value == 1) return W1;
+      else return W2;
+    };
+    if (xwave) {
+      xdma(0, X0);
+      xdma(1, X1);
+      vm_wait<NX>();
+      wg_barrier();
+      auto step = [&](auto J, int64_t u) {
+        xdma(u + 2, XB(std::integral_constant<int, (decltype(J)::value + 2) % 3>{}));
+        mfma_step(XB(J), WB(J));
+        vm_wait<NX>();
+        wg_barrier();
+      };
+      for (int64_t u = 0; u < units; u += 3) {
+        step(I0{}, u);
+        if (u + 1 < units) step(I1{}, u + 1);
+        if (u + 2 < units) step(I2{}, u + 2);
+      }
+      vm_wait<0>();   // no DMA into the workgroup's LDS outlives it
+    } else {
+      Raw q0, q1, q2;
+      auto QB = [&](auto J) -> Raw & {
+        if constexpr (decltype(J)::value == 0) return q0;
+        else if constexpr (decltype(J)::value == 1) return q1;
+        else return q2;
+      };
+      gload(q0, 0);
+      gload(q1, 1);
+      gload(q2, 2);
+      wstore(q0, W0);
+      wg_barrier();
+      auto step = [&](auto J, int64_t u) {
+        using JN = std::integral_constant<int, (decltype(J)::value + 1) % 3>;
+        gload(QB(J), u + 3);
+        mfma_step(XB(J), WB(J));
+        wstore(QB(JN{}), WB(JN{}));
+        wg_barrier();
+      };
+      for (int64_t u = 0; u < units; u += 3) {
+        step(I0{}, u);
+        if (u + 1 < units) step(I1{}, u + 1);
+        if (u + 2 < units) step(I2{}, u + 2);
+      }
     }
   }
 
