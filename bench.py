@@ -65,7 +65,8 @@ def parse():
                     help="skip the other workloads (INT4 4096^2, layer sets, decode batches, prefill)")
     ap.add_argument("--profile-workload", default=None, metavar="NAME",
                     help="only run --steps rounds over the matrices of workload NAME, rotated over >= 1.2 GB "
-                         "of copies, eagerly (for profiler runs); prints no JSON line")
+                         "of copies, eagerly (for profiler runs; kv_cache_int8_7b_8192: rounds of the KV-cache "
+                         "codec); prints no JSON line")
     ap.add_argument("--profile-plan", choices=("single", "group"), default="single",
                     help="one launch per matrix, or all matrices in one grouped launch")
     ap.add_argument("--profile-m", type=int, default=None, help="batch (activation rows) instead of the workload's")
@@ -184,6 +185,9 @@ def cpu_baseline(fmt, canonical, n, k, x, seconds):
 
 
 MFMA_F16_PEAK_TFLOPS = 2500.0
+# the 7B-like KV cache: K and V of 32 layers x 8192 tokens, 8 KV heads x 128 per row
+KV_WORKLOAD = "kv_cache_int8_7b_8192"
+KV_ROWS, KV_COLS = 2 * 32 * 8192, 8 * 128
 
 
 WARM_S = 0.15     # sustained load before a timed replay: the clocks drop within a second of idle
@@ -420,7 +424,7 @@ def extra_configs(qg, dev):
     # element; and the per-token append of a decode step (64 rows of 1024)
     import torch
     from workloads import activations
-    rows, cols = 2 * 32 * 8192, 8 * 128
+    rows, cols = KV_ROWS, KV_COLS
     x = torch.empty((rows, cols), dtype=torch.float16, device=dev)
     x.copy_(torch.from_numpy(activations(1024, cols, 3)).to(dev).repeat(rows // 1024, 1))
     codes = torch.empty((rows, cols), dtype=torch.int8, device=dev)
@@ -493,6 +497,25 @@ def main():
     import dequant_gemv_q4g32_amd as qg
     from workloads import WORKLOADS
 
+    if args.profile_workload == KV_WORKLOAD:
+        # the 8-bit KV-cache codec on the 7B-like cache: --steps rounds of quantize + dequantize
+        from workloads import activations
+        dev = torch.device("cuda:0")
+        rows, cols = KV_ROWS, KV_COLS
+        x = torch.empty((rows, cols), dtype=torch.float16, device=dev)
+        x.copy_(torch.from_numpy(activations(1024, cols, 3)).to(dev).repeat(rows // 1024, 1))
+        codes = torch.empty((rows, cols), dtype=torch.int8, device=dev)
+        scales = torch.empty((rows, cols // 32), dtype=torch.float16, device=dev)
+
+        def one_kv():
+            qg.kv_quantize(x, codes, scales)
+            qg.kv_dequantize(codes, scales, out=x)
+        _warm(one_kv)
+        for r in range(args.steps):
+            one_kv()
+        torch.cuda.synchronize()
+        log(f"[bench] profiled {KV_WORKLOAD}: {args.steps} rounds of quantize + dequantize, {rows} x {cols} fp16")
+        return
     if args.profile_workload:
         wl = WORKLOADS[args.profile_workload]
         m = args.profile_m or wl.m
