@@ -15,13 +15,15 @@
 //   * 128 x 32 (each wave one 32 x 32 MFMA tile) where 256 x 64 tiles would leave CUs without
 //     a workgroup (512 x 4096 has 128 of them, 128 x 11008 has 172): four times the tiles.
 // Roles per step:
-//   * the last waves (2 and 3; wave 3 alone for 96 columns) stream a later step's activation
-//     tile (BM rows x 128 bytes) straight into LDS with buffer_load ... lds (no registers, no
-//     LDS store instructions);
-//   * the first 2 BN threads (waves 0 and 1, waves 0-2, or wave 0; for 32 columns wave 1
-//     loads and decodes too but stores nothing) load a later step's weights (thread t: half
-//     t & 1 of the unit of weight row t >> 1) and decode the next step's to fp16 into the LDS
-//     weight tile;
+//   * activations: a later step's tile (BM rows x 128 bytes) goes straight into LDS with
+//     buffer_load ... lds (no registers, no LDS store instructions), from waves 2 and 3, or
+//     wave 3 alone for 96 columns; for q4g32, q5sb and q6sb with 96 columns every wave
+//     streams the 64 rows it multiplies itself instead (and waits for its own loads only);
+//   * weights: the first 2 BN threads (waves 0 and 1, waves 0-2, or wave 0) load a later
+//     step's weights (thread t: half t & 1 of the unit of weight row t >> 1) and decode the
+//     next step's to fp16 into the LDS weight tile. Wave 1 of the 32-column tiles, and wave 3
+//     where every wave streams its rows, load and decode a copy of row 0 and store nothing,
+//     so that the waves of one role run branch-free code;
 //   * all four waves run the current step's MFMAs (4 K-slices of 16).
 // P stages of both tiles in distinct LDS arrays (so that the compiler can see that the
 // loads into one buffer do not alias the reads of another) and one barrier per step: the
@@ -72,6 +74,13 @@ constexpr uint32_t kXRange = 0x7FFFFFF0u;    // activation buffer range; offsets
 // (and on any 8 aligned rows), so those reads hit 16 distinct 16-byte bank groups.
 __device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t c) { return r * kRowBytes + 16u * (c ^ ((r ^ (r >> 3)) & 7u)); }
 
+// 96-column tiles in which every wave streams its own activation rows and wave 3 decodes a
+// spare copy of row 0 (instead of wave 3 streaming all rows): measured per format on 512 and
+// 8192 or 11008 weight rows (K = 4096, one session) 4-12% faster for q4g32, q5sb and q6sb (and
+// their bf16 forms), and 2-27% slower for every other format (the group-wise 3/5-bit formats,
+// the INT4 group sizes other than 32, q4a32, q4g32h, q2sb and q3sb).
+template <int F> constexpr bool uni_rows() { return F == 4 || F == 5 || F == 6 || F == 15 || F == 16; }
+
 // s_waitcnt: wait until at most N vector memory loads of this wave are in flight
 template <int N> __device__ __forceinline__ void vm_wait() {
   static_assert(N >= 0 && N < 64, "vmcnt");
@@ -85,7 +94,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   static_assert((BM == 256 && (BN == 64 || BN == 96)) || (BM == 128 && BN == 32), "tile shape");
   constexpr int TM = BM / 128;                  // 32-row MFMA tiles per wave (rows BM / 4)
   constexpr int WN = BN / 32;                   // 32-column MFMA tiles per wave
-  constexpr int XW0 = BN == 96 ? 3 : 2;         // first x-wave: 2 BN threads decode weights
+  constexpr bool UNI = BN == 96 && uni_rows<F>();   // every wave streams its own activation rows
+  constexpr int XW0 = UNI ? 0 : (BN == 96 ? 3 : 2);   // first x-wave (2 BN threads decode weights)
   constexpr int NX = BM / 8 / (4 - XW0);        // 1 KB activation DMA instructions per x-wave
   constexpr int P = BN == 64 ? 2 : 3;           // pipeline stages
   __shared__ __attribute__((aligned(16))) uint8_t X0[BM * kRowBytes], X1[BM * kRowBytes], X2[P > 2 ? BM * kRowBytes : 16];
@@ -114,7 +124,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   // in the 32-column tiles, re-read the tile's first row); only the stores depend on wload.
   // With no branch around them, the compiler counts the loads in flight exactly, and the
   // wait before a decode covers only the stage it reads.
-  const bool wload = 64 * XW0 <= 2 * BN || t < 2 * BN;   // wave-uniform; always true for BN >= 64
+  const bool wload = UNI ? t < 2 * BN : (64 * XW0 <= 2 * BN || t < 2 * BN);   // wave-uniform
   const int lrow = (t >> 1) < BN ? t >> 1 : 0, h = t & 1;
   const int64_t wrow = r0 + lrow < a.n ? r0 + lrow : a.n - 1;   // rows past n are not stored
   Lane L;
@@ -153,7 +163,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  // ---- activations (waves 2, 3): instruction i of x-wave xw fills tile rows 8 R .. 8 R + 7,
+  // ---- activations (waves 2 and 3, wave 3, or every wave, which then fills the 64 rows it
+  // multiplies): instruction i of x-wave xw fills tile rows 8 R .. 8 R + 7,
   // R = NX xw + i (1 KB, written in lane order); lane l loads row 8 R + (l >> 3), chunk
   // (l & 7) ^ f(row) of the step's 128 bytes, which lands at LDS position l & 7 of that row:
   // the swizzled layout (f(8 R + j) = (j ^ R) & 7). A dead row, or the missing half of a ragged
@@ -300,7 +311,38 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       else if constexpr (decltype(J)::value == 1) return W1;
       else return W2;
     };
-    if (xwave) {
+    if constexpr (UNI) {
+      // one code path for every wave: its own activation rows, and the weights (wave 3 on a
+      // copy of row 0); the compiler's waits before the LDS reads of X cover this wave's DMA,
+      // and the barrier the weight tile
+      Raw q0, q1, q2;
+      auto QB = [&](auto J) -> Raw & {
+        if constexpr (decltype(J)::value == 0) return q0;
+        else if constexpr (decltype(J)::value == 1) return q1;
+        else return q2;
+      };
+      xdma(0, X0);
+      xdma(1, X1);
+      gload(q0, 0);
+      gload(q1, 1);
+      gload(q2, 2);
+      wstore(q0, W0);
+      wg_barrier();
+      auto step = [&](auto J, int64_t u) {
+        using JN = std::integral_constant<int, (decltype(J)::value + 1) % 3>;
+        xdma(u + 2, XB(std::integral_constant<int, (decltype(J)::value + 2) % 3>{}));
+        gload(QB(J), u + 3);
+        mfma_step(XB(J), WB(J));
+        wstore(QB(JN{}), WB(JN{}));
+        wg_barrier();
+      };
+      for (int64_t u = 0; u < units; u += 3) {
+        step(I0{}, u);
+        if (u + 1 < units) step(I1{}, u + 1);
+        if (u + 2 < units) step(I2{}, u + 2);
+      }
+      vm_wait<0>();   // no DMA into the workgroup's LDS outlives it
+    } else if (xwave) {
       xdma(0, X0);
       xdma(1, X1);
       vm_wait<NX>();
