@@ -17,13 +17,13 @@
 // Roles per step:
 //   * activations: a later step's tile (BM rows x 128 bytes) goes straight into LDS with
 //     buffer_load ... lds (no registers, no LDS store instructions), from waves 2 and 3, or
-//     wave 3 alone for 96 columns; for q4g32, q5sb and q6sb with 96 columns every wave
-//     streams the 64 rows it multiplies itself instead (and waits for its own loads only);
+//     wave 3 alone for 96 columns; for the formats of uni_rows96 / uni_rows64 every wave
+//     streams the rows it multiplies itself instead (and waits for its own loads only);
 //   * weights: the first 2 BN threads (waves 0 and 1, waves 0-2, or wave 0) load a later
 //     step's weights (thread t: half t & 1 of the unit of weight row t >> 1) and decode the
-//     next step's to fp16 into the LDS weight tile. Wave 1 of the 32-column tiles, and wave 3
-//     where every wave streams its rows, load and decode a copy of row 0 and store nothing,
-//     so that the waves of one role run branch-free code;
+//     next step's to fp16 into the LDS weight tile. Wave 1 of the 32-column tiles, and the
+//     waves past 2 BN threads where every wave streams its rows, load and decode a copy of
+//     row 0 and store nothing, so that the waves of one role run branch-free code;
 //   * all four waves run the current step's MFMAs (4 K-slices of 16).
 // P stages of both tiles in distinct LDS arrays (so that the compiler can see that the
 // loads into one buffer do not alias the reads of another) and one barrier per step: the
@@ -74,12 +74,16 @@ constexpr uint32_t kXRange = 0x7FFFFFF0u;    // activation buffer range; offsets
 // (and on any 8 aligned rows), so those reads hit 16 distinct 16-byte bank groups.
 __device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t c) { return r * kRowBytes + 16u * (c ^ ((r ^ (r >> 3)) & 7u)); }
 
-// 96-column tiles in which every wave streams its own activation rows and wave 3 decodes a
-// spare copy of row 0 (instead of wave 3 streaming all rows): measured per format on 512 and
-// 8192 or 11008 weight rows (K = 4096, one session) 4-12% faster for q4g32, q5sb and q6sb (and
-// their bf16 forms), and 2-27% slower for every other format (the group-wise 3/5-bit formats,
-// the INT4 group sizes other than 32, q4a32, q4g32h, q2sb and q3sb).
-template <int F> constexpr bool uni_rows() { return F == 4 || F == 5 || F == 6 || F == 15 || F == 16; }
+// Formats whose tiles let every wave stream its own activation rows, with the spare waves
+// decoding a copy of weight row 0 (instead of waves 2-3 streaming all rows). Measured per
+// format, one session each, K = 4096:
+//   * 96 columns (512 x 8192 and 512 x 11008): 4-12% faster for q4g32, q5sb and q6sb and their
+//     bf16 forms; 2-27% slower for every other format (the group-wise 3/5-bit formats, the
+//     INT4 group sizes other than 32, q4a32, q4g32h, q2sb and q3sb);
+//   * 64 columns (1024-4096 x 11008): q4g32 and q5sb 1-13% faster; q6sb 2-4% slower at 2048
+//     and 4096 rows.
+template <int F> constexpr bool uni_rows96() { return F == 4 || F == 5 || F == 6 || F == 15 || F == 16; }
+template <int F> constexpr bool uni_rows64() { return F == 4 || F == 5 || F == 15; }
 
 // s_waitcnt: wait until at most N vector memory loads of this wave are in flight
 template <int N> __device__ __forceinline__ void vm_wait() {
@@ -94,7 +98,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   static_assert((BM == 256 && (BN == 64 || BN == 96)) || (BM == 128 && BN == 32), "tile shape");
   constexpr int TM = BM / 128;                  // 32-row MFMA tiles per wave (rows BM / 4)
   constexpr int WN = BN / 32;                   // 32-column MFMA tiles per wave
-  constexpr bool UNI = BN == 96 && uni_rows<F>();   // every wave streams its own activation rows
+  constexpr bool UNI = (BN == 96 && uni_rows96<F>()) || (BN == 64 && uni_rows64<F>());   // see uni_rows96
   constexpr int XW0 = UNI ? 0 : (BN == 96 ? 3 : 2);   // first x-wave (2 BN threads decode weights)
   constexpr int NX = BM / 8 / (4 - XW0);        // 1 KB activation DMA instructions per x-wave
   constexpr int P = BN == 64 ? 2 : 3;           // pipeline stages
@@ -237,7 +241,38 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
   };
   const int64_t units = a.units;
-  if constexpr (P == 2) {
+  if constexpr (P == 2 && UNI) {
+    // two stages, every wave on its own activation rows (the DMA of step u + 1 may still be in
+    // flight at the barrier: the compiler's wait before the wave's LDS reads covers it)
+    auto wg_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
+    Raw q0, q1;
+    xdma(0, X0);
+    gload(q0, 0);
+    gload(q1, 1);
+    wstore(q0, W0);
+    wg_barrier();
+    int64_t u = 0;
+    for (; u + 2 <= units; u += 2) {
+      xdma(u + 1, X1);
+      gload(q0, u + 2);
+      mfma_step(X0, W0);
+      wstore(q1, W1);
+      wg_barrier();
+      xdma(u + 2, X0);
+      gload(q1, u + 3);
+      mfma_step(X1, W1);
+      wstore(q0, W0);
+      wg_barrier();
+    }
+    if (u < units) {
+      xdma(u + 1, X1);
+      gload(q0, u + 2);
+      mfma_step(X0, W0);
+      wstore(q1, W1);
+      wg_barrier();
+    }
+    vm_wait<0>();   // no DMA into the workgroup's LDS outlives it
+  } else if constexpr (P == 2) {
     // x-waves: their LDS loads of this step are complete before they reach the barrier
     auto xwait = [&]() { __builtin_amdgcn_s_waitcnt(0); };
 
