@@ -16,14 +16,14 @@
 //     a workgroup (512 x 4096 has 128 of them, 128 x 11008 has 172): four times the tiles.
 // Roles per step:
 //   * activations: a later step's tile (BM rows x 128 bytes) goes straight into LDS with
-//     buffer_load ... lds (no registers, no LDS store instructions), from waves 2 and 3, or
-//     wave 3 alone for 96 columns; for the formats of uni_rows96 / uni_rows64 every wave
-//     streams the rows it multiplies itself instead (and waits for its own loads only);
+//     buffer_load ... lds (no registers, no LDS store instructions). With 96 columns, and
+//     with 64 for the formats of uni_rows64, every wave streams the 64 rows it multiplies
+//     itself (and waits for its own loads only); otherwise waves 2 and 3 stream the tile;
 //   * weights: the first 2 BN threads (waves 0 and 1, waves 0-2, or wave 0) load a later
 //     step's weights (thread t: half t & 1 of the unit of weight row t >> 1) and decode the
-//     next step's to fp16 into the LDS weight tile. Wave 1 of the 32-column tiles, and the
-//     waves past 2 BN threads where every wave streams its rows, load and decode a copy of
-//     row 0 and store nothing, so that the waves of one role run branch-free code;
+//     next step's to fp16 into the LDS weight tile. Wave 1 of the 32-column tiles, and waves
+//     2-3 of the 64-column tiles of uni_rows64, load and decode a copy of row 0 and store
+//     nothing, so that the waves of one role run branch-free code;
 //   * all four waves run the current step's MFMAs (4 K-slices of 16).
 // P stages of both tiles in distinct LDS arrays (so that the compiler can see that the
 // loads into one buffer do not alias the reads of another) and one barrier per step: the
@@ -74,15 +74,10 @@ constexpr uint32_t kXRange = 0x7FFFFFF0u;    // activation buffer range; offsets
 // (and on any 8 aligned rows), so those reads hit 16 distinct 16-byte bank groups.
 __device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t c) { return r * kRowBytes + 16u * (c ^ ((r ^ (r >> 3)) & 7u)); }
 
-// Formats whose tiles let every wave stream its own activation rows, with the spare waves
-// decoding a copy of weight row 0 (instead of waves 2-3 streaming all rows). Measured per
-// format, one session each, K = 4096:
-//   * 96 columns (512 x 8192 and 512 x 11008): 4-12% faster for q4g32, q5sb and q6sb and their
-//     bf16 forms; 2-27% slower for every other format (the group-wise 3/5-bit formats, the
-//     INT4 group sizes other than 32, q4a32, q4g32h, q2sb and q3sb);
-//   * 64 columns (1024-4096 x 11008): q4g32 and q5sb 1-13% faster; q6sb 2-4% slower at 2048
-//     and 4096 rows.
-template <int F> constexpr bool uni_rows96() { return F == 4 || F == 5 || F == 6 || F == 15 || F == 16; }
+// Formats whose 64-column tiles let every wave stream its own activation rows, the two spare
+// waves decoding a copy of weight row 0 (instead of waves 2-3 streaming all rows): measured
+// on 1024-4096 x 11008 x 4096 (one session), q4g32 and q5sb 1-13% faster; q6sb 2-4% slower.
+// (The 96-column tiles stream each wave's own rows for every format, with no spare decode.)
 template <int F> constexpr bool uni_rows64() { return F == 4 || F == 5 || F == 15; }
 
 // s_waitcnt: wait until at most N vector memory loads of this wave are in flight
@@ -98,9 +93,10 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
   static_assert((BM == 256 && (BN == 64 || BN == 96)) || (BM == 128 && BN == 32), "tile shape");
   constexpr int TM = BM / 128;                  // 32-row MFMA tiles per wave (rows BM / 4)
   constexpr int WN = BN / 32;                   // 32-column MFMA tiles per wave
-  constexpr bool UNI = (BN == 96 && uni_rows96<F>()) || (BN == 64 && uni_rows64<F>());   // see uni_rows96
+  constexpr bool UNI = BN == 64 && uni_rows64<F>();   // every wave streams its rows, spare decode
+  constexpr bool OWN = UNI || BN == 96;         // every wave streams the activation rows it uses
   constexpr int XW0 = UNI ? 0 : (BN == 96 ? 3 : 2);   // first x-wave (2 BN threads decode weights)
-  constexpr int NX = BM / 8 / (4 - XW0);        // 1 KB activation DMA instructions per x-wave
+  constexpr int NX = OWN ? BM / 32 : BM / 8 / (4 - XW0);   // 1 KB activation DMA instructions per x-wave
   constexpr int P = BN == 64 ? 2 : 3;           // pipeline stages
   __shared__ __attribute__((aligned(16))) uint8_t X0[BM * kRowBytes], X1[BM * kRowBytes], X2[P > 2 ? BM * kRowBytes : 16];
   __shared__ __attribute__((aligned(16))) uint8_t W0[BN * kRowBytes], W1[BN * kRowBytes], W2[P > 2 ? BN * kRowBytes : 16];
@@ -167,13 +163,13 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  // ---- activations (waves 2 and 3, wave 3, or every wave, which then fills the 64 rows it
+  // ---- activations (waves 2 and 3, or every wave, which then fills the 64 rows it
   // multiplies): instruction i of x-wave xw fills tile rows 8 R .. 8 R + 7,
   // R = NX xw + i (1 KB, written in lane order); lane l loads row 8 R + (l >> 3), chunk
   // (l & 7) ^ f(row) of the step's 128 bytes, which lands at LDS position l & 7 of that row:
   // the swizzled layout (f(8 R + j) = (j ^ R) & 7). A dead row, or the missing half of a ragged
   // q4g32 unit, gets an offset past the range and reads zeros.
-  const int xw = wave - XW0 < 0 ? 0 : wave - XW0;
+  const int xw = OWN ? wave : (wave - XW0 < 0 ? 0 : wave - XW0);
   const int xrow_l = lane >> 3;
   const rsrc_t xr = make_rsrc(a.x + m0 * a.ldx, kXRange);
   // 256-row tiles: each instruction's lane offset is fixed (row and chunk) and the step adds
@@ -326,12 +322,14 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
   } else {
     // Three stages, three steps per iteration: step u computes from X_{u%3}, W_{u%3}; at its
-    // start the x-waves issue the DMA of step u + 2 and the weight waves the loads of step u + 3
-    // (into the register stage decoded at step u - 1); at its end the weight waves decode step
-    // u + 1, loaded two steps earlier, and the x-waves wait for the DMA of step u + 1 only. The
-    // barrier is s_barrier after the wave's own LDS writes: __syncthreads would add a fence that
-    // also waits for the DMA still in flight. (The memory clobber keeps every LDS access on its
-    // side of the barrier.)
+    // start the activation DMA of step u + 2 is issued and the weight waves issue the loads of
+    // step u + 3 (into the register stage decoded at step u - 1); at its end the weight waves
+    // decode step u + 1, loaded two steps earlier. 96 columns: every wave streams its own rows
+    // and reads only those, so the compiler's wait before those LDS reads (for that wave's DMA
+    // into that buffer) is all they need. 32 columns: the x-waves wait for the DMA of step
+    // u + 1 only. The barrier is s_barrier after the wave's own LDS writes: __syncthreads would
+    // add a fence that also waits for the DMA still in flight. (The memory clobber keeps every
+    // LDS access on its side of the barrier.)
     auto wg_barrier = [&]() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
@@ -346,35 +344,48 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       else if constexpr (decltype(J)::value == 1) return W1;
       else return W2;
     };
-    if constexpr (UNI) {
-      // one code path for every wave: its own activation rows, and the weights (wave 3 on a
-      // copy of row 0); the compiler's waits before the LDS reads of X cover this wave's DMA,
-      // and the barrier the weight tile
-      Raw q0, q1, q2;
-      auto QB = [&](auto J) -> Raw & {
-        if constexpr (decltype(J)::value == 0) return q0;
-        else if constexpr (decltype(J)::value == 1) return q1;
-        else return q2;
-      };
-      xdma(0, X0);
-      xdma(1, X1);
-      gload(q0, 0);
-      gload(q1, 1);
-      gload(q2, 2);
-      wstore(q0, W0);
-      wg_barrier();
-      auto step = [&](auto J, int64_t u) {
-        using JN = std::integral_constant<int, (decltype(J)::value + 1) % 3>;
-        xdma(u + 2, XB(std::integral_constant<int, (decltype(J)::value + 2) % 3>{}));
-        gload(QB(J), u + 3);
-        mfma_step(XB(J), WB(J));
-        wstore(QB(JN{}), WB(JN{}));
+    if constexpr (OWN) {
+      if (xwave) {   // wave 3: its activation rows only
+        xdma(0, X0);
+        xdma(1, X1);
         wg_barrier();
-      };
-      for (int64_t u = 0; u < units; u += 3) {
-        step(I0{}, u);
-        if (u + 1 < units) step(I1{}, u + 1);
-        if (u + 2 < units) step(I2{}, u + 2);
+        auto step = [&](auto J, int64_t u) {
+          xdma(u + 2, XB(std::integral_constant<int, (decltype(J)::value + 2) % 3>{}));
+          mfma_step(XB(J), WB(J));
+          wg_barrier();
+        };
+        for (int64_t u = 0; u < units; u += 3) {
+          step(I0{}, u);
+          if (u + 1 < units) step(I1{}, u + 1);
+          if (u + 2 < units) step(I2{}, u + 2);
+        }
+      } else {
+        Raw q0, q1, q2;
+        auto QB = [&](auto J) -> Raw & {
+          if constexpr (decltype(J)::value == 0) return q0;
+          else if constexpr (decltype(J)::value == 1) return q1;
+          else return q2;
+        };
+        xdma(0, X0);
+        xdma(1, X1);
+        gload(q0, 0);
+        gload(q1, 1);
+        gload(q2, 2);
+        wstore(q0, W0);
+        wg_barrier();
+        auto step = [&](auto J, int64_t u) {
+          using JN = std::integral_constant<int, (decltype(J)::value + 1) % 3>;
+          xdma(u + 2, XB(std::integral_constant<int, (decltype(J)::value + 2) % 3>{}));
+          gload(QB(J), u + 3);
+          mfma_step(XB(J), WB(J));
+          wstore(QB(JN{}), WB(JN{}));
+          wg_barrier();
+        };
+        for (int64_t u = 0; u < units; u += 3) {
+          step(I0{}, u);
+          if (u + 1 < units) step(I1{}, u + 1);
+          if (u + 2 < units) step(I2{}, u + 2);
+        }
       }
       vm_wait<0>();   // no DMA into the workgroup's LDS outlives it
     } else if (xwave) {
