@@ -7,24 +7,25 @@
 // into fp16 w_hat by the same per-format unit decode as the GEMV (units.h, `wide`), written
 // once per K step into an LDS tile that every wave of the workgroup reads.
 //
-// Tiling: a workgroup of 4 waves computes a BM x BN tile of Y and walks K in steps of one
+// Tiling: a workgroup of NW waves computes a BM x BN tile of Y and walks K in steps of one
 // 64-weight unit. Three shapes:
-//   * 256 x 64 (each wave a 64 x 64 block of 2 x 2 MFMA tiles): each weight is decoded once
-//     per 256 activation rows, and the 32 KB of activations a step brings in feed 2 MFLOP;
-//   * 256 x 96 (each wave 64 x 96) where 256 x 64 tiles come to just over one per CU;
-//   * 128 x 32 (each wave one 32 x 32 MFMA tile) where 256 x 64 tiles would leave CUs without
+//   * 256 x 64 (4 waves, each a 64 x 64 block of 2 x 2 MFMA tiles): each weight is decoded
+//     once per 256 activation rows, and the 32 KB of activations a step brings in feed 2 MFLOP;
+//   * 256 x 96 (8 waves, each 32 x 96) where 256 x 64 tiles come to just over one per CU: its
+//     132 KB of LDS leave one workgroup per CU, and 8 waves put two on each SIMD;
+//   * 128 x 32 (4 waves, each one 32 x 32 MFMA tile) where 256 x 64 tiles would leave CUs without
 //     a workgroup (512 x 4096 has 128 of them, 128 x 11008 has 172): four times the tiles.
 // Roles per step:
 //   * activations: a later step's tile (BM rows x 128 bytes) goes straight into LDS with
 //     buffer_load ... lds (no registers, no LDS store instructions). With 96 columns, and
-//     with 64 for the formats of uni_rows64, every wave streams the 64 rows it multiplies
-//     itself (and waits for its own loads only); otherwise waves 2 and 3 stream the tile;
+//     with 64 for the formats of uni_rows64, every wave streams the rows it multiplies itself
+//     (and waits for its own loads only); otherwise waves 2 and 3 stream the tile;
 //   * weights: the first 2 BN threads (waves 0 and 1, waves 0-2, or wave 0) load a later
 //     step's weights (thread t: half t & 1 of the unit of weight row t >> 1) and decode the
 //     next step's to fp16 into the LDS weight tile. Wave 1 of the 32-column tiles, and waves
 //     2-3 of the 64-column tiles of uni_rows64, load and decode a copy of row 0 and store
 //     nothing, so that the waves of one role run branch-free code;
-//   * all four waves run the current step's MFMAs (4 K-slices of 16).
+//   * all waves run the current step's MFMAs (4 K-slices of 16).
 // P stages of both tiles in distinct LDS arrays (so that the compiler can see that the
 // loads into one buffer do not alias the reads of another) and one barrier per step: the
 // 256 x 64 tiles take two (two workgroups fit on a CU, each hiding the other's waits), the
@@ -87,16 +88,17 @@ template <int N> __device__ __forceinline__ void vm_wait() {
 }
 
 template <int F, int BM, int BN>
-__global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
+__global__ __launch_bounds__(BN == 96 ? 512 : 256) void prefill_kernel(PrefillArgs a) {
   using U = Unit<F>;
   using Raw = typename U::Raw;
   static_assert((BM == 256 && (BN == 64 || BN == 96)) || (BM == 128 && BN == 32), "tile shape");
-  constexpr int TM = BM / 128;                  // 32-row MFMA tiles per wave (rows BM / 4)
+  constexpr int NW = BN == 96 ? 8 : 4;          // waves
+  constexpr int TM = BM / (32 * NW);            // 32-row MFMA tiles per wave (rows BM / NW)
   constexpr int WN = BN / 32;                   // 32-column MFMA tiles per wave
   constexpr bool UNI = BN == 64 && uni_rows64<F>();   // every wave streams its rows, spare decode
   constexpr bool OWN = UNI || BN == 96;         // every wave streams the activation rows it uses
   constexpr int XW0 = UNI ? 0 : (BN == 96 ? 3 : 2);   // first x-wave (2 BN threads decode weights)
-  constexpr int NX = OWN ? BM / 32 : BM / 8 / (4 - XW0);   // 1 KB activation DMA instructions per x-wave
+  constexpr int NX = OWN ? BM / (8 * NW) : BM / 8 / (4 - XW0);   // 1 KB activation DMA instructions per x-wave
   constexpr int P = BN == 64 ? 2 : 3;           // pipeline stages
   __shared__ __attribute__((aligned(16))) uint8_t X0[BM * kRowBytes], X1[BM * kRowBytes], X2[P > 2 ? BM * kRowBytes : 16];
   __shared__ __attribute__((aligned(16))) uint8_t W0[BN * kRowBytes], W1[BN * kRowBytes], W2[P > 2 ? BN * kRowBytes : 16];
@@ -163,8 +165,8 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  // ---- activations (waves 2 and 3, or every wave, which then fills the 64 rows it
-  // multiplies): instruction i of x-wave xw fills tile rows 8 R .. 8 R + 7,
+  // ---- activations (waves 2 and 3, or every wave, which then fills the rows it multiplies):
+  // instruction i of x-wave xw fills tile rows 8 R .. 8 R + 7,
   // R = NX xw + i (1 KB, written in lane order); lane l loads row 8 R + (l >> 3), chunk
   // (l & 7) ^ f(row) of the step's 128 bytes, which lands at LDS position l & 7 of that row:
   // the swizzled layout (f(8 R + j) = (j ^ R) & 7). A dead row, or the missing half of a ragged
@@ -212,7 +214,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     }
   };
 
-  // ---- MFMAs of one step: wave w covers tile rows BM w / 4 .., each of its TM 32-row blocks
+  // ---- MFMAs of one step: wave w covers tile rows BM w / NW .., each of its TM 32-row blocks
   // against every 32-column block of the weight tile
   f32x16 acc[TM][WN];
 #pragma unroll
@@ -221,7 +223,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     for (int j = 0; j < WN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-  const uint32_t arow = (uint32_t)(BM / 4 * wave + (lane & 31)), brow = (uint32_t)(lane & 31), kh = (uint32_t)(lane >> 5);
+  const uint32_t arow = (uint32_t)(BM / NW * wave + (lane & 31)), brow = (uint32_t)(lane & 31), kh = (uint32_t)(lane >> 5);
   auto mfma_step = [&](const uint8_t *X, const uint8_t *W) {
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -345,7 +347,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       else return W2;
     };
     if constexpr (OWN) {
-      if (xwave) {   // wave 3: its activation rows only
+      if (xwave) {   // waves 3-7: their activation rows only
         xdma(0, X0);
         xdma(1, X1);
         wg_barrier();
@@ -439,7 +441,7 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
     for (int j = 0; j < WN; ++j)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const int64_t row = m0 + BM / 4 * wave + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
+        const int64_t row = m0 + BM / NW * wave + 32 * i + 8 * (e >> 2) + 4 * (lane >> 5) + (e & 3);
         const int64_t col = r0 + 32 * j + (lane & 31);
         if (row < a.m && col < a.n) {
           const int64_t idx = row * a.ldy + col;
@@ -449,16 +451,21 @@ __global__ __launch_bounds__(256) void prefill_kernel(PrefillArgs a) {
       }
 }
 
-// Tile shape for m x n: 256 x 64 when that gives every CU a workgroup; else 128 x 32, four
-// times the tiles (each K step of a tile is then short, and more of them run at once). Where
-// 256 x 64 tiles come to just over one per CU (257 to 384) and 256 x 96 tiles fit in one round,
-// the wider tiles: 512 x 11008 has 344 of the first (88 CUs run two) and 230 of the second
-// (measured 2-8% faster; everywhere else the 96-row tiles were slower).
+// Tile shape for m x n: 256 rows when 256 x 64 tiles give every CU a workgroup, else 128 x 32,
+// four times the tiles (each K step of a tile is then short, and more of them run at once).
+// Between 64 and 96 columns, the one whose rounds of workgroups fill more of the CUs: two
+// 256 x 64 workgroups run on a CU at once, one 256 x 96 (8 waves, two per SIMD); at equal
+// fill the 96-column tiles are 2-5% faster, hence the margin. Measured on one MI355X (q3sb,
+// q4g32, q5sb, q6sb; 96 against 64 columns): 1024 x 11008 x 4096 460 tiles against 688,
+// 8-20% faster; 2048 x 28672 x 8192 2392 against 3584, 5%; 2048 x 4096 x 4096 344 against
+// 512, 16-22% slower.
 void prefill_tile(int64_t m, int64_t n, int *bm, int *bn) {
   const int64_t mt = (m + 255) / 256, t64 = mt * ((n + 63) / 64), t96 = mt * ((n + 95) / 96);
   const bool big = t64 >= 256;
+  const int64_t r64 = (t64 + 511) / 512, r96 = (t96 + 255) / 256;   // rounds on 256 CUs
+  const double fill64 = (double)t64 / (double)(512 * r64), fill96 = (double)t96 / (double)(256 * r96);
   *bm = big ? 256 : 128;
-  *bn = !big ? 32 : (t64 <= 384 && t96 <= 256 ? 96 : 64);
+  *bn = !big ? 32 : (fill96 + 0.07 >= fill64 ? 96 : 64);
 }
 
 int launch_prefill(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int64_t ldy, int y_f32,
@@ -491,7 +498,7 @@ int launch_prefill(int fmt, const void *w, const uint16_t *X, int64_t ldx, void 
   a.mtiles = (int)mtiles;
   a.ntiles = (int)ntiles;
   a.per_xcd = (int)((total + 7) / 8);
-  const dim3 grid((unsigned)(8 * a.per_xcd)), block(256);
+  const dim3 grid((unsigned)(8 * a.per_xcd)), block(BN == 96 ? 512 : 256);
   auto go = [&](auto big, auto small, auto wide) {
     if (BM == 128) return launch(small, grid, block, 0, s, a);
     return BN == 96 ? launch(wide, grid, block, 0, s, a) : launch(big, grid, block, 0, s, a);
