@@ -11,8 +11,9 @@
 // 64-weight unit. Three shapes:
 //   * 256 x 64 (4 waves, each a 64 x 64 block of 2 x 2 MFMA tiles): each weight is decoded
 //     once per 256 activation rows, and the 32 KB of activations a step brings in feed 2 MFLOP;
-//   * 256 x 96 (8 waves, each 32 x 96) where 256 x 64 tiles come to just over one per CU: its
-//     132 KB of LDS leave one workgroup per CU, and 8 waves put two on each SIMD;
+//   * 256 x 96 (8 waves, each 32 x 96) where its rounds of workgroups fill the CUs better
+//     (prefill_tile): its 132 KB of LDS leave one workgroup per CU, and 8 waves put two on
+//     each SIMD;
 //   * 128 x 32 (4 waves, each one 32 x 32 MFMA tile) where 256 x 64 tiles would leave CUs without
 //     a workgroup (512 x 4096 has 128 of them, 128 x 11008 has 172): four times the tiles.
 // Roles per step:
@@ -121,9 +122,10 @@ __global__ __launch_bounds__(BN == 96 ? 512 : 256) void prefill_kernel(PrefillAr
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const bool xwave = wave >= XW0;               // wave-uniform role
 
-  // ---- weights (waves 0, 1): thread t < 2 BN decodes half t & 1 of weight row t >> 1. The
-  // loads and the decode run in every thread of the weight waves (threads past 2 BN, only
-  // in the 32-column tiles, re-read the tile's first row); only the stores depend on wload.
+  // ---- weights (waves below XW0, or every wave in the uni_rows64 layout): thread t < 2 BN
+  // decodes half t & 1 of weight row t >> 1. The loads and the decode run in every thread of
+  // the weight waves (threads past 2 BN re-read the tile's first row); only the stores depend
+  // on wload.
   // With no branch around them, the compiler counts the loads in flight exactly, and the
   // wait before a decode covers only the stage it reads.
   const bool wload = UNI ? t < 2 * BN : (64 * XW0 <= 2 * BN || t < 2 * BN);   // wave-uniform
