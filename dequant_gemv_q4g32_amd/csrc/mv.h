@@ -141,17 +141,34 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
   // K passes: the wk waves of a row group cover wk * UPW units per pass. With more than one
   // pass (long K with many activation rows) each wave accumulates its partial sums in LDS.
   // Act-order with the activations staged in LDS: the workgroup copies its m rows of x
-  // (contiguous 16-byte loads) once, so that each lane's gather by the permutation reads LDS
-  // instead of issuing 2-byte global loads that touch a cache line each.
-  const uint16_t *xl = a.xl_off >= 0 ? reinterpret_cast<const uint16_t *>(red + a.xl_off) : nullptr;
-  if (PERM && xl) {
-    uint16_t *xw = reinterpret_cast<uint16_t *>(red + a.xl_off);
+  // (contiguous 16-byte loads) once, then writes them again in stored-column order (column c
+  // gets x[perm[c]], an index outside [0, k) gives 0), reading the permutation once per
+  // workgroup with contiguous loads. Each lane then reads its activations from the second
+  // copy as contiguous 16-byte pieces, as without a permutation, instead of loading its
+  // indices and gathering 2-byte values itself.
+  const uint16_t *xq = nullptr;
+  if (PERM && a.xl_off >= 0) {
+    uint16_t *xn = reinterpret_cast<uint16_t *>(red + a.xl_off);   // [m][k], natural order
+    uint16_t *xs = xn + a.m * a.k;                                  // [m][k], stored-column order
     const int64_t chunks = a.k / 8;                          // 16-byte chunks per row
     for (int64_t i = threadIdx.x; i < a.m * chunks; i += blockDim.x) {
       const int64_t mm = i / chunks, c = i % chunks;
-      *reinterpret_cast<u32x4 *>(xw + mm * a.k + 8 * c) = ld4(reinterpret_cast<const uint8_t *>(x + mm * a.ldx + 8 * c));
+      *reinterpret_cast<u32x4 *>(xn + mm * a.k + 8 * c) = ld4(reinterpret_cast<const uint8_t *>(x + mm * a.ldx + 8 * c));
     }
     __syncthreads();
+    const rsrc_t pr = make_rsrc(a.perm, (uint32_t)(a.k * 4));
+    for (int64_t i = threadIdx.x; i < a.m * chunks; i += blockDim.x) {
+      const int64_t mm = i / chunks, c = i % chunks;
+      const u32x4 i0 = bld4c(pr, (uint32_t)(c * 32), 0), i1 = bld4c(pr, (uint32_t)(c * 32 + 16), 0);
+      const uint32_t idx[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+      uint32_t hv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) hv[j] = idx[j] < (uint32_t)a.k ? xn[mm * a.k + idx[j]] : 0u;
+      *reinterpret_cast<u32x4 *>(xs + mm * a.k + 8 * c) =
+          u32x4{hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16)};
+    }
+    __syncthreads();
+    xq = xs;
   }
 
   const int passes = MP ? a.kpasses : 1;
@@ -179,38 +196,54 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
 
     // The lane's activation pairs, 16 bytes (4 pairs) at a time: local pairs 4i..4i+3 are the
     // unit's pairs pidx(h, 4i).. (consecutive), i.e. bytes 4 * pidx(h, 4i) of its 128.
-    // With an act-order permutation, the activation of stored column c is x[perm[c]]: the
-    // lane gathers its 8 activations per group of 4 pairs through 32-bit buffer loads of the
-    // indices and 16-bit buffer loads of x (an index outside [0, k) reads 0, never past x).
+    // With an act-order permutation, the activation of stored column c is x[perm[c]]: read
+    // from the workgroup's copy in stored-column order, or gathered by the lane (an index
+    // outside [0, k) reads 0, never past x).
     uint32_t xp[M][NP];
     auto load_x = [&]() {
     // (a separate instantiation: the gather's registers at the branch made the register
     // allocator spill the kernels with 4 and 8 activation rows)
     if constexpr (PERM) {
-      const rsrc_t pr = make_rsrc(a.perm, (uint32_t)(a.k * 4));
-#pragma unroll
-      for (int i = 0; i < NP / 4; ++i) {
-        uint32_t off = 4u * (uint32_t)U::pidx(h, 4 * i, S);
-        bool keepx = true;
-        if (F == 4 && half && off >= 64) { off -= 64; keepx = false; }
-        const uint32_t kb = (uint32_t)(u * kUnit) + off / 2;   // first of the 8 stored columns
-        const u32x4 i0 = bld4c(pr, kb * 4, 0), i1 = bld4c(pr, kb * 4 + 16, 0);
-        const uint32_t idx[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+      if (xq) {
 #pragma unroll
         for (int mm = 0; mm < M; ++mm) {
-          const bool live = mm < a.m && keepx;
-          const int64_t row = mm < a.m ? mm : 0;
-          uint32_t hv[8];
-          if (xl) {
+          const bool live = mm < a.m;
+          const uint16_t *px = xq + (int64_t)(live ? mm : 0) * a.k + u * kUnit;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) hv[j] = idx[j] < (uint32_t)a.k ? xl[row * a.k + idx[j]] : 0u;
-          } else {
+          for (int i = 0; i < NP / 4; ++i) {
+            uint32_t off = 4u * (uint32_t)U::pidx(h, 4 * i, S);
+            bool keepx = live;
+            if (F == 4 && half && off >= 64) { off -= 64; keepx = false; }
+            const u32x4 v = *reinterpret_cast<const u32x4 *>(px + off / 2);
+            xp[mm][4 * i + 0] = keepx ? v.x : 0u;
+            xp[mm][4 * i + 1] = keepx ? v.y : 0u;
+            xp[mm][4 * i + 2] = keepx ? v.z : 0u;
+            xp[mm][4 * i + 3] = keepx ? v.w : 0u;
+          }
+        }
+      } else {
+        // the activations did not fit in LDS: the lane gathers its 8 activations per group of 4
+        // pairs through 32-bit buffer loads of the indices and 16-bit buffer loads of x
+        const rsrc_t pr = make_rsrc(a.perm, (uint32_t)(a.k * 4));
+#pragma unroll
+        for (int i = 0; i < NP / 4; ++i) {
+          uint32_t off = 4u * (uint32_t)U::pidx(h, 4 * i, S);
+          bool keepx = true;
+          if (F == 4 && half && off >= 64) { off -= 64; keepx = false; }
+          const uint32_t kb = (uint32_t)(u * kUnit) + off / 2;   // first of the 8 stored columns
+          const u32x4 i0 = bld4c(pr, kb * 4, 0), i1 = bld4c(pr, kb * 4 + 16, 0);
+          const uint32_t idx[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+#pragma unroll
+          for (int mm = 0; mm < M; ++mm) {
+            const bool live = mm < a.m && keepx;
+            const int64_t row = mm < a.m ? mm : 0;
             const rsrc_t xr = make_rsrc(x + row * a.ldx, (uint32_t)(a.k * 2));
+            uint32_t hv[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j) hv[j] = bldh(xr, idx[j] * 2, 0);
-          }
 #pragma unroll
-          for (int r = 0; r < 4; ++r) xp[mm][4 * i + r] = live ? (hv[2 * r] | (hv[2 * r + 1] << 16)) : 0u;
+            for (int r = 0; r < 4; ++r) xp[mm][4 * i + r] = live ? (hv[2 * r] | (hv[2 * r + 1] << 16)) : 0u;
+          }
         }
       }
     } else {
@@ -385,7 +418,7 @@ inline int fill_args(int fmt, const void *w, int64_t n, int64_t k, GemvArgs &a) 
 
 constexpr int64_t kSimds = 1024;           // 256 CUs x 4 SIMDs
 constexpr int kMaxBatches = 32;
-constexpr int64_t kActOrderLds = 64 * 1024;   // most activation bytes an act-order launch stages in LDS
+constexpr int64_t kActOrderLds = 128 * 1024;  // most LDS an act-order launch stages activations in (two copies)
 constexpr int kMinBatches = 4;
 constexpr int kMaxM = 8;                   // activation rows one streaming launch serves
 constexpr int kSkinnyMaxM = 16;            // activation rows of the matrix-core decode kernel
@@ -544,8 +577,9 @@ template <int F, int M, int S, int R, bool MP, bool PERM, bool ONE, bool DYN = f
 int launch_mv_k(GemvArgs a, int64_t count, hipStream_t s) {
   void (*kern)(GemvArgs) = mv_kernel<F, M, S, R, MP, PERM, ONE, DYN>;
   static const int wps = waves_per_simd(reinterpret_cast<const void *>(kern));
-  // act-order activations staged in LDS when they fit beside the partial sums
-  const int64_t xl_bytes = a.perm ? a.m * a.k * 2 : 0;
+  // act-order activations staged in LDS (in natural and in stored-column order) when they fit
+  // beside the partial sums
+  const int64_t xl_bytes = a.perm ? 2 * a.m * a.k * 2 : 0;
   const bool stage = a.perm && xl_bytes <= kActOrderLds;
   MvPlan P = plan_mv(1, &a.n, &a.wk, &count, R, wps, mv_threads<M>() / 64, stage ? xl_bytes : 0,
                      M == 1 && !ONE ? long_nbt<F>() : 0, M == 1 && !PERM && !ONE ? prefer_w<F>() : 0);
@@ -555,7 +589,7 @@ int launch_mv_k(GemvArgs a, int64_t count, hipStream_t s) {
   const int64_t blocks = split_rows(a, R, P.nbt);
   size_t shm = red_bytes(a, R, M);
   a.xl_off = -1;
-  if (stage) {
+  if (stage && (int64_t)((shm + 15) / 16 * 16) + xl_bytes <= kLdsPerCu) {
     a.xl_off = (int64_t)((shm + 15) / 16 * 4);
     shm = (size_t)a.xl_off * 4 + (size_t)xl_bytes;
   }
