@@ -40,6 +40,7 @@ struct GemvArgs {
   int64_t m;                // activation rows (1 for the GEMV)
   const int32_t *perm;      // act-order column permutation (k entries) or null
   int64_t xl_off;           // act-order: float offset of the activations staged in LDS, or -1
+  int xl_two;               // act-order staging: 1 = natural copy then stored-column copy, 0 = the latter only
   int64_t ldx, ldy;         // elements between activation rows / output rows
   int y_f32;
   int wk;                   // waves per workgroup along K
@@ -140,30 +141,39 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
 
   // K passes: the wk waves of a row group cover wk * UPW units per pass. With more than one
   // pass (long K with many activation rows) each wave accumulates its partial sums in LDS.
-  // Act-order with the activations staged in LDS: the workgroup copies its m rows of x
-  // (contiguous 16-byte loads) once, then writes them again in stored-column order (column c
-  // gets x[perm[c]], an index outside [0, k) gives 0), reading the permutation once per
-  // workgroup with contiguous loads. Each lane then reads its activations from the second
-  // copy as contiguous 16-byte pieces, as without a permutation, instead of loading its
-  // indices and gathering 2-byte values itself.
+  // Act-order with the activations staged in LDS in stored-column order (column c holds
+  // x[perm[c]], an index outside [0, k) gives 0), built once per workgroup: each thread reads
+  // 8 permutation entries with two contiguous 16-byte loads, gathers the 8 values and stores
+  // them as one 16-byte piece. With room for two copies, the gather reads a first copy in
+  // natural order (contiguous 16-byte loads of x); otherwise it reads x in global memory.
+  // Each lane then reads its activations from the stored-column copy as contiguous 16-byte
+  // pieces, as without a permutation, instead of loading its own entries and gathering.
   const uint16_t *xq = nullptr;
   if (PERM && a.xl_off >= 0) {
     uint16_t *xn = reinterpret_cast<uint16_t *>(red + a.xl_off);   // [m][k], natural order
-    uint16_t *xs = xn + a.m * a.k;                                  // [m][k], stored-column order
+    uint16_t *xs = a.xl_two ? xn + a.m * a.k : xn;                  // [m][k], stored-column order
     const int64_t chunks = a.k / 8;                          // 16-byte chunks per row
-    for (int64_t i = threadIdx.x; i < a.m * chunks; i += blockDim.x) {
-      const int64_t mm = i / chunks, c = i % chunks;
-      *reinterpret_cast<u32x4 *>(xn + mm * a.k + 8 * c) = ld4(reinterpret_cast<const uint8_t *>(x + mm * a.ldx + 8 * c));
+    if (a.xl_two) {
+      for (int64_t i = threadIdx.x; i < a.m * chunks; i += blockDim.x) {
+        const int64_t mm = i / chunks, c = i % chunks;
+        *reinterpret_cast<u32x4 *>(xn + mm * a.k + 8 * c) = ld4(reinterpret_cast<const uint8_t *>(x + mm * a.ldx + 8 * c));
+      }
+      __syncthreads();
     }
-    __syncthreads();
     const rsrc_t pr = make_rsrc(a.perm, (uint32_t)(a.k * 4));
     for (int64_t i = threadIdx.x; i < a.m * chunks; i += blockDim.x) {
       const int64_t mm = i / chunks, c = i % chunks;
       const u32x4 i0 = bld4c(pr, (uint32_t)(c * 32), 0), i1 = bld4c(pr, (uint32_t)(c * 32 + 16), 0);
       const uint32_t idx[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
       uint32_t hv[8];
+      if (a.xl_two) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) hv[j] = idx[j] < (uint32_t)a.k ? xn[mm * a.k + idx[j]] : 0u;
+        for (int j = 0; j < 8; ++j) hv[j] = idx[j] < (uint32_t)a.k ? xn[mm * a.k + idx[j]] : 0u;
+      } else {
+        const rsrc_t xr = make_rsrc(x + mm * a.ldx, (uint32_t)(a.k * 2));
+#pragma unroll
+        for (int j = 0; j < 8; ++j) hv[j] = bldh(xr, idx[j] * 2, 0);
+      }
       *reinterpret_cast<u32x4 *>(xs + mm * a.k + 8 * c) =
           u32x4{hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16)};
     }
@@ -577,9 +587,11 @@ template <int F, int M, int S, int R, bool MP, bool PERM, bool ONE, bool DYN = f
 int launch_mv_k(GemvArgs a, int64_t count, hipStream_t s) {
   void (*kern)(GemvArgs) = mv_kernel<F, M, S, R, MP, PERM, ONE, DYN>;
   static const int wps = waves_per_simd(reinterpret_cast<const void *>(kern));
-  // act-order activations staged in LDS (in natural and in stored-column order) when they fit
-  // beside the partial sums
-  const int64_t xl_bytes = a.perm ? 2 * a.m * a.k * 2 : 0;
+  // act-order activations staged in LDS (in natural and in stored-column order, or in the
+  // latter only) when they fit beside the partial sums
+  const int64_t row_bytes = a.perm ? a.m * a.k * 2 : 0;
+  a.xl_two = 2 * row_bytes <= kActOrderLds;
+  const int64_t xl_bytes = a.xl_two ? 2 * row_bytes : row_bytes;
   const bool stage = a.perm && xl_bytes <= kActOrderLds;
   MvPlan P = plan_mv(1, &a.n, &a.wk, &count, R, wps, mv_threads<M>() / 64, stage ? xl_bytes : 0,
                      M == 1 && !ONE ? long_nbt<F>() : 0, M == 1 && !PERM && !ONE ? prefer_w<F>() : 0);
