@@ -40,7 +40,6 @@ struct GemvArgs {
   int64_t m;                // activation rows (1 for the GEMV)
   const int32_t *perm;      // act-order column permutation (k entries) or null
   int64_t xl_off;           // act-order: float offset of the activations staged in LDS, or -1
-  int xl_two;               // act-order staging: 1 = natural copy then stored-column copy, 0 = the latter only
   int64_t ldx, ldy;         // elements between activation rows / output rows
   int y_f32;
   int wk;                   // waves per workgroup along K
@@ -78,7 +77,10 @@ template <int M> constexpr int mv_threads() { return M > 4 ? 512 : 1024; }
 // One workgroup of the streaming kernel over matrix b of a (block bx along the rows). Waves
 // past wk * wr (a grouped launch whose workgroup is sized for another matrix) have no rows
 // but still reach the barrier.
-template <int F, int M, int S, int R, bool MP, bool PERM = false, bool ONE = false, bool DYN = false>
+// PERM (act-order): 0 none; 1 the activations staged in LDS in stored-column order, read as
+// contiguous pieces; 2 each lane gathers its own, from a natural-order copy in LDS (when it
+// fits) or from global memory.
+template <int F, int M, int S, int R, bool MP, int PERM = 0, bool ONE = false, bool DYN = false>
 __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b) {
   constexpr int D = ONE ? 1 : kGemvDepth;      // pipeline stages
   using U = Unit<F>;
@@ -141,44 +143,39 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
 
   // K passes: the wk waves of a row group cover wk * UPW units per pass. With more than one
   // pass (long K with many activation rows) each wave accumulates its partial sums in LDS.
-  // Act-order with the activations staged in LDS in stored-column order (column c holds
-  // x[perm[c]], an index outside [0, k) gives 0), built once per workgroup: each thread reads
-  // 8 permutation entries with two contiguous 16-byte loads, gathers the 8 values and stores
-  // them as one 16-byte piece. With room for two copies, the gather reads a first copy in
-  // natural order (contiguous 16-byte loads of x); otherwise it reads x in global memory.
-  // Each lane then reads its activations from the stored-column copy as contiguous 16-byte
-  // pieces, as without a permutation, instead of loading its own entries and gathering.
-  const uint16_t *xq = nullptr;
+  // Act-order, PERM = 1: the workgroup copies its m rows of x into LDS (contiguous 16-byte
+  // loads), then writes them again in stored-column order (column c holds x[perm[c]], an
+  // index outside [0, k) gives 0): each thread reads 8 permutation entries with two 16-byte
+  // loads, gathers the 8 values from the first copy and stores them as one 16-byte piece.
+  // Each lane then reads its activations from the second copy as contiguous 16-byte pieces,
+  // as without a permutation. PERM = 2 (one copy fits): only the natural-order copy, which
+  // each lane gathers from through its own permutation entries.
+  const uint16_t *xq = nullptr, *xl = nullptr;
   if (PERM && a.xl_off >= 0) {
     uint16_t *xn = reinterpret_cast<uint16_t *>(red + a.xl_off);   // [m][k], natural order
-    uint16_t *xs = a.xl_two ? xn + a.m * a.k : xn;                  // [m][k], stored-column order
     const int64_t chunks = a.k / 8;                          // 16-byte chunks per row
-    if (a.xl_two) {
-      for (int64_t i = threadIdx.x; i < a.m * chunks; i += blockDim.x) {
-        const int64_t mm = i / chunks, c = i % chunks;
-        *reinterpret_cast<u32x4 *>(xn + mm * a.k + 8 * c) = ld4(reinterpret_cast<const uint8_t *>(x + mm * a.ldx + 8 * c));
-      }
-      __syncthreads();
-    }
-    const rsrc_t pr = make_rsrc(a.perm, (uint32_t)(a.k * 4));
     for (int64_t i = threadIdx.x; i < a.m * chunks; i += blockDim.x) {
       const int64_t mm = i / chunks, c = i % chunks;
-      const u32x4 i0 = bld4c(pr, (uint32_t)(c * 32), 0), i1 = bld4c(pr, (uint32_t)(c * 32 + 16), 0);
-      const uint32_t idx[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
-      uint32_t hv[8];
-      if (a.xl_two) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) hv[j] = idx[j] < (uint32_t)a.k ? xn[mm * a.k + idx[j]] : 0u;
-      } else {
-        const rsrc_t xr = make_rsrc(x + mm * a.ldx, (uint32_t)(a.k * 2));
-#pragma unroll
-        for (int j = 0; j < 8; ++j) hv[j] = bldh(xr, idx[j] * 2, 0);
-      }
-      *reinterpret_cast<u32x4 *>(xs + mm * a.k + 8 * c) =
-          u32x4{hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16)};
+      *reinterpret_cast<u32x4 *>(xn + mm * a.k + 8 * c) = ld4(reinterpret_cast<const uint8_t *>(x + mm * a.ldx + 8 * c));
     }
     __syncthreads();
-    xq = xs;
+    xl = xn;
+    if constexpr (PERM == 1) {
+      uint16_t *xs = xn + a.m * a.k;                         // [m][k], stored-column order
+      const rsrc_t pr = make_rsrc(a.perm, (uint32_t)(a.k * 4));
+      for (int64_t i = threadIdx.x; i < a.m * chunks; i += blockDim.x) {
+        const int64_t mm = i / chunks, c = i % chunks;
+        const u32x4 i0 = bld4c(pr, (uint32_t)(c * 32), 0), i1 = bld4c(pr, (uint32_t)(c * 32 + 16), 0);
+        const uint32_t idx[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+        uint32_t hv[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) hv[j] = idx[j] < (uint32_t)a.k ? xn[mm * a.k + idx[j]] : 0u;
+        *reinterpret_cast<u32x4 *>(xs + mm * a.k + 8 * c) =
+            u32x4{hv[0] | (hv[1] << 16), hv[2] | (hv[3] << 16), hv[4] | (hv[5] << 16), hv[6] | (hv[7] << 16)};
+      }
+      __syncthreads();
+      xq = xs;
+    }
   }
 
   const int passes = MP ? a.kpasses : 1;
@@ -211,10 +208,10 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
     // outside [0, k) reads 0, never past x).
     uint32_t xp[M][NP];
     auto load_x = [&]() {
-    // (a separate instantiation: the gather's registers at the branch made the register
+    // (separate instantiations: the gather's registers at a branch made the register
     // allocator spill the kernels with 4 and 8 activation rows)
-    if constexpr (PERM) {
-      if (xq) {
+    if constexpr (PERM == 1) {
+      {
 #pragma unroll
         for (int mm = 0; mm < M; ++mm) {
           const bool live = mm < a.m;
@@ -231,9 +228,11 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
             xp[mm][4 * i + 3] = keepx ? v.w : 0u;
           }
         }
-      } else {
-        // the activations did not fit in LDS: the lane gathers its 8 activations per group of 4
-        // pairs through 32-bit buffer loads of the indices and 16-bit buffer loads of x
+      }
+    } else if constexpr (PERM == 2) {
+      {
+        // the lane gathers its 8 activations per group of 4 pairs through 32-bit buffer loads
+        // of the indices and reads of the LDS copy, or 16-bit buffer loads of x
         const rsrc_t pr = make_rsrc(a.perm, (uint32_t)(a.k * 4));
 #pragma unroll
         for (int i = 0; i < NP / 4; ++i) {
@@ -247,10 +246,15 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
           for (int mm = 0; mm < M; ++mm) {
             const bool live = mm < a.m && keepx;
             const int64_t row = mm < a.m ? mm : 0;
-            const rsrc_t xr = make_rsrc(x + row * a.ldx, (uint32_t)(a.k * 2));
             uint32_t hv[8];
+            if (xl) {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) hv[j] = bldh(xr, idx[j] * 2, 0);
+              for (int j = 0; j < 8; ++j) hv[j] = idx[j] < (uint32_t)a.k ? xl[row * a.k + idx[j]] : 0u;
+            } else {
+              const rsrc_t xr = make_rsrc(x + row * a.ldx, (uint32_t)(a.k * 2));
+#pragma unroll
+              for (int j = 0; j < 8; ++j) hv[j] = bldh(xr, idx[j] * 2, 0);
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r) xp[mm][4 * i + r] = live ? (hv[2 * r] | (hv[2 * r + 1] << 16)) : 0u;
           }
@@ -382,7 +386,7 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
   }
 }
 
-template <int F, int M, int S, int R, bool MP, bool PERM, bool ONE = false, bool DYN = false>
+template <int F, int M, int S, int R, bool MP, int PERM, bool ONE = false, bool DYN = false>
 __global__ __launch_bounds__(mv_threads<M>()) void mv_kernel(GemvArgs a) {
   mv_body<F, M, S, R, MP, PERM, ONE, DYN>(a, blockIdx.x, blockIdx.y);
 }
@@ -583,16 +587,15 @@ inline MvPlan plan_dyn(const int64_t *n, int ng, int64_t count, int R, int wps, 
   return {W, (batches + round - 1) / round};
 }
 
-template <int F, int M, int S, int R, bool MP, bool PERM, bool ONE, bool DYN = false>
+template <int F, int M, int S, int R, bool MP, int PERM, bool ONE, bool DYN = false>
 int launch_mv_k(GemvArgs a, int64_t count, hipStream_t s) {
+  const GemvArgs a0 = a;
   void (*kern)(GemvArgs) = mv_kernel<F, M, S, R, MP, PERM, ONE, DYN>;
   static const int wps = waves_per_simd(reinterpret_cast<const void *>(kern));
-  // act-order activations staged in LDS (in natural and in stored-column order, or in the
-  // latter only) when they fit beside the partial sums
-  const int64_t row_bytes = a.perm ? a.m * a.k * 2 : 0;
-  a.xl_two = 2 * row_bytes <= kActOrderLds;
-  const int64_t xl_bytes = a.xl_two ? 2 * row_bytes : row_bytes;
-  const bool stage = a.perm && xl_bytes <= kActOrderLds;
+  // act-order activations staged in LDS when they fit beside the partial sums: two copies
+  // (natural and stored-column order) for PERM = 1, the natural-order one for PERM = 2
+  const int64_t xl_bytes = PERM == 1 ? 2 * a.m * a.k * 2 : PERM == 2 ? a.m * a.k * 2 : 0;
+  const bool stage = PERM && xl_bytes <= kActOrderLds;
   MvPlan P = plan_mv(1, &a.n, &a.wk, &count, R, wps, mv_threads<M>() / 64, stage ? xl_bytes : 0,
                      M == 1 && !ONE ? long_nbt<F>() : 0, M == 1 && !PERM && !ONE ? prefer_w<F>() : 0);
   if (ONE) P.nbt = 1;
@@ -601,7 +604,12 @@ int launch_mv_k(GemvArgs a, int64_t count, hipStream_t s) {
   const int64_t blocks = split_rows(a, R, P.nbt);
   size_t shm = red_bytes(a, R, M);
   a.xl_off = -1;
-  if (stage && (int64_t)((shm + 15) / 16 * 16) + xl_bytes <= kLdsPerCu) {
+  const bool fits = stage && (int64_t)((shm + 15) / 16 * 16) + xl_bytes <= kLdsPerCu;
+  // PERM = 1 reads only the staged copy: without room for it, the per-lane gathers instead
+  if constexpr (PERM == 1) {
+    if (!fits) return launch_mv_k<F, M, S, R, MP, 2, ONE, DYN>(a0, count, s);
+  }
+  if (fits) {
     a.xl_off = (int64_t)((shm + 15) / 16 * 4);
     shm = (size_t)a.xl_off * 4 + (size_t)xl_bytes;
   }
@@ -611,10 +619,10 @@ int launch_mv_k(GemvArgs a, int64_t count, hipStream_t s) {
 
 template <int F, int M, int S, int R, bool MP, bool ONE = false, bool DYN = false>
 int launch_mv(GemvArgs a, int64_t count, hipStream_t s) {
-  if constexpr (ONE) return launch_mv_k<F, M, S, R, MP, false, true>(a, count, s);
-  else if constexpr (DYN) return launch_mv_k<F, M, S, R, MP, false, false, true>(a, count, s);
-  else return a.perm ? launch_mv_k<F, M, S, R, MP, true, false>(a, count, s)
-                     : launch_mv_k<F, M, S, R, MP, false, false>(a, count, s);
+  if constexpr (ONE) return launch_mv_k<F, M, S, R, MP, 0, true>(a, count, s);
+  else if constexpr (DYN) return launch_mv_k<F, M, S, R, MP, 0, false, true>(a, count, s);
+  else return a.perm ? launch_mv_k<F, M, S, R, MP, 1, false>(a, count, s)
+                     : launch_mv_k<F, M, S, R, MP, 0, false>(a, count, s);
 }
 
 template <int F, int M, int S, int R, bool MP, bool ONE = false, bool DYN = false>
