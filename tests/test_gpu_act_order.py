@@ -19,8 +19,9 @@ torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
 FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb", "q4g16", "q4g128", "q4a32", "q4g32h", "q3sb_bf16", "q5sb_bf16", "q3g32", "q5g32"]
-# activation staging by rows x k: two LDS copies up to 128 KB, the stored-column copy alone up
-# to 128 KB (k = 8192 at 4 and 8 rows), none beyond (k = 8448 at 8 rows: per-lane gathers)
+# the three forms by rows x k: two LDS copies (natural and stored-column order) up to 128 KB,
+# one natural-order copy with per-lane gathers up to 128 KB (k = 8192 at 4 and 8 rows), none
+# beyond (k = 8448 at 8 rows: per-lane gathers from global memory)
 SHAPES = [(37, 512), (300, 4352), (9, 8192), (9, 8448)]
 
 
