@@ -399,9 +399,23 @@ int qg_gemm_act_order(int fmt, const void *w, const uint16_t *X, int64_t ldx, co
   a.y = Y;
   a.ldy = m > 1 ? ldy : n;
   a.y_f32 = y_f32;
-  a.m = m;
   a.perm = perm;
-  return launch_mv_fmt(fmt, a, 1, s);
+  // Activation rows that do not fit in LDS even once (m k 2 bytes past kActOrderLds) would be
+  // gathered per lane from global memory, 2.5-3 times slower than the plain kernel; launching
+  // them in chunks of rows that fit re-reads the weights per chunk and is still faster
+  // (measured on one MI355X: 8192 x 28672 at 4 rows 115 -> 64 us, at 8 rows 202 -> 128;
+  // 4096 x 11008 at 8 rows 52 -> 43). Each chunk's result is the streaming kernel's on those
+  // rows; with long K the split of K across waves can differ from the one-launch plan's.
+  int64_t mc = m;
+  while (mc > 1 && mc * k * 2 > kActOrderLds) mc = (mc + 1) / 2;
+  for (int64_t r = 0; r < m; r += mc) {
+    a.x = X + r * a.ldx;
+    a.y = static_cast<uint8_t *>(Y) + r * a.ldy * (y_f32 ? 4 : 2);
+    a.m = m - r < mc ? m - r : mc;
+    st = launch_mv_fmt(fmt, a, 1, s);
+    if (st != QG_OK) return st;
+  }
+  return QG_OK;
 }
 
 int qg_gemm_grouped(int fmt, int count, const void *const *w, const uint16_t *const *X, const int64_t *ldx,

@@ -311,8 +311,11 @@ int qg_gemm(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int
  * the device (16-byte aligned), entries in [0, k) (an entry outside that range reads an
  * activation of 0; it never reads outside X). The gather is fused into the streaming
  * kernel's activation load, so the result equals that kernel's on the gathered activations
- * bit for bit (qg_gemm_grouped's for any m, qg_gemm's for m <= 4). m: 0..8 activation rows
- * (the streaming kernel); other arguments, limits and errors as qg_gemm. */
+ * bit for bit (qg_gemm_grouped's for any m, qg_gemm's for m <= 4). Activation rows of more
+ * than 128 KB (m * k * 2 bytes) run as several launches of half, a quarter, ... of the rows,
+ * the first size that fits; each such chunk equals qg_gemm_grouped's launch on its rows.
+ * m: 0..8 activation rows (the streaming kernel); other arguments, limits and errors as
+ * qg_gemm. */
 int qg_gemm_act_order(int fmt, const void *w, const uint16_t *X, int64_t ldx, const int32_t *perm, void *Y,
                       int64_t ldy, int y_f32, int64_t m, int64_t n, int64_t k, void *stream);
 

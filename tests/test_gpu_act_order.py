@@ -43,10 +43,15 @@ def test_act_order_matches_oracle_and_gathered_gemm(fmt, n, k):
         x = activations(m, k, 11 * m + k)
         X = torch.from_numpy(x).cuda()
         y = qg.gemm_act_order(fmt, wd, X, pd, n, k, out_f32=True)
-        # the same streaming kernel on the gathered activations (qg_gemm takes it up to 4 rows)
+        # the same streaming kernel on the gathered activations (qg_gemm takes it up to 4 rows),
+        # launched on the same row chunks (rows past 128 KB of activations run in halves, ...)
         Xg = X[:, torch.from_numpy(perm).cuda()].contiguous()
         ref = torch.empty_like(y)
-        qg.gemm_grouped(fmt, [wd], [Xg], [(n, k)], outs=[ref])
+        mc = m
+        while mc > 1 and mc * k * 2 > 128 * 1024:
+            mc = (mc + 1) // 2
+        for r in range(0, m, mc):
+            qg.gemm_grouped(fmt, [wd], [Xg[r:r + mc]], [(n, k)], outs=[ref[r:r + mc]])
         torch.cuda.synchronize()
         y_ref, bound = oracle_y(w_eff, x)
         assert_close(y.cpu().numpy(), y_ref, bound, f"{fmt} m={m} {n}x{k}")
