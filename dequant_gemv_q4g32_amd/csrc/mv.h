@@ -211,53 +211,49 @@ __device__ __forceinline__ void mv_body(const GemvArgs &a, int64_t bx, int64_t b
     // (separate instantiations: the gather's registers at a branch made the register
     // allocator spill the kernels with 4 and 8 activation rows)
     if constexpr (PERM == 1) {
-      {
 #pragma unroll
-        for (int mm = 0; mm < M; ++mm) {
-          const bool live = mm < a.m;
-          const uint16_t *px = xq + (int64_t)(live ? mm : 0) * a.k + u * kUnit;
-#pragma unroll
-          for (int i = 0; i < NP / 4; ++i) {
-            uint32_t off = 4u * (uint32_t)U::pidx(h, 4 * i, S);
-            bool keepx = live;
-            if (F == 4 && half && off >= 64) { off -= 64; keepx = false; }
-            const u32x4 v = *reinterpret_cast<const u32x4 *>(px + off / 2);
-            xp[mm][4 * i + 0] = keepx ? v.x : 0u;
-            xp[mm][4 * i + 1] = keepx ? v.y : 0u;
-            xp[mm][4 * i + 2] = keepx ? v.z : 0u;
-            xp[mm][4 * i + 3] = keepx ? v.w : 0u;
-          }
-        }
-      }
-    } else if constexpr (PERM == 2) {
-      {
-        // the lane gathers its 8 activations per group of 4 pairs through 32-bit buffer loads
-        // of the indices and reads of the LDS copy, or 16-bit buffer loads of x
-        const rsrc_t pr = make_rsrc(a.perm, (uint32_t)(a.k * 4));
+      for (int mm = 0; mm < M; ++mm) {
+        const bool live = mm < a.m;
+        const uint16_t *px = xq + (int64_t)(live ? mm : 0) * a.k + u * kUnit;
 #pragma unroll
         for (int i = 0; i < NP / 4; ++i) {
           uint32_t off = 4u * (uint32_t)U::pidx(h, 4 * i, S);
-          bool keepx = true;
+          bool keepx = live;
           if (F == 4 && half && off >= 64) { off -= 64; keepx = false; }
-          const uint32_t kb = (uint32_t)(u * kUnit) + off / 2;   // first of the 8 stored columns
-          const u32x4 i0 = bld4c(pr, kb * 4, 0), i1 = bld4c(pr, kb * 4 + 16, 0);
-          const uint32_t idx[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
+          const u32x4 v = *reinterpret_cast<const u32x4 *>(px + off / 2);
+          xp[mm][4 * i + 0] = keepx ? v.x : 0u;
+          xp[mm][4 * i + 1] = keepx ? v.y : 0u;
+          xp[mm][4 * i + 2] = keepx ? v.z : 0u;
+          xp[mm][4 * i + 3] = keepx ? v.w : 0u;
+        }
+      }
+    } else if constexpr (PERM == 2) {
+      // the lane gathers its 8 activations per group of 4 pairs through 32-bit buffer loads
+      // of the indices and reads of the LDS copy, or 16-bit buffer loads of x
+      const rsrc_t pr = make_rsrc(a.perm, (uint32_t)(a.k * 4));
 #pragma unroll
-          for (int mm = 0; mm < M; ++mm) {
-            const bool live = mm < a.m && keepx;
-            const int64_t row = mm < a.m ? mm : 0;
-            uint32_t hv[8];
-            if (xl) {
+      for (int i = 0; i < NP / 4; ++i) {
+        uint32_t off = 4u * (uint32_t)U::pidx(h, 4 * i, S);
+        bool keepx = true;
+        if (F == 4 && half && off >= 64) { off -= 64; keepx = false; }
+        const uint32_t kb = (uint32_t)(u * kUnit) + off / 2;   // first of the 8 stored columns
+        const u32x4 i0 = bld4c(pr, kb * 4, 0), i1 = bld4c(pr, kb * 4 + 16, 0);
+        const uint32_t idx[8] = {i0.x, i0.y, i0.z, i0.w, i1.x, i1.y, i1.z, i1.w};
 #pragma unroll
-              for (int j = 0; j < 8; ++j) hv[j] = idx[j] < (uint32_t)a.k ? xl[row * a.k + idx[j]] : 0u;
-            } else {
-              const rsrc_t xr = make_rsrc(x + row * a.ldx, (uint32_t)(a.k * 2));
+        for (int mm = 0; mm < M; ++mm) {
+          const bool live = mm < a.m && keepx;
+          const int64_t row = mm < a.m ? mm : 0;
+          uint32_t hv[8];
+          if (xl) {
 #pragma unroll
-              for (int j = 0; j < 8; ++j) hv[j] = bldh(xr, idx[j] * 2, 0);
-            }
+            for (int j = 0; j < 8; ++j) hv[j] = idx[j] < (uint32_t)a.k ? xl[row * a.k + idx[j]] : 0u;
+          } else {
+            const rsrc_t xr = make_rsrc(x + row * a.ldx, (uint32_t)(a.k * 2));
 #pragma unroll
-            for (int r = 0; r < 4; ++r) xp[mm][4 * i + r] = live ? (hv[2 * r] | (hv[2 * r + 1] << 16)) : 0u;
+            for (int j = 0; j < 8; ++j) hv[j] = bldh(xr, idx[j] * 2, 0);
           }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) xp[mm][4 * i + r] = live ? (hv[2 * r] | (hv[2 * r + 1] << 16)) : 0u;
         }
       }
     } else {
