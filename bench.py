@@ -67,8 +67,10 @@ def parse():
                     help="only run --steps rounds over the matrices of workload NAME, rotated over >= 1.2 GB "
                          "of copies, eagerly (for profiler runs; kv_cache_int8_7b_8192: rounds of the KV-cache "
                          "codec); prints no JSON line")
-    ap.add_argument("--profile-plan", choices=("single", "group"), default="single",
-                    help="one launch per matrix, or all matrices in one grouped launch")
+    ap.add_argument("--profile-plan", choices=("single", "group", "act_order"), default="single",
+                    help="one launch per matrix, all matrices in one grouped launch, or one act-order "
+                         "launch per matrix (a random column permutation per matrix)")
+    ap.add_argument("--profile-fmt", default=None, help="weight format instead of the workload's")
     ap.add_argument("--profile-m", type=int, default=None, help="batch (activation rows) instead of the workload's")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 512 MiB device copy (the reference kernel for HBM counters)")
@@ -519,10 +521,11 @@ def main():
     if args.profile_workload:
         wl = WORKLOADS[args.profile_workload]
         m = args.profile_m or wl.m
-        cs = [(qg.quantize(wl.fmt, wl.weights(i)), n, k) for i, (n, k) in enumerate(wl.shapes)]
+        fmt = args.profile_fmt or wl.fmt
+        cs = [(qg.quantize(fmt, wl.weights(i)), n, k) for i, (n, k) in enumerate(wl.shapes)]
         idx = list(range(len(cs)))
-        plan = [("group", idx)] if args.profile_plan == "group" else [("single", [i]) for i in idx]
-        alg, rnd = build_set(qg, wl.fmt, cs, m, torch.device("cuda:0"), plan, args.footprint_gb)
+        plan = [("group", idx)] if args.profile_plan == "group" else [(args.profile_plan, [i]) for i in idx]
+        alg, rnd = build_set(qg, fmt, cs, m, torch.device("cuda:0"), plan, args.footprint_gb)
         state = {"r": 0}
 
         def one():
@@ -534,7 +537,7 @@ def main():
             one()
         torch.cuda.synchronize()
         log(f"[bench] profiled {args.profile_workload}: {args.steps} rounds of {len(plan)} launches after "
-            f"{warm_rounds} warm-up rounds, {wl.fmt} m={m}, shapes {list(wl.shapes)}, {alg} algorithmic bytes per round")
+            f"{warm_rounds} warm-up rounds, {fmt} m={m}, shapes {list(wl.shapes)}, {alg} algorithmic bytes per round")
         return
 
     wl = WORKLOADS[args.workload]
