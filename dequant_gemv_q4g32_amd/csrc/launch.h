@@ -27,6 +27,9 @@ int launch(void (*kernel)(KArgs...), dim3 grid, dim3 block, size_t shm, hipStrea
 int launch_prefill(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int64_t ldy, int y_f32,
                    int64_t m, int64_t n, int64_t k, hipStream_t s);
 
+// Tile shape the prefill GEMM takes for m x n (BM x BN; prefill.hip).
+void prefill_tile(int64_t m, int64_t n, int *bm, int *bn);
+
 // Dequant GEMM for up to 16 activation rows through fp16 MFMA (skinny.hip; qg_gemm sends it
 // 5 <= m <= 16). Arguments are validated by the caller.
 int launch_skinny(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int64_t ldy, int y_f32,
