@@ -341,27 +341,27 @@ int qg_gemv(int fmt, const void *w, const uint16_t *x, void *y, int y_f32, int64
 
 // A few more than 16 activation rows: the prefill tiles then carry mostly dead rows, and a
 // launch takes about as long at 17 rows as at 64 (each K step of a tile costs its latency,
-// not its MFMAs). Launches of the 16-row matrix-core kernel, one per 16 rows, each re-read
-// the weights but can be faster. Estimates (measured on one MI355X for 11008 x 4096,
-// 4096 x 4096, 4096 x 11008, 12288 x 4096 and 28672 x 8192 in q4g32, q3sb and q5sb at 17 to
-// 128 rows): a 16-row launch takes 3 us plus its weight bytes at 2.7 TB/s or its weights at
-// 4.5 per ns, whichever is longer (it is bound by the decode as much as by the stream); a
-// prefill launch takes per K step and round of workgroups about 0.5 us with 128-row tiles
-// (0.68 us with more than one workgroup per CU) and 1.2 us with 256-row tiles. The chunks
-// must win by 5%. At 17-32 rows they measured 1.3-3.2x faster on those shapes; at 48-96 rows
-// they win where n = 4096 (4096 x 11008 at 64 rows: 76 -> 49 us).
+// not its MFMAs). Launches of the matrix-core decode kernel, one per 32 rows (the last one
+// 16 rows when at most 16 remain), each re-read the weights but can be faster. A 32-row
+// launch decodes each weight once for two 16-row MFMAs and takes about 1.35x a 16-row one.
+// Estimates (measured on one MI355X for 11008 x 4096, 4096 x 4096, 4096 x 11008,
+// 12288 x 4096 and 28672 x 8192 in q4g32, q3sb and q5sb at 17 to 128 rows): skinny_us for
+// each launch; a prefill launch takes per K step and round of workgroups about 0.5 us with
+// 128-row tiles (0.68 us with more than one workgroup per CU) and 1.2 us with 256-row tiles.
+// The launches must win by 5%. At 17-32 rows the single launch measured 1.3-3.9x faster
+// than the prefill tiles on those shapes; at 48-64 rows two launches win on all of them but
+// 12288 x 4096, and up to 128 rows where n = 4096.
 static bool skinny_chunks_faster(int fmt, int64_t m, int64_t n, int64_t k) {
   if (m > 8 * kSkinnyMaxM) return false;
-  qg_layout lay;
-  if (qg_device_layout(fmt, n, k, &lay) != QG_OK) return false;
   int bm, bn;
   prefill_tile(m, n, &bm, &bn);
   const int64_t tiles = ((m + bm - 1) / bm) * ((n + bn - 1) / bn), slots = bn == 96 ? 256 : 512;
   const double steps = (double)((k + kUnit - 1) / kUnit) * (double)((tiles + slots - 1) / slots);
   const double prefill_us = (bm == 128 ? (tiles > 256 ? 0.68 : 0.5) : 1.2) * steps;
-  const double stream_us = (double)lay.algorithmic_bytes / 2.7e6, decode_us = (double)n * (double)k / 4.5e6;
-  const double chunk_us = 3.0 + (stream_us > decode_us ? stream_us : decode_us);
-  return 1.05 * (double)((m + kSkinnyMaxM - 1) / kSkinnyMaxM) * chunk_us < prefill_us;
+  const int64_t rest = m % (2 * kSkinnyMaxM);
+  const double chunks_us = (double)(m / (2 * kSkinnyMaxM)) * skinny_us(fmt, 2 * kSkinnyMaxM, n, k) +
+                           (rest ? skinny_us(fmt, rest, n, k) : 0.0);
+  return 1.05 * chunks_us < prefill_us;
 }
 
 int qg_gemm(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int64_t ldy, int y_f32, int64_t m,
@@ -391,12 +391,13 @@ int qg_gemm(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int
   // up to 4 activation rows: the streaming kernel (every decoded code pair meets each row in
   // a v_dot2); 5 to 16: fp16 w_hat on the matrix cores in one weight stream (from 5 rows
   // on, the v_dot2 per row and code pair cost more than the decode that the matrix cores
-  // need once); more rows: LDS-staged fp16 tiles on the matrix cores
+  // need once); more rows: LDS-staged fp16 tiles on the matrix cores, or launches of up to 32
+  // rows of the decode kernel where they are estimated faster
   if (m > kGemmStreamMaxM && m <= kSkinnyMaxM) return launch_skinny(fmt, w, X, ldx, Y, ldy, y_f32, m, n, k, s);
   if (m > kSkinnyMaxM && skinny_chunks_faster(fmt, m, n, k)) {
-    for (int64_t r = 0; r < m; r += kSkinnyMaxM) {
+    for (int64_t r = 0; r < m; r += 2 * kSkinnyMaxM) {
       st = launch_skinny(fmt, w, X + r * ldx, ldx, static_cast<uint8_t *>(Y) + r * ldy * esz, ldy, y_f32,
-                         m - r < kSkinnyMaxM ? m - r : kSkinnyMaxM, n, k, s);
+                         m - r < 2 * kSkinnyMaxM ? m - r : 2 * kSkinnyMaxM, n, k, s);
       if (st != QG_OK) return st;
     }
     return QG_OK;

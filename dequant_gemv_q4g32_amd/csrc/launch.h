@@ -30,9 +30,14 @@ int launch_prefill(int fmt, const void *w, const uint16_t *X, int64_t ldx, void 
 // Tile shape the prefill GEMM takes for m x n (BM x BN; prefill.hip).
 void prefill_tile(int64_t m, int64_t n, int *bm, int *bn);
 
-// Dequant GEMM for up to 16 activation rows through fp16 MFMA (skinny.hip; qg_gemm sends it
-// 5 <= m <= 16). Arguments are validated by the caller.
+// Dequant GEMM for up to 32 activation rows through fp16 MFMA (skinny.hip; qg_gemm sends it
+// 5 <= m <= 16, and more rows in launches of up to 32 when skinny_us says so). Arguments are
+// validated by the caller.
 int launch_skinny(int fmt, const void *w, const uint16_t *X, int64_t ldx, void *Y, int64_t ldy, int y_f32,
                   int64_t m, int64_t n, int64_t k, hipStream_t s);
+
+// Estimated duration in microseconds of one launch_skinny of m <= 32 rows (a huge value for
+// shapes it does not take).
+double skinny_us(int fmt, int64_t m, int64_t n, int64_t k);
 
 }  // namespace qg

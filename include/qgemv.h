@@ -257,8 +257,10 @@ int qg_gemv_batched(int fmt, const void *w, int64_t w_stride, const uint16_t *x,
  * decodes each code once to fp16 and multiplies on the matrix cores in the same single
  * weight stream, and m > 16 (prefill) stages fp16 weight and activation tiles in LDS for
  * 32x32 matrix-core tiles. For 17 <= m <= 128, when a cost estimate says so (the prefill
- * tiles then carry mostly dead rows), the rows run instead as launches of the 16-row kernel,
- * one per 16 rows. Limits as dequant_gemv_*; also ldx < 2^26 for 5 <= m <= 16 and
+ * tiles then carry mostly dead rows), the rows run instead as launches of that decode
+ * kernel of up to 32 rows each (two 16-row blocks share each decoded fragment; a 32-row
+ * launch gives the same bits as two 16-row launches). Limits as dequant_gemv_*; also
+ * ldx < 2^26 for 5 <= m <= 16 and
  * ldx < 2^22 for m > 16 (32-bit activation offsets within a 16-row or a 256-row tile).
  * m == 0 or n == 0 is a no-op; k == 0 writes zeros. Errors as dequant_gemv_*.
  * Precision: m <= 4 works on the codes in fp32 (the 2e-3 * sum |W_hat x| bound holds at any

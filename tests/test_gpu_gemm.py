@@ -2,8 +2,9 @@
 
 Bar: every output Y[i, r] within 2e-3 * sum_k |X[i,k] W_hat[r,k]| (fp16 and fp32 output).
 Covers the three kernels qg_gemm routes to (the streaming kernel for 1-4 rows, built for 1,
-2 and 4 rows per launch with the unused rows masked; the matrix-core decode kernel for 5-16;
-the prefill kernel beyond), strided X and Y, K split over several waves and over several
+2 and 4 rows per launch with the unused rows masked; the matrix-core decode kernel for 5-16,
+and for 17-32 as two 16-row blocks per decoded fragment where estimated faster; the prefill
+kernel beyond), strided X and Y, K split over several waves and over several
 passes (the streaming kernel's passes at 8 rows through the grouped entry point), ragged n,
 and the full-size decode workloads with 2, 4 and 8 activation rows on sampled output rows.
 """
@@ -19,7 +20,7 @@ pytestmark = pytest.mark.gpu
 
 FMTS = ["q4g32", "q2sb", "q3sb", "q5sb", "q6sb", "q4g16", "q4g64", "q4g128", "q4a32", "q4g32h",
         "q2sb_bf16", "q3sb_bf16", "q5sb_bf16", "q6sb_bf16", "q3g32", "q5g32", "q3sb_planes"]
-MS = [1, 2, 3, 4, 5, 8, 11, 17]
+MS = [1, 2, 3, 4, 5, 8, 11, 17, 32]
 # (n, k): several row blocks and a ragged tail, K over 1..8 waves, and (5, 28672) over two
 # passes
 SHAPES = [(37, 512), (1001, 1024), (20, 4352), (9, 8192), (5, 28672)]
@@ -221,3 +222,23 @@ def test_matrix_core_plans_on_7b_shapes_sampled_rows(fmt):
             y_ref, bound = oracle_y(w_hat, x)
             torch.cuda.synchronize()
             assert_close(y.cpu().numpy()[:, rows], y_ref, bound, f"{fmt} m={m} {n}x{k}")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_32_row_launch_equals_two_16_row_launches(fmt):
+    """17-32 rows run as one launch of the matrix-core decode kernel with two 16-row blocks
+    sharing each decoded fragment (on these shapes the cost estimate prefers it to the
+    prefill tiles); each block's sums are formed as in a 16-row launch, so the output equals,
+    bit for bit, that of separate launches on rows 0-15 and 16-m. Shapes: one tile per
+    workgroup (4096 x 4096: 256 row tiles), the two-stage pipeline over 4 tiles per
+    workgroup (11008 x 4096), K over several passes (70 x 28672), a ragged n (1001 x 1024)."""
+    for n, k in ((1001, 1024), (4096, 4096), (11008, 4096), (70, 28672)):
+        wd = device_weights(fmt, laplace_weights(n, k, 0.02, 3 * n + k))
+        for m in (21, 32):
+            x = torch.from_numpy(activations(m, k, m * k + n)).cuda()
+            y = qg.gemm(fmt, wd, x, n, k, out_f32=True)
+            y0 = qg.gemm(fmt, wd, x[:16].contiguous(), n, k, out_f32=True)
+            y1 = qg.gemm(fmt, wd, x[16:].contiguous(), n, k, out_f32=True)
+            torch.cuda.synchronize()
+            assert torch.equal(y[:16], y0), f"{fmt} m={m} {n}x{k} rows 0-15"
+            assert torch.equal(y[16:], y1), f"{fmt} m={m} {n}x{k} rows 16-{m - 1}"

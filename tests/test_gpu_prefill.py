@@ -6,8 +6,9 @@ weights carry at most two fp16 roundings (about 1e-3 of |w_hat|), inside that bo
 The kernel tiles Y in 256 activation rows by 64 weight rows, by 96 where those tiles fill
 the rounds of workgroups on the CUs better, or in 128 by 32 where 256 x 64 tiles would leave
 CUs without a workgroup. Covers all three tile shapes (the small shapes below and 512 x 4099 take 128 x 32
-tiles, except 130 x 4352 at 64 and 128 rows, which qg_gemm runs as 16-row matrix-core
-launches; the wide shapes 256 x 64; 300 x 10003 and the full-size workloads 256 x 96), m
+tiles, except where qg_gemm's cost estimate runs the rows as 32-row matrix-core decode
+launches instead: 130 x 4352 at 64 rows, and in some formats 130 x 4352 at 128 rows and
+300 x 1024 at 64; the wide shapes 256 x 64; 300 x 10003 and the full-size workloads 256 x 96), m
 below, at and above one M tile and ragged across several, n not a multiple of either weight
 tile, K over one and many steps, ragged q4g32 K, strided X and Y, fp16 and fp32 output, and
 the full-size 512 x 11008 x 4096 prefill workloads on sampled weight rows.
