@@ -384,14 +384,14 @@ def extra_configs(qg, dev):
     log(f"[bench] read probe over the same launch patterns: {out['read_probe_launch_patterns_context']}")
     del pbuf
     torch.cuda.empty_cache()
-    # 70B-like layer set at batch 1, 2, 4, 8, 16 (q3sb and q5sb share the fp32 weights): one launch
+    # 70B-like layer set at batch 1, 2, 4, 8, 16, 32 (q3sb and q5sb share the fp32 weights): one launch
     # per matrix (the matrices depend on each other in a decode step), and all three in one
     # grouped launch (up to batch 8)
     wl = WORKLOADS["q3sb_70b_layer_set_m1"]
     w70 = [wl.weights(i) for i in range(len(wl.shapes))]
     for fmt in ("q3sb", "q5sb"):
         cs = [(qg.quantize(fmt, w), w.shape[0], w.shape[1]) for w in w70]
-        for m in (1, 2, 4, 8, 16):
+        for m in (1, 2, 4, 8, 16, 32):
             alg, us = measure_set(qg, fmt, cs, m, dev, [("single", [0]), ("single", [1]), ("single", [2])], rounds=12)
             flops = 2 * m * sum(n * k for _, n, k in cs)
             out[f"{fmt}_70b_layer_set_m{m}"] = {**_rate(alg, us), "TFLOPs": round(flops / us / 1e6, 2)}
