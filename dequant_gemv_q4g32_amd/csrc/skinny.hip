@@ -284,12 +284,14 @@ static SkinnyPlan skinny_plan(int64_t m, int64_t n, int64_t k) {
   const int64_t lds = p.mb == 2 ? kSkinnyLds2 : kSkinnyLds;
   const int64_t nb_lds = (lds - p.wk * kStageBytes) / (p.wk * p.mb * 256 * (int64_t)sizeof(float)) / kStages * kStages;
   if (nb > nb_lds) nb = nb_lds;
-  // A grid a little over one workgroup per CU gives most CUs one workgroup and a few two,
-  // and every workgroup re-reads all the activation rows of its K range: twice the tiles per
-  // workgroup instead, while that still keeps half the CUs busy (11008 x 4096 with 8 or 16
-  // rows: 344 workgroups of 2 tiles 16.4 us, 172 of 4 tiles 13.1 us, measured on one MI355X).
+  // A grid of up to one and a half workgroups per CU gives most CUs one workgroup and some
+  // two, and every workgroup re-reads all the activation rows of its K range: twice the
+  // tiles per workgroup instead, while that still keeps half the CUs busy (measured on one
+  // MI355X, q4g32: 11008 x 4096 at 8 or 16 rows, 344 workgroups of 2 tiles 16.4 us, 172 of
+  // 4 tiles 13.1 us; 12288 x 4096 at 16 rows, 384 of 2 18.9 us, 192 of 4 15.3 us; 12288 x
+  // 8192 at 32 rows 40.3 -> 31.4 us).
   const int64_t wgs = (tiles + nb - 1) / nb, nb2 = nb + kStages;
-  if (wgs > 256 && wgs < 384 && nb2 <= kSkinnyMaxNb && nb2 <= nb_lds && (tiles + nb2 - 1) / nb2 >= 128) nb = nb2;
+  if (wgs > 256 && wgs <= 384 && nb2 <= kSkinnyMaxNb && nb2 <= nb_lds && (tiles + nb2 - 1) / nb2 >= 128) nb = nb2;
   // At most 256 tiles: two tiles per workgroup would leave at least half the CUs idle, so
   // each workgroup takes one (an unpipelined tile).
   if (nb == kStages && tiles <= 256) nb = 1;
