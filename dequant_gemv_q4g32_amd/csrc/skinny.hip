@@ -284,14 +284,15 @@ static SkinnyPlan skinny_plan(int64_t m, int64_t n, int64_t k) {
   const int64_t lds = p.mb == 2 ? kSkinnyLds2 : kSkinnyLds;
   const int64_t nb_lds = (lds - p.wk * kStageBytes) / (p.wk * p.mb * 256 * (int64_t)sizeof(float)) / kStages * kStages;
   if (nb > nb_lds) nb = nb_lds;
-  // A grid of up to one and a half workgroups per CU gives most CUs one workgroup and some
-  // two, and every workgroup re-reads all the activation rows of its K range: twice the
-  // tiles per workgroup instead, while that still keeps half the CUs busy (measured on one
-  // MI355X, q4g32: 11008 x 4096 at 8 or 16 rows, 344 workgroups of 2 tiles 16.4 us, 172 of
-  // 4 tiles 13.1 us; 12288 x 4096 at 16 rows, 384 of 2 18.9 us, 192 of 4 15.3 us; 12288 x
-  // 8192 at 32 rows 40.3 -> 31.4 us).
-  const int64_t wgs = (tiles + nb - 1) / nb, nb2 = nb + kStages;
-  if (wgs > 256 && wgs <= 384 && nb2 <= kSkinnyMaxNb && nb2 <= nb_lds && (tiles + nb2 - 1) / nb2 >= 128) nb = nb2;
+  // A grid of more than one workgroup per CU runs in two rounds, and every workgroup
+  // re-reads all the activation rows of its K range: the next larger tile count instead when
+  // that grid fits one round and still keeps half the CUs busy (measured on one MI355X,
+  // q4g32: 11008 x 4096 at 8 or 16 rows, 344 workgroups of 2 tiles 16.4 us, 172 of 4 tiles
+  // 13.1 us; 12288 x 4096 at 16 rows, 384 of 2 18.9 us, 192 of 4 15.3 us; 14336 x 4096 at
+  // 16 rows, 448 of 2 19.1 us, 224 of 4 15.2 us; 14336 x 8192 at 32 rows 41.6 -> 32.5 us).
+  // 28672 x 8192 keeps 448 of 4: 299 of 6 would still take two rounds.
+  const int64_t wgs = (tiles + nb - 1) / nb, nb2 = nb + kStages, wgs2 = (tiles + nb2 - 1) / nb2;
+  if (wgs > 256 && wgs2 <= 256 && wgs2 >= 128 && nb2 <= kSkinnyMaxNb && nb2 <= nb_lds) nb = nb2;
   // At most 256 tiles: two tiles per workgroup would leave at least half the CUs idle, so
   // each workgroup takes one (an unpipelined tile).
   if (nb == kStages && tiles <= 256) nb = 1;
