@@ -55,8 +55,7 @@ constexpr int kSkinnyMaxWk = 8;
 constexpr int kSkinnyMaxNb = 32;           // row tiles per workgroup (a multiple of kStages)
 constexpr int kStageLine = 144;            // bytes per staged activation line (128 + 16 of padding)
 constexpr int64_t kStageBytes = 64 * kStageLine;   // one wave's staged activations
-constexpr int64_t kSkinnyLds = 128 * 1024; // LDS: staging for every wave, then wk * nb * 256 floats
-constexpr int64_t kSkinnyLds2 = 160 * 1024; // the same with 32 rows: wk * nb * 512 floats
+constexpr int64_t kSkinnyLds = 160 * 1024; // LDS: staging for every wave, then wk * nb * 256 (32 rows: 512) floats
 constexpr uint32_t kSkX = 0x7FFFFFF0u;     // activation buffer range; offsets past it read 0
 constexpr int64_t kSkinnyWaves = 4096;     // about 4 waves per SIMD
 
@@ -279,20 +278,26 @@ static SkinnyPlan skinny_plan(int64_t m, int64_t n, int64_t k) {
   int64_t nb = tiles * p.wk / kSkinnyWaves;
   nb = nb < 1 ? 1 : (nb > kSkinnyMaxNb ? kSkinnyMaxNb : nb);
   nb = (nb + kStages - 1) / kStages * kStages;      // whole pipeline rounds; extra tiles are past n
-  // staging and every wave's partial tiles fit in LDS (32 rows: the whole CU's LDS, since the
-  // partial tiles are twice the size)
-  const int64_t lds = p.mb == 2 ? kSkinnyLds2 : kSkinnyLds;
-  const int64_t nb_lds = (lds - p.wk * kStageBytes) / (p.wk * p.mb * 256 * (int64_t)sizeof(float)) / kStages * kStages;
+  // staging and every wave's partial tiles fit in the CU's LDS
+  const int64_t nb_lds = (kSkinnyLds - p.wk * kStageBytes) / (p.wk * p.mb * 256 * (int64_t)sizeof(float)) / kStages * kStages;
   if (nb > nb_lds) nb = nb_lds;
   // A grid of more than one workgroup per CU runs in two rounds, and every workgroup
-  // re-reads all the activation rows of its K range: the next larger tile count instead when
-  // that grid fits one round and still keeps half the CUs busy (measured on one MI355X,
-  // q4g32: 11008 x 4096 at 8 or 16 rows, 344 workgroups of 2 tiles 16.4 us, 172 of 4 tiles
-  // 13.1 us; 12288 x 4096 at 16 rows, 384 of 2 18.9 us, 192 of 4 15.3 us; 14336 x 4096 at
-  // 16 rows, 448 of 2 19.1 us, 224 of 4 15.2 us; 14336 x 8192 at 32 rows 41.6 -> 32.5 us).
-  // 28672 x 8192 keeps 448 of 4: 299 of 6 would still take two rounds.
-  const int64_t wgs = (tiles + nb - 1) / nb, nb2 = nb + kStages, wgs2 = (tiles + nb2 - 1) / nb2;
-  if (wgs > 256 && wgs2 <= 256 && wgs2 >= 128 && nb2 <= kSkinnyMaxNb && nb2 <= nb_lds) nb = nb2;
+  // re-reads all the activation rows of its K range: the next larger tile count (by one or
+  // two pipeline rounds) whose grid fits one round and still keeps half the CUs busy
+  // instead (measured on one MI355X, q4g32: 11008 x 4096 at 8 or 16 rows, 344 workgroups of
+  // 2 tiles 16.4 us, 172 of 4 tiles 13.1 us; 12288 x 4096 at 16 rows, 384 of 2 18.9 us,
+  // 192 of 4 15.3 us; 14336 x 4096 at 16 rows, 448 of 2 19.1 us, 224 of 4 15.2 us;
+  // 28672 x 8192 at 16 rows, 448 of 4 50.7 us, 224 of 8 44.8 us; 22016 x 4096 at 16 rows,
+  // 688 of 2 27.9 us, 230 of 6 20.1 us).
+  if ((tiles + nb - 1) / nb > 256) {
+    for (int64_t nb2 = nb + kStages; nb2 <= nb + 2 * kStages; nb2 += kStages) {
+      const int64_t wgs2 = (tiles + nb2 - 1) / nb2;
+      if (wgs2 <= 256 && wgs2 >= 128 && nb2 <= kSkinnyMaxNb && nb2 <= nb_lds) {
+        nb = nb2;
+        break;
+      }
+    }
+  }
   // At most 256 tiles: two tiles per workgroup would leave at least half the CUs idle, so
   // each workgroup takes one (an unpipelined tile).
   if (nb == kStages && tiles <= 256) nb = 1;
@@ -308,7 +313,7 @@ double skinny_us(int fmt, int64_t m, int64_t n, int64_t k) {
   const SkinnyPlan p = skinny_plan(m, n, k);
   // workgroups resident per CU: LDS, and VGPRs (about 136 per lane with 16 rows, 200 with 32:
   // 3 or 2 waves per SIMD)
-  int64_t per_cu = kSkinnyLds2 / (int64_t)p.shm;
+  int64_t per_cu = kSkinnyLds / (int64_t)p.shm;
   const int64_t by_vgpr = 4 * (p.mb == 2 ? 2 : 3) / p.wk;
   if (by_vgpr < per_cu) per_cu = by_vgpr;
   if (per_cu < 1) per_cu = 1;

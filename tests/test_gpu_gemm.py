@@ -209,9 +209,10 @@ def test_row_results_do_not_depend_on_launch_shape(fmt):
 def test_matrix_core_plans_on_7b_shapes_sampled_rows(fmt):
     """The matrix-core kernel's launch plans at 8 and 16 activation rows on the 7B-like
     shapes: 4 row tiles per workgroup (11008 x 4096, 12288 x 4096 and 14336 x 4096, grids
-    of 344, 384 and 448 workgroups at 2), and one tile per workgroup (4096 x 11008: 256
-    tiles, K over six passes); the oracle recomputes sampled output rows."""
-    for n, k in ((11008, 4096), (12288, 4096), (14336, 4096), (4096, 11008)):
+    of 344, 384 and 448 workgroups at 2), 6 (22016 x 4096: 688 at 2, 344 at 4, both over
+    one round of workgroups), and one tile per workgroup (4096 x 11008: 256 tiles, K over
+    six passes); the oracle recomputes sampled output rows."""
+    for n, k in ((11008, 4096), (12288, 4096), (14336, 4096), (22016, 4096), (4096, 11008)):
         w = laplace_weights(n, k, 0.02, n + 3 * k, outlier_frac=0.001)
         wd = device_weights(fmt, w)
         rows = _sampled_rows(n, n + k)
